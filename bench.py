@@ -1,0 +1,178 @@
+"""Benchmark: LM iterations/s of large-scale bundle adjustment on one MI355X.
+
+A step is one full LM iteration (linearise, assemble, damp, eliminate points,
+PCG on the reduced camera system, back-substitute, retract, trial cost,
+accept/reject) of libba on the synthetic large scene: 1,000 ring cameras,
+400,000 points, power-law track lengths on {2..50} (2,203,610 observations),
+1 px noise with 5 % outliers, Huber 2 px, PCG at most 50 iterations to a 1e-6
+relative residual.  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  The roofline object refers to the kernel with the
+largest total time in a profiled warm-up run; its average launch time is
+taken with HIP events on the library's stream during the timed region.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LM iterations/s and observations/s (fp64, 1 GPU); % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "nonlinear_least_squares_amd", "csrc", "ba_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_large.json")
+
+
+def pcg_iteration_bytes(n_obs, n_pts, n_cams, n_chunks):
+    """Compulsory HBM bytes of one PCG iteration of the matrix-free solve:
+    point pass (observation camera/point index and weight, point X, C~^-1,
+    written z), camera pass (point index and weight, X and z of each point,
+    chunk partials), camera vectors (B~, Cholesky of S_jj, x r z p q)."""
+    cam = n_cams * (128 + 72)
+    point_pass = n_obs * (4 + 4 + 8) + n_pts * (24 + 48 + 24) + cam
+    camera_pass = n_obs * (4 + 8) + n_pts * (24 + 24) + n_chunks * 72 * 2 + cam
+    vectors = n_cams * 8 * (45 + 45 + 9 * 9)
+    return point_pass + camera_pass + vectors
+
+
+def algorithmic_bytes(kernel, n_obs, n_pts, n_cams, n_chunks):
+    """Compulsory HBM bytes of one launch: each array element the kernel must
+    read or write once (per-camera tables are small and counted once)."""
+    cam = n_cams * (128 + 72)                 # camera table + one camera vector
+    if kernel == "pcg_pt":
+        return n_obs * (4 + 4 + 8) + n_pts * (24 + 48 + 24) + cam
+    if kernel == "pcg_cam":
+        return n_obs * (4 + 8) + n_pts * (24 + 24) + n_chunks * 72 * 2 + cam
+    if kernel == "pcg_q":
+        return n_cams * 8 * (45 + 9 * 2) + n_chunks * 72
+    if kernel == "pcg_xr":
+        return n_cams * 8 * (45 + 9 * 7)
+    if kernel == "lin_pt":
+        return n_obs * (4 + 4 + 16 + 8) + n_pts * (24 + 72) + cam
+    if kernel == "lin_cam":
+        return n_obs * (4 + 16 + 8) + n_pts * 24 + n_chunks * 54 * 8 + cam
+    if kernel == "schur_cam":
+        return n_obs * (4 + 8 + 4) + n_pts * (24 + 24 + 48) + n_chunks * 54 * 8 + cam
+    if kernel == "backsub":
+        return n_obs * (4 + 4 + 8) + n_pts * (24 + 48 + 24 + 24 + 24) + cam
+    if kernel == "cost":
+        return n_obs * (4 + 4 + 16) + n_pts * 24 + cam
+    return None
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """Counter-based HBM bytes per launch, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(sc, n_iters=3):
+    """The oracle as it stands (plain C, one thread) on the first LM
+    iterations of the same scene from the same start."""
+    import oracle
+    P = oracle.Problem.from_scene(sc)
+    t0 = time.perf_counter()
+    P.solve(n_iters)
+    dt = time.perf_counter() - t0
+    return {"value": n_iters / dt, "unit": "LM iterations/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_iters} LM iterations of the same scene "
+                      f"({len(sc['obs_cam'])} observations, PCG max {sc['pcg_max_iters']}), "
+                      f"single-threaded C oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="large")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from nonlinear_least_squares_amd import ba
+    from synthetic import ba_scene, scene_summary
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sc = ba_scene(args.config)
+    n_obs, n_pts, n_cams = len(sc["obs_cam"]), len(sc["points"]), len(sc["cams"])
+    print(f"# {scene_summary(sc)}", file=sys.stderr, flush=True)
+
+    # Warm-up on its own handle, every kernel timed, to find the dominant kernel.
+    warm = ba.Problem.from_scene(sc)
+    warm.profile()
+    warm.solve(max(args.warmup, 1))
+    prof = warm.profile_get()
+    warm.close()
+    dominant = max(prof, key=lambda k: prof[k][1])
+    print(f"# warm-up kernel totals (launches, ms): {prof}", file=sys.stderr, flush=True)
+
+    # Timed run: a fresh handle from the initial parameters, K LM iterations.
+    t0 = time.perf_counter()
+    P = ba.Problem.from_scene(sc)
+    torch.cuda.synchronize()
+    create_s = time.perf_counter() - t0
+    P.profile([dominant])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    summ = P.solve(args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    launches, kms = P.profile_get()[dominant]
+    n_chunks = sum(max(1, -(-int(c) // 1024)) for c in
+                   __import__("numpy").bincount(sc["obs_cam"], minlength=n_cams))
+    value = args.steps / dt
+
+    nbytes = algorithmic_bytes(dominant, n_obs, n_pts, n_cams, n_chunks)
+    roof = None
+    if nbytes and launches:
+        avg_s = kms / launches / 1e3
+        ach = nbytes / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant),
+                "kernel": dominant, "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches": launches, "algorithmic_bytes_per_launch": nbytes}
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "LM iterations/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * dt / args.steps, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config} BA: {n_cams} cameras, {n_pts} points, {n_obs} "
+                               f"observations, {sc['loss']} loss, PCG max {sc['pcg_max_iters']} "
+                               f"rel tol {sc['pcg_rel_tol']}",
+                   "n_obs": n_obs, "n_pts": n_pts, "n_cams": n_cams},
+        "obs_per_s": round(value * n_obs, 1),
+        "pcg_iters_per_lm_iter": round(summ["pcg_iters_total"] / args.steps, 2),
+        "accepted": summ["accepted"], "final_cost": summ["final_cost"],
+        "create_s": round(create_s, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(sc)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

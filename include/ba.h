@@ -1,0 +1,230 @@
+/* libba — one Levenberg-Marquardt iteration of large-scale bundle adjustment on
+ * an AMD Instinct MI355X (gfx950), fp64, behind a plain C ABI.
+ *
+ * The problem ("Bundle Adjustment in the Eager Mode" summary article: adjust
+ * cameras and 3-D points so that projected points line up with their image
+ * observations; every residual depends on exactly one camera and one point):
+ *
+ *   cameras   n_cams x 9 doubles, row-major: [w0 w1 w2 t0 t1 t2 f k1 k2]
+ *             w = axis-angle of the world-to-camera rotation R (P = R X + t),
+ *             f focal length in pixels, k1, k2 radial distortion on the
+ *             normalised coordinates; principal point 0.
+ *   points    n_pts x 3 doubles, row-major world coordinates.
+ *   obs       n_obs entries: obs_cam_idx[k] in [0, n_cams), obs_pt_idx[k] in
+ *             [0, n_pts), obs_uv[2k..2k+1] observed pixel.  Repeated
+ *             (camera, point) pairs are allowed (each is its own residual);
+ *             cameras or points with no observation are allowed.
+ *
+ *   residual  r_k = f (1 + k1 n + k2 n^2) p - uv_k,  p = P_xy / max(P_z, 1e-6),
+ *             n = |p|^2 (NeRF-SLAM reproduction notes, sec. 2.2: depth clamped
+ *             at 1e-6 before the division).
+ *   cost      C = sum_k rho(|r_k|): rho(e) = e^2/2, or Huber with threshold
+ *             delta (F^2SLAM article, sec. 5.3) applied to the 2-D norm.
+ *   step      Gauss-Newton normal equations H delta = -g with H = J^T W J,
+ *             g = J^T W r (NeRF-SLAM notes, sec. 3.1), Marquardt damping
+ *             H + lambda diag(max(diag H, floor)) ("Bundle Adjustment in the
+ *             Eager Mode": diagonal damping; Theseus note: LM with adaptive
+ *             damping), points eliminated by the Schur complement and the
+ *             reduced camera system (B - E C^-1 E^T) dc = -g_c + E C^-1 g_p
+ *             solved by block-Jacobi preconditioned conjugate gradients
+ *             without forming it (NeRF-SLAM notes, sec. 3.2, eqs. (1), (2);
+ *             "Bundle Adjustment in the Eager Mode": PCG for large problems),
+ *             point back-substitution dp = C^-1 (-g_p - E^T dc), retraction
+ *             R <- Exp(dphi) R and additive updates elsewhere (Theseus note,
+ *             retraction), accepted iff the cost strictly decreases.
+ *
+ * Conventions
+ *   - Every function returns BA_OK (0) or a negative BA_ERR_* code; nothing is
+ *     thrown across the ABI.  ba_status_string() gives a message; for
+ *     BA_ERR_DEVICE the last HIP error text is kept and appended.
+ *   - A handle owns all of its device memory (one arena sized once from
+ *     n_cams, n_pts, n_obs in ba_create); no LM call allocates.
+ *   - A handle is not thread-safe.  All device work is enqueued on
+ *     options.stream (a hipStream_t, NULL = the default stream).  Calls that
+ *     return host values synchronise that stream.
+ *   - Host output buffers are caller-owned.
+ */
+#ifndef LIBBA_BA_H
+#define LIBBA_BA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  BA_OK = 0,
+  BA_ERR_ARG = -1,        /* null pointer, size <= 0, index out of range, bad option  */
+  BA_ERR_NONFINITE = -2,  /* NaN/Inf in an input, or a non-finite cost                */
+  BA_ERR_NOT_SPD = -3,    /* a damped point block or camera block failed to factor   */
+  BA_ERR_DEVICE = -4,     /* HIP runtime error                                        */
+  BA_ERR_ALLOC = -5       /* device or pinned-host allocation failed                  */
+};
+
+enum { BA_MEM_HOST = 0, BA_MEM_DEVICE = 1 };
+enum { BA_LOSS_SQUARED = 0, BA_LOSS_HUBER = 1 };
+
+typedef struct {
+  int loss;              /* BA_LOSS_SQUARED or BA_LOSS_HUBER                     */
+  double huber_delta;    /* pixels (default 2.0)                                 */
+  double lambda0;        /* initial damping (1e-3)                               */
+  double lambda_up;      /* factor on a rejected step (10)                       */
+  double lambda_down;    /* divisor on an accepted step (10)                     */
+  double lambda_min;     /* 1e-16                                                */
+  double lambda_max;     /* 1e16                                                 */
+  double diag_floor;     /* floor on diag(J^T W J) in the damping term (1e-6)    */
+  int pcg_max_iters;     /* 50                                                   */
+  double pcg_rel_tol;    /* stop when |r|_2 <= tol |rhs|_2 (1e-6)                */
+  int mem;               /* BA_MEM_HOST / BA_MEM_DEVICE: where ba_create inputs
+                            and ba_set_params inputs live                       */
+  void* stream;          /* hipStream_t or NULL                                  */
+} ba_options;
+
+typedef struct {
+  double cost_before;    /* cost at the parameters the step started from       */
+  double cost_after;     /* cost at the trial parameters                        */
+  double lambda;         /* damping used for this step                          */
+  double pcg_rel_res;    /* |r|_2 / |rhs|_2 when PCG stopped                     */
+  int accepted;          /* 1 if the trial parameters were kept                 */
+  int pcg_iters;         /* PCG iterations run                                  */
+} ba_step_info;
+
+typedef struct {
+  double initial_cost, final_cost, lambda;
+  int iterations, accepted, pcg_iters_total;
+} ba_summary;
+
+typedef struct {
+  double lambda;         /* damping for the next step                           */
+  double cost;           /* cost at the current parameters                      */
+  int64_t iteration;     /* LM steps taken so far                               */
+} ba_state;
+
+typedef struct ba_problem ba_problem;
+
+/* Fills *o with the defaults listed above.  BA_ERR_ARG if o is NULL. */
+int ba_options_default(ba_options* o);
+
+/* Copies the inputs to the device (H2D, or D2D when opts->mem == BA_MEM_DEVICE),
+ * validates them on the device (index range, finiteness), sorts the
+ * observations by (point, camera, k) and by (camera, point, k) with a stable
+ * device radix sort (the sparsity pattern is fixed across iterations, the
+ * reason the eager-mode BA page caches its symbolic structure), builds the
+ * CSR offsets and work partitions, allocates the whole arena and evaluates
+ * the initial cost.  The caller may free its inputs when this returns.
+ * opts may be NULL (defaults).  On error *out is left NULL. */
+int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t n_pts,
+              const int32_t* obs_cam_idx, const int32_t* obs_pt_idx, const double* obs_uv,
+              int64_t n_obs, const ba_options* opts, ba_problem** out);
+
+/* One LM iteration: linearise (skipped when the previous step was rejected,
+ * the parameters being unchanged), damp, eliminate points, PCG, back-substitute,
+ * retract, evaluate the trial cost, accept iff it is strictly lower.  info may
+ * be NULL.  A rejected step is not an error. */
+int ba_lm_step(ba_problem* h, ba_step_info* info);
+
+/* Exactly n_iters LM iterations (no early exit).  s may be NULL. */
+int ba_solve(ba_problem* h, int n_iters, ba_summary* s);
+
+/* Cost at the current parameters, recomputed on the device. */
+int ba_cost(ba_problem* h, double* cost_out);
+
+/* Current parameters to caller-owned host buffers (n_cams x 9, n_pts x 3);
+ * either pointer may be NULL. */
+int ba_get_params(ba_problem* h, double* cams_out, double* points_out);
+
+/* Replaces the parameters (host or device pointers per options.mem; either may
+ * be NULL to keep that part), forces a re-linearisation, recomputes the cost. */
+int ba_set_params(ba_problem* h, const double* cams, const double* points);
+
+int ba_get_state(const ba_problem* h, ba_state* st);
+int ba_set_state(ba_problem* h, const ba_state* st);
+
+/* Sizes. */
+int ba_get_sizes(const ba_problem* h, int64_t* n_cams, int64_t* n_pts, int64_t* n_obs);
+
+/* ---- inspection entry points used by the parity tests ------------------- */
+
+enum {
+  BA_STAGE_LINEARIZE = 1,  /* residuals, Jacobians, B, g_c, C, g_p at the current parameters */
+  BA_STAGE_SCHUR = 2,      /* damping with the current lambda, C~^-1, v, rhs, S_jj, Cholesky */
+  BA_STAGE_PCG = 3,        /* camera step dc                                                  */
+  BA_STAGE_UPDATE = 4      /* dp, trial parameters, trial cost                                */
+};
+
+/* Runs the stages 1..upto of one LM iteration at the current parameters and
+ * lambda without taking the accept/reject decision. */
+int ba_debug_run(ba_problem* h, int upto);
+
+enum {
+  BA_DBG_PERM_PT = 0,   /* int32 n_obs: original index of the k-th observation in (pt, cam, k) order */
+  BA_DBG_PERM_CAM,      /* int32 n_obs: same for (cam, pt, k) order                                 */
+  BA_DBG_PT_PTR,        /* int32 n_pts + 1                                                          */
+  BA_DBG_CAM_PTR,       /* int32 n_cams + 1                                                         */
+  BA_DBG_R,             /* double n_obs x 2   residual, original observation order, current params */
+  BA_DBG_JC,            /* double n_obs x 18  camera Jacobian (row-major 2 x 9)                    */
+  BA_DBG_JP,            /* double n_obs x 6   point Jacobian (row-major 2 x 3)                     */
+  BA_DBG_W,             /* double n_obs       robust weight                                        */
+  BA_DBG_B,             /* double n_cams x 81                                                      */
+  BA_DBG_GC,            /* double n_cams x 9                                                       */
+  BA_DBG_C,             /* double n_pts x 9                                                        */
+  BA_DBG_GP,            /* double n_pts x 3                                                        */
+  BA_DBG_BD,            /* double n_cams x 81 damped B                                             */
+  BA_DBG_CINV,          /* double n_pts x 9   inverse of the damped point block                    */
+  BA_DBG_V,             /* double n_pts x 3                                                        */
+  BA_DBG_RHS,           /* double n_cams x 9                                                       */
+  BA_DBG_M,             /* double n_cams x 81 exact diagonal blocks S_jj                           */
+  BA_DBG_DC,            /* double n_cams x 9                                                       */
+  BA_DBG_DP,            /* double n_pts x 3                                                        */
+  BA_DBG_CAMS_TRIAL,    /* double n_cams x 9                                                       */
+  BA_DBG_PTS_TRIAL,     /* double n_pts x 3                                                        */
+  BA_DBG_PCG,           /* double 2: iterations, relative residual                                 */
+  BA_DBG_TRIAL_COST,    /* double 1                                                                */
+  BA_DBG_NUM
+};
+
+/* Byte size of one debug array (negative BA_ERR_ARG for a bad id). */
+int64_t ba_debug_size(const ba_problem* h, int which);
+
+/* Copies one array to caller-owned host memory; bytes must equal
+ * ba_debug_size(h, which). */
+int ba_debug_get(ba_problem* h, int which, void* host_out, int64_t bytes);
+
+/* ---- kernel timing for the benchmark ------------------------------------ */
+
+enum {
+  BA_K_LIN_PT = 0,   /* point-order linearisation, C and g_p                       */
+  BA_K_LIN_CAM,      /* camera-order linearisation, chunk partials of B and g_c    */
+  BA_K_DAMP_PT,      /* damped point blocks, their inverses, v                     */
+  BA_K_SCHUR_CAM,    /* camera-order E v and Ebar C~^-1 Ebar^T partials            */
+  BA_K_PRECOND,      /* per camera B~, rhs, S_jj and its Cholesky factor           */
+  BA_K_PCG_INIT,     /* PCG start: r = rhs, z = M^-1 r, p = z                      */
+  BA_K_PCG_PT,       /* PCG point pass: C~^-1 E^T p                                */
+  BA_K_PCG_CAM,      /* PCG camera pass: chunk partials of E C~^-1 E^T p            */
+  BA_K_PCG_Q,        /* PCG q = B~ p - E C~^-1 E^T p and p.q partials               */
+  BA_K_PCG_XR,       /* PCG update of x, r, z                                      */
+  BA_K_BACKSUB,      /* point back-substitution and trial points                   */
+  BA_K_RETRACT,      /* trial cameras                                              */
+  BA_K_COST,         /* trial cost                                                 */
+  BA_K_NUM
+};
+
+/* kernel_mask bit k set (k = BA_K_*): each launch of kernel k is bracketed by
+ * HIP events on the handle's stream and per-kernel totals accumulate until
+ * ba_profile_reset; 0 turns timing off.  PCG launches queued past the
+ * iteration at which the solve stopped exit at once and are not counted. */
+int ba_profile_enable(ba_problem* h, int kernel_mask);
+int ba_profile_reset(ba_problem* h);
+/* Launch count and summed duration (ms) of kernel `kernel` (BA_K_*). */
+int ba_profile_get(ba_problem* h, int kernel, int64_t* launches, double* total_ms);
+const char* ba_kernel_name(int kernel);
+
+void ba_destroy(ba_problem* h);
+const char* ba_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBBA_BA_H */

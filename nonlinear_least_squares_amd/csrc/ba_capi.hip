@@ -1,0 +1,935 @@
+// C ABI of libba: handle, device arena, structure build and the LM loop.
+// Declarations and argument documentation live in include/ba.h.
+#include <hip/hip_runtime.h>
+#include <hipcub/hipcub.hpp>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ba.h"
+#include "ba_kernels.h"
+
+using namespace ba;
+
+namespace {
+
+thread_local std::string g_err;
+
+#define HIPC(expr)                                                                   \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess) {                                                          \
+      g_err = std::string(#expr) + ": " + hipGetErrorString(e_);                     \
+      return BA_ERR_DEVICE;                                                          \
+    }                                                                                \
+  } while (0)
+
+#define CHECK_RC(expr)      \
+  do {                      \
+    int rc_ = (expr);       \
+    if (rc_ != BA_OK) return rc_; \
+  } while (0)
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+struct Arena {
+  char* base = nullptr;
+  size_t size = 0, used = 0;
+  std::vector<std::pair<void**, size_t>> plan;
+  template <class T>
+  void add(T*& p, int64_t count) {
+    plan.emplace_back(reinterpret_cast<void**>(&p), sizeof(T) * (size_t)std::max<int64_t>(count, 1));
+  }
+  int commit() {
+    size_t total = 0;
+    for (auto& e : plan) total += (e.second + 255) & ~size_t(255);
+    hipError_t err = hipMalloc(&base, total);
+    if (err != hipSuccess) {
+      base = nullptr;
+      return fail(BA_ERR_ALLOC, std::string("hipMalloc arena: ") + hipGetErrorString(err));
+    }
+    size = total;
+    size_t off = 0;
+    for (auto& e : plan) {
+      *e.first = base + off;
+      off += (e.second + 255) & ~size_t(255);
+    }
+    used = off;
+    plan.clear();
+    return BA_OK;
+  }
+};
+
+struct ProfRec {
+  int kernel;
+  int pcg_iter;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct ba_problem {
+  int64_t nc = 0, np = 0, nobs = 0;
+  ba_options opt{};
+  hipStream_t stream = nullptr;
+  int n_tiles = 0, n_chunks = 0, n_cost_blocks = 0;
+  Arena arena;   // everything sized by n_cams, n_pts, n_obs
+  Arena arena2;  // partitions and partial sums, sized after the CSR offsets
+  // parameters: [cur] current, [1 - cur] trial
+  double* cams[2] = {nullptr, nullptr};
+  double* pts[2] = {nullptr, nullptr};
+  CamT* tab[2] = {nullptr, nullptr};
+  int cur = 0;
+  // structure
+  int32_t *perm_pt = nullptr, *perm_cam = nullptr, *pt_ptr = nullptr, *cam_ptr = nullptr;
+  int32_t *o_cam = nullptr, *o_pt = nullptr, *c_pt = nullptr, *run_len = nullptr;
+  double *o_uv = nullptr, *c_uv = nullptr;
+  int32_t *tile_begin = nullptr, *chunk_begin = nullptr, *chunk_cam = nullptr,
+          *cam_chunk_ptr = nullptr;
+  // work arrays
+  double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
+         *gc = nullptr, *lin_part = nullptr;
+  double *Cinv = nullptr, *v = nullptr, *Bd = nullptr, *rhs = nullptr, *Mchol = nullptr,
+         *Mfull = nullptr, *schur_part = nullptr;
+  double *x = nullptr, *r = nullptr, *zc = nullptr, *pbuf = nullptr, *q = nullptr, *zp = nullptr,
+         *pcg_part = nullptr, *pq_cam = nullptr, *red_part = nullptr;
+  PcgState* pcg = nullptr;
+  double *dp = nullptr, *cost_part = nullptr;
+  StepOut* out = nullptr;
+  int* flags = nullptr;
+  StepOut* h_out = nullptr;  // pinned
+  int* h_done = nullptr;     // pinned, device-mapped: PCG stop flag
+  int* h_done_dev = nullptr;
+  int last_pcg_iters = 0;
+  hipEvent_t batch_ev[2] = {nullptr, nullptr};
+  // LM state
+  double lambda = 0.0, cost = 0.0;
+  int linearized = 0;
+  int64_t iteration = 0;
+  // timing
+  int prof_on = 0;
+  std::vector<ProfRec> prof_recs;
+  std::vector<hipEvent_t> prof_pool;
+  size_t prof_used = 0;
+  int64_t prof_count[BA_K_NUM] = {0};
+  double prof_ms[BA_K_NUM] = {0};
+};
+
+namespace {
+
+Dev make_dev(const ba_problem* h) {
+  Dev d{};
+  d.nc = h->nc;
+  d.np = h->np;
+  d.nobs = h->nobs;
+  d.n_tiles = h->n_tiles;
+  d.n_chunks = h->n_chunks;
+  d.n_cost_blocks = h->n_cost_blocks;
+  d.loss = h->opt.loss;
+  d.delta = h->opt.huber_delta;
+  d.diag_floor = h->opt.diag_floor;
+  d.lambda = h->lambda;
+  d.tol = h->opt.pcg_rel_tol;
+  const int c = h->cur, t = 1 - h->cur;
+  d.cams = h->cams[c];
+  d.pts = h->pts[c];
+  d.tab = h->tab[c];
+  d.cams_trial = h->cams[t];
+  d.pts_trial = h->pts[t];
+  d.tab_trial = h->tab[t];
+  d.o_cam = h->o_cam;
+  d.o_pt = h->o_pt;
+  d.o_uv = h->o_uv;
+  d.c_pt = h->c_pt;
+  d.c_uv = h->c_uv;
+  d.run_len = h->run_len;
+  d.pt_ptr = h->pt_ptr;
+  d.tile_begin = h->tile_begin;
+  d.chunk_begin = h->chunk_begin;
+  d.chunk_cam = h->chunk_cam;
+  d.cam_chunk_ptr = h->cam_chunk_ptr;
+  d.w_pt = h->w_pt;
+  d.w_cam = h->w_cam;
+  d.C = h->C;
+  d.gp = h->gp;
+  d.B = h->B;
+  d.gc = h->gc;
+  d.lin_part = h->lin_part;
+  d.Cinv = h->Cinv;
+  d.v = h->v;
+  d.Bd = h->Bd;
+  d.rhs = h->rhs;
+  d.Mchol = h->Mchol;
+  d.Mfull = h->Mfull;
+  d.schur_part = h->schur_part;
+  d.x = h->x;
+  d.r = h->r;
+  d.zc = h->zc;
+  d.pbuf = h->pbuf;
+  d.q = h->q;
+  d.zp = h->zp;
+  d.pcg_part = h->pcg_part;
+  d.pq_cam = h->pq_cam;
+  d.red_part = h->red_part;
+  d.red_nb = pcg_red_blocks(h->nc);
+  d.host_done = h->h_done_dev;
+  d.pcg = h->pcg;
+  d.dp = h->dp;
+  d.cost_part = h->cost_part;
+  d.out = h->out;
+  d.flags = h->flags;
+  return d;
+}
+
+// ---- kernel timing --------------------------------------------------------
+
+int prof_begin(ba_problem* h, int kernel, int pcg_iter, hipEvent_t* stop) {
+  *stop = nullptr;
+  if (!((h->prof_on >> kernel) & 1)) return BA_OK;
+  if (h->prof_used + 2 > h->prof_pool.size()) {
+    for (int i = 0; i < 64; ++i) {
+      hipEvent_t e;
+      HIPC(hipEventCreate(&e));
+      h->prof_pool.push_back(e);
+    }
+  }
+  hipEvent_t a = h->prof_pool[h->prof_used++], b = h->prof_pool[h->prof_used++];
+  HIPC(hipEventRecord(a, h->stream));
+  h->prof_recs.push_back({kernel, pcg_iter, a, b});
+  *stop = b;
+  return BA_OK;
+}
+
+int prof_end(ba_problem* h, hipEvent_t stop) {
+  if (stop) HIPC(hipEventRecord(stop, h->stream));
+  return BA_OK;
+}
+
+// After a synchronisation: fold the recorded pairs into the totals.  PCG
+// launches after convergence exit at once and are not counted.
+int prof_collect(ba_problem* h, int pcg_iters) {
+  for (auto& r : h->prof_recs) {
+    if (r.pcg_iter >= 0 && r.pcg_iter >= pcg_iters) continue;
+    float ms = 0.f;
+    HIPC(hipEventElapsedTime(&ms, r.a, r.b));
+    h->prof_ms[r.kernel] += ms;
+    h->prof_count[r.kernel] += 1;
+  }
+  h->prof_recs.clear();
+  h->prof_used = 0;
+  return BA_OK;
+}
+
+#define TIMED(kid, it, call)                   \
+  do {                                         \
+    hipEvent_t stop_;                          \
+    CHECK_RC(prof_begin(h, (kid), (it), &stop_)); \
+    call;                                      \
+    CHECK_RC(prof_end(h, stop_));              \
+  } while (0)
+
+// ---- pieces of one LM iteration -------------------------------------------
+
+int stage_linearize(ba_problem* h) {
+  Dev d = make_dev(h);
+  TIMED(BA_K_LIN_PT, -1, launch_lin_pt(d, h->stream));
+  TIMED(BA_K_LIN_CAM, -1, launch_lin_cam(d, h->stream));
+  launch_lin_final(d, h->stream);
+  HIPC(hipGetLastError());
+  return BA_OK;
+}
+
+int stage_schur(ba_problem* h) {
+  Dev d = make_dev(h);
+  HIPC(hipMemsetAsync(h->flags, 0, 2 * sizeof(int), h->stream));
+  TIMED(BA_K_DAMP_PT, -1, launch_damp_pt(d, h->stream));
+  TIMED(BA_K_SCHUR_CAM, -1, launch_schur_cam(d, h->stream));
+  TIMED(BA_K_PRECOND, -1, launch_precond(d, h->stream));
+  HIPC(hipGetLastError());
+  return BA_OK;
+}
+
+// PCG iterations are queued in batches.  The first batch is as long as the
+// previous solve took (the iteration count changes slowly across LM steps),
+// later ones two iterations long, always one batch ahead of the batch whose
+// completion the host waits for; the kernels raise a host-mapped flag when
+// the solve stops and every launch after that exits at once.
+int stage_pcg(ba_problem* h) {
+  Dev d = make_dev(h);
+  const int maxit = h->opt.pcg_max_iters;
+  *h->h_done = 0;
+  TIMED(BA_K_PCG_INIT, -1, launch_pcg_init(d, h->stream));
+  int next_it = 0;
+  auto enqueue = [&](int n) -> int {
+    for (int k = 0; k < n; ++k, ++next_it) {
+      TIMED(BA_K_PCG_PT, next_it, launch_pcg_pt(d, next_it, h->stream));
+      TIMED(BA_K_PCG_CAM, next_it, launch_pcg_cam(d, h->stream));
+      TIMED(BA_K_PCG_Q, next_it, launch_pcg_q(d, next_it, h->stream));
+      TIMED(BA_K_PCG_XR, next_it, launch_pcg_xr(d, next_it, h->stream));
+    }
+    return BA_OK;
+  };
+  int launched = std::min(maxit, std::max(1, h->last_pcg_iters - 1));
+  if (maxit > 0) {
+    CHECK_RC(enqueue(launched));
+    HIPC(hipEventRecord(h->batch_ev[0], h->stream));
+    int cur = 0;
+    while (launched < maxit) {
+      const int n = std::min(2, maxit - launched);
+      CHECK_RC(enqueue(n));
+      launched += n;
+      HIPC(hipEventRecord(h->batch_ev[1 - cur], h->stream));
+      HIPC(hipEventSynchronize(h->batch_ev[cur]));
+      if (__atomic_load_n(h->h_done, __ATOMIC_ACQUIRE)) break;
+      cur = 1 - cur;
+    }
+  }
+  launch_pcg_final(d, next_it, h->stream);
+  HIPC(hipGetLastError());
+  return BA_OK;
+}
+
+int stage_update(ba_problem* h) {
+  Dev d = make_dev(h);
+  TIMED(BA_K_BACKSUB, -1, launch_backsub(d, h->stream));
+  TIMED(BA_K_RETRACT, -1, launch_retract(d, h->stream));
+  TIMED(BA_K_COST, -1, launch_cost(d, d.cams_trial, d.pts_trial, d.tab_trial, h->stream));
+  HIPC(hipGetLastError());
+  return BA_OK;
+}
+
+int read_out(ba_problem* h) {
+  HIPC(hipMemcpyAsync(h->h_out, h->out, sizeof(StepOut), hipMemcpyDeviceToHost, h->stream));
+  HIPC(hipStreamSynchronize(h->stream));
+  return BA_OK;
+}
+
+int current_cost(ba_problem* h, double* c) {
+  Dev d = make_dev(h);
+  launch_cost(d, d.cams, d.pts, d.tab, h->stream);
+  HIPC(hipGetLastError());
+  CHECK_RC(read_out(h));
+  *c = h->h_out->trial_cost;
+  return BA_OK;
+}
+
+int lm_step(ba_problem* h, ba_step_info* info) {
+  if (!h->linearized) CHECK_RC(stage_linearize(h));
+  CHECK_RC(stage_schur(h));
+  h->linearized = 1;
+  CHECK_RC(stage_pcg(h));
+  CHECK_RC(stage_update(h));
+  CHECK_RC(read_out(h));
+  const StepOut o = *h->h_out;
+  h->last_pcg_iters = o.pcg_iters;
+  if (h->prof_on) CHECK_RC(prof_collect(h, o.pcg_iters));
+  if (o.not_spd) return fail(BA_ERR_NOT_SPD, "a damped block is not positive definite");
+  ba_step_info inf{};
+  inf.cost_before = h->cost;
+  inf.cost_after = o.trial_cost;
+  inf.lambda = h->lambda;
+  inf.pcg_iters = o.pcg_iters;
+  inf.pcg_rel_res = o.pcg_rel_res;
+  if (std::isfinite(o.trial_cost) && o.trial_cost < h->cost) {
+    inf.accepted = 1;
+    h->cur = 1 - h->cur;
+    h->cost = o.trial_cost;
+    h->linearized = 0;
+    h->lambda = std::max(h->lambda / h->opt.lambda_down, h->opt.lambda_min);
+  } else {
+    inf.accepted = 0;
+    h->lambda = std::min(h->lambda * h->opt.lambda_up, h->opt.lambda_max);
+  }
+  h->iteration += 1;
+  if (info) *info = inf;
+  return BA_OK;
+}
+
+// ---- structure build --------------------------------------------------------
+
+int sort_pairs(const int32_t* major, const int32_t* minor, int64_t n_major, int64_t n_minor,
+               int64_t n, int32_t* perm_out, hipStream_t s) {
+  uint64_t *k_in = nullptr, *k_out = nullptr;
+  int32_t* v_in = nullptr;
+  void* tmp = nullptr;
+  size_t tmp_bytes = 0;
+  int end_bit = 1;
+  const unsigned long long maxkey = (unsigned long long)n_major * (unsigned long long)n_minor;
+  while (end_bit < 64 && (1ull << end_bit) < maxkey) ++end_bit;
+  auto cleanup = [&]() {
+    (void)hipFree(k_in);
+    (void)hipFree(k_out);
+    (void)hipFree(v_in);
+    (void)hipFree(tmp);
+  };
+  if (hipMalloc(&k_in, sizeof(uint64_t) * n) != hipSuccess ||
+      hipMalloc(&k_out, sizeof(uint64_t) * n) != hipSuccess ||
+      hipMalloc(&v_in, sizeof(int32_t) * n) != hipSuccess) {
+    cleanup();
+    return fail(BA_ERR_ALLOC, "hipMalloc sort buffers");
+  }
+  launch_make_keys(major, minor, n_minor, n, k_in, v_in, s);
+  hipError_t e = hipcub::DeviceRadixSort::SortPairs(nullptr, tmp_bytes, k_in, k_out, v_in, perm_out,
+                                                   (int)n, 0, end_bit, s);
+  if (e == hipSuccess) e = hipMalloc(&tmp, std::max<size_t>(tmp_bytes, 1));
+  if (e == hipSuccess)
+    e = hipcub::DeviceRadixSort::SortPairs(tmp, tmp_bytes, k_in, k_out, v_in, perm_out, (int)n, 0,
+                                           end_bit, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  cleanup();
+  if (e != hipSuccess) return fail(BA_ERR_DEVICE, std::string("radix sort: ") + hipGetErrorString(e));
+  return BA_OK;
+}
+
+int build(ba_problem* h, const double* cams_in, const double* pts_in, const int32_t* cam_in,
+          const int32_t* pt_in, const double* uv_in) {
+  const int64_t nc = h->nc, np = h->np, N = h->nobs;
+  const hipStream_t s = h->stream;
+  const hipMemcpyKind kind =
+      h->opt.mem == BA_MEM_DEVICE ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+
+  // Raw inputs on the device (temporary).
+  int32_t *d_cam = nullptr, *d_pt = nullptr, *d_ccam = nullptr;
+  double* d_uv = nullptr;
+  int* d_flags = nullptr;
+  auto tmp_free = [&]() {
+    (void)hipFree(d_cam);
+    (void)hipFree(d_pt);
+    (void)hipFree(d_uv);
+    (void)hipFree(d_flags);
+    (void)hipFree(d_ccam);
+  };
+  const int64_t Na = std::max<int64_t>(N, 1);
+  if (hipMalloc(&d_cam, sizeof(int32_t) * Na) != hipSuccess ||
+      hipMalloc(&d_pt, sizeof(int32_t) * Na) != hipSuccess ||
+      hipMalloc(&d_uv, sizeof(double) * 2 * Na) != hipSuccess ||
+      hipMalloc(&d_ccam, sizeof(int32_t) * Na) != hipSuccess ||
+      hipMalloc(&d_flags, sizeof(int) * 2) != hipSuccess) {
+    tmp_free();
+    return fail(BA_ERR_ALLOC, "hipMalloc input staging");
+  }
+
+  // Persistent arena.
+  Arena& A = h->arena;
+  for (int b = 0; b < 2; ++b) {
+    A.add(h->cams[b], 9 * nc);
+    A.add(h->pts[b], 3 * np);
+    A.add(h->tab[b], nc);
+  }
+  A.add(h->perm_pt, N);
+  A.add(h->perm_cam, N);
+  A.add(h->pt_ptr, np + 1);
+  A.add(h->cam_ptr, nc + 1);
+  A.add(h->o_cam, N);
+  A.add(h->o_pt, N);
+  A.add(h->o_uv, 2 * N);
+  A.add(h->c_pt, N);
+  A.add(h->c_uv, 2 * N);
+  A.add(h->run_len, N);
+  A.add(h->w_pt, N);
+  A.add(h->w_cam, N);
+  A.add(h->C, 6 * np);
+  A.add(h->gp, 3 * np);
+  A.add(h->Cinv, 6 * np);
+  A.add(h->v, 3 * np);
+  A.add(h->zp, 3 * np);
+  A.add(h->dp, 3 * np);
+  A.add(h->B, 45 * nc);
+  A.add(h->gc, 9 * nc);
+  A.add(h->Bd, 45 * nc);
+  A.add(h->rhs, 9 * nc);
+  A.add(h->Mchol, 45 * nc);
+  A.add(h->Mfull, 45 * nc);
+  A.add(h->x, 9 * nc);
+  A.add(h->r, 9 * nc);
+  A.add(h->zc, 9 * nc);
+  A.add(h->pbuf, 18 * nc);
+  A.add(h->q, 9 * nc);
+  A.add(h->pcg, 1);
+  A.add(h->pq_cam, nc);
+  A.add(h->out, 1);
+  A.add(h->flags, 2);
+  A.add(h->cam_chunk_ptr, nc + 1);
+
+  // Partitions need the CSR offsets first, so they get a second small arena
+  // piece below; everything above is committed now.
+  int rc = A.commit();
+  if (rc != BA_OK) {
+    tmp_free();
+    return rc;
+  }
+  if (hipMemsetAsync(A.base, 0, A.size, s) != hipSuccess) {
+    tmp_free();
+    return fail(BA_ERR_DEVICE, "arena clear");
+  }
+
+  hipError_t e = hipSuccess;
+#define TRY(x)                                                         \
+  do {                                                                 \
+    e = (x);                                                           \
+    if (e != hipSuccess) {                                             \
+      tmp_free();                                                      \
+      return fail(BA_ERR_DEVICE, std::string(#x) + ": " + hipGetErrorString(e)); \
+    }                                                                  \
+  } while (0)
+  TRY(hipMemcpyAsync(h->cams[0], cams_in, sizeof(double) * 9 * nc, kind, s));
+  TRY(hipMemcpyAsync(h->pts[0], pts_in, sizeof(double) * 3 * np, kind, s));
+  if (N > 0) {
+    TRY(hipMemcpyAsync(d_cam, cam_in, sizeof(int32_t) * N, kind, s));
+    TRY(hipMemcpyAsync(d_pt, pt_in, sizeof(int32_t) * N, kind, s));
+    TRY(hipMemcpyAsync(d_uv, uv_in, sizeof(double) * 2 * N, kind, s));
+  }
+  TRY(hipMemsetAsync(d_flags, 0, sizeof(int) * 2, s));
+  launch_validate(d_cam, d_pt, d_uv, N, h->cams[0], nc, h->pts[0], np, d_flags, s);
+  int flags[2] = {0, 0};
+  TRY(hipMemcpyAsync(flags, d_flags, sizeof(flags), hipMemcpyDeviceToHost, s));
+  TRY(hipStreamSynchronize(s));
+  if (flags[0]) {
+    tmp_free();
+    return fail(BA_ERR_ARG, "observation index out of range");
+  }
+  if (flags[1]) {
+    tmp_free();
+    return fail(BA_ERR_NONFINITE, "non-finite camera, point or observation");
+  }
+
+  if (N > 0) {
+    rc = sort_pairs(d_pt, d_cam, np, nc, N, h->perm_pt, s);
+    if (rc == BA_OK) rc = sort_pairs(d_cam, d_pt, nc, np, N, h->perm_cam, s);
+    if (rc != BA_OK) {
+      tmp_free();
+      return rc;
+    }
+    launch_gather_obs(h->perm_pt, d_cam, d_pt, d_uv, N, h->o_cam, h->o_pt, h->o_uv, s);
+    launch_gather_obs(h->perm_cam, d_cam, d_pt, d_uv, N, d_ccam, h->c_pt, h->c_uv, s);
+    launch_run_len(d_ccam, h->c_pt, N, h->run_len, s);
+  }
+  launch_seg_ptr(h->o_pt, N, np, h->pt_ptr, s);
+  launch_seg_ptr(d_ccam, N, nc, h->cam_ptr, s);
+  TRY(hipGetLastError());
+
+  std::vector<int32_t> pt_ptr(np + 1), cam_ptr(nc + 1);
+  TRY(hipMemcpyAsync(pt_ptr.data(), h->pt_ptr, sizeof(int32_t) * (np + 1), hipMemcpyDeviceToHost, s));
+  TRY(hipMemcpyAsync(cam_ptr.data(), h->cam_ptr, sizeof(int32_t) * (nc + 1), hipMemcpyDeviceToHost, s));
+  TRY(hipStreamSynchronize(s));
+  tmp_free();
+  d_cam = d_pt = d_ccam = nullptr;
+  d_uv = nullptr;
+  d_flags = nullptr;
+
+  // Point tiles: whole points, at most kTile observations unless one point is longer.
+  std::vector<int32_t> tiles{0};
+  int32_t start = 0;
+  for (int64_t i = 0; i < np; ++i) {
+    if (pt_ptr[i + 1] - start > kTile && pt_ptr[i] > start) {
+      tiles.push_back(pt_ptr[i]);
+      start = pt_ptr[i];
+    }
+  }
+  if (N > start) tiles.push_back((int32_t)N);
+  // Camera chunks: every camera gets ceil(len / kChunk) >= 1 equal pieces.
+  std::vector<int32_t> chunk_begin, chunk_cam, cam_chunk_ptr(nc + 1, 0);
+  for (int64_t j = 0; j < nc; ++j) {
+    const int64_t len = cam_ptr[j + 1] - cam_ptr[j];
+    const int64_t nch = std::max<int64_t>(1, (len + kChunk - 1) / kChunk);
+    for (int64_t c = 0; c < nch; ++c) {
+      chunk_begin.push_back((int32_t)(cam_ptr[j] + (len * c) / nch));
+      chunk_cam.push_back((int32_t)j);
+    }
+    cam_chunk_ptr[j + 1] = (int32_t)chunk_begin.size();
+  }
+  chunk_begin.push_back((int32_t)N);
+  h->n_tiles = (int)tiles.size() - 1;
+  h->n_chunks = (int)chunk_cam.size();
+  h->n_cost_blocks = (int)((N + kCostBlock - 1) / kCostBlock);
+
+  Arena& P = h->arena2;
+  P.add(h->tile_begin, (int64_t)tiles.size());
+  P.add(h->chunk_begin, (int64_t)chunk_begin.size());
+  P.add(h->chunk_cam, (int64_t)chunk_cam.size());
+  P.add(h->lin_part, (int64_t)h->n_chunks * kLinCamVals);
+  P.add(h->schur_part, (int64_t)h->n_chunks * kSchurVals);
+  P.add(h->pcg_part, (int64_t)h->n_chunks * 9);
+  P.add(h->cost_part, (int64_t)std::max(h->n_cost_blocks, 1));
+  P.add(h->red_part, 6 * (int64_t)pcg_red_blocks(nc));
+  rc = P.commit();
+  if (rc != BA_OK) return rc;
+  TRY(hipMemsetAsync(P.base, 0, P.size, s));
+  TRY(hipMemcpyAsync(h->tile_begin, tiles.data(), sizeof(int32_t) * tiles.size(),
+                     hipMemcpyHostToDevice, s));
+  TRY(hipMemcpyAsync(h->chunk_begin, chunk_begin.data(), sizeof(int32_t) * chunk_begin.size(),
+                     hipMemcpyHostToDevice, s));
+  TRY(hipMemcpyAsync(h->chunk_cam, chunk_cam.data(), sizeof(int32_t) * chunk_cam.size(),
+                     hipMemcpyHostToDevice, s));
+  TRY(hipMemcpyAsync(h->cam_chunk_ptr, cam_chunk_ptr.data(), sizeof(int32_t) * (nc + 1),
+                     hipMemcpyHostToDevice, s));
+  TRY(hipStreamSynchronize(s));
+#undef TRY
+  return BA_OK;
+}
+
+}  // namespace
+
+// ============================================================== C ABI ====
+
+namespace {
+
+int check_options(const ba_options& o) {
+  if (o.loss != BA_LOSS_SQUARED && o.loss != BA_LOSS_HUBER) return fail(BA_ERR_ARG, "bad loss");
+  if (!(o.huber_delta > 0.0)) return fail(BA_ERR_ARG, "huber_delta must be > 0");
+  if (!(o.lambda0 >= 0.0) || !(o.lambda_up >= 1.0) || !(o.lambda_down >= 1.0) ||
+      !(o.lambda_min >= 0.0) || !(o.lambda_max >= o.lambda_min))
+    return fail(BA_ERR_ARG, "bad damping schedule");
+  if (!(o.diag_floor >= 0.0)) return fail(BA_ERR_ARG, "diag_floor must be >= 0");
+  if (o.pcg_max_iters < 0 || !(o.pcg_rel_tol >= 0.0)) return fail(BA_ERR_ARG, "bad PCG options");
+  if (o.mem != BA_MEM_HOST && o.mem != BA_MEM_DEVICE) return fail(BA_ERR_ARG, "bad mem");
+  return BA_OK;
+}
+
+void expand_sym(const double* packed, int n, int64_t count, double* full) {
+  for (int64_t b = 0; b < count; ++b) {
+    const double* p = packed + b * (n * (n + 1) / 2);
+    double* f = full + b * n * n;
+    for (int i = 0; i < n; ++i)
+      for (int j = i; j < n; ++j) f[i * n + j] = f[j * n + i] = p[sym_idx(n, i, j)];
+  }
+}
+
+int d2h(ba_problem* h, void* dst, const void* src, size_t bytes) {
+  if (bytes) HIPC(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, h->stream));
+  HIPC(hipStreamSynchronize(h->stream));
+  return BA_OK;
+}
+
+const char* kKernelNames[BA_K_NUM] = {"lin_pt",   "lin_cam", "damp_pt", "schur_cam",
+                                      "precond",  "pcg_init", "pcg_pt", "pcg_cam",
+                                      "pcg_q",    "pcg_xr",  "backsub", "retract",
+                                      "cost"};
+
+}  // namespace
+
+extern "C" {
+
+int ba_options_default(ba_options* o) {
+  if (!o) return BA_ERR_ARG;
+  o->loss = BA_LOSS_SQUARED;
+  o->huber_delta = 2.0;
+  o->lambda0 = 1e-3;
+  o->lambda_up = 10.0;
+  o->lambda_down = 10.0;
+  o->lambda_min = 1e-16;
+  o->lambda_max = 1e16;
+  o->diag_floor = 1e-6;
+  o->pcg_max_iters = 50;
+  o->pcg_rel_tol = 1e-6;
+  o->mem = BA_MEM_HOST;
+  o->stream = nullptr;
+  return BA_OK;
+}
+
+void ba_destroy(ba_problem* h) {
+  if (!h) return;
+  if (h->stream) (void)hipStreamSynchronize(h->stream);
+  else (void)hipDeviceSynchronize();
+  (void)hipFree(h->arena.base);
+  (void)hipFree(h->arena2.base);
+  if (h->h_out) (void)hipHostFree(h->h_out);
+  if (h->h_done) (void)hipHostFree(h->h_done);
+  for (hipEvent_t e : h->batch_ev)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
+  delete h;
+}
+
+int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t n_pts,
+              const int32_t* obs_cam_idx, const int32_t* obs_pt_idx, const double* obs_uv,
+              int64_t n_obs, const ba_options* opts, ba_problem** out) {
+  if (!out) return fail(BA_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!cams || !points || n_cams <= 0 || n_pts <= 0 || n_obs < 0)
+    return fail(BA_ERR_ARG, "null parameters or non-positive sizes");
+  if (n_obs > 0 && (!obs_cam_idx || !obs_pt_idx || !obs_uv))
+    return fail(BA_ERR_ARG, "null observation arrays");
+  if (n_obs >= (int64_t)INT32_MAX || n_cams >= (int64_t)INT32_MAX || n_pts >= (int64_t)INT32_MAX)
+    return fail(BA_ERR_ARG, "sizes must be below 2^31 - 1");
+  ba_problem* h = new ba_problem();
+  if (opts) h->opt = *opts;
+  else ba_options_default(&h->opt);
+  int rc = check_options(h->opt);
+  if (rc != BA_OK) {
+    delete h;
+    return rc;
+  }
+  h->stream = reinterpret_cast<hipStream_t>(h->opt.stream);
+  h->nc = n_cams;
+  h->np = n_pts;
+  h->nobs = n_obs;
+  if (hipHostMalloc(reinterpret_cast<void**>(&h->h_out), sizeof(StepOut), hipHostMallocDefault) !=
+      hipSuccess) {
+    h->h_out = nullptr;
+    ba_destroy(h);
+    return fail(BA_ERR_ALLOC, "hipHostMalloc");
+  }
+  if (hipHostMalloc(reinterpret_cast<void**>(&h->h_done), sizeof(int), hipHostMallocMapped) !=
+          hipSuccess ||
+      hipHostGetDevicePointer(reinterpret_cast<void**>(&h->h_done_dev), h->h_done, 0) !=
+          hipSuccess ||
+      hipEventCreateWithFlags(&h->batch_ev[0], hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->batch_ev[1], hipEventDisableTiming) != hipSuccess) {
+    ba_destroy(h);
+    return fail(BA_ERR_ALLOC, "pinned flag or events");
+  }
+  *h->h_done = 0;
+  rc = build(h, cams, points, obs_cam_idx, obs_pt_idx, obs_uv);
+  if (rc != BA_OK) {
+    ba_destroy(h);
+    return rc;
+  }
+  h->cur = 0;
+  h->lambda = h->opt.lambda0;
+  h->linearized = 0;
+  h->iteration = 0;
+  launch_cam_prep(h->cams[0], h->tab[0], h->nc, h->stream);
+  double c = 0.0;
+  rc = current_cost(h, &c);
+  if (rc == BA_OK && !std::isfinite(c)) rc = fail(BA_ERR_NONFINITE, "initial cost is not finite");
+  if (rc != BA_OK) {
+    ba_destroy(h);
+    return rc;
+  }
+  h->cost = c;
+  *out = h;
+  return BA_OK;
+}
+
+int ba_lm_step(ba_problem* h, ba_step_info* info) {
+  if (!h) return fail(BA_ERR_ARG, "null handle");
+  return lm_step(h, info);
+}
+
+int ba_solve(ba_problem* h, int n_iters, ba_summary* s) {
+  if (!h || n_iters < 0) return fail(BA_ERR_ARG, "bad arguments");
+  ba_summary sum{};
+  sum.initial_cost = h->cost;
+  for (int it = 0; it < n_iters; ++it) {
+    ba_step_info inf;
+    int rc = lm_step(h, &inf);
+    if (rc != BA_OK) return rc;
+    sum.accepted += inf.accepted;
+    sum.pcg_iters_total += inf.pcg_iters;
+  }
+  sum.iterations = n_iters;
+  sum.final_cost = h->cost;
+  sum.lambda = h->lambda;
+  if (s) *s = sum;
+  return BA_OK;
+}
+
+int ba_cost(ba_problem* h, double* cost_out) {
+  if (!h || !cost_out) return fail(BA_ERR_ARG, "bad arguments");
+  return current_cost(h, cost_out);
+}
+
+int ba_get_params(ba_problem* h, double* cams_out, double* points_out) {
+  if (!h) return fail(BA_ERR_ARG, "null handle");
+  if (cams_out) HIPC(hipMemcpyAsync(cams_out, h->cams[h->cur], sizeof(double) * 9 * h->nc,
+                                    hipMemcpyDeviceToHost, h->stream));
+  if (points_out) HIPC(hipMemcpyAsync(points_out, h->pts[h->cur], sizeof(double) * 3 * h->np,
+                                      hipMemcpyDeviceToHost, h->stream));
+  HIPC(hipStreamSynchronize(h->stream));
+  return BA_OK;
+}
+
+int ba_set_params(ba_problem* h, const double* cams, const double* points) {
+  if (!h) return fail(BA_ERR_ARG, "null handle");
+  const hipMemcpyKind kind =
+      h->opt.mem == BA_MEM_DEVICE ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  if (cams) HIPC(hipMemcpyAsync(h->cams[h->cur], cams, sizeof(double) * 9 * h->nc, kind, h->stream));
+  if (points)
+    HIPC(hipMemcpyAsync(h->pts[h->cur], points, sizeof(double) * 3 * h->np, kind, h->stream));
+  HIPC(hipMemsetAsync(h->flags, 0, 2 * sizeof(int), h->stream));
+  launch_validate(nullptr, nullptr, nullptr, 0, h->cams[h->cur], h->nc, h->pts[h->cur], h->np,
+                  h->flags, h->stream);
+  int flags[2] = {0, 0};
+  HIPC(hipMemcpyAsync(flags, h->flags, sizeof(flags), hipMemcpyDeviceToHost, h->stream));
+  HIPC(hipStreamSynchronize(h->stream));
+  if (flags[1]) return fail(BA_ERR_NONFINITE, "non-finite parameters");
+  launch_cam_prep(h->cams[h->cur], h->tab[h->cur], h->nc, h->stream);
+  double c = 0.0;
+  CHECK_RC(current_cost(h, &c));
+  if (!std::isfinite(c)) return fail(BA_ERR_NONFINITE, "cost is not finite");
+  h->cost = c;
+  h->linearized = 0;
+  return BA_OK;
+}
+
+int ba_get_state(const ba_problem* h, ba_state* st) {
+  if (!h || !st) return fail(BA_ERR_ARG, "bad arguments");
+  st->lambda = h->lambda;
+  st->cost = h->cost;
+  st->iteration = h->iteration;
+  return BA_OK;
+}
+
+int ba_set_state(ba_problem* h, const ba_state* st) {
+  if (!h || !st || !(st->lambda >= 0.0)) return fail(BA_ERR_ARG, "bad arguments");
+  h->lambda = st->lambda;    // the cost always follows the parameters; st->cost is ignored
+  h->iteration = st->iteration;
+  return BA_OK;
+}
+
+int ba_get_sizes(const ba_problem* h, int64_t* n_cams, int64_t* n_pts, int64_t* n_obs) {
+  if (!h) return fail(BA_ERR_ARG, "null handle");
+  if (n_cams) *n_cams = h->nc;
+  if (n_pts) *n_pts = h->np;
+  if (n_obs) *n_obs = h->nobs;
+  return BA_OK;
+}
+
+int ba_debug_run(ba_problem* h, int upto) {
+  if (!h || upto < BA_STAGE_LINEARIZE || upto > BA_STAGE_UPDATE)
+    return fail(BA_ERR_ARG, "bad arguments");
+  CHECK_RC(stage_linearize(h));
+  h->linearized = 1;
+  if (upto >= BA_STAGE_SCHUR) CHECK_RC(stage_schur(h));
+  if (upto >= BA_STAGE_PCG) CHECK_RC(stage_pcg(h));
+  if (upto >= BA_STAGE_UPDATE) CHECK_RC(stage_update(h));
+  CHECK_RC(read_out(h));
+  if (h->prof_on) CHECK_RC(prof_collect(h, h->h_out->pcg_iters));
+  return BA_OK;
+}
+
+int64_t ba_debug_size(const ba_problem* h, int which) {
+  if (!h) return BA_ERR_ARG;
+  const int64_t nc = h->nc, np = h->np, N = h->nobs, i4 = 4, d8 = 8;
+  switch (which) {
+    case BA_DBG_PERM_PT: case BA_DBG_PERM_CAM: return N * i4;
+    case BA_DBG_PT_PTR: return (np + 1) * i4;
+    case BA_DBG_CAM_PTR: return (nc + 1) * i4;
+    case BA_DBG_R: return 2 * N * d8;
+    case BA_DBG_JC: return 18 * N * d8;
+    case BA_DBG_JP: return 6 * N * d8;
+    case BA_DBG_W: return N * d8;
+    case BA_DBG_B: case BA_DBG_BD: case BA_DBG_M: return 81 * nc * d8;
+    case BA_DBG_GC: case BA_DBG_RHS: case BA_DBG_DC: case BA_DBG_CAMS_TRIAL: return 9 * nc * d8;
+    case BA_DBG_C: case BA_DBG_CINV: return 9 * np * d8;
+    case BA_DBG_GP: case BA_DBG_V: case BA_DBG_DP: case BA_DBG_PTS_TRIAL: return 3 * np * d8;
+    case BA_DBG_PCG: return 2 * d8;
+    case BA_DBG_TRIAL_COST: return d8;
+    default: return BA_ERR_ARG;
+  }
+}
+
+int ba_debug_get(ba_problem* h, int which, void* host_out, int64_t bytes) {
+  if (!h || !host_out) return fail(BA_ERR_ARG, "bad arguments");
+  const int64_t need = ba_debug_size(h, which);
+  if (need < 0 || bytes != need) return fail(BA_ERR_ARG, "bad array id or byte count");
+  const int64_t nc = h->nc, np = h->np, N = h->nobs;
+  const int t = 1 - h->cur;
+  switch (which) {
+    case BA_DBG_PERM_PT: return d2h(h, host_out, h->perm_pt, bytes);
+    case BA_DBG_PERM_CAM: return d2h(h, host_out, h->perm_cam, bytes);
+    case BA_DBG_PT_PTR: return d2h(h, host_out, h->pt_ptr, bytes);
+    case BA_DBG_CAM_PTR: return d2h(h, host_out, h->cam_ptr, bytes);
+    case BA_DBG_R: case BA_DBG_JC: case BA_DBG_JP: case BA_DBG_W: {
+      if (N == 0) return BA_OK;
+      double* buf = nullptr;
+      HIPC(hipMalloc(&buf, sizeof(double) * 27 * N));
+      Dev d = make_dev(h);
+      launch_debug_obs(d, h->perm_pt, buf, buf + 2 * N, buf + 20 * N, buf + 26 * N, h->stream);
+      const size_t off = which == BA_DBG_R ? 0 : which == BA_DBG_JC ? 2 * N : which == BA_DBG_JP ? 20 * N : 26 * N;
+      int rc = d2h(h, host_out, buf + off, bytes);
+      (void)hipFree(buf);
+      return rc;
+    }
+    case BA_DBG_GC: return d2h(h, host_out, h->gc, bytes);
+    case BA_DBG_GP: return d2h(h, host_out, h->gp, bytes);
+    case BA_DBG_V: return d2h(h, host_out, h->v, bytes);
+    case BA_DBG_RHS: return d2h(h, host_out, h->rhs, bytes);
+    case BA_DBG_DC: return d2h(h, host_out, h->x, bytes);
+    case BA_DBG_DP: return d2h(h, host_out, h->dp, bytes);
+    case BA_DBG_CAMS_TRIAL: return d2h(h, host_out, h->cams[t], bytes);
+    case BA_DBG_PTS_TRIAL: return d2h(h, host_out, h->pts[t], bytes);
+    case BA_DBG_B: case BA_DBG_BD: case BA_DBG_M: {
+      std::vector<double> packed(45 * nc);
+      const double* src = which == BA_DBG_B ? h->B : which == BA_DBG_BD ? h->Bd : h->Mfull;
+      CHECK_RC(d2h(h, packed.data(), src, sizeof(double) * packed.size()));
+      expand_sym(packed.data(), 9, nc, static_cast<double*>(host_out));
+      return BA_OK;
+    }
+    case BA_DBG_C: case BA_DBG_CINV: {
+      std::vector<double> packed(6 * np);
+      CHECK_RC(d2h(h, packed.data(), which == BA_DBG_C ? h->C : h->Cinv, sizeof(double) * packed.size()));
+      expand_sym(packed.data(), 3, np, static_cast<double*>(host_out));
+      return BA_OK;
+    }
+    case BA_DBG_PCG: {
+      PcgState st;
+      CHECK_RC(d2h(h, &st, h->pcg, sizeof(st)));
+      double* o = static_cast<double*>(host_out);
+      o[0] = st.iters;
+      o[1] = st.rhs_norm > 0.0 ? st.res_norm / st.rhs_norm : 0.0;
+      return BA_OK;
+    }
+    case BA_DBG_TRIAL_COST: {
+      StepOut so;
+      CHECK_RC(d2h(h, &so, h->out, sizeof(so)));
+      *static_cast<double*>(host_out) = so.trial_cost;
+      return BA_OK;
+    }
+    default: return fail(BA_ERR_ARG, "bad array id");
+  }
+}
+
+int ba_profile_enable(ba_problem* h, int kernel_mask) {
+  if (!h) return fail(BA_ERR_ARG, "null handle");
+  h->prof_on = kernel_mask;
+  h->prof_recs.clear();
+  h->prof_used = 0;
+  return BA_OK;
+}
+
+int ba_profile_reset(ba_problem* h) {
+  if (!h) return fail(BA_ERR_ARG, "null handle");
+  for (int k = 0; k < BA_K_NUM; ++k) {
+    h->prof_count[k] = 0;
+    h->prof_ms[k] = 0.0;
+  }
+  return BA_OK;
+}
+
+int ba_profile_get(ba_problem* h, int kernel, int64_t* launches, double* total_ms) {
+  if (!h || kernel < 0 || kernel >= BA_K_NUM) return fail(BA_ERR_ARG, "bad arguments");
+  if (launches) *launches = h->prof_count[kernel];
+  if (total_ms) *total_ms = h->prof_ms[kernel];
+  return BA_OK;
+}
+
+const char* ba_kernel_name(int kernel) {
+  return (kernel >= 0 && kernel < BA_K_NUM) ? kKernelNames[kernel] : "unknown";
+}
+
+const char* ba_status_string(int code) {
+  static thread_local std::string msg;
+  const char* base = "unknown status";
+  switch (code) {
+    case BA_OK: base = "ok"; break;
+    case BA_ERR_ARG: base = "invalid argument"; break;
+    case BA_ERR_NONFINITE: base = "non-finite value"; break;
+    case BA_ERR_NOT_SPD: base = "matrix not positive definite"; break;
+    case BA_ERR_DEVICE: base = "device error"; break;
+    case BA_ERR_ALLOC: base = "allocation failed"; break;
+  }
+  msg = base;
+  if (code != BA_OK && !g_err.empty()) msg += ": " + g_err;
+  return msg.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// Kernel launchers for the gfx950 bundle-adjustment LM iteration (fp64).
+//
+// Data layout in HBM (all structure-of-arrays, sized once per handle):
+//   point order  : observations sorted by (point, camera, k); o_cam, o_pt
+//                  (int32), o_uv (2 doubles), w_pt (robust weight)
+//   camera order : observations sorted by (camera, point, k); c_pt (int32),
+//                  c_uv, w_cam, run_len (length of a repeated (camera, point)
+//                  run at its first element, 0 elsewhere)
+//   per point    : X (3), C (6, packed upper), g_p (3), C~^-1 (6), v (3),
+//                  z (3), dp (3)
+//   per camera   : parameters (9), CamT table (16), B (45), g_c (9), B~ (45),
+//                  rhs (9), Cholesky of S_jj (45), PCG vectors (9 each)
+//   partitions   : point tiles (whole points, <= kTile observations unless a
+//                  single point is longer), camera chunks (<= kChunk
+//                  observations of one camera, at least one per camera)
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ba_model.h"
+
+namespace ba {
+
+constexpr int kTile = 256;        // observations per point-order sub-tile (= block size)
+constexpr int kChunk = 1024;      // observations per camera-order chunk
+constexpr int kChunkBlock = 256;  // threads per camera-order block
+constexpr int kCostBlock = 1024;  // observations per cost-reduction block
+constexpr int kUpdBlock = 1024;   // threads of the single-block cost reduction
+constexpr int kLinCamVals = 54;   // B (45) + g_c (9)
+constexpr int kSchurVals = 54;    // E v (9) + Ebar C~^-1 Ebar^T (45)
+
+struct PcgState {     // outcome of the solve, written once when it stops
+  double rhs_norm;   // |rhs|_2
+  double res_norm;   // |r|_2 after the last update
+  int iters;
+  int done;
+  int breakdown;
+  int pad;
+};
+
+struct StepOut {     // everything the host reads back after a step
+  double trial_cost;
+  double pcg_rel_res;
+  int pcg_iters;
+  int nonfinite;
+  int not_spd;
+  int pad;
+};
+
+struct Dev {
+  int64_t nc, np, nobs;
+  int n_tiles, n_chunks, n_cost_blocks;
+  int loss;
+  double delta, diag_floor, lambda, tol;
+  // parameters (current and trial)
+  const double* cams;
+  const double* pts;
+  const CamT* tab;
+  double* cams_trial;
+  double* pts_trial;
+  CamT* tab_trial;
+  // structure
+  const int32_t* o_cam;
+  const int32_t* o_pt;
+  const double* o_uv;
+  const int32_t* c_pt;
+  const double* c_uv;
+  const int32_t* run_len;
+  const int32_t* pt_ptr;
+  const int32_t* tile_begin;
+  const int32_t* chunk_begin;
+  const int32_t* chunk_cam;
+  const int32_t* cam_chunk_ptr;
+  // linearisation
+  double* w_pt;
+  double* w_cam;
+  double* C;
+  double* gp;
+  double* B;
+  double* gc;
+  double* lin_part;
+  // elimination
+  double* Cinv;
+  double* v;
+  double* Bd;
+  double* rhs;
+  double* Mchol;
+  double* Mfull;     // undamped-by-Cholesky copy of S_jj (packed) for inspection
+  double* schur_part;
+  // PCG
+  double* x;
+  double* r;
+  double* zc;
+  double* pbuf;      // two search directions (iterations of either parity), 9 nc each
+  double* q;
+  double* zp;        // per-point C~^-1 E^T p
+  double* pcg_part;
+  double* pq_cam;    // per camera p_j . q_j
+  double* red_part;  // per-block partial sums of the camera-vector kernels, 6 x red_nb
+  int red_nb;        // blocks of the camera-vector kernels
+  int* host_done;    // host-mapped copy of pcg->done, polled between batches
+  PcgState* pcg;
+  // update
+  double* dp;
+  double* cost_part;
+  StepOut* out;
+  int* flags;        // [0] non-finite seen, [1] not SPD
+};
+
+void launch_cam_prep(const double* cams, CamT* tab, int64_t nc, hipStream_t s);
+void launch_lin_pt(const Dev& d, hipStream_t s);
+void launch_lin_cam(const Dev& d, hipStream_t s);
+void launch_damp_pt(const Dev& d, hipStream_t s);
+void launch_schur_cam(const Dev& d, hipStream_t s);
+void launch_lin_final(const Dev& d, hipStream_t s);
+void launch_precond(const Dev& d, hipStream_t s);
+void launch_pcg_init(const Dev& d, hipStream_t s);
+void launch_pcg_pt(const Dev& d, int it, hipStream_t s);
+void launch_pcg_cam(const Dev& d, hipStream_t s);
+void launch_pcg_q(const Dev& d, int it, hipStream_t s);
+void launch_pcg_xr(const Dev& d, int it, hipStream_t s);
+void launch_pcg_final(const Dev& d, int iters, hipStream_t s);
+int pcg_red_blocks(int64_t nc);   // blocks of the camera-vector kernels
+void launch_backsub(const Dev& d, hipStream_t s);
+void launch_retract(const Dev& d, hipStream_t s);
+void launch_cost(const Dev& d, const double* cams, const double* pts, const CamT* tab,
+                 hipStream_t s);
+void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* Jc, double* Jp,
+                      double* w, hipStream_t s);
+
+// Structure build helpers.
+void launch_validate(const int32_t* cam_idx, const int32_t* pt_idx, const double* uv, int64_t n,
+                     const double* cams, int64_t nc, const double* pts, int64_t np, int* flags,
+                     hipStream_t s);
+void launch_make_keys(const int32_t* major, const int32_t* minor, int64_t n_minor, int64_t n,
+                      uint64_t* keys, int32_t* vals, hipStream_t s);
+void launch_gather_obs(const int32_t* perm, const int32_t* cam_idx, const int32_t* pt_idx,
+                       const double* uv, int64_t n, int32_t* out_cam, int32_t* out_pt,
+                       double* out_uv, hipStream_t s);
+void launch_seg_ptr(const int32_t* sorted_key, int64_t n, int64_t n_seg, int32_t* ptr,
+                    hipStream_t s);
+void launch_run_len(const int32_t* c_cam, const int32_t* c_pt, int64_t n, int32_t* run_len,
+                    hipStream_t s);
+
+}  // namespace ba

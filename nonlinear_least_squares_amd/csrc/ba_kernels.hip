@@ -1,0 +1,984 @@
+// gfx950 kernels for one Levenberg-Marquardt iteration of bundle adjustment.
+//
+// Point-order passes (linearisation + point blocks, PCG point side,
+// back-substitution) run one thread per observation over tiles of whole
+// points; a point's sums are formed by a wavefront segmented scan, carried
+// across wavefronts through LDS and across sub-tiles for points longer than
+// a tile.  Camera-order passes (camera blocks, Schur right-hand side and
+// preconditioner, PCG camera side) run over chunks of one camera and reduce
+// with a fixed tree; per-camera totals add chunk partials in chunk order.
+// No floating-point atomics: results are bitwise reproducible run to run.
+#include "ba_kernels.h"
+
+namespace ba {
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ void load_cam(const CamT* tab, int j, CamT& c) { c = tab[j]; }
+
+// ---------------------------------------------------------------- reductions
+
+// Deterministic block reduction of K values; the total lands in s_out[0..K).
+template <int K, int NT>
+__device__ __forceinline__ void block_reduce(double (&v)[K], double* s_buf, double* s_out) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) v[k] += __shfl_xor(v[k], off, kWave);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) s_buf[wv * K + k] = v[k];
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < K; k += NT) {
+    double s = 0.0;
+    for (int w = 0; w < NW; ++w) s += s_buf[w * K + k];
+    s_out[k] = s;
+  }
+  __syncthreads();
+}
+
+// Segmented reduction over whole points for one point-order tile.  Op supplies
+//   compute(s, pt, v[K])  : per-observation contribution (s = point-order index)
+//   finish(pt, v[K])      : called once per point with its total
+template <int K, class Op>
+__device__ __forceinline__ void point_tile_reduce(const Dev& d, Op& op, int tile) {
+  __shared__ double s_tail[kTile / kWave][K];
+  __shared__ int s_tail_pt[kTile / kWave];
+  __shared__ int s_tail_full[kTile / kWave];
+  __shared__ double s_carry[K];
+  __shared__ int s_carry_pt;
+  const int ob = d.tile_begin[tile], oe = d.tile_begin[tile + 1];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  if (tid == 0) s_carry_pt = -1;
+  for (int base = ob; base < oe; base += kTile) {
+    const int s = base + tid;
+    const bool valid = s < oe;
+    const int pt = valid ? d.o_pt[s] : -1;
+    double v[K];
+    if (valid) {
+      op.compute(s, pt, v);
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) v[k] = 0.0;
+    }
+    // segment start within the wavefront
+    const int prev_pt = __shfl_up(pt, 1, kWave);
+    const bool head = (lane == 0) || (pt != prev_pt);
+    const unsigned long long heads = __ballot(head);
+    const unsigned long long upto = (lane == kWave - 1) ? ~0ull : ((2ull << lane) - 1ull);
+    const int seg0 = 63 - __clzll(heads & upto);
+#pragma unroll
+    for (int dd = 1; dd < kWave; dd <<= 1) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const double o = __shfl_up(v[k], dd, kWave);
+        if (lane - dd >= seg0) v[k] += o;
+      }
+    }
+    if (lane == kWave - 1) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) s_tail[wv][k] = v[k];
+      s_tail_pt[wv] = pt;
+      s_tail_full[wv] = (seg0 == 0);
+    }
+    __syncthreads();
+    if (valid && seg0 == 0) {
+      // this wavefront's first segment may continue from earlier wavefronts or sub-tiles
+      double c[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) c[k] = 0.0;
+      int w = wv - 1;
+      bool more = true;
+      while (more) {
+        if (w >= 0) {
+          if (s_tail_pt[w] == pt) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) c[k] += s_tail[w][k];
+            more = s_tail_full[w] != 0;
+            --w;
+          } else {
+            more = false;
+          }
+        } else {
+          if (s_carry_pt == pt) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) c[k] += s_carry[k];
+          }
+          more = false;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) v[k] += c[k];
+    }
+    const bool is_end = valid && (s + 1 >= oe || d.o_pt[s + 1] != pt);
+    if (is_end) op.finish(pt, v);
+    __syncthreads();
+    if (tid == kTile - 1) {
+      if (valid && !is_end) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) s_carry[k] = v[k];
+        s_carry_pt = pt;
+      } else {
+        s_carry_pt = -1;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------- camera table
+
+__global__ void k_cam_prep(const double* __restrict__ cams, CamT* __restrict__ tab, int64_t nc) {
+  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (j >= nc) return;
+  const double* c = cams + 9 * j;
+  CamT t;
+  so3_exp(c[0], c[1], c[2], t.R);
+  t.t[0] = c[3];
+  t.t[1] = c[4];
+  t.t[2] = c[5];
+  t.f = c[6];
+  t.k1 = c[7];
+  t.k2 = c[8];
+  t.pad = 0.0;
+  tab[j] = t;
+}
+
+// ------------------------------------------------------------ linearisation
+
+struct LinPtOp {
+  const Dev& d;
+  __device__ void compute(int s, int pt, double* v) {
+    CamT c;
+    load_cam(d.tab, d.o_cam[s], c);
+    Geo g;
+    geo_eval(c, d.pts[3 * pt], d.pts[3 * pt + 1], d.pts[3 * pt + 2], g);
+    const double r0 = g.u0 - d.o_uv[2 * s], r1 = g.u1 - d.o_uv[2 * s + 1];
+    double w, rho;
+    robust(r0, r1, d.loss, d.delta, w, rho);
+    d.w_pt[s] = w;
+    double J[6];
+    jp_rows(g, c.R, J);
+    v[0] = w * (J[0] * J[0] + J[3] * J[3]);
+    v[1] = w * (J[0] * J[1] + J[3] * J[4]);
+    v[2] = w * (J[0] * J[2] + J[3] * J[5]);
+    v[3] = w * (J[1] * J[1] + J[4] * J[4]);
+    v[4] = w * (J[1] * J[2] + J[4] * J[5]);
+    v[5] = w * (J[2] * J[2] + J[5] * J[5]);
+    v[6] = w * (J[0] * r0 + J[3] * r1);
+    v[7] = w * (J[1] * r0 + J[4] * r1);
+    v[8] = w * (J[2] * r0 + J[5] * r1);
+  }
+  __device__ void finish(int pt, const double* v) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) d.C[6 * pt + k] = v[k];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) d.gp[3 * pt + k] = v[6 + k];
+  }
+};
+
+__global__ __launch_bounds__(kTile) void k_lin_pt(Dev d) {
+  LinPtOp op{d};
+  point_tile_reduce<9>(d, op, blockIdx.x);
+}
+
+__global__ __launch_bounds__(kChunkBlock) void k_lin_cam(Dev d) {
+  __shared__ double s_buf[(kChunkBlock / kWave) * kLinCamVals];
+  __shared__ double s_out[kLinCamVals];
+  const int ch = blockIdx.x;
+  const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
+  CamT c;
+  load_cam(d.tab, d.chunk_cam[ch], c);
+  double acc[kLinCamVals];
+#pragma unroll
+  for (int k = 0; k < kLinCamVals; ++k) acc[k] = 0.0;
+  for (int s = cb + threadIdx.x; s < ce; s += kChunkBlock) {
+    const int i = d.c_pt[s];
+    Geo g;
+    geo_eval(c, d.pts[3 * i], d.pts[3 * i + 1], d.pts[3 * i + 2], g);
+    const double r0 = g.u0 - d.c_uv[2 * s], r1 = g.u1 - d.c_uv[2 * s + 1];
+    double w, rho;
+    robust(r0, r1, d.loss, d.delta, w, rho);
+    d.w_cam[s] = w;
+    double J[18];
+    jc_rows(g, c.f, J);
+    int idx = 0;
+#pragma unroll
+    for (int a = 0; a < 9; ++a) {
+      const double wa0 = w * J[a], wa1 = w * J[9 + a];
+#pragma unroll
+      for (int b = a; b < 9; ++b) acc[idx++] += wa0 * J[b] + wa1 * J[9 + b];
+      acc[45 + a] += wa0 * r0 + wa1 * r1;
+    }
+  }
+  block_reduce<kLinCamVals, kChunkBlock>(acc, s_buf, s_out);
+  for (int k = threadIdx.x; k < kLinCamVals; k += kChunkBlock)
+    d.lin_part[(int64_t)ch * kLinCamVals + k] = s_out[k];
+}
+
+// ----------------------------------------------------- damping and Schur
+
+// Damped point block, its inverse through a 3x3 Cholesky factor, v = C~^-1 g_p.
+__global__ void k_damp_pt(Dev d) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= d.np) return;
+  double C[6], g[3];
+  const bool empty = d.pt_ptr[i] == d.pt_ptr[i + 1];
+  if (empty) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) C[k] = 0.0;
+    g[0] = g[1] = g[2] = 0.0;
+    // no observation: the step is zero and the trial point is the current one
+    d.dp[3 * i] = d.dp[3 * i + 1] = d.dp[3 * i + 2] = 0.0;
+    d.pts_trial[3 * i] = d.pts[3 * i];
+    d.pts_trial[3 * i + 1] = d.pts[3 * i + 1];
+    d.pts_trial[3 * i + 2] = d.pts[3 * i + 2];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) C[k] = d.C[6 * i + k];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) g[k] = d.gp[3 * i + k];
+  }
+  const int diag[3] = {0, 3, 5};
+#pragma unroll
+  for (int a = 0; a < 3; ++a) C[diag[a]] += d.lambda * fmax(C[diag[a]], d.diag_floor);
+  if (!chol_packed<3>(C)) {
+    d.flags[1] = 1;
+    return;
+  }
+  // L^-1 (lower), then C~^-1 = L^-T L^-1
+  const double l00 = C[0], l10 = C[1], l20 = C[2], l11 = C[3], l21 = C[4], l22 = C[5];
+  const double i00 = 1.0 / l00, i11 = 1.0 / l11, i22 = 1.0 / l22;
+  const double i10 = -l10 * i00 * i11;
+  const double i21 = -l21 * i11 * i22;
+  const double i20 = -(l20 * i00 + l21 * i10) * i22;
+  double Ci[6];
+  Ci[0] = i00 * i00 + i10 * i10 + i20 * i20;
+  Ci[1] = i10 * i11 + i20 * i21;
+  Ci[2] = i20 * i22;
+  Ci[3] = i11 * i11 + i21 * i21;
+  Ci[4] = i21 * i22;
+  Ci[5] = i22 * i22;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) d.Cinv[6 * i + k] = Ci[k];
+  d.v[3 * i] = Ci[0] * g[0] + Ci[1] * g[1] + Ci[2] * g[2];
+  d.v[3 * i + 1] = Ci[1] * g[0] + Ci[3] * g[1] + Ci[4] * g[2];
+  d.v[3 * i + 2] = Ci[2] * g[0] + Ci[4] * g[1] + Ci[5] * g[2];
+}
+
+// Camera-order pass: E v (right-hand side) and Ebar C~^-1 Ebar^T (diagonal
+// blocks of S).  Repeated (camera, point) observations share J, so
+// Ebar = (sum of their weights) Jc^T Jp and the run head adds
+// W^2 Jc^T (Jp C~^-1 Jp^T) Jc.
+__global__ __launch_bounds__(kChunkBlock) void k_schur_cam(Dev d) {
+  __shared__ double s_buf[(kChunkBlock / kWave) * kSchurVals];
+  __shared__ double s_out[kSchurVals];
+  const int ch = blockIdx.x;
+  const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
+  CamT c;
+  load_cam(d.tab, d.chunk_cam[ch], c);
+  double acc[kSchurVals];
+#pragma unroll
+  for (int k = 0; k < kSchurVals; ++k) acc[k] = 0.0;
+  for (int s = cb + threadIdx.x; s < ce; s += kChunkBlock) {
+    const int i = d.c_pt[s];
+    Geo g;
+    geo_eval(c, d.pts[3 * i], d.pts[3 * i + 1], d.pts[3 * i + 2], g);
+    const double w = d.w_cam[s];
+    double t0, t1;
+    jp_apply(g, c.R, d.v[3 * i], d.v[3 * i + 1], d.v[3 * i + 2], t0, t1);
+    jct_acc(g, c.f, w * t0, w * t1, acc);
+    const int rl = d.run_len[s];
+    if (rl > 0) {
+      double W = 0.0;
+      for (int l = 0; l < rl; ++l) W += d.w_cam[s + l];
+      double Jp[6];
+      jp_rows(g, c.R, Jp);
+      const double* Ci = d.Cinv + 6 * i;
+      const double c00 = Ci[0], c01 = Ci[1], c02 = Ci[2], c11 = Ci[3], c12 = Ci[4], c22 = Ci[5];
+      // H = Jp C~^-1 (2 x 3), G = H Jp^T (2 x 2 symmetric)
+      double H[6];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        H[3 * a] = Jp[3 * a] * c00 + Jp[3 * a + 1] * c01 + Jp[3 * a + 2] * c02;
+        H[3 * a + 1] = Jp[3 * a] * c01 + Jp[3 * a + 1] * c11 + Jp[3 * a + 2] * c12;
+        H[3 * a + 2] = Jp[3 * a] * c02 + Jp[3 * a + 1] * c12 + Jp[3 * a + 2] * c22;
+      }
+      const double W2 = W * W;
+      const double g00 = W2 * (H[0] * Jp[0] + H[1] * Jp[1] + H[2] * Jp[2]);
+      const double g01 = W2 * (H[0] * Jp[3] + H[1] * Jp[4] + H[2] * Jp[5]);
+      const double g11 = W2 * (H[3] * Jp[3] + H[4] * Jp[4] + H[5] * Jp[5]);
+      double J[18];
+      jc_rows(g, c.f, J);
+      int idx = 9;
+#pragma unroll
+      for (int a = 0; a < 9; ++a) {
+        const double k0 = g00 * J[a] + g01 * J[9 + a];
+        const double k1 = g01 * J[a] + g11 * J[9 + a];
+#pragma unroll
+        for (int b = a; b < 9; ++b) acc[idx++] += k0 * J[b] + k1 * J[9 + b];
+      }
+    }
+  }
+  block_reduce<kSchurVals, kChunkBlock>(acc, s_buf, s_out);
+  for (int k = threadIdx.x; k < kSchurVals; k += kChunkBlock)
+    d.schur_part[(int64_t)ch * kSchurVals + k] = s_out[k];
+}
+
+// Per camera: B and g_c as the chunk partials summed in chunk order.
+__global__ void k_lin_final(Dev d) {
+  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (j >= d.nc) return;
+  double B[45], g[9];
+#pragma unroll
+  for (int k = 0; k < 45; ++k) B[k] = 0.0;
+#pragma unroll
+  for (int k = 0; k < 9; ++k) g[k] = 0.0;
+  for (int ch = d.cam_chunk_ptr[j]; ch < d.cam_chunk_ptr[j + 1]; ++ch) {
+    const double* pp = d.lin_part + (int64_t)ch * kLinCamVals;
+#pragma unroll
+    for (int k = 0; k < 45; ++k) B[k] += pp[k];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) g[k] += pp[45 + k];
+  }
+#pragma unroll
+  for (int k = 0; k < 45; ++k) d.B[45 * j + k] = B[k];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) d.gc[9 * j + k] = g[k];
+}
+
+// Per camera: B~ = B + lambda D, rhs = -g_c + E v, S_jj = B~ - sum Ebar C~^-1
+// Ebar^T and its Cholesky factor.
+__global__ void k_precond(Dev d) {
+  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (j >= d.nc) return;
+  const int c0 = d.cam_chunk_ptr[j], c1 = d.cam_chunk_ptr[j + 1];
+  double B[45], g[9];
+#pragma unroll
+  for (int k = 0; k < 45; ++k) B[k] = d.B[45 * j + k];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) g[k] = d.gc[9 * j + k];
+#pragma unroll
+  for (int a = 0; a < 9; ++a) {
+    const int ii = sym_idx(9, a, a);
+    B[ii] += d.lambda * fmax(B[ii], d.diag_floor);
+  }
+#pragma unroll
+  for (int k = 0; k < 45; ++k) d.Bd[45 * j + k] = B[k];
+  double ev[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) ev[k] = 0.0;
+  for (int ch = c0; ch < c1; ++ch) {
+    const double* pp = d.schur_part + (int64_t)ch * kSchurVals;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) ev[k] += pp[k];
+#pragma unroll
+    for (int k = 0; k < 45; ++k) B[k] -= pp[9 + k];
+  }
+#pragma unroll
+  for (int k = 0; k < 9; ++k) d.rhs[9 * j + k] = -g[k] + ev[k];
+#pragma unroll
+  for (int k = 0; k < 45; ++k) d.Mfull[45 * j + k] = B[k];
+  if (!chol_packed<9>(B)) d.flags[1] = 1;
+#pragma unroll
+  for (int k = 0; k < 45; ++k) d.Mchol[45 * j + k] = B[k];
+}
+
+// ---------------------------------------------------------------------- PCG
+
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double* s_buf) {
+  double a[1] = {v};
+  __shared__ double s_out[1];
+  block_reduce<1, NT>(a, s_buf, s_out);
+  return s_out[0];
+}
+
+// Search direction of iteration `it`: z + beta p_prev, p_prev being stored in
+// the buffer of the other parity.
+__device__ __forceinline__ double p_dir(const Dev& d, int it, double beta, int64_t e) {
+  return d.zc[e] + beta * d.pbuf[(int64_t)((it + 1) & 1) * 9 * d.nc + e];
+}
+
+// Point side of S p: zp_i = C~_i^-1 sum_{k in i} w Jp^T (Jc p_cam(k)), with
+// p_cam = z + beta p_prev formed per observation (MODE 0).  MODE 1
+// (back-substitution): dp_i = C~_i^-1 (-g_p,i - sum_k w Jp^T (Jc dc_cam(k))) and
+// the trial point.
+template <int MODE>
+struct PcgPtOp {
+  const Dev& d;
+  int it;
+  double beta;
+  __device__ void compute(int s, int pt, double* v) {
+    const int j = d.o_cam[s];
+    CamT c;
+    load_cam(d.tab, j, c);
+    Geo g;
+    geo_eval(c, d.pts[3 * pt], d.pts[3 * pt + 1], d.pts[3 * pt + 2], g);
+    double xc[9];
+    if (MODE == 0) {
+#pragma unroll
+      for (int k = 0; k < 9; ++k) xc[k] = p_dir(d, it, beta, 9 * (int64_t)j + k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 9; ++k) xc[k] = d.x[9 * (int64_t)j + k];
+    }
+    double u0, u1;
+    jc_apply(g, c.f, xc, u0, u1);
+    const double w = d.w_pt[s];
+    jpt_apply(g, c.R, w * u0, w * u1, v[0], v[1], v[2]);
+  }
+  __device__ void finish(int pt, const double* v) {
+    const double* Ci = d.Cinv + 6 * (int64_t)pt;
+    double y0 = v[0], y1 = v[1], y2 = v[2];
+    if (MODE == 1) {
+      y0 = -d.gp[3 * pt] - y0;
+      y1 = -d.gp[3 * pt + 1] - y1;
+      y2 = -d.gp[3 * pt + 2] - y2;
+    }
+    const double z0 = Ci[0] * y0 + Ci[1] * y1 + Ci[2] * y2;
+    const double z1 = Ci[1] * y0 + Ci[3] * y1 + Ci[4] * y2;
+    const double z2 = Ci[2] * y0 + Ci[4] * y1 + Ci[5] * y2;
+    if (MODE == 0) {
+      d.zp[3 * pt] = z0;
+      d.zp[3 * pt + 1] = z1;
+      d.zp[3 * pt + 2] = z2;
+    } else {
+      d.dp[3 * pt] = z0;
+      d.dp[3 * pt + 1] = z1;
+      d.dp[3 * pt + 2] = z2;
+      d.pts_trial[3 * pt] = d.pts[3 * pt] + z0;
+      d.pts_trial[3 * pt + 1] = d.pts[3 * pt + 1] + z1;
+      d.pts_trial[3 * pt + 2] = d.pts[3 * pt + 2] + z2;
+    }
+  }
+};
+
+__global__ __launch_bounds__(kTile) void k_backsub(Dev d) {
+  PcgPtOp<1> op{d, 0, 0.0};
+  point_tile_reduce<3>(d, op, blockIdx.x);
+}
+
+// z_j = M_j^-1 r_j with the packed Cholesky factor of S_jj.
+// Camera vectors in the persistent solve are handled 7 cameras per wavefront,
+// 9 lanes per camera (lane 63 idle), so every load and store is coalesced.
+struct CamLane {
+  int64_t j;    // camera (clamped to a valid one on idle lanes)
+  int a;        // row 0..8
+  int base;     // first lane of the camera's group
+  bool on;      // lane holds a real (camera, row)
+};
+
+__device__ __forceinline__ CamLane cam_lane(int64_t wave, int64_t nc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  CamLane c;
+  const int64_t j = wave * 7 + lane / 9;
+  c.on = lane < 63 && j < nc;
+  c.j = c.on ? j : 0;
+  c.a = lane < 63 ? lane % 9 : 0;
+  c.base = lane < 63 ? lane - c.a : 0;
+  return c;
+}
+
+// z_a of z = M_j^-1 r_j on the 9 lanes of camera j: forward substitution
+// L y = r, then backward L^T z = y, with the packed Cholesky factor of S_jj;
+// each solved component is broadcast to the group by a shuffle.
+__device__ __forceinline__ double precond_lane(const Dev& d, const CamLane& c, double r) {
+  const double* L = d.Mchol + 45 * c.j;
+  double acc = 0.0, y = 0.0;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const double yi = __shfl(c.a == i ? (r - acc) / L[sym_idx(9, i, i)] : 0.0, c.base + i, kWave);
+    if (c.a == i) y = yi;
+    if (c.a > i) acc += L[sym_idx(9, i, c.a)] * yi;
+  }
+  acc = 0.0;
+  double z = 0.0;
+#pragma unroll
+  for (int i = 8; i >= 0; --i) {
+    const double zi = __shfl(c.a == i ? (y - acc) / L[sym_idx(9, i, i)] : 0.0, c.base + i, kWave);
+    if (c.a == i) z = zi;
+    if (c.a < i) acc += L[sym_idx(9, c.a, i)] * zi;
+  }
+  return z;
+}
+
+__device__ __forceinline__ double block_sum_array_serial(const double* a, int n) {
+  double v = 0.0;
+  for (int k = 0; k < n; ++k) v += a[k];
+  return v;
+}
+
+// Sum of n doubles in index order by one block (fixed tree): every block that
+// calls it on the same data gets the same bits.
+__device__ __forceinline__ double block_sum_array(const double* a, int n, int stride,
+                                                  double* s_buf) {
+  double v = 0.0;
+  for (int k = threadIdx.x; k < n; k += kTile) v += a[(int64_t)k * stride];
+  return block_sum<kTile>(v, s_buf);
+}
+
+// PCG on S dc = rhs with the block-Jacobi preconditioner M = blockdiag(S_jj).
+// Kernel boundaries are the only grid-wide synchronisation: every global
+// scalar is re-derived in each block that needs it from a few per-block
+// partial sums, added in block order by the same code, so all blocks agree
+// bit for bit.  Per iteration `it`:
+//   pt   beta = rz_it / rz_{it-1} (0 at it = 0); p = z + beta p_prev (formed on
+//        the fly for the gathers and stored once); zp_i = C~_i^-1 sum_{k in i}
+//        w Jp^T (Jc p_cam(k)); at it >= 1 stops first if |r| <= tol |rhs|
+//   cam  chunk partials of sum_k w Jc^T (Jp zp_pt(k))
+//   q    q_j = B~_j p_j - sum of the chunk partials of camera j; p.q partials
+//   xr   alpha = rz_it / p.q (stop if p.q is not positive); x += alpha p,
+//        r -= alpha q, z = M^-1 r; partials of r.r and r.z for it + 1
+// All four return at once after the solve has stopped, so the host may queue
+// iterations past the stopping point.
+
+// Grid size of the camera-vector kernels: 7 cameras per wavefront.
+__host__ __device__ inline int cam_vector_blocks(int64_t nc) {
+  const int64_t waves = (nc + 6) / 7;
+  return (int)((waves + kTile / kWave - 1) / (kTile / kWave));
+}
+
+// Per-block partial-sum arrays of the camera-vector kernels (nb blocks each).
+__device__ __forceinline__ double* red_rr(const Dev& d, int par) { return d.red_part + 2 * par * d.red_nb; }
+__device__ __forceinline__ double* red_rz(const Dev& d, int par) { return red_rr(d, par) + d.red_nb; }
+__device__ __forceinline__ double* red_rhs(const Dev& d) { return d.red_part + 4 * d.red_nb; }
+__device__ __forceinline__ double* red_pq(const Dev& d) { return d.red_part + 5 * d.red_nb; }
+
+__device__ __forceinline__ void stop_pcg(const Dev& d, int iters, double res, double rhs_norm,
+                                         int breakdown) {
+  d.pcg->done = 1;
+  d.pcg->iters = iters;
+  d.pcg->res_norm = res;
+  d.pcg->rhs_norm = rhs_norm;
+  d.pcg->breakdown = breakdown;
+  *d.host_done = 1;
+  __threadfence_system();
+}
+
+__global__ __launch_bounds__(kTile) void k_pcg_init(Dev d) {
+  __shared__ double s_buf[kTile / kWave];
+  const int64_t wave = ((int64_t)blockIdx.x * kTile + threadIdx.x) / kWave;
+  const CamLane c = cam_lane(wave, d.nc);
+  const int64_t e = 9 * c.j + c.a;
+  const double r = c.on ? d.rhs[e] : 0.0;
+  const double z = precond_lane(d, c, r);
+  double rr = 0.0, rz = 0.0;
+  if (c.on) {
+    d.r[e] = r;
+    d.x[e] = 0.0;
+    d.zc[e] = z;
+    d.pbuf[e] = z;                 // p of iteration 0
+    d.pbuf[9 * d.nc + e] = 0.0;    // "previous" direction, weighted by beta = 0
+    rr = r * r;
+    rz = r * z;
+  }
+  rr = block_sum<kTile>(rr, s_buf);
+  rz = block_sum<kTile>(rz, s_buf);
+  if (threadIdx.x == 0) {
+    red_rr(d, 0)[blockIdx.x] = rr;
+    red_rz(d, 0)[blockIdx.x] = rz;
+    red_rhs(d)[blockIdx.x] = rr;
+    if (blockIdx.x == 0) {
+      d.pcg->done = 0;
+      d.pcg->iters = 0;
+      d.pcg->breakdown = 0;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
+  if (d.pcg->done) return;
+  __shared__ double s_buf[kTile / kWave];
+  __shared__ double s_beta;
+  const double rhs_norm = sqrt(block_sum_array(red_rhs(d), d.red_nb, 1, s_buf));
+  double beta = 0.0;
+  if (it == 0) {
+    if (rhs_norm == 0.0) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, 0, 0.0, 0.0, 0);
+      return;
+    }
+  } else {
+    const double res = sqrt(block_sum_array(red_rr(d, it & 1), d.red_nb, 1, s_buf));
+    if (res <= d.tol * rhs_norm) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, it, res, rhs_norm, 0);
+      return;
+    }
+    const double rz_new = block_sum_array(red_rz(d, it & 1), d.red_nb, 1, s_buf);
+    const double rz_old = block_sum_array(red_rz(d, (it + 1) & 1), d.red_nb, 1, s_buf);
+    if (threadIdx.x == 0) s_beta = rz_new / rz_old;
+    __syncthreads();
+    beta = s_beta;
+    // store this iteration's direction for the camera-side kernels
+    for (int64_t e = (int64_t)blockIdx.x * kTile + threadIdx.x; e < 9 * d.nc;
+         e += (int64_t)gridDim.x * kTile)
+      d.pbuf[(int64_t)(it & 1) * 9 * d.nc + e] = p_dir(d, it, beta, e);
+  }
+  PcgPtOp<0> op{d, it, beta};
+  point_tile_reduce<3>(d, op, blockIdx.x);
+}
+
+__global__ __launch_bounds__(kTile) void k_pcg_cam(Dev d) {
+  if (d.pcg->done) return;
+  __shared__ double s_red[(kTile / kWave) * 9];
+  __shared__ double s_out[9];
+  const int ch = blockIdx.x;
+  const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
+  CamT c;
+  load_cam(d.tab, d.chunk_cam[ch], c);
+  double acc[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) acc[k] = 0.0;
+  for (int s = cb + threadIdx.x; s < ce; s += kTile) {
+    const int i = d.c_pt[s];
+    Geo g;
+    geo_eval(c, d.pts[3 * i], d.pts[3 * i + 1], d.pts[3 * i + 2], g);
+    double t0, t1;
+    jp_apply(g, c.R, d.zp[3 * i], d.zp[3 * i + 1], d.zp[3 * i + 2], t0, t1);
+    const double w = d.w_cam[s];
+    jct_acc(g, c.f, w * t0, w * t1, acc);
+  }
+  block_reduce<9, kTile>(acc, s_red, s_out);
+  if (threadIdx.x < 9) d.pcg_part[(int64_t)ch * 9 + threadIdx.x] = s_out[threadIdx.x];
+}
+
+__global__ __launch_bounds__(kTile) void k_pcg_q(Dev d, int it) {
+  if (d.pcg->done) return;
+  __shared__ double s_buf[kTile / kWave];
+  const int64_t wave = ((int64_t)blockIdx.x * kTile + threadIdx.x) / kWave;
+  const CamLane c = cam_lane(wave, d.nc);
+  const double* p = d.pbuf + (int64_t)(it & 1) * 9 * d.nc + 9 * c.j;
+  const double* Bd = d.Bd + 45 * c.j;
+  double qa = 0.0;
+#pragma unroll
+  for (int b = 0; b < 9; ++b)
+    qa += Bd[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)] * p[b];
+  for (int ch = d.cam_chunk_ptr[c.j]; ch < d.cam_chunk_ptr[c.j + 1]; ++ch)
+    qa -= d.pcg_part[(int64_t)ch * 9 + c.a];
+  double pq = 0.0;
+  if (c.on) {
+    d.q[9 * c.j + c.a] = qa;
+    pq = p[c.a] * qa;
+  }
+  pq = block_sum<kTile>(pq, s_buf);
+  if (threadIdx.x == 0) red_pq(d)[blockIdx.x] = pq;
+}
+
+__global__ __launch_bounds__(kTile) void k_pcg_xr(Dev d, int it) {
+  if (d.pcg->done) return;
+  __shared__ double s_buf[kTile / kWave];
+  const double pq = block_sum_array(red_pq(d), d.red_nb, 1, s_buf);
+  if (!(pq > 0.0) || !isfinite(pq)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      const double rhs_norm = sqrt(block_sum_array_serial(red_rhs(d), d.red_nb));
+      const double res = it == 0 ? rhs_norm : sqrt(block_sum_array_serial(red_rr(d, it & 1), d.red_nb));
+      stop_pcg(d, it, res, rhs_norm, 1);
+    }
+    return;
+  }
+  const double alpha = block_sum_array(red_rz(d, it & 1), d.red_nb, 1, s_buf) / pq;
+  const int64_t wave = ((int64_t)blockIdx.x * kTile + threadIdx.x) / kWave;
+  const CamLane c = cam_lane(wave, d.nc);
+  const int64_t e = 9 * c.j + c.a;
+  double r = 0.0;
+  if (c.on) {
+    d.x[e] += alpha * d.pbuf[(int64_t)(it & 1) * 9 * d.nc + e];
+    r = d.r[e] - alpha * d.q[e];
+    d.r[e] = r;
+  }
+  const double z = precond_lane(d, c, r);
+  double rr = 0.0, rz = 0.0;
+  if (c.on) {
+    d.zc[e] = z;
+    rr = r * r;
+    rz = r * z;
+  }
+  rr = block_sum<kTile>(rr, s_buf);
+  rz = block_sum<kTile>(rz, s_buf);
+  if (threadIdx.x == 0) {
+    red_rr(d, (it + 1) & 1)[blockIdx.x] = rr;
+    red_rz(d, (it + 1) & 1)[blockIdx.x] = rz;
+  }
+}
+
+// After the last queued iteration: record the outcome if the solve ran to the
+// iteration limit (a stop inside the loop has already been recorded).
+__global__ __launch_bounds__(kTile) void k_pcg_final(Dev d, int iters) {
+  __shared__ double s_buf[kTile / kWave];
+  if (d.pcg->done) return;
+  const double rhs_norm = sqrt(block_sum_array(red_rhs(d), d.red_nb, 1, s_buf));
+  const double res = iters == 0 ? rhs_norm
+                                : sqrt(block_sum_array(red_rr(d, iters & 1), d.red_nb, 1, s_buf));
+  if (threadIdx.x == 0) stop_pcg(d, iters, res, rhs_norm, 0);
+}
+
+// ------------------------------------------------------------ update, cost
+
+// Trial camera: rotation q(dphi) (x) q(w) in the hemisphere qw >= 0, back to
+// axis-angle by 2 atan2(|v|, qw) v / |v|; the other parameters additive.
+__global__ void k_retract(Dev d) {
+  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (j >= d.nc) return;
+  const double* c = d.cams + 9 * j;
+  const double* dx = d.x + 9 * j;
+  double qa[4], qb[4];
+  {
+    const double* w = dx;
+    const double th = sqrt(w[0] * w[0] + w[1] * w[1] + w[2] * w[2]);
+    const double h = th < 1e-8 ? 0.5 : sin(0.5 * th) / th;
+    qa[0] = th < 1e-8 ? 1.0 : cos(0.5 * th);
+    qa[1] = h * w[0];
+    qa[2] = h * w[1];
+    qa[3] = h * w[2];
+  }
+  {
+    const double* w = c;
+    const double th = sqrt(w[0] * w[0] + w[1] * w[1] + w[2] * w[2]);
+    const double h = th < 1e-8 ? 0.5 : sin(0.5 * th) / th;
+    qb[0] = th < 1e-8 ? 1.0 : cos(0.5 * th);
+    qb[1] = h * w[0];
+    qb[2] = h * w[1];
+    qb[3] = h * w[2];
+  }
+  double qw = qa[0] * qb[0] - qa[1] * qb[1] - qa[2] * qb[2] - qa[3] * qb[3];
+  double qx = qa[0] * qb[1] + qa[1] * qb[0] + qa[2] * qb[3] - qa[3] * qb[2];
+  double qy = qa[0] * qb[2] - qa[1] * qb[3] + qa[2] * qb[0] + qa[3] * qb[1];
+  double qz = qa[0] * qb[3] + qa[1] * qb[2] - qa[2] * qb[1] + qa[3] * qb[0];
+  if (qw < 0.0) {
+    qw = -qw;
+    qx = -qx;
+    qy = -qy;
+    qz = -qz;
+  }
+  const double vn = sqrt(qx * qx + qy * qy + qz * qz);
+  const double k = vn < 1e-12 ? 2.0 / qw : 2.0 * atan2(vn, qw) / vn;
+  double* o = d.cams_trial + 9 * j;
+  o[0] = k * qx;
+  o[1] = k * qy;
+  o[2] = k * qz;
+#pragma unroll
+  for (int a = 3; a < 9; ++a) o[a] = c[a] + dx[a];
+  CamT t;
+  so3_exp(o[0], o[1], o[2], t.R);
+  t.t[0] = o[3];
+  t.t[1] = o[4];
+  t.t[2] = o[5];
+  t.f = o[6];
+  t.k1 = o[7];
+  t.k2 = o[8];
+  t.pad = 0.0;
+  d.tab_trial[j] = t;
+}
+
+__global__ __launch_bounds__(256) void k_cost(Dev d, const double* __restrict__ pts,
+                                              const CamT* __restrict__ tab) {
+  __shared__ double s_buf[256 / kWave];
+  const int64_t b0 = (int64_t)blockIdx.x * kCostBlock;
+  const int64_t b1 = b0 + kCostBlock < d.nobs ? b0 + kCostBlock : d.nobs;
+  double acc = 0.0;
+  for (int64_t s = b0 + threadIdx.x; s < b1; s += 256) {
+    const int i = d.o_pt[s];
+    CamT c;
+    load_cam(tab, d.o_cam[s], c);
+    Geo g;
+    geo_eval(c, pts[3 * i], pts[3 * i + 1], pts[3 * i + 2], g);
+    double w, rho;
+    robust(g.u0 - d.o_uv[2 * s], g.u1 - d.o_uv[2 * s + 1], d.loss, d.delta, w, rho);
+    acc += rho;
+  }
+  acc = block_sum<256>(acc, s_buf);
+  if (threadIdx.x == 0) d.cost_part[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kUpdBlock) void k_cost_final(Dev d) {
+  __shared__ double s_buf[kUpdBlock / kWave];
+  double acc = 0.0;
+  for (int b = threadIdx.x; b < d.n_cost_blocks; b += kUpdBlock) acc += d.cost_part[b];
+  acc = block_sum<kUpdBlock>(acc, s_buf);
+  if (threadIdx.x == 0) {
+    d.out->trial_cost = acc;
+    d.out->pcg_iters = d.pcg->iters;
+    d.out->pcg_rel_res = d.pcg->rhs_norm > 0.0 ? d.pcg->res_norm / d.pcg->rhs_norm : 0.0;
+    d.out->nonfinite = isfinite(acc) ? 0 : 1;
+    d.out->not_spd = d.flags[1];
+  }
+}
+
+// ------------------------------------------------------------------- debug
+
+__global__ void k_debug_obs(Dev d, const int32_t* __restrict__ perm_pt, double* r, double* Jc,
+                            double* Jp, double* wout) {
+  const int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (s >= d.nobs) return;
+  const int pt = d.o_pt[s];
+  CamT c;
+  load_cam(d.tab, d.o_cam[s], c);
+  Geo g;
+  geo_eval(c, d.pts[3 * pt], d.pts[3 * pt + 1], d.pts[3 * pt + 2], g);
+  const double r0 = g.u0 - d.o_uv[2 * s], r1 = g.u1 - d.o_uv[2 * s + 1];
+  double w, rho;
+  robust(r0, r1, d.loss, d.delta, w, rho);
+  const int64_t k = perm_pt[s];
+  r[2 * k] = r0;
+  r[2 * k + 1] = r1;
+  wout[k] = w;
+  double J[18];
+  jc_rows(g, c.f, J);
+  for (int a = 0; a < 18; ++a) Jc[18 * k + a] = J[a];
+  double P[6];
+  jp_rows(g, c.R, P);
+  for (int a = 0; a < 6; ++a) Jp[6 * k + a] = P[a];
+}
+
+// ------------------------------------------------------------------ structure
+
+__global__ void k_validate(const int32_t* cam_idx, const int32_t* pt_idx, const double* uv,
+                           int64_t n, const double* cams, int64_t nc, const double* pts,
+                           int64_t np, int* flags) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  int bad_idx = 0, bad_val = 0;
+  for (int64_t k = t0; k < n; k += stride) {
+    const int32_t c = cam_idx[k], p = pt_idx[k];
+    if (c < 0 || c >= nc || p < 0 || p >= np) bad_idx = 1;
+    if (!isfinite(uv[2 * k]) || !isfinite(uv[2 * k + 1])) bad_val = 1;
+  }
+  for (int64_t k = t0; k < 9 * nc; k += stride)
+    if (!isfinite(cams[k])) bad_val = 1;
+  for (int64_t k = t0; k < 3 * np; k += stride)
+    if (!isfinite(pts[k])) bad_val = 1;
+  if (bad_idx) atomicOr(flags + 0, 1);
+  if (bad_val) atomicOr(flags + 1, 1);
+}
+
+__global__ void k_make_keys(const int32_t* major, const int32_t* minor, int64_t n_minor, int64_t n,
+                            uint64_t* keys, int32_t* vals) {
+  const int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  keys[k] = (uint64_t)major[k] * (uint64_t)n_minor + (uint64_t)minor[k];
+  vals[k] = (int32_t)k;
+}
+
+__global__ void k_gather_obs(const int32_t* perm, const int32_t* cam_idx, const int32_t* pt_idx,
+                             const double* uv, int64_t n, int32_t* out_cam, int32_t* out_pt,
+                             double* out_uv) {
+  const int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (s >= n) return;
+  const int32_t k = perm[s];
+  if (out_cam) out_cam[s] = cam_idx[k];
+  if (out_pt) out_pt[s] = pt_idx[k];
+  out_uv[2 * s] = uv[2 * k];
+  out_uv[2 * s + 1] = uv[2 * k + 1];
+}
+
+__global__ void k_seg_ptr(const int32_t* key, int64_t n, int64_t n_seg, int32_t* ptr) {
+  const int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (s > n) return;
+  const int64_t lo = s == 0 ? 0 : (int64_t)key[s - 1] + 1;
+  const int64_t hi = s == n ? n_seg : (int64_t)key[s];
+  for (int64_t g = lo; g <= hi; ++g) ptr[g] = (int32_t)s;
+}
+
+__global__ void k_run_len(const int32_t* c_cam, const int32_t* c_pt, int64_t n, int32_t* run_len) {
+  const int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (s >= n) return;
+  const bool head = s == 0 || c_cam[s] != c_cam[s - 1] || c_pt[s] != c_pt[s - 1];
+  int len = 0;
+  if (head) {
+    len = 1;
+    while (s + len < n && c_cam[s + len] == c_cam[s] && c_pt[s + len] == c_pt[s]) ++len;
+  }
+  run_len[s] = len;
+}
+
+inline unsigned blocks_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+
+void launch_cam_prep(const double* cams, CamT* tab, int64_t nc, hipStream_t s) {
+  if (nc > 0) k_cam_prep<<<blocks_for(nc, 256), 256, 0, s>>>(cams, tab, nc);
+}
+void launch_lin_pt(const Dev& d, hipStream_t s) {
+  if (d.n_tiles > 0) k_lin_pt<<<d.n_tiles, kTile, 0, s>>>(d);
+}
+void launch_lin_cam(const Dev& d, hipStream_t s) {
+  if (d.n_chunks > 0) k_lin_cam<<<d.n_chunks, kChunkBlock, 0, s>>>(d);
+}
+void launch_damp_pt(const Dev& d, hipStream_t s) {
+  if (d.np > 0) k_damp_pt<<<blocks_for(d.np, 256), 256, 0, s>>>(d);
+}
+void launch_schur_cam(const Dev& d, hipStream_t s) {
+  if (d.n_chunks > 0) k_schur_cam<<<d.n_chunks, kChunkBlock, 0, s>>>(d);
+}
+void launch_lin_final(const Dev& d, hipStream_t s) {
+  if (d.nc > 0) k_lin_final<<<blocks_for(d.nc, 64), 64, 0, s>>>(d);
+}
+void launch_precond(const Dev& d, hipStream_t s) {
+  if (d.nc > 0) k_precond<<<blocks_for(d.nc, 64), 64, 0, s>>>(d);
+}
+void launch_pcg_init(const Dev& d, hipStream_t s) {
+  k_pcg_init<<<cam_vector_blocks(d.nc), kTile, 0, s>>>(d);
+}
+void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
+  k_pcg_pt<<<d.n_tiles > 0 ? d.n_tiles : 1, kTile, 0, s>>>(d, it);
+}
+void launch_pcg_cam(const Dev& d, hipStream_t s) { k_pcg_cam<<<d.n_chunks, kTile, 0, s>>>(d); }
+void launch_pcg_q(const Dev& d, int it, hipStream_t s) {
+  k_pcg_q<<<cam_vector_blocks(d.nc), kTile, 0, s>>>(d, it);
+}
+void launch_pcg_xr(const Dev& d, int it, hipStream_t s) {
+  k_pcg_xr<<<cam_vector_blocks(d.nc), kTile, 0, s>>>(d, it);
+}
+void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
+  k_pcg_final<<<1, kTile, 0, s>>>(d, iters);
+}
+int pcg_red_blocks(int64_t nc) { return cam_vector_blocks(nc); }
+void launch_backsub(const Dev& d, hipStream_t s) {
+  if (d.n_tiles > 0) k_backsub<<<d.n_tiles, kTile, 0, s>>>(d);
+}
+void launch_retract(const Dev& d, hipStream_t s) {
+  if (d.nc > 0) k_retract<<<blocks_for(d.nc, 128), 128, 0, s>>>(d);
+}
+void launch_cost(const Dev& d, const double* cams, const double* pts, const CamT* tab,
+                 hipStream_t s) {
+  (void)cams;
+  if (d.n_cost_blocks > 0) k_cost<<<d.n_cost_blocks, 256, 0, s>>>(d, pts, tab);
+  k_cost_final<<<1, kUpdBlock, 0, s>>>(d);
+}
+void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* Jc, double* Jp,
+                      double* w, hipStream_t s) {
+  if (d.nobs > 0) k_debug_obs<<<blocks_for(d.nobs, 256), 256, 0, s>>>(d, perm_pt, r, Jc, Jp, w);
+}
+void launch_validate(const int32_t* cam_idx, const int32_t* pt_idx, const double* uv, int64_t n,
+                     const double* cams, int64_t nc, const double* pts, int64_t np, int* flags,
+                     hipStream_t s) {
+  k_validate<<<1024, 256, 0, s>>>(cam_idx, pt_idx, uv, n, cams, nc, pts, np, flags);
+}
+void launch_make_keys(const int32_t* major, const int32_t* minor, int64_t n_minor, int64_t n,
+                      uint64_t* keys, int32_t* vals, hipStream_t s) {
+  if (n > 0) k_make_keys<<<blocks_for(n, 256), 256, 0, s>>>(major, minor, n_minor, n, keys, vals);
+}
+void launch_gather_obs(const int32_t* perm, const int32_t* cam_idx, const int32_t* pt_idx,
+                       const double* uv, int64_t n, int32_t* out_cam, int32_t* out_pt,
+                       double* out_uv, hipStream_t s) {
+  if (n > 0)
+    k_gather_obs<<<blocks_for(n, 256), 256, 0, s>>>(perm, cam_idx, pt_idx, uv, n, out_cam, out_pt,
+                                                    out_uv);
+}
+void launch_seg_ptr(const int32_t* sorted_key, int64_t n, int64_t n_seg, int32_t* ptr,
+                    hipStream_t s) {
+  k_seg_ptr<<<blocks_for(n + 1, 256), 256, 0, s>>>(sorted_key, n, n_seg, ptr);
+}
+void launch_run_len(const int32_t* c_cam, const int32_t* c_pt, int64_t n, int32_t* run_len,
+                    hipStream_t s) {
+  if (n > 0) k_run_len<<<blocks_for(n, 256), 256, 0, s>>>(c_cam, c_pt, n, run_len);
+}
+
+}  // namespace ba

@@ -1,0 +1,66 @@
+"""The C-ABI libraries load and export every entry point their headers declare.
+
+No compute calls: only host-side functions that never touch a GPU are called
+(defaults, status strings, argument checks that fail before any device work).
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from nonlinear_least_squares_amd import ba as bamod
+from nonlinear_least_squares_amd import build as buildmod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECL = re.compile(r"^(?:int|void|int64_t|const char\*)\s+\**\s*((?:ba|dba)_\w+)\s*\(", re.M)
+
+
+def _declared(header):
+    with open(os.path.join(ROOT, "include", header)) as f:
+        return sorted(set(DECL.findall(f.read())))
+
+
+def _ensure(libname):
+    path = os.path.join(buildmod.HERE, libname)
+    if not os.path.exists(path):
+        buildmod.build([libname])
+    return path
+
+
+def test_libba_exports_every_declared_symbol():
+    names = _declared("ba.h")
+    assert len(names) >= 19
+    L = C.CDLL(_ensure("libba.so"))
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # The Python binding covers the whole ABI, no more and no less.
+    assert sorted(bamod.SIGNATURES) == names
+
+
+def test_host_only_entry_points():
+    L = bamod.lib()
+    o = bamod.options()
+    assert (o.loss, o.huber_delta, o.lambda0, o.pcg_max_iters, o.pcg_rel_tol) == (0, 2.0, 1e-3, 50, 1e-6)
+    assert L.ba_options_default(None) == bamod.BA_ERR_ARG
+    assert L.ba_status_string(bamod.BA_OK) == b"ok"
+    assert b"invalid argument" in L.ba_status_string(bamod.BA_ERR_ARG)
+    assert L.ba_kernel_name(0) == b"lin_pt"
+    # Argument errors are caught on the host before any device work.
+    h = C.c_void_p()
+    rc = L.ba_create(None, 1, None, 1, None, None, None, 0, None, C.byref(h))
+    assert rc == bamod.BA_ERR_ARG and not h.value
+    assert L.ba_lm_step(None, None) == bamod.BA_ERR_ARG
+    assert L.ba_debug_size(None, 0) == bamod.BA_ERR_ARG
+    bad = bamod.options(loss=7)
+    cams = (C.c_double * 9)()
+    pts = (C.c_double * 3)()
+    rc = L.ba_create(cams, 1, pts, 1, None, None, None, 0, C.byref(bad), C.byref(h))
+    assert rc == bamod.BA_ERR_ARG and not h.value
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(bamod, "_lib", None)
+    monkeypatch.setattr(bamod, "LIB_PATH", str(tmp_path / "libba.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        bamod.lib()
