@@ -98,7 +98,7 @@ struct ba_problem {
          *gc = nullptr, *lin_part = nullptr;
   double *Cinv = nullptr, *v = nullptr, *Bd = nullptr, *rhs = nullptr, *Mchol = nullptr,
          *Mfull = nullptr, *schur_part = nullptr;
-  double *x = nullptr, *r = nullptr, *zc = nullptr, *pbuf = nullptr, *q = nullptr, *zp = nullptr,
+  double *x = nullptr, *r = nullptr, *zc = nullptr, *pbuf = nullptr, *q = nullptr, *prec = nullptr,
          *pcg_part = nullptr, *pq_cam = nullptr, *red_part = nullptr;
   PcgState* pcg = nullptr;
   double *dp = nullptr, *cost_part = nullptr;
@@ -174,7 +174,7 @@ Dev make_dev(const ba_problem* h) {
   d.zc = h->zc;
   d.pbuf = h->pbuf;
   d.q = h->q;
-  d.zp = h->zp;
+  d.prec = h->prec;
   d.pcg_part = h->pcg_part;
   d.pq_cam = h->pq_cam;
   d.red_part = h->red_part;
@@ -269,6 +269,7 @@ int stage_pcg(ba_problem* h) {
   int next_it = 0;
   auto enqueue = [&](int n) -> int {
     for (int k = 0; k < n; ++k, ++next_it) {
+      launch_pcg_pnext(d, next_it, h->stream);
       TIMED(BA_K_PCG_PT, next_it, launch_pcg_pt(d, next_it, h->stream));
       TIMED(BA_K_PCG_CAM, next_it, launch_pcg_cam(d, h->stream));
       TIMED(BA_K_PCG_Q, next_it, launch_pcg_q(d, next_it, h->stream));
@@ -439,7 +440,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   A.add(h->gp, 3 * np);
   A.add(h->Cinv, 6 * np);
   A.add(h->v, 3 * np);
-  A.add(h->zp, 3 * np);
+  A.add(h->prec, 8 * np);
   A.add(h->dp, 3 * np);
   A.add(h->B, 45 * nc);
   A.add(h->gc, 9 * nc);

@@ -94,7 +94,7 @@ struct Dev {
   double* zc;
   double* pbuf;      // two search directions (iterations of either parity), 9 nc each
   double* q;
-  double* zp;        // per-point C~^-1 E^T p
+  double* prec;      // per-point 64-byte record: X (3), z = C~^-1 E^T p (3), pad (2)
   double* pcg_part;
   double* pq_cam;    // per camera p_j . q_j
   double* red_part;  // per-block partial sums of the camera-vector kernels, 6 x red_nb
@@ -116,6 +116,7 @@ void launch_schur_cam(const Dev& d, hipStream_t s);
 void launch_lin_final(const Dev& d, hipStream_t s);
 void launch_precond(const Dev& d, hipStream_t s);
 void launch_pcg_init(const Dev& d, hipStream_t s);
+void launch_pcg_pnext(const Dev& d, int it, hipStream_t s);
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s);
 void launch_pcg_cam(const Dev& d, hipStream_t s);
 void launch_pcg_q(const Dev& d, int it, hipStream_t s);

@@ -15,7 +15,14 @@ namespace {
 
 constexpr int kWave = 64;
 
-__device__ __forceinline__ void load_cam(const CamT* tab, int j, CamT& c) { c = tab[j]; }
+__device__ __forceinline__ void load_cam(const CamT* tab, int j, CamG& c) {
+  const double4* src = reinterpret_cast<const double4*>(tab + j);
+  const double4 a = src[0], b = src[1], e = src[2], f = src[3];
+  c.R[0] = a.x; c.R[1] = a.y; c.R[2] = a.z; c.R[3] = a.w;
+  c.R[4] = b.x; c.R[5] = b.y; c.R[6] = b.z; c.R[7] = b.w;
+  c.R[8] = e.x; c.t[0] = e.y; c.t[1] = e.z; c.t[2] = e.w;
+  c.f = f.x; c.k1 = f.y; c.k2 = f.z;
+}
 
 // ---------------------------------------------------------------- reductions
 
@@ -133,11 +140,19 @@ __device__ __forceinline__ void point_tile_reduce(const Dev& d, Op& op, int tile
 
 // ------------------------------------------------------------- camera table
 
+__device__ __forceinline__ void store_geometry(CamT* dst, const CamG& c) {
+  double4* o = reinterpret_cast<double4*>(dst);
+  o[0] = make_double4(c.R[0], c.R[1], c.R[2], c.R[3]);
+  o[1] = make_double4(c.R[4], c.R[5], c.R[6], c.R[7]);
+  o[2] = make_double4(c.R[8], c.t[0], c.t[1], c.t[2]);
+  o[3] = make_double4(c.f, c.k1, c.k2, 0.0);
+}
+
 __global__ void k_cam_prep(const double* __restrict__ cams, CamT* __restrict__ tab, int64_t nc) {
   const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (j >= nc) return;
   const double* c = cams + 9 * j;
-  CamT t;
+  CamG t;
   so3_exp(c[0], c[1], c[2], t.R);
   t.t[0] = c[3];
   t.t[1] = c[4];
@@ -145,8 +160,7 @@ __global__ void k_cam_prep(const double* __restrict__ cams, CamT* __restrict__ t
   t.f = c[6];
   t.k1 = c[7];
   t.k2 = c[8];
-  t.pad = 0.0;
-  tab[j] = t;
+  store_geometry(tab + j, t);
 }
 
 // ------------------------------------------------------------ linearisation
@@ -154,7 +168,7 @@ __global__ void k_cam_prep(const double* __restrict__ cams, CamT* __restrict__ t
 struct LinPtOp {
   const Dev& d;
   __device__ void compute(int s, int pt, double* v) {
-    CamT c;
+    CamG c;
     load_cam(d.tab, d.o_cam[s], c);
     Geo g;
     geo_eval(c, d.pts[3 * pt], d.pts[3 * pt + 1], d.pts[3 * pt + 2], g);
@@ -192,7 +206,7 @@ __global__ __launch_bounds__(kChunkBlock) void k_lin_cam(Dev d) {
   __shared__ double s_out[kLinCamVals];
   const int ch = blockIdx.x;
   const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
-  CamT c;
+  CamG c;
   load_cam(d.tab, d.chunk_cam[ch], c);
   double acc[kLinCamVals];
 #pragma unroll
@@ -245,6 +259,10 @@ __global__ void k_damp_pt(Dev d) {
     for (int k = 0; k < 3; ++k) g[k] = d.gp[3 * i + k];
   }
   const int diag[3] = {0, 3, 5};
+  // the camera-side PCG pass reads X and z of a point from one 64-byte record
+  d.prec[8 * i] = d.pts[3 * i];
+  d.prec[8 * i + 1] = d.pts[3 * i + 1];
+  d.prec[8 * i + 2] = d.pts[3 * i + 2];
 #pragma unroll
   for (int a = 0; a < 3; ++a) C[diag[a]] += d.lambda * fmax(C[diag[a]], d.diag_floor);
   if (!chol_packed<3>(C)) {
@@ -280,7 +298,7 @@ __global__ __launch_bounds__(kChunkBlock) void k_schur_cam(Dev d) {
   __shared__ double s_out[kSchurVals];
   const int ch = blockIdx.x;
   const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
-  CamT c;
+  CamG c;
   load_cam(d.tab, d.chunk_cam[ch], c);
   double acc[kSchurVals];
 #pragma unroll
@@ -399,35 +417,22 @@ __device__ __forceinline__ double block_sum(double v, double* s_buf) {
   return s_out[0];
 }
 
-// Search direction of iteration `it`: z + beta p_prev, p_prev being stored in
-// the buffer of the other parity.
-__device__ __forceinline__ double p_dir(const Dev& d, int it, double beta, int64_t e) {
-  return d.zc[e] + beta * d.pbuf[(int64_t)((it + 1) & 1) * 9 * d.nc + e];
-}
-
-// Point side of S p: zp_i = C~_i^-1 sum_{k in i} w Jp^T (Jc p_cam(k)), with
-// p_cam = z + beta p_prev formed per observation (MODE 0).  MODE 1
+// Point side of S p: z_i = C~_i^-1 sum_{k in i} w Jp^T (Jc p_cam(k)), stored in
+// the point record (MODE 0).  MODE 1
 // (back-substitution): dp_i = C~_i^-1 (-g_p,i - sum_k w Jp^T (Jc dc_cam(k))) and
 // the trial point.
 template <int MODE>
 struct PcgPtOp {
   const Dev& d;
   int it;
-  double beta;
   __device__ void compute(int s, int pt, double* v) {
     const int j = d.o_cam[s];
-    CamT c;
+    CamG c;
     load_cam(d.tab, j, c);
+    const double* xc = MODE == 0 ? d.pbuf + (int64_t)(it & 1) * 9 * d.nc + 9 * (int64_t)j
+                                 : d.x + 9 * (int64_t)j;
     Geo g;
     geo_eval(c, d.pts[3 * pt], d.pts[3 * pt + 1], d.pts[3 * pt + 2], g);
-    double xc[9];
-    if (MODE == 0) {
-#pragma unroll
-      for (int k = 0; k < 9; ++k) xc[k] = p_dir(d, it, beta, 9 * (int64_t)j + k);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 9; ++k) xc[k] = d.x[9 * (int64_t)j + k];
-    }
     double u0, u1;
     jc_apply(g, c.f, xc, u0, u1);
     const double w = d.w_pt[s];
@@ -445,9 +450,9 @@ struct PcgPtOp {
     const double z1 = Ci[1] * y0 + Ci[3] * y1 + Ci[4] * y2;
     const double z2 = Ci[2] * y0 + Ci[4] * y1 + Ci[5] * y2;
     if (MODE == 0) {
-      d.zp[3 * pt] = z0;
-      d.zp[3 * pt + 1] = z1;
-      d.zp[3 * pt + 2] = z2;
+      d.prec[8 * (int64_t)pt + 3] = z0;
+      d.prec[8 * (int64_t)pt + 4] = z1;
+      d.prec[8 * (int64_t)pt + 5] = z2;
     } else {
       d.dp[3 * pt] = z0;
       d.dp[3 * pt + 1] = z1;
@@ -460,7 +465,7 @@ struct PcgPtOp {
 };
 
 __global__ __launch_bounds__(kTile) void k_backsub(Dev d) {
-  PcgPtOp<1> op{d, 0, 0.0};
+  PcgPtOp<1> op{d, 0};
   point_tile_reduce<3>(d, op, blockIdx.x);
 }
 
@@ -514,6 +519,21 @@ __device__ __forceinline__ double block_sum_array_serial(const double* a, int n)
   return v;
 }
 
+// Wave-level sum: butterfly, then lane 0's value to every lane, so the result
+// has the same bits in every wavefront that adds the same data.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return __shfl(v, 0, kWave);
+}
+
+// Sum of n doubles (stride apart) by one wavefront, in a fixed order.
+__device__ __forceinline__ double wave_sum_array(const double* a, int n, int stride) {
+  double v = 0.0;
+  for (int k = threadIdx.x & (kWave - 1); k < n; k += kWave) v += a[(int64_t)k * stride];
+  return wave_sum(v);
+}
+
 // Sum of n doubles in index order by one block (fixed tree): every block that
 // calls it on the same data gets the same bits.
 __device__ __forceinline__ double block_sum_array(const double* a, int n, int stride,
@@ -538,11 +558,9 @@ __device__ __forceinline__ double block_sum_array(const double* a, int n, int st
 // All four return at once after the solve has stopped, so the host may queue
 // iterations past the stopping point.
 
-// Grid size of the camera-vector kernels: 7 cameras per wavefront.
-__host__ __device__ inline int cam_vector_blocks(int64_t nc) {
-  const int64_t waves = (nc + 6) / 7;
-  return (int)((waves + kTile / kWave - 1) / (kTile / kWave));
-}
+// Grid size of the camera-vector kernels: one wavefront per block, 7 cameras
+// per wavefront; their reductions are wavefront shuffles without barriers.
+__host__ __device__ inline int cam_vector_blocks(int64_t nc) { return (int)((nc + 6) / 7); }
 
 // Per-block partial-sum arrays of the camera-vector kernels (nb blocks each).
 __device__ __forceinline__ double* red_rr(const Dev& d, int par) { return d.red_part + 2 * par * d.red_nb; }
@@ -561,9 +579,8 @@ __device__ __forceinline__ void stop_pcg(const Dev& d, int iters, double res, do
   __threadfence_system();
 }
 
-__global__ __launch_bounds__(kTile) void k_pcg_init(Dev d) {
-  __shared__ double s_buf[kTile / kWave];
-  const int64_t wave = ((int64_t)blockIdx.x * kTile + threadIdx.x) / kWave;
+__global__ __launch_bounds__(kWave) void k_pcg_init(Dev d) {
+  const int64_t wave = blockIdx.x;
   const CamLane c = cam_lane(wave, d.nc);
   const int64_t e = 9 * c.j + c.a;
   const double r = c.on ? d.rhs[e] : 0.0;
@@ -578,8 +595,8 @@ __global__ __launch_bounds__(kTile) void k_pcg_init(Dev d) {
     rr = r * r;
     rz = r * z;
   }
-  rr = block_sum<kTile>(rr, s_buf);
-  rz = block_sum<kTile>(rz, s_buf);
+  rr = wave_sum(rr);
+  rz = wave_sum(rz);
   if (threadIdx.x == 0) {
     red_rr(d, 0)[blockIdx.x] = rr;
     red_rz(d, 0)[blockIdx.x] = rz;
@@ -592,34 +609,35 @@ __global__ __launch_bounds__(kTile) void k_pcg_init(Dev d) {
   }
 }
 
+// Start of iteration it: stop if it >= 1 and |r| <= tol |rhs| (or if rhs = 0),
+// else beta = rz_it / rz_{it-1} and p = z + beta p_prev (iteration 0 keeps the
+// p = z stored by the initialisation).
+__global__ __launch_bounds__(kWave) void k_pcg_pnext(Dev d, int it) {
+  if (d.pcg->done) return;
+  const double rhs_norm = sqrt(wave_sum_array(red_rhs(d), d.red_nb, 1));
+  if (it == 0) {
+    if (rhs_norm == 0.0 && blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, 0, 0.0, 0.0, 0);
+    return;
+  }
+  const double res = sqrt(wave_sum_array(red_rr(d, it & 1), d.red_nb, 1));
+  if (res <= d.tol * rhs_norm) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, it, res, rhs_norm, 0);
+    return;
+  }
+  const double rz_new = wave_sum_array(red_rz(d, it & 1), d.red_nb, 1);
+  const double rz_old = wave_sum_array(red_rz(d, (it + 1) & 1), d.red_nb, 1);
+  const double beta = rz_new / rz_old;
+  double* pnew = d.pbuf + (int64_t)(it & 1) * 9 * d.nc;
+  const double* pold = d.pbuf + (int64_t)((it + 1) & 1) * 9 * d.nc;
+  for (int64_t e = (int64_t)blockIdx.x * kWave + threadIdx.x; e < 9 * d.nc;
+       e += (int64_t)gridDim.x * kWave) {
+    pnew[e] = d.zc[e] + beta * pold[e];
+  }
+}
+
 __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
   if (d.pcg->done) return;
-  __shared__ double s_buf[kTile / kWave];
-  __shared__ double s_beta;
-  const double rhs_norm = sqrt(block_sum_array(red_rhs(d), d.red_nb, 1, s_buf));
-  double beta = 0.0;
-  if (it == 0) {
-    if (rhs_norm == 0.0) {
-      if (blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, 0, 0.0, 0.0, 0);
-      return;
-    }
-  } else {
-    const double res = sqrt(block_sum_array(red_rr(d, it & 1), d.red_nb, 1, s_buf));
-    if (res <= d.tol * rhs_norm) {
-      if (blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, it, res, rhs_norm, 0);
-      return;
-    }
-    const double rz_new = block_sum_array(red_rz(d, it & 1), d.red_nb, 1, s_buf);
-    const double rz_old = block_sum_array(red_rz(d, (it + 1) & 1), d.red_nb, 1, s_buf);
-    if (threadIdx.x == 0) s_beta = rz_new / rz_old;
-    __syncthreads();
-    beta = s_beta;
-    // store this iteration's direction for the camera-side kernels
-    for (int64_t e = (int64_t)blockIdx.x * kTile + threadIdx.x; e < 9 * d.nc;
-         e += (int64_t)gridDim.x * kTile)
-      d.pbuf[(int64_t)(it & 1) * 9 * d.nc + e] = p_dir(d, it, beta, e);
-  }
-  PcgPtOp<0> op{d, it, beta};
+  PcgPtOp<0> op{d, it};
   point_tile_reduce<3>(d, op, blockIdx.x);
 }
 
@@ -629,17 +647,19 @@ __global__ __launch_bounds__(kTile) void k_pcg_cam(Dev d) {
   __shared__ double s_out[9];
   const int ch = blockIdx.x;
   const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
-  CamT c;
+  CamG c;
   load_cam(d.tab, d.chunk_cam[ch], c);
   double acc[9];
 #pragma unroll
   for (int k = 0; k < 9; ++k) acc[k] = 0.0;
   for (int s = cb + threadIdx.x; s < ce; s += kTile) {
     const int i = d.c_pt[s];
+    const double4 a = *reinterpret_cast<const double4*>(d.prec + 8 * (int64_t)i);
+    const double2 b = *reinterpret_cast<const double2*>(d.prec + 8 * (int64_t)i + 4);
     Geo g;
-    geo_eval(c, d.pts[3 * i], d.pts[3 * i + 1], d.pts[3 * i + 2], g);
+    geo_eval(c, a.x, a.y, a.z, g);
     double t0, t1;
-    jp_apply(g, c.R, d.zp[3 * i], d.zp[3 * i + 1], d.zp[3 * i + 2], t0, t1);
+    jp_apply(g, c.R, a.w, b.x, b.y, t0, t1);
     const double w = d.w_cam[s];
     jct_acc(g, c.f, w * t0, w * t1, acc);
   }
@@ -647,10 +667,9 @@ __global__ __launch_bounds__(kTile) void k_pcg_cam(Dev d) {
   if (threadIdx.x < 9) d.pcg_part[(int64_t)ch * 9 + threadIdx.x] = s_out[threadIdx.x];
 }
 
-__global__ __launch_bounds__(kTile) void k_pcg_q(Dev d, int it) {
+__global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
   if (d.pcg->done) return;
-  __shared__ double s_buf[kTile / kWave];
-  const int64_t wave = ((int64_t)blockIdx.x * kTile + threadIdx.x) / kWave;
+  const int64_t wave = blockIdx.x;
   const CamLane c = cam_lane(wave, d.nc);
   const double* p = d.pbuf + (int64_t)(it & 1) * 9 * d.nc + 9 * c.j;
   const double* Bd = d.Bd + 45 * c.j;
@@ -665,14 +684,13 @@ __global__ __launch_bounds__(kTile) void k_pcg_q(Dev d, int it) {
     d.q[9 * c.j + c.a] = qa;
     pq = p[c.a] * qa;
   }
-  pq = block_sum<kTile>(pq, s_buf);
+  pq = wave_sum(pq);
   if (threadIdx.x == 0) red_pq(d)[blockIdx.x] = pq;
 }
 
-__global__ __launch_bounds__(kTile) void k_pcg_xr(Dev d, int it) {
+__global__ __launch_bounds__(kWave) void k_pcg_xr(Dev d, int it) {
   if (d.pcg->done) return;
-  __shared__ double s_buf[kTile / kWave];
-  const double pq = block_sum_array(red_pq(d), d.red_nb, 1, s_buf);
+  const double pq = wave_sum_array(red_pq(d), d.red_nb, 1);
   if (!(pq > 0.0) || !isfinite(pq)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       const double rhs_norm = sqrt(block_sum_array_serial(red_rhs(d), d.red_nb));
@@ -681,8 +699,8 @@ __global__ __launch_bounds__(kTile) void k_pcg_xr(Dev d, int it) {
     }
     return;
   }
-  const double alpha = block_sum_array(red_rz(d, it & 1), d.red_nb, 1, s_buf) / pq;
-  const int64_t wave = ((int64_t)blockIdx.x * kTile + threadIdx.x) / kWave;
+  const double alpha = wave_sum_array(red_rz(d, it & 1), d.red_nb, 1) / pq;
+  const int64_t wave = blockIdx.x;
   const CamLane c = cam_lane(wave, d.nc);
   const int64_t e = 9 * c.j + c.a;
   double r = 0.0;
@@ -698,8 +716,8 @@ __global__ __launch_bounds__(kTile) void k_pcg_xr(Dev d, int it) {
     rr = r * r;
     rz = r * z;
   }
-  rr = block_sum<kTile>(rr, s_buf);
-  rz = block_sum<kTile>(rz, s_buf);
+  rr = wave_sum(rr);
+  rz = wave_sum(rz);
   if (threadIdx.x == 0) {
     red_rr(d, (it + 1) & 1)[blockIdx.x] = rr;
     red_rz(d, (it + 1) & 1)[blockIdx.x] = rz;
@@ -708,12 +726,10 @@ __global__ __launch_bounds__(kTile) void k_pcg_xr(Dev d, int it) {
 
 // After the last queued iteration: record the outcome if the solve ran to the
 // iteration limit (a stop inside the loop has already been recorded).
-__global__ __launch_bounds__(kTile) void k_pcg_final(Dev d, int iters) {
-  __shared__ double s_buf[kTile / kWave];
+__global__ __launch_bounds__(kWave) void k_pcg_final(Dev d, int iters) {
   if (d.pcg->done) return;
-  const double rhs_norm = sqrt(block_sum_array(red_rhs(d), d.red_nb, 1, s_buf));
-  const double res = iters == 0 ? rhs_norm
-                                : sqrt(block_sum_array(red_rr(d, iters & 1), d.red_nb, 1, s_buf));
+  const double rhs_norm = sqrt(wave_sum_array(red_rhs(d), d.red_nb, 1));
+  const double res = iters == 0 ? rhs_norm : sqrt(wave_sum_array(red_rr(d, iters & 1), d.red_nb, 1));
   if (threadIdx.x == 0) stop_pcg(d, iters, res, rhs_norm, 0);
 }
 
@@ -763,7 +779,7 @@ __global__ void k_retract(Dev d) {
   o[2] = k * qz;
 #pragma unroll
   for (int a = 3; a < 9; ++a) o[a] = c[a] + dx[a];
-  CamT t;
+  CamG t;
   so3_exp(o[0], o[1], o[2], t.R);
   t.t[0] = o[3];
   t.t[1] = o[4];
@@ -771,8 +787,7 @@ __global__ void k_retract(Dev d) {
   t.f = o[6];
   t.k1 = o[7];
   t.k2 = o[8];
-  t.pad = 0.0;
-  d.tab_trial[j] = t;
+  store_geometry(d.tab_trial + j, t);
 }
 
 __global__ __launch_bounds__(256) void k_cost(Dev d, const double* __restrict__ pts,
@@ -783,7 +798,7 @@ __global__ __launch_bounds__(256) void k_cost(Dev d, const double* __restrict__ 
   double acc = 0.0;
   for (int64_t s = b0 + threadIdx.x; s < b1; s += 256) {
     const int i = d.o_pt[s];
-    CamT c;
+    CamG c;
     load_cam(tab, d.o_cam[s], c);
     Geo g;
     geo_eval(c, pts[3 * i], pts[3 * i + 1], pts[3 * i + 2], g);
@@ -816,7 +831,7 @@ __global__ void k_debug_obs(Dev d, const int32_t* __restrict__ perm_pt, double* 
   const int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (s >= d.nobs) return;
   const int pt = d.o_pt[s];
-  CamT c;
+  CamG c;
   load_cam(d.tab, d.o_cam[s], c);
   Geo g;
   geo_eval(c, d.pts[3 * pt], d.pts[3 * pt + 1], d.pts[3 * pt + 2], g);
@@ -924,20 +939,23 @@ void launch_precond(const Dev& d, hipStream_t s) {
   if (d.nc > 0) k_precond<<<blocks_for(d.nc, 64), 64, 0, s>>>(d);
 }
 void launch_pcg_init(const Dev& d, hipStream_t s) {
-  k_pcg_init<<<cam_vector_blocks(d.nc), kTile, 0, s>>>(d);
+  k_pcg_init<<<cam_vector_blocks(d.nc), kWave, 0, s>>>(d);
+}
+void launch_pcg_pnext(const Dev& d, int it, hipStream_t s) {
+  k_pcg_pnext<<<cam_vector_blocks(d.nc), kWave, 0, s>>>(d, it);
 }
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
-  k_pcg_pt<<<d.n_tiles > 0 ? d.n_tiles : 1, kTile, 0, s>>>(d, it);
+  if (d.n_tiles > 0) k_pcg_pt<<<d.n_tiles, kTile, 0, s>>>(d, it);
 }
 void launch_pcg_cam(const Dev& d, hipStream_t s) { k_pcg_cam<<<d.n_chunks, kTile, 0, s>>>(d); }
 void launch_pcg_q(const Dev& d, int it, hipStream_t s) {
-  k_pcg_q<<<cam_vector_blocks(d.nc), kTile, 0, s>>>(d, it);
+  k_pcg_q<<<cam_vector_blocks(d.nc), kWave, 0, s>>>(d, it);
 }
 void launch_pcg_xr(const Dev& d, int it, hipStream_t s) {
-  k_pcg_xr<<<cam_vector_blocks(d.nc), kTile, 0, s>>>(d, it);
+  k_pcg_xr<<<cam_vector_blocks(d.nc), kWave, 0, s>>>(d, it);
 }
 void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
-  k_pcg_final<<<1, kTile, 0, s>>>(d, iters);
+  k_pcg_final<<<1, kWave, 0, s>>>(d, iters);
 }
 int pcg_red_blocks(int64_t nc) { return cam_vector_blocks(nc); }
 void launch_backsub(const Dev& d, hipStream_t s) {

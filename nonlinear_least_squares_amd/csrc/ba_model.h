@@ -23,6 +23,13 @@ struct alignas(128) CamT {
   double f, k1, k2, pad;
 };
 
+// Geometry part of a camera table entry, as the kernels hold it in registers.
+struct CamG {
+  double R[9];
+  double t[3];
+  double f, k1, k2;
+};
+
 // Geometry of one observation at the current parameters.
 struct Geo {
   double q0, q1, q2;                     // R X
@@ -31,7 +38,7 @@ struct Geo {
   double u0, u1;                         // predicted pixel
 };
 
-__device__ __forceinline__ void geo_eval(const CamT& c, double X0, double X1, double X2, Geo& g) {
+__device__ __forceinline__ void geo_eval(const CamG& c, double X0, double X1, double X2, Geo& g) {
   g.q0 = c.R[0] * X0 + c.R[1] * X1 + c.R[2] * X2;
   g.q1 = c.R[3] * X0 + c.R[4] * X1 + c.R[5] * X2;
   g.q2 = c.R[6] * X0 + c.R[7] * X1 + c.R[8] * X2;
