@@ -3,7 +3,8 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The GPU library never loads it and shares
 no code with it.  The arithmetic lives in ``ba_oracle.c`` (plain C loops, fp64)
-and ``droid_oracle.c``; this module only builds and marshals.
+and ``droid_oracle.c`` (dense frame-graph BA, wrapped by ``oracle.droid``);
+this module only builds and marshals.
 
 Parity status: every function is pinned by tests in ``tests/test_oracle_*.py``
 (finite differences, dense solves, library routines, closed forms and
@@ -119,6 +120,8 @@ def _droid_signatures(L):
     L.dorc_size.argtypes = [vp, C.c_int]
     L.dorc_size.restype = C.c_int64
     L.dorc_residual_one.argtypes = [dp, dp, dp, dp, C.c_double, dp, dp, dp, dp, dp]
+    L.dorc_pose_matrix.argtypes = [vp, C.c_int, dp]
+    L.dorc_se3_exp.argtypes = [dp, dp, dp]
 
 
 def _p(a, ctype=C.c_double):
