@@ -10,6 +10,12 @@ relative residual.  Inputs are resident in HBM before the timed region.
 Prints one JSON line.  The roofline object refers to the kernel with the
 largest total time in a profiled warm-up run; its average launch time is
 taken with HIP events on the library's stream during the timed region.
+
+``--workload dense`` measures the fp32 dense frame-graph variant instead
+(libdba): a step is one Gauss-Newton iteration (linearise, assemble with the
+depths eliminated, Cholesky of the 84 x 84 reduced pose system, depth
+back-substitution, retraction) of the 16-keyframe scene with 48 x 64
+inverse-depth maps and 64 edges (196,608 residuals).
 """
 import argparse
 import hashlib
@@ -96,18 +102,110 @@ def cpu_baseline(sc, n_iters=3):
                       f"single-threaded C oracle, {dt:.1f} s"}
 
 
+DENSE_METRIC = "Gauss-Newton iterations/s (fp32, 1 GPU); % of fp32 vector roofline"
+FP32_PEAK_TFLOPS = 157.3
+
+
+def dense_flops_per_lin(sc):
+    """Algorithmic fp32 flops of one linearisation launch: per residual the
+    image model, the three Jacobian blocks, sqrt(w) scaling and its depth
+    terms (169); per pixel with out-degree d the B and g_c contributions of
+    its d edges (360 each) and the Schur outer product over 1 + d pose slots
+    (6 (1 + d) (6 (1 + d) + 1) + 12 (1 + d) + 31)."""
+    E, P = len(sc["edges"]), sc["height"] * sc["width"]
+    deg = __import__("numpy").bincount(sc["edges"][:, 0], minlength=len(sc["poses"]))
+    per_pixel = 0
+    for d in deg[deg > 0]:
+        m = 6 * (1 + int(d))
+        per_pixel += int(d) * 360 + m * (m + 1) + 2 * m + 31
+    return 169 * E * P + per_pixel * P
+
+
+def dense_cpu_baseline(sc, budget_s=10.0):
+    """The oracle as it stands (plain C, one thread): Gauss-Newton steps of
+    the same scene from the same start until about budget_s has passed."""
+    from oracle import droid as odroid
+    O = odroid.DroidProblem.from_scene(sc)
+    t0 = time.perf_counter()
+    n = 0
+    while n < sc["n_iters"] or time.perf_counter() - t0 < budget_s:
+        O.gn_step()
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "GN iterations/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} Gauss-Newton steps of the same scene from the same start, "
+                      f"single-threaded C oracle (fp64), {dt:.1f} s"}
+
+
+def main_dense(args):
+    import numpy as np
+    import torch
+    from nonlinear_least_squares_amd import dba
+    from synthetic import droid_scene
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sc = droid_scene()
+    E, P, n = len(sc["edges"]), sc["height"] * sc["width"], len(sc["poses"])
+    warm = dba.Problem.from_scene(sc)
+    warm.profile()
+    warm.solve(max(args.warmup, 1) * sc["n_iters"])
+    prof = warm.profile_get()
+    warm.close()
+    dominant = max(prof, key=lambda k: prof[k][1])
+    print(f"# warm-up kernel totals (launches, ms): {prof}", file=sys.stderr, flush=True)
+
+    G = dba.Problem.from_scene(sc)
+    G.profile([dominant])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    costs = G.solve(args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    launches, kms = G.profile_get()[dominant]
+    value = args.steps / dt
+    roof = None
+    if dominant == "lin" and launches:
+        avg_s = kms / launches / 1e3
+        fl = dense_flops_per_lin(sc)
+        ach = fl / avg_s / 1e12
+        roof = {"bound": "alu", "achieved": round(ach, 2), "peak": FP32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP32_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": dominant, "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches,
+                "algorithmic_flops_per_launch": fl}
+    out = {
+        "metric": DENSE_METRIC, "value": round(value, 2), "unit": "GN iterations/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * dt / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"dense frame-graph BA: {n} keyframes, {sc['height']}x"
+                               f"{sc['width']} inverse depths, {E} edges ({E * P} residuals), "
+                               f"{sc['n_fixed']} fixed poses",
+                   "n_frames": n, "n_edges": E, "n_residuals": E * P},
+        "residuals_per_s": round(value * E * P, 1),
+        "cost_first": float(costs[0]), "cost_last": float(costs[-1]),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = dense_cpu_baseline(sc)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="large")
+    ap.add_argument("--workload", choices=["ba", "dense"], default="ba")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "dense":
+        return main_dense(args)
 
     import torch
     from nonlinear_least_squares_amd import ba

@@ -6,4 +6,4 @@ bundle adjustment as hand-written gfx950 HIP kernels; ``libdba.so``
 here only marshal arguments.
 """
 
-from . import ba  # noqa: F401
+from . import ba, dba  # noqa: F401
