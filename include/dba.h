@@ -135,8 +135,8 @@ int dba_debug_get(dba_problem* h, int which, void* host_out, int64_t bytes);
 
 enum {
   DBA_K_LIN = 0,   /* back-substitution of the previous step, linearisation, Schur partials */
-  DBA_K_REDUCE,    /* sum of the partials over pixel ranges                                  */
-  DBA_K_SOLVE,     /* assembly, Cholesky, triangular solves, retraction                      */
+  DBA_K_ASSEMBLE,  /* reduced pose system and right-hand side from the partials, cost       */
+  DBA_K_SOLVE,     /* Cholesky, triangular solves, retraction                                */
   DBA_K_COST,      /* back-substitution of the last step and cost                            */
   DBA_K_NUM
 };

@@ -44,8 +44,9 @@ constexpr int kSub = 64;                  // pixels per sub-tile (one per lane i
 constexpr int kThreads = 256;             // threads of the linearisation block
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxDeg = 8;                // out-edges per frame
-constexpr int kTPW = 5;                   // tasks per wave per pass
-constexpr int kMaxTasks = 2 * kMaxDeg + 1 + kMaxDeg + kMaxDeg * (kMaxDeg - 1) / 2;
+constexpr int kTPW = 4;                   // tasks per wave per pass
+constexpr int kMaxTasks = 1 + 2 * kMaxDeg + kMaxDeg * (kMaxDeg - 1) / 2;
+constexpr int kMaxPairs = 2 * kMaxDeg + 1;
 constexpr int kMaxPasses = (kMaxTasks + kWaves * kTPW - 1) / (kWaves * kTPW);
 constexpr int kRec = 36;                  // floats per task record
 constexpr int kRedPitch = 65;
@@ -78,7 +79,7 @@ struct Group {
 
 struct Task {
   int diag, npairs;
-  int pair[3];
+  int pair[kMaxPairs];
 };
 
 struct Unit {
@@ -182,22 +183,11 @@ __device__ __forceinline__ float wave_sum_parts(const float* parts, int n) {
   return xor_sum(s);
 }
 
-// Depth step of pixel p of the group's frame from the stored coupling:
-// dd = -(g_d + col . dxi) / C, slots in fixed order.
-__device__ __forceinline__ float depth_step(const Group& g, const float* fstore, const float* estore,
-                                            const float* dx, int p, int64_t P) {
-  const float* fs = fstore + (int64_t)g.frame * 8 * P + p;
-  const float C = fs[0];
-  float s = fs[P];
-#pragma unroll
-  for (int c = 0; c < 6; ++c) s += fs[(2 + c) * P] * dx[c];
-  for (int l = 0; l < g.deg; ++l) {
-    const float* es = estore + (int64_t)g.edge[l] * 6 * P + p;
-#pragma unroll
-    for (int c = 0; c < 6; ++c) s += es[c * P] * dx[6 * (1 + l) + c];
-  }
-  return C > 0.0f ? -s / C : 0.0f;
-}
+// Items of one sub-tile: (slot, pixel) for the depth back-substitution
+// (slot 0 = the frame's own coupling C, g_d, col_i; slot 1 + l = col_j of
+// edge l) and (edge, pixel) for the linearisation, 64 pixels per slot.
+constexpr int kBsItems = (kMaxDeg + 1) * kSub / kThreads + ((kMaxDeg + 1) * kSub % kThreads ? 1 : 0);
+constexpr int kLinItems = kMaxDeg * kSub / kThreads;
 
 template <bool BACKSUB, bool LIN>
 __global__ __launch_bounds__(kThreads) void k_lin(LinArgs a) {
@@ -211,8 +201,8 @@ __global__ __launch_bounds__(kThreads) void k_lin(LinArgs a) {
   float* fac = sm;
   float* rel = sm + fac_size;                 // kMaxDeg x 12
   float* dx = rel + kMaxDeg * 12;             // (kMaxDeg + 1) x 6
-  float* dep = dx + (kMaxDeg + 1) * 6;        // kSub
-  float* wsum = dep + kSub;                   // kWaves
+  float* bs = dx + (kMaxDeg + 1) * 6;         // (kMaxDeg + 2) x kSub: C, slot parts, old depth
+  float* wsum = bs + (kMaxDeg + 3) * kSub;    // kWaves
 
   if (tid < d) {
     rel_pose(a.poseRt + 16 * frame, a.poseRt + 16 * g.slot_frame[1 + tid], rel + 12 * tid);
@@ -220,6 +210,9 @@ __global__ __launch_bounds__(kThreads) void k_lin(LinArgs a) {
   if (BACKSUB && tid < 6 * (d + 1)) dx[tid] = a.dxi[6 * g.slot_frame[tid / 6] + tid % 6];
   const bool apply = BACKSUB && *a.status == 0;
   __syncthreads();
+  float* bsC = bs;                     // C of each pixel
+  float* bsD = bs + kSub;              // depth before the update
+  float* bsS = bs + 2 * kSub;          // slot parts of g_d + col . dxi
 
   float cost = 0.0f;
   float acc[kTPW][kRec];
@@ -231,38 +224,73 @@ __global__ __launch_bounds__(kThreads) void k_lin(LinArgs a) {
 #pragma unroll
         for (int e = 0; e < kRec; ++e) acc[k][e] = 0.0f;
     }
+    const bool upd = apply && pass == 0;
     for (int sub = u.pix_begin; sub < u.pix_end; sub += kSub) {
       const int npx = min(kSub, u.pix_end - sub);
-      // phase 0: depths of the sub-tile, with the previous step applied
-      if (tid < kSub) {
-        float dv = 0.0f;
-        if (tid < npx) {
-          const int p = sub + tid;
-          const int64_t idx = (int64_t)frame * P + p;
-          dv = a.depth[idx];
-          if (apply && pass == 0) {
-            const float step = depth_step(g, a.fstore, a.estore, dx, p, P);
-            dv = dv + step;
-            a.depth[idx] = dv;
-            a.dd_out[idx] = step;
-          }
+      // every global load of the sub-tile first: targets and weights of the
+      // (edge, pixel) items, then depths and stored coupling of the slots
+      float2 tgv[kLinItems];
+      float wv[kLinItems];
+#pragma unroll
+      for (int m = 0; m < kLinItems; ++m) {
+        const int it = tid + m * kThreads, l = it >> 6, pl = it & 63;
+        tgv[m] = make_float2(0.0f, 0.0f);
+        wv[m] = 0.0f;
+        if (l < d && pl < npx) {
+          const int64_t ep = (int64_t)g.edge[l] * P + sub + pl;
+          tgv[m] = reinterpret_cast<const float2*>(a.targets)[ep];
+          wv[m] = a.weights[ep];
         }
-        dep[tid] = dv;
+      }
+#pragma unroll
+      for (int m = 0; m < kBsItems; ++m) {
+        const int it = tid + m * kThreads, sl = it >> 6, pl = it & 63;
+        if (sl > d || pl >= npx) continue;
+        const int p = sub + pl;
+        if (sl == 0) {
+          bsD[pl] = a.depth[(int64_t)frame * P + p];
+          if (upd) {
+            const float* fs = a.fstore + (int64_t)frame * 8 * P + p;
+            bsC[pl] = fs[0];
+            float v = fs[P];
+#pragma unroll
+            for (int c = 0; c < 6; ++c) v += fs[(2 + c) * P] * dx[c];
+            bsS[pl] = v;
+          }
+        } else if (upd) {
+          const float* es = a.estore + (int64_t)g.edge[sl - 1] * 6 * P + p;
+          float v = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 6; ++c) v += es[c * P] * dx[6 * sl + c];
+          bsS[sl * kSub + pl] = v;
+        }
       }
       __syncthreads();
-      // phase 1: one (edge, pixel) item per thread
-      for (int it = tid; it < d * kSub; it += kThreads) {
-        const int l = uniform(it >> 6), pl = it & 63;
+      // phase 1: depth after the previous step (redundantly per edge, same
+      // arithmetic everywhere), then one (edge, pixel) item per thread
+#pragma unroll
+      for (int m = 0; m < kLinItems; ++m) {
+        const int it = tid + m * kThreads, l = uniform(it >> 6), pl = it & 63;
+        if (l >= d) continue;
         if (pl < npx) {
           const int p = sub + pl;
-          const int e = g.edge[l];
-          const int64_t ep = (int64_t)e * P + p;
-          const float2 tg = reinterpret_cast<const float2*>(a.targets)[ep];
-          const float w = a.weights[ep];
+          float dv = bsD[pl];
+          if (upd) {
+            float sv = bsS[pl];
+            for (int s2 = 1; s2 <= d; ++s2) sv += bsS[s2 * kSub + pl];
+            const float C = bsC[pl];
+            const float step = C > 0.0f ? -sv / C : 0.0f;
+            dv = dv + step;
+            if (l == 0) {
+              const int64_t idx = (int64_t)frame * P + p;
+              a.depth[idx] = dv;
+              a.dd_out[idx] = step;
+            }
+          }
           PixOut o;
           pix_eval<LIN>(rel + 12 * l, a.fx, a.fy, a.cx, a.cy, a.ifx, a.ify, (float)(p % a.W),
-                        (float)(p / a.W), dep[pl], tg.x, tg.y, o);
-          const float sw = sqrtf(w);
+                        (float)(p / a.W), dv, tgv[m].x, tgv[m].y, o);
+          const float sw = sqrtf(wv[m]);
           const float sr0 = sw * o.r0, sr1 = sw * o.r1;
           if (pass == 0) cost += sr0 * sr0 + sr1 * sr1;
           if constexpr (LIN) {
@@ -402,17 +430,91 @@ __global__ __launch_bounds__(kThreads) void k_lin(LinArgs a) {
   }
 }
 
-// Sum of each task's records over the blocks of its group, in block order.
-__global__ void k_reduce(const Group* groups, const int* task_group, const float* partial,
-                         float* tasksum, int n_total) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_total * kRec) return;
-  const int gt = i / kRec, e = i % kRec;
-  const Group& g = groups[task_group[gt]];
-  const int local = gt - g.task_begin;
-  float s = 0.0f;
-  for (int u = 0; u < g.n_units; ++u) s += partial[(int64_t)(g.rec_begin + u * g.n_tasks + local) * kRec + e];
-  tasksum[i] = s;
+// One contribution of a task to an entry of the reduced system: the task's
+// record of pixel-range block u sits at partial[(rec0 + u * stride) * 36].
+struct Contrib {
+  int rec0, stride, mode, pad;   // mode: 0 as is, 1 transposed, 2 plus transpose, 3 packed symmetric
+};
+
+constexpr int kAsmLanes = 32;
+
+struct AsmArgs {
+  const float* partial;
+  const int* blk_ab;       // upper 6x6 blocks (A, B), A <= B, of the reduced system
+  const int* blk_ptr;      // contributions of each block
+  const Contrib* blk_ent;
+  const int* rhs_ptr;      // contributions to each free frame's right-hand side (entries 21..26)
+  const Contrib* rhs_ent;
+  const float* cost_part;
+  float* S;                // nv x nv, both triangles
+  float* rhs;              // nv
+  float* costs;
+  int n_upper, nv, n_units, units_per_group, cost_slot;
+};
+
+// Reduced system from the blocks' partial records.  32 lanes share one
+// entry (of an upper 6x6 block, then of the right-hand side): lane j takes
+// the (contribution, pixel-range block) pairs j, j + 32, ... and the lanes'
+// sums meet in a fixed butterfly.  The last block's first wave sums the cost
+// partials.
+__global__ void k_assemble(AsmArgs a) {
+  if (blockIdx.x == gridDim.x - 1) {
+    if (a.cost_slot >= 0 && threadIdx.x < 64) {
+      const float c = wave_sum_parts(a.cost_part, a.n_units);
+      if (threadIdx.x == 0) a.costs[a.cost_slot] = 0.5f * c;
+    }
+    return;
+  }
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int item = gid / kAsmLanes, ln = gid % kAsmLanes;
+  const int NU = a.units_per_group;
+  const bool is_blk = item < a.n_upper * kRec;
+  const int k = item - a.n_upper * kRec;
+  if (!is_blk && k >= a.nv) return;   // whole 32-lane groups leave together
+  int q0, q1, i0, i1 = -1, A, B, r, c;
+  const Contrib* ents;
+  if (is_blk) {
+    const int bi = item / kRec, e = item % kRec;
+    r = e / 6;
+    c = e % 6;
+    A = a.blk_ab[2 * bi];
+    B = a.blk_ab[2 * bi + 1];
+    q0 = a.blk_ptr[bi];
+    q1 = a.blk_ptr[bi + 1];
+    ents = a.blk_ent;
+  } else {
+    A = k / 6;
+    r = k % 6;
+    B = c = 0;
+    q0 = a.rhs_ptr[A];
+    q1 = a.rhs_ptr[A + 1];
+    ents = a.rhs_ent;
+  }
+  float v = 0.0f;
+  for (int pidx = ln; pidx < (q1 - q0) * NU; pidx += kAsmLanes) {
+    const Contrib ct = ents[q0 + pidx / NU];
+    const float* rec = a.partial + (int64_t)(ct.rec0 + (pidx % NU) * ct.stride) * kRec;
+    if (!is_blk) {
+      v += rec[21 + r];
+      continue;
+    }
+    switch (ct.mode) {
+      case 0: i0 = 6 * r + c; break;
+      case 1: i0 = 6 * c + r; break;
+      case 2: i0 = 6 * r + c; i1 = 6 * c + r; break;
+      default: i0 = sym6(min(r, c), max(r, c)); break;
+    }
+    v += ct.mode == 2 ? rec[i0] + rec[i1] : rec[i0];
+  }
+#pragma unroll
+  for (int m = kAsmLanes / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kAsmLanes);
+  if (ln != 0) return;
+  if (is_blk) {
+    a.S[(6 * A + r) * a.nv + 6 * B + c] = v;
+    if (A != B) a.S[(6 * B + c) * a.nv + 6 * A + r] = v;
+  } else {
+    a.rhs[k] = v;
+  }
 }
 
 __global__ void k_cost_final(const float* cost_part, int n_units, float* costs, int slot) {
@@ -505,137 +607,181 @@ __global__ void k_validate(const float* depth, int64_t nd, const float* targets,
 }
 
 struct SolveArgs {
-  const float* tasksum;
-  const int* blk_ptr;   // nfree * nfree + 1, block (A, B) with A <= B at A * nfree + B
-  const int* blk_ent;   // task << 2 | mode
-  const int* rhs_ptr;   // nfree + 1
-  const int* rhs_ent;   // task
-  const float* cost_part;
-  int n_units;
-  float* costs;
-  int cost_slot;
-  float* S_dbg;
-  float* rhs_dbg;
+  const float* S;       // nv x nv
+  const float* rhs;     // nv
   float* dxi;
   float* pose7;
   float* poseRt;
   int* status;
-  int n, nf, nv, assemble_only;
+  int n, nf, nv;
 };
 
-__device__ __forceinline__ float rd_lane(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+__host__ __device__ constexpr int tri6(int i, int j) { return i * (i + 1) / 2 + j; }
+
+constexpr int kMaxNv = 6 * kMaxFree;
+constexpr int kSolveLoads = (kMaxNv * kMaxNv + kSolveThreads - 1) / kSolveThreads;
+
+// Cholesky of the 6x6 diagonal block at (k0, k0) in place (lower triangle),
+// reciprocals of its diagonal to Ld; *flag = 1 if a pivot is not positive.
+__device__ void factor6(float* S, int pitch, int k0, float* Ld, int* flag) {
+  float L[21], id[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i)
+#pragma unroll
+    for (int j = 0; j <= i; ++j) L[tri6(i, j)] = S[(k0 + i) * pitch + k0 + j];
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    float dj = L[tri6(j, j)];
+#pragma unroll
+    for (int l = 0; l < j; ++l) dj -= L[tri6(j, l)] * L[tri6(j, l)];
+    ok = ok && dj > 0.0f && isfinite(dj);
+    id[j] = __builtin_amdgcn_rsqf(dj);    // 1 / L_jj
+    L[tri6(j, j)] = dj * id[j];
+#pragma unroll
+    for (int i = j + 1; i < 6; ++i) {
+      float t = L[tri6(i, j)];
+#pragma unroll
+      for (int l = 0; l < j; ++l) t -= L[tri6(i, l)] * L[tri6(j, l)];
+      L[tri6(i, j)] = t * id[j];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+#pragma unroll
+    for (int j = 0; j <= i; ++j) S[(k0 + i) * pitch + k0 + j] = L[tri6(i, j)];
+    Ld[k0 + i] = id[i];
+  }
+  if (!ok) *flag = 1;
 }
 
-// Assembly of the reduced system from the task sums, Cholesky (right-looking,
-// L below the diagonal kept in the upper triangle so that the column being
-// read is never written in the same step), triangular solves by one wave
-// (row values in registers, the pivot row broadcast by readlane), retraction.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Cholesky of the reduced pose system in LDS by 6x6 blocks (one pose per
+// block) with the right-hand side as an extra row, so that the factor's last
+// row is L^-1 rhs (the forward solve).  Per block column K: each row below
+// solves its 6 panel entries against L_KK, then waves 1.. update the
+// trailing matrix while wave 0 updates and factors the next diagonal block
+// (look-ahead); two barriers per block column.  The backward solve
+// L^T x = y goes block by block (every thread forms x_K, one barrier each).
+// Then the retraction of the free poses.
 __global__ __launch_bounds__(kSolveThreads) void k_solve(SolveArgs a) {
   extern __shared__ float sm[];
-  const int nv = a.nv, pitch = nv + 1, nfree = nv / 6;
-  const int tid = threadIdx.x, bd = blockDim.x;
-  float* S = sm;
-  float* Ld = S + nv * pitch;
-  float* xs = Ld + nv + 1;
-  int* flag = reinterpret_cast<int*>(xs + nv + 1);
+  const int nv = a.nv, pitch = nv + 1, nb = nv / 6;
+  const int tid = threadIdx.x, bd = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  float* S = sm;                          // (nv + 1) x pitch, row nv = rhs
+  float* Pn = S + (nv + 1) * pitch;       // (nv - 5) x 6 panel
+  float* Ld = Pn + 6 * max(nv - 5, 0);    // nv reciprocals of the factor's diagonal
+  float* xs = Ld + nv;                    // nv
+  float* xo = xs + nv;                    // nv
+  int* flag = reinterpret_cast<int*>(xo + nv);
 
-  if (!a.assemble_only && tid < 64) {
-    const float c = wave_sum_parts(a.cost_part, a.n_units);
-    if (tid == 0) a.costs[a.cost_slot] = 0.5f * c;
+  {
+    float v[kSolveLoads];
+#pragma unroll
+    for (int m = 0; m < kSolveLoads; ++m) {
+      const int e = tid + m * kSolveThreads;
+      v[m] = e < nv * nv ? a.S[e] : 0.0f;
+    }
+    const float rv = tid < nv ? a.rhs[tid] : 0.0f;
+#pragma unroll
+    for (int m = 0; m < kSolveLoads; ++m) {
+      const int e = tid + m * kSolveThreads;
+      if (e < nv * nv) S[(e / nv) * pitch + e % nv] = v[m];
+    }
+    if (tid < nv) S[nv * pitch + tid] = rv;
   }
   if (tid == 0) *flag = 0;
-  for (int e = tid; e < nv * nv; e += bd) {
-    const int R = e / nv, Cc = e % nv;
-    int A = R / 6, r = R % 6, B = Cc / 6, c = Cc % 6;
-    if (A > B) {
-      int tmp = A; A = B; B = tmp;
-      tmp = r; r = c; c = tmp;
-    }
-    const int bi = A * nfree + B;
-    float v = 0.0f;
-    for (int q = a.blk_ptr[bi]; q < a.blk_ptr[bi + 1]; ++q) {
-      const int ent = a.blk_ent[q];
-      const float* rec = a.tasksum + (int64_t)(ent >> 2) * kRec;
-      switch (ent & 3) {
-        case 0: v += rec[6 * r + c]; break;
-        case 1: v += rec[6 * c + r]; break;
-        case 2: v += rec[6 * r + c] + rec[6 * c + r]; break;
-        default: v += rec[sym6(min(r, c), max(r, c))]; break;
-      }
-    }
-    S[R * pitch + Cc] = v;
-    a.S_dbg[R * nv + Cc] = v;
-  }
-  for (int e = tid; e < nv; e += bd) {
-    const int A = e / 6, r = e % 6;
-    float v = 0.0f;
-    for (int q = a.rhs_ptr[A]; q < a.rhs_ptr[A + 1]; ++q) v += a.tasksum[(int64_t)a.rhs_ent[q] * kRec + 21 + r];
-    xs[e] = v;
-    a.rhs_dbg[e] = v;
-  }
   __syncthreads();
-  if (a.assemble_only) return;
   const bool prior_fail = *a.status != 0;
-  if (!prior_fail) {
-    for (int k = 0; k < nv; ++k) {
-      const float piv = S[k * pitch + k];
-      if (!(piv > 0.0f) || !isfinite(piv)) {
-        if (tid == 0) *flag = 1;
-        break;
+  if (!prior_fail && nb > 0) {
+    if (tid == 0) factor6(S, pitch, 0, Ld, flag);
+    __syncthreads();
+    for (int K = 0; K < nb; ++K) {
+      if (*flag) break;
+      const int k0 = 6 * K, m = nv - k0 - 6, mr = m + 1;   // rows below, with the rhs row
+      for (int t = tid; t < mr; t += bd) {
+        const float* ar = S + (k0 + 6 + t) * pitch + k0;
+        float l[6];
+#pragma unroll
+        for (int c = 0; c < 6; ++c) {
+          float v = ar[c];
+#pragma unroll
+          for (int q = 0; q < c; ++q) v -= l[q] * S[(k0 + c) * pitch + k0 + q];
+          l[c] = v * Ld[k0 + c];
+        }
+#pragma unroll
+        for (int c = 0; c < 6; ++c) Pn[6 * t + c] = l[c];
       }
-      const float lkk = sqrtf(piv), ipiv = 1.0f / piv;
-      const int m = nv - k - 1;
-      for (int t = tid; t < m * m; t += bd) {
-        const int i = k + 1 + t / m, j = k + 1 + t % m;
-        if (j <= i) S[i * pitch + j] -= S[i * pitch + k] * S[j * pitch + k] * ipiv;
+      __syncthreads();
+      if (wave == 0) {
+        if (K + 1 < nb) {
+          if (lane < 21) {
+            int r = 0;
+            while (tri6(r + 1, 0) <= lane) ++r;
+            const int c = lane - tri6(r, 0);
+            float* sp = S + (k0 + 6 + r) * pitch + k0 + 6 + c;
+            float v = *sp;
+#pragma unroll
+            for (int q = 0; q < 6; ++q) v -= Pn[6 * r + q] * Pn[6 * c + q];
+            *sp = v;
+          }
+          wave_lds_sync();
+          if (lane == 0) factor6(S, pitch, k0 + 6, Ld, flag);
+        }
+      } else {
+        const int w = tid - 64, ty = w >> 5, tx = w & 31, nty = (bd - 64) >> 5;
+        for (int t = w; t < 6 * mr; t += bd - 64) S[(k0 + 6 + t / 6) * pitch + k0 + t % 6] = Pn[t];
+        for (int ii = ty; ii < mr; ii += nty) {
+          const float* pi = Pn + 6 * ii;
+          for (int jj = tx; jj <= ii && jj < m; jj += 32) {
+            if (ii < 6) continue;    // next diagonal block: wave 0
+            const float* pj = Pn + 6 * jj;
+            float* sp = S + (k0 + 6 + ii) * pitch + k0 + 6 + jj;
+            float v = *sp;
+#pragma unroll
+            for (int c = 0; c < 6; ++c) v -= pi[c] * pj[c];
+            *sp = v;
+          }
+        }
       }
-      for (int t = tid; t < m; t += bd) S[k * pitch + k + 1 + t] = S[(k + 1 + t) * pitch + k] / lkk;
-      if (tid == 0) Ld[k] = lkk;
       __syncthreads();
     }
   }
-  __syncthreads();
   const bool failed = prior_fail || *flag != 0;
-  if (!failed && tid < 64) {
-    const int ln = tid;
-    float b0 = ln < nv ? xs[ln] : 0.0f;
-    float b1 = ln + 64 < nv ? xs[ln + 64] : 0.0f;
-    float b2 = ln + 128 < nv ? xs[ln + 128] : 0.0f;
-    // L y = b, column by column; L(i, k) is stored at S[k][i]
-    for (int k = 0; k < nv; ++k) {
-      const int kb = k >> 6, kl = k & 63;
-      const float bk = kb == 0 ? rd_lane(b0, kl) : (kb == 1 ? rd_lane(b1, kl) : rd_lane(b2, kl));
-      const float yk = bk / Ld[k];
-      if (ln > k && ln < nv) b0 -= S[k * pitch + ln] * yk;
-      if (ln + 64 > k && ln + 64 < nv) b1 -= S[k * pitch + ln + 64] * yk;
-      if (ln + 128 > k && ln + 128 < nv) b2 -= S[k * pitch + ln + 128] * yk;
-      if (ln == kl) {
-        if (kb == 0) b0 = yk; else if (kb == 1) b1 = yk; else b2 = yk;
+  if (!failed) {
+    for (int t = tid; t < nv; t += bd) xs[t] = S[nv * pitch + t];
+    __syncthreads();
+    for (int K = nb - 1; K >= 0; --K) {
+      const int k0 = 6 * K;
+      float x[6];
+#pragma unroll
+      for (int c = 5; c >= 0; --c) {
+        float v = xs[k0 + c];
+#pragma unroll
+        for (int q = c + 1; q < 6; ++q) v -= S[(k0 + q) * pitch + k0 + c] * x[q];
+        x[c] = v * Ld[k0 + c];
       }
-    }
-    // L^T x = y; L(k, i) for i < k is stored at S[i][k]
-    for (int k = nv - 1; k >= 0; --k) {
-      const int kb = k >> 6, kl = k & 63;
-      const float bk = kb == 0 ? rd_lane(b0, kl) : (kb == 1 ? rd_lane(b1, kl) : rd_lane(b2, kl));
-      const float xk = bk / Ld[k];
-      if (ln < k) b0 -= S[ln * pitch + k] * xk;
-      if (ln + 64 < k) b1 -= S[(ln + 64) * pitch + k] * xk;
-      if (ln + 128 < k) b2 -= S[(ln + 128) * pitch + k] * xk;
-      if (ln == kl) {
-        if (kb == 0) b0 = xk; else if (kb == 1) b1 = xk; else b2 = xk;
+      for (int t = tid; t < k0; t += bd) {
+        float v = xs[t];
+#pragma unroll
+        for (int c = 0; c < 6; ++c) v -= S[(k0 + c) * pitch + t] * x[c];
+        xs[t] = v;
       }
+      if (tid < 6) xo[k0 + tid] = x[tid];
+      __syncthreads();
     }
-    if (ln < nv) xs[ln] = b0;
-    if (ln + 64 < nv) xs[ln + 64] = b1;
-    if (ln + 128 < nv) xs[ln + 128] = b2;
   }
   __syncthreads();
   if (tid == 0 && failed && !prior_fail) *a.status = DBA_ERR_NOT_SPD;
   for (int f = tid; f < a.n; f += bd) {
     float xi[6] = {0, 0, 0, 0, 0, 0};
     if (!failed && f >= a.nf)
-      for (int c = 0; c < 6; ++c) xi[c] = xs[6 * (f - a.nf) + c];
+      for (int c = 0; c < 6; ++c) xi[c] = xo[6 * (f - a.nf) + c];
     for (int c = 0; c < 6; ++c) a.dxi[6 * f + c] = xi[c];
     if (!failed && f >= a.nf) {
       float* p = a.pose7 + 8 * f;
@@ -734,20 +880,22 @@ struct dba_problem {
   int64_t P = 0;
   float K[4] = {0, 0, 0, 0};
   std::vector<int> h_ei, h_ej;
-  int n_groups = 0, n_tasks = 0, n_units = 0, n_records = 0, max_deg = 0;
+  int n_groups = 0, n_tasks = 0, n_units = 0, n_records = 0, max_deg = 0, n_upper = 0;
   size_t lin_lds = 0, solve_lds = 0;
   Arena arena;
   float *pose7 = nullptr, *poseRt = nullptr, *dxi = nullptr, *depth = nullptr, *dd = nullptr;
   float *targets = nullptr, *weights = nullptr, *fstore = nullptr, *estore = nullptr;
-  float *partial = nullptr, *tasksum = nullptr, *cost_part = nullptr, *costs = nullptr;
+  float *partial = nullptr, *cost_part = nullptr, *costs = nullptr;
   float *S_dbg = nullptr, *rhs_dbg = nullptr;
   int* status = nullptr;
   int* flags = nullptr;
   Group* groups = nullptr;
   Task* tasks = nullptr;
   Unit* units = nullptr;
-  int *task_group = nullptr, *blk_ptr = nullptr, *blk_ent = nullptr, *rhs_ptr = nullptr,
-      *rhs_ent = nullptr, *edge_i = nullptr, *edge_j = nullptr;
+  int *task_group = nullptr, *blk_ab = nullptr, *blk_ptr = nullptr, *rhs_ptr = nullptr,
+      *edge_i = nullptr, *edge_j = nullptr;
+  Contrib *blk_ent = nullptr, *rhs_ent = nullptr;
+  int units_per_group = 0;
   float* h_pin = nullptr;   // pinned: costs + status
   // per-residual inspection buffers (allocated on first use)
   float *dbg_r = nullptr, *dbg_ji = nullptr, *dbg_jj = nullptr, *dbg_jd = nullptr;
@@ -833,7 +981,9 @@ LinArgs lin_args(dba_problem* h, int schur) {
   return a;
 }
 
-size_t cost_lds() { return (size_t)(kMaxDeg * 12 + (kMaxDeg + 1) * 6 + kSub + kWaves) * sizeof(float); }
+size_t cost_lds() {
+  return (size_t)(kMaxDeg * 12 + (kMaxDeg + 1) * 6 + (kMaxDeg + 3) * kSub + kWaves) * sizeof(float);
+}
 
 // Linearisation (LIN) or cost (!LIN) pass, with the previous step's depth
 // update applied first when BACKSUB.
@@ -847,28 +997,35 @@ int launch_lin(dba_problem* h, int schur) {
   return DBA_OK;
 }
 
-int launch_reduce(dba_problem* h) {
-  if (h->n_tasks == 0) return DBA_OK;
-  const int n = h->n_tasks * kRec;
-  TIMED(DBA_K_REDUCE, hipLaunchKernelGGL(k_reduce, dim3((n + 255) / 256), dim3(256), 0, h->stream,
-                                         h->groups, h->task_group, h->partial, h->tasksum,
-                                         h->n_tasks));
-  return DBA_OK;
-}
-
-int launch_solve(dba_problem* h, int slot, int assemble_only) {
-  SolveArgs a;
-  a.tasksum = h->tasksum;
+// Reduced system, right-hand side and (slot >= 0) the cost at the
+// linearisation point from the blocks' partials.
+int launch_assemble(dba_problem* h, int slot) {
+  AsmArgs a;
+  a.partial = h->partial;
+  a.blk_ab = h->blk_ab;
   a.blk_ptr = h->blk_ptr;
   a.blk_ent = h->blk_ent;
   a.rhs_ptr = h->rhs_ptr;
   a.rhs_ent = h->rhs_ent;
   a.cost_part = h->cost_part;
-  a.n_units = h->n_units;
+  a.S = h->S_dbg;
+  a.rhs = h->rhs_dbg;
   a.costs = h->costs;
+  a.n_upper = h->n_upper;
+  a.nv = h->nv;
+  a.n_units = h->n_units;
+  a.units_per_group = h->units_per_group;
   a.cost_slot = slot;
-  a.S_dbg = h->S_dbg;
-  a.rhs_dbg = h->rhs_dbg;
+  const int64_t n = (int64_t)(h->n_upper * kRec + h->nv) * kAsmLanes;
+  TIMED(DBA_K_ASSEMBLE, hipLaunchKernelGGL(k_assemble, dim3((unsigned)((n + 255) / 256) + 1),
+                                           dim3(256), 0, h->stream, a));
+  return DBA_OK;
+}
+
+int launch_solve(dba_problem* h) {
+  SolveArgs a;
+  a.S = h->S_dbg;
+  a.rhs = h->rhs_dbg;
   a.dxi = h->dxi;
   a.pose7 = h->pose7;
   a.poseRt = h->poseRt;
@@ -876,7 +1033,6 @@ int launch_solve(dba_problem* h, int slot, int assemble_only) {
   a.n = h->n;
   a.nf = h->nf;
   a.nv = h->nv;
-  a.assemble_only = assemble_only;
   TIMED(DBA_K_SOLVE, hipLaunchKernelGGL(k_solve, dim3(1), dim3(kSolveThreads), h->solve_lds,
                                         h->stream, a));
   return DBA_OK;
@@ -913,8 +1069,9 @@ int fetch(dba_problem* h, int n_costs, float* out) {
 int pack_pair(int x, int y, int z, int flags) { return x | (y << 9) | (z << 18) | flags; }
 
 int build_plan(dba_problem* h, std::vector<Group>& groups, std::vector<Task>& tasks,
-               std::vector<Unit>& units, std::vector<int>& task_group, std::vector<int>& blk_ptr,
-               std::vector<int>& blk_ent, std::vector<int>& rhs_ptr, std::vector<int>& rhs_ent) {
+               std::vector<Unit>& units, std::vector<int>& task_group, std::vector<int>& blk_ab,
+               std::vector<int>& blk_ptr, std::vector<Contrib>& blk_ent, std::vector<int>& rhs_ptr,
+               std::vector<Contrib>& rhs_ent) {
   const int n = h->n, nf = h->nf, nfree = n - nf;
   std::vector<std::vector<int>> out(n);
   for (int e = 0; e < h->E; ++e) out[h->h_ei[e]].push_back(e);
@@ -956,10 +1113,15 @@ int build_plan(dba_problem* h, std::vector<Group>& groups, std::vector<Task>& ta
       for (size_t q = 0; q < pairs.size(); ++q) t.pair[q] = pairs[q];
       tl.push_back({t, {sa, sb}});
     };
-    for (int l = 0; l < d; ++l)
-      add(0, 0, 1, {pack_pair(f_a(l), f_a(l), f_sr(l), kNegR),
-                    pack_pair(f_a(l) + 6, f_a(l) + 6, f_sr(l) + 1, kNegR)});
-    add(0, 0, 1, {pack_pair(f_s(d, 0), f_s(d, 0), f_t(d), kNegM | kSchurPair)});
+    {
+      std::vector<int> p00;
+      for (int l = 0; l < d; ++l) {
+        p00.push_back(pack_pair(f_a(l), f_a(l), f_sr(l), kNegR));
+        p00.push_back(pack_pair(f_a(l) + 6, f_a(l) + 6, f_sr(l) + 1, kNegR));
+      }
+      p00.push_back(pack_pair(f_s(d, 0), f_s(d, 0), f_t(d), kNegM | kSchurPair));
+      add(0, 0, 1, p00);
+    }
     for (int l = 0; l < d; ++l)
       add(0, 1 + l, 0, {pack_pair(f_a(l), f_b(l), 0, 0), pack_pair(f_a(l) + 6, f_b(l) + 6, 0, 0),
                         pack_pair(f_s(d, 0), f_s(d, 1 + l), 0, kNegM | kSchurPair)});
@@ -999,6 +1161,7 @@ int build_plan(dba_problem* h, std::vector<Group>& groups, std::vector<Task>& ta
     const int nu = (nsub + sub_per_unit - 1) / sub_per_unit;
     g.unit_begin = (int)units.size();
     g.n_units = nu;
+    h->units_per_group = nu;
     g.rec_begin = rec;
     for (int k = 0; k < nu; ++k) {
       Unit u;
@@ -1012,7 +1175,7 @@ int build_plan(dba_problem* h, std::vector<Group>& groups, std::vector<Task>& ta
     groups.push_back(g);
   }
   h->n_records = rec;
-  // assembly lists over the free frames
+  // assembly lists over the free frames: upper 6x6 blocks in row order
   std::vector<std::vector<int>> blk(std::max(1, nfree * nfree)), rl(std::max(1, nfree));
   for (size_t t = 0; t < tinfo.size(); ++t) {
     const int A = tinfo[t].fa - nf, B = tinfo[t].fb - nf;
@@ -1029,14 +1192,22 @@ int build_plan(dba_problem* h, std::vector<Group>& groups, std::vector<Task>& ta
       blk[B * nfree + A].push_back(tt | 1);
     }
   }
+  auto contrib = [&](int x) {
+    const int t = x >> 2;
+    const Group& g = groups[task_group[t]];
+    return Contrib{g.rec_begin + (t - g.task_begin), g.n_tasks, x & 3, 0};
+  };
   blk_ptr.assign(1, 0);
-  for (int b = 0; b < nfree * nfree; ++b) {
-    for (int x : blk[b]) blk_ent.push_back(x);
-    blk_ptr.push_back((int)blk_ent.size());
-  }
+  for (int A = 0; A < nfree; ++A)
+    for (int B = A; B < nfree; ++B) {
+      blk_ab.push_back(A);
+      blk_ab.push_back(B);
+      for (int x : blk[A * nfree + B]) blk_ent.push_back(contrib(x));
+      blk_ptr.push_back((int)blk_ent.size());
+    }
   rhs_ptr.assign(1, 0);
   for (int A = 0; A < nfree; ++A) {
-    for (int x : rl[A]) rhs_ent.push_back(x);
+    for (int x : rl[A]) rhs_ent.push_back(contrib(x << 2));
     rhs_ptr.push_back((int)rhs_ent.size());
   }
   return DBA_OK;
@@ -1125,14 +1296,18 @@ int create(const float* poses, const float* inv_depth, int n, int H, int W, cons
   std::vector<Group> groups;
   std::vector<Task> tasks;
   std::vector<Unit> units;
-  std::vector<int> task_group, blk_ptr, blk_ent, rhs_ptr, rhs_ent;
-  CHECK_RC(build_plan(h, groups, tasks, units, task_group, blk_ptr, blk_ent, rhs_ptr, rhs_ent));
+  std::vector<int> task_group, blk_ab, blk_ptr, rhs_ptr;
+  std::vector<Contrib> blk_ent, rhs_ent;
+  CHECK_RC(build_plan(h, groups, tasks, units, task_group, blk_ab, blk_ptr, blk_ent, rhs_ptr,
+                      rhs_ent));
+  h->n_upper = (int)blk_ab.size() / 2;
   h->n_groups = (int)groups.size();
   h->n_tasks = (int)tasks.size();
   h->n_units = (int)units.size();
   const int fac = h->max_deg ? std::max(n_fields(h->max_deg) * kSub, kWaves * kRec * kRedPitch) : 0;
   h->lin_lds = (size_t)fac * sizeof(float) + cost_lds();
-  h->solve_lds = ((size_t)h->nv * (h->nv + 1) + 2 * (h->nv + 1) + 4) * sizeof(float);
+  h->solve_lds = ((size_t)(h->nv + 1) * (h->nv + 1) + 6 * (size_t)std::max(h->nv - 5, 0) +
+                  3 * (size_t)h->nv + 4) * sizeof(float);
   if (h->lin_lds > 65536)
     HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin<true, true>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lin_lds));
@@ -1155,7 +1330,6 @@ int create(const float* poses, const float* inv_depth, int n, int H, int W, cons
   A.add(h->fstore, 8 * n * P);
   A.add(h->estore, 6 * E * P);
   A.add(h->partial, (int64_t)h->n_records * kRec);
-  A.add(h->tasksum, (int64_t)h->n_tasks * kRec);
   A.add(h->cost_part, std::max(1, h->n_units));
   A.add(h->costs, kCostCap);
   A.add(h->S_dbg, (int64_t)h->nv * h->nv);
@@ -1166,6 +1340,7 @@ int create(const float* poses, const float* inv_depth, int n, int H, int W, cons
   A.add(h->tasks, h->n_tasks);
   A.add(h->units, h->n_units);
   A.add(h->task_group, h->n_tasks);
+  A.add(h->blk_ab, (int64_t)blk_ab.size());
   A.add(h->blk_ptr, (int64_t)blk_ptr.size());
   A.add(h->blk_ent, (int64_t)blk_ent.size());
   A.add(h->rhs_ptr, (int64_t)rhs_ptr.size());
@@ -1181,6 +1356,7 @@ int create(const float* poses, const float* inv_depth, int n, int H, int W, cons
   CHECK_RC(upload(h, h->tasks, tasks));
   CHECK_RC(upload(h, h->units, units));
   CHECK_RC(upload(h, h->task_group, task_group));
+  CHECK_RC(upload(h, h->blk_ab, blk_ab));
   CHECK_RC(upload(h, h->blk_ptr, blk_ptr));
   CHECK_RC(upload(h, h->blk_ent, blk_ent));
   CHECK_RC(upload(h, h->rhs_ptr, rhs_ptr));
@@ -1244,8 +1420,8 @@ int dba_create(const float* poses, const float* inv_depth, int n_frames, int hei
 int dba_gn_step(dba_problem* h, dba_step_info* info) {
   if (!h) return fail(DBA_ERR_ARG, "null handle");
   CHECK_RC((launch_lin<false, true>(h, 1)));
-  CHECK_RC(launch_reduce(h));
-  CHECK_RC(launch_solve(h, 0, 0));
+  CHECK_RC(launch_assemble(h, 0));
+  CHECK_RC(launch_solve(h));
   CHECK_RC((launch_lin<true, false>(h, 1)));
   CHECK_RC(launch_cost_final(h, 1));
   float c[2];
@@ -1269,12 +1445,12 @@ int dba_solve(dba_problem* h, int n_iters, float* costs) {
   while (done < n_iters) {
     const int m = std::min(n_iters - done, kCostCap - 1);
     CHECK_RC((launch_lin<false, true>(h, 1)));
-    CHECK_RC(launch_reduce(h));
-    CHECK_RC(launch_solve(h, 0, 0));
+    CHECK_RC(launch_assemble(h, 0));
+    CHECK_RC(launch_solve(h));
     for (int k = 1; k < m; ++k) {
       CHECK_RC((launch_lin<true, true>(h, 1)));
-      CHECK_RC(launch_reduce(h));
-      CHECK_RC(launch_solve(h, k, 0));
+      CHECK_RC(launch_assemble(h, k));
+      CHECK_RC(launch_solve(h));
     }
     CHECK_RC((launch_lin<true, false>(h, 1)));
     CHECK_RC(launch_cost_final(h, m));
@@ -1328,8 +1504,7 @@ int dba_debug_run(dba_problem* h, int stage) {
   if (!h) return fail(DBA_ERR_ARG, "null handle");
   if (stage == DBA_STAGE_ASSEMBLE) {
     CHECK_RC((launch_lin<false, true>(h, 0)));
-    CHECK_RC(launch_reduce(h));
-    CHECK_RC(launch_solve(h, 0, 1));
+    CHECK_RC(launch_assemble(h, -1));
     HIPC(hipStreamSynchronize(h->stream));
     if (h->prof_on) CHECK_RC(prof_collect(h));
     return DBA_OK;
@@ -1424,7 +1599,7 @@ int dba_profile_get(dba_problem* h, int kernel, int64_t* launches, double* total
 }
 
 const char* dba_kernel_name(int kernel) {
-  static const char* names[DBA_K_NUM] = {"lin", "reduce", "solve", "cost"};
+  static const char* names[DBA_K_NUM] = {"lin", "assemble", "solve", "cost"};
   return kernel >= 0 && kernel < DBA_K_NUM ? names[kernel] : "unknown";
 }
 

@@ -21,7 +21,7 @@ DBA_ERR_DEVICE, DBA_ERR_ALLOC, DBA_ERR_LIMIT = -4, -5, -6
 DBA_MEM_HOST, DBA_MEM_DEVICE = 0, 1
 DBA_STAGE_ASSEMBLE, DBA_STAGE_JACOBIANS = 1, 2
 DBG = dict(S=0, rhs=1, dxi=2, dd=3, C=4, gd=5, r=6, Ji=7, Jj=8, Jd=9)
-KERNELS = ["lin", "reduce", "solve", "cost"]
+KERNELS = ["lin", "assemble", "solve", "cost"]
 
 
 class dba_options(C.Structure):
