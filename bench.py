@@ -191,6 +191,21 @@ def main_dense(args):
     print(json.dumps(out), flush=True)
 
 
+def copy_calibration():
+    """A plain device-to-device copy of known size (3 x 512 MiB), whose
+    FETCH_SIZE and WRITE_SIZE counter readings calibrate the byte counters
+    used for the roofline's traffic figure."""
+    import torch
+    n = 512 * 1024 * 1024 // 8
+    a = torch.ones(n, dtype=torch.float64, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_copy": n * 8, "copies": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,7 +214,11 @@ def main():
     ap.add_argument("--config", default="large")
     ap.add_argument("--workload", choices=["ba", "dense"], default="ba")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 512 MiB device copy (byte-counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
