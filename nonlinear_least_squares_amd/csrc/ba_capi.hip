@@ -190,6 +190,8 @@ Dev make_dev(const ba_problem* h) {
 
 // ---- kernel timing --------------------------------------------------------
 
+// A timed launch hands a pair of pool events to the next kernel dispatch,
+// which records them at its own start and end.
 int prof_begin(ba_problem* h, int kernel, int pcg_iter, hipEvent_t* stop) {
   *stop = nullptr;
   if (!((h->prof_on >> kernel) & 1)) return BA_OK;
@@ -201,14 +203,24 @@ int prof_begin(ba_problem* h, int kernel, int pcg_iter, hipEvent_t* stop) {
     }
   }
   hipEvent_t a = h->prof_pool[h->prof_used++], b = h->prof_pool[h->prof_used++];
-  HIPC(hipEventRecord(a, h->stream));
+  DispatchEvents& ev = dispatch_events();
+  ev.start = a;
+  ev.stop = b;
+  ev.used = false;
   h->prof_recs.push_back({kernel, pcg_iter, a, b});
   *stop = b;
   return BA_OK;
 }
 
+// Drops the record when nothing was launched (an empty launch).
 int prof_end(ba_problem* h, hipEvent_t stop) {
-  if (stop) HIPC(hipEventRecord(stop, h->stream));
+  if (!stop) return BA_OK;
+  DispatchEvents& ev = dispatch_events();
+  if (!ev.used) {
+    h->prof_recs.pop_back();
+    h->prof_used -= 2;
+  }
+  ev = DispatchEvents{};
   return BA_OK;
 }
 

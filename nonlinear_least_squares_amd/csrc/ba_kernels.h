@@ -108,6 +108,15 @@ struct Dev {
   int* flags;        // [0] non-finite seen, [1] not SPD
 };
 
+// Events that the next kernel dispatch records at its start and end (set by
+// the profiler before a timed launch, consumed by that launch; null when not
+// timing).  Recorded by the dispatch itself, so they time the kernel alone.
+struct DispatchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+DispatchEvents& dispatch_events();
+
 void launch_cam_prep(const double* cams, CamT* tab, int64_t nc, hipStream_t s);
 void launch_lin_pt(const Dev& d, hipStream_t s);
 void launch_lin_cam(const Dev& d, hipStream_t s);

@@ -10,6 +10,8 @@
 // No floating-point atomics: results are bitwise reproducible run to run.
 #include "ba_kernels.h"
 
+#include <hip/hip_ext.h>
+
 namespace ba {
 namespace {
 
@@ -917,86 +919,108 @@ inline unsigned blocks_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) /
 
 // ---------------------------------------------------------------- launchers
 
+DispatchEvents& dispatch_events() {
+  thread_local DispatchEvents ev;
+  return ev;
+}
+
+namespace {
+
+// Every launch goes through the extended dispatch so that pending profiling
+// events are recorded by the dispatch packet itself.
+template <typename... KArgs, typename... Args>
+void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  DispatchEvents& ev = dispatch_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, 0u, s, ev.start, ev.stop, 0u,
+                        static_cast<KArgs>(args)...);
+  if (ev.start) {
+    ev.used = true;
+    ev.start = ev.stop = nullptr;
+  }
+}
+
+}  // namespace
+
 void launch_cam_prep(const double* cams, CamT* tab, int64_t nc, hipStream_t s) {
-  if (nc > 0) k_cam_prep<<<blocks_for(nc, 256), 256, 0, s>>>(cams, tab, nc);
+  if (nc > 0) launch(k_cam_prep, dim3(blocks_for(nc, 256)), dim3(256), s, cams, tab, nc);
 }
 void launch_lin_pt(const Dev& d, hipStream_t s) {
-  if (d.n_tiles > 0) k_lin_pt<<<d.n_tiles, kTile, 0, s>>>(d);
+  if (d.n_tiles > 0) launch(k_lin_pt, dim3(d.n_tiles), dim3(kTile), s, d);
 }
 void launch_lin_cam(const Dev& d, hipStream_t s) {
-  if (d.n_chunks > 0) k_lin_cam<<<d.n_chunks, kChunkBlock, 0, s>>>(d);
+  if (d.n_chunks > 0) launch(k_lin_cam, dim3(d.n_chunks), dim3(kChunkBlock), s, d);
 }
 void launch_damp_pt(const Dev& d, hipStream_t s) {
-  if (d.np > 0) k_damp_pt<<<blocks_for(d.np, 256), 256, 0, s>>>(d);
+  if (d.np > 0) launch(k_damp_pt, dim3(blocks_for(d.np, 256)), dim3(256), s, d);
 }
 void launch_schur_cam(const Dev& d, hipStream_t s) {
-  if (d.n_chunks > 0) k_schur_cam<<<d.n_chunks, kChunkBlock, 0, s>>>(d);
+  if (d.n_chunks > 0) launch(k_schur_cam, dim3(d.n_chunks), dim3(kChunkBlock), s, d);
 }
 void launch_lin_final(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) k_lin_final<<<blocks_for(d.nc, 64), 64, 0, s>>>(d);
+  if (d.nc > 0) launch(k_lin_final, dim3(blocks_for(d.nc, 64)), dim3(64), s, d);
 }
 void launch_precond(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) k_precond<<<blocks_for(d.nc, 64), 64, 0, s>>>(d);
+  if (d.nc > 0) launch(k_precond, dim3(blocks_for(d.nc, 64)), dim3(64), s, d);
 }
 void launch_pcg_init(const Dev& d, hipStream_t s) {
-  k_pcg_init<<<cam_vector_blocks(d.nc), kWave, 0, s>>>(d);
+  launch(k_pcg_init, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, d);
 }
 void launch_pcg_pnext(const Dev& d, int it, hipStream_t s) {
-  k_pcg_pnext<<<cam_vector_blocks(d.nc), kWave, 0, s>>>(d, it);
+  launch(k_pcg_pnext, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, d, it);
 }
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
-  if (d.n_tiles > 0) k_pcg_pt<<<d.n_tiles, kTile, 0, s>>>(d, it);
+  if (d.n_tiles > 0) launch(k_pcg_pt, dim3(d.n_tiles), dim3(kTile), s, d, it);
 }
-void launch_pcg_cam(const Dev& d, hipStream_t s) { k_pcg_cam<<<d.n_chunks, kTile, 0, s>>>(d); }
+void launch_pcg_cam(const Dev& d, hipStream_t s) { launch(k_pcg_cam, dim3(d.n_chunks), dim3(kTile), s, d); }
 void launch_pcg_q(const Dev& d, int it, hipStream_t s) {
-  k_pcg_q<<<cam_vector_blocks(d.nc), kWave, 0, s>>>(d, it);
+  launch(k_pcg_q, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, d, it);
 }
 void launch_pcg_xr(const Dev& d, int it, hipStream_t s) {
-  k_pcg_xr<<<cam_vector_blocks(d.nc), kWave, 0, s>>>(d, it);
+  launch(k_pcg_xr, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, d, it);
 }
 void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
-  k_pcg_final<<<1, kWave, 0, s>>>(d, iters);
+  launch(k_pcg_final, dim3(1), dim3(kWave), s, d, iters);
 }
 int pcg_red_blocks(int64_t nc) { return cam_vector_blocks(nc); }
 void launch_backsub(const Dev& d, hipStream_t s) {
-  if (d.n_tiles > 0) k_backsub<<<d.n_tiles, kTile, 0, s>>>(d);
+  if (d.n_tiles > 0) launch(k_backsub, dim3(d.n_tiles), dim3(kTile), s, d);
 }
 void launch_retract(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) k_retract<<<blocks_for(d.nc, 128), 128, 0, s>>>(d);
+  if (d.nc > 0) launch(k_retract, dim3(blocks_for(d.nc, 128)), dim3(128), s, d);
 }
 void launch_cost(const Dev& d, const double* cams, const double* pts, const CamT* tab,
                  hipStream_t s) {
   (void)cams;
-  if (d.n_cost_blocks > 0) k_cost<<<d.n_cost_blocks, 256, 0, s>>>(d, pts, tab);
-  k_cost_final<<<1, kUpdBlock, 0, s>>>(d);
+  if (d.n_cost_blocks > 0) launch(k_cost, dim3(d.n_cost_blocks), dim3(256), s, d, pts, tab);
+  launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, d);
 }
 void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* Jc, double* Jp,
                       double* w, hipStream_t s) {
-  if (d.nobs > 0) k_debug_obs<<<blocks_for(d.nobs, 256), 256, 0, s>>>(d, perm_pt, r, Jc, Jp, w);
+  if (d.nobs > 0) launch(k_debug_obs, dim3(blocks_for(d.nobs, 256)), dim3(256), s, d, perm_pt, r, Jc, Jp, w);
 }
 void launch_validate(const int32_t* cam_idx, const int32_t* pt_idx, const double* uv, int64_t n,
                      const double* cams, int64_t nc, const double* pts, int64_t np, int* flags,
                      hipStream_t s) {
-  k_validate<<<1024, 256, 0, s>>>(cam_idx, pt_idx, uv, n, cams, nc, pts, np, flags);
+  launch(k_validate, dim3(1024), dim3(256), s, cam_idx, pt_idx, uv, n, cams, nc, pts, np, flags);
 }
 void launch_make_keys(const int32_t* major, const int32_t* minor, int64_t n_minor, int64_t n,
                       uint64_t* keys, int32_t* vals, hipStream_t s) {
-  if (n > 0) k_make_keys<<<blocks_for(n, 256), 256, 0, s>>>(major, minor, n_minor, n, keys, vals);
+  if (n > 0) launch(k_make_keys, dim3(blocks_for(n, 256)), dim3(256), s, major, minor, n_minor, n, keys, vals);
 }
 void launch_gather_obs(const int32_t* perm, const int32_t* cam_idx, const int32_t* pt_idx,
                        const double* uv, int64_t n, int32_t* out_cam, int32_t* out_pt,
                        double* out_uv, hipStream_t s) {
   if (n > 0)
-    k_gather_obs<<<blocks_for(n, 256), 256, 0, s>>>(perm, cam_idx, pt_idx, uv, n, out_cam, out_pt,
+    launch(k_gather_obs, dim3(blocks_for(n, 256)), dim3(256), s, perm, cam_idx, pt_idx, uv, n, out_cam, out_pt,
                                                     out_uv);
 }
 void launch_seg_ptr(const int32_t* sorted_key, int64_t n, int64_t n_seg, int32_t* ptr,
                     hipStream_t s) {
-  k_seg_ptr<<<blocks_for(n + 1, 256), 256, 0, s>>>(sorted_key, n, n_seg, ptr);
+  launch(k_seg_ptr, dim3(blocks_for(n + 1, 256)), dim3(256), s, sorted_key, n, n_seg, ptr);
 }
 void launch_run_len(const int32_t* c_cam, const int32_t* c_pt, int64_t n, int32_t* run_len,
                     hipStream_t s) {
-  if (n > 0) k_run_len<<<blocks_for(n, 256), 256, 0, s>>>(c_cam, c_pt, n, run_len);
+  if (n > 0) launch(k_run_len, dim3(blocks_for(n, 256)), dim3(256), s, c_cam, c_pt, n, run_len);
 }
 
 }  // namespace ba

@@ -27,6 +27,7 @@
 // records over a group's blocks; a single-workgroup kernel assembles the
 // reduced pose system, factors it, solves and retracts.  No floating-point
 // atomics: every sum has a fixed order, so results are bitwise reproducible.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -910,28 +911,6 @@ struct dba_problem {
 
 namespace {
 
-int prof_begin(dba_problem* h, int kernel, hipEvent_t* stop) {
-  *stop = nullptr;
-  if (!((h->prof_on >> kernel) & 1)) return DBA_OK;
-  if (h->prof_used + 2 > h->prof_pool.size()) {
-    for (int i = 0; i < 64; ++i) {
-      hipEvent_t e;
-      HIPC(hipEventCreate(&e));
-      h->prof_pool.push_back(e);
-    }
-  }
-  hipEvent_t a = h->prof_pool[h->prof_used++], b = h->prof_pool[h->prof_used++];
-  HIPC(hipEventRecord(a, h->stream));
-  h->prof_recs.push_back({kernel, a, b});
-  *stop = b;
-  return DBA_OK;
-}
-
-int prof_end(dba_problem* h, hipEvent_t stop) {
-  if (stop) HIPC(hipEventRecord(stop, h->stream));
-  return DBA_OK;
-}
-
 int prof_collect(dba_problem* h) {
   for (auto& r : h->prof_recs) {
     float ms = 0.0f;
@@ -944,14 +923,28 @@ int prof_collect(dba_problem* h) {
   return DBA_OK;
 }
 
-#define TIMED(kid, launch)                       \
-  do {                                           \
-    hipEvent_t stop_;                            \
-    CHECK_RC(prof_begin(h, (kid), &stop_));      \
-    launch;                                      \
-    HIPC(hipGetLastError());                     \
-    CHECK_RC(prof_end(h, stop_));                \
-  } while (0)
+// Launch on the handle's stream; when kernel `kid` is being timed, the
+// dispatch itself records a pair of pool events at its start and end.
+template <typename... KArgs, typename... Args>
+int timed_launch(dba_problem* h, int kid, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                 uint32_t shmem, Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if ((h->prof_on >> kid) & 1) {
+    if (h->prof_used + 2 > h->prof_pool.size()) {
+      for (int i = 0; i < 64; ++i) {
+        hipEvent_t e;
+        HIPC(hipEventCreate(&e));
+        h->prof_pool.push_back(e);
+      }
+    }
+    a = h->prof_pool[h->prof_used++];
+    b = h->prof_pool[h->prof_used++];
+    h->prof_recs.push_back({kid, a, b});
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, h->stream, a, b, 0u, static_cast<KArgs>(args)...);
+  HIPC(hipGetLastError());
+  return DBA_OK;
+}
 
 LinArgs lin_args(dba_problem* h, int schur) {
   LinArgs a;
@@ -991,10 +984,8 @@ template <bool BACKSUB, bool LIN>
 int launch_lin(dba_problem* h, int schur) {
   if (h->n_units == 0) return DBA_OK;
   const size_t lds = LIN ? h->lin_lds : cost_lds();
-  TIMED(LIN ? DBA_K_LIN : DBA_K_COST,
-        hipLaunchKernelGGL((k_lin<BACKSUB, LIN>), dim3(h->n_units), dim3(kThreads), lds, h->stream,
-                           lin_args(h, schur)));
-  return DBA_OK;
+  return timed_launch(h, LIN ? DBA_K_LIN : DBA_K_COST, &k_lin<BACKSUB, LIN>, dim3(h->n_units),
+                      dim3(kThreads), (uint32_t)lds, lin_args(h, schur));
 }
 
 // Reduced system, right-hand side and (slot >= 0) the cost at the
@@ -1017,9 +1008,8 @@ int launch_assemble(dba_problem* h, int slot) {
   a.units_per_group = h->units_per_group;
   a.cost_slot = slot;
   const int64_t n = (int64_t)(h->n_upper * kRec + h->nv) * kAsmLanes;
-  TIMED(DBA_K_ASSEMBLE, hipLaunchKernelGGL(k_assemble, dim3((unsigned)((n + 255) / 256) + 1),
-                                           dim3(256), 0, h->stream, a));
-  return DBA_OK;
+  return timed_launch(h, DBA_K_ASSEMBLE, &k_assemble, dim3((unsigned)((n + 255) / 256) + 1),
+                      dim3(256), 0u, a);
 }
 
 int launch_solve(dba_problem* h) {
@@ -1033,9 +1023,8 @@ int launch_solve(dba_problem* h) {
   a.n = h->n;
   a.nf = h->nf;
   a.nv = h->nv;
-  TIMED(DBA_K_SOLVE, hipLaunchKernelGGL(k_solve, dim3(1), dim3(kSolveThreads), h->solve_lds,
-                                        h->stream, a));
-  return DBA_OK;
+  return timed_launch(h, DBA_K_SOLVE, &k_solve, dim3(1), dim3(kSolveThreads),
+                      (uint32_t)h->solve_lds, a);
 }
 
 int launch_cost_final(dba_problem* h, int slot) {
