@@ -113,7 +113,11 @@ int ba_options_default(ba_options* o);
  * reason the eager-mode BA page caches its symbolic structure), builds the
  * CSR offsets and work partitions, allocates the whole arena and evaluates
  * the initial cost.  The caller may free its inputs when this returns.
- * opts may be NULL (defaults).  On error *out is left NULL. */
+ * opts may be NULL (defaults).  On error *out is left NULL.
+ * When the camera table fits in LDS (up to about 1,100 cameras) the point
+ * passes of the PCG and the back-substitution keep it there; the environment
+ * variable BA_NO_LDS_CAMERAS=1 at creation selects the global-table kernels
+ * instead (same results up to rounding). */
 int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t n_pts,
               const int32_t* obs_cam_idx, const int32_t* obs_pt_idx, const double* obs_uv,
               int64_t n_obs, const ba_options* opts, ba_problem** out);

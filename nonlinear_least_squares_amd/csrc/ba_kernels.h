@@ -23,6 +23,9 @@
 namespace ba {
 
 constexpr int kTile = 256;        // observations per point-order sub-tile (= block size)
+constexpr int kBigTile = 1024;    // sub-tile of the persistent LDS-camera-table kernels
+constexpr int kCamLdsStride = 17; // doubles per camera in the LDS camera table
+constexpr int kCamLdsMaxBytes = 150 * 1024;
 constexpr int kChunk = 1024;      // observations per camera-order chunk
 constexpr int kChunkBlock = 256;  // threads per camera-order block
 constexpr int kCostBlock = 1024;  // observations per cost-reduction block
@@ -51,6 +54,7 @@ struct StepOut {     // everything the host reads back after a step
 struct Dev {
   int64_t nc, np, nobs;
   int n_tiles, n_chunks, n_cost_blocks;
+  int n_big_tiles, lds_blocks, cam_lds_bytes;  // LDS camera-table kernels (bytes 0: not used)
   int loss;
   double delta, diag_floor, lambda, tol;
   // parameters (current and trial)
@@ -69,6 +73,7 @@ struct Dev {
   const int32_t* run_len;
   const int32_t* pt_ptr;
   const int32_t* tile_begin;
+  const int32_t* big_tile_begin;
   const int32_t* chunk_begin;
   const int32_t* chunk_cam;
   const int32_t* cam_chunk_ptr;
@@ -116,6 +121,9 @@ struct DispatchEvents {
   bool used = false;
 };
 DispatchEvents& dispatch_events();
+
+// Allows the LDS-camera-table kernels `bytes` of dynamic LDS.
+hipError_t set_lds_camera_limit(int bytes);
 
 void launch_cam_prep(const double* cams, CamT* tab, int64_t nc, hipStream_t s);
 void launch_lin_pt(const Dev& d, hipStream_t s);

@@ -26,6 +26,14 @@ __device__ __forceinline__ void load_cam(const CamT* tab, int j, CamG& c) {
   c.f = f.x; c.k1 = f.y; c.k2 = f.z;
 }
 
+__device__ __forceinline__ void load_cam_lds(const double* s_cam, int j, CamG& c) {
+  const double* r = s_cam + kCamLdsStride * j;
+#pragma unroll
+  for (int k = 0; k < 9; ++k) c.R[k] = r[k];
+  c.t[0] = r[9]; c.t[1] = r[10]; c.t[2] = r[11];
+  c.f = r[12]; c.k1 = r[13]; c.k2 = r[14];
+}
+
 // ---------------------------------------------------------------- reductions
 
 // Deterministic block reduction of K values; the total lands in s_out[0..K).
@@ -54,17 +62,19 @@ __device__ __forceinline__ void block_reduce(double (&v)[K], double* s_buf, doub
 // Segmented reduction over whole points for one point-order tile.  Op supplies
 //   compute(s, pt, v[K])  : per-observation contribution (s = point-order index)
 //   finish(pt, v[K])      : called once per point with its total
-template <int K, class Op>
-__device__ __forceinline__ void point_tile_reduce(const Dev& d, Op& op, int tile) {
-  __shared__ double s_tail[kTile / kWave][K];
-  __shared__ int s_tail_pt[kTile / kWave];
-  __shared__ int s_tail_full[kTile / kWave];
+template <int K, int NT = kTile, class Op>
+__device__ __forceinline__ void point_tile_reduce(const Dev& d, Op& op, int tile,
+                                                  const int32_t* tile_begin = nullptr) {
+  __shared__ double s_tail[NT / kWave][K];
+  __shared__ int s_tail_pt[NT / kWave];
+  __shared__ int s_tail_full[NT / kWave];
   __shared__ double s_carry[K];
   __shared__ int s_carry_pt;
-  const int ob = d.tile_begin[tile], oe = d.tile_begin[tile + 1];
+  const int32_t* tb = tile_begin ? tile_begin : d.tile_begin;
+  const int ob = tb[tile], oe = tb[tile + 1];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   if (tid == 0) s_carry_pt = -1;
-  for (int base = ob; base < oe; base += kTile) {
+  for (int base = ob; base < oe; base += NT) {
     const int s = base + tid;
     const bool valid = s < oe;
     const int pt = valid ? d.o_pt[s] : -1;
@@ -127,7 +137,7 @@ __device__ __forceinline__ void point_tile_reduce(const Dev& d, Op& op, int tile
     const bool is_end = valid && (s + 1 >= oe || d.o_pt[s + 1] != pt);
     if (is_end) op.finish(pt, v);
     __syncthreads();
-    if (tid == kTile - 1) {
+    if (tid == NT - 1) {
       if (valid && !is_end) {
 #pragma unroll
         for (int k = 0; k < K; ++k) s_carry[k] = v[k];
@@ -423,14 +433,31 @@ __device__ __forceinline__ double block_sum(double v, double* s_buf) {
 // the point record (MODE 0).  MODE 1
 // (back-substitution): dp_i = C~_i^-1 (-g_p,i - sum_k w Jp^T (Jc dc_cam(k))) and
 // the trial point.
-template <int MODE>
+template <int MODE, bool LDS = false>
 struct PcgPtOp {
   const Dev& d;
   int it;
+  const double* s_cam;   // LDS copy of the camera table (LDS only)
+  double ci[6];          // C~^-1 of this thread's point, loaded with the point
+  double gq[3];          // g_p of this thread's point (back-substitution)
   __device__ void compute(int s, int pt, double* v) {
     const int j = d.o_cam[s];
+    // everything that depends only on the point is loaded up front, so that
+    // finish() has no load of its own on the critical path
+    const double* Ci = d.Cinv + 6 * (int64_t)pt;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) ci[k] = Ci[k];
+    if (MODE == 1) {
+      gq[0] = d.gp[3 * pt];
+      gq[1] = d.gp[3 * pt + 1];
+      gq[2] = d.gp[3 * pt + 2];
+    }
     CamG c;
-    load_cam(d.tab, j, c);
+    if constexpr (LDS) {
+      load_cam_lds(s_cam, j, c);
+    } else {
+      load_cam(d.tab, j, c);
+    }
     const double* xc = MODE == 0 ? d.pbuf + (int64_t)(it & 1) * 9 * d.nc + 9 * (int64_t)j
                                  : d.x + 9 * (int64_t)j;
     Geo g;
@@ -441,16 +468,15 @@ struct PcgPtOp {
     jpt_apply(g, c.R, w * u0, w * u1, v[0], v[1], v[2]);
   }
   __device__ void finish(int pt, const double* v) {
-    const double* Ci = d.Cinv + 6 * (int64_t)pt;
     double y0 = v[0], y1 = v[1], y2 = v[2];
     if (MODE == 1) {
-      y0 = -d.gp[3 * pt] - y0;
-      y1 = -d.gp[3 * pt + 1] - y1;
-      y2 = -d.gp[3 * pt + 2] - y2;
+      y0 = -gq[0] - y0;
+      y1 = -gq[1] - y1;
+      y2 = -gq[2] - y2;
     }
-    const double z0 = Ci[0] * y0 + Ci[1] * y1 + Ci[2] * y2;
-    const double z1 = Ci[1] * y0 + Ci[3] * y1 + Ci[4] * y2;
-    const double z2 = Ci[2] * y0 + Ci[4] * y1 + Ci[5] * y2;
+    const double z0 = ci[0] * y0 + ci[1] * y1 + ci[2] * y2;
+    const double z1 = ci[1] * y0 + ci[3] * y1 + ci[4] * y2;
+    const double z2 = ci[2] * y0 + ci[4] * y1 + ci[5] * y2;
     if (MODE == 0) {
       d.prec[8 * (int64_t)pt + 3] = z0;
       d.prec[8 * (int64_t)pt + 4] = z1;
@@ -467,7 +493,7 @@ struct PcgPtOp {
 };
 
 __global__ __launch_bounds__(kTile) void k_backsub(Dev d) {
-  PcgPtOp<1> op{d, 0};
+  PcgPtOp<1> op{d, 0, nullptr, {}, {}};
   point_tile_reduce<3>(d, op, blockIdx.x);
 }
 
@@ -639,9 +665,35 @@ __global__ __launch_bounds__(kWave) void k_pcg_pnext(Dev d, int it) {
 
 __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
   if (d.pcg->done) return;
-  PcgPtOp<0> op{d, it};
+  PcgPtOp<0> op{d, it, nullptr, {}, {}};
   point_tile_reduce<3>(d, op, blockIdx.x);
 }
+
+// The same passes with the camera table resident in LDS: one persistent
+// block per compute unit copies the table once (kCamLdsStride doubles per
+// camera, an odd number of dword pairs so that random cameras spread over
+// the banks) and walks the kBigTile-observation point tiles.  Per-lane
+// camera gathers from L1, one cache line per lane, are what bounds the
+// global-table version.
+template <int MODE>
+__device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
+  extern __shared__ double s_cam[];
+  for (int e = threadIdx.x; e < 16 * d.nc; e += kBigTile) {
+    const int j = e >> 4, k = e & 15;
+    if (k < 15) s_cam[kCamLdsStride * j + k] = reinterpret_cast<const double*>(d.tab + j)[k];
+  }
+  __syncthreads();
+  PcgPtOp<MODE, true> op{d, it, s_cam, {}, {}};
+  for (int tile = blockIdx.x; tile < d.n_big_tiles; tile += gridDim.x)
+    point_tile_reduce<3, kBigTile>(d, op, tile, d.big_tile_begin);
+}
+
+__global__ __launch_bounds__(kBigTile) void k_pcg_pt_lds(Dev d, int it) {
+  if (d.pcg->done) return;
+  pcg_pt_lds_body<0>(d, it);
+}
+
+__global__ __launch_bounds__(kBigTile) void k_backsub_lds(Dev d) { pcg_pt_lds_body<1>(d, 0); }
 
 __global__ __launch_bounds__(kTile) void k_pcg_cam(Dev d) {
   if (d.pcg->done) return;
@@ -924,14 +976,23 @@ DispatchEvents& dispatch_events() {
   return ev;
 }
 
+hipError_t set_lds_camera_limit(int bytes) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pcg_pt_lds),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_backsub_lds),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 namespace {
 
 // Every launch goes through the extended dispatch so that pending profiling
 // events are recorded by the dispatch packet itself.
 template <typename... KArgs, typename... Args>
-void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
+void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, uint32_t shmem,
+            Args... args) {
   DispatchEvents& ev = dispatch_events();
-  hipExtLaunchKernelGGL(kernel, grid, block, 0u, s, ev.start, ev.stop, 0u,
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0u,
                         static_cast<KArgs>(args)...);
   if (ev.start) {
     ev.used = true;
@@ -942,85 +1003,95 @@ void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args
 }  // namespace
 
 void launch_cam_prep(const double* cams, CamT* tab, int64_t nc, hipStream_t s) {
-  if (nc > 0) launch(k_cam_prep, dim3(blocks_for(nc, 256)), dim3(256), s, cams, tab, nc);
+  if (nc > 0) launch(k_cam_prep, dim3(blocks_for(nc, 256)), dim3(256), s, 0u, cams, tab, nc);
 }
 void launch_lin_pt(const Dev& d, hipStream_t s) {
-  if (d.n_tiles > 0) launch(k_lin_pt, dim3(d.n_tiles), dim3(kTile), s, d);
+  if (d.n_tiles > 0) launch(k_lin_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
 }
 void launch_lin_cam(const Dev& d, hipStream_t s) {
-  if (d.n_chunks > 0) launch(k_lin_cam, dim3(d.n_chunks), dim3(kChunkBlock), s, d);
+  if (d.n_chunks > 0) launch(k_lin_cam, dim3(d.n_chunks), dim3(kChunkBlock), s, 0u, d);
 }
 void launch_damp_pt(const Dev& d, hipStream_t s) {
-  if (d.np > 0) launch(k_damp_pt, dim3(blocks_for(d.np, 256)), dim3(256), s, d);
+  if (d.np > 0) launch(k_damp_pt, dim3(blocks_for(d.np, 256)), dim3(256), s, 0u, d);
 }
 void launch_schur_cam(const Dev& d, hipStream_t s) {
-  if (d.n_chunks > 0) launch(k_schur_cam, dim3(d.n_chunks), dim3(kChunkBlock), s, d);
+  if (d.n_chunks > 0) launch(k_schur_cam, dim3(d.n_chunks), dim3(kChunkBlock), s, 0u, d);
 }
 void launch_lin_final(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) launch(k_lin_final, dim3(blocks_for(d.nc, 64)), dim3(64), s, d);
+  if (d.nc > 0) launch(k_lin_final, dim3(blocks_for(d.nc, 64)), dim3(64), s, 0u, d);
 }
 void launch_precond(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) launch(k_precond, dim3(blocks_for(d.nc, 64)), dim3(64), s, d);
+  if (d.nc > 0) launch(k_precond, dim3(blocks_for(d.nc, 64)), dim3(64), s, 0u, d);
 }
 void launch_pcg_init(const Dev& d, hipStream_t s) {
-  launch(k_pcg_init, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, d);
+  launch(k_pcg_init, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d);
 }
 void launch_pcg_pnext(const Dev& d, int it, hipStream_t s) {
-  launch(k_pcg_pnext, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, d, it);
+  launch(k_pcg_pnext, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
 }
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
-  if (d.n_tiles > 0) launch(k_pcg_pt, dim3(d.n_tiles), dim3(kTile), s, d, it);
+  if (d.cam_lds_bytes > 0) {
+    if (d.n_big_tiles > 0)
+      launch(k_pcg_pt_lds, dim3(d.lds_blocks), dim3(kBigTile), s, d.cam_lds_bytes, d, it);
+  } else if (d.n_tiles > 0) {
+    launch(k_pcg_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d, it);
+  }
 }
-void launch_pcg_cam(const Dev& d, hipStream_t s) { launch(k_pcg_cam, dim3(d.n_chunks), dim3(kTile), s, d); }
+void launch_pcg_cam(const Dev& d, hipStream_t s) { launch(k_pcg_cam, dim3(d.n_chunks), dim3(kTile), s, 0u, d); }
 void launch_pcg_q(const Dev& d, int it, hipStream_t s) {
-  launch(k_pcg_q, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, d, it);
+  launch(k_pcg_q, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
 }
 void launch_pcg_xr(const Dev& d, int it, hipStream_t s) {
-  launch(k_pcg_xr, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, d, it);
+  launch(k_pcg_xr, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
 }
 void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
-  launch(k_pcg_final, dim3(1), dim3(kWave), s, d, iters);
+  launch(k_pcg_final, dim3(1), dim3(kWave), s, 0u, d, iters);
 }
 int pcg_red_blocks(int64_t nc) { return cam_vector_blocks(nc); }
 void launch_backsub(const Dev& d, hipStream_t s) {
-  if (d.n_tiles > 0) launch(k_backsub, dim3(d.n_tiles), dim3(kTile), s, d);
+  if (d.cam_lds_bytes > 0) {
+    if (d.n_big_tiles > 0)
+      launch(k_backsub_lds, dim3(d.lds_blocks), dim3(kBigTile), s, d.cam_lds_bytes, d);
+  } else if (d.n_tiles > 0) {
+    launch(k_backsub, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
+  }
 }
 void launch_retract(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) launch(k_retract, dim3(blocks_for(d.nc, 128)), dim3(128), s, d);
+  if (d.nc > 0) launch(k_retract, dim3(blocks_for(d.nc, 128)), dim3(128), s, 0u, d);
 }
 void launch_cost(const Dev& d, const double* cams, const double* pts, const CamT* tab,
                  hipStream_t s) {
   (void)cams;
-  if (d.n_cost_blocks > 0) launch(k_cost, dim3(d.n_cost_blocks), dim3(256), s, d, pts, tab);
-  launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, d);
+  if (d.n_cost_blocks > 0) launch(k_cost, dim3(d.n_cost_blocks), dim3(256), s, 0u, d, pts, tab);
+  launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d);
 }
 void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* Jc, double* Jp,
                       double* w, hipStream_t s) {
-  if (d.nobs > 0) launch(k_debug_obs, dim3(blocks_for(d.nobs, 256)), dim3(256), s, d, perm_pt, r, Jc, Jp, w);
+  if (d.nobs > 0) launch(k_debug_obs, dim3(blocks_for(d.nobs, 256)), dim3(256), s, 0u, d, perm_pt, r, Jc, Jp, w);
 }
 void launch_validate(const int32_t* cam_idx, const int32_t* pt_idx, const double* uv, int64_t n,
                      const double* cams, int64_t nc, const double* pts, int64_t np, int* flags,
                      hipStream_t s) {
-  launch(k_validate, dim3(1024), dim3(256), s, cam_idx, pt_idx, uv, n, cams, nc, pts, np, flags);
+  launch(k_validate, dim3(1024), dim3(256), s, 0u, cam_idx, pt_idx, uv, n, cams, nc, pts, np, flags);
 }
 void launch_make_keys(const int32_t* major, const int32_t* minor, int64_t n_minor, int64_t n,
                       uint64_t* keys, int32_t* vals, hipStream_t s) {
-  if (n > 0) launch(k_make_keys, dim3(blocks_for(n, 256)), dim3(256), s, major, minor, n_minor, n, keys, vals);
+  if (n > 0) launch(k_make_keys, dim3(blocks_for(n, 256)), dim3(256), s, 0u, major, minor, n_minor, n, keys, vals);
 }
 void launch_gather_obs(const int32_t* perm, const int32_t* cam_idx, const int32_t* pt_idx,
                        const double* uv, int64_t n, int32_t* out_cam, int32_t* out_pt,
                        double* out_uv, hipStream_t s) {
   if (n > 0)
-    launch(k_gather_obs, dim3(blocks_for(n, 256)), dim3(256), s, perm, cam_idx, pt_idx, uv, n, out_cam, out_pt,
+    launch(k_gather_obs, dim3(blocks_for(n, 256)), dim3(256), s, 0u, perm, cam_idx, pt_idx, uv, n, out_cam, out_pt,
                                                     out_uv);
 }
 void launch_seg_ptr(const int32_t* sorted_key, int64_t n, int64_t n_seg, int32_t* ptr,
                     hipStream_t s) {
-  launch(k_seg_ptr, dim3(blocks_for(n + 1, 256)), dim3(256), s, sorted_key, n, n_seg, ptr);
+  launch(k_seg_ptr, dim3(blocks_for(n + 1, 256)), dim3(256), s, 0u, sorted_key, n, n_seg, ptr);
 }
 void launch_run_len(const int32_t* c_cam, const int32_t* c_pt, int64_t n, int32_t* run_len,
                     hipStream_t s) {
-  if (n > 0) launch(k_run_len, dim3(blocks_for(n, 256)), dim3(256), s, c_cam, c_pt, n, run_len);
+  if (n > 0) launch(k_run_len, dim3(blocks_for(n, 256)), dim3(256), s, 0u, c_cam, c_pt, n, run_len);
 }
 
 }  // namespace ba

@@ -136,7 +136,12 @@ def test_schur_parity(scene, lam):
 
 
 @pytest.mark.parametrize("config", ["tiny", "small"])
-def test_pcg_and_update_parity(config):
+@pytest.mark.parametrize("lds_cameras", [True, False])
+def test_pcg_and_update_parity(config, lds_cameras, monkeypatch):
+    # the camera table of these scenes fits in LDS; the environment switch,
+    # read when the handle is created, selects the global-table kernels
+    if not lds_cameras:
+        monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
     sc = ba_scene(config)
     gpu, orc = make_pair(sc)
     gpu.debug_run(bamod.BA_STAGE_UPDATE)
