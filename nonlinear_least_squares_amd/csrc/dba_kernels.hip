@@ -117,6 +117,12 @@ __device__ __forceinline__ void rel_pose(const float* Ti, const float* Tj, float
     o[9 + r] = Tj[9 + r] - (o[3 * r] * Ti[9] + o[3 * r + 1] * Ti[10] + o[3 * r + 2] * Ti[11]);
 }
 
+// Hardware reciprocal, square root and reciprocal square root (about 1 ulp,
+// against several times the latency for the correctly rounded forms).
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fsqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+__device__ __forceinline__ float frsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
 struct PixOut {
   float r0, r1;
   float ji[12], jj[12], jd[2];
@@ -133,13 +139,13 @@ __device__ __forceinline__ void pix_eval(const float* T, float fx, float fy, flo
                                          float tx, float ty, PixOut& o) {
   const float ray0 = (x - cx) * ifx, ray1 = (y - cy) * ify;
   const bool dcl = d < 1e-6f;
-  const float id = 1.0f / (dcl ? 1e-6f : d);
+  const float id = frcp(dcl ? 1e-6f : d);
   const float X0 = ray0 * id, X1 = ray1 * id, X2 = id;
   const float Y0 = T[0] * X0 + T[1] * X1 + T[2] * X2 + T[9];
   const float Y1 = T[3] * X0 + T[4] * X1 + T[5] * X2 + T[10];
   const float Y2 = T[6] * X0 + T[7] * X1 + T[8] * X2 + T[11];
   const bool zcl = Y2 < 1e-6f;
-  const float iz = 1.0f / (zcl ? 1e-6f : Y2);
+  const float iz = frcp(zcl ? 1e-6f : Y2);
   o.r0 = fx * (Y0 * iz) + cx - tx;
   o.r1 = fy * (Y1 * iz) + cy - ty;
   if constexpr (JAC) {
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_lin(LinArgs a) {
             float sv = bsS[pl];
             for (int s2 = 1; s2 <= d; ++s2) sv += bsS[s2 * kSub + pl];
             const float C = bsC[pl];
-            const float step = C > 0.0f ? -sv / C : 0.0f;
+            const float step = C > 0.0f ? -sv * frcp(C) : 0.0f;
             dv = dv + step;
             if (l == 0) {
               const int64_t idx = (int64_t)frame * P + p;
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void k_lin(LinArgs a) {
           PixOut o;
           pix_eval<LIN>(rel + 12 * l, a.fx, a.fy, a.cx, a.cy, a.ifx, a.ify, (float)(p % a.W),
                         (float)(p / a.W), dv, tgv[m].x, tgv[m].y, o);
-          const float sw = sqrtf(wv[m]);
+          const float sw = fsqrt(wv[m]);
           const float sr0 = sw * o.r0, sr1 = sw * o.r1;
           if (pass == 0) cost += sr0 * sr0 + sr1 * sr1;
           if constexpr (LIN) {
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void k_lin(LinArgs a) {
               for (int c = 0; c < 6; ++c) es[c * P] = fac[(f_s(d, 1 + l) + c) * kSub + pl];
             }
           }
-          const float inv = C > 0.0f ? 1.0f / sqrtf(C) : 0.0f;
+          const float inv = C > 0.0f ? frsq(C) : 0.0f;
 #pragma unroll
           for (int c = 0; c < 6; ++c) fac[(f_s(d, 0) + c) * kSub + pl] = col[c] * inv;
           for (int l = 0; l < d; ++l)
@@ -412,9 +418,17 @@ __global__ __launch_bounds__(kThreads) void k_lin(LinArgs a) {
         for (int e = 0; e < kRec; ++e) rw[e * kRedPitch + lane] = acc[k][e];
         __syncthreads();
         if (tl >= 0 && lane < kRec) {
-          float s = 0.0f;
-          for (int j = 0; j < 64; ++j) s += rw[lane * kRedPitch + j];
-          a.partial[(int64_t)(u.rec_begin + tl) * kRec + lane] = s;
+          // four interleaved chains, then a fixed tree
+          const float* row = rw + lane * kRedPitch;
+          float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 64; j += 4) {
+            s0 += row[j];
+            s1 += row[j + 1];
+            s2 += row[j + 2];
+            s3 += row[j + 3];
+          }
+          a.partial[(int64_t)(u.rec_begin + tl) * kRec + lane] = (s0 + s1) + (s2 + s3);
         }
         __syncthreads();
       }
@@ -624,6 +638,7 @@ constexpr int kSolveLoads = (kMaxNv * kMaxNv + kSolveThreads - 1) / kSolveThread
 
 // Cholesky of the 6x6 diagonal block at (k0, k0) in place (lower triangle),
 // reciprocals of its diagonal to Ld; *flag = 1 if a pivot is not positive.
+// One thread.
 __device__ void factor6(float* S, int pitch, int k0, float* Ld, int* flag) {
   float L[21], id[6];
 #pragma unroll
@@ -637,7 +652,7 @@ __device__ void factor6(float* S, int pitch, int k0, float* Ld, int* flag) {
 #pragma unroll
     for (int l = 0; l < j; ++l) dj -= L[tri6(j, l)] * L[tri6(j, l)];
     ok = ok && dj > 0.0f && isfinite(dj);
-    id[j] = __builtin_amdgcn_rsqf(dj);    // 1 / L_jj
+    id[j] = frsq(dj);    // 1 / L_jj
     L[tri6(j, j)] = dj * id[j];
 #pragma unroll
     for (int i = j + 1; i < 6; ++i) {
