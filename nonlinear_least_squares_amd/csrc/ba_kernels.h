@@ -27,6 +27,8 @@ constexpr int kBigTile = 1024;    // sub-tile of the persistent LDS-camera-table
 constexpr int kCamLdsStride = 17; // doubles per camera in the LDS camera table
 constexpr int kCamLdsMaxBytes = 150 * 1024;
 constexpr int kChunk = 1024;      // observations per camera-order chunk
+constexpr int kPointBands = 8;    // point-index bands of the PCG camera pass (one per XCD)
+constexpr int kBandChunk = 512;   // observations per band chunk (one wavefront)
 constexpr int kChunkBlock = 256;  // threads per camera-order block
 constexpr int kCostBlock = 1024;  // observations per cost-reduction block
 constexpr int kUpdBlock = 1024;   // threads of the single-block cost reduction
@@ -54,6 +56,7 @@ struct StepOut {     // everything the host reads back after a step
 struct Dev {
   int64_t nc, np, nobs;
   int n_tiles, n_chunks, n_cost_blocks;
+  int n_band_blocks;     // blocks of the PCG camera pass (band_block entries)
   int n_big_tiles, lds_blocks, cam_lds_bytes;  // LDS camera-table kernels (bytes 0: not used)
   int loss;
   double delta, diag_floor, lambda, tol;
@@ -77,6 +80,10 @@ struct Dev {
   const int32_t* chunk_begin;
   const int32_t* chunk_cam;
   const int32_t* cam_chunk_ptr;
+  const int32_t* bchunk_begin;   // band chunks: camera-order ranges within one point band
+  const int32_t* bchunk_cam;
+  const int32_t* cam_bchunk_ptr; // band chunks of each camera, in order
+  const int32_t* band_block;     // band chunk of each block (band = block % kPointBands), -1 none
   // linearisation
   double* w_pt;
   double* w_cam;

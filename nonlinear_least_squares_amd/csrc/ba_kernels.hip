@@ -695,18 +695,23 @@ __global__ __launch_bounds__(kBigTile) void k_pcg_pt_lds(Dev d, int it) {
 
 __global__ __launch_bounds__(kBigTile) void k_backsub_lds(Dev d) { pcg_pt_lds_body<1>(d, 0); }
 
-__global__ __launch_bounds__(kTile) void k_pcg_cam(Dev d) {
+// Camera side of S p over band chunks: the observations of one camera whose
+// points lie in one of kPointBands equal index bands.  Block b takes a chunk
+// of band b % kPointBands, and workgroups are placed on the accelerator dies
+// round-robin, so each die gathers the point records of one band only and
+// they stay in its L2.  One wavefront per chunk; partials summed by a fixed
+// butterfly.
+__global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
   if (d.pcg->done) return;
-  __shared__ double s_red[(kTile / kWave) * 9];
-  __shared__ double s_out[9];
-  const int ch = blockIdx.x;
-  const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
+  const int ch = d.band_block[blockIdx.x];
+  if (ch < 0) return;
+  const int cb = d.bchunk_begin[ch], ce = d.bchunk_begin[ch + 1];
   CamG c;
-  load_cam(d.tab, d.chunk_cam[ch], c);
+  load_cam(d.tab, d.bchunk_cam[ch], c);
   double acc[9];
 #pragma unroll
   for (int k = 0; k < 9; ++k) acc[k] = 0.0;
-  for (int s = cb + threadIdx.x; s < ce; s += kTile) {
+  for (int s = cb + threadIdx.x; s < ce; s += kWave) {
     const int i = d.c_pt[s];
     const double4 a = *reinterpret_cast<const double4*>(d.prec + 8 * (int64_t)i);
     const double2 b = *reinterpret_cast<const double2*>(d.prec + 8 * (int64_t)i + 4);
@@ -717,8 +722,12 @@ __global__ __launch_bounds__(kTile) void k_pcg_cam(Dev d) {
     const double w = d.w_cam[s];
     jct_acc(g, c.f, w * t0, w * t1, acc);
   }
-  block_reduce<9, kTile>(acc, s_red, s_out);
-  if (threadIdx.x < 9) d.pcg_part[(int64_t)ch * 9 + threadIdx.x] = s_out[threadIdx.x];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) acc[k] = wave_sum(acc[k]);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) d.pcg_part[(int64_t)ch * 9 + k] = acc[k];
+  }
 }
 
 __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
@@ -731,7 +740,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
 #pragma unroll
   for (int b = 0; b < 9; ++b)
     qa += Bd[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)] * p[b];
-  for (int ch = d.cam_chunk_ptr[c.j]; ch < d.cam_chunk_ptr[c.j + 1]; ++ch)
+  for (int ch = d.cam_bchunk_ptr[c.j]; ch < d.cam_bchunk_ptr[c.j + 1]; ++ch)
     qa -= d.pcg_part[(int64_t)ch * 9 + c.a];
   double pq = 0.0;
   if (c.on) {
@@ -1037,7 +1046,9 @@ void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
     launch(k_pcg_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d, it);
   }
 }
-void launch_pcg_cam(const Dev& d, hipStream_t s) { launch(k_pcg_cam, dim3(d.n_chunks), dim3(kTile), s, 0u, d); }
+void launch_pcg_cam(const Dev& d, hipStream_t s) {
+  if (d.n_band_blocks > 0) launch(k_pcg_cam, dim3(d.n_band_blocks), dim3(kWave), s, 0u, d);
+}
 void launch_pcg_q(const Dev& d, int it, hipStream_t s) {
   launch(k_pcg_q, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
 }
