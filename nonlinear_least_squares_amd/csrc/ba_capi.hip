@@ -81,7 +81,7 @@ struct ba_problem {
   ba_options opt{};
   hipStream_t stream = nullptr;
   int n_tiles = 0, n_chunks = 0, n_cost_blocks = 0, n_big_tiles = 0, lds_blocks = 0,
-      cam_lds_bytes = 0, n_bchunks = 0, n_band_blocks = 0;
+      cam_lds_bytes = 0, n_chunk_blocks = 0;
   Arena arena;   // everything sized by n_cams, n_pts, n_obs
   Arena arena2;  // partitions and partial sums, sized after the CSR offsets
   // parameters: [cur] current, [1 - cur] trial
@@ -94,8 +94,7 @@ struct ba_problem {
   int32_t *o_cam = nullptr, *o_pt = nullptr, *c_pt = nullptr, *run_len = nullptr;
   double *o_uv = nullptr, *c_uv = nullptr;
   int32_t *tile_begin = nullptr, *chunk_begin = nullptr, *chunk_cam = nullptr,
-          *cam_chunk_ptr = nullptr, *big_tile_begin = nullptr, *bchunk_begin = nullptr,
-          *bchunk_cam = nullptr, *cam_bchunk_ptr = nullptr, *band_block = nullptr;
+          *cam_chunk_ptr = nullptr, *big_tile_begin = nullptr, *chunk_block = nullptr;
   // work arrays
   double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
          *gc = nullptr, *lin_part = nullptr;
@@ -134,11 +133,8 @@ Dev make_dev(const ba_problem* h) {
   d.nobs = h->nobs;
   d.n_tiles = h->n_tiles;
   d.n_chunks = h->n_chunks;
-  d.n_band_blocks = h->n_band_blocks;
-  d.bchunk_begin = h->bchunk_begin;
-  d.bchunk_cam = h->bchunk_cam;
-  d.cam_bchunk_ptr = h->cam_bchunk_ptr;
-  d.band_block = h->band_block;
+  d.n_chunk_blocks = h->n_chunk_blocks;
+  d.chunk_block = h->chunk_block;
   d.n_big_tiles = h->n_big_tiles;
   d.lds_blocks = h->lds_blocks;
   d.cam_lds_bytes = h->cam_lds_bytes;
@@ -584,52 +580,42 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
       h->lds_blocks = std::min(h->n_big_tiles, std::max(cus, 1));
     }
   }
-  // Camera chunks: every camera gets ceil(len / kChunk) >= 1 equal pieces.
-  std::vector<int32_t> chunk_begin, chunk_cam, cam_chunk_ptr(nc + 1, 0);
-  for (int64_t j = 0; j < nc; ++j) {
-    const int64_t len = cam_ptr[j + 1] - cam_ptr[j];
-    const int64_t nch = std::max<int64_t>(1, (len + kChunk - 1) / kChunk);
-    for (int64_t c = 0; c < nch; ++c) {
-      chunk_begin.push_back((int32_t)(cam_ptr[j] + (len * c) / nch));
-      chunk_cam.push_back((int32_t)j);
-    }
-    cam_chunk_ptr[j + 1] = (int32_t)chunk_begin.size();
-  }
-  chunk_begin.push_back((int32_t)N);
-  // Band chunks for the PCG camera pass: a camera's observations are sorted
-  // by point, so those whose points fall in each of kPointBands equal index
-  // bands form a contiguous piece, cut into chunks of at most kBandChunk.
+  // Camera chunks: a camera's observations are sorted by point, so those whose
+  // points fall in each of kPointBands equal index bands form a contiguous
+  // piece, cut into equal chunks of at most kChunk.  Blocks are laid out so
+  // that block b takes a chunk of band b % kPointBands (-1 pads short bands).
   std::vector<int32_t> c_pt_h(N);
   if (N) TRY(hipMemcpyAsync(c_pt_h.data(), h->c_pt, sizeof(int32_t) * N, hipMemcpyDeviceToHost, s));
   TRY(hipStreamSynchronize(s));
-  std::vector<int32_t> bchunk_begin, bchunk_cam, cam_bchunk_ptr(nc + 1, 0);
+  std::vector<int32_t> chunk_begin, chunk_cam, cam_chunk_ptr(nc + 1, 0);
   std::vector<std::vector<int32_t>> band_list(kPointBands);
   const int64_t np1 = std::max<int64_t>(np, 1);
+  auto band_of = [&](int64_t k) { return (int)((int64_t)c_pt_h[k] * kPointBands / np1); };
   for (int64_t j = 0; j < nc; ++j) {
     int64_t a = cam_ptr[j];
     const int64_t b1 = cam_ptr[j + 1];
     while (a < b1) {
-      const int band = (int)((int64_t)c_pt_h[a] * kPointBands / np1);
+      const int band = band_of(a);
       int64_t e = a;
-      while (e < b1 && (int)((int64_t)c_pt_h[e] * kPointBands / np1) == band) ++e;
-      const int64_t len = e - a, nch = (len + kBandChunk - 1) / kBandChunk;
+      while (e < b1 && band_of(e) == band) ++e;
+      const int64_t len = e - a, nch = (len + kChunk - 1) / kChunk;
       for (int64_t c = 0; c < nch; ++c) {
-        band_list[band].push_back((int32_t)bchunk_cam.size());
-        bchunk_begin.push_back((int32_t)(a + (len * c) / nch));
-        bchunk_cam.push_back((int32_t)j);
+        band_list[band].push_back((int32_t)chunk_cam.size());
+        chunk_begin.push_back((int32_t)(a + (len * c) / nch));
+        chunk_cam.push_back((int32_t)j);
       }
       a = e;
     }
-    cam_bchunk_ptr[j + 1] = (int32_t)bchunk_cam.size();
+    cam_chunk_ptr[j + 1] = (int32_t)chunk_cam.size();
   }
-  bchunk_begin.push_back((int32_t)N);
+  chunk_begin.push_back((int32_t)N);
   size_t per_band = 0;
   for (auto& v : band_list) per_band = std::max(per_band, v.size());
-  std::vector<int32_t> band_block(per_band * kPointBands, -1);
+  std::vector<int32_t> chunk_block(per_band * kPointBands, -1);
   for (int bnd = 0; bnd < kPointBands; ++bnd)
-    for (size_t i = 0; i < band_list[bnd].size(); ++i) band_block[i * kPointBands + bnd] = band_list[bnd][i];
-  h->n_bchunks = (int)bchunk_cam.size();
-  h->n_band_blocks = (int)band_block.size();
+    for (size_t i = 0; i < band_list[bnd].size(); ++i)
+      chunk_block[i * kPointBands + bnd] = band_list[bnd][i];
+  h->n_chunk_blocks = (int)chunk_block.size();
   h->n_tiles = (int)tiles.size() - 1;
   h->n_chunks = (int)chunk_cam.size();
   h->n_cost_blocks = (int)((N + kCostBlock - 1) / kCostBlock);
@@ -637,15 +623,13 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   Arena& P = h->arena2;
   P.add(h->tile_begin, (int64_t)tiles.size());
   P.add(h->big_tile_begin, (int64_t)big.size());
+  const int64_t n_ch1 = std::max(h->n_chunks, 1);
   P.add(h->chunk_begin, (int64_t)chunk_begin.size());
-  P.add(h->chunk_cam, (int64_t)chunk_cam.size());
-  P.add(h->lin_part, (int64_t)h->n_chunks * kLinCamVals);
-  P.add(h->schur_part, (int64_t)h->n_chunks * kSchurVals);
-  P.add(h->pcg_part, (int64_t)std::max(h->n_bchunks, 1) * 9);
-  P.add(h->bchunk_begin, (int64_t)bchunk_begin.size());
-  P.add(h->bchunk_cam, (int64_t)std::max<size_t>(bchunk_cam.size(), 1));
-  P.add(h->cam_bchunk_ptr, (int64_t)nc + 1);
-  P.add(h->band_block, (int64_t)std::max<size_t>(band_block.size(), 1));
+  P.add(h->chunk_cam, n_ch1);
+  P.add(h->chunk_block, (int64_t)std::max<size_t>(chunk_block.size(), 1));
+  P.add(h->lin_part, n_ch1 * kLinCamVals);
+  P.add(h->schur_part, n_ch1 * kSchurVals);
+  P.add(h->pcg_part, n_ch1 * 9);
   P.add(h->cost_part, (int64_t)std::max(h->n_cost_blocks, 1));
   P.add(h->red_part, 6 * (int64_t)pcg_red_blocks(nc));
   rc = P.commit();
@@ -655,20 +639,14 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
                      hipMemcpyHostToDevice, s));
   TRY(hipMemcpyAsync(h->big_tile_begin, big.data(), sizeof(int32_t) * big.size(),
                      hipMemcpyHostToDevice, s));
-  TRY(hipMemcpyAsync(h->bchunk_begin, bchunk_begin.data(), sizeof(int32_t) * bchunk_begin.size(),
-                     hipMemcpyHostToDevice, s));
-  if (!bchunk_cam.empty())
-    TRY(hipMemcpyAsync(h->bchunk_cam, bchunk_cam.data(), sizeof(int32_t) * bchunk_cam.size(),
-                       hipMemcpyHostToDevice, s));
-  TRY(hipMemcpyAsync(h->cam_bchunk_ptr, cam_bchunk_ptr.data(), sizeof(int32_t) * (nc + 1),
-                     hipMemcpyHostToDevice, s));
-  if (!band_block.empty())
-    TRY(hipMemcpyAsync(h->band_block, band_block.data(), sizeof(int32_t) * band_block.size(),
-                       hipMemcpyHostToDevice, s));
   TRY(hipMemcpyAsync(h->chunk_begin, chunk_begin.data(), sizeof(int32_t) * chunk_begin.size(),
                      hipMemcpyHostToDevice, s));
-  TRY(hipMemcpyAsync(h->chunk_cam, chunk_cam.data(), sizeof(int32_t) * chunk_cam.size(),
-                     hipMemcpyHostToDevice, s));
+  if (!chunk_cam.empty())
+    TRY(hipMemcpyAsync(h->chunk_cam, chunk_cam.data(), sizeof(int32_t) * chunk_cam.size(),
+                       hipMemcpyHostToDevice, s));
+  if (!chunk_block.empty())
+    TRY(hipMemcpyAsync(h->chunk_block, chunk_block.data(), sizeof(int32_t) * chunk_block.size(),
+                       hipMemcpyHostToDevice, s));
   TRY(hipMemcpyAsync(h->cam_chunk_ptr, cam_chunk_ptr.data(), sizeof(int32_t) * (nc + 1),
                      hipMemcpyHostToDevice, s));
   TRY(hipStreamSynchronize(s));

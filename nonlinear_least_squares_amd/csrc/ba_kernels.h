@@ -11,8 +11,9 @@
 //   per camera   : parameters (9), CamT table (16), B (45), g_c (9), B~ (45),
 //                  rhs (9), Cholesky of S_jj (45), PCG vectors (9 each)
 //   partitions   : point tiles (whole points, <= kTile observations unless a
-//                  single point is longer), camera chunks (<= kChunk
-//                  observations of one camera, at least one per camera)
+//                  single point is longer); camera chunks: the observations
+//                  of one camera whose points lie in one of kPointBands equal
+//                  point-index bands, cut into pieces of <= kChunk
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -26,10 +27,8 @@ constexpr int kTile = 256;        // observations per point-order sub-tile (= bl
 constexpr int kBigTile = 1024;    // sub-tile of the persistent LDS-camera-table kernels
 constexpr int kCamLdsStride = 17; // doubles per camera in the LDS camera table
 constexpr int kCamLdsMaxBytes = 150 * 1024;
-constexpr int kChunk = 1024;      // observations per camera-order chunk
-constexpr int kPointBands = 8;    // point-index bands of the PCG camera pass (one per XCD)
-constexpr int kBandChunk = 512;   // observations per band chunk (one wavefront)
-constexpr int kChunkBlock = 256;  // threads per camera-order block
+constexpr int kChunk = 512;       // observations per camera chunk (one wavefront)
+constexpr int kPointBands = 8;    // point-index bands of the camera chunks (one per XCD)
 constexpr int kCostBlock = 1024;  // observations per cost-reduction block
 constexpr int kUpdBlock = 1024;   // threads of the single-block cost reduction
 constexpr int kLinCamVals = 54;   // B (45) + g_c (9)
@@ -56,7 +55,7 @@ struct StepOut {     // everything the host reads back after a step
 struct Dev {
   int64_t nc, np, nobs;
   int n_tiles, n_chunks, n_cost_blocks;
-  int n_band_blocks;     // blocks of the PCG camera pass (band_block entries)
+  int n_chunk_blocks;    // blocks of the camera passes (chunk_block entries)
   int n_big_tiles, lds_blocks, cam_lds_bytes;  // LDS camera-table kernels (bytes 0: not used)
   int loss;
   double delta, diag_floor, lambda, tol;
@@ -77,13 +76,10 @@ struct Dev {
   const int32_t* pt_ptr;
   const int32_t* tile_begin;
   const int32_t* big_tile_begin;
-  const int32_t* chunk_begin;
+  const int32_t* chunk_begin;    // camera-order range of each chunk (n_chunks + 1)
   const int32_t* chunk_cam;
-  const int32_t* cam_chunk_ptr;
-  const int32_t* bchunk_begin;   // band chunks: camera-order ranges within one point band
-  const int32_t* bchunk_cam;
-  const int32_t* cam_bchunk_ptr; // band chunks of each camera, in order
-  const int32_t* band_block;     // band chunk of each block (band = block % kPointBands), -1 none
+  const int32_t* cam_chunk_ptr;  // chunks of each camera, in order
+  const int32_t* chunk_block;    // chunk of each block (band = block % kPointBands), -1 none
   // linearisation
   double* w_pt;
   double* w_cam;

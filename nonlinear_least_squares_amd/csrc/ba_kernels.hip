@@ -59,6 +59,21 @@ __device__ __forceinline__ void block_reduce(double (&v)[K], double* s_buf, doub
   __syncthreads();
 }
 
+// K per-lane partials of one wavefront summed by a fixed butterfly (every lane
+// ends with the same bits); lane 0 stores the totals.
+template <int K>
+__device__ __forceinline__ void wave_reduce_store(double (&v)[K], double* out) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) v[k] += __shfl_xor(v[k], off, kWave);
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) out[k] = v[k];
+  }
+}
+
 // Segmented reduction over whole points for one point-order tile.  Op supplies
 //   compute(s, pt, v[K])  : per-observation contribution (s = point-order index)
 //   finish(pt, v[K])      : called once per point with its total
@@ -213,17 +228,20 @@ __global__ __launch_bounds__(kTile) void k_lin_pt(Dev d) {
   point_tile_reduce<9>(d, op, blockIdx.x);
 }
 
-__global__ __launch_bounds__(kChunkBlock) void k_lin_cam(Dev d) {
-  __shared__ double s_buf[(kChunkBlock / kWave) * kLinCamVals];
-  __shared__ double s_out[kLinCamVals];
-  const int ch = blockIdx.x;
+// Camera chunks are processed one wavefront each; block b takes a chunk of
+// point band b % kPointBands.  Workgroups are placed on the accelerator dies
+// round-robin, so each die gathers the point data of one band only and it
+// stays in that die's L2.
+__global__ __launch_bounds__(kWave) void k_lin_cam(Dev d) {
+  const int ch = d.chunk_block[blockIdx.x];
+  if (ch < 0) return;
   const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
   CamG c;
   load_cam(d.tab, d.chunk_cam[ch], c);
   double acc[kLinCamVals];
 #pragma unroll
   for (int k = 0; k < kLinCamVals; ++k) acc[k] = 0.0;
-  for (int s = cb + threadIdx.x; s < ce; s += kChunkBlock) {
+  for (int s = cb + threadIdx.x; s < ce; s += kWave) {
     const int i = d.c_pt[s];
     Geo g;
     geo_eval(c, d.pts[3 * i], d.pts[3 * i + 1], d.pts[3 * i + 2], g);
@@ -242,9 +260,7 @@ __global__ __launch_bounds__(kChunkBlock) void k_lin_cam(Dev d) {
       acc[45 + a] += wa0 * r0 + wa1 * r1;
     }
   }
-  block_reduce<kLinCamVals, kChunkBlock>(acc, s_buf, s_out);
-  for (int k = threadIdx.x; k < kLinCamVals; k += kChunkBlock)
-    d.lin_part[(int64_t)ch * kLinCamVals + k] = s_out[k];
+  wave_reduce_store<kLinCamVals>(acc, d.lin_part + (int64_t)ch * kLinCamVals);
 }
 
 // ----------------------------------------------------- damping and Schur
@@ -305,17 +321,16 @@ __global__ void k_damp_pt(Dev d) {
 // blocks of S).  Repeated (camera, point) observations share J, so
 // Ebar = (sum of their weights) Jc^T Jp and the run head adds
 // W^2 Jc^T (Jp C~^-1 Jp^T) Jc.
-__global__ __launch_bounds__(kChunkBlock) void k_schur_cam(Dev d) {
-  __shared__ double s_buf[(kChunkBlock / kWave) * kSchurVals];
-  __shared__ double s_out[kSchurVals];
-  const int ch = blockIdx.x;
+__global__ __launch_bounds__(kWave) void k_schur_cam(Dev d) {
+  const int ch = d.chunk_block[blockIdx.x];
+  if (ch < 0) return;
   const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
   CamG c;
   load_cam(d.tab, d.chunk_cam[ch], c);
   double acc[kSchurVals];
 #pragma unroll
   for (int k = 0; k < kSchurVals; ++k) acc[k] = 0.0;
-  for (int s = cb + threadIdx.x; s < ce; s += kChunkBlock) {
+  for (int s = cb + threadIdx.x; s < ce; s += kWave) {
     const int i = d.c_pt[s];
     Geo g;
     geo_eval(c, d.pts[3 * i], d.pts[3 * i + 1], d.pts[3 * i + 2], g);
@@ -355,9 +370,7 @@ __global__ __launch_bounds__(kChunkBlock) void k_schur_cam(Dev d) {
       }
     }
   }
-  block_reduce<kSchurVals, kChunkBlock>(acc, s_buf, s_out);
-  for (int k = threadIdx.x; k < kSchurVals; k += kChunkBlock)
-    d.schur_part[(int64_t)ch * kSchurVals + k] = s_out[k];
+  wave_reduce_store<kSchurVals>(acc, d.schur_part + (int64_t)ch * kSchurVals);
 }
 
 // Per camera: B and g_c as the chunk partials summed in chunk order.
@@ -695,19 +708,14 @@ __global__ __launch_bounds__(kBigTile) void k_pcg_pt_lds(Dev d, int it) {
 
 __global__ __launch_bounds__(kBigTile) void k_backsub_lds(Dev d) { pcg_pt_lds_body<1>(d, 0); }
 
-// Camera side of S p over band chunks: the observations of one camera whose
-// points lie in one of kPointBands equal index bands.  Block b takes a chunk
-// of band b % kPointBands, and workgroups are placed on the accelerator dies
-// round-robin, so each die gathers the point records of one band only and
-// they stay in its L2.  One wavefront per chunk; partials summed by a fixed
-// butterfly.
+// Camera side of S p, one wavefront per camera chunk (placed as in k_lin_cam).
 __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
   if (d.pcg->done) return;
-  const int ch = d.band_block[blockIdx.x];
+  const int ch = d.chunk_block[blockIdx.x];
   if (ch < 0) return;
-  const int cb = d.bchunk_begin[ch], ce = d.bchunk_begin[ch + 1];
+  const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
   CamG c;
-  load_cam(d.tab, d.bchunk_cam[ch], c);
+  load_cam(d.tab, d.chunk_cam[ch], c);
   double acc[9];
 #pragma unroll
   for (int k = 0; k < 9; ++k) acc[k] = 0.0;
@@ -722,12 +730,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
     const double w = d.w_cam[s];
     jct_acc(g, c.f, w * t0, w * t1, acc);
   }
-#pragma unroll
-  for (int k = 0; k < 9; ++k) acc[k] = wave_sum(acc[k]);
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int k = 0; k < 9; ++k) d.pcg_part[(int64_t)ch * 9 + k] = acc[k];
-  }
+  wave_reduce_store<9>(acc, d.pcg_part + (int64_t)ch * 9);
 }
 
 __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
@@ -740,7 +743,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
 #pragma unroll
   for (int b = 0; b < 9; ++b)
     qa += Bd[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)] * p[b];
-  for (int ch = d.cam_bchunk_ptr[c.j]; ch < d.cam_bchunk_ptr[c.j + 1]; ++ch)
+  for (int ch = d.cam_chunk_ptr[c.j]; ch < d.cam_chunk_ptr[c.j + 1]; ++ch)
     qa -= d.pcg_part[(int64_t)ch * 9 + c.a];
   double pq = 0.0;
   if (c.on) {
@@ -1018,13 +1021,13 @@ void launch_lin_pt(const Dev& d, hipStream_t s) {
   if (d.n_tiles > 0) launch(k_lin_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
 }
 void launch_lin_cam(const Dev& d, hipStream_t s) {
-  if (d.n_chunks > 0) launch(k_lin_cam, dim3(d.n_chunks), dim3(kChunkBlock), s, 0u, d);
+  if (d.n_chunk_blocks > 0) launch(k_lin_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
 }
 void launch_damp_pt(const Dev& d, hipStream_t s) {
   if (d.np > 0) launch(k_damp_pt, dim3(blocks_for(d.np, 256)), dim3(256), s, 0u, d);
 }
 void launch_schur_cam(const Dev& d, hipStream_t s) {
-  if (d.n_chunks > 0) launch(k_schur_cam, dim3(d.n_chunks), dim3(kChunkBlock), s, 0u, d);
+  if (d.n_chunk_blocks > 0) launch(k_schur_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
 }
 void launch_lin_final(const Dev& d, hipStream_t s) {
   if (d.nc > 0) launch(k_lin_final, dim3(blocks_for(d.nc, 64)), dim3(64), s, 0u, d);
@@ -1047,7 +1050,7 @@ void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
   }
 }
 void launch_pcg_cam(const Dev& d, hipStream_t s) {
-  if (d.n_band_blocks > 0) launch(k_pcg_cam, dim3(d.n_band_blocks), dim3(kWave), s, 0u, d);
+  if (d.n_chunk_blocks > 0) launch(k_pcg_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
 }
 void launch_pcg_q(const Dev& d, int it, hipStream_t s) {
   launch(k_pcg_q, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
