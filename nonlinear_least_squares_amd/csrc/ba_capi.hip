@@ -80,7 +80,7 @@ struct ba_problem {
   int64_t nc = 0, np = 0, nobs = 0;
   ba_options opt{};
   hipStream_t stream = nullptr;
-  int n_tiles = 0, n_chunks = 0, n_cost_blocks = 0, n_big_tiles = 0, lds_blocks = 0,
+  int n_tiles = 0, n_chunks = 0, n_cost_blocks = 0, lds_blocks = 0,
       cam_lds_bytes = 0, n_chunk_blocks = 0;
   Arena arena;   // everything sized by n_cams, n_pts, n_obs
   Arena arena2;  // partitions and partial sums, sized after the CSR offsets
@@ -94,7 +94,7 @@ struct ba_problem {
   int32_t *o_cam = nullptr, *o_pt = nullptr, *c_pt = nullptr, *run_len = nullptr;
   double *o_uv = nullptr, *c_uv = nullptr;
   int32_t *tile_begin = nullptr, *chunk_begin = nullptr, *chunk_cam = nullptr,
-          *cam_chunk_ptr = nullptr, *big_tile_begin = nullptr, *chunk_block = nullptr;
+          *cam_chunk_ptr = nullptr, *wave_begin = nullptr, *chunk_block = nullptr;
   // work arrays
   double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
          *gc = nullptr, *lin_part = nullptr;
@@ -135,10 +135,9 @@ Dev make_dev(const ba_problem* h) {
   d.n_chunks = h->n_chunks;
   d.n_chunk_blocks = h->n_chunk_blocks;
   d.chunk_block = h->chunk_block;
-  d.n_big_tiles = h->n_big_tiles;
   d.lds_blocks = h->lds_blocks;
   d.cam_lds_bytes = h->cam_lds_bytes;
-  d.big_tile_begin = h->big_tile_begin;
+  d.wave_begin = h->wave_begin;
   d.n_cost_blocks = h->n_cost_blocks;
   d.loss = h->opt.loss;
   d.delta = h->opt.huber_delta;
@@ -555,29 +554,31 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
     }
   }
   if (N > start) tiles.push_back((int32_t)N);
-  // Larger tiles of the same kind for the kernels that keep the camera table
-  // in LDS, when it fits.
-  std::vector<int32_t> big{0};
-  start = 0;
-  for (int64_t i = 0; i < np; ++i) {
-    if (pt_ptr[i + 1] - start > kBigTile && pt_ptr[i] > start) {
-      big.push_back(pt_ptr[i]);
-      start = pt_ptr[i];
-    }
-  }
-  if (N > start) big.push_back((int32_t)N);
-  h->n_big_tiles = (int)big.size() - 1;
+  // The kernels that keep the camera table in LDS run one block per compute
+  // unit; each wavefront takes an equal share of the observations, moved to
+  // the nearest point start at or after the even split.
+  std::vector<int32_t> wave_begin;
   {
     const int64_t bytes = (int64_t)kCamLdsStride * 8 * nc;
     int dev = 0, cus = 0;
     TRY(hipGetDevice(&dev));
     TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     h->cam_lds_bytes = 0;
+    h->lds_blocks = 0;
     const char* off = std::getenv("BA_NO_LDS_CAMERAS");
-    if (bytes <= kCamLdsMaxBytes && h->n_big_tiles > 0 && !(off && off[0] == '1')) {
+    if (bytes <= kCamLdsMaxBytes && N > 0 && !(off && off[0] == '1')) {
       TRY(set_lds_camera_limit((int)bytes));
       h->cam_lds_bytes = (int)bytes;
-      h->lds_blocks = std::min(h->n_big_tiles, std::max(cus, 1));
+      constexpr int wpb = kLdsBlock / kWave;
+      const int64_t want = (N + (int64_t)wpb * kWave - 1) / ((int64_t)wpb * kWave);
+      h->lds_blocks = (int)std::min<int64_t>(std::max(cus, 1), want);
+      const int64_t W = (int64_t)h->lds_blocks * wpb;
+      wave_begin.resize(W + 1);
+      for (int64_t w = 0; w <= W; ++w) {
+        const int64_t target = N * w / W;
+        wave_begin[w] = *std::lower_bound(pt_ptr.begin(), pt_ptr.end(), (int32_t)target);
+      }
+      wave_begin[W] = (int32_t)N;
     }
   }
   // Camera chunks: a camera's observations are sorted by point, so those whose
@@ -622,7 +623,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
 
   Arena& P = h->arena2;
   P.add(h->tile_begin, (int64_t)tiles.size());
-  P.add(h->big_tile_begin, (int64_t)big.size());
+  P.add(h->wave_begin, (int64_t)std::max<size_t>(wave_begin.size(), 1));
   const int64_t n_ch1 = std::max(h->n_chunks, 1);
   P.add(h->chunk_begin, (int64_t)chunk_begin.size());
   P.add(h->chunk_cam, n_ch1);
@@ -637,8 +638,9 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   TRY(hipMemsetAsync(P.base, 0, P.size, s));
   TRY(hipMemcpyAsync(h->tile_begin, tiles.data(), sizeof(int32_t) * tiles.size(),
                      hipMemcpyHostToDevice, s));
-  TRY(hipMemcpyAsync(h->big_tile_begin, big.data(), sizeof(int32_t) * big.size(),
-                     hipMemcpyHostToDevice, s));
+  if (!wave_begin.empty())
+    TRY(hipMemcpyAsync(h->wave_begin, wave_begin.data(), sizeof(int32_t) * wave_begin.size(),
+                       hipMemcpyHostToDevice, s));
   TRY(hipMemcpyAsync(h->chunk_begin, chunk_begin.data(), sizeof(int32_t) * chunk_begin.size(),
                      hipMemcpyHostToDevice, s));
   if (!chunk_cam.empty())

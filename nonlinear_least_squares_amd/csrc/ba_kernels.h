@@ -23,8 +23,9 @@
 
 namespace ba {
 
+constexpr int kWave = 64;         // wavefront width on gfx950
 constexpr int kTile = 256;        // observations per point-order sub-tile (= block size)
-constexpr int kBigTile = 1024;    // sub-tile of the persistent LDS-camera-table kernels
+constexpr int kLdsBlock = 1024;   // threads of the persistent LDS-camera-table kernels
 constexpr int kCamLdsStride = 17; // doubles per camera in the LDS camera table
 constexpr int kCamLdsMaxBytes = 150 * 1024;
 constexpr int kChunk = 512;       // observations per camera chunk (one wavefront)
@@ -56,7 +57,7 @@ struct Dev {
   int64_t nc, np, nobs;
   int n_tiles, n_chunks, n_cost_blocks;
   int n_chunk_blocks;    // blocks of the camera passes (chunk_block entries)
-  int n_big_tiles, lds_blocks, cam_lds_bytes;  // LDS camera-table kernels (bytes 0: not used)
+  int lds_blocks, cam_lds_bytes;  // LDS camera-table kernels (bytes 0: not used)
   int loss;
   double delta, diag_floor, lambda, tol;
   // parameters (current and trial)
@@ -75,7 +76,7 @@ struct Dev {
   const int32_t* run_len;
   const int32_t* pt_ptr;
   const int32_t* tile_begin;
-  const int32_t* big_tile_begin;
+  const int32_t* wave_begin;     // point-order range of each wavefront of the LDS kernels
   const int32_t* chunk_begin;    // camera-order range of each chunk (n_chunks + 1)
   const int32_t* chunk_cam;
   const int32_t* cam_chunk_ptr;  // chunks of each camera, in order

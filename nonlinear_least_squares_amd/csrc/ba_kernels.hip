@@ -15,7 +15,6 @@
 namespace ba {
 namespace {
 
-constexpr int kWave = 64;
 
 __device__ __forceinline__ void load_cam(const CamT* tab, int j, CamG& c) {
   const double4* src = reinterpret_cast<const double4*>(tab + j);
@@ -682,31 +681,128 @@ __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
   point_tile_reduce<3>(d, op, blockIdx.x);
 }
 
-// The same passes with the camera table resident in LDS: one persistent
-// block per compute unit copies the table once (kCamLdsStride doubles per
-// camera, an odd number of dword pairs so that random cameras spread over
-// the banks) and walks the kBigTile-observation point tiles.  Per-lane
-// camera gathers from L1, one cache line per lane, are what bounds the
-// global-table version.
+// The same passes with the camera table resident in LDS.  One persistent
+// block of kLdsBlock threads per compute unit copies the table once
+// (kCamLdsStride doubles per camera, an odd number of dword pairs so that
+// random cameras spread over the banks).  Each wavefront then owns one range
+// of point-order observations that starts and ends on point boundaries and
+// streams through it 64 observations at a time: a segmented scan across the
+// lanes sums each point's observations, a point cut by the 64-slot boundary
+// carries its partial sum in registers into the next slot, and the indices of
+// the next slot are loaded while the current one is computed.  Wavefronts
+// never wait for each other, so one's memory wait hides behind another's
+// arithmetic.
+//   MODE 0: z = C~^-1 (E^T p) into the point records (PCG);
+//   MODE 1: dp = C~^-1 (-g_p - E^T dc) and the trial points (back-substitution).
 template <int MODE>
 __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   extern __shared__ double s_cam[];
-  for (int e = threadIdx.x; e < 16 * d.nc; e += kBigTile) {
+  for (int e = threadIdx.x; e < 16 * d.nc; e += kLdsBlock) {
     const int j = e >> 4, k = e & 15;
     if (k < 15) s_cam[kCamLdsStride * j + k] = reinterpret_cast<const double*>(d.tab + j)[k];
   }
   __syncthreads();
-  PcgPtOp<MODE, true> op{d, it, s_cam, {}, {}};
-  for (int tile = blockIdx.x; tile < d.n_big_tiles; tile += gridDim.x)
-    point_tile_reduce<3, kBigTile>(d, op, tile, d.big_tile_begin);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = blockIdx.x * (kLdsBlock / kWave) + threadIdx.x / kWave;
+  const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
+  const double* xbase = MODE == 0 ? d.pbuf + (int64_t)(it & 1) * 9 * d.nc : d.x;
+  int cpt = -1, cj = 0;
+  if (sb + lane < se) {
+    cpt = d.o_pt[sb + lane];
+    cj = d.o_cam[sb + lane];
+  }
+  double carry[3] = {0.0, 0.0, 0.0};
+  int carry_pt = -1;
+  for (int base = sb; base < se; base += kWave) {
+    const int s = base + lane;
+    int npt = -1, nj = 0;
+    if (s + kWave < se) {
+      npt = d.o_pt[s + kWave];
+      nj = d.o_cam[s + kWave];
+    }
+    const bool valid = cpt >= 0;
+    double v[3] = {0.0, 0.0, 0.0};
+    double ci[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    double gq[3] = {0.0, 0.0, 0.0};
+    if (valid) {
+      const double* Ci = d.Cinv + 6 * (int64_t)cpt;
+#pragma unroll
+      for (int k = 0; k < 6; ++k) ci[k] = Ci[k];
+      if (MODE == 1) {
+        gq[0] = d.gp[3 * cpt];
+        gq[1] = d.gp[3 * cpt + 1];
+        gq[2] = d.gp[3 * cpt + 2];
+      }
+      const double w = d.w_pt[s];
+      const double* xc = xbase + 9 * (int64_t)cj;
+      CamG c;
+      load_cam_lds(s_cam, cj, c);
+      Geo g;
+      geo_eval(c, d.pts[3 * cpt], d.pts[3 * cpt + 1], d.pts[3 * cpt + 2], g);
+      double u0, u1;
+      jc_apply(g, c.f, xc, u0, u1);
+      jpt_apply(g, c.R, w * u0, w * u1, v[0], v[1], v[2]);
+    }
+    // segmented inclusive scan across the lanes
+    const int prev_pt = __shfl_up(cpt, 1, kWave);
+    const bool head = (lane == 0) || (cpt != prev_pt);
+    const unsigned long long heads = __ballot(head);
+    const unsigned long long upto = (lane == kWave - 1) ? ~0ull : ((2ull << lane) - 1ull);
+    const int seg0 = 63 - __clzll(heads & upto);
+#pragma unroll
+    for (int dd = 1; dd < kWave; dd <<= 1) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const double o = __shfl_up(v[k], dd, kWave);
+        if (lane - dd >= seg0) v[k] += o;
+      }
+    }
+    if (valid && seg0 == 0 && cpt == carry_pt) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) v[k] += carry[k];
+    }
+    const int down_pt = __shfl_down(cpt, 1, kWave);
+    const int first_next = __shfl(npt, 0, kWave);
+    const int next_pt = lane == kWave - 1 ? first_next : down_pt;
+    const bool is_end = valid && next_pt != cpt;
+    if (is_end) {
+      double y0 = v[0], y1 = v[1], y2 = v[2];
+      if (MODE == 1) {
+        y0 = -gq[0] - y0;
+        y1 = -gq[1] - y1;
+        y2 = -gq[2] - y2;
+      }
+      const double z0 = ci[0] * y0 + ci[1] * y1 + ci[2] * y2;
+      const double z1 = ci[1] * y0 + ci[3] * y1 + ci[4] * y2;
+      const double z2 = ci[2] * y0 + ci[4] * y1 + ci[5] * y2;
+      if (MODE == 0) {
+        d.prec[8 * (int64_t)cpt + 3] = z0;
+        d.prec[8 * (int64_t)cpt + 4] = z1;
+        d.prec[8 * (int64_t)cpt + 5] = z2;
+      } else {
+        d.dp[3 * cpt] = z0;
+        d.dp[3 * cpt + 1] = z1;
+        d.dp[3 * cpt + 2] = z2;
+        d.pts_trial[3 * cpt] = d.pts[3 * cpt] + z0;
+        d.pts_trial[3 * cpt + 1] = d.pts[3 * cpt + 1] + z1;
+        d.pts_trial[3 * cpt + 2] = d.pts[3 * cpt + 2] + z2;
+      }
+    }
+    // the last lane's running sum carries over when its point goes on
+#pragma unroll
+    for (int k = 0; k < 3; ++k) carry[k] = __shfl(v[k], kWave - 1, kWave);
+    carry_pt = __shfl(valid && !is_end ? cpt : -1, kWave - 1, kWave);
+    cpt = npt;
+    cj = nj;
+  }
 }
 
-__global__ __launch_bounds__(kBigTile) void k_pcg_pt_lds(Dev d, int it) {
+__global__ __launch_bounds__(kLdsBlock) void k_pcg_pt_lds(Dev d, int it) {
   if (d.pcg->done) return;
   pcg_pt_lds_body<0>(d, it);
 }
 
-__global__ __launch_bounds__(kBigTile) void k_backsub_lds(Dev d) { pcg_pt_lds_body<1>(d, 0); }
+__global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d) { pcg_pt_lds_body<1>(d, 0); }
 
 // Camera side of S p, one wavefront per camera chunk (placed as in k_lin_cam).
 __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
@@ -1043,8 +1139,8 @@ void launch_pcg_pnext(const Dev& d, int it, hipStream_t s) {
 }
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
   if (d.cam_lds_bytes > 0) {
-    if (d.n_big_tiles > 0)
-      launch(k_pcg_pt_lds, dim3(d.lds_blocks), dim3(kBigTile), s, d.cam_lds_bytes, d, it);
+    if (d.lds_blocks > 0)
+      launch(k_pcg_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s, d.cam_lds_bytes, d, it);
   } else if (d.n_tiles > 0) {
     launch(k_pcg_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d, it);
   }
@@ -1064,8 +1160,8 @@ void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
 int pcg_red_blocks(int64_t nc) { return cam_vector_blocks(nc); }
 void launch_backsub(const Dev& d, hipStream_t s) {
   if (d.cam_lds_bytes > 0) {
-    if (d.n_big_tiles > 0)
-      launch(k_backsub_lds, dim3(d.lds_blocks), dim3(kBigTile), s, d.cam_lds_bytes, d);
+    if (d.lds_blocks > 0)
+      launch(k_backsub_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s, d.cam_lds_bytes, d);
   } else if (d.n_tiles > 0) {
     launch(k_backsub, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
   }
