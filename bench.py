@@ -9,7 +9,8 @@ relative residual.  Inputs are resident in HBM before the timed region.
 
 Prints one JSON line.  The roofline object refers to the kernel with the
 largest total time in a profiled warm-up run; its average launch time is
-taken with HIP events on the library's stream during the timed region.
+taken with HIP events on the library's stream during the timed region, on
+every eighth launch.
 
 ``--workload dense`` measures the fp32 dense frame-graph variant instead
 (libdba): a step is one Gauss-Newton iteration (linearise, assemble with the
@@ -29,6 +30,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LM iterations/s and observations/s (fp64, 1 GPU); % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
+# The dominant kernel is timed inside the timed region by HIP events that its
+# own dispatch records; a timed dispatch cannot overlap its neighbours, so only
+# every PROFILE_EVERY-th launch is timed, which keeps that cost out of `value`.
+PROFILE_EVERY = 8
 KERNEL_SRC = os.path.join(ROOT, "nonlinear_least_squares_amd", "csrc", "ba_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_large.json")
 
@@ -171,7 +176,7 @@ def main_dense(args):
     print(f"# warm-up kernel totals (launches, ms): {prof}", file=sys.stderr, flush=True)
 
     G = dba.Problem.from_scene(sc)
-    G.profile([dominant])
+    G.profile([dominant], every=PROFILE_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     costs = G.solve(args.steps)
@@ -265,7 +270,7 @@ def main():
     P = ba.Problem.from_scene(sc)
     torch.cuda.synchronize()
     create_s = time.perf_counter() - t0
-    P.profile([dominant])
+    P.profile([dominant], every=PROFILE_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     summ = P.solve(args.steps)

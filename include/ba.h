@@ -214,11 +214,15 @@ enum {
   BA_K_NUM
 };
 
-/* kernel_mask bit k set (k = BA_K_*): each launch of kernel k is bracketed by
- * HIP events on the handle's stream and per-kernel totals accumulate until
- * ba_profile_reset; 0 turns timing off.  PCG launches queued past the
- * iteration at which the solve stopped exit at once and are not counted. */
-int ba_profile_enable(ba_problem* h, int kernel_mask);
+/* kernel_mask bit k set (k = BA_K_*): launches of kernel k are bracketed by
+ * HIP events, recorded by the kernel's own dispatch on the handle's stream, and
+ * per-kernel totals accumulate until ba_profile_reset; 0 turns timing off.
+ * every >= 1 times only every every-th launch of each such kernel (a timed
+ * dispatch cannot overlap its neighbours, so sparse sampling keeps the cost of
+ * timing out of the throughput being timed).  PCG launches queued past the
+ * iteration at which the solve stopped exit at once and are not counted.
+ * Returns BA_ERR_ARG for a null handle or every < 1. */
+int ba_profile_enable(ba_problem* h, int kernel_mask, int every);
 int ba_profile_reset(ba_problem* h);
 /* Launch count and summed duration (ms) of kernel `kernel` (BA_K_*). */
 int ba_profile_get(ba_problem* h, int kernel, int64_t* launches, double* total_ms);

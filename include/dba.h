@@ -140,7 +140,13 @@ enum {
   DBA_K_COST,      /* back-substitution of the last step and cost                            */
   DBA_K_NUM
 };
-int dba_profile_enable(dba_problem* h, int kernel_mask);
+/* kernel_mask bit k set (k = DBA_K_*): launches of kernel k are bracketed by
+ * HIP events recorded by the kernel's own dispatch on the handle's stream;
+ * per-kernel totals accumulate until dba_profile_reset; 0 turns timing off.
+ * every >= 1 times only every every-th launch of each such kernel (a timed
+ * dispatch cannot overlap its neighbours).  DBA_ERR_ARG for a null handle or
+ * every < 1. */
+int dba_profile_enable(dba_problem* h, int kernel_mask, int every);
 int dba_profile_reset(dba_problem* h);
 int dba_profile_get(dba_problem* h, int kernel, int64_t* launches, double* total_ms);
 const char* dba_kernel_name(int kernel);

@@ -93,7 +93,7 @@ SIGNATURES = {
     "ba_debug_run": (C.c_int, [C.c_void_p, C.c_int]),
     "ba_debug_size": (C.c_int64, [C.c_void_p, C.c_int]),
     "ba_debug_get": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int64]),
-    "ba_profile_enable": (C.c_int, [C.c_void_p, C.c_int]),
+    "ba_profile_enable": (C.c_int, [C.c_void_p, C.c_int, C.c_int]),
     "ba_profile_reset": (C.c_int, [C.c_void_p]),
     "ba_profile_get": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_int64),
                                  C.POINTER(C.c_double)]),
@@ -248,13 +248,14 @@ class Problem:
                "ba_debug_get")
         return out.reshape(DBG_SHAPE[name]) if name in DBG_SHAPE else out
 
-    def profile(self, kernels=None):
-        """Time the named kernels (all when None; an empty list turns timing off)."""
+    def profile(self, kernels=None, every=1):
+        """Time the named kernels (all when None; an empty list turns timing off),
+        every ``every``-th launch of each."""
         names = KERNELS if kernels is None else kernels
         mask = 0
         for n in names:
             mask |= 1 << KERNELS.index(n)
-        _check(lib().ba_profile_enable(self.h, mask), "ba_profile_enable")
+        _check(lib().ba_profile_enable(self.h, mask, int(every)), "ba_profile_enable")
 
     def profile_reset(self):
         _check(lib().ba_profile_reset(self.h), "ba_profile_reset")

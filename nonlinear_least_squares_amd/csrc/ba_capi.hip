@@ -98,7 +98,7 @@ struct ba_problem {
   // work arrays
   double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
          *gc = nullptr, *lin_part = nullptr;
-  double *Cinv = nullptr, *v = nullptr, *Bd = nullptr, *rhs = nullptr, *Mchol = nullptr,
+  double *Cinv = nullptr, *v = nullptr, *Bd = nullptr, *rhs = nullptr, *Minv = nullptr,
          *Mfull = nullptr, *schur_part = nullptr;
   double *x = nullptr, *r = nullptr, *zc = nullptr, *pbuf = nullptr, *q = nullptr, *prec = nullptr,
          *pcg_part = nullptr, *pq_cam = nullptr, *red_part = nullptr;
@@ -117,6 +117,8 @@ struct ba_problem {
   int64_t iteration = 0;
   // timing
   int prof_on = 0;
+  int prof_every = 1;
+  int64_t prof_seen[BA_K_NUM] = {0};
   std::vector<ProfRec> prof_recs;
   std::vector<hipEvent_t> prof_pool;
   size_t prof_used = 0;
@@ -173,7 +175,7 @@ Dev make_dev(const ba_problem* h) {
   d.v = h->v;
   d.Bd = h->Bd;
   d.rhs = h->rhs;
-  d.Mchol = h->Mchol;
+  d.Minv = h->Minv;
   d.Mfull = h->Mfull;
   d.schur_part = h->schur_part;
   d.x = h->x;
@@ -202,6 +204,7 @@ Dev make_dev(const ba_problem* h) {
 int prof_begin(ba_problem* h, int kernel, int pcg_iter, hipEvent_t* stop) {
   *stop = nullptr;
   if (!((h->prof_on >> kernel) & 1)) return BA_OK;
+  if (h->prof_seen[kernel]++ % h->prof_every != 0) return BA_OK;
   if (h->prof_used + 2 > h->prof_pool.size()) {
     for (int i = 0; i < 64; ++i) {
       hipEvent_t e;
@@ -465,7 +468,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   A.add(h->gc, 9 * nc);
   A.add(h->Bd, 45 * nc);
   A.add(h->rhs, 9 * nc);
-  A.add(h->Mchol, 45 * nc);
+  A.add(h->Minv, 45 * nc);
   A.add(h->Mfull, 45 * nc);
   A.add(h->x, 9 * nc);
   A.add(h->r, 9 * nc);
@@ -969,9 +972,12 @@ int ba_debug_get(ba_problem* h, int which, void* host_out, int64_t bytes) {
   }
 }
 
-int ba_profile_enable(ba_problem* h, int kernel_mask) {
+int ba_profile_enable(ba_problem* h, int kernel_mask, int every) {
   if (!h) return fail(BA_ERR_ARG, "null handle");
+  if (every < 1) return fail(BA_ERR_ARG, "every must be >= 1");
   h->prof_on = kernel_mask;
+  h->prof_every = every;
+  for (int k = 0; k < BA_K_NUM; ++k) h->prof_seen[k] = 0;
   h->prof_recs.clear();
   h->prof_used = 0;
   return BA_OK;

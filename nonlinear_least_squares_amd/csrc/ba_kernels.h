@@ -9,7 +9,7 @@
 //   per point    : X (3), C (6, packed upper), g_p (3), C~^-1 (6), v (3),
 //                  z (3), dp (3)
 //   per camera   : parameters (9), CamT table (16), B (45), g_c (9), B~ (45),
-//                  rhs (9), Cholesky of S_jj (45), PCG vectors (9 each)
+//                  rhs (9), S_jj^-1 (45, packed), PCG vectors (9 each)
 //   partitions   : point tiles (whole points, <= kTile observations unless a
 //                  single point is longer); camera chunks: the observations
 //                  of one camera whose points lie in one of kPointBands equal
@@ -94,7 +94,7 @@ struct Dev {
   double* v;
   double* Bd;
   double* rhs;
-  double* Mchol;
+  double* Minv;
   double* Mfull;     // undamped-by-Cholesky copy of S_jj (packed) for inspection
   double* schur_part;
   // PCG

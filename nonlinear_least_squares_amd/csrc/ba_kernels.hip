@@ -395,7 +395,9 @@ __global__ void k_lin_final(Dev d) {
 }
 
 // Per camera: B~ = B + lambda D, rhs = -g_c + E v, S_jj = B~ - sum Ebar C~^-1
-// Ebar^T and its Cholesky factor.
+// Ebar^T, and the preconditioner block M_j^-1 = S_jj^-1 formed once from the
+// Cholesky factor, column by column, so that a PCG iteration applies it as a
+// plain 9 x 9 product.
 __global__ void k_precond(Dev d) {
   const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (j >= d.nc) return;
@@ -427,8 +429,16 @@ __global__ void k_precond(Dev d) {
 #pragma unroll
   for (int k = 0; k < 45; ++k) d.Mfull[45 * j + k] = B[k];
   if (!chol_packed<9>(B)) d.flags[1] = 1;
+  double* Mi = d.Minv + 45 * j;
+  for (int b = 0; b < 9; ++b) {
+    double e[9], x[9];
 #pragma unroll
-  for (int k = 0; k < 45; ++k) d.Mchol[45 * j + k] = B[k];
+    for (int a = 0; a < 9; ++a) e[a] = a == b ? 1.0 : 0.0;
+    chol_solve_packed<9>(B, e, x);
+#pragma unroll
+    for (int a = 0; a < 9; ++a)
+      if (a <= b) Mi[sym_idx(9, a, b)] = x[a];
+  }
 }
 
 // ---------------------------------------------------------------------- PCG
@@ -531,25 +541,22 @@ __device__ __forceinline__ CamLane cam_lane(int64_t wave, int64_t nc) {
 }
 
 // z_a of z = M_j^-1 r_j on the 9 lanes of camera j: forward substitution
-// L y = r, then backward L^T z = y, with the packed Cholesky factor of S_jj;
-// each solved component is broadcast to the group by a shuffle.
+// Keeps a loaded value from being sunk below this point: the small PCG kernels
+// issue every load before their stop test, so a launch costs one memory round
+// trip instead of one for the test and one more for the data.
+__device__ __forceinline__ void pin(double& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(int& x) { asm volatile("" : "+v"(x)); }
+
+// z = M_j^-1 r for the lane's row of camera j: the row of the packed inverse
+// times r, whose components come from the group's lanes by shuffles.
 __device__ __forceinline__ double precond_lane(const Dev& d, const CamLane& c, double r) {
-  const double* L = d.Mchol + 45 * c.j;
-  double acc = 0.0, y = 0.0;
+  const double* Mi = d.Minv + 45 * c.j;
+  double m[9];
 #pragma unroll
-  for (int i = 0; i < 9; ++i) {
-    const double yi = __shfl(c.a == i ? (r - acc) / L[sym_idx(9, i, i)] : 0.0, c.base + i, kWave);
-    if (c.a == i) y = yi;
-    if (c.a > i) acc += L[sym_idx(9, i, c.a)] * yi;
-  }
-  acc = 0.0;
+  for (int b = 0; b < 9; ++b) m[b] = Mi[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)];
   double z = 0.0;
 #pragma unroll
-  for (int i = 8; i >= 0; --i) {
-    const double zi = __shfl(c.a == i ? (y - acc) / L[sym_idx(9, i, i)] : 0.0, c.base + i, kWave);
-    if (c.a == i) z = zi;
-    if (c.a < i) acc += L[sym_idx(9, c.a, i)] * zi;
-  }
+  for (int b = 0; b < 9; ++b) z += m[b] * __shfl(r, c.base + b, kWave);
   return z;
 }
 
@@ -567,11 +574,43 @@ __device__ __forceinline__ double wave_sum(double v) {
   return __shfl(v, 0, kWave);
 }
 
-// Sum of n doubles (stride apart) by one wavefront, in a fixed order.
-__device__ __forceinline__ double wave_sum_array(const double* a, int n, int stride) {
-  double v = 0.0;
-  for (int k = threadIdx.x & (kWave - 1); k < n; k += kWave) v += a[(int64_t)k * stride];
-  return wave_sum(v);
+// This lane's share of the sums of NA arrays of n >= 1 doubles each: a[lane],
+// a[lane + 64], ... in that order.  The first four loads of every array are
+// issued unconditionally (clamped index, the value then dropped) before any is
+// used, so they are all in flight together; longer arrays finish in a loop.
+template <int NA>
+__device__ __forceinline__ void lane_partials(const double* const (&a)[NA], int n,
+                                              double (&v)[NA]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  double x[NA][4];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[i][u] = a[i][min(lane + u * kWave, n - 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    v[i] = 0.0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[i] += lane + u * kWave < n ? x[i][u] : 0.0;
+  }
+  if (n > 4 * kWave) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      for (int k = lane + 4 * kWave; k < n; k += kWave) v[i] += a[i][k];
+  }
+}
+
+__device__ __forceinline__ double lane_partial(const double* a, int n) {
+  const double* const arr[1] = {a};
+  double v[1];
+  lane_partials<1>(arr, n, v);
+  return v[0];
+}
+
+// Sum of n >= 1 doubles by one wavefront, in a fixed order.
+__device__ __forceinline__ double wave_sum_array(const double* a, int n) {
+  return wave_sum(lane_partial(a, n));
 }
 
 // Sum of n doubles in index order by one block (fixed tree): every block that
@@ -653,26 +692,37 @@ __global__ __launch_bounds__(kWave) void k_pcg_init(Dev d) {
 // else beta = rz_it / rz_{it-1} and p = z + beta p_prev (iteration 0 keeps the
 // p = z stored by the initialisation).
 __global__ __launch_bounds__(kWave) void k_pcg_pnext(Dev d, int it) {
-  if (d.pcg->done) return;
-  const double rhs_norm = sqrt(wave_sum_array(red_rhs(d), d.red_nb, 1));
+  int done = d.pcg->done;
+  const int64_t e = (int64_t)blockIdx.x * kWave + threadIdx.x;
+  const bool on = e < 9 * d.nc;
+  double* pnew = d.pbuf + (int64_t)(it & 1) * 9 * d.nc;
+  const double* pold = d.pbuf + (int64_t)((it + 1) & 1) * 9 * d.nc;
+  double ze = on ? d.zc[e] : 0.0, pe = on ? pold[e] : 0.0;
+  const double* const arr[4] = {red_rhs(d), red_rr(d, it & 1), red_rz(d, it & 1),
+                                red_rz(d, (it + 1) & 1)};
+  double part[4];
+  lane_partials<4>(arr, d.red_nb, part);
+  double rhs2 = part[0], rr = part[1], rz_new = part[2], rz_old = part[3];
+  pin(rhs2);
+  pin(rr);
+  pin(rz_new);
+  pin(rz_old);
+  pin(ze);
+  pin(pe);
+  pin(done);
+  if (done) return;
+  const double rhs_norm = sqrt(wave_sum(rhs2));
   if (it == 0) {
     if (rhs_norm == 0.0 && blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, 0, 0.0, 0.0, 0);
     return;
   }
-  const double res = sqrt(wave_sum_array(red_rr(d, it & 1), d.red_nb, 1));
+  const double res = sqrt(wave_sum(rr));
   if (res <= d.tol * rhs_norm) {
     if (blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, it, res, rhs_norm, 0);
     return;
   }
-  const double rz_new = wave_sum_array(red_rz(d, it & 1), d.red_nb, 1);
-  const double rz_old = wave_sum_array(red_rz(d, (it + 1) & 1), d.red_nb, 1);
-  const double beta = rz_new / rz_old;
-  double* pnew = d.pbuf + (int64_t)(it & 1) * 9 * d.nc;
-  const double* pold = d.pbuf + (int64_t)((it + 1) & 1) * 9 * d.nc;
-  for (int64_t e = (int64_t)blockIdx.x * kWave + threadIdx.x; e < 9 * d.nc;
-       e += (int64_t)gridDim.x * kWave) {
-    pnew[e] = d.zc[e] + beta * pold[e];
-  }
+  const double beta = wave_sum(rz_new) / wave_sum(rz_old);
+  if (on) pnew[e] = ze + beta * pe;
 }
 
 __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
@@ -697,52 +747,110 @@ __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
 template <int MODE>
 __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   extern __shared__ double s_cam[];
-  for (int e = threadIdx.x; e < 16 * d.nc; e += kLdsBlock) {
-    const int j = e >> 4, k = e & 15;
-    if (k < 15) s_cam[kCamLdsStride * j + k] = reinterpret_cast<const double*>(d.tab + j)[k];
-  }
-  __syncthreads();
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * (kLdsBlock / kWave) + threadIdx.x / kWave;
   const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
   const double* xbase = MODE == 0 ? d.pbuf + (int64_t)(it & 1) * 9 * d.nc : d.x;
-  int cpt = -1, cj = 0;
-  if (sb + lane < se) {
-    cpt = d.o_pt[sb + lane];
-    cj = d.o_cam[sb + lane];
+  // Pipeline: indices two slots ahead, point coordinates and weight one slot
+  // ahead.  Every load in the loop is issued unconditionally (indices past the
+  // range are clamped into it and the results discarded), so the number of
+  // loads in flight is the same on every path and the compiler can wait for
+  // exactly the one it needs.  The first two slots' indices are requested
+  // before the camera table is copied, so the two latencies overlap.
+  const int last = max(se - 1, 0);
+  int p0 = 0, j0 = 0, p1 = 0, j1 = 0;
+  if (sb < se) {
+    const int s0 = sb + lane, s1 = s0 + kWave;
+    p0 = d.o_pt[min(s0, last)];
+    j0 = d.o_cam[min(s0, last)];
+    p1 = d.o_pt[min(s1, last)];
+    j1 = d.o_cam[min(s1, last)];
   }
+  // Camera table: all loads of a round are issued before any LDS store.  The
+  // PCG stop flag is read with the first round and tested only then, so a
+  // working launch does not pay a memory round trip for the test.
+  {
+    constexpr int kRound = 8;
+    const double2* src = reinterpret_cast<const double2*>(d.tab);
+    const int n2 = 8 * (int)d.nc;   // double2 per table (16 doubles per camera)
+    int done = MODE == 0 ? d.pcg->done : 0;
+    for (int e0 = threadIdx.x; e0 < n2; e0 += kRound * kLdsBlock) {
+      double2 t[kRound];
+#pragma unroll
+      for (int u = 0; u < kRound; ++u) {
+        const int e = e0 + u * kLdsBlock;
+        t[u] = src[min(e, n2 - 1)];
+      }
+      if (done) return;
+#pragma unroll
+      for (int u = 0; u < kRound; ++u) {
+        const int e = e0 + u * kLdsBlock;
+        if (e < n2) {
+          const int j = e >> 3, k = 2 * (e & 7);
+          s_cam[kCamLdsStride * j + k] = t[u].x;
+          if (k < 14) s_cam[kCamLdsStride * j + k + 1] = t[u].y;
+        }
+      }
+    }
+    if (done) return;
+  }
+  int cpt = -1, cj = 0, npt = -1, nj = 0;
+  double cx0 = 0.0, cx1 = 0.0, cx2 = 0.0, cw = 0.0;
+  if (sb < se) {
+    const int s0 = sb + lane, s1 = s0 + kWave;
+    cpt = s0 < se ? p0 : -1;
+    cj = j0;
+    npt = s1 < se ? p1 : -1;
+    nj = j1;
+    cx0 = d.pts[3 * p0];
+    cx1 = d.pts[3 * p0 + 1];
+    cx2 = d.pts[3 * p0 + 2];
+    cw = d.w_pt[min(s0, last)];
+  }
+  __syncthreads();
   double carry[3] = {0.0, 0.0, 0.0};
   int carry_pt = -1;
   for (int base = sb; base < se; base += kWave) {
     const int s = base + lane;
-    int npt = -1, nj = 0;
-    if (s + kWave < se) {
-      npt = d.o_pt[s + kWave];
-      nj = d.o_cam[s + kWave];
-    }
     const bool valid = cpt >= 0;
-    double v[3] = {0.0, 0.0, 0.0};
-    double ci[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    double gq[3] = {0.0, 0.0, 0.0};
-    if (valid) {
-      const double* Ci = d.Cinv + 6 * (int64_t)cpt;
+    const int cpt_c = max(cpt, 0);
+    // Loads in a fixed order (the scheduling barriers keep it): the camera
+    // vector this slot needs first, then the point data it needs only at the
+    // end, then the next slots' indices and coordinates.  Waits are by count,
+    // in issue order, so each wait covers only what is needed by then.
+    double xv[9];
+    const double* xc = xbase + 9 * (int64_t)cj;
 #pragma unroll
-      for (int k = 0; k < 6; ++k) ci[k] = Ci[k];
-      if (MODE == 1) {
-        gq[0] = d.gp[3 * cpt];
-        gq[1] = d.gp[3 * cpt + 1];
-        gq[2] = d.gp[3 * cpt + 2];
-      }
-      const double w = d.w_pt[s];
-      const double* xc = xbase + 9 * (int64_t)cj;
-      CamG c;
-      load_cam_lds(s_cam, cj, c);
-      Geo g;
-      geo_eval(c, d.pts[3 * cpt], d.pts[3 * cpt + 1], d.pts[3 * cpt + 2], g);
-      double u0, u1;
-      jc_apply(g, c.f, xc, u0, u1);
-      jpt_apply(g, c.R, w * u0, w * u1, v[0], v[1], v[2]);
+    for (int k = 0; k < 9; ++k) xv[k] = xc[k];
+    __builtin_amdgcn_sched_barrier(0);
+    double ci[6];
+    const double* Ci = d.Cinv + 6 * (int64_t)cpt_c;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) ci[k] = Ci[k];
+    double gq[3] = {0.0, 0.0, 0.0};
+    if (MODE == 1) {
+      gq[0] = d.gp[3 * cpt_c];
+      gq[1] = d.gp[3 * cpt_c + 1];
+      gq[2] = d.gp[3 * cpt_c + 2];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const int s2 = s + 2 * kWave;
+    const int p2 = d.o_pt[min(s2, last)], j2 = d.o_cam[min(s2, last)];
+    const int n2pt = s2 < se ? p2 : -1, n2j = j2;
+    const int npt_c = max(npt, 0);
+    const double nx0 = d.pts[3 * npt_c], nx1 = d.pts[3 * npt_c + 1], nx2 = d.pts[3 * npt_c + 2];
+    const double nw = d.w_pt[min(s + kWave, last)];
+    __builtin_amdgcn_sched_barrier(0);
+    CamG c;
+    load_cam_lds(s_cam, cj, c);
+    Geo g;
+    geo_eval(c, cx0, cx1, cx2, g);
+    double u0, u1;
+    jc_apply(g, c.f, xv, u0, u1);
+    double v[3];
+    jpt_apply(g, c.R, cw * u0, cw * u1, v[0], v[1], v[2]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) v[k] = valid ? v[k] : 0.0;
     // segmented inclusive scan across the lanes
     const int prev_pt = __shfl_up(cpt, 1, kWave);
     const bool head = (lane == 0) || (cpt != prev_pt);
@@ -762,19 +870,23 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
       for (int k = 0; k < 3; ++k) v[k] += carry[k];
     }
     const int down_pt = __shfl_down(cpt, 1, kWave);
-    const int first_next = __shfl(npt, 0, kWave);
+    const int first_next = __shfl(npt, 0, kWave);   // -1 past the range
     const int next_pt = lane == kWave - 1 ? first_next : down_pt;
     const bool is_end = valid && next_pt != cpt;
+    // Pin C~^-1 here, ahead of the store branch: otherwise its loads sink into
+    // the branch and their full latency is paid after the arithmetic.
+#pragma unroll
+    for (int k = 0; k < 6; ++k) asm volatile("" : "+v"(ci[k]));
+    double y0 = v[0], y1 = v[1], y2 = v[2];
+    if (MODE == 1) {
+      y0 = -gq[0] - y0;
+      y1 = -gq[1] - y1;
+      y2 = -gq[2] - y2;
+    }
+    const double z0 = ci[0] * y0 + ci[1] * y1 + ci[2] * y2;
+    const double z1 = ci[1] * y0 + ci[3] * y1 + ci[4] * y2;
+    const double z2 = ci[2] * y0 + ci[4] * y1 + ci[5] * y2;
     if (is_end) {
-      double y0 = v[0], y1 = v[1], y2 = v[2];
-      if (MODE == 1) {
-        y0 = -gq[0] - y0;
-        y1 = -gq[1] - y1;
-        y2 = -gq[2] - y2;
-      }
-      const double z0 = ci[0] * y0 + ci[1] * y1 + ci[2] * y2;
-      const double z1 = ci[1] * y0 + ci[3] * y1 + ci[4] * y2;
-      const double z2 = ci[2] * y0 + ci[4] * y1 + ci[5] * y2;
       if (MODE == 0) {
         d.prec[8 * (int64_t)cpt + 3] = z0;
         d.prec[8 * (int64_t)cpt + 4] = z1;
@@ -783,9 +895,9 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
         d.dp[3 * cpt] = z0;
         d.dp[3 * cpt + 1] = z1;
         d.dp[3 * cpt + 2] = z2;
-        d.pts_trial[3 * cpt] = d.pts[3 * cpt] + z0;
-        d.pts_trial[3 * cpt + 1] = d.pts[3 * cpt + 1] + z1;
-        d.pts_trial[3 * cpt + 2] = d.pts[3 * cpt + 2] + z2;
+        d.pts_trial[3 * cpt] = cx0 + z0;
+        d.pts_trial[3 * cpt + 1] = cx1 + z1;
+        d.pts_trial[3 * cpt + 2] = cx2 + z2;
       }
     }
     // the last lane's running sum carries over when its point goes on
@@ -794,11 +906,16 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     carry_pt = __shfl(valid && !is_end ? cpt : -1, kWave - 1, kWave);
     cpt = npt;
     cj = nj;
+    npt = n2pt;
+    nj = n2j;
+    cx0 = nx0;
+    cx1 = nx1;
+    cx2 = nx2;
+    cw = nw;
   }
 }
 
 __global__ __launch_bounds__(kLdsBlock) void k_pcg_pt_lds(Dev d, int it) {
-  if (d.pcg->done) return;
   pcg_pt_lds_body<0>(d, it);
 }
 
@@ -806,9 +923,9 @@ __global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d) { pcg_pt_lds_b
 
 // Camera side of S p, one wavefront per camera chunk (placed as in k_lin_cam).
 __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
-  if (d.pcg->done) return;
+  const int done = d.pcg->done;
   const int ch = d.chunk_block[blockIdx.x];
-  if (ch < 0) return;
+  if (done || ch < 0) return;
   const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
   CamG c;
   load_cam(d.tab, d.chunk_cam[ch], c);
@@ -830,17 +947,30 @@ __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
 }
 
 __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
-  if (d.pcg->done) return;
-  const int64_t wave = blockIdx.x;
-  const CamLane c = cam_lane(wave, d.nc);
+  const CamLane c = cam_lane(blockIdx.x, d.nc);
   const double* p = d.pbuf + (int64_t)(it & 1) * 9 * d.nc + 9 * c.j;
   const double* Bd = d.Bd + 45 * c.j;
+  int done = d.pcg->done;
+  int c0 = d.cam_chunk_ptr[c.j], c1 = d.cam_chunk_ptr[c.j + 1];
+  double bd[9], pv[9];
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    bd[b] = Bd[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)];
+    pv[b] = p[b];
+  }
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    pin(bd[b]);
+    pin(pv[b]);
+  }
+  pin(c0);
+  pin(c1);
+  pin(done);
+  if (done) return;
   double qa = 0.0;
 #pragma unroll
-  for (int b = 0; b < 9; ++b)
-    qa += Bd[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)] * p[b];
-  for (int ch = d.cam_chunk_ptr[c.j]; ch < d.cam_chunk_ptr[c.j + 1]; ++ch)
-    qa -= d.pcg_part[(int64_t)ch * 9 + c.a];
+  for (int b = 0; b < 9; ++b) qa += bd[b] * pv[b];
+  for (int ch = c0; ch < c1; ++ch) qa -= d.pcg_part[(int64_t)ch * 9 + c.a];
   double pq = 0.0;
   if (c.on) {
     d.q[9 * c.j + c.a] = qa;
@@ -851,8 +981,30 @@ __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
 }
 
 __global__ __launch_bounds__(kWave) void k_pcg_xr(Dev d, int it) {
-  if (d.pcg->done) return;
-  const double pq = wave_sum_array(red_pq(d), d.red_nb, 1);
+  const CamLane c = cam_lane(blockIdx.x, d.nc);
+  const int64_t e = 9 * c.j + c.a;
+  int done = d.pcg->done;
+  double pe = d.pbuf[(int64_t)(it & 1) * 9 * d.nc + e];
+  double xe = d.x[e], re = d.r[e], qe = d.q[e];
+  const double* Mi = d.Minv + 45 * c.j;
+  double m[9];
+#pragma unroll
+  for (int b = 0; b < 9; ++b) m[b] = Mi[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)];
+  const double* const arr[2] = {red_pq(d), red_rz(d, it & 1)};
+  double part[2];
+  lane_partials<2>(arr, d.red_nb, part);
+  double pq = part[0], rz = part[1];
+  pin(pq);
+  pin(rz);
+  pin(pe);
+  pin(xe);
+  pin(re);
+  pin(qe);
+#pragma unroll
+  for (int b = 0; b < 9; ++b) pin(m[b]);
+  pin(done);
+  if (done) return;
+  pq = wave_sum(pq);
   if (!(pq > 0.0) || !isfinite(pq)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       const double rhs_norm = sqrt(block_sum_array_serial(red_rhs(d), d.red_nb));
@@ -861,28 +1013,27 @@ __global__ __launch_bounds__(kWave) void k_pcg_xr(Dev d, int it) {
     }
     return;
   }
-  const double alpha = wave_sum_array(red_rz(d, it & 1), d.red_nb, 1) / pq;
-  const int64_t wave = blockIdx.x;
-  const CamLane c = cam_lane(wave, d.nc);
-  const int64_t e = 9 * c.j + c.a;
+  const double alpha = wave_sum(rz) / pq;
   double r = 0.0;
   if (c.on) {
-    d.x[e] += alpha * d.pbuf[(int64_t)(it & 1) * 9 * d.nc + e];
-    r = d.r[e] - alpha * d.q[e];
+    d.x[e] = xe + alpha * pe;
+    r = re - alpha * qe;
     d.r[e] = r;
   }
-  const double z = precond_lane(d, c, r);
-  double rr = 0.0, rz = 0.0;
+  double z = 0.0;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) z += m[b] * __shfl(r, c.base + b, kWave);
+  double rr = 0.0, rzn = 0.0;
   if (c.on) {
     d.zc[e] = z;
     rr = r * r;
-    rz = r * z;
+    rzn = r * z;
   }
   rr = wave_sum(rr);
-  rz = wave_sum(rz);
+  rzn = wave_sum(rzn);
   if (threadIdx.x == 0) {
     red_rr(d, (it + 1) & 1)[blockIdx.x] = rr;
-    red_rz(d, (it + 1) & 1)[blockIdx.x] = rz;
+    red_rz(d, (it + 1) & 1)[blockIdx.x] = rzn;
   }
 }
 
@@ -890,8 +1041,8 @@ __global__ __launch_bounds__(kWave) void k_pcg_xr(Dev d, int it) {
 // iteration limit (a stop inside the loop has already been recorded).
 __global__ __launch_bounds__(kWave) void k_pcg_final(Dev d, int iters) {
   if (d.pcg->done) return;
-  const double rhs_norm = sqrt(wave_sum_array(red_rhs(d), d.red_nb, 1));
-  const double res = iters == 0 ? rhs_norm : sqrt(wave_sum_array(red_rr(d, iters & 1), d.red_nb, 1));
+  const double rhs_norm = sqrt(wave_sum_array(red_rhs(d), d.red_nb));
+  const double res = iters == 0 ? rhs_norm : sqrt(wave_sum_array(red_rr(d, iters & 1), d.red_nb));
   if (threadIdx.x == 0) stop_pcg(d, iters, res, rhs_norm, 0);
 }
 

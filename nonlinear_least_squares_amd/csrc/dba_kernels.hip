@@ -917,6 +917,8 @@ struct dba_problem {
   float *dbg_r = nullptr, *dbg_ji = nullptr, *dbg_jj = nullptr, *dbg_jd = nullptr;
   // profiling
   int prof_on = 0;
+  int prof_every = 1;
+  int64_t prof_seen[DBA_K_NUM] = {0, 0, 0, 0};
   std::vector<ProfRec> prof_recs;
   std::vector<hipEvent_t> prof_pool;
   size_t prof_used = 0;
@@ -944,7 +946,7 @@ template <typename... KArgs, typename... Args>
 int timed_launch(dba_problem* h, int kid, void (*kernel)(KArgs...), dim3 grid, dim3 block,
                  uint32_t shmem, Args... args) {
   hipEvent_t a = nullptr, b = nullptr;
-  if ((h->prof_on >> kid) & 1) {
+  if (((h->prof_on >> kid) & 1) && h->prof_seen[kid]++ % h->prof_every == 0) {
     if (h->prof_used + 2 > h->prof_pool.size()) {
       for (int i = 0; i < 64; ++i) {
         hipEvent_t e;
@@ -1578,9 +1580,12 @@ int dba_debug_get(dba_problem* h, int which, void* host_out, int64_t bytes) {
   return DBA_OK;
 }
 
-int dba_profile_enable(dba_problem* h, int kernel_mask) {
+int dba_profile_enable(dba_problem* h, int kernel_mask, int every) {
   if (!h) return fail(DBA_ERR_ARG, "null handle");
+  if (every < 1) return fail(DBA_ERR_ARG, "every must be >= 1");
   h->prof_on = kernel_mask;
+  h->prof_every = every;
+  for (int k = 0; k < DBA_K_NUM; ++k) h->prof_seen[k] = 0;
   h->prof_recs.clear();
   h->prof_used = 0;
   return DBA_OK;

@@ -55,7 +55,7 @@ SIGNATURES = {
     "dba_debug_run": (i32, [vp, i32]),
     "dba_debug_size": (i64, [vp, i32]),
     "dba_debug_get": (i32, [vp, i32, vp, i64]),
-    "dba_profile_enable": (i32, [vp, i32]),
+    "dba_profile_enable": (i32, [vp, i32, i32]),
     "dba_profile_reset": (i32, [vp]),
     "dba_profile_get": (i32, [vp, i32, C.POINTER(i64), C.POINTER(C.c_double)]),
     "dba_kernel_name": (C.c_char_p, [i32]),
@@ -185,12 +185,14 @@ class Problem:
                       Jj=(self.E, self.P, 2, 6), Jd=(self.E, self.P, 2))
         return out.reshape(shapes[name]) if name in shapes else out
 
-    def profile(self, kernels=None):
+    def profile(self, kernels=None, every=1):
+        """Time the named kernels (all when None; an empty list turns timing off),
+        every ``every``-th launch of each."""
         names = KERNELS if kernels is None else kernels
         mask = 0
         for n in names:
             mask |= 1 << KERNELS.index(n)
-        _check(lib().dba_profile_enable(self.h, mask), "dba_profile_enable")
+        _check(lib().dba_profile_enable(self.h, mask, int(every)), "dba_profile_enable")
 
     def profile_reset(self):
         _check(lib().dba_profile_reset(self.h), "dba_profile_reset")
