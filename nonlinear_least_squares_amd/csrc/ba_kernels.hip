@@ -747,6 +747,7 @@ __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
 template <int MODE>
 __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   extern __shared__ double s_cam[];
+  __shared__ int s_prog;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * (kLdsBlock / kWave) + threadIdx.x / kWave;
   const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
@@ -794,6 +795,7 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     }
     if (done) return;
   }
+  if (threadIdx.x == 0) s_prog = 0;
   int cpt = -1, cj = 0, npt = -1, nj = 0;
   double cx0 = 0.0, cx1 = 0.0, cx2 = 0.0, cw = 0.0;
   if (sb < se) {
@@ -810,6 +812,7 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   __syncthreads();
   double carry[3] = {0.0, 0.0, 0.0};
   int carry_pt = -1;
+  int mine = 0;
   for (int base = sb; base < se; base += kWave) {
     const int s = base + lane;
     const bool valid = cpt >= 0;
@@ -912,6 +915,25 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     cx1 = nx1;
     cx2 = nx2;
     cw = nw;
+    // Every wavefront has the same number of slots, but the hardware issues
+    // the oldest ready wavefront first, so the youngest would finish last with
+    // the SIMD half idle.  A wavefront behind the block's average progress (an
+    // LDS count of finished slots) raises its issue priority, one ahead lowers
+    // it, which keeps them finishing together.
+    ++mine;
+    int tot = 0;
+    if (lane == 0) tot = atomicAdd(&s_prog, 1) + 1;
+    tot = __builtin_amdgcn_readfirstlane(tot);
+    const int ahead = mine * (kLdsBlock / kWave) - tot;   // in 1/16 slot
+    if (ahead <= -(kLdsBlock / kWave)) {
+      __builtin_amdgcn_s_setprio(3);
+    } else if (ahead <= 0) {
+      __builtin_amdgcn_s_setprio(2);
+    } else if (ahead < (kLdsBlock / kWave)) {
+      __builtin_amdgcn_s_setprio(1);
+    } else {
+      __builtin_amdgcn_s_setprio(0);
+    }
   }
 }
 
