@@ -73,6 +73,52 @@ __device__ __forceinline__ void wave_reduce_store(double (&v)[K], double* out) {
   }
 }
 
+// Lane moves by DPP (a VALU modifier, no LDS traffic).  CTRL is the DPP
+// control (row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143,
+// wave_shr:1 = 0x138, wave_shl:1 = 0x130); lanes whose source is outside the
+// pattern, or whose row is not in ROW_MASK, get `old`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_mov(double x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), CTRL, ROW_MASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), CTRL, ROW_MASK, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov_int(int x, int old) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ double read_lane(double x, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), l);
+  return __hiloint2double(hi, lo);
+}
+
+// Inclusive scan of K values over each run of lanes [seg0, lane]: shifts by
+// 1, 2, 4, 8 inside 16-lane rows, then the last lane of row 0 and of row 2 is
+// added to rows 1 and 3, and lane 31 to rows 2 and 3, each only where the
+// lane's run started before the lanes added.  The order of the additions is
+// fixed, so equal inputs give equal bits.
+template <int K>
+__device__ __forceinline__ void seg_scan_dpp(double (&v)[K], int lane, int seg0) {
+#define SEG_STEP(CTRL, MASK, COND)                       \
+  {                                                      \
+    const bool take = (COND);                            \
+    _Pragma("unroll") for (int k = 0; k < K; ++k) {      \
+      const double o = dpp_mov<CTRL, MASK>(v[k]);        \
+      if (take) v[k] += o;                               \
+    }                                                    \
+  }
+  SEG_STEP(0x111, 0xf, lane - 1 >= seg0)
+  SEG_STEP(0x112, 0xf, lane - 2 >= seg0)
+  SEG_STEP(0x114, 0xf, lane - 4 >= seg0)
+  SEG_STEP(0x118, 0xf, lane - 8 >= seg0)
+  SEG_STEP(0x142, 0xa, (lane & 16) && seg0 < (lane & ~15))
+  SEG_STEP(0x143, 0xc, lane >= 32 && seg0 <= 31)
+#undef SEG_STEP
+}
+
 // Segmented reduction over whole points for one point-order tile.  Op supplies
 //   compute(s, pt, v[K])  : per-observation contribution (s = point-order index)
 //   finish(pt, v[K])      : called once per point with its total
@@ -855,25 +901,18 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) v[k] = valid ? v[k] : 0.0;
     // segmented inclusive scan across the lanes
-    const int prev_pt = __shfl_up(cpt, 1, kWave);
+    const int prev_pt = dpp_mov_int<0x138>(cpt, -1);   // wave_shr:1
     const bool head = (lane == 0) || (cpt != prev_pt);
     const unsigned long long heads = __ballot(head);
     const unsigned long long upto = (lane == kWave - 1) ? ~0ull : ((2ull << lane) - 1ull);
     const int seg0 = 63 - __clzll(heads & upto);
-#pragma unroll
-    for (int dd = 1; dd < kWave; dd <<= 1) {
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const double o = __shfl_up(v[k], dd, kWave);
-        if (lane - dd >= seg0) v[k] += o;
-      }
-    }
+    seg_scan_dpp<3>(v, lane, seg0);
     if (valid && seg0 == 0 && cpt == carry_pt) {
 #pragma unroll
       for (int k = 0; k < 3; ++k) v[k] += carry[k];
     }
-    const int down_pt = __shfl_down(cpt, 1, kWave);
-    const int first_next = __shfl(npt, 0, kWave);   // -1 past the range
+    const int down_pt = dpp_mov_int<0x130>(cpt, -1);   // wave_shl:1
+    const int first_next = __builtin_amdgcn_readlane(npt, 0);   // -1 past the range
     const int next_pt = lane == kWave - 1 ? first_next : down_pt;
     const bool is_end = valid && next_pt != cpt;
     // Pin C~^-1 here, ahead of the store branch: otherwise its loads sink into
@@ -905,8 +944,8 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     }
     // the last lane's running sum carries over when its point goes on
 #pragma unroll
-    for (int k = 0; k < 3; ++k) carry[k] = __shfl(v[k], kWave - 1, kWave);
-    carry_pt = __shfl(valid && !is_end ? cpt : -1, kWave - 1, kWave);
+    for (int k = 0; k < 3; ++k) carry[k] = read_lane(v[k], kWave - 1);
+    carry_pt = __builtin_amdgcn_readlane(valid && !is_end ? cpt : -1, kWave - 1);
     cpt = npt;
     cj = nj;
     npt = n2pt;
