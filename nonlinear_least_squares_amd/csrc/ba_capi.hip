@@ -93,8 +93,9 @@ struct ba_problem {
   int32_t *perm_pt = nullptr, *perm_cam = nullptr, *pt_ptr = nullptr, *cam_ptr = nullptr;
   int32_t *o_cam = nullptr, *o_pt = nullptr, *c_pt = nullptr, *run_len = nullptr;
   double *o_uv = nullptr, *c_uv = nullptr;
-  int32_t *tile_begin = nullptr, *chunk_begin = nullptr, *chunk_cam = nullptr,
-          *cam_chunk_ptr = nullptr, *wave_begin = nullptr, *chunk_block = nullptr;
+  int32_t *tile_begin = nullptr,
+          *cam_chunk_ptr = nullptr, *wave_begin = nullptr;
+  int4* blk_chunk = nullptr;
   // work arrays
   double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
          *gc = nullptr, *lin_part = nullptr;
@@ -136,7 +137,7 @@ Dev make_dev(const ba_problem* h) {
   d.n_tiles = h->n_tiles;
   d.n_chunks = h->n_chunks;
   d.n_chunk_blocks = h->n_chunk_blocks;
-  d.chunk_block = h->chunk_block;
+  d.blk_chunk = h->blk_chunk;
   d.lds_blocks = h->lds_blocks;
   d.cam_lds_bytes = h->cam_lds_bytes;
   d.wave_begin = h->wave_begin;
@@ -161,8 +162,6 @@ Dev make_dev(const ba_problem* h) {
   d.run_len = h->run_len;
   d.pt_ptr = h->pt_ptr;
   d.tile_begin = h->tile_begin;
-  d.chunk_begin = h->chunk_begin;
-  d.chunk_cam = h->chunk_cam;
   d.cam_chunk_ptr = h->cam_chunk_ptr;
   d.w_pt = h->w_pt;
   d.w_cam = h->w_cam;
@@ -615,11 +614,13 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   chunk_begin.push_back((int32_t)N);
   size_t per_band = 0;
   for (auto& v : band_list) per_band = std::max(per_band, v.size());
-  std::vector<int32_t> chunk_block(per_band * kPointBands, -1);
+  std::vector<int4> blk_chunk(per_band * kPointBands, make_int4(0, 0, 0, -1));
   for (int bnd = 0; bnd < kPointBands; ++bnd)
-    for (size_t i = 0; i < band_list[bnd].size(); ++i)
-      chunk_block[i * kPointBands + bnd] = band_list[bnd][i];
-  h->n_chunk_blocks = (int)chunk_block.size();
+    for (size_t i = 0; i < band_list[bnd].size(); ++i) {
+      const int32_t ch = band_list[bnd][i];
+      blk_chunk[i * kPointBands + bnd] = make_int4(chunk_begin[ch], chunk_begin[ch + 1], chunk_cam[ch], ch);
+    }
+  h->n_chunk_blocks = (int)blk_chunk.size();
   h->n_tiles = (int)tiles.size() - 1;
   h->n_chunks = (int)chunk_cam.size();
   h->n_cost_blocks = (int)((N + kCostBlock - 1) / kCostBlock);
@@ -628,9 +629,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   P.add(h->tile_begin, (int64_t)tiles.size());
   P.add(h->wave_begin, (int64_t)std::max<size_t>(wave_begin.size(), 1));
   const int64_t n_ch1 = std::max(h->n_chunks, 1);
-  P.add(h->chunk_begin, (int64_t)chunk_begin.size());
-  P.add(h->chunk_cam, n_ch1);
-  P.add(h->chunk_block, (int64_t)std::max<size_t>(chunk_block.size(), 1));
+  P.add(h->blk_chunk, (int64_t)std::max<size_t>(blk_chunk.size(), 1));
   P.add(h->lin_part, n_ch1 * kLinCamVals);
   P.add(h->schur_part, n_ch1 * kSchurVals);
   P.add(h->pcg_part, n_ch1 * 9);
@@ -644,13 +643,8 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   if (!wave_begin.empty())
     TRY(hipMemcpyAsync(h->wave_begin, wave_begin.data(), sizeof(int32_t) * wave_begin.size(),
                        hipMemcpyHostToDevice, s));
-  TRY(hipMemcpyAsync(h->chunk_begin, chunk_begin.data(), sizeof(int32_t) * chunk_begin.size(),
-                     hipMemcpyHostToDevice, s));
-  if (!chunk_cam.empty())
-    TRY(hipMemcpyAsync(h->chunk_cam, chunk_cam.data(), sizeof(int32_t) * chunk_cam.size(),
-                       hipMemcpyHostToDevice, s));
-  if (!chunk_block.empty())
-    TRY(hipMemcpyAsync(h->chunk_block, chunk_block.data(), sizeof(int32_t) * chunk_block.size(),
+  if (!blk_chunk.empty())
+    TRY(hipMemcpyAsync(h->blk_chunk, blk_chunk.data(), sizeof(int4) * blk_chunk.size(),
                        hipMemcpyHostToDevice, s));
   TRY(hipMemcpyAsync(h->cam_chunk_ptr, cam_chunk_ptr.data(), sizeof(int32_t) * (nc + 1),
                      hipMemcpyHostToDevice, s));

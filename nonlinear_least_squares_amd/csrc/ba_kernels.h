@@ -28,8 +28,9 @@ constexpr int kTile = 256;        // observations per point-order sub-tile (= bl
 constexpr int kLdsBlock = 1024;   // threads of the persistent LDS-camera-table kernels
 constexpr int kCamLdsStride = 17; // doubles per camera in the LDS camera table
 constexpr int kCamLdsMaxBytes = 150 * 1024;
-constexpr int kChunk = 512;       // observations per camera chunk (one wavefront)
-constexpr int kPointBands = 8;    // point-index bands of the camera chunks (one per XCD)
+constexpr int kChunk = 1024;      // observations per camera chunk (one wavefront)
+constexpr int kPointBands = 4;    // point-index bands of the camera chunks (block b: band b % 4,
+                                  // on dies b % 8: two dies' L2 per band)
 constexpr int kCostBlock = 1024;  // observations per cost-reduction block
 constexpr int kUpdBlock = 1024;   // threads of the single-block cost reduction
 constexpr int kLinCamVals = 54;   // B (45) + g_c (9)
@@ -56,7 +57,7 @@ struct StepOut {     // everything the host reads back after a step
 struct Dev {
   int64_t nc, np, nobs;
   int n_tiles, n_chunks, n_cost_blocks;
-  int n_chunk_blocks;    // blocks of the camera passes (chunk_block entries)
+  int n_chunk_blocks;    // blocks of the camera passes (blk_chunk entries)
   int lds_blocks, cam_lds_bytes;  // LDS camera-table kernels (bytes 0: not used)
   int loss;
   double delta, diag_floor, lambda, tol;
@@ -77,10 +78,9 @@ struct Dev {
   const int32_t* pt_ptr;
   const int32_t* tile_begin;
   const int32_t* wave_begin;     // point-order range of each wavefront of the LDS kernels
-  const int32_t* chunk_begin;    // camera-order range of each chunk (n_chunks + 1)
-  const int32_t* chunk_cam;
   const int32_t* cam_chunk_ptr;  // chunks of each camera, in order
-  const int32_t* chunk_block;    // chunk of each block (band = block % kPointBands), -1 none
+  const int4* blk_chunk;         // per block of the camera passes: chunk begin, end, camera,
+                                 // chunk id (band = block % kPointBands; id -1: no chunk)
   // linearisation
   double* w_pt;
   double* w_cam;

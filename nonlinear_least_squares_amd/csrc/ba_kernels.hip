@@ -278,11 +278,11 @@ __global__ __launch_bounds__(kTile) void k_lin_pt(Dev d) {
 // round-robin, so each die gathers the point data of one band only and it
 // stays in that die's L2.
 __global__ __launch_bounds__(kWave) void k_lin_cam(Dev d) {
-  const int ch = d.chunk_block[blockIdx.x];
+  const int4 bi = d.blk_chunk[blockIdx.x];
+  const int cb = bi.x, ce = bi.y, ch = bi.w;
   if (ch < 0) return;
-  const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
   CamG c;
-  load_cam(d.tab, d.chunk_cam[ch], c);
+  load_cam(d.tab, bi.z, c);
   double acc[kLinCamVals];
 #pragma unroll
   for (int k = 0; k < kLinCamVals; ++k) acc[k] = 0.0;
@@ -367,11 +367,11 @@ __global__ void k_damp_pt(Dev d) {
 // Ebar = (sum of their weights) Jc^T Jp and the run head adds
 // W^2 Jc^T (Jp C~^-1 Jp^T) Jc.
 __global__ __launch_bounds__(kWave) void k_schur_cam(Dev d) {
-  const int ch = d.chunk_block[blockIdx.x];
+  const int4 bi = d.blk_chunk[blockIdx.x];
+  const int cb = bi.x, ce = bi.y, ch = bi.w;
   if (ch < 0) return;
-  const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
   CamG c;
-  load_cam(d.tab, d.chunk_cam[ch], c);
+  load_cam(d.tab, bi.z, c);
   double acc[kSchurVals];
 #pragma unroll
   for (int k = 0; k < kSchurVals; ++k) acc[k] = 0.0;
@@ -983,28 +983,68 @@ __global__ __launch_bounds__(kLdsBlock) void k_pcg_pt_lds(Dev d, int it) {
 __global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d) { pcg_pt_lds_body<1>(d, 0); }
 
 // Camera side of S p, one wavefront per camera chunk (placed as in k_lin_cam).
+// The camera is uniform, so its parameters sit in scalar registers.  Loads run
+// ahead of the arithmetic (point indices two slots, point records one slot),
+// issued unconditionally with indices clamped into the chunk; slots past the
+// chunk's end get weight 0.  The loop body is written out for two slots so
+// that the two record buffers alternate in place: loop-carried copies would
+// make each iteration wait for the loads it has just issued.  The lane sums
+// are added by a DPP scan.
+struct PtRec {
+  double4 a;   // X, z0
+  double2 b;   // z1, z2
+  double w;
+};
+
+__device__ __forceinline__ void pcg_cam_slot(const CamG& c, const PtRec& r, bool on,
+                                             double (&acc)[9]) {
+  Geo g;
+  geo_eval(c, r.a.x, r.a.y, r.a.z, g);
+  double t0, t1;
+  jp_apply(g, c.R, r.a.w, r.b.x, r.b.y, t0, t1);
+  const double w = on ? r.w : 0.0;
+  jct_acc(g, c.f, w * t0, w * t1, acc);
+}
+
 __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
   const int done = d.pcg->done;
-  const int ch = d.chunk_block[blockIdx.x];
+  const int4 bi = d.blk_chunk[blockIdx.x];
+  const int cb = bi.x, ce = bi.y, ch = bi.w;
   if (done || ch < 0) return;
-  const int cb = d.chunk_begin[ch], ce = d.chunk_begin[ch + 1];
+  const int lane = threadIdx.x;
+  const int last = ce - 1;   // chunks are never empty
   CamG c;
-  load_cam(d.tab, d.chunk_cam[ch], c);
+  load_cam(d.tab, bi.z, c);
+  const double* pr = d.prec;
+  auto load_rec = [&](int i, int s, PtRec& r) {
+    r.a = *reinterpret_cast<const double4*>(pr + 8 * (int64_t)i);
+    r.b = *reinterpret_cast<const double2*>(pr + 8 * (int64_t)i + 4);
+    r.w = d.w_cam[min(s, last)];
+  };
+  PtRec ra, rb;
+  int ib = d.c_pt[min(cb + lane + kWave, last)];
+  load_rec(d.c_pt[min(cb + lane, last)], cb + lane, ra);
   double acc[9];
 #pragma unroll
   for (int k = 0; k < 9; ++k) acc[k] = 0.0;
-  for (int s = cb + threadIdx.x; s < ce; s += kWave) {
-    const int i = d.c_pt[s];
-    const double4 a = *reinterpret_cast<const double4*>(d.prec + 8 * (int64_t)i);
-    const double2 b = *reinterpret_cast<const double2*>(d.prec + 8 * (int64_t)i + 4);
-    Geo g;
-    geo_eval(c, a.x, a.y, a.z, g);
-    double t0, t1;
-    jp_apply(g, c.R, a.w, b.x, b.y, t0, t1);
-    const double w = d.w_cam[s];
-    jct_acc(g, c.f, w * t0, w * t1, acc);
+  for (int base = cb; base < ce; base += 2 * kWave) {
+    const int s = base + lane;
+    const int ic = d.c_pt[min(s + 2 * kWave, last)];
+    load_rec(ib, s + kWave, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    pcg_cam_slot(c, ra, s < ce, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    ib = d.c_pt[min(s + 3 * kWave, last)];
+    load_rec(ic, s + 2 * kWave, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    pcg_cam_slot(c, rb, s + kWave < ce, acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  wave_reduce_store<9>(acc, d.pcg_part + (int64_t)ch * 9);
+  seg_scan_dpp<9>(acc, lane, 0);
+  if (lane == kWave - 1) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) d.pcg_part[(int64_t)ch * 9 + k] = acc[k];
+  }
 }
 
 __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
