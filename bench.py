@@ -75,6 +75,16 @@ def algorithmic_bytes(kernel, n_obs, n_pts, n_cams, n_chunks):
     return None
 
 
+def camera_chunks(obs_cam, obs_pt, n_pts, bands=4, chunk=1024):
+    """Number of camera-order chunks of libba's camera passes: the observations
+    of one camera whose points lie in one of `bands` equal point-index bands,
+    cut into pieces of at most `chunk` (the library's kPointBands, kChunk)."""
+    import numpy as np
+    key = obs_cam.astype(np.int64) * bands + (obs_pt.astype(np.int64) * bands) // max(n_pts, 1)
+    cnt = np.bincount(key)
+    return int(np.sum((cnt + chunk - 1) // chunk))
+
+
 def kernel_hash():
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -277,8 +287,7 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     launches, kms = P.profile_get()[dominant]
-    n_chunks = sum(max(1, -(-int(c) // 1024)) for c in
-                   __import__("numpy").bincount(sc["obs_cam"], minlength=n_cams))
+    n_chunks = camera_chunks(sc["obs_cam"], sc["obs_pt"], n_pts)
     value = args.steps / dt
 
     nbytes = algorithmic_bytes(dominant, n_obs, n_pts, n_cams, n_chunks)
