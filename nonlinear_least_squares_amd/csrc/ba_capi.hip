@@ -88,6 +88,7 @@ struct ba_problem {
   double* cams[2] = {nullptr, nullptr};
   double* pts[2] = {nullptr, nullptr};
   CamT* tab[2] = {nullptr, nullptr};
+  double* camq[2] = {nullptr, nullptr};
   int cur = 0;
   // structure
   int32_t *perm_pt = nullptr, *perm_cam = nullptr, *pt_ptr = nullptr, *cam_ptr = nullptr;
@@ -151,9 +152,11 @@ Dev make_dev(const ba_problem* h) {
   d.cams = h->cams[c];
   d.pts = h->pts[c];
   d.tab = h->tab[c];
+  d.camq = h->camq[c];
   d.cams_trial = h->cams[t];
   d.pts_trial = h->pts[t];
   d.tab_trial = h->tab[t];
+  d.camq_trial = h->camq[t];
   d.o_cam = h->o_cam;
   d.o_pt = h->o_pt;
   d.o_uv = h->o_uv;
@@ -444,6 +447,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
     A.add(h->cams[b], 9 * nc);
     A.add(h->pts[b], 3 * np);
     A.add(h->tab[b], nc);
+    A.add(h->camq[b], 4 * nc);
   }
   A.add(h->perm_pt, N);
   A.add(h->perm_cam, N);
@@ -774,7 +778,7 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
   h->lambda = h->opt.lambda0;
   h->linearized = 0;
   h->iteration = 0;
-  launch_cam_prep(h->cams[0], h->tab[0], h->nc, h->stream);
+  launch_cam_prep(h->cams[0], h->tab[0], h->camq[0], h->nc, h->stream);
   double c = 0.0;
   rc = current_cost(h, &c);
   if (rc == BA_OK && !std::isfinite(c)) rc = fail(BA_ERR_NONFINITE, "initial cost is not finite");
@@ -839,7 +843,7 @@ int ba_set_params(ba_problem* h, const double* cams, const double* points) {
   HIPC(hipMemcpyAsync(flags, h->flags, sizeof(flags), hipMemcpyDeviceToHost, h->stream));
   HIPC(hipStreamSynchronize(h->stream));
   if (flags[1]) return fail(BA_ERR_NONFINITE, "non-finite parameters");
-  launch_cam_prep(h->cams[h->cur], h->tab[h->cur], h->nc, h->stream);
+  launch_cam_prep(h->cams[h->cur], h->tab[h->cur], h->camq[h->cur], h->nc, h->stream);
   double c = 0.0;
   CHECK_RC(current_cost(h, &c));
   if (!std::isfinite(c)) return fail(BA_ERR_NONFINITE, "cost is not finite");

@@ -26,8 +26,9 @@ namespace ba {
 constexpr int kWave = 64;         // wavefront width on gfx950
 constexpr int kTile = 256;        // observations per point-order sub-tile (= block size)
 constexpr int kLdsBlock = 1024;   // threads of the persistent LDS-camera-table kernels
-constexpr int kCamLdsStride = 17; // doubles per camera in the LDS camera table
-constexpr int kCamLdsMaxBytes = 150 * 1024;
+constexpr int kCamLdsStride = 19; // doubles per camera in the LDS table: q (4), t, f, k1, k2, vector (9)
+constexpr int kCamLdsFill = 20;   // table elements per thread in the copy (>= 19 * max cameras / kLdsBlock)
+constexpr int kCamLdsMaxBytes = kCamLdsStride * 8 * (kCamLdsFill * 1024 / kCamLdsStride);  // 1,077 cameras
 constexpr int kChunk = 1024;      // observations per camera chunk (one wavefront)
 constexpr int kPointBands = 4;    // point-index bands of the camera chunks (block b: band b % 4,
                                   // on dies b % 8: two dies' L2 per band)
@@ -65,9 +66,11 @@ struct Dev {
   const double* cams;
   const double* pts;
   const CamT* tab;
+  const double* camq;    // unit quaternion of each camera (4), R = quat_to_R(camq)
   double* cams_trial;
   double* pts_trial;
   CamT* tab_trial;
+  double* camq_trial;
   // structure
   const int32_t* o_cam;
   const int32_t* o_pt;
@@ -129,7 +132,7 @@ DispatchEvents& dispatch_events();
 // Allows the LDS-camera-table kernels `bytes` of dynamic LDS.
 hipError_t set_lds_camera_limit(int bytes);
 
-void launch_cam_prep(const double* cams, CamT* tab, int64_t nc, hipStream_t s);
+void launch_cam_prep(const double* cams, CamT* tab, double* camq, int64_t nc, hipStream_t s);
 void launch_lin_pt(const Dev& d, hipStream_t s);
 void launch_lin_cam(const Dev& d, hipStream_t s);
 void launch_damp_pt(const Dev& d, hipStream_t s);

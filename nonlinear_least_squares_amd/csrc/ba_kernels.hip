@@ -25,14 +25,6 @@ __device__ __forceinline__ void load_cam(const CamT* tab, int j, CamG& c) {
   c.f = f.x; c.k1 = f.y; c.k2 = f.z;
 }
 
-__device__ __forceinline__ void load_cam_lds(const double* s_cam, int j, CamG& c) {
-  const double* r = s_cam + kCamLdsStride * j;
-#pragma unroll
-  for (int k = 0; k < 9; ++k) c.R[k] = r[k];
-  c.t[0] = r[9]; c.t[1] = r[10]; c.t[2] = r[11];
-  c.f = r[12]; c.k1 = r[13]; c.k2 = r[14];
-}
-
 // ---------------------------------------------------------------- reductions
 
 // Deterministic block reduction of K values; the total lands in s_out[0..K).
@@ -75,12 +67,13 @@ __device__ __forceinline__ void wave_reduce_store(double (&v)[K], double* out) {
 
 // Lane moves by DPP (a VALU modifier, no LDS traffic).  CTRL is the DPP
 // control (row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143,
-// wave_shr:1 = 0x138, wave_shl:1 = 0x130); lanes whose source is outside the
-// pattern, or whose row is not in ROW_MASK, get `old`.
-template <int CTRL, int ROW_MASK = 0xf>
+// wave_shr:1 = 0x138, wave_shl:1 = 0x130).  Lanes whose source lies outside the
+// pattern read 0 (bound_ctrl), so every lane gets either another lane's value
+// or 0, and no destination needs clearing first.
+template <int CTRL>
 __device__ __forceinline__ double dpp_mov(double x) {
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), CTRL, ROW_MASK, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), CTRL, ROW_MASK, 0xf, false);
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), CTRL, 0xf, 0xf, true);
   return __hiloint2double(hi, lo);
 }
 
@@ -98,24 +91,24 @@ __device__ __forceinline__ double read_lane(double x, int l) {
 // Inclusive scan of K values over each run of lanes [seg0, lane]: shifts by
 // 1, 2, 4, 8 inside 16-lane rows, then the last lane of row 0 and of row 2 is
 // added to rows 1 and 3, and lane 31 to rows 2 and 3, each only where the
-// lane's run started before the lanes added.  The order of the additions is
-// fixed, so equal inputs give equal bits.
+// lane's run started before the lanes added.  A step adds fma(m, moved, v) with
+// m = 1 or 0: the same bits as adding or not (every lane holds a finite value,
+// so 0 * moved is a zero), without a select per value.  The order of the
+// additions is fixed, so equal inputs give equal bits.
 template <int K>
 __device__ __forceinline__ void seg_scan_dpp(double (&v)[K], int lane, int seg0) {
-#define SEG_STEP(CTRL, MASK, COND)                       \
+#define SEG_STEP(CTRL, COND)                             \
   {                                                      \
-    const bool take = (COND);                            \
-    _Pragma("unroll") for (int k = 0; k < K; ++k) {      \
-      const double o = dpp_mov<CTRL, MASK>(v[k]);        \
-      if (take) v[k] += o;                               \
-    }                                                    \
+    const double m = (COND) ? 1.0 : 0.0;                 \
+    _Pragma("unroll") for (int k = 0; k < K; ++k)        \
+      v[k] = fma(m, dpp_mov<CTRL>(v[k]), v[k]);          \
   }
-  SEG_STEP(0x111, 0xf, lane - 1 >= seg0)
-  SEG_STEP(0x112, 0xf, lane - 2 >= seg0)
-  SEG_STEP(0x114, 0xf, lane - 4 >= seg0)
-  SEG_STEP(0x118, 0xf, lane - 8 >= seg0)
-  SEG_STEP(0x142, 0xa, (lane & 16) && seg0 < (lane & ~15))
-  SEG_STEP(0x143, 0xc, lane >= 32 && seg0 <= 31)
+  SEG_STEP(0x111, lane - 1 >= seg0)
+  SEG_STEP(0x112, lane - 2 >= seg0)
+  SEG_STEP(0x114, lane - 4 >= seg0)
+  SEG_STEP(0x118, lane - 8 >= seg0)
+  SEG_STEP(0x142, (lane & 16) && seg0 < (lane & ~15))
+  SEG_STEP(0x143, lane >= 32 && seg0 <= 31)
 #undef SEG_STEP
 }
 
@@ -220,12 +213,19 @@ __device__ __forceinline__ void store_geometry(CamT* dst, const CamG& c) {
   o[3] = make_double4(c.f, c.k1, c.k2, 0.0);
 }
 
-__global__ void k_cam_prep(const double* __restrict__ cams, CamT* __restrict__ tab, int64_t nc) {
+// Camera geometry from the parameters: the unit quaternion of the rotation
+// vector (kept for the kernels that hold cameras in LDS) and R formed from it.
+__global__ void k_cam_prep(const double* __restrict__ cams, CamT* __restrict__ tab,
+                           double* __restrict__ camq, int64_t nc) {
   const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (j >= nc) return;
   const double* c = cams + 9 * j;
   CamG t;
-  so3_exp(c[0], c[1], c[2], t.R);
+  double q[4];
+  quat_from_rotvec(c[0], c[1], c[2], q);
+  quat_to_R(q, t.R);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) camq[4 * j + k] = q[k];
   t.t[0] = c[3];
   t.t[1] = c[4];
   t.t[2] = c[5];
@@ -501,11 +501,10 @@ __device__ __forceinline__ double block_sum(double v, double* s_buf) {
 // the point record (MODE 0).  MODE 1
 // (back-substitution): dp_i = C~_i^-1 (-g_p,i - sum_k w Jp^T (Jc dc_cam(k))) and
 // the trial point.
-template <int MODE, bool LDS = false>
+template <int MODE>
 struct PcgPtOp {
   const Dev& d;
   int it;
-  const double* s_cam;   // LDS copy of the camera table (LDS only)
   double ci[6];          // C~^-1 of this thread's point, loaded with the point
   double gq[3];          // g_p of this thread's point (back-substitution)
   __device__ void compute(int s, int pt, double* v) {
@@ -521,11 +520,7 @@ struct PcgPtOp {
       gq[2] = d.gp[3 * pt + 2];
     }
     CamG c;
-    if constexpr (LDS) {
-      load_cam_lds(s_cam, j, c);
-    } else {
-      load_cam(d.tab, j, c);
-    }
+    load_cam(d.tab, j, c);
     const double* xc = MODE == 0 ? d.pbuf + (int64_t)(it & 1) * 9 * d.nc + 9 * (int64_t)j
                                  : d.x + 9 * (int64_t)j;
     Geo g;
@@ -561,7 +556,7 @@ struct PcgPtOp {
 };
 
 __global__ __launch_bounds__(kTile) void k_backsub(Dev d) {
-  PcgPtOp<1> op{d, 0, nullptr, {}, {}};
+  PcgPtOp<1> op{d, 0, {}, {}};
   point_tile_reduce<3>(d, op, blockIdx.x);
 }
 
@@ -773,14 +768,14 @@ __global__ __launch_bounds__(kWave) void k_pcg_pnext(Dev d, int it) {
 
 __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
   if (d.pcg->done) return;
-  PcgPtOp<0> op{d, it, nullptr, {}, {}};
+  PcgPtOp<0> op{d, it, {}, {}};
   point_tile_reduce<3>(d, op, blockIdx.x);
 }
 
 // The same passes with the camera table resident in LDS.  One persistent
 // block of kLdsBlock threads per compute unit copies the table once
 // (kCamLdsStride doubles per camera, an odd number of dword pairs so that
-// random cameras spread over the banks).  Each wavefront then owns one range
+// random cameras spread over the banks; R is formed from the row's quaternion).  Each wavefront then owns one range
 // of point-order observations that starts and ends on point boundaries and
 // streams through it 64 observations at a time: a segmented scan across the
 // lanes sums each point's observations, a point cut by the 64-slot boundary
@@ -813,33 +808,32 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     p1 = d.o_pt[min(s1, last)];
     j1 = d.o_cam[min(s1, last)];
   }
-  // Camera table: all loads of a round are issued before any LDS store.  The
-  // PCG stop flag is read with the first round and tested only then, so a
-  // working launch does not pay a memory round trip for the test.
+  // Camera table: one row of kCamLdsStride doubles per camera, the unit
+  // quaternion, t, f, k1, k2 (from the geometry tables) and the camera's
+  // 9-vector that this pass applies (p in the PCG, dc in the back-substitution),
+  // so that the loop reads no camera data from memory.  Every thread issues all
+  // of its loads before its first LDS store.  The PCG stop flag is read with
+  // them and tested only then, so a working launch does not pay a memory round
+  // trip for the test.
   {
-    constexpr int kRound = 8;
-    const double2* src = reinterpret_cast<const double2*>(d.tab);
-    const int n2 = 8 * (int)d.nc;   // double2 per table (16 doubles per camera)
+    const int ne = kCamLdsStride * (int)d.nc;
+    const double* tabd = reinterpret_cast<const double*>(d.tab);
     int done = MODE == 0 ? d.pcg->done : 0;
-    for (int e0 = threadIdx.x; e0 < n2; e0 += kRound * kLdsBlock) {
-      double2 t[kRound];
+    double t[kCamLdsFill];
 #pragma unroll
-      for (int u = 0; u < kRound; ++u) {
-        const int e = e0 + u * kLdsBlock;
-        t[u] = src[min(e, n2 - 1)];
-      }
-      if (done) return;
-#pragma unroll
-      for (int u = 0; u < kRound; ++u) {
-        const int e = e0 + u * kLdsBlock;
-        if (e < n2) {
-          const int j = e >> 3, k = 2 * (e & 7);
-          s_cam[kCamLdsStride * j + k] = t[u].x;
-          if (k < 14) s_cam[kCamLdsStride * j + k + 1] = t[u].y;
-        }
-      }
+    for (int u = 0; u < kCamLdsFill; ++u) {
+      const int e = min((int)threadIdx.x + u * kLdsBlock, ne - 1);
+      const int j = e / kCamLdsStride, k = e - j * kCamLdsStride;
+      const double* src = k < 4 ? d.camq + 4 * j + k
+                                : (k < 10 ? tabd + 16 * j + 9 + (k - 4) : xbase + 9 * j + (k - 10));
+      t[u] = *src;
     }
     if (done) return;
+#pragma unroll
+    for (int u = 0; u < kCamLdsFill; ++u) {
+      const int e = (int)threadIdx.x + u * kLdsBlock;
+      if (e < ne) s_cam[e] = t[u];
+    }
   }
   if (threadIdx.x == 0) s_prog = 0;
   int cpt = -1, cj = 0, npt = -1, nj = 0;
@@ -863,15 +857,12 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     const int s = base + lane;
     const bool valid = cpt >= 0;
     const int cpt_c = max(cpt, 0);
-    // Loads in a fixed order (the scheduling barriers keep it): the camera
-    // vector this slot needs first, then the point data it needs only at the
-    // end, then the next slots' indices and coordinates.  Waits are by count,
-    // in issue order, so each wait covers only what is needed by then.
-    double xv[9];
-    const double* xc = xbase + 9 * (int64_t)cj;
-#pragma unroll
-    for (int k = 0; k < 9; ++k) xv[k] = xc[k];
-    __builtin_amdgcn_sched_barrier(0);
+    // Loads in a fixed order (the scheduling barriers keep it): the point data
+    // this slot needs only at the end, then the indices of the slot after next
+    // and the coordinates of the next slot.  Every load is issued
+    // unconditionally (indices clamped into range, results of idle lanes
+    // dropped), so the loads in flight are the same on every path and each
+    // wait, by count in issue order, covers only what is needed by then.
     double ci[6];
     const double* Ci = d.Cinv + 6 * (int64_t)cpt_c;
 #pragma unroll
@@ -891,15 +882,31 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     const double nw = d.w_pt[min(s + kWave, last)];
     __builtin_amdgcn_sched_barrier(0);
     CamG c;
-    load_cam_lds(s_cam, cj, c);
+    double xv[9];
+    {
+      const double* r = s_cam + kCamLdsStride * cj;
+      double q[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q[k] = r[k];
+      quat_to_R(q, c.R);
+      c.t[0] = r[4];
+      c.t[1] = r[5];
+      c.t[2] = r[6];
+      c.f = r[7];
+      c.k1 = r[8];
+      c.k2 = r[9];
+#pragma unroll
+      for (int k = 0; k < 9; ++k) xv[k] = r[10 + k];
+    }
     Geo g;
     geo_eval(c, cx0, cx1, cx2, g);
     double u0, u1;
     jc_apply(g, c.f, xv, u0, u1);
+    // idle lanes (past the range, their data clamped to a real observation)
+    // get weight 0 and so add zeros
+    const double wv = valid ? cw : 0.0;
     double v[3];
-    jpt_apply(g, c.R, cw * u0, cw * u1, v[0], v[1], v[2]);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) v[k] = valid ? v[k] : 0.0;
+    jpt_apply(g, c.R, wv * u0, wv * u1, v[0], v[1], v[2]);
     // segmented inclusive scan across the lanes
     const int prev_pt = dpp_mov_int<0x138>(cpt, -1);   // wave_shr:1
     const bool head = (lane == 0) || (cpt != prev_pt);
@@ -1194,7 +1201,11 @@ __global__ void k_retract(Dev d) {
 #pragma unroll
   for (int a = 3; a < 9; ++a) o[a] = c[a] + dx[a];
   CamG t;
-  so3_exp(o[0], o[1], o[2], t.R);
+  double qt[4];
+  quat_from_rotvec(o[0], o[1], o[2], qt);
+  quat_to_R(qt, t.R);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) d.camq_trial[4 * j + k] = qt[k];
   t.t[0] = o[3];
   t.t[1] = o[4];
   t.t[2] = o[5];
@@ -1362,8 +1373,8 @@ void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, uint
 
 }  // namespace
 
-void launch_cam_prep(const double* cams, CamT* tab, int64_t nc, hipStream_t s) {
-  if (nc > 0) launch(k_cam_prep, dim3(blocks_for(nc, 256)), dim3(256), s, 0u, cams, tab, nc);
+void launch_cam_prep(const double* cams, CamT* tab, double* camq, int64_t nc, hipStream_t s) {
+  if (nc > 0) launch(k_cam_prep, dim3(blocks_for(nc, 256)), dim3(256), s, 0u, cams, tab, camq, nc);
 }
 void launch_lin_pt(const Dev& d, hipStream_t s) {
   if (d.n_tiles > 0) launch(k_lin_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d);

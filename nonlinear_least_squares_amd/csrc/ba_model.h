@@ -31,6 +31,17 @@ struct CamG {
 };
 
 // Geometry of one observation at the current parameters.
+// 1/x for x >= 1e-6: the hardware estimate refined by two Newton steps, each
+// r <- r + r (1 - x r), which doubles the correct bits of an estimate good to
+// about 2^-23; the result is within an ulp or so of the rounded quotient.
+__device__ __forceinline__ double recip(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  double e = fma(-x, r, 1.0);
+  r = fma(r, e, r);
+  e = fma(-x, r, 1.0);
+  return fma(r, e, r);
+}
+
 struct Geo {
   double q0, q1, q2;                     // R X
   double p0, p1, n, s;                   // normalised coordinates, |p|^2, radial factor
@@ -44,7 +55,7 @@ __device__ __forceinline__ void geo_eval(const CamG& c, double X0, double X1, do
   g.q2 = c.R[6] * X0 + c.R[7] * X1 + c.R[8] * X2;
   const double P0 = g.q0 + c.t[0], P1 = g.q1 + c.t[1], P2 = g.q2 + c.t[2];
   const bool clamped = P2 < 1e-6;
-  const double iz = 1.0 / (clamped ? 1e-6 : P2);
+  const double iz = recip(clamped ? 1e-6 : P2);
   g.p0 = P0 * iz;
   g.p1 = P1 * iz;
   g.n = g.p0 * g.p0 + g.p1 * g.p1;
@@ -157,31 +168,35 @@ __device__ __forceinline__ void robust(double r0, double r1, int loss, double de
   }
 }
 
-// Rodrigues: R = I + sin(a)/a K + (1 - cos a)/a^2 K^2, K = [w]x, with
-// (1 - cos a)/a^2 written as 2 sin^2(a/2)/a^2 to avoid cancellation; the
-// second-order series below a = 1e-8.
-__device__ __forceinline__ void so3_exp(double w0, double w1, double w2, double* R) {
-  const double th2 = w0 * w0 + w1 * w1 + w2 * w2;
-  const double th = sqrt(th2);
-  double a, b;
-  if (th < 1e-8) {
-    a = 1.0;
-    b = 0.5;
-  } else {
-    a = sin(th) / th;
-    const double h = sin(0.5 * th) / th;
-    b = 2.0 * h * h;
-  }
-  const double d = 1.0 - b * th2;
-  R[0] = d + b * w0 * w0;
-  R[1] = -a * w2 + b * w0 * w1;
-  R[2] = a * w1 + b * w0 * w2;
-  R[3] = a * w2 + b * w1 * w0;
-  R[4] = d + b * w1 * w1;
-  R[5] = -a * w0 + b * w1 * w2;
-  R[6] = -a * w1 + b * w2 * w0;
-  R[7] = a * w0 + b * w2 * w1;
-  R[8] = d + b * w2 * w2;
+// Unit quaternion (w, x, y, z), w >= 0, of the rotation vector (w0, w1, w2):
+// (cos(th/2), sin(th/2) w / th), and (1, w / 2) below th = 1e-8.
+__device__ __forceinline__ void quat_from_rotvec(double w0, double w1, double w2, double* q) {
+  const double th = sqrt(w0 * w0 + w1 * w1 + w2 * w2);
+  const double h = th < 1e-8 ? 0.5 : sin(0.5 * th) / th;
+  q[0] = th < 1e-8 ? 1.0 : cos(0.5 * th);
+  q[1] = h * w0;
+  q[2] = h * w1;
+  q[3] = h * w2;
+}
+
+// Rotation matrix (row-major) of a unit quaternion: I + 2 w [v]x + 2 [v]x^2.
+// Every kernel that needs a camera's R forms it with this function from the
+// same quaternion, so all of them see the same bits.
+__device__ __forceinline__ void quat_to_R(const double* q, double* R) {
+  const double w = q[0], x = q[1], y = q[2], z = q[3];
+  const double x2 = x + x, y2 = y + y, z2 = z + z;
+  const double xx = x * x2, yy = y * y2, zz = z * z2;
+  const double xy = x * y2, xz = x * z2, yz = y * z2;
+  const double wx = w * x2, wy = w * y2, wz = w * z2;
+  R[0] = 1.0 - (yy + zz);
+  R[1] = xy - wz;
+  R[2] = xz + wy;
+  R[3] = xy + wz;
+  R[4] = 1.0 - (xx + zz);
+  R[5] = yz - wx;
+  R[6] = xz - wy;
+  R[7] = yz + wx;
+  R[8] = 1.0 - (xx + yy);
 }
 
 // Packed symmetric storage: upper triangle row by row, index of (i, j), i <= j.
