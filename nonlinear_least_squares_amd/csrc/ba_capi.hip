@@ -282,7 +282,7 @@ int stage_schur(ba_problem* h) {
 
 // PCG iterations are queued in batches.  The first batch is as long as the
 // previous solve took (the iteration count changes slowly across LM steps),
-// later ones two iterations long, always one batch ahead of the batch whose
+// later ones one iteration long, always one batch ahead of the batch whose
 // completion the host waits for; the kernels raise a host-mapped flag when
 // the solve stops and every launch after that exits at once.
 int stage_pcg(ba_problem* h) {
@@ -307,7 +307,7 @@ int stage_pcg(ba_problem* h) {
     HIPC(hipEventRecord(h->batch_ev[0], h->stream));
     int cur = 0;
     while (launched < maxit) {
-      const int n = std::min(2, maxit - launched);
+      const int n = std::min(1, maxit - launched);
       CHECK_RC(enqueue(n));
       launched += n;
       HIPC(hipEventRecord(h->batch_ev[1 - cur], h->stream));

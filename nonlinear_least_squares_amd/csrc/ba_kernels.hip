@@ -444,47 +444,47 @@ __global__ void k_lin_final(Dev d) {
 // Ebar^T, and the preconditioner block M_j^-1 = S_jj^-1 formed once from the
 // Cholesky factor, column by column, so that a PCG iteration applies it as a
 // plain 9 x 9 product.
-__global__ void k_precond(Dev d) {
-  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (j >= d.nc) return;
+__global__ __launch_bounds__(64) void k_precond(Dev d) {
+  // nine threads per camera: each forms the damped block, S_jj and its factor
+  // (the same bits in all nine), writes a ninth of B~ and S_jj, one rhs entry,
+  // and column `col` of S_jj^-1
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= 9 * d.nc) return;
+  const int64_t j = t / 9;
+  const int col = (int)(t - 9 * j);
   const int c0 = d.cam_chunk_ptr[j], c1 = d.cam_chunk_ptr[j + 1];
-  double B[45], g[9];
+  double B[45];
 #pragma unroll
   for (int k = 0; k < 45; ++k) B[k] = d.B[45 * j + k];
-#pragma unroll
-  for (int k = 0; k < 9; ++k) g[k] = d.gc[9 * j + k];
+  const double g = d.gc[9 * j + col];
 #pragma unroll
   for (int a = 0; a < 9; ++a) {
     const int ii = sym_idx(9, a, a);
     B[ii] += d.lambda * fmax(B[ii], d.diag_floor);
   }
 #pragma unroll
-  for (int k = 0; k < 45; ++k) d.Bd[45 * j + k] = B[k];
-  double ev[9];
-#pragma unroll
-  for (int k = 0; k < 9; ++k) ev[k] = 0.0;
+  for (int k = 0; k < 45; ++k)
+    if (k % 9 == col) d.Bd[45 * j + k] = B[k];
+  double ev = 0.0;
   for (int ch = c0; ch < c1; ++ch) {
     const double* pp = d.schur_part + (int64_t)ch * kSchurVals;
-#pragma unroll
-    for (int k = 0; k < 9; ++k) ev[k] += pp[k];
+    ev += pp[col];
 #pragma unroll
     for (int k = 0; k < 45; ++k) B[k] -= pp[9 + k];
   }
+  d.rhs[9 * j + col] = -g + ev;
 #pragma unroll
-  for (int k = 0; k < 9; ++k) d.rhs[9 * j + k] = -g[k] + ev[k];
-#pragma unroll
-  for (int k = 0; k < 45; ++k) d.Mfull[45 * j + k] = B[k];
+  for (int k = 0; k < 45; ++k)
+    if (k % 9 == col) d.Mfull[45 * j + k] = B[k];
   if (!chol_packed<9>(B)) d.flags[1] = 1;
+  double e[9], x[9];
+#pragma unroll
+  for (int a = 0; a < 9; ++a) e[a] = a == col ? 1.0 : 0.0;
+  chol_solve_packed<9>(B, e, x);
   double* Mi = d.Minv + 45 * j;
-  for (int b = 0; b < 9; ++b) {
-    double e[9], x[9];
 #pragma unroll
-    for (int a = 0; a < 9; ++a) e[a] = a == b ? 1.0 : 0.0;
-    chol_solve_packed<9>(B, e, x);
-#pragma unroll
-    for (int a = 0; a < 9; ++a)
-      if (a <= b) Mi[sym_idx(9, a, b)] = x[a];
-  }
+  for (int a = 0; a < 9; ++a)
+    if (a <= col) Mi[sym_idx(9, a, col)] = x[a];
 }
 
 // ---------------------------------------------------------------------- PCG
@@ -1392,7 +1392,7 @@ void launch_lin_final(const Dev& d, hipStream_t s) {
   if (d.nc > 0) launch(k_lin_final, dim3(blocks_for(d.nc, 64)), dim3(64), s, 0u, d);
 }
 void launch_precond(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) launch(k_precond, dim3(blocks_for(d.nc, 64)), dim3(64), s, 0u, d);
+  if (d.nc > 0) launch(k_precond, dim3(blocks_for(9 * d.nc, 64)), dim3(64), s, 0u, d);
 }
 void launch_pcg_init(const Dev& d, hipStream_t s) {
   launch(k_pcg_init, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d);
