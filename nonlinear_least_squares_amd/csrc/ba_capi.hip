@@ -325,7 +325,7 @@ int stage_update(ba_problem* h) {
   Dev d = make_dev(h);
   TIMED(BA_K_BACKSUB, -1, launch_backsub(d, h->stream));
   TIMED(BA_K_RETRACT, -1, launch_retract(d, h->stream));
-  TIMED(BA_K_COST, -1, launch_cost(d, d.cams_trial, d.pts_trial, d.tab_trial, h->stream));
+  TIMED(BA_K_COST, -1, launch_cost(d, d.pts_trial, d.tab_trial, d.camq_trial, h->stream));
   HIPC(hipGetLastError());
   return BA_OK;
 }
@@ -338,7 +338,7 @@ int read_out(ba_problem* h) {
 
 int current_cost(ba_problem* h, double* c) {
   Dev d = make_dev(h);
-  launch_cost(d, d.cams, d.pts, d.tab, h->stream);
+  launch_cost(d, d.pts, d.tab, d.camq, h->stream);
   HIPC(hipGetLastError());
   CHECK_RC(read_out(h));
   *c = h->h_out->trial_cost;

@@ -28,7 +28,9 @@ constexpr int kTile = 256;        // observations per point-order sub-tile (= bl
 constexpr int kLdsBlock = 1024;   // threads of the persistent LDS-camera-table kernels
 constexpr int kCamLdsStride = 19; // doubles per camera in the LDS table: q (4), t, f, k1, k2, vector (9)
 constexpr int kCamLdsFill = 20;   // table elements per thread in the copy (>= 19 * max cameras / kLdsBlock)
-constexpr int kCamLdsMaxBytes = kCamLdsStride * 8 * (kCamLdsFill * 1024 / kCamLdsStride);  // 1,077 cameras
+constexpr int kCamLdsMaxCams = kCamLdsFill * 1024 / kCamLdsStride;   // 1,077
+constexpr int kCamLdsMaxBytes = kCamLdsStride * 8 * kCamLdsMaxCams;
+constexpr int kCostLdsFill = (10 * kCamLdsMaxCams + 1023) / 1024;   // geometry elements per thread
 constexpr int kChunk = 1024;      // observations per camera chunk (one wavefront)
 constexpr int kPointBands = 4;    // point-index bands of the camera chunks (block b: band b % 4,
                                   // on dies b % 8: two dies' L2 per band)
@@ -149,7 +151,7 @@ void launch_pcg_final(const Dev& d, int iters, hipStream_t s);
 int pcg_red_blocks(int64_t nc);   // blocks of the camera-vector kernels
 void launch_backsub(const Dev& d, hipStream_t s);
 void launch_retract(const Dev& d, hipStream_t s);
-void launch_cost(const Dev& d, const double* cams, const double* pts, const CamT* tab,
+void launch_cost(const Dev& d, const double* pts, const CamT* tab, const double* camq,
                  hipStream_t s);
 void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* Jc, double* Jp,
                       double* w, hipStream_t s);

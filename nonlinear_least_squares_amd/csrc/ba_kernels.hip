@@ -1235,10 +1235,87 @@ __global__ __launch_bounds__(256) void k_cost(Dev d, const double* __restrict__ 
   if (threadIdx.x == 0) d.cost_part[blockIdx.x] = acc;
 }
 
-__global__ __launch_bounds__(kUpdBlock) void k_cost_final(Dev d) {
+// The same cost with the camera geometry resident in LDS (rows of q, t, f,
+// k1, k2; R formed from q as everywhere else): one persistent block per compute
+// unit, each wavefront summing its point-aligned observation range 64 at a
+// time with the next slot's loads in flight, then a DPP scan across the lanes
+// and the block's wavefronts in order.  One partial per block.
+constexpr int kCostLdsStride = 11;
+
+__global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __restrict__ pts,
+                                                        const CamT* __restrict__ tab,
+                                                        const double* __restrict__ camq) {
+  extern __shared__ double s_cam[];
+  __shared__ double s_wsum[kLdsBlock / kWave];
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int wave = blockIdx.x * (kLdsBlock / kWave) + wv;
+  const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
+  const int nlast = (int)d.nobs - 1;
+  {
+    const int na = 10 * (int)d.nc;
+    const double* tabd = reinterpret_cast<const double*>(tab);
+    double ta[kCostLdsFill];
+#pragma unroll
+    for (int u = 0; u < kCostLdsFill; ++u) {
+      const int e = min((int)threadIdx.x + u * kLdsBlock, na - 1);
+      const int j = e / 10, k = e - 10 * j;
+      ta[u] = k < 4 ? camq[4 * j + k] : tabd[16 * j + 5 + k];
+    }
+#pragma unroll
+    for (int u = 0; u < kCostLdsFill; ++u) {
+      const int e = (int)threadIdx.x + u * kLdsBlock;
+      const int j = e / 10, k = e - 10 * j;
+      if (e < na) s_cam[kCostLdsStride * j + k] = ta[u];
+    }
+  }
+  // first slot's observation data, in flight across the barrier
+  int s0 = min(sb + lane, nlast);
+  int pt = d.o_pt[s0], cj = d.o_cam[s0];
+  double2 uv = reinterpret_cast<const double2*>(d.o_uv)[s0];
+  __syncthreads();
+  double acc = 0.0;
+  for (int base = sb; base < se; base += kWave) {
+    const bool valid = base + lane < se;
+    const double X0 = pts[3 * pt], X1 = pts[3 * pt + 1], X2 = pts[3 * pt + 2];
+    const int s1 = min(base + kWave + lane, nlast);
+    const int npt = d.o_pt[s1], ncj = d.o_cam[s1];
+    const double2 nuv = reinterpret_cast<const double2*>(d.o_uv)[s1];
+    CamG c;
+    {
+      const double* r = s_cam + kCostLdsStride * cj;
+      double q[4] = {r[0], r[1], r[2], r[3]};
+      quat_to_R(q, c.R);
+      c.t[0] = r[4];
+      c.t[1] = r[5];
+      c.t[2] = r[6];
+      c.f = r[7];
+      c.k1 = r[8];
+      c.k2 = r[9];
+    }
+    Geo g;
+    geo_eval(c, X0, X1, X2, g);
+    double w, rho;
+    robust(g.u0 - uv.x, g.u1 - uv.y, d.loss, d.delta, w, rho);
+    acc += valid ? rho : 0.0;
+    pt = npt;
+    cj = ncj;
+    uv = nuv;
+  }
+  double v[1] = {acc};
+  seg_scan_dpp<1>(v, lane, 0);
+  if (lane == kWave - 1) s_wsum[wv] = v[0];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double b = 0.0;
+    for (int k = 0; k < kLdsBlock / kWave; ++k) b += s_wsum[k];
+    d.cost_part[blockIdx.x] = b;
+  }
+}
+
+__global__ __launch_bounds__(kUpdBlock) void k_cost_final(Dev d, int n_parts) {
   __shared__ double s_buf[kUpdBlock / kWave];
   double acc = 0.0;
-  for (int b = threadIdx.x; b < d.n_cost_blocks; b += kUpdBlock) acc += d.cost_part[b];
+  for (int b = threadIdx.x; b < n_parts; b += kUpdBlock) acc += d.cost_part[b];
   acc = block_sum<kUpdBlock>(acc, s_buf);
   if (threadIdx.x == 0) {
     d.out->trial_cost = acc;
@@ -1351,6 +1428,9 @@ hipError_t set_lds_camera_limit(int bytes) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pcg_pt_lds),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cost_lds),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_backsub_lds),
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
@@ -1432,11 +1512,16 @@ void launch_backsub(const Dev& d, hipStream_t s) {
 void launch_retract(const Dev& d, hipStream_t s) {
   if (d.nc > 0) launch(k_retract, dim3(blocks_for(d.nc, 128)), dim3(128), s, 0u, d);
 }
-void launch_cost(const Dev& d, const double* cams, const double* pts, const CamT* tab,
+void launch_cost(const Dev& d, const double* pts, const CamT* tab, const double* camq,
                  hipStream_t s) {
-  (void)cams;
-  if (d.n_cost_blocks > 0) launch(k_cost, dim3(d.n_cost_blocks), dim3(256), s, 0u, d, pts, tab);
-  launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d);
+  if (d.cam_lds_bytes > 0 && d.lds_blocks > 0) {
+    launch(k_cost_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
+           (uint32_t)(kCostLdsStride * 8 * d.nc), d, pts, tab, camq);
+    launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.lds_blocks);
+  } else {
+    if (d.n_cost_blocks > 0) launch(k_cost, dim3(d.n_cost_blocks), dim3(256), s, 0u, d, pts, tab);
+    launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.n_cost_blocks);
+  }
 }
 void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* Jc, double* Jp,
                       double* w, hipStream_t s) {
