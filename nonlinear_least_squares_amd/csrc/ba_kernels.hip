@@ -1235,13 +1235,46 @@ __global__ __launch_bounds__(256) void k_cost(Dev d, const double* __restrict__ 
   if (threadIdx.x == 0) d.cost_part[blockIdx.x] = acc;
 }
 
-// The same cost with the camera geometry resident in LDS (rows of q, t, f,
-// k1, k2; R formed from q as everywhere else): one persistent block per compute
+// Camera geometry rows in LDS for the point-order kernels that need no camera
+// vector (linearisation, cost): q, t, f, k1, k2 at an odd stride; R is formed
+// from q as everywhere else.  Every thread issues its loads before its stores.
+constexpr int kGeoLdsStride = 11;
+
+__device__ __forceinline__ void fill_geometry_lds(double* s_geo, const CamT* __restrict__ tab,
+                                                  const double* __restrict__ camq, int nc) {
+  const int na = 10 * nc;
+  const double* tabd = reinterpret_cast<const double*>(tab);
+  double ta[kCostLdsFill];
+#pragma unroll
+  for (int u = 0; u < kCostLdsFill; ++u) {
+    const int e = min((int)threadIdx.x + u * kLdsBlock, na - 1);
+    const int j = e / 10, k = e - 10 * j;
+    ta[u] = k < 4 ? camq[4 * j + k] : tabd[16 * j + 5 + k];
+  }
+#pragma unroll
+  for (int u = 0; u < kCostLdsFill; ++u) {
+    const int e = (int)threadIdx.x + u * kLdsBlock;
+    const int j = e / 10, k = e - 10 * j;
+    if (e < na) s_geo[kGeoLdsStride * j + k] = ta[u];
+  }
+}
+
+__device__ __forceinline__ void geometry_from_lds(const double* s_geo, int j, CamG& c) {
+  const double* r = s_geo + kGeoLdsStride * j;
+  const double q[4] = {r[0], r[1], r[2], r[3]};
+  quat_to_R(q, c.R);
+  c.t[0] = r[4];
+  c.t[1] = r[5];
+  c.t[2] = r[6];
+  c.f = r[7];
+  c.k1 = r[8];
+  c.k2 = r[9];
+}
+
+// The cost with the camera geometry in LDS: one persistent block per compute
 // unit, each wavefront summing its point-aligned observation range 64 at a
 // time with the next slot's loads in flight, then a DPP scan across the lanes
 // and the block's wavefronts in order.  One partial per block.
-constexpr int kCostLdsStride = 11;
-
 __global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __restrict__ pts,
                                                         const CamT* __restrict__ tab,
                                                         const double* __restrict__ camq) {
@@ -1251,23 +1284,7 @@ __global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __r
   const int wave = blockIdx.x * (kLdsBlock / kWave) + wv;
   const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
   const int nlast = (int)d.nobs - 1;
-  {
-    const int na = 10 * (int)d.nc;
-    const double* tabd = reinterpret_cast<const double*>(tab);
-    double ta[kCostLdsFill];
-#pragma unroll
-    for (int u = 0; u < kCostLdsFill; ++u) {
-      const int e = min((int)threadIdx.x + u * kLdsBlock, na - 1);
-      const int j = e / 10, k = e - 10 * j;
-      ta[u] = k < 4 ? camq[4 * j + k] : tabd[16 * j + 5 + k];
-    }
-#pragma unroll
-    for (int u = 0; u < kCostLdsFill; ++u) {
-      const int e = (int)threadIdx.x + u * kLdsBlock;
-      const int j = e / 10, k = e - 10 * j;
-      if (e < na) s_cam[kCostLdsStride * j + k] = ta[u];
-    }
-  }
+  fill_geometry_lds(s_cam, tab, camq, (int)d.nc);
   // first slot's observation data, in flight across the barrier
   int s0 = min(sb + lane, nlast);
   int pt = d.o_pt[s0], cj = d.o_cam[s0];
@@ -1281,17 +1298,7 @@ __global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __r
     const int npt = d.o_pt[s1], ncj = d.o_cam[s1];
     const double2 nuv = reinterpret_cast<const double2*>(d.o_uv)[s1];
     CamG c;
-    {
-      const double* r = s_cam + kCostLdsStride * cj;
-      double q[4] = {r[0], r[1], r[2], r[3]};
-      quat_to_R(q, c.R);
-      c.t[0] = r[4];
-      c.t[1] = r[5];
-      c.t[2] = r[6];
-      c.f = r[7];
-      c.k1 = r[8];
-      c.k2 = r[9];
-    }
+    geometry_from_lds(s_cam, cj, c);
     Geo g;
     geo_eval(c, X0, X1, X2, g);
     double w, rho;
@@ -1309,6 +1316,92 @@ __global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __r
     double b = 0.0;
     for (int k = 0; k < kLdsBlock / kWave; ++k) b += s_wsum[k];
     d.cost_part[blockIdx.x] = b;
+  }
+}
+
+// Point-side linearisation with the camera geometry in LDS, structured as the
+// PCG point pass: one point-aligned observation range per wavefront, 64 slots
+// at a time, a DPP segmented scan of the 9 values per observation (w Jp^T Jp,
+// w Jp^T r) with register carries across slots, C and g_p written at each
+// point's last observation, the robust weight at every observation.
+__global__ __launch_bounds__(kLdsBlock) void k_lin_pt_lds(Dev d) {
+  extern __shared__ double s_cam[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = blockIdx.x * (kLdsBlock / kWave) + threadIdx.x / kWave;
+  const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
+  const int nlast = (int)d.nobs - 1;
+  fill_geometry_lds(s_cam, d.tab, d.camq, (int)d.nc);
+  const double2* ouv = reinterpret_cast<const double2*>(d.o_uv);
+  int cpt, cj;
+  double2 uv;
+  {
+    const int s0 = min(sb + lane, nlast);
+    const int p0 = d.o_pt[s0];
+    cpt = sb + lane < se ? p0 : -1;
+    cj = d.o_cam[s0];
+    uv = ouv[s0];
+  }
+  __syncthreads();
+  double carry[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) carry[k] = 0.0;
+  int carry_pt = -1;
+  for (int base = sb; base < se; base += kWave) {
+    const int s = base + lane;
+    const bool valid = cpt >= 0;
+    const int cpt_c = max(cpt, 0);
+    const double X0 = d.pts[3 * cpt_c], X1 = d.pts[3 * cpt_c + 1], X2 = d.pts[3 * cpt_c + 2];
+    const int s1 = min(s + kWave, nlast);
+    const int p1 = d.o_pt[s1], ncj = d.o_cam[s1];
+    const int npt = s + kWave < se ? p1 : -1;
+    const double2 nuv = ouv[s1];
+    CamG c;
+    geometry_from_lds(s_cam, cj, c);
+    Geo g;
+    geo_eval(c, X0, X1, X2, g);
+    const double r0 = g.u0 - uv.x, r1 = g.u1 - uv.y;
+    double w, rho;
+    robust(r0, r1, d.loss, d.delta, w, rho);
+    if (valid) d.w_pt[s] = w;
+    const double wv = valid ? w : 0.0;
+    double J[6];
+    jp_rows(g, c.R, J);
+    double v[9];
+    v[0] = wv * (J[0] * J[0] + J[3] * J[3]);
+    v[1] = wv * (J[0] * J[1] + J[3] * J[4]);
+    v[2] = wv * (J[0] * J[2] + J[3] * J[5]);
+    v[3] = wv * (J[1] * J[1] + J[4] * J[4]);
+    v[4] = wv * (J[1] * J[2] + J[4] * J[5]);
+    v[5] = wv * (J[2] * J[2] + J[5] * J[5]);
+    v[6] = wv * (J[0] * r0 + J[3] * r1);
+    v[7] = wv * (J[1] * r0 + J[4] * r1);
+    v[8] = wv * (J[2] * r0 + J[5] * r1);
+    const int prev_pt = dpp_mov_int<0x138>(cpt, -1);   // wave_shr:1
+    const bool head = (lane == 0) || (cpt != prev_pt);
+    const unsigned long long heads = __ballot(head);
+    const unsigned long long upto = (lane == kWave - 1) ? ~0ull : ((2ull << lane) - 1ull);
+    const int seg0 = 63 - __clzll(heads & upto);
+    seg_scan_dpp<9>(v, lane, seg0);
+    if (valid && seg0 == 0 && cpt == carry_pt) {
+#pragma unroll
+      for (int k = 0; k < 9; ++k) v[k] += carry[k];
+    }
+    const int down_pt = dpp_mov_int<0x130>(cpt, -1);   // wave_shl:1
+    const int first_next = __builtin_amdgcn_readlane(npt, 0);
+    const int next_pt = lane == kWave - 1 ? first_next : down_pt;
+    if (valid && next_pt != cpt) {
+#pragma unroll
+      for (int k = 0; k < 6; ++k) d.C[6 * cpt + k] = v[k];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) d.gp[3 * cpt + k] = v[6 + k];
+    }
+    const bool cont = valid && next_pt == cpt;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) carry[k] = read_lane(v[k], kWave - 1);
+    carry_pt = __builtin_amdgcn_readlane(cont ? cpt : -1, kWave - 1);
+    cpt = npt;
+    cj = ncj;
+    uv = nuv;
   }
 }
 
@@ -1425,6 +1518,9 @@ DispatchEvents& dispatch_events() {
 }
 
 hipError_t set_lds_camera_limit(int bytes) {
+  hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin_pt_lds),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e0 != hipSuccess) return e0;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pcg_pt_lds),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
@@ -1457,7 +1553,13 @@ void launch_cam_prep(const double* cams, CamT* tab, double* camq, int64_t nc, hi
   if (nc > 0) launch(k_cam_prep, dim3(blocks_for(nc, 256)), dim3(256), s, 0u, cams, tab, camq, nc);
 }
 void launch_lin_pt(const Dev& d, hipStream_t s) {
-  if (d.n_tiles > 0) launch(k_lin_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
+  if (d.cam_lds_bytes > 0) {
+    if (d.lds_blocks > 0)
+      launch(k_lin_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
+             (uint32_t)(kGeoLdsStride * 8 * d.nc), d);
+  } else if (d.n_tiles > 0) {
+    launch(k_lin_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
+  }
 }
 void launch_lin_cam(const Dev& d, hipStream_t s) {
   if (d.n_chunk_blocks > 0) launch(k_lin_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
@@ -1516,7 +1618,7 @@ void launch_cost(const Dev& d, const double* pts, const CamT* tab, const double*
                  hipStream_t s) {
   if (d.cam_lds_bytes > 0 && d.lds_blocks > 0) {
     launch(k_cost_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
-           (uint32_t)(kCostLdsStride * 8 * d.nc), d, pts, tab, camq);
+           (uint32_t)(kGeoLdsStride * 8 * d.nc), d, pts, tab, camq);
     launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.lds_blocks);
   } else {
     if (d.n_cost_blocks > 0) launch(k_cost, dim3(d.n_cost_blocks), dim3(256), s, 0u, d, pts, tab);
