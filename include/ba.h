@@ -176,7 +176,7 @@ enum {
   BA_DBG_GP,            /* double n_pts x 3                                                        */
   BA_DBG_BD,            /* double n_cams x 81 damped B                                             */
   BA_DBG_CINV,          /* double n_pts x 9   inverse of the damped point block                    */
-  BA_DBG_V,             /* double n_pts x 3                                                        */
+  BA_DBG_V,             /* double n_pts x 3; valid after BA_STAGE_SCHUR, until a PCG stage runs    */
   BA_DBG_RHS,           /* double n_cams x 9                                                       */
   BA_DBG_M,             /* double n_cams x 81 exact diagonal blocks S_jj                           */
   BA_DBG_DC,            /* double n_cams x 9                                                       */

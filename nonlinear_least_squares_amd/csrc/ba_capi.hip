@@ -100,7 +100,7 @@ struct ba_problem {
   // work arrays
   double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
          *gc = nullptr, *lin_part = nullptr;
-  double *Cinv = nullptr, *v = nullptr, *Bd = nullptr, *rhs = nullptr, *Minv = nullptr,
+  double *Cinv = nullptr, *Bd = nullptr, *rhs = nullptr, *Minv = nullptr,
          *Mfull = nullptr, *schur_part = nullptr;
   double *x = nullptr, *r = nullptr, *zc = nullptr, *pbuf = nullptr, *q = nullptr, *prec = nullptr,
          *pcg_part = nullptr, *pq_cam = nullptr, *red_part = nullptr;
@@ -174,7 +174,6 @@ Dev make_dev(const ba_problem* h) {
   d.gc = h->gc;
   d.lin_part = h->lin_part;
   d.Cinv = h->Cinv;
-  d.v = h->v;
   d.Bd = h->Bd;
   d.rhs = h->rhs;
   d.Minv = h->Minv;
@@ -464,7 +463,6 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   A.add(h->C, 6 * np);
   A.add(h->gp, 3 * np);
   A.add(h->Cinv, 6 * np);
-  A.add(h->v, 3 * np);
   A.add(h->prec, 8 * np);
   A.add(h->dp, 3 * np);
   A.add(h->B, 45 * nc);
@@ -933,7 +931,12 @@ int ba_debug_get(ba_problem* h, int which, void* host_out, int64_t bytes) {
     }
     case BA_DBG_GC: return d2h(h, host_out, h->gc, bytes);
     case BA_DBG_GP: return d2h(h, host_out, h->gp, bytes);
-    case BA_DBG_V: return d2h(h, host_out, h->v, bytes);
+    case BA_DBG_V:   // v = C~^-1 g_p sits in elements 3..5 of each point record until the PCG
+      if (bytes) HIPC(hipMemcpy2DAsync(host_out, 3 * sizeof(double), h->prec + 3, 8 * sizeof(double),
+                                       3 * sizeof(double), (size_t)h->np, hipMemcpyDeviceToHost,
+                                       h->stream));
+      HIPC(hipStreamSynchronize(h->stream));
+      return BA_OK;
     case BA_DBG_RHS: return d2h(h, host_out, h->rhs, bytes);
     case BA_DBG_DC: return d2h(h, host_out, h->x, bytes);
     case BA_DBG_DP: return d2h(h, host_out, h->dp, bytes);

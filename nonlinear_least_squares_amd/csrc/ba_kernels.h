@@ -96,7 +96,6 @@ struct Dev {
   double* lin_part;
   // elimination
   double* Cinv;
-  double* v;
   double* Bd;
   double* rhs;
   double* Minv;

@@ -332,10 +332,7 @@ __global__ void k_damp_pt(Dev d) {
     for (int k = 0; k < 3; ++k) g[k] = d.gp[3 * i + k];
   }
   const int diag[3] = {0, 3, 5};
-  // the camera-side PCG pass reads X and z of a point from one 64-byte record
-  d.prec[8 * i] = d.pts[3 * i];
-  d.prec[8 * i + 1] = d.pts[3 * i + 1];
-  d.prec[8 * i + 2] = d.pts[3 * i + 2];
+  const double X0 = d.pts[3 * i], X1 = d.pts[3 * i + 1], X2 = d.pts[3 * i + 2];
 #pragma unroll
   for (int a = 0; a < 3; ++a) C[diag[a]] += d.lambda * fmax(C[diag[a]], d.diag_floor);
   if (!chol_packed<3>(C)) {
@@ -357,9 +354,13 @@ __global__ void k_damp_pt(Dev d) {
   Ci[5] = i22 * i22;
 #pragma unroll
   for (int k = 0; k < 6; ++k) d.Cinv[6 * i + k] = Ci[k];
-  d.v[3 * i] = Ci[0] * g[0] + Ci[1] * g[1] + Ci[2] * g[2];
-  d.v[3 * i + 1] = Ci[1] * g[0] + Ci[3] * g[1] + Ci[4] * g[2];
-  d.v[3 * i + 2] = Ci[2] * g[0] + Ci[4] * g[1] + Ci[5] * g[2];
+  // The point record (64 B): X, and in the slot the PCG later fills with z,
+  // v = C~^-1 g_p, so that the Schur camera pass reads both from one place.
+  double2* rec = reinterpret_cast<double2*>(d.prec + 8 * i);
+  rec[0] = make_double2(X0, X1);
+  rec[1] = make_double2(X2, Ci[0] * g[0] + Ci[1] * g[1] + Ci[2] * g[2]);
+  rec[2] = make_double2(Ci[1] * g[0] + Ci[3] * g[1] + Ci[4] * g[2],
+                        Ci[2] * g[0] + Ci[4] * g[1] + Ci[5] * g[2]);
 }
 
 // Camera-order pass: E v (right-hand side) and Ebar C~^-1 Ebar^T (diagonal
@@ -377,11 +378,13 @@ __global__ __launch_bounds__(kWave) void k_schur_cam(Dev d) {
   for (int k = 0; k < kSchurVals; ++k) acc[k] = 0.0;
   for (int s = cb + threadIdx.x; s < ce; s += kWave) {
     const int i = d.c_pt[s];
+    const double4 ra = *reinterpret_cast<const double4*>(d.prec + 8 * (int64_t)i);      // X, v0
+    const double2 rb = *reinterpret_cast<const double2*>(d.prec + 8 * (int64_t)i + 4);  // v1, v2
     Geo g;
-    geo_eval(c, d.pts[3 * i], d.pts[3 * i + 1], d.pts[3 * i + 2], g);
+    geo_eval(c, ra.x, ra.y, ra.z, g);
     const double w = d.w_cam[s];
     double t0, t1;
-    jp_apply(g, c.R, d.v[3 * i], d.v[3 * i + 1], d.v[3 * i + 2], t0, t1);
+    jp_apply(g, c.R, ra.w, rb.x, rb.y, t0, t1);
     jct_acc(g, c.f, w * t0, w * t1, acc);
     const int rl = d.run_len[s];
     if (rl > 0) {
