@@ -10,7 +10,7 @@ relative residual.  Inputs are resident in HBM before the timed region.
 Prints one JSON line.  The roofline object refers to the kernel with the
 largest total time in a profiled warm-up run; its average launch time is
 taken with HIP events on the library's stream during the timed region, on
-every eighth launch.
+every sixteenth launch.
 
 ``--workload dense`` measures the fp32 dense frame-graph variant instead
 (libdba): a step is one Gauss-Newton iteration (linearise, assemble with the
@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # The dominant kernel is timed inside the timed region by HIP events that its
 # own dispatch records; a timed dispatch cannot overlap its neighbours, so only
 # every PROFILE_EVERY-th launch is timed, which keeps that cost out of `value`.
-PROFILE_EVERY = 8
+PROFILE_EVERY = 16
 KERNEL_SRC = os.path.join(ROOT, "nonlinear_least_squares_amd", "csrc", "ba_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_large.json")
 

@@ -40,6 +40,9 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
+// PCG batches in flight: the host waits for a batch when this many are queued.
+constexpr int kBatchEvents = 2;
+
 struct Arena {
   char* base = nullptr;
   size_t size = 0, used = 0;
@@ -112,7 +115,7 @@ struct ba_problem {
   int* h_done = nullptr;     // pinned, device-mapped: PCG stop flag
   int* h_done_dev = nullptr;
   int last_pcg_iters = 0;
-  hipEvent_t batch_ev[2] = {nullptr, nullptr};
+  hipEvent_t batch_ev[kBatchEvents] = {};
   // LM state
   double lambda = 0.0, cost = 0.0;
   int linearized = 0;
@@ -302,17 +305,20 @@ int stage_pcg(ba_problem* h) {
   };
   int launched = std::min(maxit, std::max(1, h->last_pcg_iters - 1));
   if (maxit > 0) {
+    // batch b ends with event b % kBatchEvents; the host waits for batch b
+    // only once batches b + 1 .. b + kBatchEvents - 1 are queued behind it
     CHECK_RC(enqueue(launched));
     HIPC(hipEventRecord(h->batch_ev[0], h->stream));
-    int cur = 0;
+    int queued = 1, waited = 0;
     while (launched < maxit) {
-      const int n = std::min(1, maxit - launched);
-      CHECK_RC(enqueue(n));
-      launched += n;
-      HIPC(hipEventRecord(h->batch_ev[1 - cur], h->stream));
-      HIPC(hipEventSynchronize(h->batch_ev[cur]));
+      CHECK_RC(enqueue(1));
+      launched += 1;
+      HIPC(hipEventRecord(h->batch_ev[queued % kBatchEvents], h->stream));
+      ++queued;
+      if (queued - waited < kBatchEvents) continue;
+      HIPC(hipEventSynchronize(h->batch_ev[waited % kBatchEvents]));
+      ++waited;
       if (__atomic_load_n(h->h_done, __ATOMIC_ACQUIRE)) break;
-      cur = 1 - cur;
     }
   }
   launch_pcg_final(d, next_it, h->stream);
@@ -757,12 +763,13 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
     ba_destroy(h);
     return fail(BA_ERR_ALLOC, "hipHostMalloc");
   }
-  if (hipHostMalloc(reinterpret_cast<void**>(&h->h_done), sizeof(int), hipHostMallocMapped) !=
-          hipSuccess ||
-      hipHostGetDevicePointer(reinterpret_cast<void**>(&h->h_done_dev), h->h_done, 0) !=
-          hipSuccess ||
-      hipEventCreateWithFlags(&h->batch_ev[0], hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->batch_ev[1], hipEventDisableTiming) != hipSuccess) {
+  bool ok = hipHostMalloc(reinterpret_cast<void**>(&h->h_done), sizeof(int), hipHostMallocMapped) ==
+                hipSuccess &&
+            hipHostGetDevicePointer(reinterpret_cast<void**>(&h->h_done_dev), h->h_done, 0) ==
+                hipSuccess;
+  for (int k = 0; ok && k < kBatchEvents; ++k)
+    ok = hipEventCreateWithFlags(&h->batch_ev[k], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
     ba_destroy(h);
     return fail(BA_ERR_ALLOC, "pinned flag or events");
   }
