@@ -295,7 +295,6 @@ int stage_pcg(ba_problem* h) {
   int next_it = 0;
   auto enqueue = [&](int n) -> int {
     for (int k = 0; k < n; ++k, ++next_it) {
-      launch_pcg_pnext(d, next_it, h->stream);
       TIMED(BA_K_PCG_PT, next_it, launch_pcg_pt(d, next_it, h->stream));
       TIMED(BA_K_PCG_CAM, next_it, launch_pcg_cam(d, h->stream));
       TIMED(BA_K_PCG_Q, next_it, launch_pcg_q(d, next_it, h->stream));
@@ -480,7 +479,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   A.add(h->x, 9 * nc);
   A.add(h->r, 9 * nc);
   A.add(h->zc, 9 * nc);
-  A.add(h->pbuf, 18 * nc);
+  A.add(h->pbuf, 9 * nc);
   A.add(h->q, 9 * nc);
   A.add(h->pcg, 1);
   A.add(h->pq_cam, nc);

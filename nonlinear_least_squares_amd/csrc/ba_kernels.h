@@ -105,7 +105,7 @@ struct Dev {
   double* x;
   double* r;
   double* zc;
-  double* pbuf;      // two search directions (iterations of either parity), 9 nc each
+  double* pbuf;      // search direction p, 9 nc
   double* q;
   double* prec;      // per-point 64-byte record: X (3), z = C~^-1 E^T p (3), pad (2)
   double* pcg_part;
@@ -141,7 +141,6 @@ void launch_schur_cam(const Dev& d, hipStream_t s);
 void launch_lin_final(const Dev& d, hipStream_t s);
 void launch_precond(const Dev& d, hipStream_t s);
 void launch_pcg_init(const Dev& d, hipStream_t s);
-void launch_pcg_pnext(const Dev& d, int it, hipStream_t s);
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s);
 void launch_pcg_cam(const Dev& d, hipStream_t s);
 void launch_pcg_q(const Dev& d, int it, hipStream_t s);

@@ -507,7 +507,6 @@ __device__ __forceinline__ double block_sum(double v, double* s_buf) {
 template <int MODE>
 struct PcgPtOp {
   const Dev& d;
-  int it;
   double ci[6];          // C~^-1 of this thread's point, loaded with the point
   double gq[3];          // g_p of this thread's point (back-substitution)
   __device__ void compute(int s, int pt, double* v) {
@@ -524,8 +523,7 @@ struct PcgPtOp {
     }
     CamG c;
     load_cam(d.tab, j, c);
-    const double* xc = MODE == 0 ? d.pbuf + (int64_t)(it & 1) * 9 * d.nc + 9 * (int64_t)j
-                                 : d.x + 9 * (int64_t)j;
+    const double* xc = (MODE == 0 ? d.zc : d.x) + 9 * (int64_t)j;
     Geo g;
     geo_eval(c, d.pts[3 * pt], d.pts[3 * pt + 1], d.pts[3 * pt + 2], g);
     double u0, u1;
@@ -559,7 +557,7 @@ struct PcgPtOp {
 };
 
 __global__ __launch_bounds__(kTile) void k_backsub(Dev d) {
-  PcgPtOp<1> op{d, 0, {}, {}};
+  PcgPtOp<1> op{d, {}, {}};
   point_tile_reduce<3>(d, op, blockIdx.x);
 }
 
@@ -670,12 +668,16 @@ __device__ __forceinline__ double block_sum_array(const double* a, int n, int st
 // Kernel boundaries are the only grid-wide synchronisation: every global
 // scalar is re-derived in each block that needs it from a few per-block
 // partial sums, added in block order by the same code, so all blocks agree
-// bit for bit.  Per iteration `it`:
-//   pt   beta = rz_it / rz_{it-1} (0 at it = 0); p = z + beta p_prev (formed on
-//        the fly for the gathers and stored once); zp_i = C~_i^-1 sum_{k in i}
-//        w Jp^T (Jc p_cam(k)); at it >= 1 stops first if |r| <= tol |rhs|
-//   cam  chunk partials of sum_k w Jc^T (Jp zp_pt(k))
-//   q    q_j = B~_j p_j - sum of the chunk partials of camera j; p.q partials
+// bit for bit.  The two passes over the observations apply S to the
+// preconditioned residual z, not to the direction p: since p = z + beta p_prev,
+// S p = S z + beta S p_prev, so q = S p follows by the same recurrence as p and
+// no kernel has to form p before the passes.  Per iteration `it`:
+//   pt   stop if it >= 1 and |r| <= tol |rhs| (or rhs = 0);
+//        else u_i = C~_i^-1 sum_{k in i} w Jp^T (Jc z_cam(k))
+//   cam  chunk partials of sum_k w Jc^T (Jp u_pt(k))
+//   q    beta = rz_it / rz_{it-1} (0 at it = 0); S z_j = B~_j z_j - sum of the
+//        chunk partials of camera j; p = z + beta p, q = S z + beta q in
+//        place; p.q partials
 //   xr   alpha = rz_it / p.q (stop if p.q is not positive); x += alpha p,
 //        r -= alpha q, z = M^-1 r; partials of r.r and r.z for it + 1
 // All four return at once after the solve has stopped, so the host may queue
@@ -713,8 +715,6 @@ __global__ __launch_bounds__(kWave) void k_pcg_init(Dev d) {
     d.r[e] = r;
     d.x[e] = 0.0;
     d.zc[e] = z;
-    d.pbuf[e] = z;                 // p of iteration 0
-    d.pbuf[9 * d.nc + e] = 0.0;    // "previous" direction, weighted by beta = 0
     rr = r * r;
     rz = r * z;
   }
@@ -732,46 +732,41 @@ __global__ __launch_bounds__(kWave) void k_pcg_init(Dev d) {
   }
 }
 
-// Start of iteration it: stop if it >= 1 and |r| <= tol |rhs| (or if rhs = 0),
-// else beta = rz_it / rz_{it-1} and p = z + beta p_prev (iteration 0 keeps the
-// p = z stored by the initialisation).
-__global__ __launch_bounds__(kWave) void k_pcg_pnext(Dev d, int it) {
-  int done = d.pcg->done;
-  const int64_t e = (int64_t)blockIdx.x * kWave + threadIdx.x;
-  const bool on = e < 9 * d.nc;
-  double* pnew = d.pbuf + (int64_t)(it & 1) * 9 * d.nc;
-  const double* pold = d.pbuf + (int64_t)((it + 1) & 1) * 9 * d.nc;
-  double ze = on ? d.zc[e] : 0.0, pe = on ? pold[e] : 0.0;
-  const double* const arr[4] = {red_rhs(d), red_rr(d, it & 1), red_rz(d, it & 1),
-                                red_rz(d, (it + 1) & 1)};
-  double part[4];
-  lane_partials<4>(arr, d.red_nb, part);
-  double rhs2 = part[0], rr = part[1], rz_new = part[2], rz_old = part[3];
-  pin(rhs2);
-  pin(rr);
-  pin(rz_new);
-  pin(rz_old);
-  pin(ze);
-  pin(pe);
-  pin(done);
-  if (done) return;
+// Start of iteration it, by one wavefront from its lane partials of |rhs|^2
+// and |r_it|^2: true if the solve stops here (it >= 1 and |r| <= tol |rhs|,
+// or rhs = 0 at it = 0).  The wavefront of block 0 that decides so records
+// the outcome.
+__device__ __forceinline__ bool pcg_stop_test(const Dev& d, int it, double rhs2, double rr,
+                                              bool record) {
   const double rhs_norm = sqrt(wave_sum(rhs2));
   if (it == 0) {
-    if (rhs_norm == 0.0 && blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, 0, 0.0, 0.0, 0);
-    return;
+    const bool stop = rhs_norm == 0.0;
+    if (stop && record && threadIdx.x == 0) stop_pcg(d, 0, 0.0, 0.0, 0);
+    return stop;
   }
   const double res = sqrt(wave_sum(rr));
-  if (res <= d.tol * rhs_norm) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) stop_pcg(d, it, res, rhs_norm, 0);
-    return;
-  }
-  const double beta = wave_sum(rz_new) / wave_sum(rz_old);
-  if (on) pnew[e] = ze + beta * pe;
+  const bool stop = res <= d.tol * rhs_norm;
+  if (stop && record && threadIdx.x == 0) stop_pcg(d, it, res, rhs_norm, 0);
+  return stop;
 }
 
-__global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
+// The stop test on its own, ahead of the tile-parallel point pass (the LDS
+// point pass makes it in each block itself).
+__global__ __launch_bounds__(kWave) void k_pcg_stop(Dev d, int it) {
+  int done = d.pcg->done;
+  const double* const arr[2] = {red_rhs(d), red_rr(d, it & 1)};
+  double part[2];
+  lane_partials<2>(arr, d.red_nb, part);
+  pin(part[0]);
+  pin(part[1]);
+  pin(done);
+  if (done) return;
+  (void)pcg_stop_test(d, it, part[0], part[1], true);
+}
+
+__global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d) {
   if (d.pcg->done) return;
-  PcgPtOp<0> op{d, it, {}, {}};
+  PcgPtOp<0> op{d, {}, {}};
   point_tile_reduce<3>(d, op, blockIdx.x);
 }
 
@@ -786,7 +781,8 @@ __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d, int it) {
 // the next slot are loaded while the current one is computed.  Wavefronts
 // never wait for each other, so one's memory wait hides behind another's
 // arithmetic.
-//   MODE 0: z = C~^-1 (E^T p) into the point records (PCG);
+//   MODE 0: u = C~^-1 (E^T z) into the point records (PCG), after the
+//           iteration's stop test, which wavefront 0 of each block makes;
 //   MODE 1: dp = C~^-1 (-g_p - E^T dc) and the trial points (back-substitution).
 template <int MODE>
 __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
@@ -795,7 +791,8 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * (kLdsBlock / kWave) + threadIdx.x / kWave;
   const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
-  const double* xbase = MODE == 0 ? d.pbuf + (int64_t)(it & 1) * 9 * d.nc : d.x;
+  __shared__ int s_stop;
+  const double* xbase = MODE == 0 ? d.zc : d.x;
   // Pipeline: indices two slots ahead, point coordinates and weight one slot
   // ahead.  Every load in the loop is issued unconditionally (indices past the
   // range are clamped into it and the results discarded), so the number of
@@ -813,11 +810,13 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   }
   // Camera table: one row of kCamLdsStride doubles per camera, the unit
   // quaternion, t, f, k1, k2 (from the geometry tables) and the camera's
-  // 9-vector that this pass applies (p in the PCG, dc in the back-substitution),
+  // 9-vector that this pass applies (z in the PCG, dc in the back-substitution),
   // so that the loop reads no camera data from memory.  Every thread issues all
-  // of its loads before its first LDS store.  The PCG stop flag is read with
-  // them and tested only then, so a working launch does not pay a memory round
-  // trip for the test.
+  // of its loads before its first LDS store.  The PCG stop flag, and in
+  // wavefront 0 the partial sums of the stop test, are read with them and
+  // used only then, so a working launch does not pay a memory round trip for
+  // the test; its outcome reaches the other wavefronts through LDS at the
+  // barrier before the loop.
   {
     const int ne = kCamLdsStride * (int)d.nc;
     const double* tabd = reinterpret_cast<const double*>(d.tab);
@@ -831,11 +830,21 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
                                 : (k < 10 ? tabd + 16 * j + 9 + (k - 4) : xbase + 9 * j + (k - 10));
       t[u] = *src;
     }
+    const bool tester = MODE == 0 && threadIdx.x < kWave;
+    double part[2] = {0.0, 0.0};
+    if (tester) {
+      const double* const arr[2] = {red_rhs(d), red_rr(d, it & 1)};
+      lane_partials<2>(arr, d.red_nb, part);
+    }
     if (done) return;
 #pragma unroll
     for (int u = 0; u < kCamLdsFill; ++u) {
       const int e = (int)threadIdx.x + u * kLdsBlock;
       if (e < ne) s_cam[e] = t[u];
+    }
+    if (tester) {
+      const bool stop = pcg_stop_test(d, it, part[0], part[1], blockIdx.x == 0);
+      if (threadIdx.x == 0) s_stop = stop;
     }
   }
   if (threadIdx.x == 0) s_prog = 0;
@@ -853,6 +862,7 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     cw = d.w_pt[min(s0, last)];
   }
   __syncthreads();
+  if (MODE == 0 && s_stop) return;
   double carry[3] = {0.0, 0.0, 0.0};
   int carry_pt = -1;
   int mine = 0;
@@ -1059,33 +1069,50 @@ __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
 
 __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
   const CamLane c = cam_lane(blockIdx.x, d.nc);
-  const double* p = d.pbuf + (int64_t)(it & 1) * 9 * d.nc + 9 * c.j;
+  const int64_t e = 9 * c.j + c.a;
+  const double* z = d.zc + 9 * c.j;
   const double* Bd = d.Bd + 45 * c.j;
   int done = d.pcg->done;
   int c0 = d.cam_chunk_ptr[c.j], c1 = d.cam_chunk_ptr[c.j + 1];
-  double bd[9], pv[9];
+  double bd[9], zv[9];
 #pragma unroll
   for (int b = 0; b < 9; ++b) {
     bd[b] = Bd[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)];
-    pv[b] = p[b];
+    zv[b] = z[b];
   }
+  double ze = z[c.a], pe = d.pbuf[e], qe = d.q[e];   // p and q of it - 1 (unused at it = 0)
+  const double* const arr[2] = {red_rz(d, it & 1), red_rz(d, (it + 1) & 1)};
+  double part[2];
+  lane_partials<2>(arr, d.red_nb, part);
 #pragma unroll
   for (int b = 0; b < 9; ++b) {
     pin(bd[b]);
-    pin(pv[b]);
+    pin(zv[b]);
   }
+  pin(ze);
+  pin(pe);
+  pin(qe);
+  pin(part[0]);
+  pin(part[1]);
   pin(c0);
   pin(c1);
   pin(done);
   if (done) return;
-  double qa = 0.0;
+  double sz = 0.0;
 #pragma unroll
-  for (int b = 0; b < 9; ++b) qa += bd[b] * pv[b];
-  for (int ch = c0; ch < c1; ++ch) qa -= d.pcg_part[(int64_t)ch * 9 + c.a];
+  for (int b = 0; b < 9; ++b) sz += bd[b] * zv[b];
+  for (int ch = c0; ch < c1; ++ch) sz -= d.pcg_part[(int64_t)ch * 9 + c.a];
+  double pn = ze, qn = sz;
+  if (it > 0) {
+    const double beta = wave_sum(part[0]) / wave_sum(part[1]);
+    pn = ze + beta * pe;
+    qn = sz + beta * qe;
+  }
   double pq = 0.0;
   if (c.on) {
-    d.q[9 * c.j + c.a] = qa;
-    pq = p[c.a] * qa;
+    d.pbuf[e] = pn;
+    d.q[e] = qn;
+    pq = pn * qn;
   }
   pq = wave_sum(pq);
   if (threadIdx.x == 0) red_pq(d)[blockIdx.x] = pq;
@@ -1095,7 +1122,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_xr(Dev d, int it) {
   const CamLane c = cam_lane(blockIdx.x, d.nc);
   const int64_t e = 9 * c.j + c.a;
   int done = d.pcg->done;
-  double pe = d.pbuf[(int64_t)(it & 1) * 9 * d.nc + e];
+  double pe = d.pbuf[e];
   double xe = d.x[e], re = d.r[e], qe = d.q[e];
   const double* Mi = d.Minv + 45 * c.j;
   double m[9];
@@ -1582,16 +1609,14 @@ void launch_precond(const Dev& d, hipStream_t s) {
 void launch_pcg_init(const Dev& d, hipStream_t s) {
   launch(k_pcg_init, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d);
 }
-void launch_pcg_pnext(const Dev& d, int it, hipStream_t s) {
-  launch(k_pcg_pnext, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
-}
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
-  if (d.cam_lds_bytes > 0) {
-    if (d.lds_blocks > 0)
-      launch(k_pcg_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s, d.cam_lds_bytes, d, it);
-  } else if (d.n_tiles > 0) {
-    launch(k_pcg_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d, it);
+  if (d.cam_lds_bytes > 0 && d.lds_blocks > 0) {
+    launch(k_pcg_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s, d.cam_lds_bytes, d, it);
+    return;
   }
+  launch(k_pcg_stop, dim3(1), dim3(kWave), s, 0u, d, it);
+  if (d.cam_lds_bytes == 0 && d.n_tiles > 0)
+    launch(k_pcg_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
 }
 void launch_pcg_cam(const Dev& d, hipStream_t s) {
   if (d.n_chunk_blocks > 0) launch(k_pcg_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
