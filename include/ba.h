@@ -203,11 +203,13 @@ enum {
   BA_K_DAMP_PT,      /* damped point blocks, their inverses, v                     */
   BA_K_SCHUR_CAM,    /* camera-order E v and Ebar C~^-1 Ebar^T partials            */
   BA_K_PRECOND,      /* per camera B~, rhs, S_jj and its Cholesky factor           */
-  BA_K_PCG_INIT,     /* PCG start: r = rhs, z = M^-1 r, p = z                      */
-  BA_K_PCG_PT,       /* PCG point pass: C~^-1 E^T p                                */
-  BA_K_PCG_CAM,      /* PCG camera pass: chunk partials of E C~^-1 E^T p            */
-  BA_K_PCG_Q,        /* PCG q = B~ p - E C~^-1 E^T p and p.q partials               */
-  BA_K_PCG_XR,       /* PCG update of x, r, z                                      */
+  BA_K_PCG_INIT,     /* PCG start: r = rhs, z = M^-1 r                              */
+  BA_K_PCG_PT,       /* PCG point pass: stop test, C~^-1 E^T z                      */
+  BA_K_PCG_CAM,      /* PCG camera pass: chunk partials of E C~^-1 E^T z            */
+  BA_K_PCG_Q,        /* PCG p, q = S p by recurrence, p.q partials (no launches
+                        when the camera table fits in LDS: BA_K_PCG_XR does it)     */
+  BA_K_PCG_XR,       /* PCG update of x, r, z (with the camera table in LDS, one
+                        kernel that also forms p, q and p.q)                        */
   BA_K_BACKSUB,      /* point back-substitution and trial points                   */
   BA_K_RETRACT,      /* trial cameras                                              */
   BA_K_COST,         /* trial cost                                                 */

@@ -106,7 +106,7 @@ struct ba_problem {
   double *Cinv = nullptr, *Bd = nullptr, *rhs = nullptr, *Minv = nullptr,
          *Mfull = nullptr, *schur_part = nullptr;
   double *x = nullptr, *r = nullptr, *zc = nullptr, *pbuf = nullptr, *q = nullptr, *prec = nullptr,
-         *pcg_part = nullptr, *pq_cam = nullptr, *red_part = nullptr;
+         *pcg_part = nullptr, *red_part = nullptr, *pt_dot = nullptr;
   PcgState* pcg = nullptr;
   double *dp = nullptr, *cost_part = nullptr;
   StepOut* out = nullptr;
@@ -189,8 +189,8 @@ Dev make_dev(const ba_problem* h) {
   d.q = h->q;
   d.prec = h->prec;
   d.pcg_part = h->pcg_part;
-  d.pq_cam = h->pq_cam;
   d.red_part = h->red_part;
+  d.pt_dot = h->pt_dot;
   d.red_nb = pcg_red_blocks(h->nc);
   d.host_done = h->h_done_dev;
   d.pcg = h->pcg;
@@ -297,8 +297,12 @@ int stage_pcg(ba_problem* h) {
     for (int k = 0; k < n; ++k, ++next_it) {
       TIMED(BA_K_PCG_PT, next_it, launch_pcg_pt(d, next_it, h->stream));
       TIMED(BA_K_PCG_CAM, next_it, launch_pcg_cam(d, h->stream));
-      TIMED(BA_K_PCG_Q, next_it, launch_pcg_q(d, next_it, h->stream));
-      TIMED(BA_K_PCG_XR, next_it, launch_pcg_xr(d, next_it, h->stream));
+      if (pcg_fused_step(d)) {
+        TIMED(BA_K_PCG_XR, next_it, launch_pcg_step(d, next_it, h->stream));
+      } else {
+        TIMED(BA_K_PCG_Q, next_it, launch_pcg_q(d, next_it, h->stream));
+        TIMED(BA_K_PCG_XR, next_it, launch_pcg_xr(d, next_it, h->stream));
+      }
     }
     return BA_OK;
   };
@@ -482,7 +486,6 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   A.add(h->pbuf, 9 * nc);
   A.add(h->q, 9 * nc);
   A.add(h->pcg, 1);
-  A.add(h->pq_cam, nc);
   A.add(h->out, 1);
   A.add(h->flags, 2);
   A.add(h->cam_chunk_ptr, nc + 1);
@@ -641,7 +644,8 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   P.add(h->schur_part, n_ch1 * kSchurVals);
   P.add(h->pcg_part, n_ch1 * 9);
   P.add(h->cost_part, (int64_t)std::max(h->n_cost_blocks, 1));
-  P.add(h->red_part, 6 * (int64_t)pcg_red_blocks(nc));
+  P.add(h->red_part, 8 * (int64_t)pcg_red_blocks(nc) + 2);
+  P.add(h->pt_dot, (int64_t)std::max(h->lds_blocks, 1));
   rc = P.commit();
   if (rc != BA_OK) return rc;
   TRY(hipMemsetAsync(P.base, 0, P.size, s));

@@ -109,8 +109,8 @@ struct Dev {
   double* q;
   double* prec;      // per-point 64-byte record: X (3), z = C~^-1 E^T p (3), pad (2)
   double* pcg_part;
-  double* pq_cam;    // per camera p_j . q_j
-  double* red_part;  // per-block partial sums of the camera-vector kernels, 6 x red_nb
+  double* red_part;  // per-block partial sums of the camera-vector kernels, 8 x red_nb, then 2
+  double* pt_dot;    // per-block partials of z^T E C~^-1 E^T z from the LDS point pass
   int red_nb;        // blocks of the camera-vector kernels
   int* host_done;    // host-mapped copy of pcg->done, polled between batches
   PcgState* pcg;
@@ -145,6 +145,9 @@ void launch_pcg_pt(const Dev& d, int it, hipStream_t s);
 void launch_pcg_cam(const Dev& d, hipStream_t s);
 void launch_pcg_q(const Dev& d, int it, hipStream_t s);
 void launch_pcg_xr(const Dev& d, int it, hipStream_t s);
+// With the LDS point pass, k_pcg_step replaces k_pcg_q and k_pcg_xr.
+bool pcg_fused_step(const Dev& d);
+void launch_pcg_step(const Dev& d, int it, hipStream_t s);
 void launch_pcg_final(const Dev& d, int iters, hipStream_t s);
 int pcg_red_blocks(int64_t nc);   // blocks of the camera-vector kernels
 void launch_backsub(const Dev& d, hipStream_t s);

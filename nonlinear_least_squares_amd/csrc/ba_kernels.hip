@@ -602,6 +602,18 @@ __device__ __forceinline__ double precond_lane(const Dev& d, const CamLane& c, d
   return z;
 }
 
+// (B~_j v_j)_a for the lanes of a camera group that each hold one entry of v.
+__device__ __forceinline__ double bd_row_times(const Dev& d, const CamLane& c, double v) {
+  const double* Bd = d.Bd + 45 * c.j;
+  double m[9];
+#pragma unroll
+  for (int b = 0; b < 9; ++b) m[b] = Bd[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)];
+  double y = 0.0;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) y += m[b] * __shfl(v, c.base + b, kWave);
+  return y;
+}
+
 __device__ __forceinline__ double block_sum_array_serial(const double* a, int n) {
   double v = 0.0;
   for (int k = 0; k < n; ++k) v += a[k];
@@ -680,7 +692,8 @@ __device__ __forceinline__ double block_sum_array(const double* a, int n, int st
 //        place; p.q partials
 //   xr   alpha = rz_it / p.q (stop if p.q is not positive); x += alpha p,
 //        r -= alpha q, z = M^-1 r; partials of r.r and r.z for it + 1
-// All four return at once after the solve has stopped, so the host may queue
+// With the LDS point pass, k_pcg_step does q and xr in one launch.  All of
+// them return at once after the solve has stopped, so the host may queue
 // iterations past the stopping point.
 
 // Grid size of the camera-vector kernels: one wavefront per block, 7 cameras
@@ -692,6 +705,9 @@ __device__ __forceinline__ double* red_rr(const Dev& d, int par) { return d.red_
 __device__ __forceinline__ double* red_rz(const Dev& d, int par) { return red_rr(d, par) + d.red_nb; }
 __device__ __forceinline__ double* red_rhs(const Dev& d) { return d.red_part + 4 * d.red_nb; }
 __device__ __forceinline__ double* red_pq(const Dev& d) { return d.red_part + 5 * d.red_nb; }
+__device__ __forceinline__ double* red_zbz(const Dev& d, int par) { return d.red_part + (6 + par) * d.red_nb; }
+// p.q of the iterations of either parity (written by block 0 of k_pcg_step)
+__device__ __forceinline__ double* pcg_pq_hist(const Dev& d) { return d.red_part + 8 * d.red_nb; }
 
 __device__ __forceinline__ void stop_pcg(const Dev& d, int iters, double res, double rhs_norm,
                                          int breakdown) {
@@ -710,19 +726,23 @@ __global__ __launch_bounds__(kWave) void k_pcg_init(Dev d) {
   const int64_t e = 9 * c.j + c.a;
   const double r = c.on ? d.rhs[e] : 0.0;
   const double z = precond_lane(d, c, r);
-  double rr = 0.0, rz = 0.0;
+  const double bz = bd_row_times(d, c, z);
+  double rr = 0.0, rz = 0.0, zbz = 0.0;
   if (c.on) {
     d.r[e] = r;
     d.x[e] = 0.0;
     d.zc[e] = z;
     rr = r * r;
     rz = r * z;
+    zbz = z * bz;
   }
   rr = wave_sum(rr);
   rz = wave_sum(rz);
+  zbz = wave_sum(zbz);
   if (threadIdx.x == 0) {
     red_rr(d, 0)[blockIdx.x] = rr;
     red_rz(d, 0)[blockIdx.x] = rz;
+    red_zbz(d, 0)[blockIdx.x] = zbz;
     red_rhs(d)[blockIdx.x] = rr;
     if (blockIdx.x == 0) {
       d.pcg->done = 0;
@@ -866,6 +886,7 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   double carry[3] = {0.0, 0.0, 0.0};
   int carry_pt = -1;
   int mine = 0;
+  double ydot = 0.0;   // MODE 0: this lane's share of sum_i y_i . u_i
   for (int base = sb; base < se; base += kWave) {
     const int s = base + lane;
     const bool valid = cpt >= 0;
@@ -953,6 +974,7 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
         d.prec[8 * (int64_t)cpt + 3] = z0;
         d.prec[8 * (int64_t)cpt + 4] = z1;
         d.prec[8 * (int64_t)cpt + 5] = z2;
+        ydot += y0 * z0 + y1 * z1 + y2 * z2;
       } else {
         d.dp[3 * cpt] = z0;
         d.dp[3 * cpt + 1] = z1;
@@ -992,6 +1014,21 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
       __builtin_amdgcn_s_setprio(1);
     } else {
       __builtin_amdgcn_s_setprio(0);
+    }
+  }
+  if (MODE == 0) {
+    // z^T E C~^-1 E^T z = sum_i y_i . u_i (y_i = the point's sum before C~^-1),
+    // added per wavefront, then in wavefront order: one partial per block.
+    __shared__ double s_ydot[kLdsBlock / kWave];
+    __builtin_amdgcn_s_setprio(0);
+    ydot = wave_sum(ydot);
+    if (lane == 0) s_ydot[threadIdx.x / kWave] = ydot;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int w = 0; w < kLdsBlock / kWave; ++w) t += s_ydot[w];
+      d.pt_dot[blockIdx.x] = t;
     }
   }
 }
@@ -1172,6 +1209,108 @@ __global__ __launch_bounds__(kWave) void k_pcg_xr(Dev d, int it) {
   if (threadIdx.x == 0) {
     red_rr(d, (it + 1) & 1)[blockIdx.x] = rr;
     red_rz(d, (it + 1) & 1)[blockIdx.x] = rzn;
+  }
+}
+
+// q, p.q and the update in one launch (used with the LDS point pass, which
+// leaves one partial of z^T E C~^-1 E^T z per block).  p.q needs no sum over
+// the new q: with p = z + beta p_prev and the directions S-conjugate,
+// p^T S p = z^T S z - beta^2 p_prev^T S p_prev (the recurrence of Chronopoulos
+// and Gear), and z^T S z = z^T B~ z - z^T E C~^-1 E^T z comes from partials
+// that the previous update (z^T B~ z) and the point pass (the rest) leave.
+__global__ __launch_bounds__(kWave) void k_pcg_step(Dev d, int it) {
+  const CamLane c = cam_lane(blockIdx.x, d.nc);
+  const int64_t e = 9 * c.j + c.a;
+  const double* z = d.zc + 9 * c.j;
+  const double* Bd = d.Bd + 45 * c.j;
+  const double* Mi = d.Minv + 45 * c.j;
+  int done = d.pcg->done;
+  int c0 = d.cam_chunk_ptr[c.j], c1 = d.cam_chunk_ptr[c.j + 1];
+  double bd[9], zv[9], m[9];
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const int k = c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a);
+    bd[b] = Bd[k];
+    zv[b] = z[b];
+    m[b] = Mi[k];
+  }
+  double ze = z[c.a], pe = d.pbuf[e], qe = d.q[e], xe = d.x[e], re = d.r[e];
+  double pq_prev = pcg_pq_hist(d)[(it + 1) & 1];
+  const double* const arr[3] = {red_rz(d, it & 1), red_rz(d, (it + 1) & 1), red_zbz(d, it & 1)};
+  double part[3];
+  lane_partials<3>(arr, d.red_nb, part);
+  double ydot = lane_partial(d.pt_dot, d.lds_blocks);
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    pin(bd[b]);
+    pin(zv[b]);
+    pin(m[b]);
+  }
+  pin(ze);
+  pin(pe);
+  pin(qe);
+  pin(xe);
+  pin(re);
+  pin(pq_prev);
+  pin(part[0]);
+  pin(part[1]);
+  pin(part[2]);
+  pin(ydot);
+  pin(c0);
+  pin(c1);
+  pin(done);
+  if (done) return;
+  double sz = 0.0;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) sz += bd[b] * zv[b];
+  for (int ch = c0; ch < c1; ++ch) sz -= d.pcg_part[(int64_t)ch * 9 + c.a];
+  const double rz = wave_sum(part[0]);
+  double pq = wave_sum(part[2]) - wave_sum(ydot);
+  double pn = ze, qn = sz;
+  if (it > 0) {
+    const double beta = rz / wave_sum(part[1]);
+    pq -= beta * beta * pq_prev;
+    pn = ze + beta * pe;
+    qn = sz + beta * qe;
+  }
+  if (!(pq > 0.0) || !isfinite(pq)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      const double rhs_norm = sqrt(block_sum_array_serial(red_rhs(d), d.red_nb));
+      const double res = it == 0 ? rhs_norm : sqrt(block_sum_array_serial(red_rr(d, it & 1), d.red_nb));
+      stop_pcg(d, it, res, rhs_norm, 1);
+    }
+    return;
+  }
+  const double alpha = rz / pq;
+  double r = 0.0;
+  if (c.on) {
+    d.pbuf[e] = pn;
+    d.q[e] = qn;
+    d.x[e] = xe + alpha * pn;
+    r = re - alpha * qn;
+    d.r[e] = r;
+  }
+  double zn = 0.0;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) zn += m[b] * __shfl(r, c.base + b, kWave);
+  double bz = 0.0;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) bz += bd[b] * __shfl(zn, c.base + b, kWave);
+  double rr = 0.0, rzn = 0.0, zbz = 0.0;
+  if (c.on) {
+    d.zc[e] = zn;
+    rr = r * r;
+    rzn = r * zn;
+    zbz = zn * bz;
+  }
+  rr = wave_sum(rr);
+  rzn = wave_sum(rzn);
+  zbz = wave_sum(zbz);
+  if (threadIdx.x == 0) {
+    red_rr(d, (it + 1) & 1)[blockIdx.x] = rr;
+    red_rz(d, (it + 1) & 1)[blockIdx.x] = rzn;
+    red_zbz(d, (it + 1) & 1)[blockIdx.x] = zbz;
+    if (blockIdx.x == 0) pcg_pq_hist(d)[it & 1] = pq;
   }
 }
 
@@ -1610,7 +1749,7 @@ void launch_pcg_init(const Dev& d, hipStream_t s) {
   launch(k_pcg_init, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d);
 }
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
-  if (d.cam_lds_bytes > 0 && d.lds_blocks > 0) {
+  if (pcg_fused_step(d)) {
     launch(k_pcg_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s, d.cam_lds_bytes, d, it);
     return;
   }
@@ -1626,6 +1765,10 @@ void launch_pcg_q(const Dev& d, int it, hipStream_t s) {
 }
 void launch_pcg_xr(const Dev& d, int it, hipStream_t s) {
   launch(k_pcg_xr, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
+}
+bool pcg_fused_step(const Dev& d) { return d.cam_lds_bytes > 0 && d.lds_blocks > 0; }
+void launch_pcg_step(const Dev& d, int it, hipStream_t s) {
+  launch(k_pcg_step, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
 }
 void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
   launch(k_pcg_final, dim3(1), dim3(kWave), s, 0u, d, iters);
