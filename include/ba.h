@@ -63,6 +63,16 @@ enum {
 };
 
 enum { BA_MEM_HOST = 0, BA_MEM_DEVICE = 1 };
+/* Solver of the reduced camera system S dc = rhs (the Schur complement of the
+ * point blocks, eq. (2) of the NeRF-SLAM reproduction notes, sec. 3.2):
+ *   BA_SOLVER_PCG          implicit S, block-Jacobi PCG (any size);
+ *   BA_SOLVER_DENSE_SCHUR  explicit S and a Cholesky factorisation on the
+ *                          device, the direct solver that the eager-mode BA
+ *                          summary uses for small and medium problems; up to
+ *                          BA_DENSE_MAX_CAMS cameras (S takes (9 n_cams)^2
+ *                          doubles of device memory). */
+enum { BA_SOLVER_PCG = 0, BA_SOLVER_DENSE_SCHUR = 1 };
+#define BA_DENSE_MAX_CAMS 2048
 enum { BA_LOSS_SQUARED = 0, BA_LOSS_HUBER = 1 };
 
 typedef struct {
@@ -79,6 +89,9 @@ typedef struct {
   int mem;               /* BA_MEM_HOST / BA_MEM_DEVICE: where ba_create inputs
                             and ba_set_params inputs live                       */
   void* stream;          /* hipStream_t or NULL                                  */
+  int solver;            /* BA_SOLVER_PCG (default) or BA_SOLVER_DENSE_SCHUR;
+                            with the dense solver, pcg_iters and pcg_rel_res
+                            of the step information are 0                       */
 } ba_options;
 
 typedef struct {
@@ -153,7 +166,7 @@ int ba_get_sizes(const ba_problem* h, int64_t* n_cams, int64_t* n_pts, int64_t* 
 enum {
   BA_STAGE_LINEARIZE = 1,  /* residuals, Jacobians, B, g_c, C, g_p at the current parameters */
   BA_STAGE_SCHUR = 2,      /* damping with the current lambda, C~^-1, v, rhs, S_jj, Cholesky */
-  BA_STAGE_PCG = 3,        /* camera step dc                                                  */
+  BA_STAGE_PCG = 3,        /* camera step dc (PCG, or the dense solve when selected)          */
   BA_STAGE_UPDATE = 4      /* dp, trial parameters, trial cost                                */
 };
 
@@ -185,6 +198,9 @@ enum {
   BA_DBG_PTS_TRIAL,     /* double n_pts x 3                                                        */
   BA_DBG_PCG,           /* double 2: iterations, relative residual                                 */
   BA_DBG_TRIAL_COST,    /* double 1                                                                */
+  BA_DBG_S,             /* double (9 n_cams)^2: the explicit reduced camera matrix S, row-major,
+                           assembled on the device from the state after BA_STAGE_SCHUR (the dense
+                           solver only; BA_ERR_ARG otherwise)                                      */
   BA_DBG_NUM
 };
 
@@ -213,6 +229,12 @@ enum {
   BA_K_BACKSUB,      /* point back-substitution and trial points                   */
   BA_K_RETRACT,      /* trial cameras                                              */
   BA_K_COST,         /* trial cost                                                 */
+  BA_K_DS_RUNS,      /* dense solver: F = Ebar chol(C~^-1) per (point, camera) run  */
+  BA_K_DS_FILL,      /* dense solver: S cleared, padding, rhs row                  */
+  BA_K_DS_ASSEMBLE,  /* dense solver: lower 9x9 blocks of S                        */
+  BA_K_DS_PANEL,     /* dense solver: diagonal tile factor and tile-row solves      */
+  BA_K_DS_UPDATE,    /* dense solver: trailing update (fp64 MFMA)                  */
+  BA_K_DS_BACKSOLVE, /* dense solver: L^T dc = L^-1 rhs                            */
   BA_K_NUM
 };
 

@@ -17,17 +17,20 @@ BA_OK, BA_ERR_ARG, BA_ERR_NONFINITE, BA_ERR_NOT_SPD, BA_ERR_DEVICE, BA_ERR_ALLOC
 BA_MEM_HOST, BA_MEM_DEVICE = 0, 1
 BA_LOSS_SQUARED, BA_LOSS_HUBER = 0, 1
 BA_STAGE_LINEARIZE, BA_STAGE_SCHUR, BA_STAGE_PCG, BA_STAGE_UPDATE = 1, 2, 3, 4
+BA_SOLVER_PCG, BA_SOLVER_DENSE_SCHUR = 0, 1
+BA_DENSE_MAX_CAMS = 2048
 
 DBG = dict(perm_pt=0, perm_cam=1, pt_ptr=2, cam_ptr=3, r=4, Jc=5, Jp=6, w=7, B=8, gc=9, C=10,
            gp=11, Bd=12, Cinv=13, v=14, rhs=15, M=16, dc=17, dp=18, cams_trial=19,
-           points_trial=20, pcg=21, trial_cost=22)
+           points_trial=20, pcg=21, trial_cost=22, S=23)
 DBG_INT = {"perm_pt", "perm_cam", "pt_ptr", "cam_ptr"}
 DBG_SHAPE = {"r": (-1, 2), "Jc": (-1, 2, 9), "Jp": (-1, 2, 3), "B": (-1, 9, 9), "gc": (-1, 9),
              "C": (-1, 3, 3), "gp": (-1, 3), "Bd": (-1, 9, 9), "Cinv": (-1, 3, 3), "v": (-1, 3),
              "rhs": (-1, 9), "M": (-1, 9, 9), "dc": (-1, 9), "dp": (-1, 3),
              "cams_trial": (-1, 9), "points_trial": (-1, 3)}
 KERNELS = ["lin_pt", "lin_cam", "damp_pt", "schur_cam", "precond", "pcg_init", "pcg_pt",
-           "pcg_cam", "pcg_q", "pcg_xr", "backsub", "retract", "cost"]
+           "pcg_cam", "pcg_q", "pcg_xr", "backsub", "retract", "cost", "ds_runs", "ds_fill",
+           "ds_assemble", "ds_panel", "ds_update", "ds_backsolve"]
 
 
 class ba_options(C.Structure):
@@ -35,7 +38,8 @@ class ba_options(C.Structure):
                 ("lambda_up", C.c_double), ("lambda_down", C.c_double),
                 ("lambda_min", C.c_double), ("lambda_max", C.c_double),
                 ("diag_floor", C.c_double), ("pcg_max_iters", C.c_int),
-                ("pcg_rel_tol", C.c_double), ("mem", C.c_int), ("stream", C.c_void_p)]
+                ("pcg_rel_tol", C.c_double), ("mem", C.c_int), ("stream", C.c_void_p),
+                ("solver", C.c_int)]
 
 
 class ba_step_info(C.Structure):
@@ -246,6 +250,8 @@ class Problem:
                        dtype=np.int32 if name in DBG_INT else np.float64)
         _check(lib().ba_debug_get(self.h, which, C.c_void_p(out.ctypes.data), nbytes),
                "ba_debug_get")
+        if name == "S":
+            return out.reshape(9 * self.n_cams, 9 * self.n_cams)
         return out.reshape(DBG_SHAPE[name]) if name in DBG_SHAPE else out
 
     def profile(self, kernels=None, every=1):

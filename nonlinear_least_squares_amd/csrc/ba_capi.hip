@@ -87,6 +87,7 @@ struct ba_problem {
       cam_lds_bytes = 0, n_chunk_blocks = 0;
   Arena arena;   // everything sized by n_cams, n_pts, n_obs
   Arena arena2;  // partitions and partial sums, sized after the CSR offsets
+  Arena arena3;  // dense solver: runs, block pair lists, S
   // parameters: [cur] current, [1 - cur] trial
   double* cams[2] = {nullptr, nullptr};
   double* pts[2] = {nullptr, nullptr};
@@ -100,6 +101,11 @@ struct ba_problem {
   int32_t *tile_begin = nullptr,
           *cam_chunk_ptr = nullptr, *wave_begin = nullptr;
   int4* blk_chunk = nullptr;
+  // dense solver
+  int ds_ld = 0, ds_T = 0, ds_nruns = 0, ds_nblk = 0;
+  int32_t *ds_run = nullptr, *ds_blk_ptr = nullptr;
+  int2 *ds_blk = nullptr, *ds_pair = nullptr;
+  double *ds_F = nullptr, *ds_S = nullptr, *ds_diag = nullptr;
   // work arrays
   double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
          *gc = nullptr, *lin_part = nullptr;
@@ -198,6 +204,18 @@ Dev make_dev(const ba_problem* h) {
   d.cost_part = h->cost_part;
   d.out = h->out;
   d.flags = h->flags;
+  d.ds_n = (int)(9 * h->nc);
+  d.ds_ld = h->ds_ld;
+  d.ds_T = h->ds_T;
+  d.ds_nruns = h->ds_nruns;
+  d.ds_nblk = h->ds_nblk;
+  d.ds_run = h->ds_run;
+  d.ds_blk = h->ds_blk;
+  d.ds_blk_ptr = h->ds_blk_ptr;
+  d.ds_pair = h->ds_pair;
+  d.ds_F = h->ds_F;
+  d.ds_S = h->ds_S;
+  d.ds_diag = h->ds_diag;
   return d;
 }
 
@@ -329,6 +347,27 @@ int stage_pcg(ba_problem* h) {
   return BA_OK;
 }
 
+// Dense solve of S dc = rhs: explicit S, Cholesky by tile columns with the
+// rhs as an extra row, back-substitution.
+int stage_dense(ba_problem* h) {
+  Dev d = make_dev(h);
+  hipStream_t s = h->stream;
+  TIMED(BA_K_DS_RUNS, -1, launch_ds_runs(d, s));
+  TIMED(BA_K_DS_FILL, -1, launch_ds_fill(d, s));
+  TIMED(BA_K_DS_ASSEMBLE, -1, launch_ds_assemble(d, s));
+  for (int k = 0; k < h->ds_T; ++k) {
+    TIMED(BA_K_DS_PANEL, -1, launch_ds_panel(d, k, s));
+    TIMED(BA_K_DS_UPDATE, -1, launch_ds_update(d, k, s));
+  }
+  TIMED(BA_K_DS_BACKSOLVE, -1, launch_ds_backsolve(d, s));
+  HIPC(hipGetLastError());
+  return BA_OK;
+}
+
+int stage_solve(ba_problem* h) {
+  return h->opt.solver == BA_SOLVER_DENSE_SCHUR ? stage_dense(h) : stage_pcg(h);
+}
+
 int stage_update(ba_problem* h) {
   Dev d = make_dev(h);
   TIMED(BA_K_BACKSUB, -1, launch_backsub(d, h->stream));
@@ -357,7 +396,7 @@ int lm_step(ba_problem* h, ba_step_info* info) {
   if (!h->linearized) CHECK_RC(stage_linearize(h));
   CHECK_RC(stage_schur(h));
   h->linearized = 1;
-  CHECK_RC(stage_pcg(h));
+  CHECK_RC(stage_solve(h));
   CHECK_RC(stage_update(h));
   CHECK_RC(read_out(h));
   const StepOut o = *h->h_out;
@@ -670,6 +709,79 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
 
 namespace {
 
+// Structure of the dense solver, once per handle: the (point, camera) runs of
+// the point order; for every lower 9x9 block (j2, j1) of S with j2 >= j1 the
+// pairs of runs (camera j2, camera j1) that share a point, in point order
+// (every diagonal block is listed, with no pairs when the camera sees
+// nothing); the arena for the run blocks F, S with its rhs rows and the
+// factor's diagonal tiles.
+int plan_dense(ba_problem* h) {
+  hipStream_t s = h->stream;
+  const int64_t N = h->nobs, nc = h->nc;
+  std::vector<int32_t> oc(N), op(N);
+  if (N) {
+    HIPC(hipMemcpyAsync(oc.data(), h->o_cam, sizeof(int32_t) * N, hipMemcpyDeviceToHost, s));
+    HIPC(hipMemcpyAsync(op.data(), h->o_pt, sizeof(int32_t) * N, hipMemcpyDeviceToHost, s));
+  }
+  HIPC(hipStreamSynchronize(s));
+  std::vector<int32_t> run;
+  for (int64_t k = 0; k < N; ++k)
+    if (k == 0 || oc[k] != oc[k - 1] || op[k] != op[k - 1]) run.push_back((int32_t)k);
+  const int64_t nruns = (int64_t)run.size();
+  run.push_back((int32_t)N);
+  // runs of one point are consecutive and in camera order
+  std::vector<int64_t> off((size_t)(nc * nc), 0);
+  auto for_pairs = [&](auto&& fn) {
+    for (int64_t g0 = 0; g0 < nruns;) {
+      int64_t g1 = g0 + 1;
+      while (g1 < nruns && op[run[g1]] == op[run[g0]]) ++g1;
+      for (int64_t a = g0; a < g1; ++a)
+        for (int64_t b = g0; b <= a; ++b) fn((int64_t)oc[run[a]] * nc + oc[run[b]], a, b);
+      g0 = g1;
+    }
+  };
+  for_pairs([&](int64_t key, int64_t, int64_t) { ++off[key]; });
+  std::vector<int2> blk;
+  std::vector<int32_t> blk_ptr;
+  int64_t npairs = 0;
+  for (int64_t j2 = 0; j2 < nc; ++j2)
+    for (int64_t j1 = 0; j1 <= j2; ++j1) {
+      const int64_t key = j2 * nc + j1, cnt = off[key];
+      if (cnt == 0 && j1 != j2) continue;
+      blk.push_back(make_int2((int)j2, (int)j1));
+      blk_ptr.push_back((int32_t)npairs);
+      off[key] = npairs;
+      npairs += cnt;
+    }
+  blk_ptr.push_back((int32_t)npairs);
+  if (npairs >= (int64_t)INT32_MAX) return fail(BA_ERR_ARG, "too many co-visible run pairs");
+  std::vector<int2> pair((size_t)std::max<int64_t>(npairs, 1));
+  for_pairs([&](int64_t key, int64_t a, int64_t b) { pair[off[key]++] = make_int2((int)a, (int)b); });
+  const int kt = ds_tile();
+  h->ds_ld = (int)((9 * nc + kt - 1) / kt * kt);
+  h->ds_T = h->ds_ld / kt;
+  h->ds_nruns = (int)nruns;
+  h->ds_nblk = (int)blk.size();
+  Arena& A = h->arena3;
+  A.add(h->ds_run, nruns + 1);
+  A.add(h->ds_blk, (int64_t)blk.size());
+  A.add(h->ds_blk_ptr, (int64_t)blk_ptr.size());
+  A.add(h->ds_pair, npairs);
+  A.add(h->ds_F, 27 * nruns);
+  A.add(h->ds_S, ((int64_t)h->ds_ld + kt) * h->ds_ld);
+  A.add(h->ds_diag, (int64_t)h->ds_T * kt * kt);
+  CHECK_RC(A.commit());
+  HIPC(hipMemcpyAsync(h->ds_run, run.data(), sizeof(int32_t) * run.size(), hipMemcpyHostToDevice, s));
+  HIPC(hipMemcpyAsync(h->ds_blk, blk.data(), sizeof(int2) * blk.size(), hipMemcpyHostToDevice, s));
+  HIPC(hipMemcpyAsync(h->ds_blk_ptr, blk_ptr.data(), sizeof(int32_t) * blk_ptr.size(),
+                      hipMemcpyHostToDevice, s));
+  if (npairs)
+    HIPC(hipMemcpyAsync(h->ds_pair, pair.data(), sizeof(int2) * npairs, hipMemcpyHostToDevice, s));
+  HIPC(ds_backsolve_limit(h->ds_ld));
+  HIPC(hipStreamSynchronize(s));
+  return BA_OK;
+}
+
 int check_options(const ba_options& o) {
   if (o.loss != BA_LOSS_SQUARED && o.loss != BA_LOSS_HUBER) return fail(BA_ERR_ARG, "bad loss");
   if (!(o.huber_delta > 0.0)) return fail(BA_ERR_ARG, "huber_delta must be > 0");
@@ -679,6 +791,7 @@ int check_options(const ba_options& o) {
   if (!(o.diag_floor >= 0.0)) return fail(BA_ERR_ARG, "diag_floor must be >= 0");
   if (o.pcg_max_iters < 0 || !(o.pcg_rel_tol >= 0.0)) return fail(BA_ERR_ARG, "bad PCG options");
   if (o.mem != BA_MEM_HOST && o.mem != BA_MEM_DEVICE) return fail(BA_ERR_ARG, "bad mem");
+  if (o.solver != BA_SOLVER_PCG && o.solver != BA_SOLVER_DENSE_SCHUR) return fail(BA_ERR_ARG, "bad solver");
   return BA_OK;
 }
 
@@ -697,10 +810,11 @@ int d2h(ba_problem* h, void* dst, const void* src, size_t bytes) {
   return BA_OK;
 }
 
-const char* kKernelNames[BA_K_NUM] = {"lin_pt",   "lin_cam", "damp_pt", "schur_cam",
-                                      "precond",  "pcg_init", "pcg_pt", "pcg_cam",
-                                      "pcg_q",    "pcg_xr",  "backsub", "retract",
-                                      "cost"};
+const char* kKernelNames[BA_K_NUM] = {"lin_pt",   "lin_cam",  "damp_pt",     "schur_cam",
+                                      "precond",  "pcg_init", "pcg_pt",      "pcg_cam",
+                                      "pcg_q",    "pcg_xr",   "backsub",     "retract",
+                                      "cost",     "ds_runs",  "ds_fill",     "ds_assemble",
+                                      "ds_panel", "ds_update", "ds_backsolve"};
 
 }  // namespace
 
@@ -720,6 +834,7 @@ int ba_options_default(ba_options* o) {
   o->pcg_rel_tol = 1e-6;
   o->mem = BA_MEM_HOST;
   o->stream = nullptr;
+  o->solver = BA_SOLVER_PCG;
   return BA_OK;
 }
 
@@ -729,6 +844,7 @@ void ba_destroy(ba_problem* h) {
   else (void)hipDeviceSynchronize();
   (void)hipFree(h->arena.base);
   (void)hipFree(h->arena2.base);
+  (void)hipFree(h->arena3.base);
   if (h->h_out) (void)hipHostFree(h->h_out);
   if (h->h_done) (void)hipHostFree(h->h_done);
   for (hipEvent_t e : h->batch_ev)
@@ -760,6 +876,10 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
   h->nc = n_cams;
   h->np = n_pts;
   h->nobs = n_obs;
+  if (h->opt.solver == BA_SOLVER_DENSE_SCHUR && n_cams > BA_DENSE_MAX_CAMS) {
+    delete h;
+    return fail(BA_ERR_ARG, "the dense solver takes at most BA_DENSE_MAX_CAMS cameras");
+  }
   if (hipHostMalloc(reinterpret_cast<void**>(&h->h_out), sizeof(StepOut), hipHostMallocDefault) !=
       hipSuccess) {
     h->h_out = nullptr;
@@ -778,6 +898,7 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
   }
   *h->h_done = 0;
   rc = build(h, cams, points, obs_cam_idx, obs_pt_idx, obs_uv);
+  if (rc == BA_OK && h->opt.solver == BA_SOLVER_DENSE_SCHUR) rc = plan_dense(h);
   if (rc != BA_OK) {
     ba_destroy(h);
     return rc;
@@ -889,7 +1010,7 @@ int ba_debug_run(ba_problem* h, int upto) {
   CHECK_RC(stage_linearize(h));
   h->linearized = 1;
   if (upto >= BA_STAGE_SCHUR) CHECK_RC(stage_schur(h));
-  if (upto >= BA_STAGE_PCG) CHECK_RC(stage_pcg(h));
+  if (upto >= BA_STAGE_PCG) CHECK_RC(stage_solve(h));
   if (upto >= BA_STAGE_UPDATE) CHECK_RC(stage_update(h));
   CHECK_RC(read_out(h));
   if (h->prof_on) CHECK_RC(prof_collect(h, h->h_out->pcg_iters));
@@ -913,6 +1034,7 @@ int64_t ba_debug_size(const ba_problem* h, int which) {
     case BA_DBG_GP: case BA_DBG_V: case BA_DBG_DP: case BA_DBG_PTS_TRIAL: return 3 * np * d8;
     case BA_DBG_PCG: return 2 * d8;
     case BA_DBG_TRIAL_COST: return d8;
+    case BA_DBG_S: return h->opt.solver == BA_SOLVER_DENSE_SCHUR ? 81 * nc * nc * d8 : BA_ERR_ARG;
     default: return BA_ERR_ARG;
   }
 }
@@ -971,6 +1093,22 @@ int ba_debug_get(ba_problem* h, int which, void* host_out, int64_t bytes) {
       double* o = static_cast<double*>(host_out);
       o[0] = st.iters;
       o[1] = st.rhs_norm > 0.0 ? st.res_norm / st.rhs_norm : 0.0;
+      return BA_OK;
+    }
+    case BA_DBG_S: {
+      // assembled again from the current state (the solve factors it in place)
+      Dev d = make_dev(h);
+      launch_ds_runs(d, h->stream);
+      launch_ds_fill(d, h->stream);
+      launch_ds_assemble(d, h->stream);
+      HIPC(hipGetLastError());
+      const int64_t n = 9 * nc, ld = h->ds_ld;
+      double* o = static_cast<double*>(host_out);
+      HIPC(hipMemcpy2DAsync(o, n * sizeof(double), h->ds_S, ld * sizeof(double), n * sizeof(double),
+                            (size_t)n, hipMemcpyDeviceToHost, h->stream));
+      HIPC(hipStreamSynchronize(h->stream));
+      for (int64_t i = 0; i < n; ++i)   // only the lower triangle is assembled
+        for (int64_t j = i + 1; j < n; ++j) o[i * n + j] = o[j * n + i];
       return BA_OK;
     }
     case BA_DBG_TRIAL_COST: {

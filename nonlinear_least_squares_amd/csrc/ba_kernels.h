@@ -119,6 +119,20 @@ struct Dev {
   double* cost_part;
   StepOut* out;
   int* flags;        // [0] non-finite seen, [1] not SPD
+  // dense reduced-camera solve (ba_dense.hip), when selected
+  int ds_n;          // 9 nc
+  int ds_ld;         // ds_n rounded up to the tile order: order and row stride of S
+  int ds_T;          // ds_ld / tile order; tile row ds_T holds the right-hand side
+  int ds_nruns;      // (point, camera) runs in point order
+  int ds_nblk;       // lower 9x9 blocks of S that are assembled (all diagonal ones included)
+  const int32_t* ds_run;      // point-order start of each run, ds_nruns + 1
+  const int2* ds_blk;         // per block: camera of the block row (x) and column (y), x >= y
+  const int32_t* ds_blk_ptr;  // run pairs of each block, ds_nblk + 1
+  const int2* ds_pair;        // (run of camera x, run of camera y) of one point
+  double* ds_F;      // per run: Ebar L, 9 x 3 row-major, L L^T = C~^-1 of its point
+  double* ds_S;      // (ds_ld + tile) x ds_ld row-major: S, factored in place below the
+                     // diagonal tiles; rhs row at ds_ld
+  double* ds_diag;   // ds_T tiles of tile^2: the factor's diagonal tiles (lower, row-major)
 };
 
 // Events that the next kernel dispatch records at its start and end (set by
@@ -156,6 +170,18 @@ void launch_cost(const Dev& d, const double* pts, const CamT* tab, const double*
                  hipStream_t s);
 void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* Jc, double* Jp,
                       double* w, hipStream_t s);
+
+// Dense reduced-camera solve: runs' F blocks, S and its rhs row, Cholesky by
+// tile columns (panel, trailing MFMA update), back-substitution into x.
+int ds_tile();
+void launch_ds_runs(const Dev& d, hipStream_t s);
+void launch_ds_fill(const Dev& d, hipStream_t s);
+void launch_ds_assemble(const Dev& d, hipStream_t s);
+void launch_ds_panel(const Dev& d, int k, hipStream_t s);
+int ds_update_tiles(const Dev& d, int k);
+void launch_ds_update(const Dev& d, int k, hipStream_t s);
+hipError_t ds_backsolve_limit(int ld);
+void launch_ds_backsolve(const Dev& d, hipStream_t s);
 
 // Structure build helpers.
 void launch_validate(const int32_t* cam_idx, const int32_t* pt_idx, const double* uv, int64_t n,

@@ -1,0 +1,173 @@
+"""GPU parity of the dense reduced-camera solver (libba, solver =
+BA_SOLVER_DENSE_SCHUR) against the CPU oracle's dense Schur solve.
+
+Bars (fp64):
+- S, assembled on the device, per 9x9 block within the larger of 1e-10 and
+  the first-order bound that two correct Cholesky inverses of the point
+  blocks may differ by (32 kappa(C~_i) eps per point, carried to each block
+  through sum_i |Ebar_i,a| |Ebar_i,b| |C~_i^-1|);
+- the device solve is backward stable in its own S:
+  |S dc - rhs| <= 4 n eps |S| |dc| (norm-wise, n = 9 n_cams);
+- the camera step against the oracle's: |dc - dc_ref| <= kappa(S) (|dS| / |S|
+  + 8 n eps) |dc_ref| + 1e-12 |dc_ref|, with dS the measured difference of
+  the two S and kappa its 2-norm condition number (two backward-stable
+  solves of systems that differ by dS);
+- LM traces (trial costs 1e-6, decisions) and the final cost (1e-6) as for
+  the PCG solver.
+"""
+import numpy as np
+import pytest
+import scipy.sparse as sp
+
+import oracle
+from synthetic import ba_scene
+from test_gpu_ba_parity import EPS, BLOCK_TOL, _edge_scene, blocks_close, traces_agree
+
+pytestmark = pytest.mark.gpu
+
+bamod = pytest.importorskip("nonlinear_least_squares_amd.ba")
+
+
+def make_pair(sc, **kw):
+    gpu = bamod.Problem.from_scene(sc, solver=bamod.BA_SOLVER_DENSE_SCHUR, **kw)
+    orc = oracle.Problem.from_scene(sc, solver=1, **kw)
+    return gpu, orc
+
+
+def lower_blocks(S, nc):
+    """(block row a >= block column b) 9x9 blocks of S, row-major block order."""
+    B = S.reshape(nc, 9, nc, 9).transpose(0, 2, 1, 3)
+    a, b = np.tril_indices(nc)
+    return a, b, B[a, b].reshape(len(a), 81)
+
+
+def s_block_tolerances(orc, sc, a, b, ref_blocks):
+    """Per lower block: relative tolerance from the point-inverse bound."""
+    Cinv = orc.get("Cinv")
+    kappa = np.linalg.cond(Cinv)
+    c_i = np.linalg.norm(Cinv.reshape(len(Cinv), -1), axis=1) * 32 * kappa * EPS
+    Jc, Jp, w = orc.get("Jc"), orc.get("Jp"), orc.get("w")
+    E = w[:, None, None] * np.einsum("kra,krb->kab", Jc, Jp)
+    En = np.linalg.norm(E.reshape(len(E), -1), axis=1)
+    pt, cam = sc["obs_pt"], sc["obs_cam"]
+    nc, npt = len(sc["cams"]), len(sc["points"])
+    A = sp.csr_matrix((En * np.sqrt(c_i[pt]), (pt, cam)), shape=(npt, nc))
+    bound = np.asarray((A.T @ A).todense())
+    absb = bound[a, b]
+    norm = np.linalg.norm(ref_blocks, axis=1)
+    return np.maximum(BLOCK_TOL, absb / np.maximum(norm, 1e-300) + BLOCK_TOL)
+
+
+@pytest.fixture(scope="module", params=["tiny", "small", "medium"])
+def scene(request):
+    return ba_scene(request.param)
+
+
+@pytest.mark.parametrize("lam", [1e-3, 1e-6])
+def test_explicit_S_parity(scene, lam):
+    gpu, orc = make_pair(scene)
+    gpu.set_state(lam)
+    orc.lam = lam
+    gpu.debug_run(bamod.BA_STAGE_SCHUR)
+    orc.linearize()
+    orc.damp()
+    orc.schur()
+    nc = len(scene["cams"])
+    S, S_ref = gpu.debug_get("S"), orc.explicit_S()
+    assert np.array_equal(S, S.T)
+    a, b, got = lower_blocks(S, nc)
+    _, _, ref = lower_blocks(S_ref, nc)
+    blocks_close("S", got, ref, s_block_tolerances(orc, scene, a, b, ref))
+
+
+@pytest.mark.parametrize("lam", [1e-3, 1e-6])
+def test_dense_solve_parity(scene, lam):
+    gpu, orc = make_pair(scene)
+    gpu.set_state(lam)
+    orc.lam = lam
+    gpu.debug_run(bamod.BA_STAGE_PCG)
+    S = gpu.debug_get("S")
+    dc = gpu.debug_get("dc").ravel()
+    g_it, g_rel = gpu.debug_get("pcg")
+    assert g_it == 0 and g_rel == 0.0
+    orc.linearize()
+    orc.damp()
+    orc.schur()
+    S_ref = orc.explicit_S()
+    orc.dense_schur_solve()
+    dc_ref = orc.get("dc").ravel()
+    rhs = orc.get("rhs").ravel()
+    n = len(rhs)
+    # backward stability of the device factorisation and solves, in its own S
+    s2 = np.linalg.norm(S, 2)
+    assert np.linalg.norm(S @ dc - rhs) <= 4 * n * EPS * s2 * np.linalg.norm(dc)
+    # forward error against the oracle's solve
+    kappa = np.linalg.cond(S_ref)
+    dS = np.linalg.norm(S - S_ref, 2) / np.linalg.norm(S_ref, 2)
+    bound = (kappa * (dS + 8 * n * EPS) + 1e-12) * np.linalg.norm(dc_ref)
+    assert np.linalg.norm(dc - dc_ref) <= bound, (np.linalg.norm(dc - dc_ref) / np.linalg.norm(dc_ref),
+                                                   kappa, dS)
+
+
+@pytest.mark.parametrize("config", ["tiny", "small"])
+def test_dense_lm_parity(config):
+    sc = ba_scene(config)
+    gpu, orc = make_pair(sc)
+    n = sc["n_iters"]
+    g_tr = [gpu.lm_step() for _ in range(n)]
+    o_tr = orc.solve(n)
+    assert traces_agree(g_tr, o_tr)
+    assert all(t["pcg_iters"] == 0 for t in g_tr)
+    final, ref = gpu.get_state()["cost"], orc.cost
+    assert abs(final - ref) <= 1e-6 * ref, (final, ref)
+
+
+def test_dense_medium_three_lm_steps():
+    sc = ba_scene("medium")
+    gpu, orc = make_pair(sc)
+    g_tr = [gpu.lm_step() for _ in range(3)]
+    o_tr = orc.solve(3)
+    assert traces_agree(g_tr, o_tr)
+
+
+def test_dense_agrees_with_tight_pcg_on_gpu():
+    sc = ba_scene("small")
+    d = bamod.Problem.from_scene(sc, solver=bamod.BA_SOLVER_DENSE_SCHUR)
+    p = bamod.Problem.from_scene(sc, pcg_rel_tol=1e-13, pcg_max_iters=2000)
+    d.debug_run(bamod.BA_STAGE_PCG)
+    p.debug_run(bamod.BA_STAGE_PCG)
+    a, b = d.debug_get("dc"), p.debug_get("dc")
+    assert np.linalg.norm(a - b) <= 1e-8 * np.linalg.norm(b)
+
+
+def test_dense_edge_cases_parity():
+    """Repeated (camera, point) runs, a 700-observation point, an unobserved
+    point and an unobserved camera (its diagonal block of S is B~ alone)."""
+    sc = _edge_scene()
+    gpu, orc = make_pair(sc)
+    gpu.debug_run(bamod.BA_STAGE_SCHUR)
+    orc.linearize()
+    orc.damp()
+    orc.schur()
+    nc = len(sc["cams"])
+    a, b, got = lower_blocks(gpu.debug_get("S"), nc)
+    _, _, ref = lower_blocks(orc.explicit_S(), nc)
+    blocks_close("S", got, ref, s_block_tolerances(orc, sc, a, b, ref))
+    gpu2, orc2 = make_pair(sc)
+    g_tr = [gpu2.lm_step() for _ in range(6)]
+    o_tr = orc2.solve(6)
+    assert traces_agree(g_tr, o_tr)
+    assert abs(gpu2.get_state()["cost"] - orc2.cost) <= 1e-6 * orc2.cost
+    cams, pts = gpu2.get_params()
+    np.testing.assert_array_equal(pts[11], sc["points"][11])
+
+
+def test_dense_bitwise_determinism():
+    sc = ba_scene("small")
+    a = bamod.Problem.from_scene(sc, solver=bamod.BA_SOLVER_DENSE_SCHUR)
+    b = bamod.Problem.from_scene(sc, solver=bamod.BA_SOLVER_DENSE_SCHUR)
+    a.solve(3)
+    b.solve(3)
+    ca, pa = a.get_params()
+    cb, pb = b.get_params()
+    assert np.array_equal(ca, cb) and np.array_equal(pa, pb)

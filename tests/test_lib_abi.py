@@ -58,6 +58,15 @@ def test_host_only_entry_points():
     pts = (C.c_double * 3)()
     rc = L.ba_create(cams, 1, pts, 1, None, None, None, 0, C.byref(bad), C.byref(h))
     assert rc == bamod.BA_ERR_ARG and not h.value
+    # solver choice: PCG by default; the dense solver is capped by the size of S
+    assert o.solver == bamod.BA_SOLVER_PCG
+    rc = L.ba_create(cams, 1, pts, 1, None, None, None, 0, C.byref(bamod.options(solver=5)), C.byref(h))
+    assert rc == bamod.BA_ERR_ARG and not h.value
+    many = (C.c_double * (9 * (bamod.BA_DENSE_MAX_CAMS + 1)))()
+    rc = L.ba_create(many, bamod.BA_DENSE_MAX_CAMS + 1, pts, 1, None, None, None, 0,
+                     C.byref(bamod.options(solver=bamod.BA_SOLVER_DENSE_SCHUR)), C.byref(h))
+    assert rc == bamod.BA_ERR_ARG and not h.value
+    assert [L.ba_kernel_name(k) for k in range(len(bamod.KERNELS))] == [n.encode() for n in bamod.KERNELS]
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
