@@ -72,7 +72,7 @@ enum { BA_MEM_HOST = 0, BA_MEM_DEVICE = 1 };
  *                          BA_DENSE_MAX_CAMS cameras (S takes (9 n_cams)^2
  *                          doubles of device memory). */
 enum { BA_SOLVER_PCG = 0, BA_SOLVER_DENSE_SCHUR = 1 };
-#define BA_DENSE_MAX_CAMS 2048
+#define BA_DENSE_MAX_CAMS 1536
 enum { BA_LOSS_SQUARED = 0, BA_LOSS_HUBER = 1 };
 
 typedef struct {

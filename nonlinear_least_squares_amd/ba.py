@@ -18,7 +18,7 @@ BA_MEM_HOST, BA_MEM_DEVICE = 0, 1
 BA_LOSS_SQUARED, BA_LOSS_HUBER = 0, 1
 BA_STAGE_LINEARIZE, BA_STAGE_SCHUR, BA_STAGE_PCG, BA_STAGE_UPDATE = 1, 2, 3, 4
 BA_SOLVER_PCG, BA_SOLVER_DENSE_SCHUR = 0, 1
-BA_DENSE_MAX_CAMS = 2048
+BA_DENSE_MAX_CAMS = 1536
 
 DBG = dict(perm_pt=0, perm_cam=1, pt_ptr=2, cam_ptr=3, r=4, Jc=5, Jp=6, w=7, B=8, gc=9, C=10,
            gp=11, Bd=12, Cinv=13, v=14, rhs=15, M=16, dc=17, dp=18, cams_trial=19,

@@ -105,7 +105,7 @@ struct ba_problem {
   int ds_ld = 0, ds_T = 0, ds_nruns = 0, ds_nblk = 0;
   int32_t *ds_run = nullptr, *ds_blk_ptr = nullptr;
   int2 *ds_blk = nullptr, *ds_pair = nullptr;
-  double *ds_F = nullptr, *ds_S = nullptr, *ds_diag = nullptr;
+  double *ds_F = nullptr, *ds_S = nullptr, *ds_diag = nullptr, *ds_diagT = nullptr, *ds_dinv = nullptr;
   // work arrays
   double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
          *gc = nullptr, *lin_part = nullptr;
@@ -216,6 +216,8 @@ Dev make_dev(const ba_problem* h) {
   d.ds_F = h->ds_F;
   d.ds_S = h->ds_S;
   d.ds_diag = h->ds_diag;
+  d.ds_diagT = h->ds_diagT;
+  d.ds_dinv = h->ds_dinv;
   return d;
 }
 
@@ -355,6 +357,7 @@ int stage_dense(ba_problem* h) {
   TIMED(BA_K_DS_RUNS, -1, launch_ds_runs(d, s));
   TIMED(BA_K_DS_FILL, -1, launch_ds_fill(d, s));
   TIMED(BA_K_DS_ASSEMBLE, -1, launch_ds_assemble(d, s));
+  TIMED(BA_K_DS_PANEL, -1, launch_ds_diag0(d, s));
   for (int k = 0; k < h->ds_T; ++k) {
     TIMED(BA_K_DS_PANEL, -1, launch_ds_panel(d, k, s));
     TIMED(BA_K_DS_UPDATE, -1, launch_ds_update(d, k, s));
@@ -770,6 +773,8 @@ int plan_dense(ba_problem* h) {
   A.add(h->ds_F, 27 * nruns);
   A.add(h->ds_S, ((int64_t)h->ds_ld + kt) * h->ds_ld);
   A.add(h->ds_diag, (int64_t)h->ds_T * kt * kt);
+  A.add(h->ds_diagT, (int64_t)h->ds_T * kt * kt);
+  A.add(h->ds_dinv, (int64_t)h->ds_ld);
   CHECK_RC(A.commit());
   HIPC(hipMemcpyAsync(h->ds_run, run.data(), sizeof(int32_t) * run.size(), hipMemcpyHostToDevice, s));
   HIPC(hipMemcpyAsync(h->ds_blk, blk.data(), sizeof(int2) * blk.size(), hipMemcpyHostToDevice, s));

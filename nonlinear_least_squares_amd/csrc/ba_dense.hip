@@ -8,7 +8,8 @@
 // F_r = Ebar_r L_i, with L_i L_i^T = C~_i^-1, turns every point's
 // contribution into outer products: S_{j2 j1} -= sum_i F_{i,j2} F_{i,j1}^T.
 // Each lower 9x9 block of S is summed by one workgroup over a fixed list of
-// run pairs (no atomics, so the result is the same bits on every run).
+// run pairs, with fp64 MFMA (no atomics, so the result is the same bits on
+// every run).
 //
 // Storage: S is row-major with leading dimension N_p = 9 n_c rounded up to a
 // multiple of 32 (padding: identity on the diagonal, zeros elsewhere).  Row
@@ -19,13 +20,14 @@
 //
 // Factorisation, right-looking by 32 x 32 tiles, two launches per tile
 // column k:
-//   panel   one wavefront per tile row i >= k (and the rhs row): the diagonal
-//           tile is factored in registers (lane r holds row r; column values
-//           move by readlane), redundantly in every wavefront, and the row's
-//           tile is solved against it, L_ik = A_ik L_kk^-T;
+//   panel   one wavefront per tile row i > k (and the rhs row) solves its
+//           tile against the factored diagonal tile, L_ik = A_ik L_kk^-T;
 //   update  one wavefront per trailing tile (i, j), k < j <= i:
 //           A_ij -= L_ik L_jk^T with fp64 MFMA (16x16x4), the one dense
-//           contraction of the bundle-adjustment pages' methods.
+//           contraction of the bundle-adjustment pages' methods; the
+//           wavefront of tile (k + 1, k + 1) then factors it (lane r holds
+//           row r, column values move by readlane), so the next panel starts
+//           from a factored diagonal tile.
 // The factor's diagonal tiles are kept apart (ds_diag); the back-substitution
 // L^T dc = y runs in one workgroup, tile by tile.
 #include <hip/hip_ext.h>
@@ -39,9 +41,8 @@ namespace {
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr int kT = 32;            // tile order of the factorisation
-constexpr int kAsmThreads = 128;  // threads of an assembly block (81 used)
-constexpr int kAsmBatch = 16;     // run pairs staged in LDS at a time
 constexpr int kSolveThreads = 1024;
+static_assert(kT * kT == kSolveThreads, "the back-substitution loads one diagonal tile per thread");
 
 __device__ __forceinline__ double lane_bcast(double x, int l) {
   const int lo = __builtin_amdgcn_readlane(__double2loint(x), l);
@@ -109,58 +110,84 @@ __global__ void k_ds_fill(Dev d) {
 }
 
 // One lower 9x9 block (j2, j1) of S per workgroup: B~ on the diagonal minus
-// the sum over the block's run pairs of F_a F_b^T, in list order.
-__global__ __launch_bounds__(kAsmThreads) void k_ds_assemble(Dev d) {
-  __shared__ double s_f[kAsmBatch][54];
+// sum over the block's run pairs (a, b) of F_a F_b^T.  That sum is a product
+// of a 9 x 3p and a 3p x 9 matrix, done with fp64 MFMA (16x16x4): one pair per
+// instruction, the 9 x 3 blocks padded to 16 x 4 (lane l supplies row l % 16,
+// column l / 16 of F_a and of F_b).  The block's pairs are split into
+// kAsmWaves contiguous shares, one per wavefront, 16 pairs in flight; the
+// wavefronts' sums are added in wavefront order, so the result does not
+// depend on timing.
+constexpr int kAsmWaves = 4;
+__global__ __launch_bounds__(64 * kAsmWaves) void k_ds_assemble(Dev d) {
+  __shared__ double s_acc[kAsmWaves][4][64];
   const int blk = blockIdx.x;
   const int2 jj = d.ds_blk[blk];   // x = j2 (row block), y = j1 (column block), j2 >= j1
   const int p0 = d.ds_blk_ptr[blk], p1 = d.ds_blk_ptr[blk + 1];
-  const int t = threadIdx.x;
-  const int al = t / 9, be = t - 9 * (t / 9);
-  double acc = 0.0;
-  for (int pb = p0; pb < p1; pb += kAsmBatch) {
-    const int np = min(kAsmBatch, p1 - pb);
-    for (int e = t; e < np * 54; e += kAsmThreads) {
-      const int p = e / 54, k = e - 54 * p;
-      const int2 pr = d.ds_pair[pb + p];
-      s_f[p][k] = k < 27 ? d.ds_F[27 * (int64_t)pr.x + k] : d.ds_F[27 * (int64_t)pr.y + (k - 27)];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = lane & 15, kk = lane >> 4;
+  const bool act = m < 9 && kk < 3;
+  const int off = act ? 3 * m + kk : 0;
+  const int q0 = p0 + (int)(((int64_t)(p1 - p0) * w) / kAsmWaves);
+  const int q1 = p0 + (int)(((int64_t)(p1 - p0) * (w + 1)) / kAsmWaves);
+  const double* F = d.ds_F;
+  v4d acc = {0.0, 0.0, 0.0, 0.0};
+  for (int pb = q0; pb < q1; pb += 16) {
+    const int nb = min(16, q1 - pb);
+    const int2 pr = d.ds_pair[pb + min(lane, nb - 1)];
+    double av[16], bv[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int ra = __builtin_amdgcn_readlane(pr.x, q), rb = __builtin_amdgcn_readlane(pr.y, q);
+      av[q] = F[27 * (int64_t)ra + off];
+      bv[q] = F[27 * (int64_t)rb + off];
     }
-    __syncthreads();
-    if (t < 81) {
-      for (int p = 0; p < np; ++p) {
-        const double* fa = s_f[p] + 3 * al;
-        const double* fb = s_f[p] + 27 + 3 * be;
-        acc += fa[0] * fb[0] + fa[1] * fb[1] + fa[2] * fb[2];
-      }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const bool on = act && q < nb;
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(on ? av[q] : 0.0, on ? bv[q] : 0.0, acc, 0, 0, 0);
     }
-    __syncthreads();
   }
-  if (t < 81) {
-    double v = -acc;
-    if (jj.x == jj.y) v += d.Bd[45 * (int64_t)jj.x + (al <= be ? sym_idx(9, al, be) : sym_idx(9, be, al))];
-    d.ds_S[(9 * (int64_t)jj.x + al) * d.ds_ld + 9 * (int64_t)jj.y + be] = v;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) s_acc[w][v][lane] = acc[v];
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    double tot = 0.0;
+#pragma unroll
+    for (int u = 0; u < kAsmWaves; ++u) tot += s_acc[u][v][lane];
+    const int al = 4 * v + kk, be = m;   // element v of lane l: row 4 v + l / 16, column l % 16
+    if (al < 9 && be < 9) {
+      double val = -tot;
+      if (jj.x == jj.y) val += d.Bd[45 * (int64_t)jj.x + (al <= be ? sym_idx(9, al, be) : sym_idx(9, be, al))];
+      d.ds_S[(9 * (int64_t)jj.x + al) * d.ds_ld + 9 * (int64_t)jj.y + be] = val;
+    }
   }
 }
 
-// Tile column k: wavefront b factors the diagonal tile and then handles tile
-// row k + b (the diagonal tile itself for b = 0; the rhs tile row for
-// k + b = T).  Every wavefront reads the diagonal tile, so its factor goes to
-// a separate array (ds_diag) rather than back in place.  Lanes 32..63 repeat
-// lanes 0..31 and store nothing.
-__global__ __launch_bounds__(64) void k_ds_panel(Dev d, int k) {
-  const int i = k + blockIdx.x;
+// 1 / sqrt(x) for x > 0: the hardware estimate and two Newton steps
+// y <- y (3 - x y^2) / 2, each doubling the correct bits of an estimate good
+// to about 2^-23.
+__device__ __forceinline__ double rsqrt_newton(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * fma(-0.5 * x, y * y, 1.5);
+  return y * fma(-0.5 * x, y * y, 1.5);
+}
+
+// Factor one 32 x 32 diagonal tile held as rows src[r * stride + c] (lane r
+// holds row r) into ds_diag (L, row-major, zeros above the diagonal),
+// ds_diagT (its transpose) and ds_dinv (1 / L(c, c)).  Column c's values move
+// to every lane by readlane.  One wavefront; lanes 32..63 repeat lanes 0..31
+// and store nothing.  A pivot that is not positive and finite sets the not-SPD
+// flag (and is taken as 1).
+__device__ __forceinline__ void factor_diag_tile(const Dev& d, int kt, const double* src,
+                                                 int64_t stride) {
   const int r = threadIdx.x & (kT - 1);
-  const int64_t ld = d.ds_ld;
-  double* S = d.ds_S;
-  double a[kT], b[kT];
-  const double* arow = S + (int64_t)(kT * k + r) * ld + kT * k;
-  const double* brow = S + (int64_t)(kT * i + r) * ld + kT * k;
+  double a[kT];
 #pragma unroll
-  for (int c = 0; c < kT; ++c) {
-    a[c] = arow[c];
-    b[c] = brow[c];
-  }
+  for (int c = 0; c < kT; ++c) a[c] = src[r * stride + c];
   bool bad = false;
+  double myinv = 0.0;
 #pragma unroll
   for (int c = 0; c < kT; ++c) {
     double piv = lane_bcast(a[c], c);
@@ -168,31 +195,65 @@ __global__ __launch_bounds__(64) void k_ds_panel(Dev d, int k) {
       bad = true;
       piv = 1.0;
     }
-    const double lc = sqrt(piv), inv = 1.0 / lc;
-    a[c] = r == c ? lc : a[c] * inv;   // L(r, c) for r >= c
-    b[c] *= inv;                        // x_c of this row
+    const double inv = rsqrt_newton(piv);
+    a[c] = r == c ? piv * inv : a[c] * inv;   // L(r, c) for r >= c
+    if (r == c) myinv = inv;
 #pragma unroll
-    for (int j = c + 1; j < kT; ++j) {
-      const double ljc = lane_bcast(a[c], j);   // L(j, c)
-      a[j] -= a[c] * ljc;
-      b[j] -= b[c] * ljc;
-    }
+    for (int j = c + 1; j < kT; ++j) a[j] -= a[c] * lane_bcast(a[c], j);   // L(j, c)
   }
-  if (bad && blockIdx.x == 0 && threadIdx.x == 0) d.flags[1] = 1;
+  if (bad && threadIdx.x == 0) d.flags[1] = 1;
   if (threadIdx.x >= kT) return;
-  if (i == k) {
-    double* out = d.ds_diag + (int64_t)k * kT * kT + kT * r;
+  double* L = d.ds_diag + (int64_t)kt * kT * kT;
+  double* LT = d.ds_diagT + (int64_t)kt * kT * kT;
 #pragma unroll
-    for (int c = 0; c < kT; ++c) out[c] = c <= r ? a[c] : 0.0;
-  } else {
-    double* out = S + (int64_t)(kT * i + r) * ld + kT * k;
-#pragma unroll
-    for (int c = 0; c < kT; ++c) out[c] = b[c];
+  for (int c = 0; c < kT; ++c) {
+    const double v = c <= r ? a[c] : 0.0;
+    L[kT * r + c] = v;
+    LT[kT * c + r] = v;
   }
+  d.ds_dinv[kT * kt + r] = myinv;
+}
+
+// The first diagonal tile (the update kernel factors each later one).
+__global__ __launch_bounds__(64) void k_ds_diag0(Dev d) {
+  factor_diag_tile(d, 0, d.ds_S, d.ds_ld);
+}
+
+// Tile column k, its diagonal tile already factored: one wavefront per tile
+// row i = k + 1 .. T (T: the rhs tile row) solves L_ik L_kk^T = A_ik in place,
+// lane r taking row r.  The factor's columns and pivot reciprocals are staged
+// in LDS and read at wavefront-uniform addresses (broadcasts).
+__global__ __launch_bounds__(64) void k_ds_panel(Dev d, int k) {
+  __shared__ double s_l[kT * kT + kT];
+  const int i = k + 1 + blockIdx.x;
+  const int r = threadIdx.x & (kT - 1);
+  const int64_t ld = d.ds_ld;
+  double* row = d.ds_S + (int64_t)(kT * i + r) * ld + kT * k;
+  const double* LT = d.ds_diagT + (int64_t)k * kT * kT;
+  double b[kT];
+#pragma unroll
+  for (int c = 0; c < kT; ++c) b[c] = row[c];
+  double lt[kT * kT / 64];
+#pragma unroll
+  for (int u = 0; u < kT * kT / 64; ++u) lt[u] = LT[threadIdx.x + 64 * u];
+#pragma unroll
+  for (int u = 0; u < kT * kT / 64; ++u) s_l[threadIdx.x + 64 * u] = lt[u];
+  if (threadIdx.x < kT) s_l[kT * kT + threadIdx.x] = d.ds_dinv[kT * k + threadIdx.x];
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kT; ++c) {
+    b[c] *= s_l[kT * kT + c];
+#pragma unroll
+    for (int j = c + 1; j < kT; ++j) b[j] -= b[c] * s_l[kT * c + j];   // L(j, c)
+  }
+  if (threadIdx.x >= kT) return;
+#pragma unroll
+  for (int c = 0; c < kT; ++c) row[c] = b[c];
 }
 
 // Trailing update after tile column k: one wavefront per tile (i, j) with
-// k < j <= i < T, then the rhs tile row (T, j).  A_ij -= L_ik L_jk^T as 2 x 2
+// k < j <= i < T, then the rhs tile row (T, j).  The wavefront of tile
+// (k + 1, k + 1) then factors that tile for the next panel.  A_ij -= L_ik L_jk^T as 2 x 2
 // MFMA tiles of 16 x 16 over K = 32 in steps of 4.  Operand layout of
 // v_mfma_f64_16x16x4_f64 (lane l): A(m, kk) with m = l % 16, kk = l / 16;
 // B(kk, n) with n = l % 16; accumulator element v (0..3) is row 4 v + l / 16
@@ -248,43 +309,75 @@ __global__ __launch_bounds__(64) void k_ds_update(Dev d, int k) {
     for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
       for (int v = 0; v < 4; ++v) C[(int64_t)(16 * mh + 4 * v + lk) * ld + 16 * nh + lr] = acc[mh][nh][v];
+  if (id == 0) {
+    // tile (k + 1, k + 1) is final now: factor it for the next panel, its
+    // rows passed through LDS
+    __shared__ double s_t[kT * kT];
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+      for (int nh = 0; nh < 2; ++nh)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_t[(16 * mh + 4 * v + lk) * kT + 16 * nh + lr] = acc[mh][nh][v];
+    __syncthreads();
+    factor_diag_tile(d, k + 1, s_t, kT);
+  }
 }
 
-// L^T dc = y by tile columns from the last: the contribution of the solved
-// unknowns below the tile (a 32-column GEMV over those rows, 32 row groups of
-// 32 threads, summed in group order), then the 32 x 32 triangular solve by
-// one wavefront holding the tile's columns.  Writes dc and the solver state.
+// L^T dc = y by tile columns from the last, right-looking: v starts as y (in
+// LDS); for each tile column kt, one wavefront solves the 32 x 32 triangle
+// L_kk^T x_kt = v_kt (lane c holds column c of L_kk; the pivots' reciprocals
+// are formed up front, so each of the 32 dependent steps is a broadcast and a
+// multiply-add), then all threads take x_kt out of the unknowns above it,
+// v_j -= sum_e L(32 kt + e, j) x_e for j < 32 kt, reading tile row kt of L
+// row by row (coalesced; 32 loads in flight per column).  The next diagonal
+// tile is loaded one step ahead.  Writes dc and the solver state.
 __global__ __launch_bounds__(kSolveThreads) void k_ds_backsolve(Dev d) {
-  extern __shared__ double s_x[];               // N_p unknowns
-  __shared__ double s_part[kT][kT + 1];
+  extern __shared__ double s_v[];               // N_p: y, then x where solved
+  __shared__ double s_diag[kT * kT];
   const int64_t ld = d.ds_ld;
   const double* S = d.ds_S;
   const double* y = S + ld * ld;                // the rhs row after the factorisation
-  const int t = threadIdx.x, c = t & (kT - 1), g = t / kT;
+  const int t = threadIdx.x, c = t & (kT - 1);
+  for (int64_t j = t; j < ld; j += kSolveThreads) s_v[j] = y[j];
+  s_diag[t] = d.ds_diag[(int64_t)(d.ds_T - 1) * kT * kT + t];   // kT * kT == kSolveThreads
+  __syncthreads();
   for (int kt = d.ds_T - 1; kt >= 0; --kt) {
-    double acc = 0.0;
-    for (int64_t row = kT * (int64_t)(kt + 1) + g; row < ld; row += kSolveThreads / kT)
-      acc += S[row * ld + kT * kt + c] * s_x[row];
-    s_part[g][c] = acc;
-    __syncthreads();
+    const double dg_next = d.ds_diag[(int64_t)max(kt - 1, 0) * kT * kT + t];
     if (t < 64) {
       double col[kT];
 #pragma unroll
-      for (int e = 0; e < kT; ++e) col[e] = d.ds_diag[(int64_t)kt * kT * kT + kT * e + c];   // L(e, c)
-      double v = y[kT * kt + c];
-      for (int gg = 0; gg < kSolveThreads / kT; ++gg) v -= s_part[gg][c];
+      for (int e = 0; e < kT; ++e) col[e] = s_diag[kT * e + c];   // L(e, c)
+      double dsel = col[0];
+#pragma unroll
+      for (int e = 1; e < kT; ++e)
+        if (c == e) dsel = col[e];
+      const double inv = 1.0 / dsel;
+      double v = s_v[kT * kt + c];
       double xm = 0.0;
 #pragma unroll
       for (int e = kT - 1; e >= 0; --e) {
-        const double xe = lane_bcast(v, e) / lane_bcast(col[e], e);
+        const double xe = lane_bcast(v * inv, e);
         if (c == e) xm = xe;
         if (c < e) v -= col[e] * xe;
       }
-      if (t < kT) s_x[kT * kt + c] = xm;
+      if (t < kT) s_v[kT * kt + c] = xm;
+    }
+    __syncthreads();
+    s_diag[t] = dg_next;
+    const double* Lrow = S + (int64_t)(kT * kt) * ld;
+    for (int64_t j = t; j < kT * (int64_t)kt; j += kSolveThreads) {
+      double lv[kT];
+#pragma unroll
+      for (int e = 0; e < kT; ++e) lv[e] = Lrow[e * ld + j];
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < kT; ++e) acc += lv[e] * s_v[kT * kt + e];
+      s_v[j] -= acc;
     }
     __syncthreads();
   }
-  for (int e = t; e < d.ds_n; e += kSolveThreads) d.x[e] = s_x[e];
+  for (int e = t; e < d.ds_n; e += kSolveThreads) d.x[e] = s_v[e];
   if (t == 0) {
     d.pcg->done = 1;
     d.pcg->iters = 0;
@@ -318,10 +411,11 @@ void launch_ds_fill(const Dev& d, hipStream_t s) {
   launch(k_ds_fill, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, d);
 }
 void launch_ds_assemble(const Dev& d, hipStream_t s) {
-  if (d.ds_nblk > 0) launch(k_ds_assemble, dim3(d.ds_nblk), dim3(kAsmThreads), s, 0u, d);
+  if (d.ds_nblk > 0) launch(k_ds_assemble, dim3(d.ds_nblk), dim3(64 * kAsmWaves), s, 0u, d);
 }
+void launch_ds_diag0(const Dev& d, hipStream_t s) { launch(k_ds_diag0, dim3(1), dim3(64), s, 0u, d); }
 void launch_ds_panel(const Dev& d, int k, hipStream_t s) {
-  launch(k_ds_panel, dim3(d.ds_T - k + 1), dim3(64), s, 0u, d, k);
+  launch(k_ds_panel, dim3(d.ds_T - k), dim3(64), s, 0u, d, k);
 }
 int ds_update_tiles(const Dev& d, int k) {
   const int m = d.ds_T - k - 1;

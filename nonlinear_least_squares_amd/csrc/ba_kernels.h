@@ -133,6 +133,8 @@ struct Dev {
   double* ds_S;      // (ds_ld + tile) x ds_ld row-major: S, factored in place below the
                      // diagonal tiles; rhs row at ds_ld
   double* ds_diag;   // ds_T tiles of tile^2: the factor's diagonal tiles (lower, row-major)
+  double* ds_diagT;  // the same tiles transposed
+  double* ds_dinv;   // ds_ld: reciprocals of the factor's diagonal
 };
 
 // Events that the next kernel dispatch records at its start and end (set by
@@ -172,11 +174,14 @@ void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* J
                       double* w, hipStream_t s);
 
 // Dense reduced-camera solve: runs' F blocks, S and its rhs row, Cholesky by
-// tile columns (panel, trailing MFMA update), back-substitution into x.
+// tile columns (first diagonal tile; then per column the panel solves and the
+// trailing MFMA update, which factors the next diagonal tile),
+// back-substitution into x.
 int ds_tile();
 void launch_ds_runs(const Dev& d, hipStream_t s);
 void launch_ds_fill(const Dev& d, hipStream_t s);
 void launch_ds_assemble(const Dev& d, hipStream_t s);
+void launch_ds_diag0(const Dev& d, hipStream_t s);
 void launch_ds_panel(const Dev& d, int k, hipStream_t s);
 int ds_update_tiles(const Dev& d, int k);
 void launch_ds_update(const Dev& d, int k, hipStream_t s);
