@@ -17,6 +17,12 @@ every sixteenth launch.
 depths eliminated, Cholesky of the 84 x 84 reduced pose system, depth
 back-substitution, retraction) of the 16-keyframe scene with 48 x 64
 inverse-depth maps and 64 edges (196,608 residuals).
+
+``--workload schur-dense`` measures libba with the dense reduced-camera
+solver on the medium scene (250 walk cameras, 60,000 points, about 300,000
+observations): a step is one LM iteration whose camera step comes from the
+explicit S (order 2,250) and its tile Cholesky; the roofline refers to the
+fp64 MFMA trailing update when that kernel dominates.
 """
 import argparse
 import hashlib
@@ -221,6 +227,103 @@ def main_dense(args):
     print(json.dumps(out), flush=True)
 
 
+SCHUR_DENSE_METRIC = ("LM iterations/s (fp64, 1 GPU, dense reduced-camera Cholesky); "
+                      "% of fp64 MFMA roofline")
+FP64_MFMA_PEAK_TFLOPS = 78.6
+DS_TILE = 32
+
+
+def schur_dense_update_flops(n_cams):
+    """Algorithmic fp64 flops of one trailing-update launch of the dense
+    solver, averaged over the launches of one factorisation: S (9 n_cams
+    rounded up to the 32-tile) by tile columns; after column k the m = T-k-1
+    trailing tile columns take m (m - 1) / 2 full 32 x 32 x 32 products below
+    the diagonal and m half products on it (the Cholesky update's n^3/3)."""
+    T = -(-9 * n_cams // DS_TILE)
+    total, launches = 0, 0
+    for k in range(T):
+        m = T - k - 1
+        if m == 0:
+            continue
+        total += 2 * DS_TILE ** 3 * (m * (m - 1) // 2) + DS_TILE ** 3 * m
+        launches += 1
+    return total // max(launches, 1)
+
+
+def schur_dense_cpu_baseline(sc, n_iters=8):
+    """The oracle as it stands (plain C, one thread) with its dense Schur
+    solver: the first LM iterations of the same scene from the same start."""
+    import oracle
+    P = oracle.Problem.from_scene(sc, solver=1)
+    t0 = time.perf_counter()
+    P.solve(n_iters)
+    dt = time.perf_counter() - t0
+    return {"value": n_iters / dt, "unit": "LM iterations/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_iters} LM iterations of the same scene "
+                      f"({len(sc['obs_cam'])} observations, explicit S and dense Cholesky), "
+                      f"single-threaded C oracle, {dt:.1f} s"}
+
+
+def main_schur_dense(args):
+    import torch
+    from nonlinear_least_squares_amd import ba
+    from synthetic import ba_scene, scene_summary
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    config = args.config or "medium"
+    sc = ba_scene(config)
+    n_obs, n_pts, n_cams = len(sc["obs_cam"]), len(sc["points"]), len(sc["cams"])
+    print(f"# {scene_summary(sc)}", file=sys.stderr, flush=True)
+    dense = dict(solver=ba.BA_SOLVER_DENSE_SCHUR)
+    warm = ba.Problem.from_scene(sc, **dense)
+    warm.profile()
+    warm.solve(max(args.warmup, 1))
+    prof = warm.profile_get()
+    warm.close()
+    dominant = max(prof, key=lambda k: prof[k][1])
+    print(f"# warm-up kernel totals (launches, ms): {prof}", file=sys.stderr, flush=True)
+
+    P = ba.Problem.from_scene(sc, **dense)
+    P.profile([dominant], every=PROFILE_EVERY)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    summ = P.solve(args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    launches, kms = P.profile_get()[dominant]
+    value = args.steps / dt
+    roof = None
+    if launches and dominant == "ds_update":
+        avg_s = kms / launches / 1e3
+        fl = schur_dense_update_flops(n_cams)
+        ach = fl / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": FP64_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP64_MFMA_PEAK_TFLOPS, 5), "traffic": None,
+                "kernel": dominant, "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches,
+                "algorithmic_flops_per_launch": fl}
+    elif launches:
+        roof = {"bound": None, "achieved": None, "peak": None, "unit": None, "frac": None,
+                "traffic": None, "kernel": dominant,
+                "avg_launch_us": round(kms / launches * 1e3, 2), "launches": launches}
+    out = {
+        "metric": SCHUR_DENSE_METRIC, "value": round(value, 3), "unit": "LM iterations/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * dt / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{config} BA, dense reduced-camera solve: {n_cams} cameras "
+                               f"(S of order {9 * n_cams}), {n_pts} points, {n_obs} observations, "
+                               f"{sc['loss']} loss",
+                   "n_obs": n_obs, "n_pts": n_pts, "n_cams": n_cams},
+        "obs_per_s": round(value * n_obs, 1),
+        "accepted": summ["accepted"], "final_cost": summ["final_cost"],
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = schur_dense_cpu_baseline(sc)
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration():
     """A plain device-to-device copy of known size (3 x 512 MiB), whose
     FETCH_SIZE and WRITE_SIZE counter readings calibrate the byte counters
@@ -241,8 +344,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="large")
-    ap.add_argument("--workload", choices=["ba", "dense"], default="ba")
+    ap.add_argument("--config", default=None,
+                    help="BA scene (default: large for ba, medium for schur-dense)")
+    ap.add_argument("--workload", choices=["ba", "dense", "schur-dense"], default="ba")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (byte-counter calibration)")
@@ -255,6 +359,9 @@ def main():
         sys.exit(2)
     if args.workload == "dense":
         return main_dense(args)
+    if args.workload == "schur-dense":
+        return main_schur_dense(args)
+    args.config = args.config or "large"
 
     import torch
     from nonlinear_least_squares_amd import ba
