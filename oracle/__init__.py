@@ -91,6 +91,7 @@ def lib():
         L.orc_cost_at.argtypes = [vp, dp, dp, dp]
         L.orc_lm_step.argtypes = [vp, C.POINTER(StepInfo)]
         L.orc_solve.argtypes = [vp, C.c_int, C.POINTER(StepInfo)]
+        L.orc_backward.argtypes = [vp, dp, dp, dp, C.POINTER(C.c_int), dp]
         L.orc_get_lambda.argtypes = [vp]
         L.orc_get_lambda.restype = d
         L.orc_set_lambda.argtypes = [vp, d]
@@ -208,6 +209,20 @@ class Problem:
 
     def dense_schur_solve(self):
         self._check(lib().orc_dense_schur_solve(self.h), "dense_schur_solve")
+
+    def backward(self, grad_cams, grad_points):
+        """df/du (n_obs x 2, original order) by implicit differentiation of one
+        damped Gauss-Newton step at the current parameters and lambda; also
+        returns the PCG iteration count and relative residual (0 for the dense
+        solver)."""
+        gc = np.ascontiguousarray(grad_cams, dtype=np.float64).ravel()
+        gp = np.ascontiguousarray(grad_points, dtype=np.float64).ravel()
+        assert gc.size == 9 * self.nc and gp.size == 3 * self.np
+        out = np.empty(2 * self.nobs)
+        it, rel = C.c_int(), C.c_double()
+        self._check(lib().orc_backward(self.h, _p(gc), _p(gp), _p(out), C.byref(it), C.byref(rel)),
+                    "backward")
+        return out.reshape(-1, 2), it.value, rel.value
 
     def backsub(self):
         self._check(lib().orc_backsub(self.h), "backsub")

@@ -837,6 +837,68 @@ int orc_lm_step(orc_problem* h, orc_step_info* info) {
   return ORC_OK;
 }
 
+/* Implicit backward ([THESEUS], "backward modes", implicit differentiation):
+ * with the optimality condition g(theta; u) = grad_theta S = 0, the note gets
+ * D_u theta* = -(D_theta g)^-1 D_u g by differentiating one Newton step at the
+ * solution, h(theta; u) = theta - [Hess S]^-1_stop grad S, the Hessian held
+ * fixed.  Readings: the Hessian is the damped Gauss-Newton matrix of the
+ * current LM state, H~ = J^T W J + lambda diag (the damping makes it
+ * invertible; the undamped one is singular along the 7-dimensional gauge of a
+ * BA problem); u are the observed pixels.  grad S = sum_k J_k^T psi(r_k) with
+ * psi(r) = d rho(|r|) / dr and r_k = u^_k(theta) - u_k, so
+ * d grad S / d u_k = -J_k^T psi'(r_k) and, for a loss f of the solution with
+ * gradient G,
+ *   df/du_k = psi'(r_k) J_k H~^-1 G,
+ * psi' = I for the squared loss and inside the Huber threshold, and
+ * (delta / |r|) (I - r r^T / |r|^2) beyond it.  H~^-1 G is the damped system
+ * of an LM step solved with g = -G: Schur complement, the configured solver
+ * (PCG, or the dense Cholesky of S), back-substitution.  grad_cams is nc x 9,
+ * grad_pts np x 3, out_uv nobs x 2 in the original observation order. */
+int orc_backward(orc_problem* h, const double* grad_cams, const double* grad_pts, double* out_uv,
+                 int* iters_out, double* rel_res_out) {
+  int rc = orc_linearize(h);
+  if (rc) return rc;
+  for (int64_t e = 0; e < 9 * h->nc; e++) h->gc[e] = -grad_cams[e];
+  for (int64_t e = 0; e < 3 * h->np; e++) h->gp[e] = -grad_pts[e];
+  h->linearized = 0; /* g no longer holds the gradient of the cost */
+  if ((rc = orc_damp(h))) return rc;
+  if ((rc = orc_schur(h))) return rc;
+  int iters = 0;
+  double rel = 0.0;
+  if (h->opt.solver == 1) {
+    if ((rc = orc_dense_schur_solve(h))) return rc;
+  } else {
+    if ((rc = orc_pcg(h, h->opt.pcg_max_iters, h->opt.pcg_rel_tol, &iters, &rel))) return rc;
+  }
+  if ((rc = orc_backsub(h))) return rc;
+  for (int64_t k = 0; k < h->nobs; k++) {
+    const double* Jc = h->Jc + 18 * k;
+    const double* Jp = h->Jp + 6 * k;
+    const double* xc = h->dc + 9 * h->cam_idx[k];
+    const double* xp = h->dp + 3 * h->pt_idx[k];
+    double y[2];
+    for (int a = 0; a < 2; a++) {
+      double t = 0.0;
+      for (int b = 0; b < 9; b++) t += Jc[9 * a + b] * xc[b];
+      for (int b = 0; b < 3; b++) t += Jp[3 * a + b] * xp[b];
+      y[a] = t;
+    }
+    const double* r = h->r + 2 * k;
+    const double e = sqrt(r[0] * r[0] + r[1] * r[1]);
+    if (h->opt.loss == 1 && e > h->opt.huber_delta) {
+      const double ry = (r[0] * y[0] + r[1] * y[1]) / (e * e);
+      out_uv[2 * k] = h->opt.huber_delta / e * (y[0] - r[0] * ry);
+      out_uv[2 * k + 1] = h->opt.huber_delta / e * (y[1] - r[1] * ry);
+    } else {
+      out_uv[2 * k] = y[0];
+      out_uv[2 * k + 1] = y[1];
+    }
+  }
+  if (iters_out) *iters_out = iters;
+  if (rel_res_out) *rel_res_out = rel;
+  return ORC_OK;
+}
+
 int orc_solve(orc_problem* h, int n_iters, orc_step_info* infos) {
   for (int it = 0; it < n_iters; it++) {
     int rc = orc_lm_step(h, infos ? infos + it : NULL);

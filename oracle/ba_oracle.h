@@ -86,6 +86,11 @@ int orc_retract(orc_problem* h);
 int orc_cost_at(const orc_problem* h, const double* cams, const double* pts, double* cost);
 int orc_lm_step(orc_problem* h, orc_step_info* info);
 int orc_solve(orc_problem* h, int n_iters, orc_step_info* infos);
+/* df/du (nobs x 2) for a loss f of the LM solution with gradient
+ * (grad_cams, grad_pts), by implicit differentiation of one damped
+ * Gauss-Newton step at the current parameters and lambda. */
+int orc_backward(orc_problem* h, const double* grad_cams, const double* grad_pts, double* out_uv,
+                 int* iters, double* rel_res);
 
 double orc_get_lambda(const orc_problem* h);
 void orc_set_lambda(orc_problem* h, double lam);
