@@ -147,6 +147,27 @@ int ba_solve(ba_problem* h, int n_iters, ba_summary* s);
 /* Cost at the current parameters, recomputed on the device. */
 int ba_cost(ba_problem* h, double* cost_out);
 
+/* Implicit backward through the LM solution, the implicit mode of the Theseus
+ * note: one Newton step at the current parameters, h(theta; u) = theta -
+ * H~^-1 grad S(theta; u), is differentiated with H~ held fixed, H~ being the
+ * damped Gauss-Newton matrix of the current LM state (lambda as the next step
+ * would use it; the undamped matrix is singular along the gauge of a BA
+ * problem), u the observed pixels.  Given the gradient G of a loss f with
+ * respect to the parameters (grad_cams n_cams x 9 in the tangent of the
+ * forward step, grad_points n_pts x 3), writes for every observation, in the
+ * original order, grad_uv (n_obs x 2):
+ *   df/du_k = psi'(r_k) J_k H~^-1 G,
+ * with psi(r) = d rho(|r|)/dr: psi' = I for the squared loss and inside the
+ * Huber threshold, (delta/|r|)(I - r r^T/|r|^2) beyond it.  H~^-1 G is solved
+ * like an LM step (Schur elimination, the handle's solver and tolerance,
+ * back-substitution).  The three arrays live where opts.mem says (host or
+ * device).  pcg_iters (nullable) receives the PCG iterations (0 with the dense
+ * solver).  The parameters and lambda are unchanged; the next LM step
+ * linearises again.  BA_ERR_ARG for null arrays, BA_ERR_NOT_SPD if a damped
+ * block fails to factor. */
+int ba_backward(ba_problem* h, const double* grad_cams, const double* grad_points, double* grad_uv,
+                int* pcg_iters);
+
 /* Current parameters to caller-owned host buffers (n_cams x 9, n_pts x 3);
  * either pointer may be NULL. */
 int ba_get_params(ba_problem* h, double* cams_out, double* points_out);

@@ -88,6 +88,8 @@ SIGNATURES = {
     "ba_lm_step": (C.c_int, [C.c_void_p, C.POINTER(ba_step_info)]),
     "ba_solve": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(ba_summary)]),
     "ba_cost": (C.c_int, [C.c_void_p, C.POINTER(C.c_double)]),
+    "ba_backward": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                              C.POINTER(C.c_int)]),
     "ba_get_params": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "ba_set_params": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "ba_get_state": (C.c_int, [C.c_void_p, C.POINTER(ba_state)]),
@@ -209,6 +211,22 @@ class Problem:
         c = C.c_double()
         _check(lib().ba_cost(self.h, C.byref(c)), "ba_cost")
         return c.value
+
+    def backward(self, grad_cams, grad_points, out=None):
+        """df/du (n_obs x 2, original order) by implicit differentiation of one
+        damped Gauss-Newton step at the current parameters (ba_backward).
+        Inputs are numpy arrays (host handles) or device tensors (device
+        handles); for a device handle ``out`` must be a device tensor of
+        n_obs x 2 doubles.  Returns (grad_uv, pcg_iters)."""
+        pc, kc = _ptr(grad_cams, np.float64)
+        pp, kp = _ptr(grad_points, np.float64)
+        if out is None:
+            out = np.empty((self.n_obs, 2))
+        po, ko = _ptr(out, np.float64)
+        it = C.c_int()
+        _check(lib().ba_backward(self.h, pc, pp, po, C.byref(it)), "ba_backward")
+        del kc, kp
+        return ko, it.value
 
     def get_params(self):
         cams = np.empty((self.n_cams, 9))

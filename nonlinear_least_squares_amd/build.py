@@ -23,7 +23,7 @@ COMMON = [
 ]
 
 LIBS = {
-    "libba.so": ["ba_kernels.hip", "ba_dense.hip", "ba_capi.hip"],
+    "libba.so": ["ba_kernels.hip", "ba_dense.hip", "ba_backward.hip", "ba_capi.hip"],
     "libdba.so": ["dba_kernels.hip"],
 }
 

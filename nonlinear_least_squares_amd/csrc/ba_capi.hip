@@ -115,6 +115,7 @@ struct ba_problem {
          *pcg_part = nullptr, *red_part = nullptr, *pt_dot = nullptr;
   PcgState* pcg = nullptr;
   double *dp = nullptr, *cost_part = nullptr;
+  double* vjp = nullptr;     // backward: df/du in the original observation order
   StepOut* out = nullptr;
   int* flags = nullptr;
   StepOut* h_out = nullptr;  // pinned
@@ -516,6 +517,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   A.add(h->Cinv, 6 * np);
   A.add(h->prec, 8 * np);
   A.add(h->dp, 3 * np);
+  A.add(h->vjp, 2 * N);
   A.add(h->B, 45 * nc);
   A.add(h->gc, 9 * nc);
   A.add(h->Bd, 45 * nc);
@@ -945,6 +947,39 @@ int ba_solve(ba_problem* h, int n_iters, ba_summary* s) {
   sum.final_cost = h->cost;
   sum.lambda = h->lambda;
   if (s) *s = sum;
+  return BA_OK;
+}
+
+int ba_backward(ba_problem* h, const double* grad_cams, const double* grad_points, double* grad_uv,
+                int* pcg_iters) {
+  if (!h || !grad_cams || !grad_points || (h->nobs > 0 && !grad_uv))
+    return fail(BA_ERR_ARG, "bad arguments");
+  const int64_t nc = h->nc, np = h->np, N = h->nobs;
+  const bool dev = h->opt.mem == BA_MEM_DEVICE;
+  const hipMemcpyKind kin = dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  CHECK_RC(stage_linearize(h));
+  // g = -G: the damped step system then solves H~ x = G
+  HIPC(hipMemcpyAsync(h->gc, grad_cams, sizeof(double) * 9 * nc, kin, h->stream));
+  HIPC(hipMemcpyAsync(h->gp, grad_points, sizeof(double) * 3 * np, kin, h->stream));
+  launch_negate(h->gc, 9 * nc, h->stream);
+  launch_negate(h->gp, 3 * np, h->stream);
+  h->linearized = 0;   // g no longer holds the gradient of the cost
+  CHECK_RC(stage_schur(h));
+  CHECK_RC(stage_solve(h));
+  Dev d = make_dev(h);
+  TIMED(BA_K_BACKSUB, -1, launch_backsub(d, h->stream));
+  launch_vjp_obs(d, h->perm_pt, dev ? grad_uv : h->vjp, h->stream);
+  HIPC(hipGetLastError());
+  if (!dev && N) HIPC(hipMemcpyAsync(grad_uv, h->vjp, sizeof(double) * 2 * N, hipMemcpyDeviceToHost,
+                                     h->stream));
+  PcgState st;
+  HIPC(hipMemcpyAsync(&st, h->pcg, sizeof(st), hipMemcpyDeviceToHost, h->stream));
+  int flags[2] = {0, 0};
+  HIPC(hipMemcpyAsync(flags, h->flags, sizeof(flags), hipMemcpyDeviceToHost, h->stream));
+  HIPC(hipStreamSynchronize(h->stream));
+  if (h->prof_on) CHECK_RC(prof_collect(h, st.iters));
+  if (flags[1]) return fail(BA_ERR_NOT_SPD, "a damped block is not positive definite");
+  if (pcg_iters) *pcg_iters = st.iters;
   return BA_OK;
 }
 

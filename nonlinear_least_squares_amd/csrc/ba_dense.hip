@@ -30,10 +30,9 @@
 //           from a factored diagonal tile.
 // The factor's diagonal tiles are kept apart (ds_diag); the back-substitution
 // L^T dc = y runs in one workgroup, tile by tile.
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
-#include "ba_kernels.h"
+#include "ba_launch.h"
 
 namespace ba {
 namespace {
@@ -387,35 +386,23 @@ __global__ __launch_bounds__(kSolveThreads) void k_ds_backsolve(Dev d) {
   }
 }
 
-template <typename... KArgs, typename... Args>
-void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, uint32_t shmem,
-            Args... args) {
-  DispatchEvents& ev = dispatch_events();
-  hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0u,
-                        static_cast<KArgs>(args)...);
-  if (ev.start) {
-    ev.used = true;
-    ev.start = ev.stop = nullptr;
-  }
-}
-
 }  // namespace
 
 int ds_tile() { return kT; }
 
 void launch_ds_runs(const Dev& d, hipStream_t s) {
-  if (d.ds_nruns > 0) launch(k_ds_runs, dim3((d.ds_nruns + 255) / 256), dim3(256), s, 0u, d);
+  if (d.ds_nruns > 0) launch_timed(k_ds_runs, dim3((d.ds_nruns + 255) / 256), dim3(256), s, 0u, d);
 }
 void launch_ds_fill(const Dev& d, hipStream_t s) {
   const int64_t n = ((int64_t)d.ds_ld + kT) * d.ds_ld;
-  launch(k_ds_fill, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, d);
+  launch_timed(k_ds_fill, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, d);
 }
 void launch_ds_assemble(const Dev& d, hipStream_t s) {
-  if (d.ds_nblk > 0) launch(k_ds_assemble, dim3(d.ds_nblk), dim3(64 * kAsmWaves), s, 0u, d);
+  if (d.ds_nblk > 0) launch_timed(k_ds_assemble, dim3(d.ds_nblk), dim3(64 * kAsmWaves), s, 0u, d);
 }
-void launch_ds_diag0(const Dev& d, hipStream_t s) { launch(k_ds_diag0, dim3(1), dim3(64), s, 0u, d); }
+void launch_ds_diag0(const Dev& d, hipStream_t s) { launch_timed(k_ds_diag0, dim3(1), dim3(64), s, 0u, d); }
 void launch_ds_panel(const Dev& d, int k, hipStream_t s) {
-  launch(k_ds_panel, dim3(d.ds_T - k), dim3(64), s, 0u, d, k);
+  launch_timed(k_ds_panel, dim3(d.ds_T - k), dim3(64), s, 0u, d, k);
 }
 int ds_update_tiles(const Dev& d, int k) {
   const int m = d.ds_T - k - 1;
@@ -423,14 +410,14 @@ int ds_update_tiles(const Dev& d, int k) {
 }
 void launch_ds_update(const Dev& d, int k, hipStream_t s) {
   const int n = ds_update_tiles(d, k);
-  if (n > 0) launch(k_ds_update, dim3(n), dim3(64), s, 0u, d, k);
+  if (n > 0) launch_timed(k_ds_update, dim3(n), dim3(64), s, 0u, d, k);
 }
 hipError_t ds_backsolve_limit(int ld) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ds_backsolve),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(8 * ld));
 }
 void launch_ds_backsolve(const Dev& d, hipStream_t s) {
-  launch(k_ds_backsolve, dim3(1), dim3(kSolveThreads), s, (uint32_t)(8 * d.ds_ld), d);
+  launch_timed(k_ds_backsolve, dim3(1), dim3(kSolveThreads), s, (uint32_t)(8 * d.ds_ld), d);
 }
 
 }  // namespace ba
