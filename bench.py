@@ -23,6 +23,11 @@ solver on the medium scene (250 walk cameras, 60,000 points, about 300,000
 observations): a step is one LM iteration whose camera step comes from the
 explicit S (order 2,250) and its tile Cholesky; the roofline refers to the
 fp64 MFMA trailing update when that kernel dominates.
+
+``--workload backward`` measures ba_backward on the large scene after two LM
+steps: a step is one implicit backward pass (linearise, Schur elimination
+with the parameter gradient as right-hand side, PCG, back-substitution,
+per-observation products), with the arrays resident on the device.
 """
 import argparse
 import hashlib
@@ -324,6 +329,104 @@ def main_schur_dense(args):
     print(json.dumps(out), flush=True)
 
 
+BACKWARD_METRIC = "implicit backward passes/s (fp64, 1 GPU); % of HBM roofline"
+
+
+def backward_cpu_baseline(sc, G_c, G_p, n_calls=3):
+    """The oracle's implicit backward (plain C, one thread) on the same scene
+    and state: linearisation, Schur elimination, PCG, back-substitution."""
+    import oracle
+    P = oracle.Problem.from_scene(sc)
+    P.solve(2)
+    t0 = time.perf_counter()
+    for _ in range(n_calls):
+        P.backward(G_c, G_p)
+    dt = time.perf_counter() - t0
+    return {"value": n_calls / dt, "unit": "backward passes/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_calls} backward passes of the same scene after 2 LM iterations "
+                      f"({len(sc['obs_cam'])} observations, PCG max {sc['pcg_max_iters']}), "
+                      f"single-threaded C oracle, {dt:.1f} s"}
+
+
+def main_backward(args):
+    import numpy as np
+    import torch
+    from nonlinear_least_squares_amd import ba
+    from synthetic import ba_scene, scene_summary
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    config = args.config or "large"
+    sc = ba_scene(config)
+    n_obs, n_pts, n_cams = len(sc["obs_cam"]), len(sc["points"]), len(sc["cams"])
+    print(f"# {scene_summary(sc)}", file=sys.stderr, flush=True)
+    rng = np.random.default_rng(21)
+    G_c, G_p = rng.standard_normal((n_cams, 9)), rng.standard_normal((n_pts, 3))
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    t = {k: torch.from_numpy(np.ascontiguousarray(sc[k])).to(dev)
+         for k in ("cams", "points", "obs_cam", "obs_pt", "obs_uv")}
+    gcd, gpd = torch.from_numpy(G_c).to(dev), torch.from_numpy(G_p).to(dev)
+    out = torch.empty((n_obs, 2), dtype=torch.float64, device=dev)
+    torch.cuda.synchronize()
+
+    def make():
+        P = ba.Problem(t["cams"], t["points"], t["obs_cam"], t["obs_pt"], t["obs_uv"],
+                       loss=ba.BA_LOSS_HUBER if sc["loss"] == "huber" else ba.BA_LOSS_SQUARED,
+                       huber_delta=sc["huber_delta"], pcg_max_iters=sc["pcg_max_iters"],
+                       pcg_rel_tol=sc["pcg_rel_tol"], mem=ba.BA_MEM_DEVICE, stream=stream)
+        P.solve(2)
+        return P
+
+    warm = make()
+    warm.profile()
+    for _ in range(max(args.warmup, 1)):
+        warm.backward(gcd, gpd, out=out)
+    prof = warm.profile_get()
+    warm.close()
+    dominant = max(prof, key=lambda k: prof[k][1])
+    print(f"# warm-up kernel totals (launches, ms): {prof}", file=sys.stderr, flush=True)
+
+    P = make()
+    P.profile([dominant], every=PROFILE_EVERY)
+    iters = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        _, it = P.backward(gcd, gpd, out=out)
+        iters += it
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    launches, kms = P.profile_get()[dominant]
+    value = args.steps / dt
+    n_chunks = camera_chunks(sc["obs_cam"], sc["obs_pt"], n_pts)
+    nbytes = algorithmic_bytes(dominant, n_obs, n_pts, n_cams, n_chunks)
+    roof = None
+    if nbytes and launches:
+        avg_s = kms / launches / 1e3
+        ach = nbytes / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant),
+                "kernel": dominant, "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches": launches, "algorithmic_bytes_per_launch": nbytes}
+    res = {
+        "metric": BACKWARD_METRIC, "value": round(value, 3), "unit": "backward passes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * dt / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{config} BA implicit backward (df/du through one damped GN "
+                               f"step, arrays resident on the device): {n_cams} cameras, "
+                               f"{n_pts} points, {n_obs} observations, PCG max "
+                               f"{sc['pcg_max_iters']} rel tol {sc['pcg_rel_tol']}",
+                   "n_obs": n_obs, "n_pts": n_pts, "n_cams": n_cams},
+        "pcg_iters_per_pass": round(iters / args.steps, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = backward_cpu_baseline(sc, G_c, G_p)
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration():
     """A plain device-to-device copy of known size (3 x 512 MiB), whose
     FETCH_SIZE and WRITE_SIZE counter readings calibrate the byte counters
@@ -346,7 +449,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default=None,
                     help="BA scene (default: large for ba, medium for schur-dense)")
-    ap.add_argument("--workload", choices=["ba", "dense", "schur-dense"], default="ba")
+    ap.add_argument("--workload", choices=["ba", "dense", "schur-dense", "backward"], default="ba")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (byte-counter calibration)")
@@ -361,6 +464,8 @@ def main():
         return main_dense(args)
     if args.workload == "schur-dense":
         return main_schur_dense(args)
+    if args.workload == "backward":
+        return main_backward(args)
     args.config = args.config or "large"
 
     import torch

@@ -12,7 +12,8 @@
 // (delta / |r|)(I - r r^T / |r|^2) beyond it.  H~^-1 G is the damped system of
 // an LM step with g = -G, solved by the same Schur elimination, solver and
 // back-substitution as the forward step (ba_capi.hip); the kernels here set
-// g = -G and apply psi'(r_k) J_k to the solution per observation.
+// g = -G and apply psi'(r_k) J_k to the solution per observation, in camera
+// order (camera chunks, the camera's data uniform across a wavefront).
 #include <hip/hip_runtime.h>
 
 #include "ba_launch.h"
@@ -25,13 +26,15 @@ __global__ void k_negate(double* a, int64_t n) {
   if (e < n) a[e] = -a[e];
 }
 
-// One thread per point-order observation s; the result goes to the
-// observation's original index perm_pt[s].  x holds the camera part of
-// H~^-1 G, dp its point part.
-__global__ void k_vjp_obs(Dev d, const int32_t* __restrict__ perm_pt, double* __restrict__ out) {
-  const int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (s >= d.nobs) return;
-  const int j = d.o_cam[s], i = d.o_pt[s];
+// One wavefront per camera chunk (the camera passes' blocks): the camera and
+// its part of H~^-1 G (x) are uniform across the wavefront; per observation
+// the point, its part dp and the observed pixel are read, and the result goes
+// to the observation's original index perm_cam[s].
+__global__ __launch_bounds__(64) void k_vjp_cam(Dev d, const int32_t* __restrict__ perm_cam,
+                                                double* __restrict__ out) {
+  const int4 bi = d.blk_chunk[blockIdx.x];
+  const int cb = bi.x, ce = bi.y, j = bi.z;
+  if (bi.w < 0) return;
   const CamT& t = d.tab[j];
   CamG c;
 #pragma unroll
@@ -41,23 +44,29 @@ __global__ void k_vjp_obs(Dev d, const int32_t* __restrict__ perm_pt, double* __
   c.f = t.f;
   c.k1 = t.k1;
   c.k2 = t.k2;
-  Geo g;
-  geo_eval(c, d.pts[3 * (int64_t)i], d.pts[3 * (int64_t)i + 1], d.pts[3 * (int64_t)i + 2], g);
-  const double r0 = g.u0 - d.o_uv[2 * s], r1 = g.u1 - d.o_uv[2 * s + 1];
-  double y0, y1, t0, t1;
-  jc_apply(g, c.f, d.x + 9 * (int64_t)j, y0, y1);
-  jp_apply(g, c.R, d.dp[3 * (int64_t)i], d.dp[3 * (int64_t)i + 1], d.dp[3 * (int64_t)i + 2], t0, t1);
-  y0 += t0;
-  y1 += t1;
-  const double e = sqrt(r0 * r0 + r1 * r1);
-  if (d.loss == 1 && e > d.delta) {
-    const double ry = (r0 * y0 + r1 * y1) / (e * e), sc = d.delta / e;
-    y0 = sc * (y0 - r0 * ry);
-    y1 = sc * (y1 - r1 * ry);
+  double xc[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) xc[k] = d.x[9 * (int64_t)j + k];
+  for (int s = cb + (int)threadIdx.x; s < ce; s += 64) {
+    const int64_t i = d.c_pt[s];
+    Geo g;
+    geo_eval(c, d.pts[3 * i], d.pts[3 * i + 1], d.pts[3 * i + 2], g);
+    const double r0 = g.u0 - d.c_uv[2 * (int64_t)s], r1 = g.u1 - d.c_uv[2 * (int64_t)s + 1];
+    double y0, y1, t0, t1;
+    jc_apply(g, c.f, xc, y0, y1);
+    jp_apply(g, c.R, d.dp[3 * i], d.dp[3 * i + 1], d.dp[3 * i + 2], t0, t1);
+    y0 += t0;
+    y1 += t1;
+    const double e = sqrt(r0 * r0 + r1 * r1);
+    if (d.loss == 1 && e > d.delta) {
+      const double ry = (r0 * y0 + r1 * y1) / (e * e), sc = d.delta / e;
+      y0 = sc * (y0 - r0 * ry);
+      y1 = sc * (y1 - r1 * ry);
+    }
+    const int64_t k = perm_cam[s];
+    out[2 * k] = y0;
+    out[2 * k + 1] = y1;
   }
-  const int64_t k = perm_pt[s];
-  out[2 * k] = y0;
-  out[2 * k + 1] = y1;
 }
 
 }  // namespace
@@ -66,9 +75,9 @@ void launch_negate(double* a, int64_t n, hipStream_t s) {
   if (n > 0) launch_timed(k_negate, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, a, n);
 }
 
-void launch_vjp_obs(const Dev& d, const int32_t* perm_pt, double* out, hipStream_t s) {
-  if (d.nobs > 0)
-    launch_timed(k_vjp_obs, dim3((unsigned)((d.nobs + 255) / 256)), dim3(256), s, 0u, d, perm_pt, out);
+void launch_vjp_obs(const Dev& d, const int32_t* perm_cam, double* out, hipStream_t s) {
+  if (d.n_chunk_blocks > 0)
+    launch_timed(k_vjp_cam, dim3(d.n_chunk_blocks), dim3(64), s, 0u, d, perm_cam, out);
 }
 
 }  // namespace ba

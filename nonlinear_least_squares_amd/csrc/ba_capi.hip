@@ -968,7 +968,7 @@ int ba_backward(ba_problem* h, const double* grad_cams, const double* grad_point
   CHECK_RC(stage_solve(h));
   Dev d = make_dev(h);
   TIMED(BA_K_BACKSUB, -1, launch_backsub(d, h->stream));
-  launch_vjp_obs(d, h->perm_pt, dev ? grad_uv : h->vjp, h->stream);
+  launch_vjp_obs(d, h->perm_cam, dev ? grad_uv : h->vjp, h->stream);
   HIPC(hipGetLastError());
   if (!dev && N) HIPC(hipMemcpyAsync(grad_uv, h->vjp, sizeof(double) * 2 * N, hipMemcpyDeviceToHost,
                                      h->stream));

@@ -189,9 +189,9 @@ hipError_t ds_backsolve_limit(int ld);
 void launch_ds_backsolve(const Dev& d, hipStream_t s);
 
 // Implicit backward: a <- -a; per observation psi'(r) (Jc x_cam + Jp dp_pt) to
-// out[2 perm_pt[s] ..].
+// out[2 perm_cam[s] ..], s the camera-order slot.
 void launch_negate(double* a, int64_t n, hipStream_t s);
-void launch_vjp_obs(const Dev& d, const int32_t* perm_pt, double* out, hipStream_t s);
+void launch_vjp_obs(const Dev& d, const int32_t* perm_cam, double* out, hipStream_t s);
 
 // Structure build helpers.
 void launch_validate(const int32_t* cam_idx, const int32_t* pt_idx, const double* uv, int64_t n,
