@@ -3,7 +3,8 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The GPU library never loads it and shares
 no code with it.  The arithmetic lives in ``ba_oracle.c`` (plain C loops, fp64)
-and ``droid_oracle.c`` (dense frame-graph BA, wrapped by ``oracle.droid``);
+``droid_oracle.c`` (dense frame-graph BA, wrapped by ``oracle.droid``) and
+``pgo_oracle.c`` (pose-graph optimisation, wrapped by ``oracle.pgo``);
 this module only builds and marshals.
 
 Parity status: every function is pinned by tests in ``tests/test_oracle_*.py``
@@ -20,7 +21,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libba_oracle.so")
-SOURCES = [os.path.join(HERE, n) for n in ("ba_oracle.c", "droid_oracle.c")
+SOURCES = [os.path.join(HERE, n) for n in ("ba_oracle.c", "droid_oracle.c", "pgo_oracle.c")
            if os.path.exists(os.path.join(HERE, n))]
 
 (ORC_CAMS, ORC_PTS, ORC_PERM_PT, ORC_PERM_CAM, ORC_PT_PTR, ORC_CAM_PTR, ORC_R, ORC_JC, ORC_JP,
