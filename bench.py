@@ -28,6 +28,12 @@ fp64 MFMA trailing update when that kernel dominates.
 steps: a step is one implicit backward pass (linearise, Schur elimination
 with the parameter gradient as right-hand side, PCG, back-substitution,
 per-observation products), with the arrays resident on the device.
+
+``--workload pgo`` measures libpgo, pose-graph optimisation: a step is one LM
+iteration (linearise the relative-pose edges, per-pose H and g sums, damping,
+PCG with 6 x 6 block-Jacobi, retraction, trial cost, accept/reject) of the
+sphere graph (2,500 poses, 4,949 edges; ``--config large``: 524,288 poses,
+1,047,551 edges).
 """
 import argparse
 import hashlib
@@ -427,6 +433,103 @@ def main_backward(args):
     print(json.dumps(res), flush=True)
 
 
+PGO_METRIC = "pose-graph LM iterations/s (fp64, 1 GPU); % of HBM roofline"
+
+
+def pgo_algorithmic_bytes(kernel, n, m, n_fixed):
+    """Compulsory HBM bytes of one launch of a pose-graph PCG kernel: each
+    array element it must read or write once, per-block partials ignored.
+    pcg_a: damped diagonal block (288 B) and z (48) of every pose, p and q
+    read and written (192), the per-pose half-edge list (4 + 4 per half edge);
+    each edge's H_ij (288) and index pair (8) once.  pcg_b: block-Jacobi
+    inverse (288), x and r read and written (192), p and q read (96), z
+    written (48)."""
+    if kernel == "pcg_a":
+        return n * (288 + 48 + 192 + 4) + m * (288 + 8 + 2 * 4)
+    if kernel == "pcg_b":
+        return n * (288 + 192 + 96 + 48)
+    return None
+
+
+def pgo_cpu_baseline(sc, budget_s=15.0):
+    """The oracle as it stands (plain C, one thread, PCG as on the GPU): LM
+    iterations of the same graph from the same start, as many as fit in about
+    budget_s (at least one)."""
+    from oracle import pgo as opgo
+    P = opgo.PGOProblem.from_scene(sc)
+    t0 = time.perf_counter()
+    k = 0
+    while k < sc["n_iters"] and (k == 0 or time.perf_counter() - t0 < budget_s):
+        P.lm_step()
+        k += 1
+    dt = time.perf_counter() - t0
+    return {"value": k / dt, "unit": "LM iterations/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {k} LM iterations of the same graph ({len(sc['poses'])} poses, "
+                      f"{len(sc['edges'])} edges, PCG max {sc['pcg_max_iters']}), "
+                      f"single-threaded C oracle, {dt:.1f} s"}
+
+
+def main_pgo(args):
+    import torch
+    from nonlinear_least_squares_amd import pgo
+    from synthetic import pgo_scene, pgo_summary
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    config = args.config or "sphere"
+    sc = pgo_scene(config)
+    n, m, nf = len(sc["poses"]), len(sc["edges"]), sc["n_fixed"]
+    print(f"# {pgo_summary(sc)}", file=sys.stderr, flush=True)
+    warm = pgo.Problem.from_scene(sc)
+    warm.profile()
+    warm.solve(max(args.warmup, 1))
+    prof = warm.profile_get()
+    warm.close()
+    dominant = max(prof, key=lambda k: prof[k][1])
+    print(f"# warm-up kernel totals (launches, ms): {prof}", file=sys.stderr, flush=True)
+
+    P = pgo.Problem.from_scene(sc)
+    P.profile([dominant], every=PROFILE_EVERY)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tr = P.solve(args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    launches, kms = P.profile_get()[dominant]
+    value = args.steps / dt
+    nbytes = pgo_algorithmic_bytes(dominant, n, m, nf)
+    roof = None
+    if launches:
+        avg_s = kms / launches / 1e3
+        roof = {"bound": None, "achieved": None, "peak": None, "unit": None, "frac": None,
+                "traffic": None, "kernel": dominant, "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches": launches}
+        if nbytes:
+            ach = nbytes / avg_s / 1e9
+            roof.update({"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": nbytes})
+    pcg = sum(t["pcg_iters"] for t in tr)
+    out = {
+        "metric": PGO_METRIC, "value": round(value, 3), "unit": "LM iterations/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * dt / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{config} pose graph: {n} SE(3) poses on a sphere, {m} "
+                               f"relative-pose edges (odometry and loop closures), PCG with "
+                               f"6x6 block-Jacobi, max {sc['pcg_max_iters']} rel tol "
+                               f"{sc['pcg_rel_tol']}",
+                   "n_poses": n, "n_edges": m},
+        "edges_per_s": round(value * m, 1),
+        "pcg_iters_per_lm_iter": round(pcg / args.steps, 2),
+        "accepted": sum(t["accepted"] for t in tr), "final_cost": P.cost(),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = pgo_cpu_baseline(sc)
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration():
     """A plain device-to-device copy of known size (3 x 512 MiB), whose
     FETCH_SIZE and WRITE_SIZE counter readings calibrate the byte counters
@@ -448,8 +551,10 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default=None,
-                    help="BA scene (default: large for ba, medium for schur-dense)")
-    ap.add_argument("--workload", choices=["ba", "dense", "schur-dense", "backward"], default="ba")
+                    help="scene (default: large for ba and backward, medium for "
+                         "schur-dense, sphere for pgo)")
+    ap.add_argument("--workload", choices=["ba", "dense", "schur-dense", "backward", "pgo"],
+                    default="ba")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (byte-counter calibration)")
@@ -466,6 +571,8 @@ def main():
         return main_schur_dense(args)
     if args.workload == "backward":
         return main_backward(args)
+    if args.workload == "pgo":
+        return main_pgo(args)
     args.config = args.config or "large"
 
     import torch

@@ -1,8 +1,9 @@
 """Builds the gfx950 shared libraries in-tree with hipcc.
 
 ``python -m nonlinear_least_squares_amd.build`` compiles ``libba.so`` (the
-fp64 bundle-adjustment LM iteration) and ``libdba.so`` (the fp32 dense
-frame-graph variant) next to this file.
+fp64 bundle-adjustment LM iteration), ``libdba.so`` (the fp32 dense
+frame-graph variant) and ``libpgo.so`` (fp64 pose-graph optimisation) next
+to this file.
 """
 
 import os
@@ -25,6 +26,7 @@ COMMON = [
 LIBS = {
     "libba.so": ["ba_kernels.hip", "ba_dense.hip", "ba_backward.hip", "ba_capi.hip"],
     "libdba.so": ["dba_kernels.hip"],
+    "libpgo.so": ["pgo_kernels.hip", "pgo_capi.hip"],
 }
 
 

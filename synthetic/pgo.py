@@ -21,6 +21,10 @@ Configurations:
 * ``small``  : 10 x 20 (200 poses, 379 edges).
 * ``sphere`` : 50 x 50 (2,500 poses, 4,949 edges), the size of the sphere
   benchmarks.
+* ``medium`` : 100 x 100 (10,000 poses, 19,899 edges).
+* ``large``  : 512 x 1024 (524,288 poses, 1,047,551 edges): as many poses as
+  the batched pose-graph benchmark of the Theseus note holds in total (256
+  graphs of 2,048 poses), here as one connected graph.
 
 Every draw comes from ``numpy.random.Generator(PCG64(seed))``; the forward
 model (composition of the true poses) is written on scipy's ``Rotation`` and
@@ -34,6 +38,8 @@ PGO_CONFIGS = {
     "tiny": dict(n_rings=4, per_ring=8, seed=31, n_iters=10),
     "small": dict(n_rings=10, per_ring=20, seed=32, n_iters=15),
     "sphere": dict(n_rings=50, per_ring=50, seed=33, n_iters=20),
+    "medium": dict(n_rings=100, per_ring=100, seed=35, n_iters=20),
+    "large": dict(n_rings=512, per_ring=1024, seed=34, n_iters=20),
 }
 
 SPHERE_RADIUS = 10.0
@@ -44,17 +50,14 @@ INIT_R = 0.05        # initial error, rotation (rad)
 
 
 def _true_poses(n_rings, per_ring):
-    R, t = [], []
-    for a in range(n_rings):
-        lat = np.pi * (a + 1) / (n_rings + 1) - np.pi / 2
-        for b in range(per_ring):
-            lon = 2 * np.pi * b / per_ring
-            out = np.array([np.cos(lat) * np.cos(lon), np.cos(lat) * np.sin(lon), np.sin(lat)])
-            east = np.array([-np.sin(lon), np.cos(lon), 0.0])
-            north = np.cross(out, east)
-            R.append(np.stack([east, north, out], axis=1))   # columns: body axes in world
-            t.append(SPHERE_RADIUS * out)
-    return np.array(R), np.array(t)
+    a, b = np.meshgrid(np.arange(n_rings), np.arange(per_ring), indexing="ij")
+    lat = (np.pi * (a + 1) / (n_rings + 1) - np.pi / 2).ravel()
+    lon = (2 * np.pi * b / per_ring).ravel()
+    out = np.stack([np.cos(lat) * np.cos(lon), np.cos(lat) * np.sin(lon), np.sin(lat)], axis=1)
+    east = np.stack([-np.sin(lon), np.cos(lon), np.zeros_like(lon)], axis=1)
+    north = np.cross(out, east)
+    R = np.stack([east, north, out], axis=2)   # columns: body axes in world
+    return R, SPHERE_RADIUS * out
 
 
 def _edges(n_rings, per_ring):
