@@ -439,15 +439,15 @@ PGO_METRIC = "pose-graph LM iterations/s (fp64, 1 GPU); % of HBM roofline"
 def pgo_algorithmic_bytes(kernel, n, m, n_fixed):
     """Compulsory HBM bytes of one launch of a pose-graph PCG kernel: each
     array element it must read or write once, per-block partials ignored.
-    pcg_a: damped diagonal block (288 B) and z (48) of every pose, p and q
-    read and written (192), the per-pose half-edge list (4 + 4 per half edge);
-    each edge's H_ij (288) and index pair (8) once.  pcg_b: block-Jacobi
-    inverse (288), x and r read and written (192), p and q read (96), z
-    written (48)."""
+    pcg_a: damped diagonal block (upper triangle, 168 B) and z (48) of every
+    pose, p and q read and written (192), the list offset (4); per edge the
+    compact H_ij (160) once and its two half-edge entries (16).  pcg_b:
+    block-Jacobi inverse (upper triangle, 168), x and r read and written (192),
+    p and q read (96), z written (48)."""
     if kernel == "pcg_a":
-        return n * (288 + 48 + 192 + 4) + m * (288 + 8 + 2 * 4)
+        return n * (168 + 48 + 192 + 4) + m * (160 + 16)
     if kernel == "pcg_b":
-        return n * (288 + 192 + 96 + 48)
+        return n * (168 + 192 + 96 + 48)
     return None
 
 

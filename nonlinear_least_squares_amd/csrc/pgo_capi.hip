@@ -85,7 +85,7 @@ struct pgo_problem {
   double *meas = nullptr, *meas_tab = nullptr, *info = nullptr;
   int32_t* half_ptr = nullptr;
   int2* nbr = nullptr;
-  double *r = nullptr, *Ji = nullptr, *Jj = nullptr, *Ho = nullptr, *half = nullptr,
+  double *r = nullptr, *Ji = nullptr, *Jj = nullptr, *Hc = nullptr, *half = nullptr,
          *cost_part = nullptr;
   double *Hd = nullptr, *Hdd = nullptr, *Minv = nullptr, *g = nullptr;
   double *x = nullptr, *rv = nullptr, *z = nullptr, *p = nullptr, *q = nullptr, *red = nullptr,
@@ -131,7 +131,7 @@ Dev make_dev(const pgo_problem* h) {
   d.r = h->r;
   d.Ji = h->Ji;
   d.Jj = h->Jj;
-  d.Ho = h->Ho;
+  d.Hc = h->Hc;
   d.half = h->half;
   d.cost_part = h->cost_part;
   d.n_cost_parts = edge_blocks(h->m);
@@ -422,12 +422,12 @@ int pgo_create(const double* poses, int64_t n, const int32_t* edges, const doubl
   A.add(h->r, 6 * m);
   A.add(h->Ji, 36 * m);
   A.add(h->Jj, 36 * m);
-  A.add(h->Ho, 36 * m);
+  A.add(h->Hc, (int64_t)kCoupVals * m);
   A.add(h->half, (int64_t)kHalfVals * 2 * m);
   A.add(h->cost_part, edge_blocks(m));
   A.add(h->Hd, 36 * n);
-  A.add(h->Hdd, 36 * n);
-  A.add(h->Minv, 36 * n);
+  A.add(h->Hdd, (int64_t)kSymVals * n);
+  A.add(h->Minv, (int64_t)kSymVals * n);
   A.add(h->g, 6 * n);
   A.add(h->x, 6 * n);
   A.add(h->rv, 6 * n);
@@ -550,7 +550,19 @@ int pgo_debug_get(pgo_problem* h, int which, double* out, int64_t count) {
     case PGO_DBG_JI: src = h->Ji; break;
     case PGO_DBG_JJ: src = h->Jj; break;
     case PGO_DBG_HD: src = h->Hd; break;
-    case PGO_DBG_HO: src = h->Ho; break;
+    case PGO_DBG_HO: {
+      if (count == 0) return PGO_OK;
+      double* tmp = nullptr;
+      HIPC(hipMallocAsync(reinterpret_cast<void**>(&tmp), sizeof(double) * count, h->stream));
+      launch_expand_coupling(make_dev(h), tmp, h->stream);
+      hipError_t e1 = hipGetLastError();
+      hipError_t e2 = hipMemcpyAsync(out, tmp, sizeof(double) * count, hipMemcpyDeviceToHost, h->stream);
+      hipError_t e3 = hipFreeAsync(tmp, h->stream);
+      hipError_t e4 = hipStreamSynchronize(h->stream);
+      for (hipError_t e : {e1, e2, e3, e4})
+        if (e != hipSuccess) return fail(PGO_ERR_DEVICE, std::string("coupling blocks: ") + hipGetErrorString(e));
+      return PGO_OK;
+    }
     case PGO_DBG_G: src = h->g; break;
     case PGO_DBG_DX: src = h->x; break;
     case PGO_DBG_PCG: {

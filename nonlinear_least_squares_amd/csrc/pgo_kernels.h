@@ -5,7 +5,12 @@
 //              block of H (36) undamped and damped, block-Jacobi inverse (36),
 //              g (6), PCG vectors x r z p q (6 each)
 //   per edge : (i, j), measured R_e (9) and t_e (3), info [w_R, w_t],
-//              residual (6), Jacobians (36 + 36), H_ij (36), cost
+//              residual (6), Jacobians (36 + 36), cost, and H_ij in kCoupVals
+//              doubles: with R_i^T R_i = I its lower-left 3x3 block is zero and
+//              its lower-right one is -w_t I, so it is kept as the upper-left
+//              block (9), the upper-right block (9), -w_t, and a 0
+//   per pose : the damped diagonal block and its inverse are symmetric and
+//              kept as their upper triangles, row by row (kSymVals)
 //   per half edge (2m, side 0 = the edge's i, side 1 = its j): that end's
 //              contribution to its diagonal block (36) and to g (6); each
 //              pose lists its half edges in edge order (CSR) as pairs (half
@@ -22,6 +27,8 @@
 namespace pgo {
 
 constexpr int kHalfVals = 42;   // 6x6 block + 6-vector
+constexpr int kCoupVals = 20;   // H_ij: two 3x3 blocks, -w_t, 0
+constexpr int kSymVals = 21;    // upper triangle of a symmetric 6x6 block
 constexpr int kPosesPerWave = 10;
 constexpr int kPosesPerBlock = 4 * kPosesPerWave;   // PCG blocks of four wavefronts
 // Above this many PCG blocks the partial sums go through k_pcg_sum.
@@ -55,13 +62,13 @@ struct Dev {
   double* r;               // m x 6
   double* Ji;              // m x 36
   double* Jj;              // m x 36
-  double* Ho;              // m x 36
+  double* Hc;              // m x kCoupVals
   double* half;            // 2m x kHalfVals
   double* cost_part;       // per edge-kernel block
   int n_cost_parts;
   double* Hd;              // n x 36 undamped
-  double* Hdd;             // n x 36 damped, identity on held poses
-  double* Minv;            // n x 36
+  double* Hdd;             // n x kSymVals damped, identity on held poses
+  double* Minv;            // n x kSymVals block-Jacobi inverse
   double* g;               // n x 6
   double *x, *rv, *z, *p, *q;   // PCG vectors, 6n each
   double* red;             // per-block partials, kNumSums arrays of red_nb
@@ -97,5 +104,7 @@ void launch_retract(const Dev& d, hipStream_t s);
 void launch_cost(const Dev& d, const double* tab, hipStream_t s);
 void launch_cost_final(const Dev& d, hipStream_t s);
 void launch_validate(const Dev& d, const double* meas, int* flags, hipStream_t s);
+// Full 6x6 H_ij blocks (m x 36) from the compact ones, for inspection.
+void launch_expand_coupling(const Dev& d, double* out, hipStream_t s);
 
 }  // namespace pgo

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void k_edge(Dev d) {
     mat3_tmul(A, Jr, AtJ);
     double* Hi = d.half + kHalfVals * (2 * e);
     double* Hj = d.half + kHalfVals * (2 * e + 1);
-    double* Ho = d.Ho + 36 * e;
+    double* Hc = d.Hc + kCoupVals * e;
 #pragma unroll
     for (int a = 0; a < 3; ++a)
 #pragma unroll
@@ -207,11 +207,11 @@ __global__ __launch_bounds__(256) void k_edge(Dev d) {
         Hj[6 * a + 3 + b] = 0.0;
         Hj[6 * (3 + a) + b] = 0.0;
         Hj[6 * (3 + a) + 3 + b] = wt * QtQ[3 * a + b];
-        Ho[6 * a + b] = wR * AtJ[3 * a + b];
-        Ho[6 * a + 3 + b] = wt * UtQ[3 * a + b];
-        Ho[6 * (3 + a) + b] = 0.0;
-        Ho[6 * (3 + a) + 3 + b] = -wt * QtQ[3 * a + b];
+        Hc[3 * a + b] = wR * AtJ[3 * a + b];
+        Hc[9 + 3 * a + b] = wt * UtQ[3 * a + b];
       }
+    Hc[18] = -wt;
+    Hc[19] = 0.0;
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
       const double aR = A[a] * r[0] + A[3 + a] * r[1] + A[6 + a] * r[2];
@@ -303,11 +303,20 @@ __global__ __launch_bounds__(128) void k_pose(Dev d) {
   }
   double Mi[36];
   if (!inv6(H, Mi)) d.flags[1] = 1;
+  int k = 0;
 #pragma unroll
-  for (int k = 0; k < 36; ++k) {
-    d.Hdd[36 * i + k] = H[k];
-    d.Minv[36 * i + k] = Mi[k];
-  }
+  for (int a = 0; a < 6; ++a)
+#pragma unroll
+    for (int b = a; b < 6; ++b, ++k) {
+      d.Hdd[kSymVals * i + k] = H[6 * a + b];
+      d.Minv[kSymVals * i + k] = Mi[6 * a + b];
+    }
+}
+
+// Index of entry (a, b) of a symmetric 6x6 block kept as its upper triangle.
+__device__ __forceinline__ int sym_idx(int a, int b) {
+  const int i = min(a, b), j = max(a, b);
+  return i * (11 - i) / 2 + j;
 }
 
 // ---- PCG on H~ dx = -g: six lanes per pose, ten poses per wavefront, four
@@ -327,10 +336,19 @@ struct Lane {
   bool on;
 };
 
+// Blocks are handed to the eight XCDs in turn (block b to XCD b mod 8); this
+// gives XCD x one contiguous range of poses, so a pose's graph neighbours,
+// whose z and H_ij it gathers, mostly sit in the same XCD's L2.
+__device__ __forceinline__ int64_t xcd_block() {
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int per = nb / 8, rem = nb % 8, x = b % 8, local = b / 8;
+  return x < rem ? (int64_t)x * (per + 1) + local : (int64_t)rem * (per + 1) + (int64_t)(x - rem) * per + local;
+}
+
 __device__ __forceinline__ Lane pose_lane(int64_t n) {
   const int lane = threadIdx.x & 63;
   Lane l;
-  const int64_t i = (int64_t)blockIdx.x * kPosesPerBlock + (threadIdx.x >> 6) * kPosesPerWave + lane / 6;
+  const int64_t i = xcd_block() * kPosesPerBlock + (threadIdx.x >> 6) * kPosesPerWave + lane / 6;
   l.on = lane < 6 * kPosesPerWave && i < n;
   l.i = l.on ? i : 0;
   l.a = lane % 6;
@@ -372,11 +390,11 @@ __device__ __forceinline__ double total(const Dev& d, int k) {
   return d.inline_sums ? partial_sum(red_arr(d, k), d.red_nb) : d.scal[k];
 }
 
-// row a of (M v) for the pose of this lane group
-__device__ __forceinline__ double apply6(const double* M, const Lane& l, double v) {
+// row a of (M v) for the pose of this lane group, M symmetric (upper triangle)
+__device__ __forceinline__ double apply_sym6(const double* M, const Lane& l, double v) {
   double s = 0.0;
 #pragma unroll
-  for (int b = 0; b < 6; ++b) s += M[6 * l.a + b] * __shfl(v, l.base + b, 64);
+  for (int b = 0; b < 6; ++b) s += M[sym_idx(l.a, b)] * __shfl(v, l.base + b, 64);
   return s;
 }
 
@@ -396,7 +414,7 @@ __global__ __launch_bounds__(256) void k_pcg_init(Dev d) {
   const Lane l = pose_lane(d.n);
   const int64_t e = 6 * l.i + l.a;
   const double b = (l.on && l.i >= d.n_fixed) ? -d.g[e] : 0.0;
-  const double z = apply6(d.Minv + 36 * l.i, l, b);
+  const double z = apply_sym6(d.Minv + kSymVals * l.i, l, b);
   double rr = 0.0, rz = 0.0;
   if (l.on) {
     d.x[e] = 0.0;
@@ -419,6 +437,21 @@ __global__ __launch_bounds__(256) void k_pcg_init(Dev d) {
   }
 }
 
+// Entry of the compact H_ij that multiplies z_other[b] in row a of this
+// pose's product: side 0 (this pose is the edge's i) takes row a of H_ij,
+// side 1 (it is the edge's j) row a of H_ij^T.  With H_ij = [[M, N], [0, -w I]]
+// held as M (0..8), N (9..17), -w (18), 0 (19):
+//   side 0, a < 3: M[a][b] (b < 3), N[a][b-3];   a >= 3: -w if b == a
+//   side 1, a < 3: M[b][a] (b < 3), 0;           a >= 3: N[b][a-3] (b < 3), -w if b == a
+__device__ __forceinline__ int coup_idx(int side, int a, int b) {
+  if (side == 0) {
+    if (a < 3) return b < 3 ? 3 * a + b : 9 + 3 * a + (b - 3);
+    return b == a ? 18 : 19;
+  }
+  if (a < 3) return b < 3 ? 3 * b + a : 19;
+  return b < 3 ? 9 + 3 * b + (a - 3) : (b == a ? 18 : 19);
+}
+
 __global__ __launch_bounds__(256) void k_pcg_a(Dev d, int it) {
   __shared__ double s_buf[4];
   if (d.pcg->done) return;
@@ -428,7 +461,7 @@ __global__ __launch_bounds__(256) void k_pcg_a(Dev d, int it) {
   const double zi = d.z[e];
   double hrow[6];
 #pragma unroll
-  for (int b = 0; b < 6; ++b) hrow[b] = d.Hdd[36 * l.i + 6 * l.a + b];
+  for (int b = 0; b < 6; ++b) hrow[b] = d.Hdd[kSymVals * l.i + sym_idx(l.a, b)];
   const bool free_pose = l.on && l.i >= d.n_fixed;
   const int h0 = d.half_ptr[l.i], h1 = free_pose ? d.half_ptr[l.i + 1] : h0;
   const double pe = d.p[e], qe = d.q[e];
@@ -458,16 +491,12 @@ __global__ __launch_bounds__(256) void k_pcg_a(Dev d, int it) {
     double hv[4][6], zv[4][6];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const double* Ho = d.Ho + 36 * (int64_t)(nb[k].x >> 1);
+      const double* Hc = d.Hc + kCoupVals * (int64_t)(nb[k].x >> 1);
       const double* zo = d.z + 6 * (int64_t)nb[k].y;
-      // side 0 (this pose is the edge's i): row a of H_ij against z_j;
-      // side 1 (it is the edge's j): column a of H_ij against z_i
-      const int side = nb[k].x & 1;
-      const int stride = side ? 6 : 1, first = side ? l.a : 6 * l.a;
       const bool live = h + k < h1;
 #pragma unroll
       for (int b = 0; b < 6; ++b) {
-        const double v = Ho[first + stride * b];
+        const double v = Hc[coup_idx(nb[k].x & 1, l.a, b)];
         hv[k][b] = live ? v : 0.0;
         zv[k][b] = zo[b];
       }
@@ -500,7 +529,7 @@ __global__ __launch_bounds__(256) void k_pcg_b(Dev d, int it) {
   const int64_t e = 6 * l.i + l.a;
   double mrow[6];
 #pragma unroll
-  for (int b = 0; b < 6; ++b) mrow[b] = d.Minv[36 * l.i + 6 * l.a + b];
+  for (int b = 0; b < 6; ++b) mrow[b] = d.Minv[kSymVals * l.i + sym_idx(l.a, b)];
   const double xe = d.x[e], re = d.rv[e], pe = d.p[e], qe = d.q[e];
   const double pq = total(d, kPQ);
   if (!(pq > 0.0) || !isfinite(pq)) {
@@ -643,6 +672,16 @@ __global__ void k_validate(Dev d, const double* meas, int* flags) {
       if (!isfinite(d.poses[6 * k + c])) flags[0] = 1;
 }
 
+__global__ void k_expand_coupling(Dev d, double* out) {
+  const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (e >= d.m) return;
+  const double* Hc = d.Hc + kCoupVals * e;
+#pragma unroll
+  for (int a = 0; a < 6; ++a)
+#pragma unroll
+    for (int b = 0; b < 6; ++b) out[36 * e + 6 * a + b] = Hc[coup_idx(0, a, b)];
+}
+
 template <typename... KArgs, typename... Args>
 void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
   DispatchEvents& ev = dispatch_events();
@@ -694,6 +733,9 @@ void launch_cost(const Dev& d, const double* tab, hipStream_t s) {
   launch(k_cost, dim3(edge_blocks(d.m)), dim3(256), s, d, tab);
 }
 void launch_cost_final(const Dev& d, hipStream_t s) { launch(k_cost_final, dim3(1), dim3(256), s, d); }
+void launch_expand_coupling(const Dev& d, double* out, hipStream_t s) {
+  if (d.m > 0) launch(k_expand_coupling, dim3(blocks(d.m, 256)), dim3(256), s, d, out);
+}
 void launch_validate(const Dev& d, const double* meas, int* flags, hipStream_t s) {
   const int64_t n = std::max<int64_t>(std::max<int64_t>(d.n, d.m), 1);
   launch(k_validate, dim3(blocks(n, 256)), dim3(256), s, d, meas, flags);
