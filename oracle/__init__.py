@@ -100,6 +100,7 @@ def lib():
         L.orc_get_cost.restype = d
         L.orc_schur_matvec.argtypes = [vp, dp, dp]
         L.orc_explicit_S.argtypes = [vp, dp]
+        L.orc_covariance.argtypes = [vp, dp]
         L.orc_project_one.argtypes = [dp, dp, dp, C.c_int, d, dp, dp, dp, dp, dp]
         L.orc_retract_camera.argtypes = [dp, dp, dp]
         L.orc_so3_exp.argtypes = [dp, dp]
@@ -224,6 +225,13 @@ class Problem:
         self._check(lib().orc_backward(self.h, _p(gc), _p(gp), _p(out), C.byref(it), C.byref(rel)),
                     "backward")
         return out.reshape(-1, 2), it.value, rel.value
+
+    def covariance(self):
+        """Camera marginal covariance: the 9x9 diagonal blocks of S~^-1 at the
+        current parameters and lambda (n_cams x 9 x 9)."""
+        out = np.empty(81 * self.nc)
+        self._check(lib().orc_covariance(self.h, _p(out)), "covariance")
+        return out.reshape(-1, 9, 9)
 
     def backsub(self):
         self._check(lib().orc_backsub(self.h), "backsub")

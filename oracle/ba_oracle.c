@@ -759,6 +759,43 @@ int orc_dense_schur_solve(orc_problem* h) {
   return ORC_OK;
 }
 
+/* Camera marginal covariance ([NSLAM] sec. 3.2, the dense reference step: the
+ * Cholesky factor of S that gives the camera update also gives S^-1 by solving
+ * against the identity, column by column; S is never inverted directly).
+ * Computed at the current parameters and lambda: linearise, damp, form S~ =
+ * B~ - E C~^-1 E^T, factor it, and solve S~ x = e_k for every k.  out receives
+ * the 9x9 diagonal blocks of S~^-1 (nc x 81, row-major): each camera's
+ * marginal covariance under the damped Gauss-Newton model. */
+int orc_covariance(orc_problem* h, double* out) {
+  int rc = orc_linearize(h);
+  if (rc) return rc;
+  if ((rc = orc_damp(h))) return rc;
+  const int64_t n = 9 * h->nc;
+  double* S = (double*)malloc(sizeof(double) * (size_t)(n * n));
+  double* e = (double*)calloc((size_t)n, sizeof(double));
+  double* x = (double*)malloc(sizeof(double) * (size_t)n);
+  if (!S || !e || !x) {
+    free(S);
+    free(e);
+    free(x);
+    return ORC_ERR_ALLOC;
+  }
+  orc_explicit_S(h, S);
+  rc = chol(S, (int)n) ? ORC_ERR_NOT_SPD : ORC_OK;
+  for (int64_t k = 0; k < n && rc == ORC_OK; k++) {
+    e[k] = 1.0;
+    chol_solve(S, (int)n, e, x);   /* column k of S~^-1 */
+    e[k] = 0.0;
+    const int64_t j = k / 9;
+    const int b = (int)(k % 9);
+    for (int a = 0; a < 9; a++) out[81 * j + 9 * a + b] = x[9 * j + a];
+  }
+  free(S);
+  free(e);
+  free(x);
+  return rc;
+}
+
 /* Point back-substitution, [NSLAM] sec. 3.2 eq. (1): dp = C~^-1 (b_d - E^T dc)
  * with b_d = -g_p. */
 int orc_backsub(orc_problem* h) {

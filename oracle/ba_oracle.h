@@ -81,6 +81,9 @@ int orc_damp(orc_problem* h);
 int orc_schur(orc_problem* h);
 int orc_pcg(orc_problem* h, int max_iters, double rel_tol, int* iters, double* rel_res);
 int orc_dense_schur_solve(orc_problem* h);
+/* Camera marginal covariance: the 9x9 diagonal blocks of S~^-1 at the current
+ * parameters and lambda (out: nc x 81). */
+int orc_covariance(orc_problem* h, double* out);
 int orc_backsub(orc_problem* h);
 int orc_retract(orc_problem* h);
 int orc_cost_at(const orc_problem* h, const double* cams, const double* pts, double* cost);
