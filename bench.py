@@ -29,6 +29,12 @@ steps: a step is one implicit backward pass (linearise, Schur elimination
 with the parameter gradient as right-hand side, PCG, back-substitution,
 per-observation products), with the arrays resident on the device.
 
+``--workload covariance`` measures ba_covariance on the medium scene: a step
+is one camera marginal covariance evaluation (linearise, damp, eliminate the
+points, assemble and factor S~, form Z = L^-T by tiles with fp64 MFMA
+updates, each camera's 9x9 block of Z Z^T); the roofline refers to the fp64
+MFMA update of Z.
+
 ``--workload pgo`` measures libpgo, pose-graph optimisation: a step is one LM
 iteration (linearise the relative-pose edges, per-pose H and g sums, damping,
 PCG with 6 x 6 block-Jacobi, retraction, trial cost, accept/reject) of the
@@ -335,6 +341,99 @@ def main_schur_dense(args):
     print(json.dumps(out), flush=True)
 
 
+COV_METRIC = "camera covariance evaluations/s (fp64, 1 GPU); % of fp64 MFMA roofline"
+
+
+def cov_update_flops(n_cams):
+    """Algorithmic fp64 flops of one Z_ji -= Z_jk L_ik^T launch of the
+    covariance, averaged over the launches of one evaluation: after tile
+    column k, (k + 1) (T - k - 1) full 32 x 32 x 32 tile products (Z = L^-T
+    by tiles costs the n^3 / 3 of a triangular inverse)."""
+    T = -(-9 * n_cams // DS_TILE)
+    total, launches = 0, 0
+    for k in range(T):
+        tiles = (k + 1) * (T - k - 1)
+        if tiles:
+            total += 2 * DS_TILE ** 3 * tiles
+            launches += 1
+    return total // max(launches, 1)
+
+
+def cov_cpu_baseline(sc):
+    """The oracle as it stands (plain C, one thread): one covariance at the
+    initial state, S~ formed, factored and solved against the identity."""
+    import oracle
+    P = oracle.Problem.from_scene(sc, solver=1)
+    t0 = time.perf_counter()
+    P.covariance()
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "covariance evaluations/s", "cores": 1, "kind": "oracle",
+            "sample": f"one evaluation on the same scene ({len(sc['cams'])} cameras, S of order "
+                      f"{9 * len(sc['cams'])}), single-threaded C oracle, {dt:.1f} s"}
+
+
+def main_covariance(args):
+    import numpy as np
+    import torch
+    from nonlinear_least_squares_amd import ba
+    from synthetic import ba_scene, scene_summary
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    config = args.config or "medium"
+    sc = ba_scene(config)
+    n_obs, n_pts, n_cams = len(sc["obs_cam"]), len(sc["points"]), len(sc["cams"])
+    print(f"# {scene_summary(sc)}", file=sys.stderr, flush=True)
+    dense = dict(solver=ba.BA_SOLVER_DENSE_SCHUR)
+    warm = ba.Problem.from_scene(sc, **dense)
+    warm.profile()
+    for _ in range(max(args.warmup, 1)):
+        warm.covariance()
+    prof = warm.profile_get()
+    warm.close()
+    dominant = max(prof, key=lambda k: prof[k][1])
+    print(f"# warm-up kernel totals (launches, ms): {prof}", file=sys.stderr, flush=True)
+    P = ba.Problem.from_scene(sc, **dense)
+    P.profile([dominant], every=PROFILE_EVERY)
+    out = np.empty((n_cams, 9, 9))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        P.covariance(out)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    launches, kms = P.profile_get()[dominant]
+    value = args.steps / dt
+    roof = None
+    if launches:
+        avg_s = kms / launches / 1e3
+        roof = {"bound": None, "achieved": None, "peak": None, "unit": None, "frac": None,
+                "traffic": None, "kernel": dominant, "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches": launches}
+        fl = {"cov_update": cov_update_flops(n_cams),
+              "ds_update": schur_dense_update_flops(n_cams)}.get(dominant)
+        if fl:
+            ach = fl / avg_s / 1e12
+            roof.update({"bound": "mfma", "achieved": round(ach, 3), "peak": FP64_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / FP64_MFMA_PEAK_TFLOPS, 5),
+                         "algorithmic_flops_per_launch": fl})
+    res = {
+        "metric": COV_METRIC, "value": round(value, 3), "unit": "covariance evaluations/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * dt / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{config} BA camera marginal covariance (linearise, damp, "
+                               f"eliminate the points, assemble and factor S~ of order "
+                               f"{9 * n_cams}, Z = L^-T by tiles, 9x9 blocks of Z Z^T): "
+                               f"{n_cams} cameras, {n_pts} points, {n_obs} observations",
+                   "n_obs": n_obs, "n_pts": n_pts, "n_cams": n_cams},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cov_cpu_baseline(sc)
+    print(json.dumps(res), flush=True)
+
+
 BACKWARD_METRIC = "implicit backward passes/s (fp64, 1 GPU); % of HBM roofline"
 
 
@@ -552,9 +651,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default=None,
                     help="scene (default: large for ba and backward, medium for "
-                         "schur-dense, sphere for pgo)")
-    ap.add_argument("--workload", choices=["ba", "dense", "schur-dense", "backward", "pgo"],
-                    default="ba")
+                         "schur-dense and covariance, sphere for pgo)")
+    ap.add_argument("--workload", choices=["ba", "dense", "schur-dense", "backward", "pgo",
+                                           "covariance"], default="ba")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (byte-counter calibration)")
@@ -573,6 +672,8 @@ def main():
         return main_backward(args)
     if args.workload == "pgo":
         return main_pgo(args)
+    if args.workload == "covariance":
+        return main_covariance(args)
     args.config = args.config or "large"
 
     import torch

@@ -168,6 +168,22 @@ int ba_cost(ba_problem* h, double* cost_out);
 int ba_backward(ba_problem* h, const double* grad_cams, const double* grad_points, double* grad_uv,
                 int* pcg_iters);
 
+/* Camera marginal covariance, as in the NeRF-SLAM notes' dense step (sec.
+ * 3.2): the Cholesky factor of the reduced camera matrix S gives S^-1 by
+ * solves against the identity; S is never inverted directly.  At the current
+ * parameters and lambda this linearises, damps, eliminates the points,
+ * assembles and factors S~ = L L^T (as an LM step with the dense solver
+ * would), forms Z = L^-T by 32 x 32 tiles (fp64 MFMA updates) and writes each
+ * camera's 9x9 diagonal block of S~^-1 = Z Z^T to cov_out (n_cams x 81,
+ * row-major; host memory for BA_MEM_HOST handles, device memory for
+ * BA_MEM_DEVICE ones).  The blocks are the cameras' marginal covariances
+ * under the damped Gauss-Newton model (S~ includes lambda's damping; at
+ * lambda = 0 the reduced matrix of a BA problem is singular along its gauge).
+ * Needs opts.solver == BA_SOLVER_DENSE_SCHUR, whose storage holds the factor
+ * (BA_ERR_ARG otherwise); BA_ERR_NOT_SPD if S~ fails to factor.  Parameters,
+ * lambda and cost are unchanged. */
+int ba_covariance(ba_problem* h, double* cov_out);
+
 /* Current parameters to caller-owned host buffers (n_cams x 9, n_pts x 3);
  * either pointer may be NULL. */
 int ba_get_params(ba_problem* h, double* cams_out, double* points_out);
@@ -256,6 +272,10 @@ enum {
   BA_K_DS_PANEL,     /* dense solver: diagonal tile factor and tile-row solves      */
   BA_K_DS_UPDATE,    /* dense solver: trailing update (fp64 MFMA)                  */
   BA_K_DS_BACKSOLVE, /* dense solver: L^T dc = L^-1 rhs                            */
+  BA_K_COV_INIT,     /* covariance: Z = I in the upper tiles of S                  */
+  BA_K_COV_PANEL,    /* covariance: tiles of Z = L^-T solved against L_kk^T         */
+  BA_K_COV_UPDATE,   /* covariance: Z_ji -= Z_jk L_ik^T (fp64 MFMA)                 */
+  BA_K_COV_BLOCKS,   /* covariance: per camera, the 9x9 block of Z Z^T              */
   BA_K_NUM
 };
 

@@ -30,7 +30,8 @@ DBG_SHAPE = {"r": (-1, 2), "Jc": (-1, 2, 9), "Jp": (-1, 2, 3), "B": (-1, 9, 9), 
              "cams_trial": (-1, 9), "points_trial": (-1, 3)}
 KERNELS = ["lin_pt", "lin_cam", "damp_pt", "schur_cam", "precond", "pcg_init", "pcg_pt",
            "pcg_cam", "pcg_q", "pcg_xr", "backsub", "retract", "cost", "ds_runs", "ds_fill",
-           "ds_assemble", "ds_panel", "ds_update", "ds_backsolve"]
+           "ds_assemble", "ds_panel", "ds_update", "ds_backsolve", "cov_init", "cov_panel",
+           "cov_update", "cov_blocks"]
 
 
 class ba_options(C.Structure):
@@ -90,6 +91,7 @@ SIGNATURES = {
     "ba_cost": (C.c_int, [C.c_void_p, C.POINTER(C.c_double)]),
     "ba_backward": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.POINTER(C.c_int)]),
+    "ba_covariance": (C.c_int, [C.c_void_p, C.c_void_p]),
     "ba_get_params": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "ba_set_params": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "ba_get_state": (C.c_int, [C.c_void_p, C.POINTER(ba_state)]),
@@ -227,6 +229,17 @@ class Problem:
         _check(lib().ba_backward(self.h, pc, pp, po, C.byref(it)), "ba_backward")
         del kc, kp
         return ko, it.value
+
+    def covariance(self, out=None):
+        """Camera marginal covariance: each camera's 9x9 diagonal block of the
+        inverse of the damped reduced camera matrix at the current parameters
+        and lambda (ba_covariance; needs the dense solver).  ``out``: a device
+        tensor of n_cams x 81 doubles for device handles."""
+        if out is None:
+            out = np.empty((self.n_cams, 9, 9))
+        po, ko = _ptr(out, np.float64)
+        _check(lib().ba_covariance(self.h, po), "ba_covariance")
+        return ko
 
     def get_params(self):
         cams = np.empty((self.n_cams, 9))

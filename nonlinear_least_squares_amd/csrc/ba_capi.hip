@@ -105,7 +105,8 @@ struct ba_problem {
   int ds_ld = 0, ds_T = 0, ds_nruns = 0, ds_nblk = 0;
   int32_t *ds_run = nullptr, *ds_blk_ptr = nullptr;
   int2 *ds_blk = nullptr, *ds_pair = nullptr;
-  double *ds_F = nullptr, *ds_S = nullptr, *ds_diag = nullptr, *ds_diagT = nullptr, *ds_dinv = nullptr;
+  double *ds_F = nullptr, *ds_S = nullptr, *ds_diag = nullptr, *ds_diagT = nullptr, *ds_dinv = nullptr,
+         *ds_cov = nullptr;
   // work arrays
   double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
          *gc = nullptr, *lin_part = nullptr;
@@ -350,9 +351,9 @@ int stage_pcg(ba_problem* h) {
   return BA_OK;
 }
 
-// Dense solve of S dc = rhs: explicit S, Cholesky by tile columns with the
-// rhs as an extra row, back-substitution.
-int stage_dense(ba_problem* h) {
+// Explicit S and its Cholesky factorisation by tile columns, the rhs as an
+// extra row (it ends as L^-1 rhs).
+int stage_dense_factor(ba_problem* h) {
   Dev d = make_dev(h);
   hipStream_t s = h->stream;
   TIMED(BA_K_DS_RUNS, -1, launch_ds_runs(d, s));
@@ -363,7 +364,15 @@ int stage_dense(ba_problem* h) {
     TIMED(BA_K_DS_PANEL, -1, launch_ds_panel(d, k, s));
     TIMED(BA_K_DS_UPDATE, -1, launch_ds_update(d, k, s));
   }
-  TIMED(BA_K_DS_BACKSOLVE, -1, launch_ds_backsolve(d, s));
+  HIPC(hipGetLastError());
+  return BA_OK;
+}
+
+// Dense solve of S dc = rhs: factorisation, then back-substitution.
+int stage_dense(ba_problem* h) {
+  CHECK_RC(stage_dense_factor(h));
+  Dev d = make_dev(h);
+  TIMED(BA_K_DS_BACKSOLVE, -1, launch_ds_backsolve(d, h->stream));
   HIPC(hipGetLastError());
   return BA_OK;
 }
@@ -777,6 +786,7 @@ int plan_dense(ba_problem* h) {
   A.add(h->ds_diag, (int64_t)h->ds_T * kt * kt);
   A.add(h->ds_diagT, (int64_t)h->ds_T * kt * kt);
   A.add(h->ds_dinv, (int64_t)h->ds_ld);
+  A.add(h->ds_cov, 81 * nc);
   CHECK_RC(A.commit());
   HIPC(hipMemcpyAsync(h->ds_run, run.data(), sizeof(int32_t) * run.size(), hipMemcpyHostToDevice, s));
   HIPC(hipMemcpyAsync(h->ds_blk, blk.data(), sizeof(int2) * blk.size(), hipMemcpyHostToDevice, s));
@@ -821,7 +831,8 @@ const char* kKernelNames[BA_K_NUM] = {"lin_pt",   "lin_cam",  "damp_pt",     "sc
                                       "precond",  "pcg_init", "pcg_pt",      "pcg_cam",
                                       "pcg_q",    "pcg_xr",   "backsub",     "retract",
                                       "cost",     "ds_runs",  "ds_fill",     "ds_assemble",
-                                      "ds_panel", "ds_update", "ds_backsolve"};
+                                      "ds_panel", "ds_update", "ds_backsolve", "cov_init",
+                                      "cov_panel", "cov_update", "cov_blocks"};
 
 }  // namespace
 
@@ -980,6 +991,34 @@ int ba_backward(ba_problem* h, const double* grad_cams, const double* grad_point
   if (h->prof_on) CHECK_RC(prof_collect(h, st.iters));
   if (flags[1]) return fail(BA_ERR_NOT_SPD, "a damped block is not positive definite");
   if (pcg_iters) *pcg_iters = st.iters;
+  return BA_OK;
+}
+
+int ba_covariance(ba_problem* h, double* cov_out) {
+  if (!h || !cov_out) return fail(BA_ERR_ARG, "bad arguments");
+  if (h->opt.solver != BA_SOLVER_DENSE_SCHUR)
+    return fail(BA_ERR_ARG, "the covariance needs the dense solver (opts.solver = BA_SOLVER_DENSE_SCHUR)");
+  const int64_t nc = h->nc;
+  CHECK_RC(stage_linearize(h));
+  h->linearized = 1;
+  CHECK_RC(stage_schur(h));
+  CHECK_RC(stage_dense_factor(h));
+  Dev d = make_dev(h);
+  hipStream_t s = h->stream;
+  TIMED(BA_K_COV_INIT, -1, launch_cov_init(d, s));
+  for (int k = 0; k < h->ds_T; ++k) {
+    TIMED(BA_K_COV_PANEL, -1, launch_cov_panel(d, k, s));
+    TIMED(BA_K_COV_UPDATE, -1, launch_cov_update(d, k, s));
+  }
+  const bool dev = h->opt.mem == BA_MEM_DEVICE;
+  TIMED(BA_K_COV_BLOCKS, -1, launch_cov_blocks(d, dev ? cov_out : h->ds_cov, nc, s));
+  HIPC(hipGetLastError());
+  if (!dev) HIPC(hipMemcpyAsync(cov_out, h->ds_cov, sizeof(double) * 81 * nc, hipMemcpyDeviceToHost, s));
+  int flags[2] = {0, 0};
+  HIPC(hipMemcpyAsync(flags, h->flags, sizeof(flags), hipMemcpyDeviceToHost, s));
+  HIPC(hipStreamSynchronize(s));
+  if (h->prof_on) CHECK_RC(prof_collect(h, 0));
+  if (flags[1]) return fail(BA_ERR_NOT_SPD, "the damped system is not positive definite");
   return BA_OK;
 }
 

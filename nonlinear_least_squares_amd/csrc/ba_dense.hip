@@ -222,12 +222,11 @@ __global__ __launch_bounds__(64) void k_ds_diag0(Dev d) {
 // row i = k + 1 .. T (T: the rhs tile row) solves L_ik L_kk^T = A_ik in place,
 // lane r taking row r.  The factor's columns and pivot reciprocals are staged
 // in LDS and read at wavefront-uniform addresses (broadcasts).
-__global__ __launch_bounds__(64) void k_ds_panel(Dev d, int k) {
-  __shared__ double s_l[kT * kT + kT];
-  const int i = k + 1 + blockIdx.x;
-  const int r = threadIdx.x & (kT - 1);
-  const int64_t ld = d.ds_ld;
-  double* row = d.ds_S + (int64_t)(kT * i + r) * ld + kT * k;
+// Row r (lane r & 31) of one tile at `row` (stride ld) solved in place
+// against the factored diagonal tile k, X L_kk^T = A: the factor's columns and
+// pivot reciprocals are staged in LDS (s_l, kT * kT + kT doubles) and read at
+// wavefront-uniform addresses (broadcasts).
+__device__ __forceinline__ void panel_solve(const Dev& d, int k, double* row, double* s_l) {
   const double* LT = d.ds_diagT + (int64_t)k * kT * kT;
   double b[kT];
 #pragma unroll
@@ -250,45 +249,34 @@ __global__ __launch_bounds__(64) void k_ds_panel(Dev d, int k) {
   for (int c = 0; c < kT; ++c) row[c] = b[c];
 }
 
-// Trailing update after tile column k: one wavefront per tile (i, j) with
-// k < j <= i < T, then the rhs tile row (T, j).  The wavefront of tile
-// (k + 1, k + 1) then factors that tile for the next panel.  A_ij -= L_ik L_jk^T as 2 x 2
-// MFMA tiles of 16 x 16 over K = 32 in steps of 4.  Operand layout of
-// v_mfma_f64_16x16x4_f64 (lane l): A(m, kk) with m = l % 16, kk = l / 16;
-// B(kk, n) with n = l % 16; accumulator element v (0..3) is row 4 v + l / 16
-// of column l % 16.
-__global__ __launch_bounds__(64) void k_ds_update(Dev d, int k) {
-  const int m = d.ds_T - k - 1;          // trailing tile columns
-  const int tri = m * (m + 1) / 2;
-  const int id = blockIdx.x;
-  int i, j;
-  if (id < tri) {
-    int ii = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
-    while ((ii + 1) * (ii + 2) / 2 <= id) ++ii;
-    while (ii * (ii + 1) / 2 > id) --ii;
-    i = k + 1 + ii;
-    j = k + 1 + (id - ii * (ii + 1) / 2);
-  } else {
-    i = d.ds_T;
-    j = k + 1 + (id - tri);
-  }
+// Tile column k, its diagonal tile already factored: one wavefront per tile
+// row i = k + 1 .. T (T: the rhs tile row) solves L_ik L_kk^T = A_ik in place,
+// lane r taking row r.
+__global__ __launch_bounds__(64) void k_ds_panel(Dev d, int k) {
+  __shared__ double s_l[kT * kT + kT];
+  const int i = k + 1 + blockIdx.x;
+  const int r = threadIdx.x & (kT - 1);
+  panel_solve(d, k, d.ds_S + (int64_t)(kT * i + r) * d.ds_ld + kT * k, s_l);
+}
+
+// C -= A B^T for 32 x 32 tiles of S (leading dimension ld) as 2 x 2 MFMA
+// tiles of 16 x 16 over K = 32 in steps of 4; the accumulators are left in acc.
+// Operand layout of v_mfma_f64_16x16x4_f64 (lane l): A(m, kk) with m = l % 16,
+// kk = l / 16; B(kk, n) with n = l % 16; accumulator element v (0..3) is row
+// 4 v + l / 16 of column l % 16.
+__device__ __forceinline__ void tile_sub_abt(double* C, const double* A, const double* B,
+                                             int64_t ld, v4d (&acc)[2][2]) {
   const int l = threadIdx.x;
   const int lr = l & 15, lk = l >> 4;
-  const int64_t ld = d.ds_ld;
-  double* S = d.ds_S;
-  const double* Li = S + (int64_t)(kT * i) * ld + kT * k;
-  const double* Lj = S + (int64_t)(kT * j) * ld + kT * k;
-  double* C = S + (int64_t)(kT * i) * ld + kT * j;
   double av[2][8], bv[2][8];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      av[h][s] = -Li[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
-      bv[h][s] = Lj[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
+      av[h][s] = -A[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
+      bv[h][s] = B[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
     }
   }
-  v4d acc[2][2];
 #pragma unroll
   for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
@@ -308,6 +296,33 @@ __global__ __launch_bounds__(64) void k_ds_update(Dev d, int k) {
     for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
       for (int v = 0; v < 4; ++v) C[(int64_t)(16 * mh + 4 * v + lk) * ld + 16 * nh + lr] = acc[mh][nh][v];
+}
+
+// Trailing update after tile column k: one wavefront per tile (i, j) with
+// k < j <= i < T, then the rhs tile row (T, j): A_ij -= L_ik L_jk^T.  The
+// wavefront of tile (k + 1, k + 1) then factors that tile for the next panel.
+__global__ __launch_bounds__(64) void k_ds_update(Dev d, int k) {
+  const int m = d.ds_T - k - 1;          // trailing tile columns
+  const int tri = m * (m + 1) / 2;
+  const int id = blockIdx.x;
+  int i, j;
+  if (id < tri) {
+    int ii = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
+    while ((ii + 1) * (ii + 2) / 2 <= id) ++ii;
+    while (ii * (ii + 1) / 2 > id) --ii;
+    i = k + 1 + ii;
+    j = k + 1 + (id - ii * (ii + 1) / 2);
+  } else {
+    i = d.ds_T;
+    j = k + 1 + (id - tri);
+  }
+  const int l = threadIdx.x;
+  const int lr = l & 15, lk = l >> 4;
+  const int64_t ld = d.ds_ld;
+  double* S = d.ds_S;
+  v4d acc[2][2];
+  tile_sub_abt(S + (int64_t)(kT * i) * ld + kT * j, S + (int64_t)(kT * i) * ld + kT * k,
+               S + (int64_t)(kT * j) * ld + kT * k, ld, acc);
   if (id == 0) {
     // tile (k + 1, k + 1) is final now: factor it for the next panel, its
     // rows passed through LDS
@@ -320,6 +335,95 @@ __global__ __launch_bounds__(64) void k_ds_update(Dev d, int k) {
         for (int v = 0; v < 4; ++v) s_t[(16 * mh + 4 * v + lk) * kT + 16 * nh + lr] = acc[mh][nh][v];
     __syncthreads();
     factor_diag_tile(d, k + 1, s_t, kT);
+  }
+}
+
+// ---- camera marginal covariance: blocks of S^-1 = L^-T L^-1 ---------------
+//
+// After the factorisation, Z = L^-T (upper triangular) is formed by tiles in
+// the upper triangle of S, which the factorisation no longer reads (its
+// diagonal tiles live in ds_diag): Z L^T = I gives, tile by tile,
+//   Z_jk L_kk^T = delta_jk I - sum_{m < k} Z_jm L_km^T,
+// so, right-looking over tile columns k: a panel solves the tiles Z_jk,
+// j <= k, against L_kk^T (the factorisation's panel solve), and an update
+// takes them out of the later columns, Z_ji -= Z_jk L_ik^T for j <= k < i
+// (the factorisation's MFMA tile product).  Each camera's 9x9 block of
+// S^-1 = Z Z^T is then the 45 dot products of its 9 rows of Z.
+
+// Z = I in the upper tiles (j <= k) of S; the lower tiles hold L.
+__global__ void k_cov_init(Dev d) {
+  const int64_t ld = d.ds_ld;
+  const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (e >= ld * ld) return;
+  const int64_t row = e / ld, col = e - row * ld;
+  if (col / kT >= row / kT) d.ds_S[e] = row == col ? 1.0 : 0.0;
+}
+
+// Tiles Z_jk, j = 0 .. k, solved against L_kk^T, one wavefront each.
+__global__ __launch_bounds__(64) void k_cov_panel(Dev d, int k) {
+  __shared__ double s_l[kT * kT + kT];
+  const int j = blockIdx.x;
+  const int r = threadIdx.x & (kT - 1);
+  panel_solve(d, k, d.ds_S + (int64_t)(kT * j + r) * d.ds_ld + kT * k, s_l);
+}
+
+// Z_ji -= Z_jk L_ik^T for every j <= k < i < T, one wavefront per tile.
+__global__ __launch_bounds__(64) void k_cov_update(Dev d, int k) {
+  const int id = blockIdx.x;
+  const int j = id % (k + 1), i = k + 1 + id / (k + 1);
+  const int64_t ld = d.ds_ld;
+  double* S = d.ds_S;
+  v4d acc[2][2];
+  tile_sub_abt(S + (int64_t)(kT * j) * ld + kT * i, S + (int64_t)(kT * j) * ld + kT * k,
+               S + (int64_t)(kT * i) * ld + kT * k, ld, acc);
+}
+
+// One workgroup per camera c: rows r_a = 9 c + a of Z (a < 9), each nonzero
+// from its own tile's first column on; cov_c[a][b] = sum over columns of
+// Z[r_a] Z[r_b].  Thread t takes columns t, t + 256, ...; the 45 sums are
+// reduced across the wavefront, then over the four wavefronts in order.
+__global__ __launch_bounds__(256) void k_cov_blocks(Dev d, double* out) {
+  __shared__ double s_part[4][45];
+  const int c = blockIdx.x;
+  const int64_t ld = d.ds_ld, n = d.ds_n;
+  const int64_t r0 = 9 * (int64_t)c;
+  const double* Z = d.ds_S;
+  int64_t start[9];
+#pragma unroll
+  for (int a = 0; a < 9; ++a) start[a] = (r0 + a) / kT * kT;
+  double acc[45];
+#pragma unroll
+  for (int q = 0; q < 45; ++q) acc[q] = 0.0;
+  for (int64_t col = start[0] + threadIdx.x; col < n; col += 256) {
+    double z[9];
+#pragma unroll
+    for (int a = 0; a < 9; ++a) z[a] = col >= start[a] ? Z[(r0 + a) * ld + col] : 0.0;
+    int q = 0;
+#pragma unroll
+    for (int a = 0; a < 9; ++a)
+#pragma unroll
+      for (int b = a; b < 9; ++b, ++q) acc[q] += z[a] * z[b];
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 45; ++q) {
+    double v = acc[q];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) s_part[w][q] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 45) {
+    const int q = threadIdx.x;
+    const double v = ((s_part[0][q] + s_part[1][q]) + s_part[2][q]) + s_part[3][q];
+    int a = 0, rem = q;
+    while (rem >= 9 - a) {
+      rem -= 9 - a;
+      ++a;
+    }
+    const int b = a + rem;
+    out[81 * (int64_t)c + 9 * a + b] = v;
+    out[81 * (int64_t)c + 9 * b + a] = v;
   }
 }
 
@@ -389,6 +493,22 @@ __global__ __launch_bounds__(kSolveThreads) void k_ds_backsolve(Dev d) {
 }  // namespace
 
 int ds_tile() { return kT; }
+
+void launch_cov_init(const Dev& d, hipStream_t s) {
+  const int64_t n = (int64_t)d.ds_ld * d.ds_ld;
+  launch_timed(k_cov_init, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, d);
+}
+void launch_cov_panel(const Dev& d, int k, hipStream_t s) {
+  launch_timed(k_cov_panel, dim3(k + 1), dim3(64), s, 0u, d, k);
+}
+int cov_update_tiles(const Dev& d, int k) { return (k + 1) * (d.ds_T - k - 1); }
+void launch_cov_update(const Dev& d, int k, hipStream_t s) {
+  const int n = cov_update_tiles(d, k);
+  if (n > 0) launch_timed(k_cov_update, dim3(n), dim3(64), s, 0u, d, k);
+}
+void launch_cov_blocks(const Dev& d, double* out, int64_t n_cams, hipStream_t s) {
+  if (n_cams > 0) launch_timed(k_cov_blocks, dim3((unsigned)n_cams), dim3(256), s, 0u, d, out);
+}
 
 void launch_ds_runs(const Dev& d, hipStream_t s) {
   if (d.ds_nruns > 0) launch_timed(k_ds_runs, dim3((d.ds_nruns + 255) / 256), dim3(256), s, 0u, d);

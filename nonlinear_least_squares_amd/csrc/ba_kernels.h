@@ -187,6 +187,12 @@ int ds_update_tiles(const Dev& d, int k);
 void launch_ds_update(const Dev& d, int k, hipStream_t s);
 hipError_t ds_backsolve_limit(int ld);
 void launch_ds_backsolve(const Dev& d, hipStream_t s);
+// Camera marginal covariance from the dense factor (ba_dense.hip).
+void launch_cov_init(const Dev& d, hipStream_t s);
+void launch_cov_panel(const Dev& d, int k, hipStream_t s);
+int cov_update_tiles(const Dev& d, int k);
+void launch_cov_update(const Dev& d, int k, hipStream_t s);
+void launch_cov_blocks(const Dev& d, double* out, int64_t n_cams, hipStream_t s);
 
 // Implicit backward: a <- -a; per observation psi'(r) (Jc x_cam + Jp dp_pt) to
 // out[2 perm_cam[s] ..], s the camera-order slot.
