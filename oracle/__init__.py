@@ -43,17 +43,22 @@ class Opts(C.Structure):
                 ("lambda_up", C.c_double), ("lambda_down", C.c_double),
                 ("lambda_min", C.c_double), ("lambda_max", C.c_double),
                 ("diag_floor", C.c_double), ("pcg_max_iters", C.c_int),
-                ("pcg_rel_tol", C.c_double), ("solver", C.c_int)]
+                ("pcg_rel_tol", C.c_double), ("solver", C.c_int), ("strategy", C.c_int),
+                ("dl_radius0", C.c_double), ("dl_gn_damping", C.c_double)]
 
 
 class StepInfo(C.Structure):
     _fields_ = [("cost_before", C.c_double), ("cost_after", C.c_double), ("lambda_", C.c_double),
-                ("pcg_rel_res", C.c_double), ("accepted", C.c_int), ("pcg_iters", C.c_int)]
+                ("pcg_rel_res", C.c_double), ("accepted", C.c_int), ("pcg_iters", C.c_int),
+                ("radius", C.c_double), ("gain_ratio", C.c_double), ("step_norm", C.c_double),
+                ("step_kind", C.c_int)]
 
     def as_dict(self):
         return dict(cost_before=self.cost_before, cost_after=self.cost_after,
                     lam=self.lambda_, accepted=self.accepted, pcg_iters=self.pcg_iters,
-                    pcg_rel_res=self.pcg_rel_res)
+                    pcg_rel_res=self.pcg_rel_res, radius=self.radius,
+                    gain_ratio=self.gain_ratio, step_norm=self.step_norm,
+                    step_kind=self.step_kind)
 
 
 def build(force=True):
@@ -101,6 +106,9 @@ def lib():
         L.orc_schur_matvec.argtypes = [vp, dp, dp]
         L.orc_explicit_S.argtypes = [vp, dp]
         L.orc_covariance.argtypes = [vp, dp]
+        L.orc_get_radius.argtypes = [vp]
+        L.orc_get_radius.restype = d
+        L.orc_set_radius.argtypes = [vp, d]
         L.orc_project_one.argtypes = [dp, dp, dp, C.c_int, d, dp, dp, dp, dp, dp]
         L.orc_retract_camera.argtypes = [dp, dp, dp]
         L.orc_so3_exp.argtypes = [dp, dp]
@@ -249,6 +257,14 @@ class Problem:
     @property
     def cost(self):
         return lib().orc_get_cost(self.h)
+
+    @property
+    def radius(self):
+        return lib().orc_get_radius(self.h)
+
+    @radius.setter
+    def radius(self, v):
+        lib().orc_set_radius(self.h, v)
 
     @property
     def lam(self):

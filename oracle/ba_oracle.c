@@ -38,6 +38,11 @@ struct orc_problem {
   double *cams_trial, *pts_trial;
   double lambda, cost;
   int linearized;
+  /* dogleg: radius, and at the current linearisation (dl_valid) the
+   * Gauss-Newton step (in dc, dp) and the scalars of the step's model */
+  double radius;
+  int dl_valid, dl_iters;
+  double dl_rel, dl_gg, dl_nn, dl_gn, dl_JgJg, dl_JgJn, dl_JnJn;
 };
 
 /* ---------------------------------------------------------------- SO(3) -- */
@@ -300,6 +305,9 @@ int orc_opts_default(orc_opts* o) {
   o->pcg_max_iters = 50;
   o->pcg_rel_tol = 1e-6;
   o->solver = 0;
+  o->strategy = 0;
+  o->dl_radius0 = 1.0;
+  o->dl_gn_damping = 1e-6;
   return ORC_OK;
 }
 
@@ -384,6 +392,8 @@ int orc_create(const double* cams, int64_t nc, const double* pts, int64_t np,
   }
   build_structure(h);
   h->lambda = h->opt.lambda0;
+  h->radius = h->opt.dl_radius0;
+  h->dl_valid = 0;
   h->linearized = 0;
   orc_cost_at(h, h->cams, h->pts, &h->cost);
   if (!isfinite(h->cost)) {
@@ -457,11 +467,14 @@ int orc_set(orc_problem* h, int which, const void* in) {
   if (which != ORC_CAMS && which != ORC_PTS) return ORC_ERR_ARG;
   memcpy(array_ptr(h, which), in, elem_size(which) * (size_t)orc_array_size(h, which));
   h->linearized = 0;
+  h->dl_valid = 0;
   orc_cost_at(h, h->cams, h->pts, &h->cost);
   return ORC_OK;
 }
 
 double orc_get_lambda(const orc_problem* h) { return h->lambda; }
+double orc_get_radius(const orc_problem* h) { return h->radius; }
+void orc_set_radius(orc_problem* h, double radius) { h->radius = radius; }
 void orc_set_lambda(orc_problem* h, double lam) { h->lambda = lam; }
 double orc_get_cost(const orc_problem* h) { return h->cost; }
 
@@ -767,6 +780,7 @@ int orc_dense_schur_solve(orc_problem* h) {
  * the 9x9 diagonal blocks of S~^-1 (nc x 81, row-major): each camera's
  * marginal covariance under the damped Gauss-Newton model. */
 int orc_covariance(orc_problem* h, double* out) {
+  h->dl_valid = 0;
   int rc = orc_linearize(h);
   if (rc) return rc;
   if ((rc = orc_damp(h))) return rc;
@@ -837,6 +851,7 @@ int orc_retract(orc_problem* h) {
  * A rejected iteration still counts. */
 int orc_lm_step(orc_problem* h, orc_step_info* info) {
   int rc;
+  if (h->opt.strategy == 1) return orc_dogleg_step(h, info);
   if (!h->linearized && (rc = orc_linearize(h))) return rc;
   if ((rc = orc_damp(h))) return rc;
   if ((rc = orc_schur(h))) return rc;
@@ -852,6 +867,7 @@ int orc_lm_step(orc_problem* h, orc_step_info* info) {
   double trial;
   orc_cost_at(h, h->cams_trial, h->pts_trial, &trial);
   orc_step_info inf;
+  memset(&inf, 0, sizeof(inf));
   inf.cost_before = h->cost;
   inf.cost_after = trial;
   inf.lambda = h->lambda;
@@ -870,6 +886,158 @@ int orc_lm_step(orc_problem* h, orc_step_info* info) {
     h->lambda = h->lambda * h->opt.lambda_up;
     if (h->lambda > h->opt.lambda_max) h->lambda = h->opt.lambda_max;
   }
+  if (info) *info = inf;
+  return ORC_OK;
+}
+
+/* One dogleg iteration ([THESEUS]: LM with adaptive damping, and Dogleg, are
+ * offered beside Gauss-Newton; [BAE] names dogleg among the further
+ * optimisers).  Powell's dogleg in the trust-region form of Madsen, Nielsen
+ * and Tingleff's notes on non-linear least squares, with the quadratic model
+ * L(h) = C + g^T h + 1/2 h^T H h, H = J^T W J (the IRLS weights for Huber):
+ *   h_sd = -alpha g, alpha = |g|^2 / |J g|_W^2, the model's minimiser along -g;
+ *   h_gn from (H + mu D) h = -g by the configured solver (Schur elimination,
+ *        PCG or the dense Cholesky of S, back-substitution).  Reading: mu is a
+ *        small fixed Marquardt damping (opts.dl_gn_damping, D as for LM),
+ *        because H of a BA problem is singular along its gauge;
+ *   h = h_gn if |h_gn| <= radius; else -(radius / |g|) g if alpha |g| >=
+ *        radius; else -alpha g + beta (h_gn + alpha g) with |h| = radius;
+ *   gain ratio rho = (C - C(x + h)) / (L(0) - L(h)); the step is kept iff the
+ *        cost is strictly lower (as for LM); radius = max(radius, 3 |h|) when
+ *        rho > 0.75, radius / 2 when rho < 0.25.
+ * |.| is the Euclidean norm over all parameters in the tangent of the
+ * retraction.  h_gn, alpha and the model's scalars are kept while the point
+ * of linearisation does not move, so a rejected step costs one trial cost. */
+int orc_dogleg_step(orc_problem* h, orc_step_info* info) {
+  int rc;
+  const int64_t nc = h->nc, np = h->np;
+  if (!h->dl_valid) {
+    if (!h->linearized && (rc = orc_linearize(h))) return rc;
+    const double lam = h->lambda;
+    h->lambda = h->opt.dl_gn_damping;
+    rc = orc_damp(h);
+    if (!rc) rc = orc_schur(h);
+    int iters = 0;
+    double rel = 0.0;
+    if (!rc) {
+      if (h->opt.solver == 1) rc = orc_dense_schur_solve(h);
+      else rc = orc_pcg(h, h->opt.pcg_max_iters, h->opt.pcg_rel_tol, &iters, &rel);
+    }
+    if (!rc) rc = orc_backsub(h);
+    h->lambda = lam;
+    if (rc) return rc;
+    double gg = 0.0, nn = 0.0, gn = 0.0;
+    for (int64_t e = 0; e < 9 * nc; e++) {
+      gg += h->gc[e] * h->gc[e];
+      nn += h->dc[e] * h->dc[e];
+      gn += h->gc[e] * h->dc[e];
+    }
+    for (int64_t e = 0; e < 3 * np; e++) {
+      gg += h->gp[e] * h->gp[e];
+      nn += h->dp[e] * h->dp[e];
+      gn += h->gp[e] * h->dp[e];
+    }
+    double uu = 0.0, uv = 0.0, vv = 0.0;   /* |J g|_W^2, (J g)^T W (J h_gn), |J h_gn|_W^2 */
+    for (int64_t k = 0; k < h->nobs; k++) {
+      const double* Jc = h->Jc + 18 * k;
+      const double* Jp = h->Jp + 6 * k;
+      const double* gcj = h->gc + 9 * h->cam_idx[k];
+      const double* gpi = h->gp + 3 * h->pt_idx[k];
+      const double* dcj = h->dc + 9 * h->cam_idx[k];
+      const double* dpi = h->dp + 3 * h->pt_idx[k];
+      for (int a = 0; a < 2; a++) {
+        double u = 0.0, v = 0.0;
+        for (int b = 0; b < 9; b++) {
+          u += Jc[9 * a + b] * gcj[b];
+          v += Jc[9 * a + b] * dcj[b];
+        }
+        for (int b = 0; b < 3; b++) {
+          u += Jp[3 * a + b] * gpi[b];
+          v += Jp[3 * a + b] * dpi[b];
+        }
+        uu += h->w[k] * u * u;
+        uv += h->w[k] * u * v;
+        vv += h->w[k] * v * v;
+      }
+    }
+    h->dl_gg = gg;
+    h->dl_nn = nn;
+    h->dl_gn = gn;
+    h->dl_JgJg = uu;
+    h->dl_JgJn = uv;
+    h->dl_JnJn = vv;
+    h->dl_iters = iters;
+    h->dl_rel = rel;
+    h->dl_valid = 1;
+  }
+  /* the step as h = s_g g + s_n h_gn */
+  const double R = h->radius, gnorm = sqrt(h->dl_gg), nnorm = sqrt(h->dl_nn);
+  double s_g = 0.0, s_n = 0.0;
+  int kind = 0;
+  if (h->dl_gg == 0.0) {
+    kind = 0;   /* stationary: no step */
+  } else if (nnorm <= R) {
+    s_n = 1.0;
+    kind = 0;
+  } else {
+    const double alpha = h->dl_JgJg > 0.0 ? h->dl_gg / h->dl_JgJg : INFINITY;
+    if (alpha * gnorm >= R) {
+      s_g = -R / gnorm;
+      kind = 1;
+    } else {
+      /* a = -alpha g, b = h_gn: |a + beta (b - a)| = R */
+      const double aa = alpha * alpha * h->dl_gg;
+      const double c = -alpha * h->dl_gn - aa;                 /* a^T (b - a) */
+      const double dd = h->dl_nn + 2.0 * alpha * h->dl_gn + aa;   /* |b - a|^2 */
+      const double disc = sqrt(c * c + dd * (R * R - aa));
+      const double beta = c <= 0.0 ? (-c + disc) / dd : (R * R - aa) / (c + disc);
+      s_g = -alpha * (1.0 - beta);
+      s_n = beta;
+      kind = 2;
+    }
+  }
+  const double hh = s_g * s_g * h->dl_gg + 2.0 * s_g * s_n * h->dl_gn + s_n * s_n * h->dl_nn;
+  const double hnorm = sqrt(hh > 0.0 ? hh : 0.0);
+  const double gh = s_g * h->dl_gg + s_n * h->dl_gn;
+  const double hHh = s_g * s_g * h->dl_JgJg + 2.0 * s_g * s_n * h->dl_JgJn + s_n * s_n * h->dl_JnJn;
+  const double model = -gh - 0.5 * hHh;   /* L(0) - L(h) */
+  for (int64_t j = 0; j < nc; j++) {
+    double d[9];
+    for (int a = 0; a < 9; a++) d[a] = s_g * h->gc[9 * j + a] + s_n * h->dc[9 * j + a];
+    orc_retract_camera(h->cams + 9 * j, d, h->cams_trial + 9 * j);
+  }
+  for (int64_t e = 0; e < 3 * np; e++) h->pts_trial[e] = h->pts[e] + (s_g * h->gp[e] + s_n * h->dp[e]);
+  double trial;
+  orc_cost_at(h, h->cams_trial, h->pts_trial, &trial);
+  const double rho = model > 0.0 ? (h->cost - trial) / model : 0.0;
+  orc_step_info inf;
+  memset(&inf, 0, sizeof(inf));
+  inf.cost_before = h->cost;
+  inf.cost_after = trial;
+  inf.lambda = h->lambda;
+  inf.pcg_iters = h->dl_iters;
+  inf.pcg_rel_res = h->dl_rel;
+  inf.radius = R;
+  inf.gain_ratio = rho;
+  inf.step_norm = hnorm;
+  inf.step_kind = kind;
+  if (rho > 0.75) {
+    if (3.0 * hnorm > h->radius) h->radius = 3.0 * hnorm;
+  } else if (rho < 0.25) {
+    h->radius = 0.5 * h->radius;
+  }
+  if (isfinite(trial) && trial < h->cost) {
+    inf.accepted = 1;
+    memcpy(h->cams, h->cams_trial, sizeof(double) * 9 * nc);
+    memcpy(h->pts, h->pts_trial, sizeof(double) * 3 * np);
+    h->cost = trial;
+    h->linearized = 0;
+    h->dl_valid = 0;
+  } else {
+    inf.accepted = 0;
+  }
+  h->dl_iters = 0;   /* a repeat at this linearisation runs no solve */
+  h->dl_rel = 0.0;
   if (info) *info = inf;
   return ORC_OK;
 }
@@ -898,6 +1066,7 @@ int orc_backward(orc_problem* h, const double* grad_cams, const double* grad_pts
   for (int64_t e = 0; e < 9 * h->nc; e++) h->gc[e] = -grad_cams[e];
   for (int64_t e = 0; e < 3 * h->np; e++) h->gp[e] = -grad_pts[e];
   h->linearized = 0; /* g no longer holds the gradient of the cost */
+  h->dl_valid = 0;
   if ((rc = orc_damp(h))) return rc;
   if ((rc = orc_schur(h))) return rc;
   int iters = 0;

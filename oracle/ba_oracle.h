@@ -25,11 +25,18 @@ typedef struct {
   int pcg_max_iters;
   double pcg_rel_tol;
   int solver;          /* 0 Schur + PCG, 1 Schur + dense Cholesky of S          */
+  int strategy;        /* 0 Levenberg-Marquardt, 1 dogleg trust region          */
+  double dl_radius0;   /* dogleg: initial trust radius                          */
+  double dl_gn_damping;/* dogleg: Marquardt damping of its Gauss-Newton step     */
 } orc_opts;
 
 typedef struct {
   double cost_before, cost_after, lambda, pcg_rel_res;
   int accepted, pcg_iters;
+  /* dogleg only: trust radius used, gain ratio, |h|, 0 Gauss-Newton step,
+   * 1 steepest-descent step cut at the radius, 2 blend */
+  double radius, gain_ratio, step_norm;
+  int step_kind;
 } orc_step_info;
 
 typedef struct orc_problem orc_problem;
@@ -88,6 +95,10 @@ int orc_backsub(orc_problem* h);
 int orc_retract(orc_problem* h);
 int orc_cost_at(const orc_problem* h, const double* cams, const double* pts, double* cost);
 int orc_lm_step(orc_problem* h, orc_step_info* info);
+/* One dogleg iteration (orc_lm_step calls it when opts.strategy is 1). */
+int orc_dogleg_step(orc_problem* h, orc_step_info* info);
+double orc_get_radius(const orc_problem* h);
+void orc_set_radius(orc_problem* h, double radius);
 int orc_solve(orc_problem* h, int n_iters, orc_step_info* infos);
 /* df/du (nobs x 2) for a loss f of the LM solution with gradient
  * (grad_cams, grad_pts), by implicit differentiation of one damped
