@@ -35,6 +35,10 @@ points, assemble and factor S~, form Z = L^-T by tiles with fp64 MFMA
 updates, each camera's 9x9 block of Z Z^T); the roofline refers to the fp64
 MFMA update of Z.
 
+``--workload dogleg`` measures the same large scene with the dogleg trust
+region (BA_STRATEGY_DOGLEG): a step is one dogleg iteration; a new point of
+linearisation costs a Gauss-Newton solve, a rejected step one trial cost.
+
 ``--workload pgo`` measures libpgo, pose-graph optimisation: a step is one LM
 iteration (linearise the relative-pose edges, per-pose H and g sums, damping,
 PCG with 6 x 6 block-Jacobi, retraction, trial cost, accept/reject) of the
@@ -52,6 +56,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "LM iterations/s and observations/s (fp64, 1 GPU); % of HBM roofline"
+DOGLEG_METRIC = "dogleg iterations/s and observations/s (fp64, 1 GPU); % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 # The dominant kernel is timed inside the timed region by HIP events that its
 # own dispatch records; a timed dispatch cannot overlap its neighbours, so only
@@ -126,16 +131,17 @@ def measured_traffic(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(sc, n_iters=3):
-    """The oracle as it stands (plain C, one thread) on the first LM
-    iterations of the same scene from the same start."""
+def cpu_baseline(sc, n_iters=3, strategy=0):
+    """The oracle as it stands (plain C, one thread) on the first LM (or
+    dogleg) iterations of the same scene from the same start."""
     import oracle
-    P = oracle.Problem.from_scene(sc)
+    P = oracle.Problem.from_scene(sc, strategy=strategy)
     t0 = time.perf_counter()
     P.solve(n_iters)
     dt = time.perf_counter() - t0
-    return {"value": n_iters / dt, "unit": "LM iterations/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n_iters} LM iterations of the same scene "
+    kind = "dogleg" if strategy else "LM"
+    return {"value": n_iters / dt, "unit": f"{kind} iterations/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_iters} {kind} iterations of the same scene "
                       f"({len(sc['obs_cam'])} observations, PCG max {sc['pcg_max_iters']}), "
                       f"single-threaded C oracle, {dt:.1f} s"}
 
@@ -652,8 +658,8 @@ def main():
     ap.add_argument("--config", default=None,
                     help="scene (default: large for ba and backward, medium for "
                          "schur-dense and covariance, sphere for pgo)")
-    ap.add_argument("--workload", choices=["ba", "dense", "schur-dense", "backward", "pgo",
-                                           "covariance"], default="ba")
+    ap.add_argument("--workload", choices=["ba", "dogleg", "dense", "schur-dense", "backward",
+                                           "pgo", "covariance"], default="ba")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (byte-counter calibration)")
@@ -686,8 +692,10 @@ def main():
     n_obs, n_pts, n_cams = len(sc["obs_cam"]), len(sc["points"]), len(sc["cams"])
     print(f"# {scene_summary(sc)}", file=sys.stderr, flush=True)
 
+    dogleg = args.workload == "dogleg"
+    strat = dict(strategy=ba.BA_STRATEGY_DOGLEG) if dogleg else {}
     # Warm-up on its own handle, every kernel timed, to find the dominant kernel.
-    warm = ba.Problem.from_scene(sc)
+    warm = ba.Problem.from_scene(sc, **strat)
     warm.profile()
     warm.solve(max(args.warmup, 1))
     prof = warm.profile_get()
@@ -697,7 +705,7 @@ def main():
 
     # Timed run: a fresh handle from the initial parameters, K LM iterations.
     t0 = time.perf_counter()
-    P = ba.Problem.from_scene(sc)
+    P = ba.Problem.from_scene(sc, **strat)
     torch.cuda.synchronize()
     create_s = time.perf_counter() - t0
     P.profile([dominant], every=PROFILE_EVERY)
@@ -721,11 +729,13 @@ def main():
                 "launches": launches, "algorithmic_bytes_per_launch": nbytes}
 
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "LM iterations/s", "n_gpus": 1,
+        "metric": DOGLEG_METRIC if dogleg else METRIC, "value": round(value, 3),
+        "unit": "dogleg iterations/s" if dogleg else "LM iterations/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * dt / args.steps, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": f"{args.config} BA: {n_cams} cameras, {n_pts} points, {n_obs} "
+        "config": {"workload": f"{args.config} BA{', dogleg trust region' if dogleg else ''}: "
+                               f"{n_cams} cameras, {n_pts} points, {n_obs} "
                                f"observations, {sc['loss']} loss, PCG max {sc['pcg_max_iters']} "
                                f"rel tol {sc['pcg_rel_tol']}",
                    "n_obs": n_obs, "n_pts": n_pts, "n_cams": n_cams},
@@ -736,7 +746,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(sc)
+        out["cpu_baseline"] = cpu_baseline(sc, strategy=1 if dogleg else 0)
     print(json.dumps(out), flush=True)
 
 

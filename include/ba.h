@@ -74,6 +74,24 @@ enum { BA_MEM_HOST = 0, BA_MEM_DEVICE = 1 };
 enum { BA_SOLVER_PCG = 0, BA_SOLVER_DENSE_SCHUR = 1 };
 #define BA_DENSE_MAX_CAMS 1536
 enum { BA_LOSS_SQUARED = 0, BA_LOSS_HUBER = 1 };
+/* Step strategy of ba_lm_step / ba_solve (the Theseus note offers LM with
+ * adaptive damping and Dogleg):
+ *   BA_STRATEGY_LM      Levenberg-Marquardt (default);
+ *   BA_STRATEGY_DOGLEG  Powell's dogleg trust region: the Gauss-Newton step
+ *                       (the damped system with the small fixed damping
+ *                       dl_gn_damping, which keeps the gauge-singular BA
+ *                       system solvable), the Cauchy point -alpha g with
+ *                       alpha = |g|^2 / |J g|_W^2, and their blend at the
+ *                       trust radius; gain ratio against the quadratic model
+ *                       C + g^T h + 1/2 h^T J^T W J h; the radius becomes
+ *                       max(radius, 3 |h|) when the ratio exceeds 0.75 and is
+ *                       halved below 0.25; a step is kept iff the cost is
+ *                       strictly lower.  |.| is the Euclidean norm over all
+ *                       parameters in the tangent of the retraction.  While
+ *                       the point of linearisation stays, the Gauss-Newton
+ *                       step is kept, so a rejected step costs one trial
+ *                       cost. */
+enum { BA_STRATEGY_LM = 0, BA_STRATEGY_DOGLEG = 1 };
 
 typedef struct {
   int loss;              /* BA_LOSS_SQUARED or BA_LOSS_HUBER                     */
@@ -92,6 +110,11 @@ typedef struct {
   int solver;            /* BA_SOLVER_PCG (default) or BA_SOLVER_DENSE_SCHUR;
                             with the dense solver, pcg_iters and pcg_rel_res
                             of the step information are 0                       */
+  int strategy;          /* BA_STRATEGY_LM (default) or BA_STRATEGY_DOGLEG       */
+  double dl_radius0;     /* dogleg: initial trust radius (1.0)                   */
+  double dl_gn_damping;  /* dogleg: Marquardt damping of its Gauss-Newton step,
+                            also used by ba_backward and ba_covariance on a
+                            dogleg handle (1e-6)                                */
 } ba_options;
 
 typedef struct {
@@ -101,6 +124,11 @@ typedef struct {
   double pcg_rel_res;    /* |r|_2 / |rhs|_2 when PCG stopped                     */
   int accepted;          /* 1 if the trial parameters were kept                 */
   int pcg_iters;         /* PCG iterations run                                  */
+  double radius;         /* dogleg: trust radius of this step (0 for LM)        */
+  double gain_ratio;     /* dogleg: cost decrease / model decrease              */
+  double step_norm;      /* dogleg: |h|                                         */
+  int step_kind;         /* dogleg: 0 Gauss-Newton, 1 steepest descent cut at
+                            the radius, 2 blend of the two                     */
 } ba_step_info;
 
 typedef struct {
@@ -112,6 +140,8 @@ typedef struct {
   double lambda;         /* damping for the next step                           */
   double cost;           /* cost at the current parameters                      */
   int64_t iteration;     /* LM steps taken so far                               */
+  double radius;         /* dogleg trust radius; ba_set_state leaves it as it is
+                            when this is 0                                      */
 } ba_state;
 
 typedef struct ba_problem ba_problem;
@@ -276,6 +306,8 @@ enum {
   BA_K_COV_PANEL,    /* covariance: tiles of Z = L^-T solved against L_kk^T         */
   BA_K_COV_UPDATE,   /* covariance: Z_ji -= Z_jk L_ik^T (fp64 MFMA)                 */
   BA_K_COV_BLOCKS,   /* covariance: per camera, the 9x9 block of Z Z^T              */
+  BA_K_DL_OBS,       /* dogleg: |J g|^2, (J g).(J h_gn), |J h_gn|^2 partials        */
+  BA_K_DL_STEP,      /* dogleg: the step's camera part and the trial points         */
   BA_K_NUM
 };
 

@@ -18,6 +18,7 @@ BA_MEM_HOST, BA_MEM_DEVICE = 0, 1
 BA_LOSS_SQUARED, BA_LOSS_HUBER = 0, 1
 BA_STAGE_LINEARIZE, BA_STAGE_SCHUR, BA_STAGE_PCG, BA_STAGE_UPDATE = 1, 2, 3, 4
 BA_SOLVER_PCG, BA_SOLVER_DENSE_SCHUR = 0, 1
+BA_STRATEGY_LM, BA_STRATEGY_DOGLEG = 0, 1
 BA_DENSE_MAX_CAMS = 1536
 
 DBG = dict(perm_pt=0, perm_cam=1, pt_ptr=2, cam_ptr=3, r=4, Jc=5, Jp=6, w=7, B=8, gc=9, C=10,
@@ -31,7 +32,7 @@ DBG_SHAPE = {"r": (-1, 2), "Jc": (-1, 2, 9), "Jp": (-1, 2, 3), "B": (-1, 9, 9), 
 KERNELS = ["lin_pt", "lin_cam", "damp_pt", "schur_cam", "precond", "pcg_init", "pcg_pt",
            "pcg_cam", "pcg_q", "pcg_xr", "backsub", "retract", "cost", "ds_runs", "ds_fill",
            "ds_assemble", "ds_panel", "ds_update", "ds_backsolve", "cov_init", "cov_panel",
-           "cov_update", "cov_blocks"]
+           "cov_update", "cov_blocks", "dl_obs", "dl_step"]
 
 
 class ba_options(C.Structure):
@@ -40,17 +41,22 @@ class ba_options(C.Structure):
                 ("lambda_min", C.c_double), ("lambda_max", C.c_double),
                 ("diag_floor", C.c_double), ("pcg_max_iters", C.c_int),
                 ("pcg_rel_tol", C.c_double), ("mem", C.c_int), ("stream", C.c_void_p),
-                ("solver", C.c_int)]
+                ("solver", C.c_int), ("strategy", C.c_int), ("dl_radius0", C.c_double),
+                ("dl_gn_damping", C.c_double)]
 
 
 class ba_step_info(C.Structure):
     _fields_ = [("cost_before", C.c_double), ("cost_after", C.c_double), ("lambda_", C.c_double),
-                ("pcg_rel_res", C.c_double), ("accepted", C.c_int), ("pcg_iters", C.c_int)]
+                ("pcg_rel_res", C.c_double), ("accepted", C.c_int), ("pcg_iters", C.c_int),
+                ("radius", C.c_double), ("gain_ratio", C.c_double), ("step_norm", C.c_double),
+                ("step_kind", C.c_int)]
 
     def as_dict(self):
         return dict(cost_before=self.cost_before, cost_after=self.cost_after, lam=self.lambda_,
                     accepted=self.accepted, pcg_iters=self.pcg_iters,
-                    pcg_rel_res=self.pcg_rel_res)
+                    pcg_rel_res=self.pcg_rel_res, radius=self.radius,
+                    gain_ratio=self.gain_ratio, step_norm=self.step_norm,
+                    step_kind=self.step_kind)
 
 
 class ba_summary(C.Structure):
@@ -59,7 +65,8 @@ class ba_summary(C.Structure):
 
 
 class ba_state(C.Structure):
-    _fields_ = [("lambda_", C.c_double), ("cost", C.c_double), ("iteration", C.c_int64)]
+    _fields_ = [("lambda_", C.c_double), ("cost", C.c_double), ("iteration", C.c_int64),
+                ("radius", C.c_double)]
 
 
 class BAError(RuntimeError):
@@ -263,10 +270,10 @@ class Problem:
     def get_state(self):
         st = ba_state()
         _check(lib().ba_get_state(self.h, C.byref(st)), "ba_get_state")
-        return dict(lam=st.lambda_, cost=st.cost, iteration=st.iteration)
+        return dict(lam=st.lambda_, cost=st.cost, iteration=st.iteration, radius=st.radius)
 
-    def set_state(self, lam, iteration=0):
-        st = ba_state(lam, 0.0, iteration)
+    def set_state(self, lam, iteration=0, radius=0.0):
+        st = ba_state(lam, 0.0, iteration, radius)
         _check(lib().ba_set_state(self.h, C.byref(st)), "ba_set_state")
 
     def debug_run(self, upto):

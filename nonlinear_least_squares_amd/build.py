@@ -24,7 +24,7 @@ COMMON = [
 ]
 
 LIBS = {
-    "libba.so": ["ba_kernels.hip", "ba_dense.hip", "ba_backward.hip", "ba_capi.hip"],
+    "libba.so": ["ba_kernels.hip", "ba_dense.hip", "ba_backward.hip", "ba_dogleg.hip", "ba_capi.hip"],
     "libdba.so": ["dba_kernels.hip"],
     "libpgo.so": ["pgo_kernels.hip", "pgo_capi.hip"],
 }

@@ -117,6 +117,12 @@ struct ba_problem {
   PcgState* pcg = nullptr;
   double *dp = nullptr, *cost_part = nullptr;
   double* vjp = nullptr;     // backward: df/du in the original observation order
+  // dogleg: partials and sums of the step's model, the step's camera part
+  double *dl_vpart = nullptr, *dl_opart = nullptr, *dl_out = nullptr, *dl_hc = nullptr;
+  double radius = 0.0;
+  int dl_valid = 0, dl_iters = 0;
+  double dl_rel = 0.0;
+  double dl_sums[6] = {0, 0, 0, 0, 0, 0};   // g.g, h.h, g.h, |Jg|^2, Jg.Jh, |Jh|^2
   StepOut* out = nullptr;
   int* flags = nullptr;
   StepOut* h_out = nullptr;  // pinned
@@ -157,7 +163,7 @@ Dev make_dev(const ba_problem* h) {
   d.loss = h->opt.loss;
   d.delta = h->opt.huber_delta;
   d.diag_floor = h->opt.diag_floor;
-  d.lambda = h->lambda;
+  d.lambda = h->opt.strategy == BA_STRATEGY_DOGLEG ? h->opt.dl_gn_damping : h->lambda;
   d.tol = h->opt.pcg_rel_tol;
   const int c = h->cur, t = 1 - h->cur;
   d.cams = h->cams[c];
@@ -405,7 +411,10 @@ int current_cost(ba_problem* h, double* c) {
   return BA_OK;
 }
 
+int dogleg_step(ba_problem* h, ba_step_info* info);
+
 int lm_step(ba_problem* h, ba_step_info* info) {
+  if (h->opt.strategy == BA_STRATEGY_DOGLEG) return dogleg_step(h, info);
   if (!h->linearized) CHECK_RC(stage_linearize(h));
   CHECK_RC(stage_schur(h));
   h->linearized = 1;
@@ -431,6 +440,104 @@ int lm_step(ba_problem* h, ba_step_info* info) {
   } else {
     inf.accepted = 0;
     h->lambda = std::min(h->lambda * h->opt.lambda_up, h->opt.lambda_max);
+  }
+  h->iteration += 1;
+  if (info) *info = inf;
+  return BA_OK;
+}
+
+// One dogleg iteration (BA_STRATEGY_DOGLEG in include/ba.h): at a new point
+// of linearisation the Gauss-Newton step of the system damped by
+// dl_gn_damping (Schur elimination, the configured solver,
+// back-substitution) and the six sums of the quadratic model; then the step
+// h = s_g g + s_n h_gn for the current radius, the trial cost and the gain
+// ratio.  The step's coefficients are chosen on the host from the sums.
+int dogleg_step(ba_problem* h, ba_step_info* info) {
+  hipStream_t s = h->stream;
+  int pcg_iters = 0;
+  double pcg_rel = 0.0;
+  if (!h->dl_valid) {
+    if (!h->linearized) CHECK_RC(stage_linearize(h));
+    h->linearized = 1;
+    CHECK_RC(stage_schur(h));
+    CHECK_RC(stage_solve(h));
+    Dev d = make_dev(h);
+    TIMED(BA_K_BACKSUB, -1, launch_backsub(d, s));
+    launch_dl_vec(d, h->dl_vpart, s);
+    TIMED(BA_K_DL_OBS, -1, launch_dl_obs(d, h->dl_opart, s));
+    launch_dl_final(d, h->dl_vpart, h->dl_opart, h->dl_out, s);
+    HIPC(hipGetLastError());
+    PcgState st;
+    int flags[2] = {0, 0};
+    HIPC(hipMemcpyAsync(h->dl_sums, h->dl_out, sizeof(h->dl_sums), hipMemcpyDeviceToHost, s));
+    HIPC(hipMemcpyAsync(&st, h->pcg, sizeof(st), hipMemcpyDeviceToHost, s));
+    HIPC(hipMemcpyAsync(flags, h->flags, sizeof(flags), hipMemcpyDeviceToHost, s));
+    HIPC(hipStreamSynchronize(s));
+    if (flags[1]) return fail(BA_ERR_NOT_SPD, "a damped block is not positive definite");
+    h->dl_iters = pcg_iters = st.iters;
+    h->dl_rel = pcg_rel = st.rhs_norm > 0.0 ? st.res_norm / st.rhs_norm : 0.0;
+    h->last_pcg_iters = st.iters;
+    h->dl_valid = 1;
+  }
+  const double gg = h->dl_sums[0], nn = h->dl_sums[1], gn = h->dl_sums[2];
+  const double JgJg = h->dl_sums[3], JgJn = h->dl_sums[4], JnJn = h->dl_sums[5];
+  const double R = h->radius, gnorm = std::sqrt(gg), nnorm = std::sqrt(nn);
+  double s_g = 0.0, s_n = 0.0;
+  int kind = 0;
+  if (gg == 0.0) {
+    kind = 0;   // stationary: no step
+  } else if (nnorm <= R) {
+    s_n = 1.0;
+  } else {
+    const double alpha = JgJg > 0.0 ? gg / JgJg : INFINITY;
+    if (alpha * gnorm >= R) {
+      s_g = -R / gnorm;
+      kind = 1;
+    } else {
+      // a = -alpha g, b = h_gn: |a + beta (b - a)| = R
+      const double aa = alpha * alpha * gg;
+      const double c = -alpha * gn - aa;
+      const double dd = nn + 2.0 * alpha * gn + aa;
+      const double disc = std::sqrt(c * c + dd * (R * R - aa));
+      const double beta = c <= 0.0 ? (-c + disc) / dd : (R * R - aa) / (c + disc);
+      s_g = -alpha * (1.0 - beta);
+      s_n = beta;
+      kind = 2;
+    }
+  }
+  const double hh = s_g * s_g * gg + 2.0 * s_g * s_n * gn + s_n * s_n * nn;
+  const double hnorm = std::sqrt(hh > 0.0 ? hh : 0.0);
+  const double model = -(s_g * gg + s_n * gn) - 0.5 * (s_g * s_g * JgJg + 2.0 * s_g * s_n * JgJn +
+                                                       s_n * s_n * JnJn);
+  Dev d = make_dev(h);
+  TIMED(BA_K_DL_STEP, -1, launch_dl_step(d, s_g, s_n, h->dl_hc, s));
+  Dev dr = d;
+  dr.x = h->dl_hc;
+  TIMED(BA_K_RETRACT, -1, launch_retract(dr, s));
+  TIMED(BA_K_COST, -1, launch_cost(d, d.pts_trial, d.tab_trial, d.camq_trial, s));
+  HIPC(hipGetLastError());
+  CHECK_RC(read_out(h));
+  const double trial = h->h_out->trial_cost;
+  if (h->prof_on) CHECK_RC(prof_collect(h, pcg_iters));
+  const double rho = model > 0.0 ? (h->cost - trial) / model : 0.0;
+  ba_step_info inf{};
+  inf.cost_before = h->cost;
+  inf.cost_after = trial;
+  inf.lambda = h->opt.dl_gn_damping;
+  inf.pcg_iters = pcg_iters;
+  inf.pcg_rel_res = pcg_rel;
+  inf.radius = R;
+  inf.gain_ratio = rho;
+  inf.step_norm = hnorm;
+  inf.step_kind = kind;
+  if (rho > 0.75) h->radius = std::max(h->radius, 3.0 * hnorm);
+  else if (rho < 0.25) h->radius = 0.5 * h->radius;
+  if (std::isfinite(trial) && trial < h->cost) {
+    inf.accepted = 1;
+    h->cur = 1 - h->cur;
+    h->cost = trial;
+    h->linearized = 0;
+    h->dl_valid = 0;
   }
   h->iteration += 1;
   if (info) *info = inf;
@@ -699,6 +806,10 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   P.add(h->cost_part, (int64_t)std::max(h->n_cost_blocks, 1));
   P.add(h->red_part, 8 * (int64_t)pcg_red_blocks(nc) + 2);
   P.add(h->pt_dot, (int64_t)std::max(h->lds_blocks, 1));
+  P.add(h->dl_vpart, 3 * (int64_t)dl_vec_blocks(nc, h->np));
+  P.add(h->dl_opart, 3 * (int64_t)std::max(h->n_chunk_blocks, 1));
+  P.add(h->dl_out, 6);
+  P.add(h->dl_hc, 9 * nc);
   rc = P.commit();
   if (rc != BA_OK) return rc;
   TRY(hipMemsetAsync(P.base, 0, P.size, s));
@@ -809,6 +920,9 @@ int check_options(const ba_options& o) {
   if (o.pcg_max_iters < 0 || !(o.pcg_rel_tol >= 0.0)) return fail(BA_ERR_ARG, "bad PCG options");
   if (o.mem != BA_MEM_HOST && o.mem != BA_MEM_DEVICE) return fail(BA_ERR_ARG, "bad mem");
   if (o.solver != BA_SOLVER_PCG && o.solver != BA_SOLVER_DENSE_SCHUR) return fail(BA_ERR_ARG, "bad solver");
+  if (o.strategy != BA_STRATEGY_LM && o.strategy != BA_STRATEGY_DOGLEG) return fail(BA_ERR_ARG, "bad strategy");
+  if (!(o.dl_radius0 > 0.0) || !std::isfinite(o.dl_radius0) || !(o.dl_gn_damping >= 0.0))
+    return fail(BA_ERR_ARG, "bad dogleg options");
   return BA_OK;
 }
 
@@ -832,7 +946,8 @@ const char* kKernelNames[BA_K_NUM] = {"lin_pt",   "lin_cam",  "damp_pt",     "sc
                                       "pcg_q",    "pcg_xr",   "backsub",     "retract",
                                       "cost",     "ds_runs",  "ds_fill",     "ds_assemble",
                                       "ds_panel", "ds_update", "ds_backsolve", "cov_init",
-                                      "cov_panel", "cov_update", "cov_blocks"};
+                                      "cov_panel", "cov_update", "cov_blocks", "dl_obs",
+                                      "dl_step"};
 
 }  // namespace
 
@@ -853,6 +968,9 @@ int ba_options_default(ba_options* o) {
   o->mem = BA_MEM_HOST;
   o->stream = nullptr;
   o->solver = BA_SOLVER_PCG;
+  o->strategy = BA_STRATEGY_LM;
+  o->dl_radius0 = 1.0;
+  o->dl_gn_damping = 1e-6;
   return BA_OK;
 }
 
@@ -923,6 +1041,7 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
   }
   h->cur = 0;
   h->lambda = h->opt.lambda0;
+  h->radius = h->opt.dl_radius0;
   h->linearized = 0;
   h->iteration = 0;
   launch_cam_prep(h->cams[0], h->tab[0], h->camq[0], h->nc, h->stream);
@@ -975,6 +1094,7 @@ int ba_backward(ba_problem* h, const double* grad_cams, const double* grad_point
   launch_negate(h->gc, 9 * nc, h->stream);
   launch_negate(h->gp, 3 * np, h->stream);
   h->linearized = 0;   // g no longer holds the gradient of the cost
+  h->dl_valid = 0;     // nor x and dp the dogleg's Gauss-Newton step
   CHECK_RC(stage_schur(h));
   CHECK_RC(stage_solve(h));
   Dev d = make_dev(h);
@@ -1001,6 +1121,7 @@ int ba_covariance(ba_problem* h, double* cov_out) {
   const int64_t nc = h->nc;
   CHECK_RC(stage_linearize(h));
   h->linearized = 1;
+  h->dl_valid = 0;
   CHECK_RC(stage_schur(h));
   CHECK_RC(stage_dense_factor(h));
   Dev d = make_dev(h);
@@ -1057,6 +1178,7 @@ int ba_set_params(ba_problem* h, const double* cams, const double* points) {
   if (!std::isfinite(c)) return fail(BA_ERR_NONFINITE, "cost is not finite");
   h->cost = c;
   h->linearized = 0;
+  h->dl_valid = 0;
   return BA_OK;
 }
 
@@ -1065,12 +1187,15 @@ int ba_get_state(const ba_problem* h, ba_state* st) {
   st->lambda = h->lambda;
   st->cost = h->cost;
   st->iteration = h->iteration;
+  st->radius = h->radius;
   return BA_OK;
 }
 
 int ba_set_state(ba_problem* h, const ba_state* st) {
-  if (!h || !st || !(st->lambda >= 0.0)) return fail(BA_ERR_ARG, "bad arguments");
+  if (!h || !st || !(st->lambda >= 0.0) || !(st->radius >= 0.0) || !std::isfinite(st->radius))
+    return fail(BA_ERR_ARG, "bad arguments");
   h->lambda = st->lambda;    // the cost always follows the parameters; st->cost is ignored
+  if (st->radius > 0.0) h->radius = st->radius;
   h->iteration = st->iteration;
   return BA_OK;
 }

@@ -187,6 +187,13 @@ int ds_update_tiles(const Dev& d, int k);
 void launch_ds_update(const Dev& d, int k, hipStream_t s);
 hipError_t ds_backsolve_limit(int ld);
 void launch_ds_backsolve(const Dev& d, hipStream_t s);
+// Dogleg (ba_dogleg.hip): the six sums of the step's model, and the trial
+// points with the step's camera part for the retraction.
+int dl_vec_blocks(int64_t nc, int64_t np);
+void launch_dl_vec(const Dev& d, double* vpart, hipStream_t s);
+void launch_dl_obs(const Dev& d, double* opart, hipStream_t s);
+void launch_dl_final(const Dev& d, const double* vpart, const double* opart, double* out, hipStream_t s);
+void launch_dl_step(const Dev& d, double s_g, double s_n, double* hc, hipStream_t s);
 // Camera marginal covariance from the dense factor (ba_dense.hip).
 void launch_cov_init(const Dev& d, hipStream_t s);
 void launch_cov_panel(const Dev& d, int k, hipStream_t s);
