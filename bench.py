@@ -31,9 +31,9 @@ per-observation products), with the arrays resident on the device.
 
 ``--workload covariance`` measures ba_covariance on the medium scene: a step
 is one camera marginal covariance evaluation (linearise, damp, eliminate the
-points, assemble and factor S~, form Z = L^-T by tiles with fp64 MFMA
-updates, each camera's 9x9 block of Z Z^T); the roofline refers to the fp64
-MFMA update of Z.
+points, assemble and factor S~ while forming Z = L^-T by tiles in the same
+launches, each camera's 9x9 block of Z Z^T); the roofline refers to the fp64
+MFMA trailing update, which carries both.
 
 ``--workload dogleg`` measures the same large scene with the dogleg trust
 region (BA_STRATEGY_DOGLEG): a step is one dogleg iteration; a new point of
@@ -351,17 +351,20 @@ COV_METRIC = "camera covariance evaluations/s (fp64, 1 GPU); % of fp64 MFMA roof
 
 
 def cov_update_flops(n_cams):
-    """Algorithmic fp64 flops of one Z_ji -= Z_jk L_ik^T launch of the
-    covariance, averaged over the launches of one evaluation: after tile
-    column k, (k + 1) (T - k - 1) full 32 x 32 x 32 tile products (Z = L^-T
-    by tiles costs the n^3 / 3 of a triangular inverse)."""
+    """Algorithmic fp64 flops of one trailing-update launch of a covariance
+    evaluation, averaged over the launches: after tile column k the launch
+    carries the Cholesky update (as in schur_dense_update_flops) and the
+    (k + 1) (T - k - 1) tile products Z_ji -= Z_jk L_ik^T of Z = L^-T (in all
+    n^3 / 3 + n^3 / 3 flops)."""
     T = -(-9 * n_cams // DS_TILE)
     total, launches = 0, 0
     for k in range(T):
-        tiles = (k + 1) * (T - k - 1)
-        if tiles:
-            total += 2 * DS_TILE ** 3 * tiles
-            launches += 1
+        m = T - k - 1
+        tiles = (k + 1) * m
+        if m == 0:
+            continue
+        total += 2 * DS_TILE ** 3 * (m * (m - 1) // 2) + DS_TILE ** 3 * m + 2 * DS_TILE ** 3 * tiles
+        launches += 1
     return total // max(launches, 1)
 
 
@@ -416,8 +419,7 @@ def main_covariance(args):
         roof = {"bound": None, "achieved": None, "peak": None, "unit": None, "frac": None,
                 "traffic": None, "kernel": dominant, "avg_launch_us": round(avg_s * 1e6, 2),
                 "launches": launches}
-        fl = {"cov_update": cov_update_flops(n_cams),
-              "ds_update": schur_dense_update_flops(n_cams)}.get(dominant)
+        fl = {"ds_update": cov_update_flops(n_cams)}.get(dominant)
         if fl:
             ach = fl / avg_s / 1e12
             roof.update({"bound": "mfma", "achieved": round(ach, 3), "peak": FP64_MFMA_PEAK_TFLOPS,

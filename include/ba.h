@@ -203,8 +203,9 @@ int ba_backward(ba_problem* h, const double* grad_cams, const double* grad_point
  * solves against the identity; S is never inverted directly.  At the current
  * parameters and lambda this linearises, damps, eliminates the points,
  * assembles and factors S~ = L L^T (as an LM step with the dense solver
- * would), forms Z = L^-T by 32 x 32 tiles (fp64 MFMA updates) and writes each
- * camera's 9x9 diagonal block of S~^-1 = Z Z^T to cov_out (n_cams x 81,
+ * would) while forming Z = L^-T by 32 x 32 tiles in the same launches (fp64
+ * MFMA updates), and writes each camera's 9x9 diagonal block of
+ * S~^-1 = Z Z^T to cov_out (n_cams x 81,
  * row-major; host memory for BA_MEM_HOST handles, device memory for
  * BA_MEM_DEVICE ones).  The blocks are the cameras' marginal covariances
  * under the damped Gauss-Newton model (S~ includes lambda's damping; at
@@ -302,9 +303,10 @@ enum {
   BA_K_DS_PANEL,     /* dense solver: diagonal tile factor and tile-row solves      */
   BA_K_DS_UPDATE,    /* dense solver: trailing update (fp64 MFMA)                  */
   BA_K_DS_BACKSOLVE, /* dense solver: L^T dc = L^-1 rhs                            */
-  BA_K_COV_INIT,     /* covariance: Z = I in the upper tiles of S                  */
-  BA_K_COV_PANEL,    /* covariance: tiles of Z = L^-T solved against L_kk^T         */
-  BA_K_COV_UPDATE,   /* covariance: Z_ji -= Z_jk L_ik^T (fp64 MFMA)                 */
+  BA_K_COV_ZERO,     /* covariance: zeros in the strictly upper tiles of S, which
+                        then receive Z = L^-T: its tiles are solved and updated
+                        (fp64 MFMA) within the BA_K_DS_PANEL / BA_K_DS_UPDATE
+                        launches of the factorisation                           */
   BA_K_COV_BLOCKS,   /* covariance: per camera, the 9x9 block of Z Z^T              */
   BA_K_DL_OBS,       /* dogleg: |J g|^2, (J g).(J h_gn), |J h_gn|^2 partials        */
   BA_K_DL_STEP,      /* dogleg: the step's camera part and the trial points         */

@@ -31,8 +31,8 @@ DBG_SHAPE = {"r": (-1, 2), "Jc": (-1, 2, 9), "Jp": (-1, 2, 3), "B": (-1, 9, 9), 
              "cams_trial": (-1, 9), "points_trial": (-1, 3)}
 KERNELS = ["lin_pt", "lin_cam", "damp_pt", "schur_cam", "precond", "pcg_init", "pcg_pt",
            "pcg_cam", "pcg_q", "pcg_xr", "backsub", "retract", "cost", "ds_runs", "ds_fill",
-           "ds_assemble", "ds_panel", "ds_update", "ds_backsolve", "cov_init", "cov_panel",
-           "cov_update", "cov_blocks", "dl_obs", "dl_step"]
+           "ds_assemble", "ds_panel", "ds_update", "ds_backsolve", "cov_zero", "cov_blocks",
+           "dl_obs", "dl_step"]
 
 
 class ba_options(C.Structure):

@@ -358,17 +358,19 @@ int stage_pcg(ba_problem* h) {
 }
 
 // Explicit S and its Cholesky factorisation by tile columns, the rhs as an
-// extra row (it ends as L^-1 rhs).
-int stage_dense_factor(ba_problem* h) {
+// extra row (it ends as L^-1 rhs); with `cov` the same launches also form
+// Z = L^-T in the upper tiles.
+int stage_dense_factor(ba_problem* h, int cov) {
   Dev d = make_dev(h);
   hipStream_t s = h->stream;
   TIMED(BA_K_DS_RUNS, -1, launch_ds_runs(d, s));
   TIMED(BA_K_DS_FILL, -1, launch_ds_fill(d, s));
   TIMED(BA_K_DS_ASSEMBLE, -1, launch_ds_assemble(d, s));
+  if (cov) TIMED(BA_K_COV_ZERO, -1, launch_cov_zero(d, s));
   TIMED(BA_K_DS_PANEL, -1, launch_ds_diag0(d, s));
   for (int k = 0; k < h->ds_T; ++k) {
-    TIMED(BA_K_DS_PANEL, -1, launch_ds_panel(d, k, s));
-    TIMED(BA_K_DS_UPDATE, -1, launch_ds_update(d, k, s));
+    TIMED(BA_K_DS_PANEL, -1, launch_ds_panel(d, k, cov, s));
+    TIMED(BA_K_DS_UPDATE, -1, launch_ds_update(d, k, cov, s));
   }
   HIPC(hipGetLastError());
   return BA_OK;
@@ -376,7 +378,7 @@ int stage_dense_factor(ba_problem* h) {
 
 // Dense solve of S dc = rhs: factorisation, then back-substitution.
 int stage_dense(ba_problem* h) {
-  CHECK_RC(stage_dense_factor(h));
+  CHECK_RC(stage_dense_factor(h, 0));
   Dev d = make_dev(h);
   TIMED(BA_K_DS_BACKSOLVE, -1, launch_ds_backsolve(d, h->stream));
   HIPC(hipGetLastError());
@@ -945,9 +947,8 @@ const char* kKernelNames[BA_K_NUM] = {"lin_pt",   "lin_cam",  "damp_pt",     "sc
                                       "precond",  "pcg_init", "pcg_pt",      "pcg_cam",
                                       "pcg_q",    "pcg_xr",   "backsub",     "retract",
                                       "cost",     "ds_runs",  "ds_fill",     "ds_assemble",
-                                      "ds_panel", "ds_update", "ds_backsolve", "cov_init",
-                                      "cov_panel", "cov_update", "cov_blocks", "dl_obs",
-                                      "dl_step"};
+                                      "ds_panel", "ds_update", "ds_backsolve", "cov_zero",
+                                      "cov_blocks", "dl_obs",      "dl_step"};
 
 }  // namespace
 
@@ -1123,14 +1124,9 @@ int ba_covariance(ba_problem* h, double* cov_out) {
   h->linearized = 1;
   h->dl_valid = 0;
   CHECK_RC(stage_schur(h));
-  CHECK_RC(stage_dense_factor(h));
+  CHECK_RC(stage_dense_factor(h, 1));
   Dev d = make_dev(h);
   hipStream_t s = h->stream;
-  TIMED(BA_K_COV_INIT, -1, launch_cov_init(d, s));
-  for (int k = 0; k < h->ds_T; ++k) {
-    TIMED(BA_K_COV_PANEL, -1, launch_cov_panel(d, k, s));
-    TIMED(BA_K_COV_UPDATE, -1, launch_cov_update(d, k, s));
-  }
   const bool dev = h->opt.mem == BA_MEM_DEVICE;
   TIMED(BA_K_COV_BLOCKS, -1, launch_cov_blocks(d, dev ? cov_out : h->ds_cov, nc, s));
   HIPC(hipGetLastError());

@@ -226,11 +226,14 @@ __global__ __launch_bounds__(64) void k_ds_diag0(Dev d) {
 // against the factored diagonal tile k, X L_kk^T = A: the factor's columns and
 // pivot reciprocals are staged in LDS (s_l, kT * kT + kT doubles) and read at
 // wavefront-uniform addresses (broadcasts).
-__device__ __forceinline__ void panel_solve(const Dev& d, int k, double* row, double* s_l) {
+// With `ident` the tile starts as the identity instead of being read.
+__device__ __forceinline__ void panel_solve(const Dev& d, int k, double* row, double* s_l,
+                                            bool ident) {
   const double* LT = d.ds_diagT + (int64_t)k * kT * kT;
+  const int r = threadIdx.x & (kT - 1);
   double b[kT];
 #pragma unroll
-  for (int c = 0; c < kT; ++c) b[c] = row[c];
+  for (int c = 0; c < kT; ++c) b[c] = ident ? (c == r ? 1.0 : 0.0) : row[c];
   double lt[kT * kT / 64];
 #pragma unroll
   for (int u = 0; u < kT * kT / 64; ++u) lt[u] = LT[threadIdx.x + 64 * u];
@@ -251,12 +254,16 @@ __device__ __forceinline__ void panel_solve(const Dev& d, int k, double* row, do
 
 // Tile column k, its diagonal tile already factored: one wavefront per tile
 // row i = k + 1 .. T (T: the rhs tile row) solves L_ik L_kk^T = A_ik in place,
-// lane r taking row r.
-__global__ __launch_bounds__(64) void k_ds_panel(Dev d, int k) {
+// lane r taking row r.  With `cov`, k + 1 more wavefronts solve the tiles
+// Z_jk (j <= k) of Z = L^-T against the same L_kk^T (Z_kk from the identity).
+__global__ __launch_bounds__(64) void k_ds_panel(Dev d, int k, int cov) {
   __shared__ double s_l[kT * kT + kT];
-  const int i = k + 1 + blockIdx.x;
+  const int nds = d.ds_T - k;
+  const int b = blockIdx.x;
   const int r = threadIdx.x & (kT - 1);
-  panel_solve(d, k, d.ds_S + (int64_t)(kT * i + r) * d.ds_ld + kT * k, s_l);
+  const int row_tile = b < nds ? k + 1 + b : b - nds;
+  panel_solve(d, k, d.ds_S + (int64_t)(kT * row_tile + r) * d.ds_ld + kT * k, s_l,
+              b >= nds && row_tile == k);
 }
 
 // C -= A B^T for 32 x 32 tiles of S (leading dimension ld) as 2 x 2 MFMA
@@ -301,10 +308,21 @@ __device__ __forceinline__ void tile_sub_abt(double* C, const double* A, const d
 // Trailing update after tile column k: one wavefront per tile (i, j) with
 // k < j <= i < T, then the rhs tile row (T, j): A_ij -= L_ik L_jk^T.  The
 // wavefront of tile (k + 1, k + 1) then factors that tile for the next panel.
-__global__ __launch_bounds__(64) void k_ds_update(Dev d, int k) {
+// With `cov`, one more wavefront per tile Z_ji, j <= k < i: Z_ji -= Z_jk L_ik^T.
+__global__ __launch_bounds__(64) void k_ds_update(Dev d, int k, int cov) {
   const int m = d.ds_T - k - 1;          // trailing tile columns
   const int tri = m * (m + 1) / 2;
   const int id = blockIdx.x;
+  if (id >= tri + m) {
+    const int cid = id - (tri + m);
+    const int j = cid % (k + 1), i = k + 1 + cid / (k + 1);
+    const int64_t ld = d.ds_ld;
+    double* S = d.ds_S;
+    v4d acc[2][2];
+    tile_sub_abt(S + (int64_t)(kT * j) * ld + kT * i, S + (int64_t)(kT * j) * ld + kT * k,
+                 S + (int64_t)(kT * i) * ld + kT * k, ld, acc);
+    return;
+  }
   int i, j;
   if (id < tri) {
     int ii = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
@@ -340,42 +358,25 @@ __global__ __launch_bounds__(64) void k_ds_update(Dev d, int k) {
 
 // ---- camera marginal covariance: blocks of S^-1 = L^-T L^-1 ---------------
 //
-// After the factorisation, Z = L^-T (upper triangular) is formed by tiles in
-// the upper triangle of S, which the factorisation no longer reads (its
-// diagonal tiles live in ds_diag): Z L^T = I gives, tile by tile,
+// Z = L^-T (upper triangular) is formed by tiles in the strictly upper tiles
+// of S, which the factorisation never reads, and in its diagonal tiles once
+// they are factored (the factor's diagonal tiles live in ds_diag).  Z L^T = I
+// gives, tile by tile,
 //   Z_jk L_kk^T = delta_jk I - sum_{m < k} Z_jm L_km^T,
-// so, right-looking over tile columns k: a panel solves the tiles Z_jk,
-// j <= k, against L_kk^T (the factorisation's panel solve), and an update
-// takes them out of the later columns, Z_ji -= Z_jk L_ik^T for j <= k < i
-// (the factorisation's MFMA tile product).  Each camera's 9x9 block of
-// S^-1 = Z Z^T is then the 45 dot products of its 9 rows of Z.
+// so the factorisation's launches carry it along: the panel of tile column k
+// also solves the tiles Z_jk, j <= k, against L_kk^T, and the update after it
+// also takes them out of the later columns, Z_ji -= Z_jk L_ik^T for j <= k < i.
+// Each camera's 9x9 block of S^-1 = Z Z^T is then the 45 dot products of its
+// 9 rows of Z.
 
-// Z = I in the upper tiles (j <= k) of S; the lower tiles hold L.
-__global__ void k_cov_init(Dev d) {
+// Zeros in the strictly upper tiles of S (the assembly may have written the
+// upper part of a diagonal 9x9 block there), before the factorisation.
+__global__ void k_cov_zero(Dev d) {
   const int64_t ld = d.ds_ld;
   const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (e >= ld * ld) return;
   const int64_t row = e / ld, col = e - row * ld;
-  if (col / kT >= row / kT) d.ds_S[e] = row == col ? 1.0 : 0.0;
-}
-
-// Tiles Z_jk, j = 0 .. k, solved against L_kk^T, one wavefront each.
-__global__ __launch_bounds__(64) void k_cov_panel(Dev d, int k) {
-  __shared__ double s_l[kT * kT + kT];
-  const int j = blockIdx.x;
-  const int r = threadIdx.x & (kT - 1);
-  panel_solve(d, k, d.ds_S + (int64_t)(kT * j + r) * d.ds_ld + kT * k, s_l);
-}
-
-// Z_ji -= Z_jk L_ik^T for every j <= k < i < T, one wavefront per tile.
-__global__ __launch_bounds__(64) void k_cov_update(Dev d, int k) {
-  const int id = blockIdx.x;
-  const int j = id % (k + 1), i = k + 1 + id / (k + 1);
-  const int64_t ld = d.ds_ld;
-  double* S = d.ds_S;
-  v4d acc[2][2];
-  tile_sub_abt(S + (int64_t)(kT * j) * ld + kT * i, S + (int64_t)(kT * j) * ld + kT * k,
-               S + (int64_t)(kT * i) * ld + kT * k, ld, acc);
+  if (col / kT > row / kT) d.ds_S[e] = 0.0;
 }
 
 // One workgroup per camera c: rows r_a = 9 c + a of Z (a < 9), each nonzero
@@ -494,18 +495,11 @@ __global__ __launch_bounds__(kSolveThreads) void k_ds_backsolve(Dev d) {
 
 int ds_tile() { return kT; }
 
-void launch_cov_init(const Dev& d, hipStream_t s) {
+void launch_cov_zero(const Dev& d, hipStream_t s) {
   const int64_t n = (int64_t)d.ds_ld * d.ds_ld;
-  launch_timed(k_cov_init, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, d);
-}
-void launch_cov_panel(const Dev& d, int k, hipStream_t s) {
-  launch_timed(k_cov_panel, dim3(k + 1), dim3(64), s, 0u, d, k);
+  launch_timed(k_cov_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, d);
 }
 int cov_update_tiles(const Dev& d, int k) { return (k + 1) * (d.ds_T - k - 1); }
-void launch_cov_update(const Dev& d, int k, hipStream_t s) {
-  const int n = cov_update_tiles(d, k);
-  if (n > 0) launch_timed(k_cov_update, dim3(n), dim3(64), s, 0u, d, k);
-}
 void launch_cov_blocks(const Dev& d, double* out, int64_t n_cams, hipStream_t s) {
   if (n_cams > 0) launch_timed(k_cov_blocks, dim3((unsigned)n_cams), dim3(256), s, 0u, d, out);
 }
@@ -521,16 +515,16 @@ void launch_ds_assemble(const Dev& d, hipStream_t s) {
   if (d.ds_nblk > 0) launch_timed(k_ds_assemble, dim3(d.ds_nblk), dim3(64 * kAsmWaves), s, 0u, d);
 }
 void launch_ds_diag0(const Dev& d, hipStream_t s) { launch_timed(k_ds_diag0, dim3(1), dim3(64), s, 0u, d); }
-void launch_ds_panel(const Dev& d, int k, hipStream_t s) {
-  launch_timed(k_ds_panel, dim3(d.ds_T - k), dim3(64), s, 0u, d, k);
+void launch_ds_panel(const Dev& d, int k, int cov, hipStream_t s) {
+  launch_timed(k_ds_panel, dim3(d.ds_T - k + (cov ? k + 1 : 0)), dim3(64), s, 0u, d, k, cov);
 }
 int ds_update_tiles(const Dev& d, int k) {
   const int m = d.ds_T - k - 1;
   return m * (m + 1) / 2 + m;
 }
-void launch_ds_update(const Dev& d, int k, hipStream_t s) {
-  const int n = ds_update_tiles(d, k);
-  if (n > 0) launch_timed(k_ds_update, dim3(n), dim3(64), s, 0u, d, k);
+void launch_ds_update(const Dev& d, int k, int cov, hipStream_t s) {
+  const int n = ds_update_tiles(d, k) + (cov ? cov_update_tiles(d, k) : 0);
+  if (n > 0) launch_timed(k_ds_update, dim3(n), dim3(64), s, 0u, d, k, cov);
 }
 hipError_t ds_backsolve_limit(int ld) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ds_backsolve),
