@@ -558,6 +558,26 @@ def pgo_algorithmic_bytes(kernel, n, m, n_fixed):
     return None
 
 
+PGO_KERNEL_SRC = os.path.join(ROOT, "nonlinear_least_squares_amd", "csrc", "pgo_kernels.hip")
+PGO_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pgo.json")
+
+
+def pgo_measured_traffic(config, kernel):
+    """Counter-based HBM bytes per launch for the pose-graph kernel, if taken
+    on the current kernel source."""
+    try:
+        with open(PGO_TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(PGO_KERNEL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != sha:
+        return None
+    k = t.get("configs", {}).get(config, {}).get("k_" + kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
 def pgo_cpu_baseline(sc, budget_s=15.0):
     """The oracle as it stands (plain C, one thread, PCG as on the GPU): LM
     iterations of the same graph from the same start, as many as fit in about
@@ -615,6 +635,7 @@ def main_pgo(args):
             ach = nbytes / avg_s / 1e9
             roof.update({"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                         "traffic": pgo_measured_traffic(config, dominant),
                          "algorithmic_bytes_per_launch": nbytes})
     pcg = sum(t["pcg_iters"] for t in tr)
     out = {

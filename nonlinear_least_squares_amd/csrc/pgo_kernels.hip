@@ -454,14 +454,21 @@ __device__ __forceinline__ int coup_idx(int side, int a, int b) {
 
 __global__ __launch_bounds__(256) void k_pcg_a(Dev d, int it) {
   __shared__ double s_buf[4];
+  __shared__ double s_coup[4][4 * kPosesPerWave * kCoupVals];   // per wavefront: 4 slots x 10 poses
+  __shared__ double s_hdd[4][kPosesPerWave * kSymVals];          // per wavefront: 10 damped blocks
   if (d.pcg->done) return;
   const Lane l = pose_lane(d.n);
   const int64_t e = 6 * l.i + l.a;
-  // loads that do not depend on the stop test
+  // loads that do not depend on the stop test; the pose's 21 damped-block
+  // values are fetched once by its six lanes (a, a + 6, a + 12, a + 18)
   const double zi = d.z[e];
-  double hrow[6];
+  double hv4[4];
+  {
+    const double* Hp = d.Hdd + kSymVals * l.i;
 #pragma unroll
-  for (int b = 0; b < 6; ++b) hrow[b] = d.Hdd[kSymVals * l.i + sym_idx(l.a, b)];
+    for (int u = 0; u < 3; ++u) hv4[u] = Hp[6 * u + l.a];
+    hv4[3] = l.a < 3 ? Hp[18 + l.a] : 0.0;
+  }
   const bool free_pose = l.on && l.i >= d.n_fixed;
   const int h0 = d.half_ptr[l.i], h1 = free_pose ? d.half_ptr[l.i + 1] : h0;
   const double pe = d.p[e], qe = d.q[e];
@@ -478,33 +485,69 @@ __global__ __launch_bounds__(256) void k_pcg_a(Dev d, int it) {
       return;
     }
   }
+  const int lane = threadIdx.x & 63, grp = lane / 6;
+  double* s_h = s_hdd[threadIdx.x >> 6] + min(grp, kPosesPerWave - 1) * kSymVals;
+  if (lane < 6 * kPosesPerWave) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) s_h[6 * u + l.a] = hv4[u];
+    if (l.a < 3) s_h[18 + l.a] = hv4[3];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   double w = 0.0;
 #pragma unroll
-  for (int b = 0; b < 6; ++b) w += hrow[b] * __shfl(zi, l.base + b, 64);
+  for (int b = 0; b < 6; ++b) w += s_h[sym_idx(l.a, b)] * __shfl(zi, l.base + b, 64);
   // Half edges four at a time, so that their gathers are in flight together.
   // Past the end of the list the last entry is loaded again and its terms are
-  // zeroed (w + 0 * z is w), so the terms still add up in list order.
+  // zeroed (w + 0 * z is w), so the terms still add up in list order.  The six
+  // lanes of a pose share the loads: lane a fetches element a of the other
+  // end's z, passed to the group by shuffles, and 16-byte pieces a and a + 6
+  // of the 20-double coupling block, staged in the wavefront's LDS rows, from
+  // which each lane reads its six coefficients.
+  double* s_c = s_coup[threadIdx.x >> 6];
   for (int h = h0; h < h1; h += 4) {
     int2 nb[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) nb[k] = d.nbr[min(h + k, h1 - 1)];
-    double hv[4][6], zv[4][6];
+    double2 c0[4], c1[4];
+    double zk[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const double* Hc = d.Hc + kCoupVals * (int64_t)(nb[k].x >> 1);
-      const double* zo = d.z + 6 * (int64_t)nb[k].y;
-      const bool live = h + k < h1;
+      const double2* src = reinterpret_cast<const double2*>(d.Hc + kCoupVals * (int64_t)(nb[k].x >> 1));
+      c0[k] = src[l.a];
+      c1[k] = l.a < 4 ? src[6 + l.a] : make_double2(0.0, 0.0);
+      zk[k] = d.z[6 * (int64_t)nb[k].y + l.a];
+    }
+    if (lane < 6 * kPosesPerWave) {
 #pragma unroll
-      for (int b = 0; b < 6; ++b) {
-        const double v = Hc[coup_idx(nb[k].x & 1, l.a, b)];
-        hv[k][b] = live ? v : 0.0;
-        zv[k][b] = zo[b];
+      for (int k = 0; k < 4; ++k) {
+        double* row = s_c + (k * kPosesPerWave + grp) * kCoupVals;
+        row[2 * l.a] = c0[k].x;
+        row[2 * l.a + 1] = c0[k].y;
+        if (l.a < 4) {
+          row[12 + 2 * l.a] = c1[k].x;
+          row[13 + 2 * l.a] = c1[k].y;
+        }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 4; ++k) {
+      const double* row = s_c + (k * kPosesPerWave + min(grp, kPosesPerWave - 1)) * kCoupVals;
+      const bool live = h + k < h1;
+      const int side = nb[k].x & 1;
 #pragma unroll
-      for (int b = 0; b < 6; ++b) w += hv[k][b] * zv[k][b];
+      for (int b = 0; b < 6; ++b) {
+        const double v = row[coup_idx(side, l.a, b)];
+        w += (live ? v : 0.0) * __shfl(zk[k], l.base + b, 64);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   const double beta = it > 0 ? total(d, kRZ0 + (it & 1)) / total(d, kRZ0 + ((it + 1) & 1)) : 0.0;
   double pn = 0.0, qn = 0.0;
