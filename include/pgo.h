@@ -128,8 +128,6 @@ enum {
   PGO_K_PCG_B,      /* PCG: x, r, z = M^-1 r                              */
   PGO_K_RETRACT,    /* trial poses                                        */
   PGO_K_COST,       /* trial cost per edge                                */
-  PGO_K_PCG_SUM,    /* PCG: one-block totals of the per-block partials (large
-                       graphs only; small ones sum inside PCG_A and PCG_B)  */
   PGO_K_NUM
 };
 /* Bit k of kernel_mask times kernel k with HIP events recorded by its own

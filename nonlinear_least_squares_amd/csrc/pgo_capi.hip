@@ -88,8 +88,7 @@ struct pgo_problem {
   double *r = nullptr, *Ji = nullptr, *Jj = nullptr, *Hc = nullptr, *half = nullptr,
          *cost_part = nullptr;
   double *Hd = nullptr, *Hdd = nullptr, *Minv = nullptr, *g = nullptr;
-  double *x = nullptr, *rv = nullptr, *z = nullptr, *p = nullptr, *q = nullptr, *red = nullptr,
-         *scal = nullptr;
+  double *x = nullptr, *rv = nullptr, *z = nullptr, *p = nullptr, *q = nullptr, *red = nullptr;
   PcgState* pcg = nullptr;
   StepOut* out = nullptr;
   int* flags = nullptr;
@@ -146,8 +145,7 @@ Dev make_dev(const pgo_problem* h) {
   d.q = h->q;
   d.red = h->red;
   d.red_nb = red_blocks(h->n);
-  d.inline_sums = d.red_nb <= kInlineSumsMax;
-  d.scal = h->scal;
+  d.n_chunks = pcg_chunks(h->n);
   d.pcg = h->pcg;
   d.host_done = h->h_done_dev;
   d.out = h->out;
@@ -223,18 +221,13 @@ int stage_step(pgo_problem* h) {
   HIPC(hipMemsetAsync(h->flags, 0, 2 * sizeof(int), h->stream));
   TIMED(PGO_K_POSE, -1, launch_pose(d, h->stream));
   launch_pcg_init(d, h->stream);
-  TIMED(PGO_K_PCG_SUM, -1, launch_pcg_sum(d, (1u << kRR0) | (1u << kRZ0) | (1u << kBB), h->stream));
   *h->h_done = 0;
   const int maxit = h->opt.pcg_max_iters;
   int next = 0;
   auto enqueue = [&](int k) -> int {
     for (int u = 0; u < k && next < maxit; ++u, ++next) {
-      const int par = (next + 1) & 1;
       TIMED(PGO_K_PCG_A, next, launch_pcg_a(d, next, h->stream));
-      TIMED(PGO_K_PCG_SUM, next, launch_pcg_sum(d, 1u << kPQ, h->stream));
       TIMED(PGO_K_PCG_B, next, launch_pcg_b(d, next, h->stream));
-      TIMED(PGO_K_PCG_SUM, next,
-            launch_pcg_sum(d, (1u << (kRR0 + par)) | (1u << (kRZ0 + par)), h->stream));
     }
     return PGO_OK;
   };
@@ -435,7 +428,6 @@ int pgo_create(const double* poses, int64_t n, const int32_t* edges, const doubl
   A.add(h->p, 6 * n);
   A.add(h->q, 6 * n);
   A.add(h->red, kNumSums * (int64_t)red_blocks(n));
-  A.add(h->scal, kNumSums);
   A.add(h->pcg, 1);
   A.add(h->out, 1);
   A.add(h->flags, 2);

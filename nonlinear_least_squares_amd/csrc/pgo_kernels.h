@@ -17,8 +17,8 @@
 //              edge id 2 e + side, pose at the other end), so every sum has a
 //              fixed order and the product's gathers depend on one load
 //   PCG scalars: per-block partials of r.r (two parities), r.z (two), b.b and
-//              p.q; on small grids every block sums them itself, on large
-//              grids a one-block kernel sums each set once into `scal`
+//              p.q, at most kMaxPcgBlocks of each; every block adds them all
+//              in a fixed order
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -30,10 +30,12 @@ constexpr int kHalfVals = 42;   // 6x6 block + 6-vector
 constexpr int kCoupVals = 20;   // H_ij: two 3x3 blocks, -w_t, 0
 constexpr int kSymVals = 21;    // upper triangle of a symmetric 6x6 block
 constexpr int kPosesPerWave = 10;
-constexpr int kPosesPerBlock = 4 * kPosesPerWave;   // PCG blocks of four wavefronts
-// Above this many PCG blocks the partial sums go through k_pcg_sum.
-constexpr int kInlineSumsMax = 256;
-// Indices of the partial-sum arrays (and of their totals in `scal`).
+// PCG blocks: kBigPcgWaves wavefronts when the graph fills kMaxPcgBlocks
+// such blocks, else kSmallPcgWaves; a chunk is ten poses per wavefront.
+constexpr int kBigPcgWaves = 16;
+constexpr int kSmallPcgWaves = 4;
+constexpr int kMaxPcgBlocks = 256;   // one per compute unit
+// Indices of the partial-sum arrays.
 enum { kRR0 = 0, kRR1 = 1, kRZ0 = 2, kRZ1 = 3, kBB = 4, kPQ = 5, kNumSums = 6 };
 
 struct PcgState {
@@ -72,9 +74,8 @@ struct Dev {
   double* g;               // n x 6
   double *x, *rv, *z, *p, *q;   // PCG vectors, 6n each
   double* red;             // per-block partials, kNumSums arrays of red_nb
-  int red_nb;
-  int inline_sums;         // red_nb <= kInlineSumsMax
-  double* scal;            // kNumSums totals (k_pcg_sum)
+  int red_nb;              // PCG blocks
+  int64_t n_chunks;        // PCG chunks of pcg_waves(n) x 10 poses
   PcgState* pcg;
   int* host_done;
   StepOut* out;
@@ -87,16 +88,16 @@ struct DispatchEvents {
 };
 DispatchEvents& dispatch_events();
 
+int pcg_waves(int64_t n);
 int red_blocks(int64_t n);
+int64_t pcg_chunks(int64_t n);
 int edge_blocks(int64_t m);
 void launch_prep(const double* poses, double* tab, int64_t n, hipStream_t s);
 void launch_meas_prep(const double* meas, double* meas_tab, int64_t m, hipStream_t s);
 void launch_edge(const Dev& d, hipStream_t s);
 void launch_pose(const Dev& d, hipStream_t s);
 void launch_pcg_init(const Dev& d, hipStream_t s);
-// Sums the partial arrays whose bits are set in `mask` into d.scal (no-op on
-// small grids, whose kernels sum the partials themselves).
-void launch_pcg_sum(const Dev& d, unsigned mask, hipStream_t s);
+
 void launch_pcg_a(const Dev& d, int it, hipStream_t s);
 void launch_pcg_b(const Dev& d, int it, hipStream_t s);
 void launch_pcg_final(const Dev& d, int iters, hipStream_t s);

@@ -319,15 +319,17 @@ __device__ __forceinline__ int sym_idx(int a, int b) {
   return i * (11 - i) / 2 + j;
 }
 
-// ---- PCG on H~ dx = -g: six lanes per pose, ten poses per wavefront, four
-// wavefronts per block --------------------------------------------------------
+// ---- PCG on H~ dx = -g: six lanes per pose, ten poses per wavefront ---------
 //
 // As in the bundle-adjustment solve, the product is applied to z, and
 // p = z + beta p and q = H~ p = H~ z + beta q follow by recurrence, so one
 // kernel does the product, the stop test and the recurrences and a second the
-// update of x, r and z.  Each block leaves one partial per sum; the totals are
-// summed in a fixed order, by every wavefront itself on small grids and once
-// by k_pcg_sum on large ones.
+// update of x, r and z.  The poses are cut into chunks of W x 10 (ten per
+// wavefront of a block of W); at most kMaxPcgBlocks blocks each take a fixed
+// set of chunks, so each block leaves one partial per sum and every block can
+// add all the partials itself, in a fixed order, to get the same totals.
+// Large graphs use blocks of 16 wavefronts (one per compute unit), smaller
+// ones blocks of 4, so that they still spread over many compute units.
 
 struct Lane {
   int64_t i;   // pose (clamped on idle lanes)
@@ -336,19 +338,30 @@ struct Lane {
   bool on;
 };
 
-// Blocks are handed to the eight XCDs in turn (block b to XCD b mod 8); this
-// gives XCD x one contiguous range of poses, so a pose's graph neighbours,
-// whose z and H_ij it gathers, mostly sit in the same XCD's L2.
-__device__ __forceinline__ int64_t xcd_block() {
-  const int nb = gridDim.x, b = blockIdx.x;
-  const int per = nb / 8, rem = nb % 8, x = b % 8, local = b / 8;
-  return x < rem ? (int64_t)x * (per + 1) + local : (int64_t)rem * (per + 1) + (int64_t)(x - rem) * per + local;
+// The chunks of this block.  Blocks are handed to the eight XCDs in turn
+// (block b to XCD b mod 8); each XCD takes one contiguous range of chunks,
+// in proportion to its blocks, and its blocks take that range's chunks in
+// turn, so a pose's graph neighbours, whose z and H_ij it gathers, mostly sit
+// in the same XCD's L2.
+struct Chunks {
+  int64_t first, end;
+  int step;
+};
+
+__device__ __forceinline__ Chunks my_chunks(int64_t n_chunks) {
+  const int G = gridDim.x, b = blockIdx.x, x = b % 8, l = b / 8;
+  const int per = G / 8, rem = G % 8;
+  const int bx = per + (x < rem ? 1 : 0);
+  const int sx = x * per + min(x, rem);
+  const int64_t cb = n_chunks * sx / G, ce = n_chunks * (sx + bx) / G;
+  return {cb + l, ce, bx};
 }
 
-__device__ __forceinline__ Lane pose_lane(int64_t n) {
+template <int W>
+__device__ __forceinline__ Lane pose_lane(int64_t chunk, int64_t n) {
   const int lane = threadIdx.x & 63;
   Lane l;
-  const int64_t i = xcd_block() * kPosesPerBlock + (threadIdx.x >> 6) * kPosesPerWave + lane / 6;
+  const int64_t i = chunk * (W * kPosesPerWave) + (threadIdx.x >> 6) * kPosesPerWave + lane / 6;
   l.on = lane < 6 * kPosesPerWave && i < n;
   l.i = l.on ? i : 0;
   l.a = lane % 6;
@@ -366,13 +379,16 @@ __device__ __forceinline__ double wave_sum(double v) {
   return __shfl(v, 0, 64);
 }
 
-// Sum over the block's four wavefronts in wave order; the result is valid in
-// thread 0.
-__device__ __forceinline__ double block4_sum(double v, double* s_buf) {
+// Sum over the block's W wavefronts in wave order (every thread gets it).
+template <int W>
+__device__ __forceinline__ double block_waves_sum(double v, double* s_buf) {
   v = wave_sum(v);
   if ((threadIdx.x & 63) == 0) s_buf[threadIdx.x >> 6] = v;
   __syncthreads();
-  return ((s_buf[0] + s_buf[1]) + s_buf[2]) + s_buf[3];
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) t += s_buf[w];
+  return t;
 }
 
 __device__ __forceinline__ double partial_sum(const double* a, int n) {
@@ -384,10 +400,9 @@ __device__ __forceinline__ double partial_sum(const double* a, int n) {
 
 __device__ __forceinline__ double* red_arr(const Dev& d, int k) { return d.red + k * d.red_nb; }
 
-// Total of partial array k: summed here on small grids, read from k_pcg_sum's
-// result on large ones.  Either way every block gets the same value.
+// Total of partial array k, the same in every block.
 __device__ __forceinline__ double total(const Dev& d, int k) {
-  return d.inline_sums ? partial_sum(red_arr(d, k), d.red_nb) : d.scal[k];
+  return partial_sum(red_arr(d, k), d.red_nb);
 }
 
 // row a of (M v) for the pose of this lane group, M symmetric (upper triangle)
@@ -409,22 +424,26 @@ __device__ __forceinline__ void stop_pcg(const Dev& d, int iters, double res, do
   __threadfence_system();
 }
 
-__global__ __launch_bounds__(256) void k_pcg_init(Dev d) {
-  __shared__ double s_rr[4], s_rz[4];
-  const Lane l = pose_lane(d.n);
-  const int64_t e = 6 * l.i + l.a;
-  const double b = (l.on && l.i >= d.n_fixed) ? -d.g[e] : 0.0;
-  const double z = apply_sym6(d.Minv + kSymVals * l.i, l, b);
+template <int W>
+__global__ __launch_bounds__(64 * W) void k_pcg_init(Dev d) {
+  __shared__ double s_rr[W], s_rz[W];
   double rr = 0.0, rz = 0.0;
-  if (l.on) {
-    d.x[e] = 0.0;
-    d.rv[e] = b;
-    d.z[e] = z;
-    rr = b * b;
-    rz = b * z;
+  const Chunks ch = my_chunks(d.n_chunks);
+  for (int64_t c = ch.first; c < ch.end; c += ch.step) {
+    const Lane l = pose_lane<W>(c, d.n);
+    const int64_t e = 6 * l.i + l.a;
+    const double b = (l.on && l.i >= d.n_fixed) ? -d.g[e] : 0.0;
+    const double z = apply_sym6(d.Minv + kSymVals * l.i, l, b);
+    if (l.on) {
+      d.x[e] = 0.0;
+      d.rv[e] = b;
+      d.z[e] = z;
+      rr += b * b;
+      rz += b * z;
+    }
   }
-  rr = block4_sum(rr, s_rr);
-  rz = block4_sum(rz, s_rz);
+  rr = block_waves_sum<W>(rr, s_rr);
+  rz = block_waves_sum<W>(rz, s_rz);
   if (threadIdx.x == 0) {
     red_arr(d, kRR0)[blockIdx.x] = rr;
     red_arr(d, kRZ0)[blockIdx.x] = rz;
@@ -452,26 +471,12 @@ __device__ __forceinline__ int coup_idx(int side, int a, int b) {
   return b < 3 ? 9 + 3 * b + (a - 3) : (b == a ? 18 : 19);
 }
 
-__global__ __launch_bounds__(256) void k_pcg_a(Dev d, int it) {
-  __shared__ double s_buf[4];
-  __shared__ double s_coup[4][4 * kPosesPerWave * kCoupVals];   // per wavefront: 4 slots x 10 poses
-  __shared__ double s_hdd[4][kPosesPerWave * kSymVals];          // per wavefront: 10 damped blocks
+template <int W>
+__global__ __launch_bounds__(64 * W) void k_pcg_a(Dev d, int it) {
+  __shared__ double s_buf[W];
+  __shared__ double s_coup[W][4 * kPosesPerWave * kCoupVals];   // 4 slots x 10 poses
+  __shared__ double s_hdd[W][kPosesPerWave * kSymVals];          // 10 damped blocks
   if (d.pcg->done) return;
-  const Lane l = pose_lane(d.n);
-  const int64_t e = 6 * l.i + l.a;
-  // loads that do not depend on the stop test; the pose's 21 damped-block
-  // values are fetched once by its six lanes (a, a + 6, a + 12, a + 18)
-  const double zi = d.z[e];
-  double hv4[4];
-  {
-    const double* Hp = d.Hdd + kSymVals * l.i;
-#pragma unroll
-    for (int u = 0; u < 3; ++u) hv4[u] = Hp[6 * u + l.a];
-    hv4[3] = l.a < 3 ? Hp[18 + l.a] : 0.0;
-  }
-  const bool free_pose = l.on && l.i >= d.n_fixed;
-  const int h0 = d.half_ptr[l.i], h1 = free_pose ? d.half_ptr[l.i + 1] : h0;
-  const double pe = d.p[e], qe = d.q[e];
   const double rhs = sqrt(total(d, kBB));
   if (it == 0) {
     if (rhs == 0.0) {
@@ -485,95 +490,111 @@ __global__ __launch_bounds__(256) void k_pcg_a(Dev d, int it) {
       return;
     }
   }
+  const double beta = it > 0 ? total(d, kRZ0 + (it & 1)) / total(d, kRZ0 + ((it + 1) & 1)) : 0.0;
   const int lane = threadIdx.x & 63, grp = lane / 6;
-  double* s_h = s_hdd[threadIdx.x >> 6] + min(grp, kPosesPerWave - 1) * kSymVals;
-  if (lane < 6 * kPosesPerWave) {
-#pragma unroll
-    for (int u = 0; u < 3; ++u) s_h[6 * u + l.a] = hv4[u];
-    if (l.a < 3) s_h[18 + l.a] = hv4[3];
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  double w = 0.0;
-#pragma unroll
-  for (int b = 0; b < 6; ++b) w += s_h[sym_idx(l.a, b)] * __shfl(zi, l.base + b, 64);
-  // Half edges four at a time, so that their gathers are in flight together.
-  // Past the end of the list the last entry is loaded again and its terms are
-  // zeroed (w + 0 * z is w), so the terms still add up in list order.  The six
-  // lanes of a pose share the loads: lane a fetches element a of the other
-  // end's z, passed to the group by shuffles, and 16-byte pieces a and a + 6
-  // of the 20-double coupling block, staged in the wavefront's LDS rows, from
-  // which each lane reads its six coefficients.
   double* s_c = s_coup[threadIdx.x >> 6];
-  for (int h = h0; h < h1; h += 4) {
-    int2 nb[4];
+  double* s_h = s_hdd[threadIdx.x >> 6] + min(grp, kPosesPerWave - 1) * kSymVals;
+  double pq = 0.0;
+  const Chunks ch = my_chunks(d.n_chunks);
+  for (int64_t c = ch.first; c < ch.end; c += ch.step) {
+    const Lane l = pose_lane<W>(c, d.n);
+    const int64_t e = 6 * l.i + l.a;
+    // the pose's 21 damped-block values are fetched once by its six lanes
+    // (a, a + 6, a + 12, a + 18) and passed through LDS
+    const double zi = d.z[e];
+    double hv4[4];
+    {
+      const double* Hp = d.Hdd + kSymVals * l.i;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) nb[k] = d.nbr[min(h + k, h1 - 1)];
-    double2 c0[4], c1[4];
-    double zk[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const double2* src = reinterpret_cast<const double2*>(d.Hc + kCoupVals * (int64_t)(nb[k].x >> 1));
-      c0[k] = src[l.a];
-      c1[k] = l.a < 4 ? src[6 + l.a] : make_double2(0.0, 0.0);
-      zk[k] = d.z[6 * (int64_t)nb[k].y + l.a];
+      for (int u = 0; u < 3; ++u) hv4[u] = Hp[6 * u + l.a];
+      hv4[3] = l.a < 3 ? Hp[18 + l.a] : 0.0;
     }
+    const bool free_pose = l.on && l.i >= d.n_fixed;
+    const int h0 = d.half_ptr[l.i], h1 = free_pose ? d.half_ptr[l.i + 1] : h0;
+    const double pe = d.p[e], qe = d.q[e];
     if (lane < 6 * kPosesPerWave) {
 #pragma unroll
+      for (int u = 0; u < 3; ++u) s_h[6 * u + l.a] = hv4[u];
+      if (l.a < 3) s_h[18 + l.a] = hv4[3];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    double w = 0.0;
+#pragma unroll
+    for (int b = 0; b < 6; ++b) w += s_h[sym_idx(l.a, b)] * __shfl(zi, l.base + b, 64);
+    // Half edges four at a time, so that their gathers are in flight
+    // together.  Past the end of the list the last entry is loaded again and
+    // its terms are zeroed (w + 0 * z is w), so the terms still add up in list
+    // order.  The six lanes of a pose share the loads: lane a fetches element
+    // a of the other end's z, passed to the group by shuffles, and 16-byte
+    // pieces a and a + 6 of the 20-double coupling block, staged in the
+    // wavefront's LDS rows, from which each lane reads its six coefficients.
+    for (int h = h0; h < h1; h += 4) {
+      int2 nb[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) nb[k] = d.nbr[min(h + k, h1 - 1)];
+      double2 c0[4], c1[4];
+      double zk[4];
+#pragma unroll
       for (int k = 0; k < 4; ++k) {
-        double* row = s_c + (k * kPosesPerWave + grp) * kCoupVals;
-        row[2 * l.a] = c0[k].x;
-        row[2 * l.a + 1] = c0[k].y;
-        if (l.a < 4) {
-          row[12 + 2 * l.a] = c1[k].x;
-          row[13 + 2 * l.a] = c1[k].y;
+        const double2* src = reinterpret_cast<const double2*>(d.Hc + kCoupVals * (int64_t)(nb[k].x >> 1));
+        c0[k] = src[l.a];
+        c1[k] = l.a < 4 ? src[6 + l.a] : make_double2(0.0, 0.0);
+        zk[k] = d.z[6 * (int64_t)nb[k].y + l.a];
+      }
+      if (lane < 6 * kPosesPerWave) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          double* row = s_c + (k * kPosesPerWave + grp) * kCoupVals;
+          row[2 * l.a] = c0[k].x;
+          row[2 * l.a + 1] = c0[k].y;
+          if (l.a < 4) {
+            row[12 + 2 * l.a] = c1[k].x;
+            row[13 + 2 * l.a] = c1[k].y;
+          }
         }
       }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const double* row = s_c + (k * kPosesPerWave + min(grp, kPosesPerWave - 1)) * kCoupVals;
-      const bool live = h + k < h1;
-      const int side = nb[k].x & 1;
+      for (int k = 0; k < 4; ++k) {
+        const double* row = s_c + (k * kPosesPerWave + min(grp, kPosesPerWave - 1)) * kCoupVals;
+        const bool live = h + k < h1;
+        const int side = nb[k].x & 1;
 #pragma unroll
-      for (int b = 0; b < 6; ++b) {
-        const double v = row[coup_idx(side, l.a, b)];
-        w += (live ? v : 0.0) * __shfl(zk[k], l.base + b, 64);
+        for (int b = 0; b < 6; ++b) {
+          const double v = row[coup_idx(side, l.a, b)];
+          w += (live ? v : 0.0) * __shfl(zk[k], l.base + b, 64);
+        }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (l.on) {
+      double pn = zi, qn = w;
+      if (it > 0) {
+        pn = zi + beta * pe;
+        qn = w + beta * qe;
+      }
+      d.p[e] = pn;
+      d.q[e] = qn;
+      pq += pn * qn;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  const double beta = it > 0 ? total(d, kRZ0 + (it & 1)) / total(d, kRZ0 + ((it + 1) & 1)) : 0.0;
-  double pn = 0.0, qn = 0.0;
-  if (l.on) {
-    pn = zi;
-    qn = w;
-    if (it > 0) {
-      pn = zi + beta * pe;
-      qn = w + beta * qe;
-    }
-    d.p[e] = pn;
-    d.q[e] = qn;
-  }
-  const double pq = block4_sum(l.on ? pn * qn : 0.0, s_buf);
+  pq = block_waves_sum<W>(pq, s_buf);
   if (threadIdx.x == 0) red_arr(d, kPQ)[blockIdx.x] = pq;
 }
 
-__global__ __launch_bounds__(256) void k_pcg_b(Dev d, int it) {
-  __shared__ double s_rr[4], s_rz[4];
+template <int W>
+__global__ __launch_bounds__(64 * W) void k_pcg_b(Dev d, int it) {
+  __shared__ double s_rr[W], s_rz[W];
   if (d.pcg->done) return;
-  const Lane l = pose_lane(d.n);
-  const int64_t e = 6 * l.i + l.a;
-  double mrow[6];
-#pragma unroll
-  for (int b = 0; b < 6; ++b) mrow[b] = d.Minv[kSymVals * l.i + sym_idx(l.a, b)];
-  const double xe = d.x[e], re = d.rv[e], pe = d.p[e], qe = d.q[e];
   const double pq = total(d, kPQ);
   if (!(pq > 0.0) || !isfinite(pq)) {
     // every block reads its totals before block 0 stops the solve
@@ -582,23 +603,32 @@ __global__ __launch_bounds__(256) void k_pcg_b(Dev d, int it) {
     return;
   }
   const double alpha = total(d, kRZ0 + (it & 1)) / pq;
-  double r = 0.0;
-  if (l.on) {
-    d.x[e] = xe + alpha * pe;
-    r = re - alpha * qe;
-    d.rv[e] = r;
-  }
-  double z = 0.0;
-#pragma unroll
-  for (int b = 0; b < 6; ++b) z += mrow[b] * __shfl(r, l.base + b, 64);
   double rr = 0.0, rz = 0.0;
-  if (l.on) {
-    d.z[e] = z;
-    rr = r * r;
-    rz = r * z;
+  const Chunks ch = my_chunks(d.n_chunks);
+  for (int64_t c = ch.first; c < ch.end; c += ch.step) {
+    const Lane l = pose_lane<W>(c, d.n);
+    const int64_t e = 6 * l.i + l.a;
+    double mrow[6];
+#pragma unroll
+    for (int b = 0; b < 6; ++b) mrow[b] = d.Minv[kSymVals * l.i + sym_idx(l.a, b)];
+    const double xe = d.x[e], re = d.rv[e], pe = d.p[e], qe = d.q[e];
+    double r = 0.0;
+    if (l.on) {
+      d.x[e] = xe + alpha * pe;
+      r = re - alpha * qe;
+      d.rv[e] = r;
+    }
+    double z = 0.0;
+#pragma unroll
+    for (int b = 0; b < 6; ++b) z += mrow[b] * __shfl(r, l.base + b, 64);
+    if (l.on) {
+      d.z[e] = z;
+      rr += r * r;
+      rz += r * z;
+    }
   }
-  rr = block4_sum(rr, s_rr);
-  rz = block4_sum(rz, s_rz);
+  rr = block_waves_sum<W>(rr, s_rr);
+  rz = block_waves_sum<W>(rz, s_rz);
   if (threadIdx.x == 0) {
     red_arr(d, kRR0 + ((it + 1) & 1))[blockIdx.x] = rr;
     red_arr(d, kRZ0 + ((it + 1) & 1))[blockIdx.x] = rz;
@@ -610,31 +640,6 @@ __global__ __launch_bounds__(64) void k_pcg_final(Dev d, int iters) {
   const double rhs = sqrt(total(d, kBB));
   const double res = iters == 0 ? rhs : sqrt(total(d, kRR0 + (iters & 1)));
   if (threadIdx.x == 0) stop_pcg(d, iters, res, rhs, 0);
-}
-
-// One block: the totals of the partial arrays in `mask`, each summed in a
-// fixed order (thread t takes entries t, t + 1024, ... in four interleaved
-// accumulators, then a fixed tree over the block).
-__global__ __launch_bounds__(1024) void k_pcg_sum(Dev d, unsigned mask) {
-  __shared__ double s_buf[16];
-  if (d.pcg->done) return;
-  const int nb = d.red_nb;
-  for (int k = 0; k < kNumSums; ++k) {
-    if (!((mask >> k) & 1)) continue;
-    const double* a = red_arr(d, k);
-    double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
-    int j = threadIdx.x;
-    for (; j + 3 * 1024 < nb; j += 4 * 1024) {
-      v0 += a[j];
-      v1 += a[j + 1024];
-      v2 += a[j + 2048];
-      v3 += a[j + 3072];
-    }
-    for (; j < nb; j += 1024) v0 += a[j];
-    const double t = block_sum((v0 + v1) + (v2 + v3), s_buf);
-    if (threadIdx.x == 0) d.scal[k] = t;
-    __syncthreads();
-  }
 }
 
 // Trial poses: q(R) (x) q(dphi) in the hemisphere q_w >= 0, back to axis-angle
@@ -745,7 +750,15 @@ DispatchEvents& dispatch_events() {
   return ev;
 }
 
-int red_blocks(int64_t n) { return (int)((n + kPosesPerBlock - 1) / kPosesPerBlock); }
+int pcg_waves(int64_t n) {
+  return (n + kBigPcgWaves * kPosesPerWave - 1) / (kBigPcgWaves * kPosesPerWave) >= kMaxPcgBlocks
+             ? kBigPcgWaves : kSmallPcgWaves;
+}
+int64_t pcg_chunks(int64_t n) {
+  const int64_t c = (int64_t)pcg_waves(n) * kPosesPerWave;
+  return (n + c - 1) / c;
+}
+int red_blocks(int64_t n) { return (int)std::max<int64_t>(std::min<int64_t>(pcg_chunks(n), kMaxPcgBlocks), 1); }
 int edge_blocks(int64_t m) { return (int)std::max<int64_t>((m + 255) / 256, 1); }
 
 void launch_prep(const double* poses, double* tab, int64_t n, hipStream_t s) {
@@ -758,15 +771,23 @@ void launch_edge(const Dev& d, hipStream_t s) {
   launch(k_edge, dim3(edge_blocks(d.m)), dim3(256), s, d);
 }
 void launch_pose(const Dev& d, hipStream_t s) { launch(k_pose, dim3(blocks(d.n, 128)), dim3(128), s, d); }
-void launch_pcg_init(const Dev& d, hipStream_t s) { launch(k_pcg_init, dim3(d.red_nb), dim3(256), s, d); }
-void launch_pcg_sum(const Dev& d, unsigned mask, hipStream_t s) {
-  if (!d.inline_sums) launch(k_pcg_sum, dim3(1), dim3(1024), s, d, mask);
+void launch_pcg_init(const Dev& d, hipStream_t s) {
+  if (pcg_waves(d.n) == kBigPcgWaves)
+    launch(k_pcg_init<kBigPcgWaves>, dim3(d.red_nb), dim3(64 * kBigPcgWaves), s, d);
+  else
+    launch(k_pcg_init<kSmallPcgWaves>, dim3(d.red_nb), dim3(64 * kSmallPcgWaves), s, d);
 }
 void launch_pcg_a(const Dev& d, int it, hipStream_t s) {
-  launch(k_pcg_a, dim3(d.red_nb), dim3(256), s, d, it);
+  if (pcg_waves(d.n) == kBigPcgWaves)
+    launch(k_pcg_a<kBigPcgWaves>, dim3(d.red_nb), dim3(64 * kBigPcgWaves), s, d, it);
+  else
+    launch(k_pcg_a<kSmallPcgWaves>, dim3(d.red_nb), dim3(64 * kSmallPcgWaves), s, d, it);
 }
 void launch_pcg_b(const Dev& d, int it, hipStream_t s) {
-  launch(k_pcg_b, dim3(d.red_nb), dim3(256), s, d, it);
+  if (pcg_waves(d.n) == kBigPcgWaves)
+    launch(k_pcg_b<kBigPcgWaves>, dim3(d.red_nb), dim3(64 * kBigPcgWaves), s, d, it);
+  else
+    launch(k_pcg_b<kSmallPcgWaves>, dim3(d.red_nb), dim3(64 * kSmallPcgWaves), s, d, it);
 }
 void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
   launch(k_pcg_final, dim3(1), dim3(64), s, d, iters);

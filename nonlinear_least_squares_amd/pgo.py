@@ -26,7 +26,7 @@ PGO_STAGE_LINEARIZE, PGO_STAGE_STEP = 1, 2
 DBG = dict(r=0, Ji=1, Jj=2, Hd=3, Ho=4, g=5, dx=6, pcg=7)
 DBG_SHAPE = dict(r=(-1, 6), Ji=(-1, 6, 6), Jj=(-1, 6, 6), Hd=(-1, 6, 6), Ho=(-1, 6, 6),
                  g=(-1, 6), dx=(-1, 6), pcg=(2,))
-KERNELS = ["prep", "edge", "pose", "pcg_a", "pcg_b", "retract", "cost", "pcg_sum"]
+KERNELS = ["prep", "edge", "pose", "pcg_a", "pcg_b", "retract", "cost"]
 
 
 class pgo_options(C.Structure):

@@ -24,16 +24,21 @@ pgomod = pytest.importorskip("nonlinear_least_squares_amd.pgo")
 BLOCK_TOL = 1e-10
 
 # ragged: 91 poses (not a multiple of the ten poses a PCG wavefront holds),
-# 168 edges (less than one 256-edge block); medium: 1,000 PCG blocks, whose
-# partial sums go through the one-block reduction kernel (the others sum
-# them inside every block)
+# 168 edges (less than one 256-edge block); medium: 250 PCG chunks of 40
+# poses (blocks of four wavefronts), one per block; mid: 12,000 poses in 300
+# chunks of 40 and multi: 44,000 poses in 275 chunks of 160 (blocks of
+# sixteen wavefronts), so that some of the 256 PCG blocks take two chunks
+# (linearisation and PCG steps only: the oracle's LM runs take minutes there)
 CASES = [("tiny", {}), ("ragged", dict(n_rings=7, per_ring=13)), ("small", {}), ("sphere", {}),
          ("medium", {})]
+STEP_CASES = CASES + [("mid", dict(n_rings=100, per_ring=120)),
+                      ("multi", dict(n_rings=220, per_ring=200))]
 
 
 def scene(name, **kw):
-    if name == "ragged":
-        return pgo_scene("tiny", **CASES[1][1], **kw)
+    over = dict(STEP_CASES)[name]
+    if over:
+        return pgo_scene("tiny" if name == "ragged" else "medium", **over, **kw)
     return pgo_scene(name, **kw)
 
 
@@ -54,7 +59,7 @@ def blocks_close(name, got, ref, tol=BLOCK_TOL):
     return worst
 
 
-@pytest.mark.parametrize("name", [c[0] for c in CASES])
+@pytest.mark.parametrize("name", [c[0] for c in STEP_CASES])
 def test_linearization_parity(name):
     sc = scene(name)
     print(f"pgo linearize {name}: {len(sc['poses'])} poses, {len(sc['edges'])} edges", flush=True)
@@ -67,7 +72,7 @@ def test_linearization_parity(name):
         blocks_close(key, gpu.debug_get(key), orc.get(key))
 
 
-@pytest.mark.parametrize("name", [c[0] for c in CASES])
+@pytest.mark.parametrize("name", [c[0] for c in STEP_CASES])
 def test_pcg_step_parity_at_equal_iterations(name):
     sc = scene(name)
     k = 12
