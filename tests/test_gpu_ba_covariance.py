@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from synthetic import ba_scene
-from test_gpu_ba_parity import EPS
+from test_gpu_ba_parity import EPS, _edge_scene
 
 pytestmark = pytest.mark.gpu
 
@@ -111,3 +111,25 @@ def test_covariance_device_output_and_solver_check():
     with pytest.raises(bamod.BAError) as e:
         pcg.covariance()
     assert e.value.code == bamod.BA_ERR_ARG
+
+
+def test_covariance_edge_scene():
+    """Repeated (camera, point) runs, a 700-observation point, an unobserved
+    point, and an unobserved camera, whose block is the inverse of its damped
+    B~ alone (floored diagonal)."""
+    sc = _edge_scene()
+    gpu, orc = make_pair(sc)
+    gpu.set_state(1e-2)
+    orc.lam = 1e-2
+    nc = len(sc["cams"])
+    cov = gpu.covariance()
+    S = gpu.debug_get("S")
+    cov_ref = orc.covariance()
+    S_ref = orc.explicit_S()
+    n = 9 * nc
+    dS = np.linalg.norm(S - S_ref, 2) / np.linalg.norm(S_ref, 2)
+    assert dS < 1e-9, dS
+    kappa = np.linalg.cond(S_ref)
+    inv_norm = 1.0 / np.linalg.eigvalsh(S_ref)[0]
+    check_blocks("oracle", cov, cov_ref, (kappa * (dS + 8 * n * EPS) + 1e-12) * inv_norm)
+    np.testing.assert_allclose(cov[9], np.linalg.inv(S_ref[81:90, 81:90]), rtol=1e-10)
