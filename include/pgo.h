@@ -113,7 +113,9 @@ enum {
   PGO_DBG_PCG,     /* 2: PCG iterations, relative residual           */
   PGO_DBG_NUM
 };
-/* Number of doubles of one debug array (negative PGO_ERR_ARG for a bad id). */
+/* r, J_i and J_j are stored only by pgo_debug_run (LM steps do not keep
+ * them); the other arrays hold the last step's values.
+ * Number of doubles of one debug array (negative PGO_ERR_ARG for a bad id). */
 int64_t pgo_debug_size(const pgo_problem* h, int which);
 /* Copies it to caller-owned host memory; count must equal pgo_debug_size. */
 int pgo_debug_get(pgo_problem* h, int which, double* out, int64_t count);

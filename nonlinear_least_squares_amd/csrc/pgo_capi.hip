@@ -206,9 +206,9 @@ int prof_collect(pgo_problem* h, int pcg_iters) {
     CHECK_RC(prof_end(h, stop_));                     \
   } while (0)
 
-int stage_linearize(pgo_problem* h) {
+int stage_linearize(pgo_problem* h, bool jac) {
   Dev d = make_dev(h);
-  TIMED(PGO_K_EDGE, -1, launch_edge(d, h->stream));
+  TIMED(PGO_K_EDGE, -1, launch_edge(d, jac, h->stream));
   HIPC(hipGetLastError());
   return PGO_OK;
 }
@@ -267,7 +267,7 @@ int current_cost(pgo_problem* h, double* c) {
 }
 
 int lm_step(pgo_problem* h, pgo_step_info* info) {
-  if (!h->linearized) CHECK_RC(stage_linearize(h));
+  if (!h->linearized) CHECK_RC(stage_linearize(h, false));
   h->linearized = 1;
   CHECK_RC(stage_step(h));
   Dev d = make_dev(h);
@@ -506,7 +506,7 @@ int pgo_get_lambda(const pgo_problem* h, double* lambda_out) {
 
 int pgo_debug_run(pgo_problem* h, int upto) {
   if (!h || upto < PGO_STAGE_LINEARIZE || upto > PGO_STAGE_STEP) return fail(PGO_ERR_ARG, "bad arguments");
-  CHECK_RC(stage_linearize(h));
+  CHECK_RC(stage_linearize(h, true));
   h->linearized = 1;
   if (upto >= PGO_STAGE_STEP) {
     CHECK_RC(stage_step(h));

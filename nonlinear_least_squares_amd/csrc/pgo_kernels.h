@@ -12,7 +12,8 @@
 //   per pose : the damped diagonal block and its inverse are symmetric and
 //              kept as their upper triangles, row by row (kSymVals)
 //   per half edge (2m, side 0 = the edge's i, side 1 = its j): that end's
-//              contribution to its diagonal block (36) and to g (6); each
+//              contribution to its diagonal block (36) and to g (6), side-major
+//              (row side m + e); each
 //              pose lists its half edges in edge order (CSR) as pairs (half
 //              edge id 2 e + side, pose at the other end), so every sum has a
 //              fixed order and the product's gathers depend on one load
@@ -65,7 +66,7 @@ struct Dev {
   double* Ji;              // m x 36
   double* Jj;              // m x 36
   double* Hc;              // m x kCoupVals
-  double* half;            // 2m x kHalfVals
+  double* half;            // 2m x kHalfVals, side-major
   double* cost_part;       // per edge-kernel block
   int n_cost_parts;
   double* Hd;              // n x 36 undamped
@@ -94,7 +95,8 @@ int64_t pcg_chunks(int64_t n);
 int edge_blocks(int64_t m);
 void launch_prep(const double* poses, double* tab, int64_t n, hipStream_t s);
 void launch_meas_prep(const double* meas, double* meas_tab, int64_t m, hipStream_t s);
-void launch_edge(const Dev& d, hipStream_t s);
+// jac: also store r, J_i and J_j (for inspection).
+void launch_edge(const Dev& d, bool jac, hipStream_t s);
 void launch_pose(const Dev& d, hipStream_t s);
 void launch_pcg_init(const Dev& d, hipStream_t s);
 

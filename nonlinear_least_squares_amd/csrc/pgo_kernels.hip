@@ -157,7 +157,11 @@ __device__ __forceinline__ double block_sum(double v, double* s_buf) {
 }
 
 // Per edge: residual, Jacobians, the three blocks of J^T Omega J, both ends'
-// g parts, and a per-block partial of the cost.
+// g parts, and a per-block partial of the cost.  The residual and the
+// Jacobian blocks are stored only for inspection (kJac); the products are
+// written as 16-byte pieces, the ends' shares side-major (all side-0 rows in
+// edge order, then all side-1 rows).
+template <bool kJac>
 __global__ __launch_bounds__(256) void k_edge(Dev d) {
   __shared__ double s_buf[4];
   const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -167,24 +171,26 @@ __global__ __launch_bounds__(256) void k_edge(Dev d) {
     c = edge_eval(d, d.tab, e, r, Jr, A, u, Q);
     const double wR = d.info[2 * e], wt = d.info[2 * e + 1];
     const double U[9] = {0.0, -u[2], u[1], u[2], 0.0, -u[0], -u[1], u[0], 0.0};
-    // Jacobians, row-major 6x6
-    double* Ji = d.Ji + 36 * e;
-    double* Jj = d.Jj + 36 * e;
+    if (kJac) {
+      // Jacobians, row-major 6x6
+      double* Ji = d.Ji + 36 * e;
+      double* Jj = d.Jj + 36 * e;
 #pragma unroll
-    for (int a = 0; a < 3; ++a)
+      for (int a = 0; a < 3; ++a)
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
-        Ji[6 * a + b] = A[3 * a + b];
-        Ji[6 * a + 3 + b] = 0.0;
-        Ji[6 * (3 + a) + b] = U[3 * a + b];
-        Ji[6 * (3 + a) + 3 + b] = -Q[3 * a + b];
-        Jj[6 * a + b] = Jr[3 * a + b];
-        Jj[6 * a + 3 + b] = 0.0;
-        Jj[6 * (3 + a) + b] = 0.0;
-        Jj[6 * (3 + a) + 3 + b] = Q[3 * a + b];
-      }
+        for (int b = 0; b < 3; ++b) {
+          Ji[6 * a + b] = A[3 * a + b];
+          Ji[6 * a + 3 + b] = 0.0;
+          Ji[6 * (3 + a) + b] = U[3 * a + b];
+          Ji[6 * (3 + a) + 3 + b] = -Q[3 * a + b];
+          Jj[6 * a + b] = Jr[3 * a + b];
+          Jj[6 * a + 3 + b] = 0.0;
+          Jj[6 * (3 + a) + b] = 0.0;
+          Jj[6 * (3 + a) + 3 + b] = Q[3 * a + b];
+        }
 #pragma unroll
-    for (int k = 0; k < 6; ++k) d.r[6 * e + k] = r[k];
+      for (int k = 0; k < 6; ++k) d.r[6 * e + k] = r[k];
+    }
     double AtA[9], UtU[9], UtQ[9], QtQ[9], JtJ[9], AtJ[9];
     mat3_tmul(A, A, AtA);
     mat3_tmul(U, U, UtU);
@@ -192,9 +198,7 @@ __global__ __launch_bounds__(256) void k_edge(Dev d) {
     mat3_tmul(Q, Q, QtQ);
     mat3_tmul(Jr, Jr, JtJ);
     mat3_tmul(A, Jr, AtJ);
-    double* Hi = d.half + kHalfVals * (2 * e);
-    double* Hj = d.half + kHalfVals * (2 * e + 1);
-    double* Hc = d.Hc + kCoupVals * e;
+    double Hi[kHalfVals], Hj[kHalfVals], Hc[kCoupVals];
 #pragma unroll
     for (int a = 0; a < 3; ++a)
 #pragma unroll
@@ -223,6 +227,16 @@ __global__ __launch_bounds__(256) void k_edge(Dev d) {
       Hj[36 + a] = wR * jR;
       Hj[39 + a] = wt * qT;
     }
+    double2* hi = reinterpret_cast<double2*>(d.half + kHalfVals * e);
+    double2* hj = reinterpret_cast<double2*>(d.half + kHalfVals * (d.m + e));
+    double2* hc = reinterpret_cast<double2*>(d.Hc + kCoupVals * e);
+#pragma unroll
+    for (int k = 0; k < kHalfVals / 2; ++k) {
+      hi[k] = make_double2(Hi[2 * k], Hi[2 * k + 1]);
+      hj[k] = make_double2(Hj[2 * k], Hj[2 * k + 1]);
+    }
+#pragma unroll
+    for (int k = 0; k < kCoupVals / 2; ++k) hc[k] = make_double2(Hc[2 * k], Hc[2 * k + 1]);
   }
   const double t = block_sum(c, s_buf);
   if (threadIdx.x == 0) d.cost_part[blockIdx.x] = t;
@@ -284,11 +298,21 @@ __global__ __launch_bounds__(128) void k_pose(Dev d) {
 #pragma unroll
   for (int k = 0; k < 6; ++k) g[k] = 0.0;
   for (int h = d.half_ptr[i]; h < d.half_ptr[i + 1]; ++h) {
-    const double* src = d.half + kHalfVals * (int64_t)d.nbr[h].x;
+    const int hid = d.nbr[h].x;   // 2 e + side; rows are side-major
+    const double2* src =
+        reinterpret_cast<const double2*>(d.half + kHalfVals * ((hid & 1) * d.m + (hid >> 1)));
 #pragma unroll
-    for (int k = 0; k < 36; ++k) H[k] += src[k];
+    for (int k = 0; k < 18; ++k) {
+      const double2 v = src[k];
+      H[2 * k] += v.x;
+      H[2 * k + 1] += v.y;
+    }
 #pragma unroll
-    for (int k = 0; k < 6; ++k) g[k] += src[36 + k];
+    for (int k = 0; k < 3; ++k) {
+      const double2 v = src[18 + k];
+      g[2 * k] += v.x;
+      g[2 * k + 1] += v.y;
+    }
   }
 #pragma unroll
   for (int k = 0; k < 36; ++k) d.Hd[36 * i + k] = H[k];
@@ -767,8 +791,9 @@ void launch_prep(const double* poses, double* tab, int64_t n, hipStream_t s) {
 void launch_meas_prep(const double* meas, double* meas_tab, int64_t m, hipStream_t s) {
   if (m > 0) launch(k_prep, dim3(blocks(m, 256)), dim3(256), s, meas, meas_tab, m);
 }
-void launch_edge(const Dev& d, hipStream_t s) {
-  launch(k_edge, dim3(edge_blocks(d.m)), dim3(256), s, d);
+void launch_edge(const Dev& d, bool jac, hipStream_t s) {
+  if (jac) launch(k_edge<true>, dim3(edge_blocks(d.m)), dim3(256), s, d);
+  else launch(k_edge<false>, dim3(edge_blocks(d.m)), dim3(256), s, d);
 }
 void launch_pose(const Dev& d, hipStream_t s) { launch(k_pose, dim3(blocks(d.n, 128)), dim3(128), s, d); }
 void launch_pcg_init(const Dev& d, hipStream_t s) {
