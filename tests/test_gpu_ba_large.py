@@ -101,3 +101,21 @@ def test_large_one_lm_step(large):
     if abs(oi["cost_after"] - oi["cost_before"]) > 1e-10 * oi["cost_before"]:
         assert gi["accepted"] == oi["accepted"]
     assert gi["pcg_iters"] == oi["pcg_iters"]
+
+
+def test_large_one_dogleg_step(large):
+    """One dogleg iteration at full size.  The first radius (1.0) is far below
+    the Gauss-Newton step, so the step is the cut steepest descent (or a blend
+    when the Cauchy point falls inside): the kind, the radius and the norm
+    match the oracle's; the trial cost is held to 1e-6 when the step does not
+    depend on a Gauss-Newton solve that stopped at its iteration cap."""
+    sc = large
+    g = bamod.Problem.from_scene(sc, strategy=bamod.BA_STRATEGY_DOGLEG)
+    gi = g.lm_step()
+    o = oracle.Problem.from_scene(sc, strategy=1)
+    oi = o.lm_step()
+    assert abs(gi["cost_before"] - oi["cost_before"]) <= 1e-10 * oi["cost_before"]
+    assert gi["step_kind"] == oi["step_kind"] and gi["radius"] == oi["radius"] == 1.0
+    assert abs(gi["step_norm"] - oi["step_norm"]) <= 1e-6 * oi["step_norm"]
+    if oi["step_kind"] == 1 or oi["pcg_rel_res"] <= sc["pcg_rel_tol"]:
+        assert abs(gi["cost_after"] - oi["cost_after"]) <= 1e-6 * oi["cost_after"]
