@@ -690,7 +690,7 @@ def main():
     if args.copy_calibration:
         return copy_calibration()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the libraries have no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     if args.workload == "dense":
