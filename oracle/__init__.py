@@ -127,6 +127,7 @@ def _droid_signatures(L):
     L.dorc_destroy.argtypes = [vp]
     L.dorc_cost.argtypes = [vp, dp]
     L.dorc_gn_step.argtypes = [vp, dp, dp]
+    L.dorc_covariance.argtypes = [vp, dp]
     L.dorc_get.argtypes = [vp, C.c_int, vp]
     L.dorc_size.argtypes = [vp, C.c_int]
     L.dorc_size.restype = C.c_int64

@@ -82,6 +82,16 @@ class DroidProblem:
             raise RuntimeError(f"dorc_cost failed: {rc}")
         return c.value
 
+    def covariance(self):
+        """Pose marginal covariance S^-1 of the free poses at the current state
+        (nv x nv, nv = 6 free poses), from the Cholesky factor of S."""
+        nv = 6 * (self.n - self.n_fixed)
+        out = np.empty(nv * nv)
+        rc = lib().dorc_covariance(self.h, out.ctypes.data_as(C.POINTER(C.c_double)))
+        if rc != 0:
+            raise RuntimeError(f"dorc_covariance failed: {rc}")
+        return out.reshape(nv, nv)
+
     def gn_step(self):
         c0, c1 = C.c_double(), C.c_double()
         rc = lib().dorc_gn_step(self.h, C.byref(c0), C.byref(c1))

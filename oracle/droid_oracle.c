@@ -254,11 +254,12 @@ static int chol(double* A, int n) {
 /* One Gauss-Newton step ([THESEUS] linearise, solve, retract) with the depths
  * eliminated by the Schur complement ([NSLAM] sec. 3.2).  The step is applied
  * unconditionally.  cost_before / cost_after may be NULL. */
-int dorc_gn_step(dorc* h, double* cost_before, double* cost_after) {
+/* Linearisation, B, g_c, C, g_d, and the reduced pose system S, rhs at the
+ * current state (the first part of a Gauss-Newton step). */
+static void dorc_assemble(dorc* h) {
   int n = h->n, nf = h->nf;
   int64_t P = h->P, N6 = 6 * (int64_t)n, nv = 6 * (int64_t)(n - nf);
   double K[4] = {h->fx, h->fy, h->cx, h->cy};
-  if (cost_before) *cost_before = dorc_cost_value(h);
   memset(h->B, 0, 8 * N6 * N6);
   memset(h->gc, 0, 8 * N6);
   memset(h->C, 0, 8 * n * P);
@@ -326,6 +327,43 @@ int dorc_gn_step(dorc* h, double* cost_before, double* cost_after) {
       }
     }
   }
+  free(col);
+}
+
+/* Pose marginal covariance, the notes' cov_cam ([NSLAM] sec. 3.2, the dense
+ * reference step): S factored by Cholesky and S^-1 obtained by solving
+ * against the identity, column by column (S is never inverted directly).
+ * At the current state; out is nv x nv (nv = 6 free poses), row-major. */
+int dorc_covariance(dorc* h, double* out) {
+  dorc_assemble(h);
+  const int64_t nv = 6 * (int64_t)(h->n - h->nf);
+  double* L = (double*)malloc(8 * (nv * nv + 1));
+  double* y = (double*)calloc(nv + 1, 8);
+  memcpy(L, h->S, 8 * nv * nv);
+  int rc = chol(L, (int)nv);
+  for (int64_t c = 0; c < nv && rc == 0; c++) {
+    for (int64_t a = 0; a < nv; a++) {
+      double s = a == c ? 1.0 : 0.0;
+      for (int64_t l = 0; l < a; l++) s -= L[a * nv + l] * y[l];
+      y[a] = s / L[a * nv + a];
+    }
+    for (int64_t a = nv - 1; a >= 0; a--) {
+      double s = y[a];
+      for (int64_t l = a + 1; l < nv; l++) s -= L[l * nv + a] * y[l];
+      y[a] = s / L[a * nv + a];
+    }
+    for (int64_t a = 0; a < nv; a++) out[a * nv + c] = y[a];
+  }
+  free(L);
+  free(y);
+  return rc == 0 ? 0 : -3;
+}
+
+int dorc_gn_step(dorc* h, double* cost_before, double* cost_after) {
+  int n = h->n, nf = h->nf;
+  int64_t P = h->P, N6 = 6 * (int64_t)n, nv = 6 * (int64_t)(n - nf);
+  if (cost_before) *cost_before = dorc_cost_value(h);
+  dorc_assemble(h);
   /* dense Cholesky of S and the camera step */
   double* L = (double*)malloc(8 * (nv * nv + 1));
   memcpy(L, h->S, 8 * nv * nv);
@@ -347,10 +385,7 @@ int dorc_gn_step(dorc* h, double* cost_before, double* cost_after) {
     free(y);
   }
   free(L);
-  if (rc != 0) {
-    free(col);
-    return -3;
-  }
+  if (rc != 0) return -3;
   /* depth back-substitution ([NSLAM] sec. 3.2 eq. (1)): dd = (-g_d - E^T dxi) / C */
   for (int i = 0; i < n; i++) {
     for (int64_t p = 0; p < P; p++) {
@@ -368,7 +403,6 @@ int dorc_gn_step(dorc* h, double* cost_before, double* cost_after) {
       h->dd[i * P + p] = c > 0.0 ? s / c : 0.0;
     }
   }
-  free(col);
   /* retraction: T <- Exp(xi) T for the free poses, depths additive */
   for (int i = nf; i < n; i++) {
     double Re[9], te[3], Rn[9], tn[3];

@@ -278,3 +278,23 @@ def test_invalid_inputs_rejected():
     with pytest.raises(RuntimeError):
         droid.DroidProblem(sc["poses"], sc["inv_depth"], sc["intrinsics"], sc["edges"],
                            sc["targets"], sc["weights"], 6, 8, 5)
+
+
+def test_covariance_is_pose_block_of_inverse_normal_matrix():
+    """The pose covariance is the free-pose block of the inverse of the full
+    normal matrix (block inversion: that block is the inverse of the Schur
+    complement of the depths); it is symmetric positive definite."""
+    sc, P = small_problem()
+    cov = P.covariance()
+    J, w, r = dense_system(P, sc)
+    nf, n6 = P.n_fixed, 6 * P.n
+    free = np.r_[6 * nf:n6, n6:J.shape[1]]
+    Jf = J[:, free]
+    H = Jf.T @ (w[:, None] * Jf)
+    nv = n6 - 6 * nf
+    ref = np.linalg.inv(H)[:nv, :nv]
+    np.testing.assert_allclose(cov, ref, rtol=1e-8, atol=1e-10 * abs(ref).max())
+    np.testing.assert_allclose(cov, cov.T, rtol=0, atol=1e-12 * abs(cov).max())
+    assert np.linalg.eigvalsh(cov).min() > 0
+    # covariance times the reduced matrix is the identity
+    np.testing.assert_allclose(cov @ P.get("S"), np.eye(nv), atol=1e-8)
