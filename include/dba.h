@@ -96,6 +96,18 @@ int dba_solve(dba_problem* h, int n_iters, float* costs);
 /* Cost at the current state. */
 int dba_cost(dba_problem* h, float* cost);
 
+/* Pose marginal covariance at the current state: S^-1, the inverse of the
+ * reduced pose system after the depths are eliminated (NeRF-SLAM
+ * reproduction notes, sec. 3.2, the cov_cam output of the dense step).  One
+ * workgroup factors S by Cholesky in LDS and solves against the identity, in
+ * fp32.  cov: caller-owned HOST buffer of nv x nv floats, row-major, nv =
+ * 6 (n_frames - n_fixed) (nothing is written when nv is 0).  The state does
+ * not change; the inspection arrays S, rhs, C and g_d then hold this
+ * linearisation.  DBA_ERR_NOT_SPD (cov untouched) when S is not positive
+ * definite; the first call allocates an nv x nv device buffer that the handle
+ * keeps. */
+int dba_covariance(dba_problem* h, float* cov);
+
 /* Current state to caller-owned host buffers (either may be NULL); poses are
  * normalised with qw >= 0. */
 int dba_get_state(dba_problem* h, float* poses, float* inv_depth);

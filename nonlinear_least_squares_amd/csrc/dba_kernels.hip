@@ -810,6 +810,61 @@ __global__ __launch_bounds__(kSolveThreads) void k_solve(SolveArgs a) {
   }
 }
 
+// Pose marginal covariance S^-1 of the free poses (the NeRF-SLAM notes'
+// cov_cam, sec. 3.2): one workgroup.  Right-looking Cholesky of S in LDS, a
+// column per step (scale the column, barrier, update the trailing lower
+// triangle, barrier), then thread c solves L L^T x = e_c for column c of the
+// inverse, in place in the output (row-major nv x nv, column c written by
+// thread c only).  A prior failure or a pivot that is not positive sets
+// *status and leaves out untouched.
+__global__ __launch_bounds__(kSolveThreads) void k_cov(const float* S_in, int* status,
+                                                       float* out, int nv) {
+  extern __shared__ float sm[];
+  const int pitch = nv + 1, tid = threadIdx.x, bd = blockDim.x;
+  float* L = sm;                 // nv x pitch, lower triangle used
+  float* Ld = L + nv * pitch;    // nv reciprocals of the factor's diagonal
+  for (int e = tid; e < nv * nv; e += bd) L[(e / nv) * pitch + e % nv] = S_in[e];
+  const bool prior_fail = *status != 0;
+  __syncthreads();
+  bool ok = !prior_fail;
+  for (int j = 0; j < nv && ok; ++j) {
+    const float djj = L[j * pitch + j];        // every thread reads the same value
+    ok = djj > 0.0f && isfinite(djj);
+    if (!ok) break;
+    const float inv = 1.0f / sqrtf(djj);
+    for (int i = j + 1 + tid; i < nv; i += bd) L[i * pitch + j] *= inv;
+    if (tid == 0) Ld[j] = inv;   // the diagonal itself stays: other waves may still read it
+    __syncthreads();
+    const int m = nv - j - 1, ty = tid >> 5, tx = tid & 31, nty = bd >> 5;
+    for (int ii = ty; ii < m; ii += nty) {
+      const int i = j + 1 + ii;
+      const float lij = L[i * pitch + j];
+      for (int k = j + 1 + tx; k <= i; k += 32) L[i * pitch + k] -= lij * L[k * pitch + j];
+    }
+    __syncthreads();
+  }
+  if (!ok) {
+    if (tid == 0 && !prior_fail) *status = DBA_ERR_NOT_SPD;
+    return;
+  }
+  const int c = tid;
+  if (c >= nv) return;
+  // forward: y = L^-1 e_c (zero above row c)
+  for (int a = 0; a < c; ++a) out[(int64_t)a * nv + c] = 0.0f;
+  out[(int64_t)c * nv + c] = Ld[c];
+  for (int a = c + 1; a < nv; ++a) {
+    float s = 0.0f;
+    for (int l = c; l < a; ++l) s -= L[a * pitch + l] * out[(int64_t)l * nv + c];
+    out[(int64_t)a * nv + c] = s * Ld[a];
+  }
+  // backward: x = L^-T y
+  for (int a = nv - 1; a >= 0; --a) {
+    float s = out[(int64_t)a * nv + c];
+    for (int l = a + 1; l < nv; ++l) s -= L[l * pitch + a] * out[(int64_t)l * nv + c];
+    out[(int64_t)a * nv + c] = s * Ld[a];
+  }
+}
+
 // Per-residual values for inspection, same device function as the solver.
 __global__ void k_debug_jac(const float* poseRt, const int* edge_i, const int* edge_j,
                             const float* depth, const float* targets, int E, int P, int W,
@@ -915,6 +970,7 @@ struct dba_problem {
   float* h_pin = nullptr;   // pinned: costs + status
   // per-residual inspection buffers (allocated on first use)
   float *dbg_r = nullptr, *dbg_ji = nullptr, *dbg_jj = nullptr, *dbg_jd = nullptr;
+  float* cov_buf = nullptr;   // nv x nv pose covariance (allocated on first use)
   // profiling
   int prof_on = 0;
   int prof_every = 1;
@@ -1320,9 +1376,13 @@ int create(const float* poses, const float* inv_depth, int n, int H, int W, cons
   if (h->lin_lds > 65536)
     HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin<false, true>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lin_lds));
-  if (h->solve_lds > 65536)
+  if (h->solve_lds > 65536) {
     HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_solve),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->solve_lds));
+    // k_cov needs nv (nv + 2) floats, within the solver's size
+    HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cov),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->solve_lds));
+  }
 
   const int64_t P = h->P;
   Arena& A = h->arena;
@@ -1397,7 +1457,7 @@ void dba_destroy(dba_problem* h) {
     (void)hipFree(h->arena.base);
   }
   if (h->h_pin) (void)hipHostFree(h->h_pin);
-  for (float* p : {h->dbg_r, h->dbg_ji, h->dbg_jj, h->dbg_jd})
+  for (float* p : {h->dbg_r, h->dbg_ji, h->dbg_jj, h->dbg_jd, h->cov_buf})
     if (p) (void)hipFree(p);
   for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
   delete h;
@@ -1471,6 +1531,25 @@ int dba_cost(dba_problem* h, float* cost) {
   CHECK_RC((launch_lin<false, false>(h, 1)));
   CHECK_RC(launch_cost_final(h, 0));
   return fetch(h, 1, cost);
+}
+
+int dba_covariance(dba_problem* h, float* cov) {
+  if (!h || !cov) return fail(DBA_ERR_ARG, "null argument");
+  const int64_t nv = h->nv;
+  if (nv == 0) return DBA_OK;
+  if (!h->cov_buf && hipMalloc(&h->cov_buf, sizeof(float) * nv * nv) != hipSuccess) {
+    h->cov_buf = nullptr;
+    return fail(DBA_ERR_ALLOC, "covariance buffer");
+  }
+  CHECK_RC((launch_lin<false, true>(h, 1)));
+  CHECK_RC(launch_assemble(h, -1));
+  hipLaunchKernelGGL(k_cov, dim3(1), dim3(kSolveThreads), h->solve_lds, h->stream, h->S_dbg,
+                     h->status, h->cov_buf, h->nv);
+  HIPC(hipGetLastError());
+  CHECK_RC(fetch(h, 0, nullptr));
+  HIPC(hipMemcpyAsync(cov, h->cov_buf, sizeof(float) * nv * nv, hipMemcpyDeviceToHost, h->stream));
+  HIPC(hipStreamSynchronize(h->stream));
+  return DBA_OK;
 }
 
 int dba_get_state(dba_problem* h, float* poses, float* inv_depth) {

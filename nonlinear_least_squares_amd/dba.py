@@ -52,6 +52,7 @@ SIGNATURES = {
     "dba_get_state": (i32, [vp, vp, vp]),
     "dba_set_state": (i32, [vp, vp, vp]),
     "dba_get_sizes": (i32, [vp, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32), C.POINTER(i32)]),
+    "dba_covariance": (i32, [vp, vp]),
     "dba_debug_run": (i32, [vp, i32]),
     "dba_debug_size": (i64, [vp, i32]),
     "dba_debug_get": (i32, [vp, i32, vp, i64]),
@@ -149,6 +150,13 @@ class Problem:
         c = C.c_float()
         _check(lib().dba_cost(self.h, C.byref(c)), "dba_cost")
         return c.value
+
+    def covariance(self):
+        """Pose marginal covariance S^-1 (nv x nv float32, nv = 6 free poses)."""
+        nv = 6 * (self.n - self.n_fixed)
+        out = np.empty((nv, nv), dtype=np.float32)
+        _check(lib().dba_covariance(self.h, C.c_void_p(out.ctypes.data)), "dba_covariance")
+        return out
 
     def get_state(self):
         poses = np.empty((self.n, 7), dtype=np.float32)

@@ -342,3 +342,39 @@ def test_state_roundtrip(scenes):
     # normalised again on the way in, which may move its last bits
     assert np.array_equal(p[:, :3], p2[:, :3]) and np.array_equal(d, d2)
     np.testing.assert_allclose(p2[:, 3:], p[:, 3:], rtol=0, atol=4 * EPS32)
+
+
+@pytest.mark.parametrize("name", ["small", "mid", "full"])
+def test_pose_covariance(scenes, name):
+    """S^-1 (fp32, one workgroup) against the oracle's fp64 S^-1 at the same
+    state.  First-order perturbation bound for an inverse: the relative
+    Frobenius error is at most kappa(S) d / (1 - kappa(S) d), d the relative
+    difference of the two reduced matrices plus the factorisation's own
+    n eps32; the test allows 4x that.  The state and the cost do not change."""
+    sc = scenes[name]
+    G = gpu().Problem.from_scene(sc)
+    O = odroid.DroidProblem.from_scene(sc)
+    p0, d0 = G.get_state()
+    c0 = G.cost()
+    X = G.covariance().astype(np.float64)
+    ref = O.covariance()
+    S_ref = O.get("S")
+    S_gpu = G.debug_get("S").astype(np.float64)   # this linearisation
+    nv = S_ref.shape[0]
+    kappa = np.linalg.cond(S_ref)
+    d = np.linalg.norm(S_gpu - S_ref) / np.linalg.norm(S_ref) + nv * EPS32
+    assert kappa * d < 0.25, (kappa, d)
+    rel = np.linalg.norm(X - ref) / np.linalg.norm(ref)
+    assert rel <= 4 * kappa * d / (1 - kappa * d), (rel, kappa, d)
+    assert np.linalg.norm(X - X.T) <= 4 * kappa * d * np.linalg.norm(ref)
+    assert np.linalg.eigvalsh(0.5 * (X + X.T)).min() > 0
+    p1, d1 = G.get_state()
+    assert np.array_equal(p0, p1) and np.array_equal(d0, d1)
+    assert G.cost() == c0
+
+
+def test_pose_covariance_all_fixed_is_empty():
+    sc = droid_scene(**SMALL)
+    sc = dict(sc, n_fixed=sc["poses"].shape[0])
+    G = gpu().Problem.from_scene(sc)
+    assert G.covariance().shape == (0, 0)
