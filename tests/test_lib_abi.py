@@ -102,6 +102,7 @@ def test_libdba_host_only_entry_points():
     assert L.dba_gn_step(None, None) == dbamod.DBA_ERR_ARG
     assert L.dba_debug_size(None, 0) == dbamod.DBA_ERR_ARG
     assert L.dba_solve(None, 1, None) == dbamod.DBA_ERR_ARG
+    assert L.dba_covariance(None, None) == dbamod.DBA_ERR_ARG
     # sizes are checked before any device work
     buf = (C.c_float * 16)()
     rc = L.dba_create(buf, buf, 2, 2, 2, buf, None, 0, None, None, 3, None, C.byref(h))
