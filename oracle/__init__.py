@@ -21,6 +21,10 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libba_oracle.so")
+# The same sources built with -fopenmp: loops that own their outputs run on
+# several threads, every sum keeps its observation order, so the results are
+# the plain build's bits (tests/test_oracle_threads.py).
+LIB_OMP = os.path.join(HERE, "libba_oracle_omp.so")
 SOURCES = [os.path.join(HERE, n) for n in ("ba_oracle.c", "droid_oracle.c", "pgo_oracle.c")
            if os.path.exists(os.path.join(HERE, n))]
 
@@ -62,25 +66,29 @@ class StepInfo(C.Structure):
 
 
 def build(force=True):
-    """Compile the oracle with gcc (plain -O2, no FMA contraction)."""
-    if not force and os.path.exists(LIB):
+    """Compile the oracle with gcc (plain -O2, no FMA contraction), once as is
+    and once with OpenMP."""
+    if not force and os.path.exists(LIB) and os.path.exists(LIB_OMP):
         return LIB
-    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-o", LIB + ".tmp",
-           *SOURCES, "-lm"]
-    subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    for out, extra in ((LIB, []), (LIB_OMP, ["-fopenmp"])):
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", *extra, "-o",
+               out + ".tmp", *SOURCES, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(out + ".tmp", out)
     return LIB
 
 
-_lib = None
+_libs = {}
 
 
-def lib():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB):
+def lib(parallel=False):
+    """The oracle library: the plain build, or with ``parallel`` the OpenMP
+    build (threads per OMP_NUM_THREADS)."""
+    if parallel not in _libs:
+        path = LIB_OMP if parallel else LIB
+        if not os.path.exists(path):
             build()
-        L = C.CDLL(LIB)
+        L = C.CDLL(path)
         d, i64, i32p = C.c_double, C.c_int64, C.POINTER(C.c_int32)
         dp, vp = C.POINTER(C.c_double), C.c_void_p
         L.orc_create.argtypes = [dp, i64, dp, i64, i32p, i32p, dp, i64, C.POINTER(Opts),
@@ -113,10 +121,16 @@ def lib():
         L.orc_retract_camera.argtypes = [dp, dp, dp]
         L.orc_so3_exp.argtypes = [dp, dp]
         L.orc_opts_default.argtypes = [C.POINTER(Opts)]
+        L.orc_num_threads.restype = C.c_int
         if hasattr(L, "dorc_create"):
             _droid_signatures(L)
-        _lib = L
-    return _lib
+        _libs[parallel] = L
+    return _libs[parallel]
+
+
+def num_threads(parallel=False):
+    """Threads the oracle's loops run on."""
+    return lib(parallel).orc_num_threads()
 
 
 def _droid_signatures(L):
@@ -158,8 +172,8 @@ def opts_for_scene(sc, **kw):
 class Problem:
     """Thin ctypes handle around ``orc_problem``."""
 
-    def __init__(self, cams, points, obs_cam, obs_pt, obs_uv, opts=None):
-        L = lib()
+    def __init__(self, cams, points, obs_cam, obs_pt, obs_uv, opts=None, parallel=False):
+        L = self._L = lib(parallel)
         self._keep = [np.ascontiguousarray(cams, dtype=np.float64),
                       np.ascontiguousarray(points, dtype=np.float64),
                       np.ascontiguousarray(obs_cam, dtype=np.int32),
@@ -175,20 +189,20 @@ class Problem:
             raise RuntimeError(f"orc_create failed: {rc}")
 
     @classmethod
-    def from_scene(cls, sc, **kw):
+    def from_scene(cls, sc, parallel=False, **kw):
         return cls(sc["cams"], sc["points"], sc["obs_cam"], sc["obs_pt"], sc["obs_uv"],
-                   opts_for_scene(sc, **kw))
+                   opts_for_scene(sc, **kw), parallel=parallel)
 
     def __del__(self):
         if getattr(self, "h", None) and self.h.value:
-            lib().orc_destroy(self.h)
+            self._L.orc_destroy(self.h)
             self.h = C.c_void_p()
 
     def get(self, name):
         which = NAMES[name]
-        n = lib().orc_array_size(self.h, which)
+        n = self._L.orc_array_size(self.h, which)
         out = np.empty(n, dtype=np.int32 if which in INT_ARRAYS else np.float64)
-        lib().orc_get(self.h, which, out.ctypes.data_as(C.c_void_p))
+        self._L.orc_get(self.h, which, out.ctypes.data_as(C.c_void_p))
         shapes = {"cams": (-1, 9), "points": (-1, 3), "r": (-1, 2), "Jc": (-1, 2, 9),
                   "Jp": (-1, 2, 3), "B": (-1, 9, 9), "gc": (-1, 9), "C": (-1, 3, 3),
                   "gp": (-1, 3), "Bd": (-1, 9, 9), "Cinv": (-1, 3, 3), "v": (-1, 3),
@@ -198,28 +212,28 @@ class Problem:
 
     def set(self, name, arr):
         arr = np.ascontiguousarray(arr, dtype=np.float64)
-        lib().orc_set(self.h, NAMES[name], arr.ctypes.data_as(C.c_void_p))
+        self._L.orc_set(self.h, NAMES[name], arr.ctypes.data_as(C.c_void_p))
 
     def _check(self, rc, what):
         if rc != 0:
             raise RuntimeError(f"{what} failed: {rc}")
 
     def linearize(self):
-        self._check(lib().orc_linearize(self.h), "linearize")
+        self._check(self._L.orc_linearize(self.h), "linearize")
 
     def damp(self):
-        self._check(lib().orc_damp(self.h), "damp")
+        self._check(self._L.orc_damp(self.h), "damp")
 
     def schur(self):
-        self._check(lib().orc_schur(self.h), "schur")
+        self._check(self._L.orc_schur(self.h), "schur")
 
     def pcg(self, max_iters=50, rel_tol=1e-6):
         it, rel = C.c_int(), C.c_double()
-        self._check(lib().orc_pcg(self.h, max_iters, rel_tol, C.byref(it), C.byref(rel)), "pcg")
+        self._check(self._L.orc_pcg(self.h, max_iters, rel_tol, C.byref(it), C.byref(rel)), "pcg")
         return it.value, rel.value
 
     def dense_schur_solve(self):
-        self._check(lib().orc_dense_schur_solve(self.h), "dense_schur_solve")
+        self._check(self._L.orc_dense_schur_solve(self.h), "dense_schur_solve")
 
     def backward(self, grad_cams, grad_points):
         """df/du (n_obs x 2, original order) by implicit differentiation of one
@@ -231,7 +245,7 @@ class Problem:
         assert gc.size == 9 * self.nc and gp.size == 3 * self.np
         out = np.empty(2 * self.nobs)
         it, rel = C.c_int(), C.c_double()
-        self._check(lib().orc_backward(self.h, _p(gc), _p(gp), _p(out), C.byref(it), C.byref(rel)),
+        self._check(self._L.orc_backward(self.h, _p(gc), _p(gp), _p(out), C.byref(it), C.byref(rel)),
                     "backward")
         return out.reshape(-1, 2), it.value, rel.value
 
@@ -239,62 +253,62 @@ class Problem:
         """Camera marginal covariance: the 9x9 diagonal blocks of S~^-1 at the
         current parameters and lambda (n_cams x 9 x 9)."""
         out = np.empty(81 * self.nc)
-        self._check(lib().orc_covariance(self.h, _p(out)), "covariance")
+        self._check(self._L.orc_covariance(self.h, _p(out)), "covariance")
         return out.reshape(-1, 9, 9)
 
     def backsub(self):
-        self._check(lib().orc_backsub(self.h), "backsub")
+        self._check(self._L.orc_backsub(self.h), "backsub")
 
     def retract(self):
-        self._check(lib().orc_retract(self.h), "retract")
+        self._check(self._L.orc_retract(self.h), "retract")
 
     def cost_at(self, cams, points):
         c = np.ascontiguousarray(cams, dtype=np.float64)
         p = np.ascontiguousarray(points, dtype=np.float64)
         out = C.c_double()
-        lib().orc_cost_at(self.h, _p(c), _p(p), C.byref(out))
+        self._L.orc_cost_at(self.h, _p(c), _p(p), C.byref(out))
         return out.value
 
     @property
     def cost(self):
-        return lib().orc_get_cost(self.h)
+        return self._L.orc_get_cost(self.h)
 
     @property
     def radius(self):
-        return lib().orc_get_radius(self.h)
+        return self._L.orc_get_radius(self.h)
 
     @radius.setter
     def radius(self, v):
-        lib().orc_set_radius(self.h, v)
+        self._L.orc_set_radius(self.h, v)
 
     @property
     def lam(self):
-        return lib().orc_get_lambda(self.h)
+        return self._L.orc_get_lambda(self.h)
 
     @lam.setter
     def lam(self, v):
-        lib().orc_set_lambda(self.h, v)
+        self._L.orc_set_lambda(self.h, v)
 
     def lm_step(self):
         info = StepInfo()
-        self._check(lib().orc_lm_step(self.h, C.byref(info)), "lm_step")
+        self._check(self._L.orc_lm_step(self.h, C.byref(info)), "lm_step")
         return info.as_dict()
 
     def solve(self, n_iters):
         infos = (StepInfo * max(n_iters, 1))()
-        self._check(lib().orc_solve(self.h, n_iters, infos), "solve")
+        self._check(self._L.orc_solve(self.h, n_iters, infos), "solve")
         return [infos[i].as_dict() for i in range(n_iters)]
 
     def schur_matvec(self, x):
         x = np.ascontiguousarray(x, dtype=np.float64).ravel()
         out = np.empty(9 * self.nc)
-        self._check(lib().orc_schur_matvec(self.h, _p(x), _p(out)), "matvec")
+        self._check(self._L.orc_schur_matvec(self.h, _p(x), _p(out)), "matvec")
         return out
 
     def explicit_S(self):
         n = 9 * self.nc
         S = np.empty((n, n))
-        self._check(lib().orc_explicit_S(self.h, _p(S)), "explicit_S")
+        self._check(self._L.orc_explicit_S(self.h, _p(S)), "explicit_S")
         return S
 
 

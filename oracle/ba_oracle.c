@@ -1,8 +1,18 @@
 /* CPU oracle for one Levenberg-Marquardt iteration of bundle adjustment (fp64).
  *
- * TEST INFRASTRUCTURE ONLY: plain loops, no blocking, no fusion, no threads.
- * Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
- * may load it.  It shares no code with the GPU library.
+ * TEST INFRASTRUCTURE ONLY: plain loops, no blocking, no fusion.  Only the test
+ * suite, the smoke check and the CPU-baseline leg of the benchmark may load it.
+ * It shares no code with the GPU library.
+ *
+ * Threads: built with -fopenmp, loops whose iterations own their outputs (one
+ * observation, camera or point each) are shared out, and every sum over
+ * observations is an "owner scan": each thread owns a contiguous range of
+ * cameras (or points), walks all observations in index order and adds those
+ * of its own, so every accumulator receives its terms in observation order
+ * from one thread, as in the plain loop.  The cost is a serial sum of
+ * per-observation terms.  Both builds therefore give the same bits (pinned by
+ * a test).  Without -fopenmp the pragmas are ignored and a scan is the plain
+ * loop over all observations.
  *
  * Pages cited (by title and section):
  *  [BAE]      "Bundle Adjustment in the Eager Mode" (summary article): one residual
@@ -24,6 +34,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 struct orc_problem {
   int64_t nc, np, nobs;
@@ -31,6 +44,7 @@ struct orc_problem {
   double *cams, *pts, *uv;
   int32_t *cam_idx, *pt_idx;
   int32_t *perm_pt, *perm_cam, *pt_ptr, *cam_ptr;
+  double* terms;   /* per-observation cost terms of orc_cost_at */
   double *r, *Jc, *Jp, *w, *rho;
   double *B, *gc, *C, *gp;
   double *Bd, *Cinv, *v, *rhs, *M, *Mchol;
@@ -44,6 +58,20 @@ struct orc_problem {
   int dl_valid, dl_iters;
   double dl_rel, dl_gg, dl_nn, dl_gn, dl_JgJg, dl_JgJn, dl_JnJn;
 };
+
+/* ------------------------------------------------------------- threads -- */
+
+/* [lo, hi): the calling thread's share of n owned items (all of them outside
+ * a parallel region or without OpenMP). */
+static void my_range(int64_t n, int64_t* lo, int64_t* hi) {
+#ifdef _OPENMP
+  const int64_t t = omp_get_thread_num(), T = omp_get_num_threads();
+#else
+  const int64_t t = 0, T = 1;
+#endif
+  *lo = n * t / T;
+  *hi = n * (t + 1) / T;
+}
 
 /* ---------------------------------------------------------------- SO(3) -- */
 
@@ -314,7 +342,7 @@ int orc_opts_default(orc_opts* o) {
 void orc_destroy(orc_problem* h) {
   if (!h) return;
   void* bufs[] = {h->cams, h->pts, h->uv, h->cam_idx, h->pt_idx, h->perm_pt, h->perm_cam,
-                  h->pt_ptr, h->cam_ptr, h->r, h->Jc, h->Jp, h->w, h->rho, h->B, h->gc,
+                  h->pt_ptr, h->cam_ptr, h->terms, h->r, h->Jc, h->Jp, h->w, h->rho, h->B, h->gc,
                   h->C, h->gp, h->Bd, h->Cinv, h->v, h->rhs, h->M, h->Mchol, h->dc, h->dp,
                   h->cams_trial, h->pts_trial};
   for (size_t i = 0; i < sizeof(bufs) / sizeof(bufs[0]); i++) free(bufs[i]);
@@ -363,6 +391,7 @@ int orc_create(const double* cams, int64_t nc, const double* pts, int64_t np,
   ALLOC(h->perm_cam, N, int32_t);
   ALLOC(h->pt_ptr, np + 1, int32_t);
   ALLOC(h->cam_ptr, nc + 1, int32_t);
+  ALLOC(h->terms, N, double);
   ALLOC(h->r, 2 * N, double);
   ALLOC(h->Jc, 18 * N, double);
   ALLOC(h->Jp, 6 * N, double);
@@ -483,10 +512,12 @@ double orc_get_cost(const orc_problem* h) { return h->cost; }
 /* Total cost sum_k rho_k, summed in observation order ([THESEUS] cost
  * S = 1/2 sum |w c|^2; with the robust kernel, sum rho). */
 int orc_cost_at(const orc_problem* h, const double* cams, const double* pts, double* cost) {
-  double s = 0.0;
+#pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < h->nobs; k++)
-    s += obs_cost(cams + 9 * h->cam_idx[k], pts + 3 * h->pt_idx[k], h->uv + 2 * k, h->opt.loss,
-                  h->opt.huber_delta);
+    h->terms[k] = obs_cost(cams + 9 * h->cam_idx[k], pts + 3 * h->pt_idx[k], h->uv + 2 * k,
+                           h->opt.loss, h->opt.huber_delta);
+  double s = 0.0;
+  for (int64_t k = 0; k < h->nobs; k++) s += h->terms[k];
   *cost = s;
   return isfinite(s) ? ORC_OK : ORC_ERR_NONFINITE;
 }
@@ -499,23 +530,38 @@ int orc_linearize(orc_problem* h) {
   memset(h->gc, 0, sizeof(double) * 9 * h->nc);
   memset(h->C, 0, sizeof(double) * 9 * h->np);
   memset(h->gp, 0, sizeof(double) * 3 * h->np);
+#pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < h->nobs; k++) {
     int32_t j = h->cam_idx[k], i = h->pt_idx[k];
-    double* r = h->r + 2 * k;
-    double* Jc = h->Jc + 18 * k;
-    double* Jp = h->Jp + 6 * k;
     orc_project_one(h->cams + 9 * j, h->pts + 3 * i, h->uv + 2 * k, h->opt.loss,
-                    h->opt.huber_delta, r, Jc, Jp, h->w + k, h->rho + k);
-    double w = h->w[k];
-    double* B = h->B + 81 * j;
-    double* C = h->C + 9 * i;
-    for (int a = 0; a < 9; a++) {
-      for (int b = 0; b < 9; b++) B[9 * a + b] += w * (Jc[a] * Jc[b] + Jc[9 + a] * Jc[9 + b]);
-      h->gc[9 * j + a] += w * (Jc[a] * r[0] + Jc[9 + a] * r[1]);
-    }
-    for (int a = 0; a < 3; a++) {
-      for (int b = 0; b < 3; b++) C[3 * a + b] += w * (Jp[a] * Jp[b] + Jp[3 + a] * Jp[3 + b]);
-      h->gp[3 * i + a] += w * (Jp[a] * r[0] + Jp[3 + a] * r[1]);
+                    h->opt.huber_delta, h->r + 2 * k, h->Jc + 18 * k, h->Jp + 6 * k, h->w + k,
+                    h->rho + k);
+  }
+#pragma omp parallel
+  {
+    int64_t j0, j1, i0, i1;
+    my_range(h->nc, &j0, &j1);
+    my_range(h->np, &i0, &i1);
+    for (int64_t k = 0; k < h->nobs; k++) {
+      int32_t j = h->cam_idx[k], i = h->pt_idx[k];
+      const double* r = h->r + 2 * k;
+      const double* Jc = h->Jc + 18 * k;
+      const double* Jp = h->Jp + 6 * k;
+      double w = h->w[k];
+      if (j >= j0 && j < j1) {
+        double* B = h->B + 81 * j;
+        for (int a = 0; a < 9; a++) {
+          for (int b = 0; b < 9; b++) B[9 * a + b] += w * (Jc[a] * Jc[b] + Jc[9 + a] * Jc[9 + b]);
+          h->gc[9 * j + a] += w * (Jc[a] * r[0] + Jc[9 + a] * r[1]);
+        }
+      }
+      if (i >= i0 && i < i1) {
+        double* C = h->C + 9 * i;
+        for (int a = 0; a < 3; a++) {
+          for (int b = 0; b < 3; b++) C[3 * a + b] += w * (Jp[a] * Jp[b] + Jp[3 + a] * Jp[3 + b]);
+          h->gp[3 * i + a] += w * (Jp[a] * r[0] + Jp[3 + a] * r[1]);
+        }
+      }
     }
   }
   h->linearized = 1;
@@ -538,6 +584,8 @@ static void E_block(const orc_problem* h, int64_t k, double* E) {
  * because the blocks are tiny (via its Cholesky factor).  v_i = C~_i^-1 g_p,i. */
 int orc_damp(orc_problem* h) {
   double lam = h->lambda, fl = h->opt.diag_floor;
+  int bad = 0;
+#pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < h->nc; j++) {
     double* Bd = h->Bd + 81 * j;
     memcpy(Bd, h->B + 81 * j, sizeof(double) * 81);
@@ -546,6 +594,7 @@ int orc_damp(orc_problem* h) {
       Bd[10 * a] += lam * (d > fl ? d : fl);
     }
   }
+#pragma omp parallel for schedule(static) reduction(| : bad)
   for (int64_t i = 0; i < h->np; i++) {
     double L[9];
     memcpy(L, h->C + 9 * i, sizeof(double) * 9);
@@ -553,7 +602,10 @@ int orc_damp(orc_problem* h) {
       double d = L[4 * a];
       L[4 * a] += lam * (d > fl ? d : fl);
     }
-    if (chol(L, 3)) return ORC_ERR_NOT_SPD;
+    if (chol(L, 3)) {
+      bad = 1;
+      continue;
+    }
     double* Ci = h->Cinv + 9 * i;
     for (int c = 0; c < 3; c++) {
       double e[3] = {0.0, 0.0, 0.0}, x[3];
@@ -565,7 +617,7 @@ int orc_damp(orc_problem* h) {
       h->v[3 * i + a] = Ci[3 * a] * h->gp[3 * i] + Ci[3 * a + 1] * h->gp[3 * i + 1] +
                         Ci[3 * a + 2] * h->gp[3 * i + 2];
   }
-  return ORC_OK;
+  return bad ? ORC_ERR_NOT_SPD : ORC_OK;
 }
 
 /* Reduced right-hand side and block-Jacobi preconditioner ([NSLAM] sec. 3.2,
@@ -578,16 +630,27 @@ int orc_schur(orc_problem* h) {
     for (int a = 0; a < 9; a++) h->rhs[9 * j + a] = -h->gc[9 * j + a];
     memcpy(h->M + 81 * j, h->Bd + 81 * j, sizeof(double) * 81);
   }
-  for (int64_t k = 0; k < h->nobs; k++) {
-    double E[27];
-    E_block(h, k, E);
-    int32_t j = h->cam_idx[k], i = h->pt_idx[k];
-    const double* vi = h->v + 3 * i;
-    for (int a = 0; a < 9; a++)
-      h->rhs[9 * j + a] += E[3 * a] * vi[0] + E[3 * a + 1] * vi[1] + E[3 * a + 2] * vi[2];
+#pragma omp parallel
+  {
+    int64_t j0, j1;
+    my_range(h->nc, &j0, &j1);
+    for (int64_t k = 0; k < h->nobs; k++) {
+      int32_t j = h->cam_idx[k], i = h->pt_idx[k];
+      if (j < j0 || j >= j1) continue;
+      double E[27];
+      E_block(h, k, E);
+      const double* vi = h->v + 3 * i;
+      for (int a = 0; a < 9; a++)
+        h->rhs[9 * j + a] += E[3 * a] * vi[0] + E[3 * a + 1] * vi[1] + E[3 * a + 2] * vi[2];
+    }
   }
-  int64_t s = 0;
-  while (s < h->nobs) {
+  /* the (camera, point) runs of the (cam, pt, k) order; a camera's runs are
+   * contiguous, so each camera's block is formed by one thread in run order */
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t jc = 0; jc < h->nc; jc++) {
+  int64_t s = h->cam_ptr[jc];
+  while (s < h->cam_ptr[jc + 1]) {
     int32_t k0 = h->perm_cam[s];
     int32_t j = h->cam_idx[k0], i = h->pt_idx[k0];
     double Eb[27] = {0};
@@ -609,11 +672,10 @@ int orc_schur(orc_problem* h) {
     }
     s = e;
   }
-  for (int64_t j = 0; j < h->nc; j++) {
-    memcpy(h->Mchol + 81 * j, h->M + 81 * j, sizeof(double) * 81);
-    if (chol(h->Mchol + 81 * j, 9)) return ORC_ERR_NOT_SPD;
+  memcpy(h->Mchol + 81 * jc, h->M + 81 * jc, sizeof(double) * 81);
+  if (chol(h->Mchol + 81 * jc, 9)) bad = 1;
   }
-  return ORC_OK;
+  return bad ? ORC_ERR_NOT_SPD : ORC_OK;
 }
 
 /* Implicit Schur product S x = B~ x - E C~^-1 E^T x, without forming S:
@@ -627,22 +689,30 @@ int orc_schur_matvec(orc_problem* h, const double* x, double* out) {
     free(y);
     return ORC_ERR_ALLOC;
   }
-  for (int64_t k = 0; k < h->nobs; k++) {
-    double E[27];
-    E_block(h, k, E);
-    const double* xc = x + 9 * h->cam_idx[k];
-    double* yi = y + 3 * h->pt_idx[k];
-    for (int b = 0; b < 3; b++) {
-      double s = 0.0;
-      for (int a = 0; a < 9; a++) s += E[3 * a + b] * xc[a];
-      yi[b] += s;
+#pragma omp parallel
+  {
+    int64_t i0, i1;
+    my_range(h->np, &i0, &i1);
+    for (int64_t k = 0; k < h->nobs; k++) {
+      if (h->pt_idx[k] < i0 || h->pt_idx[k] >= i1) continue;
+      double E[27];
+      E_block(h, k, E);
+      const double* xc = x + 9 * h->cam_idx[k];
+      double* yi = y + 3 * h->pt_idx[k];
+      for (int b = 0; b < 3; b++) {
+        double s = 0.0;
+        for (int a = 0; a < 9; a++) s += E[3 * a + b] * xc[a];
+        yi[b] += s;
+      }
     }
   }
+#pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < h->np; i++) {
     const double* Ci = h->Cinv + 9 * i;
     for (int a = 0; a < 3; a++)
       z[3 * i + a] = Ci[3 * a] * y[3 * i] + Ci[3 * a + 1] * y[3 * i + 1] + Ci[3 * a + 2] * y[3 * i + 2];
   }
+#pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < h->nc; j++) {
     const double* Bd = h->Bd + 81 * j;
     for (int a = 0; a < 9; a++) {
@@ -651,12 +721,18 @@ int orc_schur_matvec(orc_problem* h, const double* x, double* out) {
       out[9 * j + a] = s;
     }
   }
-  for (int64_t k = 0; k < h->nobs; k++) {
-    double E[27];
-    E_block(h, k, E);
-    const double* zi = z + 3 * h->pt_idx[k];
-    double* o = out + 9 * h->cam_idx[k];
-    for (int a = 0; a < 9; a++) o[a] -= E[3 * a] * zi[0] + E[3 * a + 1] * zi[1] + E[3 * a + 2] * zi[2];
+#pragma omp parallel
+  {
+    int64_t j0, j1;
+    my_range(h->nc, &j0, &j1);
+    for (int64_t k = 0; k < h->nobs; k++) {
+      if (h->cam_idx[k] < j0 || h->cam_idx[k] >= j1) continue;
+      double E[27];
+      E_block(h, k, E);
+      const double* zi = z + 3 * h->pt_idx[k];
+      double* o = out + 9 * h->cam_idx[k];
+      for (int a = 0; a < 9; a++) o[a] -= E[3 * a] * zi[0] + E[3 * a + 1] * zi[1] + E[3 * a + 2] * zi[2];
+    }
   }
   free(z);
   free(y);
@@ -689,6 +765,7 @@ int orc_pcg(orc_problem* h, int max_iters, double rel_tol, int* iters_out, doubl
   int it = 0;
   double res = rhs_norm;
   if (rhs_norm > 0.0) {
+#pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < h->nc; j++) chol_solve(h->Mchol + 81 * j, 9, r + 9 * j, z + 9 * j);
     memcpy(p, z, sizeof(double) * n);
     double rz = dot(r, z, n);
@@ -704,6 +781,7 @@ int orc_pcg(orc_problem* h, int max_iters, double rel_tol, int* iters_out, doubl
       it = k;
       res = sqrt(dot(r, r, n));
       if (res <= rel_tol * rhs_norm) break;
+#pragma omp parallel for schedule(static)
       for (int64_t j = 0; j < h->nc; j++) chol_solve(h->Mchol + 81 * j, 9, r + 9 * j, z + 9 * j);
       double rz_new = dot(r, z, n);
       double beta = rz_new / rz;
@@ -816,17 +894,24 @@ int orc_backsub(orc_problem* h) {
   double* y = (double*)malloc(sizeof(double) * (size_t)(3 * h->np));
   if (!y) return ORC_ERR_ALLOC;
   for (int64_t i = 0; i < 3 * h->np; i++) y[i] = -h->gp[i];
-  for (int64_t k = 0; k < h->nobs; k++) {
-    double E[27];
-    E_block(h, k, E);
-    const double* xc = h->dc + 9 * h->cam_idx[k];
-    double* yi = y + 3 * h->pt_idx[k];
-    for (int b = 0; b < 3; b++) {
-      double s = 0.0;
-      for (int a = 0; a < 9; a++) s += E[3 * a + b] * xc[a];
-      yi[b] -= s;
+#pragma omp parallel
+  {
+    int64_t i0, i1;
+    my_range(h->np, &i0, &i1);
+    for (int64_t k = 0; k < h->nobs; k++) {
+      if (h->pt_idx[k] < i0 || h->pt_idx[k] >= i1) continue;
+      double E[27];
+      E_block(h, k, E);
+      const double* xc = h->dc + 9 * h->cam_idx[k];
+      double* yi = y + 3 * h->pt_idx[k];
+      for (int b = 0; b < 3; b++) {
+        double s = 0.0;
+        for (int a = 0; a < 9; a++) s += E[3 * a + b] * xc[a];
+        yi[b] -= s;
+      }
     }
   }
+#pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < h->np; i++) {
     const double* Ci = h->Cinv + 9 * i;
     for (int a = 0; a < 3; a++)
@@ -838,6 +923,7 @@ int orc_backsub(orc_problem* h) {
 
 /* Trial parameters x' = x (+) delta: camera retraction, points additive. */
 int orc_retract(orc_problem* h) {
+#pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < h->nc; j++)
     orc_retract_camera(h->cams + 9 * j, h->dc + 9 * j, h->cams_trial + 9 * j);
   for (int64_t i = 0; i < 3 * h->np; i++) h->pts_trial[i] = h->pts[i] + h->dp[i];
@@ -1077,6 +1163,7 @@ int orc_backward(orc_problem* h, const double* grad_cams, const double* grad_pts
     if ((rc = orc_pcg(h, h->opt.pcg_max_iters, h->opt.pcg_rel_tol, &iters, &rel))) return rc;
   }
   if ((rc = orc_backsub(h))) return rc;
+#pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < h->nobs; k++) {
     const double* Jc = h->Jc + 18 * k;
     const double* Jp = h->Jp + 6 * k;
@@ -1111,4 +1198,13 @@ int orc_solve(orc_problem* h, int n_iters, orc_step_info* infos) {
     if (rc) return rc;
   }
   return ORC_OK;
+}
+
+/* Threads the loops above run on (1 without OpenMP). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

@@ -117,5 +117,8 @@ int orc_project_one(const double* cam, const double* X, const double* uv, int lo
                     double* r, double* Jc, double* Jp, double* w, double* rho);
 int orc_retract_camera(const double* cam, const double* delta, double* out);
 void orc_so3_exp(const double* w, double* R);
+/* Threads the oracle's loops run on: 1 for the plain build, OpenMP's maximum
+ * for the -fopenmp build. */
+int orc_num_threads(void);
 
 #endif
