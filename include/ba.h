@@ -149,6 +149,12 @@ typedef struct ba_problem ba_problem;
 /* Fills *o with the defaults listed above.  BA_ERR_ARG if o is NULL. */
 int ba_options_default(ba_options* o);
 
+/* Largest sizes ba_create accepts (the kernels index observations and points
+ * with 32-bit products below these). */
+#define BA_MAX_OBS ((int64_t)1 << 30)
+#define BA_MAX_PTS ((int64_t)1 << 28)
+#define BA_MAX_CAMS ((int64_t)1 << 24)
+
 /* Copies the inputs to the device (H2D, or D2D when opts->mem == BA_MEM_DEVICE),
  * validates them on the device (index range, finiteness), sorts the
  * observations by (point, camera, k) and by (camera, point, k) with a stable
@@ -220,7 +226,9 @@ int ba_covariance(ba_problem* h, double* cov_out);
 int ba_get_params(ba_problem* h, double* cams_out, double* points_out);
 
 /* Replaces the parameters (host or device pointers per options.mem; either may
- * be NULL to keep that part), forces a re-linearisation, recomputes the cost. */
+ * be NULL to keep that part), forces a re-linearisation, recomputes the cost.
+ * BA_ERR_NONFINITE if a new parameter or the new cost is not finite; the
+ * handle then keeps its previous parameters, cost and linearisation. */
 int ba_set_params(ba_problem* h, const double* cams, const double* points);
 
 int ba_get_state(const ba_problem* h, ba_state* st);

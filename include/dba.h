@@ -113,7 +113,9 @@ int dba_covariance(dba_problem* h, float* cov);
 int dba_get_state(dba_problem* h, float* poses, float* inv_depth);
 
 /* Replaces the state from host or device memory per options.mem (either
- * pointer may be NULL to keep that part). */
+ * pointer may be NULL to keep that part).  DBA_ERR_NONFINITE if a new depth
+ * or pose is non-finite or a quaternion is zero; the handle then keeps its
+ * previous state. */
 int dba_set_state(dba_problem* h, const float* poses, const float* inv_depth);
 
 int dba_get_sizes(const dba_problem* h, int* n_frames, int* n_pixels, int* n_edges, int* n_fixed);

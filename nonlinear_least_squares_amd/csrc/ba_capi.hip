@@ -999,8 +999,8 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
     return fail(BA_ERR_ARG, "null parameters or non-positive sizes");
   if (n_obs > 0 && (!obs_cam_idx || !obs_pt_idx || !obs_uv))
     return fail(BA_ERR_ARG, "null observation arrays");
-  if (n_obs >= (int64_t)INT32_MAX || n_cams >= (int64_t)INT32_MAX || n_pts >= (int64_t)INT32_MAX)
-    return fail(BA_ERR_ARG, "sizes must be below 2^31 - 1");
+  if (n_obs > BA_MAX_OBS || n_cams > BA_MAX_CAMS || n_pts > BA_MAX_PTS)
+    return fail(BA_ERR_ARG, "sizes beyond BA_MAX_OBS, BA_MAX_CAMS or BA_MAX_PTS");
   ba_problem* h = new ba_problem();
   if (opts) h->opt = *opts;
   else ba_options_default(&h->opt);
@@ -1154,25 +1154,34 @@ int ba_get_params(ba_problem* h, double* cams_out, double* points_out) {
   return BA_OK;
 }
 
+// The new parameters are staged in the trial buffers (free between steps) and
+// checked there; only when they are finite and give a finite cost do they
+// become the current ones, so a rejected call leaves the handle as it was.
 int ba_set_params(ba_problem* h, const double* cams, const double* points) {
   if (!h) return fail(BA_ERR_ARG, "null handle");
   const hipMemcpyKind kind =
       h->opt.mem == BA_MEM_DEVICE ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
-  if (cams) HIPC(hipMemcpyAsync(h->cams[h->cur], cams, sizeof(double) * 9 * h->nc, kind, h->stream));
-  if (points)
-    HIPC(hipMemcpyAsync(h->pts[h->cur], points, sizeof(double) * 3 * h->np, kind, h->stream));
-  HIPC(hipMemsetAsync(h->flags, 0, 2 * sizeof(int), h->stream));
-  launch_validate(nullptr, nullptr, nullptr, 0, h->cams[h->cur], h->nc, h->pts[h->cur], h->np,
-                  h->flags, h->stream);
+  const int c = h->cur, t = 1 - h->cur;
+  hipStream_t s = h->stream;
+  if (cams) HIPC(hipMemcpyAsync(h->cams[t], cams, sizeof(double) * 9 * h->nc, kind, s));
+  else HIPC(hipMemcpyAsync(h->cams[t], h->cams[c], sizeof(double) * 9 * h->nc, hipMemcpyDeviceToDevice, s));
+  if (points) HIPC(hipMemcpyAsync(h->pts[t], points, sizeof(double) * 3 * h->np, kind, s));
+  else HIPC(hipMemcpyAsync(h->pts[t], h->pts[c], sizeof(double) * 3 * h->np, hipMemcpyDeviceToDevice, s));
+  HIPC(hipMemsetAsync(h->flags, 0, 2 * sizeof(int), s));
+  launch_validate(nullptr, nullptr, nullptr, 0, h->cams[t], h->nc, h->pts[t], h->np, h->flags, s);
   int flags[2] = {0, 0};
-  HIPC(hipMemcpyAsync(flags, h->flags, sizeof(flags), hipMemcpyDeviceToHost, h->stream));
-  HIPC(hipStreamSynchronize(h->stream));
+  HIPC(hipMemcpyAsync(flags, h->flags, sizeof(flags), hipMemcpyDeviceToHost, s));
+  HIPC(hipStreamSynchronize(s));
   if (flags[1]) return fail(BA_ERR_NONFINITE, "non-finite parameters");
-  launch_cam_prep(h->cams[h->cur], h->tab[h->cur], h->camq[h->cur], h->nc, h->stream);
-  double c = 0.0;
-  CHECK_RC(current_cost(h, &c));
-  if (!std::isfinite(c)) return fail(BA_ERR_NONFINITE, "cost is not finite");
-  h->cost = c;
+  launch_cam_prep(h->cams[t], h->tab[t], h->camq[t], h->nc, s);
+  Dev d = make_dev(h);
+  launch_cost(d, d.pts_trial, d.tab_trial, d.camq_trial, s);
+  HIPC(hipGetLastError());
+  CHECK_RC(read_out(h));
+  const double cost = h->h_out->trial_cost;
+  if (!std::isfinite(cost)) return fail(BA_ERR_NONFINITE, "cost is not finite");
+  h->cur = t;
+  h->cost = cost;
   h->linearized = 0;
   h->dl_valid = 0;
   return BA_OK;
@@ -1213,7 +1222,16 @@ int ba_debug_run(ba_problem* h, int upto) {
   if (upto >= BA_STAGE_PCG) CHECK_RC(stage_solve(h));
   if (upto >= BA_STAGE_UPDATE) CHECK_RC(stage_update(h));
   CHECK_RC(read_out(h));
-  if (h->prof_on) CHECK_RC(prof_collect(h, h->h_out->pcg_iters));
+  if (h->prof_on) {
+    // the step record carries the PCG count only after the update stage
+    int iters = h->h_out->pcg_iters;
+    if (upto == BA_STAGE_PCG) {
+      PcgState st;
+      CHECK_RC(d2h(h, &st, h->pcg, sizeof(st)));
+      iters = st.iters;
+    }
+    CHECK_RC(prof_collect(h, iters));
+  }
   return BA_OK;
 }
 

@@ -955,6 +955,7 @@ struct dba_problem {
   size_t lin_lds = 0, solve_lds = 0;
   Arena arena;
   float *pose7 = nullptr, *poseRt = nullptr, *dxi = nullptr, *depth = nullptr, *dd = nullptr;
+  float *pose7_stage = nullptr, *poseRt_stage = nullptr;   // dba_set_state checks new poses here
   float *targets = nullptr, *weights = nullptr, *fstore = nullptr, *estore = nullptr;
   float *partial = nullptr, *cost_part = nullptr, *costs = nullptr;
   float *S_dbg = nullptr, *rhs_dbg = nullptr;
@@ -1388,6 +1389,8 @@ int create(const float* poses, const float* inv_depth, int n, int H, int W, cons
   Arena& A = h->arena;
   A.add(h->pose7, 8 * (int64_t)n);
   A.add(h->poseRt, 16 * (int64_t)n);
+  A.add(h->pose7_stage, 8 * (int64_t)n);
+  A.add(h->poseRt_stage, 16 * (int64_t)n);
   A.add(h->dxi, 6 * (int64_t)n);
   A.add(h->depth, n * P);
   A.add(h->dd, n * P);
@@ -1564,16 +1567,39 @@ int dba_get_state(dba_problem* h, float* poses, float* inv_depth) {
   return DBA_OK;
 }
 
+// The new state is staged and checked first (depths in the depth-step buffer,
+// which holds nothing between steps; poses in their own staging rows) and
+// copied over the current state only when it is valid, so a rejected call
+// leaves the handle as it was.
 int dba_set_state(dba_problem* h, const float* poses, const float* inv_depth) {
   if (!h) return fail(DBA_ERR_ARG, "null handle");
-  if (inv_depth) CHECK_RC(copy_in(h, h->depth, inv_depth, sizeof(float) * h->n * h->P));
-  if (poses) CHECK_RC(poses_in(h, poses));
+  const size_t dbytes = sizeof(float) * h->n * h->P;
   if (inv_depth) {
-    hipLaunchKernelGGL(k_validate, dim3(64), dim3(256), 0, h->stream, h->depth, h->n * h->P,
+    CHECK_RC(copy_in(h, h->dd, inv_depth, dbytes));
+    hipLaunchKernelGGL(k_validate, dim3(64), dim3(256), 0, h->stream, h->dd, h->n * h->P,
                        h->targets, (int64_t)0, h->weights, (int64_t)0, h->flags);
     HIPC(hipGetLastError());
   }
-  return check_flags(h);
+  if (poses) {
+    HIPC(hipMemcpy2DAsync(h->pose7_stage, 8 * sizeof(float), poses, 7 * sizeof(float),
+                          7 * sizeof(float), h->n,
+                          h->opt.mem == DBA_MEM_DEVICE ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
+                          h->stream));
+    hipLaunchKernelGGL(k_pose_prep, dim3((h->n + 63) / 64), dim3(64), 0, h->stream, h->pose7_stage,
+                       h->poseRt_stage, h->n, h->flags);
+    HIPC(hipGetLastError());
+  }
+  CHECK_RC(check_flags(h));
+  if (inv_depth && dbytes)
+    HIPC(hipMemcpyAsync(h->depth, h->dd, dbytes, hipMemcpyDeviceToDevice, h->stream));
+  if (poses) {
+    HIPC(hipMemcpyAsync(h->pose7, h->pose7_stage, sizeof(float) * 8 * h->n, hipMemcpyDeviceToDevice,
+                        h->stream));
+    HIPC(hipMemcpyAsync(h->poseRt, h->poseRt_stage, sizeof(float) * 16 * h->n,
+                        hipMemcpyDeviceToDevice, h->stream));
+  }
+  HIPC(hipStreamSynchronize(h->stream));
+  return DBA_OK;
 }
 
 int dba_get_sizes(const dba_problem* h, int* n_frames, int* n_pixels, int* n_edges, int* n_fixed) {

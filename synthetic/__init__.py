@@ -7,6 +7,6 @@ linear solve or parameter update).  The CPU oracle and the GPU library both take
 their inputs from here and share nothing else.
 """
 
-from .ba import CONFIGS, ba_scene, scene_summary  # noqa: F401
+from .ba import CONFIGS, ba_scene, heavy_camera_scene, scene_summary  # noqa: F401
 from .droid import droid_scene  # noqa: F401
 from .pgo import PGO_CONFIGS, pgo_scene, pgo_summary  # noqa: F401

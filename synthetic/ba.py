@@ -23,6 +23,11 @@ Configurations (sizes from the workload list of the task):
 * ``large``  : 1,000 ring cameras, 400,000 points, power-law track lengths on
   {2..50} with exponent 2.02 (about 2.2 M observations), 1 px noise, 5 %
   outliers, Huber 2 px, 30 LM iterations.
+* ``wide``   : as ``large`` with 1,500 ring cameras and 90,000 points (about
+  500,000 observations), 20 LM iterations.
+
+``heavy_camera_scene`` adds to a ring scene one camera that sees thousands of
+points of one contiguous index range (a camera far busier than the rest).
 
 Every draw comes from ``numpy.random.Generator(PCG64(seed))``.
 """
@@ -43,6 +48,11 @@ CONFIGS = {
     "large": dict(n_cams=1000, n_pts=400000, seed=4, layout="ring", tracks="powerlaw",
                   outlier_frac=0.05, loss="huber", huber_delta=2.0, n_iters=30,
                   pcg_max_iters=50, pcg_rel_tol=1e-6),
+    # more cameras than a per-camera table of the point passes holds in one
+    # compute unit's LDS (the library then keeps it in global memory)
+    "wide": dict(n_cams=1500, n_pts=90000, seed=6, layout="ring", tracks="powerlaw",
+                 outlier_frac=0.05, loss="huber", huber_delta=2.0, n_iters=20,
+                 pcg_max_iters=50, pcg_rel_tol=1e-6),
 }
 
 RING_RADIUS = 20.0      # ring cameras sit 20 units from the centre of the point box
@@ -262,3 +272,32 @@ def ba_scene(config="tiny", seed=None, noise_px=1.0, outlier_frac=None,
 def scene_summary(sc):
     n_c, n_p, n_o = len(sc["cams"]), len(sc["points"]), len(sc["obs_cam"])
     return f"{sc['config']}: {n_c} cameras, {n_p} points, {n_o} observations"
+
+
+def heavy_camera_scene(n_extra=3000, camera=0, config="small", n_pts=12000, seed=None,
+                       loss="huber", outlier_frac=0.02):
+    """A ring scene in which camera ``camera`` additionally observes points
+    0 .. n_extra - 1 (one observation each, synthesised like the others: the
+    true projection plus 1 px noise, ``outlier_frac`` of them replaced by
+    uniform +-50 px outliers).  With ``n_pts`` = 12,000 those points fill the
+    lowest quarter of the point indices, so the camera holds about 3,200
+    observations of points in that quarter."""
+    sc = ba_scene(config, seed=seed, n_pts=n_pts, outlier_frac=outlier_frac)
+    rng = np.random.Generator(np.random.PCG64(1000 + sc["seed"]))
+    ct, Xt = sc["cams_true"], sc["points_true"]
+    pts = np.arange(n_extra)
+    cam = np.full(n_extra, camera)
+    rots = Rotation.from_rotvec(ct[cam, 0:3])
+    uv, depth = image_model(rots, ct[cam, 3:6], ct[cam, 6], ct[cam, 7], ct[cam, 8], Xt[pts])
+    assert depth.min() > 0.5
+    noise = rng.normal(0.0, 1.0, size=(n_extra, 2))
+    out = rng.random(n_extra) < outlier_frac
+    noise = np.where(out[:, None], rng.uniform(-50.0, 50.0, size=(n_extra, 2)), noise)
+    order = rng.permutation(len(sc["obs_cam"]) + n_extra)
+    sc["obs_cam"] = np.ascontiguousarray(np.concatenate([sc["obs_cam"], cam])[order], dtype=np.int32)
+    sc["obs_pt"] = np.ascontiguousarray(np.concatenate([sc["obs_pt"], pts])[order], dtype=np.int32)
+    sc["obs_uv"] = np.ascontiguousarray(np.concatenate([sc["obs_uv"], uv + noise])[order])
+    sc["is_outlier"] = np.concatenate([sc["is_outlier"], out])[order]
+    sc["loss"] = loss
+    sc["config"] = f"{config} with a heavy camera"
+    return sc

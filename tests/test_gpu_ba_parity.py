@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synthetic import ba_scene
+from synthetic import ba_scene, heavy_camera_scene
 
 pytestmark = pytest.mark.gpu
 
@@ -316,3 +316,77 @@ def test_device_resident_inputs_on_torch_stream():
     gpu.solve(5)
     host.solve(5)
     assert gpu.get_state() == host.get_state()
+
+
+def _max_band_segment(sc, bands=4):
+    """Longest run of one camera's observations whose points share one of the
+    library's point-index bands (its camera passes cut such a run into chunks
+    of at most 1,024 observations)."""
+    key = sc["obs_cam"].astype(np.int64) * bands + (sc["obs_pt"].astype(np.int64) * bands) // len(sc["points"])
+    return int(np.bincount(key).max())
+
+
+@pytest.mark.parametrize("lds_cameras", [True, False])
+def test_heavy_camera_multi_chunk_parity(lds_cameras, monkeypatch):
+    """One camera with about 3,200 observations in one point band: its
+    camera-order segment is split into several chunks, whose partials the
+    per-camera kernels (B and g_c, rhs and S_jj, the PCG's camera side) add in
+    chunk order.  Both kernel families: the camera table in LDS and, by the
+    environment switch read at creation, in global memory."""
+    if not lds_cameras:
+        monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
+    sc = heavy_camera_scene()
+    assert _max_band_segment(sc) > 2048
+    gpu, orc = make_pair(sc)
+    gpu.debug_run(bamod.BA_STAGE_SCHUR)
+    orc.linearize()
+    orc.damp()
+    orc.schur()
+    for name in ("B", "gc", "C", "gp", "Bd"):
+        blocks_close(name, gpu.debug_get(name), orc.get(name))
+    tols = inverse_bounds(orc, sc)
+    for name in ("Cinv", "v", "rhs", "M"):
+        blocks_close(name, gpu.debug_get(name), orc.get(name), tols[name])
+    gpu.debug_run(bamod.BA_STAGE_UPDATE)
+    it, rel = orc.pcg(sc["pcg_max_iters"], sc["pcg_rel_tol"])
+    orc.backsub()
+    g_it, _ = gpu.debug_get("pcg")
+    assert int(g_it) == it
+    dc, dc_ref = gpu.debug_get("dc"), orc.get("dc")
+    assert np.linalg.norm(dc - dc_ref) <= 1e-8 * np.linalg.norm(dc_ref)
+    dp, dp_ref = gpu.debug_get("dp"), orc.get("dp")
+    assert np.linalg.norm(dp - dp_ref) <= 1e-8 * np.linalg.norm(dp_ref)
+    gpu2, orc2 = make_pair(sc)
+    g_tr = [gpu2.lm_step() for _ in range(6)]
+    o_tr = orc2.solve(6)
+    assert traces_agree(g_tr, o_tr)
+    assert abs(gpu2.get_state()["cost"] - orc2.cost) <= 1e-6 * orc2.cost
+
+
+def test_rejected_set_params_leaves_the_handle():
+    """ba_set_params with a non-finite camera fails and changes nothing: the
+    parameters, the cost and the next LM step are those of an untouched
+    handle, bit for bit."""
+    sc = ba_scene("small")
+    a = bamod.Problem.from_scene(sc)
+    b = bamod.Problem.from_scene(sc)
+    a.solve(2)
+    b.solve(2)
+    cams, pts = a.get_params()
+    bad = cams.copy()
+    bad[3, 4] = np.nan
+    with pytest.raises(bamod.BAError) as e:
+        a.set_params(bad, pts)
+    assert e.value.code == bamod.BA_ERR_NONFINITE
+    bad_pts = pts.copy()
+    bad_pts[7, 1] = np.inf
+    with pytest.raises(bamod.BAError) as e:
+        a.set_params(None, bad_pts)
+    assert e.value.code == bamod.BA_ERR_NONFINITE
+    ca, pa = a.get_params()
+    assert np.array_equal(ca, cams) and np.array_equal(pa, pts)
+    assert a.get_state() == b.get_state()
+    assert a.lm_step() == b.lm_step()
+    ca, pa = a.get_params()
+    cb, pb = b.get_params()
+    assert np.array_equal(ca, cb) and np.array_equal(pa, pb)

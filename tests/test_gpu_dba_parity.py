@@ -378,3 +378,28 @@ def test_pose_covariance_all_fixed_is_empty():
     sc = dict(sc, n_fixed=sc["poses"].shape[0])
     G = gpu().Problem.from_scene(sc)
     assert G.covariance().shape == (0, 0)
+
+
+def test_rejected_set_state_leaves_the_state(scenes):
+    """dba_set_state with a non-finite depth or a zero quaternion fails and
+    changes nothing: the state and the next step match an untouched handle."""
+    dba = gpu()
+    sc = scenes["small"]
+    G = dba.Problem.from_scene(sc)
+    H = dba.Problem.from_scene(sc)
+    G.gn_step()
+    H.gn_step()
+    p0, d0 = G.get_state()
+    bad_d = d0.copy()
+    bad_d.flat[3] = np.nan
+    with pytest.raises(dba.DBAError) as ex:
+        G.set_state(p0, bad_d)
+    assert ex.value.code == dba.DBA_ERR_NONFINITE
+    bad_p = p0.copy()
+    bad_p[1, 3:] = 0.0
+    with pytest.raises(dba.DBAError) as ex:
+        G.set_state(bad_p, None)
+    assert ex.value.code == dba.DBA_ERR_NONFINITE
+    p1, d1 = G.get_state()
+    assert np.array_equal(p0, p1) and np.array_equal(d0, d1)
+    assert G.gn_step() == H.gn_step()
