@@ -237,6 +237,36 @@ int ba_set_state(ba_problem* h, const ba_state* st);
 /* Sizes. */
 int ba_get_sizes(const ba_problem* h, int64_t* n_cams, int64_t* n_pts, int64_t* n_obs);
 
+/* ---- cost without allocation ---------------------------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * cost as ba_cost (sum over observations of rho(|r_k|), squared or Huber
+ * loss, the same camera model and per-observation arithmetic), but with no
+ * handle: every array is caller-owned DEVICE memory in the layout of
+ * ba_create (cams n_cams x 9, points n_pts x 3, obs_cam_idx / obs_pt_idx
+ * n_obs int32, obs_uv n_obs x 2), and the result is written to cost_out, one
+ * double in device memory.  All work is enqueued on `stream` (a hipStream_t,
+ * NULL = the default stream); nothing synchronises, so the call can be
+ * captured into a graph.  It calls no hipMalloc, hipFree or allocating
+ * library routine: its scratch (camera table and per-block partial sums,
+ * 768 KiB) is a static device array that each GPU holds until the process
+ * ends.  Every call on a GPU shares that array, so calls that overlap on one
+ * GPU (on different streams or host threads) race; calls queued on one
+ * stream do not.  The per-block partials are added in a fixed order, so
+ * equal inputs give equal bits.
+ *
+ * Returns BA_ERR_ARG for null pointers, n_cams or n_pts <= 0, n_obs < 0,
+ * n_cams > BA_NOALLOC_MAX_CAMS, n_obs > BA_NOALLOC_MAX_OBS, a bad loss or a
+ * huber_delta that is not positive, all before any device work.  An
+ * observation index out of range is not read: the kernel writes NaN to
+ * cost_out instead (as it does for non-finite inputs). */
+#define BA_NOALLOC_MAX_CAMS 4096
+#define BA_NOALLOC_MAX_OBS (16384 * 1024)
+int ba_cost_noalloc(const double* cams, int64_t n_cams, const double* points, int64_t n_pts,
+                    const int32_t* obs_cam_idx, const int32_t* obs_pt_idx, const double* obs_uv,
+                    int64_t n_obs, int loss, double huber_delta, double* cost_out, void* stream);
+
 /* ---- inspection entry points used by the parity tests ------------------- */
 
 enum {

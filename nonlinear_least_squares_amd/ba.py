@@ -20,6 +20,7 @@ BA_STAGE_LINEARIZE, BA_STAGE_SCHUR, BA_STAGE_PCG, BA_STAGE_UPDATE = 1, 2, 3, 4
 BA_SOLVER_PCG, BA_SOLVER_DENSE_SCHUR = 0, 1
 BA_STRATEGY_LM, BA_STRATEGY_DOGLEG = 0, 1
 BA_DENSE_MAX_CAMS = 1536
+BA_NOALLOC_MAX_CAMS, BA_NOALLOC_MAX_OBS = 4096, 16384 * 1024
 
 DBG = dict(perm_pt=0, perm_cam=1, pt_ptr=2, cam_ptr=3, r=4, Jc=5, Jp=6, w=7, B=8, gc=9, C=10,
            gp=11, Bd=12, Cinv=13, v=14, rhs=15, M=16, dc=17, dp=18, cams_trial=19,
@@ -113,6 +114,9 @@ SIGNATURES = {
     "ba_profile_get": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_int64),
                                  C.POINTER(C.c_double)]),
     "ba_kernel_name": (C.c_char_p, [C.c_int]),
+    "ba_cost_noalloc": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p,
+                                  C.c_void_p, C.c_void_p, C.c_int64, C.c_int, C.c_double,
+                                  C.c_void_p, C.c_void_p]),
     "ba_destroy": (None, [C.c_void_p]),
     "ba_status_string": (C.c_char_p, [C.c_int]),
 }
@@ -158,6 +162,25 @@ def _ptr(a, dtype):
         return C.c_void_p(a.data_ptr()), a
     arr = np.ascontiguousarray(a, dtype=dtype)
     return C.c_void_p(arr.ctypes.data), arr
+
+
+def cost_noalloc(cams, points, obs_cam, obs_pt, obs_uv, out, loss=BA_LOSS_SQUARED,
+                 huber_delta=2.0, stream=None):
+    """ba_cost_noalloc: the cost of the given parameters and observations,
+    written to ``out`` (a device tensor of one double), with no handle and no
+    device allocation.  Every array is a contiguous device tensor of the
+    ba_create layout (float64 parameters and pixels, int32 indices);
+    ``stream`` is a raw hipStream_t value (None: the default stream).  The
+    call enqueues work and returns without synchronising."""
+    ptrs = [C.c_void_p(a.data_ptr()) for a in (cams, points, obs_cam, obs_pt, obs_uv, out)]
+    for a, want in ((cams, "float64"), (points, "float64"), (obs_cam, "int32"), (obs_pt, "int32"),
+                    (obs_uv, "float64"), (out, "float64")):
+        if not a.is_cuda or str(a.dtype) != "torch." + want or not a.is_contiguous():
+            raise ValueError(f"cost_noalloc needs contiguous {want} device tensors")
+    _check(lib().ba_cost_noalloc(ptrs[0], len(cams), ptrs[1], len(points), ptrs[2], ptrs[3],
+                                 ptrs[4], len(obs_cam), int(loss), float(huber_delta), ptrs[5],
+                                 C.c_void_p(stream or 0)), "ba_cost_noalloc")
+    return out
 
 
 class Problem:

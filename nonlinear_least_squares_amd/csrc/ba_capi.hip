@@ -79,6 +79,8 @@ struct ProfRec {
 
 }  // namespace
 
+int ba::set_error(int code, const std::string& msg) { return fail(code, msg); }
+
 struct ba_problem {
   int64_t nc = 0, np = 0, nobs = 0;
   ba_options opt{};

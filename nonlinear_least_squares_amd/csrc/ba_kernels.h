@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <string>
 
 #include "ba_model.h"
 
@@ -38,6 +39,9 @@ constexpr int kCostBlock = 1024;  // observations per cost-reduction block
 constexpr int kUpdBlock = 1024;   // threads of the single-block cost reduction
 constexpr int kLinCamVals = 54;   // B (45) + g_c (9)
 constexpr int kSchurVals = 54;    // E v (9) + Ebar C~^-1 Ebar^T (45)
+
+// Keeps msg as the text ba_status_string() appends to `code`; returns code.
+int set_error(int code, const std::string& msg);
 
 struct PcgState {     // outcome of the solve, written once when it stops
   double rhs_norm;   // |rhs|_2

@@ -1702,17 +1702,20 @@ hipError_t set_lds_camera_limit(int bytes) {
 
 namespace {
 
-// Every launch goes through the extended dispatch so that pending profiling
-// events are recorded by the dispatch packet itself.
+// A launch with pending profiling events goes through the extended dispatch,
+// so that the events are recorded by the dispatch packet itself; the others
+// are plain launches (which stream capture also accepts).
 template <typename... KArgs, typename... Args>
 void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, uint32_t shmem,
             Args... args) {
   DispatchEvents& ev = dispatch_events();
-  hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0u,
-                        static_cast<KArgs>(args)...);
   if (ev.start) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0u,
+                          static_cast<KArgs>(args)...);
     ev.used = true;
     ev.start = ev.stop = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, static_cast<KArgs>(args)...);
   }
 }
 

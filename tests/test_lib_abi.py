@@ -54,6 +54,20 @@ def test_host_only_entry_points():
     assert rc == bamod.BA_ERR_ARG and not h.value
     assert L.ba_lm_step(None, None) == bamod.BA_ERR_ARG
     assert L.ba_debug_size(None, 0) == bamod.BA_ERR_ARG
+    # the allocation-free cost rejects null pointers and sizes beyond its
+    # scratch array before it looks up the device
+    one = (C.c_double * 9)()
+    rc = L.ba_cost_noalloc(None, 1, one, 1, None, None, None, 0, 0, 2.0, one, None)
+    assert rc == bamod.BA_ERR_ARG
+    rc = L.ba_cost_noalloc(one, bamod.BA_NOALLOC_MAX_CAMS + 1, one, 1, None, None, None, 0, 0, 2.0,
+                           one, None)
+    assert rc == bamod.BA_ERR_ARG and b"BA_NOALLOC_MAX_CAMS" in L.ba_status_string(rc)
+    idx = (C.c_int32 * 1)()
+    rc = L.ba_cost_noalloc(one, 1, one, 1, idx, idx, one, bamod.BA_NOALLOC_MAX_OBS + 1, 0, 2.0,
+                           one, None)
+    assert rc == bamod.BA_ERR_ARG
+    rc = L.ba_cost_noalloc(one, 1, one, 1, idx, idx, one, 1, 0, -1.0, one, None)
+    assert rc == bamod.BA_ERR_ARG
     bad = bamod.options(loss=7)
     cams = (C.c_double * 9)()
     pts = (C.c_double * 3)()
