@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synthetic import ba_scene
+from synthetic import ba_scene, heavy_camera_scene
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +119,19 @@ def test_backward_device_arrays_match_host():
     s.synchronize()
     out_h, _ = gh.backward(G_c, G_p)
     assert np.array_equal(out_d.cpu().numpy(), out_h)
+
+
+@pytest.mark.parametrize("lds_cameras", [True, False])
+def test_backward_heavy_camera(lds_cameras, monkeypatch):
+    """The per-observation products of a camera with about 3,200 observations
+    in one point band run over several of its chunks (Huber loss, outliers)."""
+    if not lds_cameras:
+        monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
+    sc = heavy_camera_scene()
+    G_c, G_p = _grads(sc, seed=14)
+    gpu = bamod.Problem.from_scene(sc)
+    orc = oracle.Problem.from_scene(sc)
+    out, it = gpu.backward(G_c, G_p)
+    ref, it_ref, _ = orc.backward(G_c, G_p)
+    assert it == it_ref
+    assert _rel(out, ref) <= 1e-8, _rel(out, ref)

@@ -8,10 +8,16 @@ Bars (fp64):
   through sum_i |Ebar_i,a| |Ebar_i,b| |C~_i^-1|);
 - the device solve is backward stable in its own S:
   |S dc - rhs| <= 4 n eps |S| |dc| (norm-wise, n = 9 n_cams);
-- the camera step against the oracle's: |dc - dc_ref| <= kappa(S) (|dS| / |S|
-  + 8 n eps) |dc_ref| + 1e-12 |dc_ref|, with dS the measured difference of
-  the two S and kappa its 2-norm condition number (two backward-stable
-  solves of systems that differ by dS);
+- the camera step against the oracle's, per component: in the diagonally
+  scaled variables y = D^1/2 dc (D = diag S; Cholesky does not see the
+  scaling), |y - y_ref| <= (kappa(S_s) (|dS_s| / |S_s| + |drhs_s| / |rhs_s|
+  + 8 n eps) + 1e-12) |y_ref|, dS_s and drhs_s the measured differences of
+  the two scaled systems (two backward-stable solves of systems that differ
+  by them), carried back to each component by 1/sqrt(d_a), and the bound
+  checked to stay below 1e-3 of the step wherever kappa(S_s) (dS_s + drhs_s +
+  8 n eps) < 1e-4 (not on the walk scene at lambda = 1e-6, where the two S
+  differ by what nearly singular point-block inverses may move, and only the
+  backward error constrains the step);
 - LM traces (trial costs 1e-6, decisions) and the final cost (1e-6) as for
   the PCG solver.
 """
@@ -101,12 +107,39 @@ def test_dense_solve_parity(scene, lam):
     # backward stability of the device factorisation and solves, in its own S
     s2 = np.linalg.norm(S, 2)
     assert np.linalg.norm(S @ dc - rhs) <= 4 * n * EPS * s2 * np.linalg.norm(dc)
-    # forward error against the oracle's solve
-    kappa = np.linalg.cond(S_ref)
-    dS = np.linalg.norm(S - S_ref, 2) / np.linalg.norm(S_ref, 2)
-    bound = (kappa * (dS + 8 * n * EPS) + 1e-12) * np.linalg.norm(dc_ref)
-    assert np.linalg.norm(dc - dc_ref) <= bound, (np.linalg.norm(dc - dc_ref) / np.linalg.norm(dc_ref),
-                                                   kappa, dS)
+    # forward error against the oracle's solve, per component.  Cholesky does
+    # not see a diagonal scaling (van der Sluis): with D = diag(S_ref) and
+    # y = D^1/2 dc, both solves are backward stable for S_s y = D^-1/2 rhs,
+    # S_s = D^-1/2 S D^-1/2, whose condition number is far below that of S
+    # (camera parameters of very different scales).  Two backward-stable
+    # solves of scaled systems that differ by the measured dS_s, drhs_s give
+    # |y - y_ref| <= (kappa(S_s) (dS_s + drhs_s + 8 n eps) + 1e-12) |y_ref|,
+    # so component a of dc is off by at most that / sqrt(d_a).
+    d = np.sqrt(np.diag(S_ref))
+    S_s = S_ref / np.outer(d, d)
+    dS_s = np.linalg.norm((S - S_ref) / np.outer(d, d), 2) / np.linalg.norm(S_s, 2)
+    rhs_g = gpu.debug_get("rhs").ravel()
+    drhs_s = np.linalg.norm((rhs_g - rhs) / d) / np.linalg.norm(rhs / d)
+    y_ref = d * dc_ref
+    e = (np.linalg.cond(S_s) * (dS_s + drhs_s + 8 * n * EPS) + 1e-12) * np.linalg.norm(y_ref)
+    bound = e / d
+    err = np.abs(dc - dc_ref)
+    assert (err <= bound).all(), ((err / bound).max(), np.linalg.cond(S_s), dS_s, drhs_s)
+    # and the bound is informative wherever the two systems are close enough
+    # for perturbation theory to bound the forward error usefully
+    # (kappa(S_s) (dS_s + drhs_s + 8 n eps) below 1e-4).  On the walk scene at
+    # lambda = 1e-6 the two S already differ by what inverting nearly singular
+    # two-view point blocks may move (their own bound, checked by
+    # test_explicit_S_parity), so there only the backward error above
+    # constrains the step.
+    kappa_s = np.linalg.cond(S_s)
+    factor = kappa_s * (dS_s + drhs_s + 8 * n * EPS)
+    print(f"  kappa(S_s) {kappa_s:.3g}, dS_s {dS_s:.3g}, drhs_s {drhs_s:.3g}, forward bound "
+          f"{np.linalg.norm(bound) / np.linalg.norm(dc_ref):.3g} of the step, error "
+          f"{np.linalg.norm(err) / np.linalg.norm(dc_ref):.3g}", flush=True)
+    if factor < 1e-4:
+        assert np.linalg.norm(bound) <= 1e-3 * np.linalg.norm(dc_ref), \
+            np.linalg.norm(bound) / np.linalg.norm(dc_ref)
 
 
 @pytest.mark.parametrize("config", ["tiny", "small"])

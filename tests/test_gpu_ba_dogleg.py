@@ -119,3 +119,19 @@ def test_dogleg_edge_scene(solver):
     cams, pts = gpu.get_params()
     np.testing.assert_array_equal(pts[11], sc["points"][11])
     np.testing.assert_array_equal(cams[9], sc["cams"][9])
+
+
+@pytest.mark.parametrize("lds_cameras", [True, False])
+def test_dogleg_heavy_camera(lds_cameras, monkeypatch):
+    """A camera with about 3,200 observations in one point band: the model
+    sums over the observations run over several chunks of that camera."""
+    if not lds_cameras:
+        monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
+    from synthetic import heavy_camera_scene
+    sc = heavy_camera_scene()
+    gpu = bamod.Problem.from_scene(sc, strategy=bamod.BA_STRATEGY_DOGLEG)
+    orc = oracle.Problem.from_scene(sc, strategy=1)
+    tg = [gpu.lm_step() for _ in range(6)]
+    to = orc.solve(6)
+    dogleg_traces_agree(tg, to, sc["pcg_rel_tol"])
+    assert abs(gpu.get_state()["cost"] - orc.cost) <= 1e-6 * orc.cost

@@ -1,16 +1,20 @@
 """Parity at the full large-scene size (1,000 cameras, 400,000 points,
 2,203,610 observations), in the launch configuration the benchmark times.
 
-The oracle cannot afford element-by-element comparison of every array at this
-size inside a test, so it checks:
+It checks:
   * sampled observations (residual, both Jacobians, robust weight) against the
-    oracle's per-observation function,
-  * sampled point blocks C_i and camera blocks B_j summed by the oracle's
-    per-observation function over that point's or camera's observations,
-  * the PCG result through a property that holds at any size: the oracle's
-    own implicit Schur operator applied to the GPU step leaves a residual within
-    the stopping tolerance of the oracle's right-hand side,
-  * one full LM step: cost before, trial cost and the decision.
+    oracle's per-observation function, and sampled point blocks C_i and camera
+    blocks B_j summed by that function over the point's or camera's
+    observations (an independent path through the oracle);
+  * every array of one LM iteration element by element against the oracle's
+    (its threaded build, which gives the plain build's bits): r, both
+    Jacobians, the weights, B, g_c, C, g_p and B~ within 1e-10 per block,
+    C~^-1, v, rhs and S_jj within their first-order inverse bounds, then the
+    PCG camera step at the oracle's iteration count within 1e-8, the point
+    step within 1e-8 and the trial cost within 1e-8;
+  * one full LM step and one dogleg step: cost before, trial cost, decision.
+The 20- and 30-iteration LM traces are replayed against stored oracle traces
+in test_gpu_ba_golden.py.
 """
 import numpy as np
 import pytest
@@ -18,6 +22,8 @@ import pytest
 import oracle
 from nonlinear_least_squares_amd import ba as bamod
 from synthetic import ba_scene
+
+from test_gpu_ba_parity import blocks_close, inverse_bounds, residual_bounds
 
 pytestmark = pytest.mark.gpu
 
@@ -70,31 +76,46 @@ def test_large_sampled_linearisation(large):
         assert _close(B[j], acc, 1e-10, 1e-6)
 
 
-def test_large_pcg_step_solves_the_oracle_system(large):
+def test_large_lm_iteration_elementwise(large):
     sc = large
     g = bamod.Problem.from_scene(sc)
-    g.debug_run(bamod.BA_STAGE_PCG)
-    dc = g.debug_get("dc").ravel()
-    iters, rel = g.debug_get("pcg")
-    o = oracle.Problem.from_scene(sc)
+    o = oracle.Problem.from_scene(sc, parallel=True)
+    g.debug_run(bamod.BA_STAGE_SCHUR)
     o.linearize()
     o.damp()
     o.schur()
-    rhs = o.get("rhs").ravel()
-    assert np.linalg.norm(g.debug_get("rhs").ravel() - rhs) <= 1e-9 * np.linalg.norm(rhs)
-    res = np.linalg.norm(o.schur_matvec(dc) - rhs) / np.linalg.norm(rhs)
-    assert int(iters) < sc["pcg_max_iters"]
-    # the GPU stopped at its own relative residual <= 1e-6; the oracle's
-    # operator agrees with the GPU's to rounding
-    assert rel <= sc["pcg_rel_tol"]
-    assert res <= 1.01 * sc["pcg_rel_tol"] + 1e-9, (res, rel)
+    for name in ("r", "Jc", "Jp", "w", "B", "gc", "C", "gp", "Bd"):
+        got, ref = g.debug_get(name), o.get(name)
+        if name == "w":
+            got, ref = got[:, None], ref[:, None]
+        blocks_close(name, got, ref, residual_bounds(o, sc) if name == "r" else 1e-10)
+        del got, ref
+    tols = inverse_bounds(o, sc)
+    for name in ("Cinv", "v", "rhs", "M"):
+        blocks_close(name, g.debug_get(name), o.get(name), tols[name])
+    g.debug_run(bamod.BA_STAGE_UPDATE)
+    it, rel = o.pcg(sc["pcg_max_iters"], sc["pcg_rel_tol"])
+    o.backsub()
+    o.retract()
+    g_it, g_rel = g.debug_get("pcg")
+    assert int(g_it) == it < sc["pcg_max_iters"], (g_it, it)
+    assert g_rel <= sc["pcg_rel_tol"] and rel <= sc["pcg_rel_tol"]
+    dc, dc_ref = g.debug_get("dc"), o.get("dc")
+    assert np.linalg.norm(dc - dc_ref) <= 1e-8 * np.linalg.norm(dc_ref)
+    dp, dp_ref = g.debug_get("dp"), o.get("dp")
+    assert np.linalg.norm(dp - dp_ref) <= 1e-8 * np.linalg.norm(dp_ref)
+    blocks_close("cams_trial", g.debug_get("cams_trial"), o.get("cams_trial"), 1e-8)
+    blocks_close("points_trial", g.debug_get("points_trial"), o.get("points_trial"), 1e-8)
+    trial = float(g.debug_get("trial_cost")[0])
+    ref = o.cost_at(o.get("cams_trial"), o.get("points_trial"))
+    assert abs(trial - ref) <= 1e-8 * ref
 
 
 def test_large_one_lm_step(large):
     sc = large
     g = bamod.Problem.from_scene(sc)
     gi = g.lm_step()
-    o = oracle.Problem.from_scene(sc)
+    o = oracle.Problem.from_scene(sc, parallel=True)
     oi = o.lm_step()
     assert abs(gi["cost_before"] - oi["cost_before"]) <= 1e-10 * oi["cost_before"]
     assert abs(gi["cost_after"] - oi["cost_after"]) <= 1e-6 * oi["cost_after"]
@@ -112,7 +133,7 @@ def test_large_one_dogleg_step(large):
     sc = large
     g = bamod.Problem.from_scene(sc, strategy=bamod.BA_STRATEGY_DOGLEG)
     gi = g.lm_step()
-    o = oracle.Problem.from_scene(sc, strategy=1)
+    o = oracle.Problem.from_scene(sc, strategy=1, parallel=True)
     oi = o.lm_step()
     assert abs(gi["cost_before"] - oi["cost_before"]) <= 1e-10 * oi["cost_before"]
     assert gi["step_kind"] == oi["step_kind"] and gi["radius"] == oi["radius"] == 1.0
