@@ -113,6 +113,38 @@ def camera_chunks(obs_cam, obs_pt, n_pts, bands=4, chunk=1024):
     return int(np.sum((cnt + chunk - 1) // chunk))
 
 
+def stored_jacobian_bytes(n_obs, n_pts):
+    """Bytes of one PCG iteration in the survey's stored-Jacobian byte model:
+    each observation's sqrt(w)-scaled 2x9 and 2x3 blocks (24 doubles) read
+    once and each point's C~^-1 (6 doubles) once.  This design stores no
+    Jacobian, so the figure is a model-equivalent rate, never achieved
+    bandwidth."""
+    return 192 * n_obs + 48 * n_pts
+
+
+# Algorithmic fp64 flops of the survey's flop model: per observation about 500
+# for the residual, both Jacobian blocks and the B / C / g sums, about 430 for
+# the Schur right-hand side and the exact S_jj blocks, 96 per PCG iteration
+# (E^T x and E z with the Jacobians at hand), 96 for the back-substitution and
+# 40 for the trial cost; per point 18 per PCG iteration and about 60 for the
+# damped 3x3 inverse and v.
+def model_flops_per_lm_iteration(n_obs, n_pts, pcg_iters):
+    return n_obs * (500 + 430 + 96 * pcg_iters + 96 + 40) + n_pts * (60 + 18 * pcg_iters)
+
+
+def cpu_model():
+    """The host CPU's model name (lscpu), or None."""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return None
+
+
 def kernel_hash():
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -131,19 +163,35 @@ def measured_traffic(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(sc, n_iters=3, strategy=0):
-    """The oracle as it stands (plain C, one thread) on the first LM (or
-    dogleg) iterations of the same scene from the same start."""
+def cpu_baseline(sc, n_iters=3, strategy=0, budget_s=12.0):
+    """The oracle as it stands on the first LM (or dogleg) iterations of the
+    same scene from the same start, on all the host's cores (its OpenMP
+    build, which gives the plain build's bits) and on one core (the plain
+    build).  The all-core leg runs as many iterations as fit in about
+    budget_s (at least n_iters)."""
     import oracle
+    kind = "dogleg" if strategy else "LM"
     P = oracle.Problem.from_scene(sc, strategy=strategy)
     t0 = time.perf_counter()
     P.solve(n_iters)
-    dt = time.perf_counter() - t0
-    kind = "dogleg" if strategy else "LM"
-    return {"value": n_iters / dt, "unit": f"{kind} iterations/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n_iters} {kind} iterations of the same scene "
+    dt1 = time.perf_counter() - t0
+    Q = oracle.Problem.from_scene(sc, strategy=strategy, parallel=True)
+    t0 = time.perf_counter()
+    k = 0
+    while k < n_iters or (time.perf_counter() - t0 < budget_s and k < 30):
+        Q.lm_step()
+        k += 1
+    dtn = time.perf_counter() - t0
+    threads = oracle.num_threads(True)
+    model = cpu_model()
+    return {"value": k / dtn, "unit": f"{kind} iterations/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {k} {kind} iterations of the same scene "
                       f"({len(sc['obs_cam'])} observations, PCG max {sc['pcg_max_iters']}), "
-                      f"single-threaded C oracle, {dt:.1f} s"}
+                      f"C oracle with OpenMP on {threads} threads, {dtn:.1f} s",
+            "cpu_model": model,
+            "single_thread": {"value": n_iters / dt1, "cores": 1,
+                              "sample": f"first {n_iters} {kind} iterations, plain C oracle on "
+                                        f"one thread, {dt1:.1f} s"}}
 
 
 DENSE_METRIC = "Gauss-Newton iterations/s (fp32, 1 GPU); % of fp32 vector roofline"
@@ -725,6 +773,11 @@ def main():
     warm.close()
     dominant = max(prof, key=lambda k: prof[k][1])
     print(f"# warm-up kernel totals (launches, ms): {prof}", file=sys.stderr, flush=True)
+    # one PCG iteration's kernels, from the fully timed warm-up: total kernel
+    # time of the per-iteration launches over the iterations run
+    pcg_kernels = ("pcg_pt", "pcg_cam", "pcg_q", "pcg_xr")
+    warm_iters = prof["pcg_pt"][0]
+    pcg_iter_us = (1e3 * sum(prof[k][1] for k in pcg_kernels) / warm_iters) if warm_iters else None
 
     # Timed run: a fresh handle from the initial parameters, K LM iterations.
     t0 = time.perf_counter()
@@ -751,6 +804,22 @@ def main():
                 "kernel": dominant, "avg_launch_us": round(avg_s * 1e6, 2),
                 "launches": launches, "algorithmic_bytes_per_launch": nbytes}
 
+    k_mean = summ["pcg_iters_total"] / args.steps
+    flops = model_flops_per_lm_iteration(n_obs, n_pts, k_mean)
+    model = {
+        "bytes_per_pcg_iteration": stored_jacobian_bytes(n_obs, n_pts),
+        "pcg_iteration_us": round(pcg_iter_us, 2) if pcg_iter_us else None,
+        "equivalent_GBps": (round(stored_jacobian_bytes(n_obs, n_pts) / (pcg_iter_us * 1e3), 1)
+                            if pcg_iter_us else None),
+        "note": "survey byte model of a design that stores sqrt(w)-scaled Jacobian blocks, over "
+                "the measured kernel time of one PCG iteration (warm-up, every launch timed); a "
+                "model-equivalent rate, not achieved bandwidth",
+    }
+    fp64 = {"model_flops_per_lm_iteration": int(flops),
+            "tflops": round(flops / (dt / args.steps) / 1e12, 3),
+            "peak_vector_tflops": 78.6,
+            "note": "algorithmic fp64 flops of the survey's flop model at the measured mean PCG "
+                    "iteration count, over ms_per_step"}
     out = {
         "metric": DOGLEG_METRIC if dogleg else METRIC, "value": round(value, 3),
         "unit": "dogleg iterations/s" if dogleg else "LM iterations/s", "n_gpus": 1,
@@ -766,6 +835,8 @@ def main():
         "pcg_iters_per_lm_iter": round(summ["pcg_iters_total"] / args.steps, 2),
         "accepted": summ["accepted"], "final_cost": summ["final_cost"],
         "create_s": round(create_s, 3),
+        "fp64": fp64,
+        "stored_jacobian_model": model,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
