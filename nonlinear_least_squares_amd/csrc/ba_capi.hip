@@ -115,7 +115,7 @@ struct ba_problem {
   double *Cinv = nullptr, *Bd = nullptr, *rhs = nullptr, *Minv = nullptr,
          *Mfull = nullptr, *schur_part = nullptr;
   double *x = nullptr, *r = nullptr, *zc = nullptr, *pbuf = nullptr, *q = nullptr, *prec = nullptr,
-         *pcg_part = nullptr, *red_part = nullptr, *pt_dot = nullptr;
+         *pcg_part = nullptr, *red_part = nullptr, *pt_dot = nullptr, *cam_rows = nullptr;
   PcgState* pcg = nullptr;
   double *dp = nullptr, *cost_part = nullptr;
   double* vjp = nullptr;     // backward: df/du in the original observation order
@@ -207,6 +207,7 @@ Dev make_dev(const ba_problem* h) {
   d.pcg_part = h->pcg_part;
   d.red_part = h->red_part;
   d.pt_dot = h->pt_dot;
+  d.cam_rows = h->cam_rows;
   d.red_nb = pcg_red_blocks(h->nc);
   d.host_done = h->h_done_dev;
   d.pcg = h->pcg;
@@ -810,6 +811,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   P.add(h->cost_part, (int64_t)std::max(h->n_cost_blocks, 1));
   P.add(h->red_part, 8 * (int64_t)pcg_red_blocks(nc) + 2);
   P.add(h->pt_dot, (int64_t)std::max(h->lds_blocks, 1));
+  P.add(h->cam_rows, h->cam_lds_bytes > 0 ? (int64_t)kCamLdsFill * kLdsBlock : 1);
   P.add(h->dl_vpart, 3 * (int64_t)dl_vec_blocks(nc, h->np));
   P.add(h->dl_opart, 3 * (int64_t)std::max(h->n_chunk_blocks, 1));
   P.add(h->dl_out, 6);

@@ -115,6 +115,8 @@ struct Dev {
   double* pcg_part;
   double* red_part;  // per-block partial sums of the camera-vector kernels, 8 x red_nb, then 2
   double* pt_dot;    // per-block partials of z^T E C~^-1 E^T z from the LDS point pass
+  double* cam_rows;  // LDS point pass, PCG: the camera table rows (kCamLdsStride doubles:
+                     // q, t, f, k1, k2, z) padded to kCamLdsFill * kLdsBlock, copied as is
   int red_nb;        // blocks of the camera-vector kernels
   int* host_done;    // host-mapped copy of pcg->done, polled between batches
   PcgState* pcg;

@@ -65,6 +65,45 @@ __device__ __forceinline__ void wave_reduce_store(double (&v)[K], double* out) {
   }
 }
 
+// K per-lane partials of a one-wavefront block summed through LDS, in two
+// halves of H = ceil(K/2) values.  Each half is written as 2H rows of 32
+// doubles (row k: value k of lanes 0-31, row H + k: of lanes 32-63) at a
+// stride of 33, so that the stores are two runs of consecutive words and the
+// reads of a half-wavefront fall in distinct banks.  Lane l < 32 then adds row
+// l and lane l + 32 row H + l (four interleaved partial sums, added pairwise),
+// the two halves of a value meet by one lane swap, and lane k < H stores value
+// k.  The order of every addition is fixed, so equal inputs give equal bits.
+// s_red holds 2 * H * 33 doubles.
+template <int K>
+__device__ __forceinline__ void wave_sum_store_lds(double (&v)[K], double* out, double* s_red) {
+  constexpr int H = (K + 1) / 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int hi = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int k = 0; k < H; ++k)
+      if (h * H + k < K) s_red[(hi * H + k) * 33 + col] = v[h * H + k];
+    __syncthreads();
+    double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
+    if (col < H) {
+      const double* row = s_red + (hi * H + col) * 33;
+#pragma unroll
+      for (int m = 0; m < 32; m += 4) {
+        p0 += row[m];
+        p1 += row[m + 1];
+        p2 += row[m + 2];
+        p3 += row[m + 3];
+      }
+    }
+    const double part = (p0 + p1) + (p2 + p3);
+    const double other = __shfl_xor(part, 32, kWave);
+    const double tot = hi ? other + part : part + other;
+    if (hi == 0 && col < H && h * H + col < K) out[h * H + col] = tot;
+    __syncthreads();
+  }
+}
+
 // Lane moves by DPP (a VALU modifier, no LDS traffic).  CTRL is the DPP
 // control (row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143,
 // wave_shr:1 = 0x138, wave_shl:1 = 0x130).  Lanes whose source lies outside the
@@ -273,39 +312,82 @@ __global__ __launch_bounds__(kTile) void k_lin_pt(Dev d) {
   point_tile_reduce<9>(d, op, blockIdx.x);
 }
 
+// One slot (64 observations) of a camera chunk: robust weight, stored for the
+// later camera passes (real slots only), and the lane's share of B and g_c.
+// Slots past the chunk's end carry a clamped copy of a real observation and
+// weight 0, so they add zeros.
+struct LinIn {
+  double X0, X1, X2, v0, v1;
+};
+
+__device__ __forceinline__ void lin_cam_slot(const Dev& d, const CamG& c, const LinIn& in, int s,
+                                             bool on, double (&acc)[kLinCamVals]) {
+  Geo g;
+  geo_eval(c, in.X0, in.X1, in.X2, g);
+  const double r0 = g.u0 - in.v0, r1 = g.u1 - in.v1;
+  double w, rho;
+  robust(r0, r1, d.loss, d.delta, w, rho);
+  if (on) d.w_cam[s] = w;
+  w = on ? w : 0.0;
+  double J[18];
+  jc_rows(g, c.f, J);
+  int idx = 0;
+#pragma unroll
+  for (int a = 0; a < 9; ++a) {
+    const double wa0 = w * J[a], wa1 = w * J[9 + a];
+#pragma unroll
+    for (int b = a; b < 9; ++b) acc[idx++] += wa0 * J[b] + wa1 * J[9 + b];
+    acc[45 + a] += wa0 * r0 + wa1 * r1;
+  }
+}
+
 // Camera chunks are processed one wavefront each; block b takes a chunk of
 // point band b % kPointBands.  Workgroups are placed on the accelerator dies
 // round-robin, so each die gathers the point data of one band only and it
-// stays in that die's L2.
+// stays in that die's L2.  Loads run ahead of the arithmetic (point indices
+// two slots, point coordinates and pixels one slot), issued unconditionally
+// with indices clamped into the chunk; the body covers two slots so that the
+// two input buffers alternate in place (a loop-carried copy would make each
+// slot wait for the loads just issued).
 __global__ __launch_bounds__(kWave) void k_lin_cam(Dev d) {
+  __shared__ double s_red[2 * ((kLinCamVals + 1) / 2) * 33];
   const int4 bi = d.blk_chunk[blockIdx.x];
   const int cb = bi.x, ce = bi.y, ch = bi.w;
   if (ch < 0) return;
+  const int lane = threadIdx.x;
+  const int last = ce - 1;   // chunks are never empty
   CamG c;
   load_cam(d.tab, bi.z, c);
+  auto load_in = [&](int i, int s, LinIn& in) {
+    const double* X = d.pts + 3 * (int64_t)i;
+    in.X0 = X[0];
+    in.X1 = X[1];
+    in.X2 = X[2];
+    const double2 uv = *reinterpret_cast<const double2*>(d.c_uv + 2 * (int64_t)min(s, last));
+    in.v0 = uv.x;
+    in.v1 = uv.y;
+  };
   double acc[kLinCamVals];
 #pragma unroll
   for (int k = 0; k < kLinCamVals; ++k) acc[k] = 0.0;
-  for (int s = cb + threadIdx.x; s < ce; s += kWave) {
-    const int i = d.c_pt[s];
-    Geo g;
-    geo_eval(c, d.pts[3 * i], d.pts[3 * i + 1], d.pts[3 * i + 2], g);
-    const double r0 = g.u0 - d.c_uv[2 * s], r1 = g.u1 - d.c_uv[2 * s + 1];
-    double w, rho;
-    robust(r0, r1, d.loss, d.delta, w, rho);
-    d.w_cam[s] = w;
-    double J[18];
-    jc_rows(g, c.f, J);
-    int idx = 0;
-#pragma unroll
-    for (int a = 0; a < 9; ++a) {
-      const double wa0 = w * J[a], wa1 = w * J[9 + a];
-#pragma unroll
-      for (int b = a; b < 9; ++b) acc[idx++] += wa0 * J[b] + wa1 * J[9 + b];
-      acc[45 + a] += wa0 * r0 + wa1 * r1;
-    }
+  LinIn ia, ib;
+  int ib_pt = d.c_pt[min(cb + lane + kWave, last)];
+  load_in(d.c_pt[min(cb + lane, last)], cb + lane, ia);
+  for (int base = cb; base < ce; base += 2 * kWave) {
+    const int s = base + lane;
+    const int ic_pt = d.c_pt[min(s + 2 * kWave, last)];
+    load_in(ib_pt, s + kWave, ib);
+    __builtin_amdgcn_sched_barrier(0);
+    lin_cam_slot(d, c, ia, s, s < ce, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (base + kWave >= ce) break;   // uniform: the chunk ends in this slot
+    ib_pt = d.c_pt[min(s + 3 * kWave, last)];
+    load_in(ic_pt, s + 2 * kWave, ia);
+    __builtin_amdgcn_sched_barrier(0);
+    lin_cam_slot(d, c, ib, s + kWave, s + kWave < ce, acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  wave_reduce_store<kLinCamVals>(acc, d.lin_part + (int64_t)ch * kLinCamVals);
+  wave_sum_store_lds<kLinCamVals>(acc, d.lin_part + (int64_t)ch * kLinCamVals, s_red);
 }
 
 // ----------------------------------------------------- damping and Schur
@@ -363,62 +445,104 @@ __global__ void k_damp_pt(Dev d) {
                         Ci[2] * g[0] + Ci[4] * g[1] + Ci[5] * g[2]);
 }
 
+// One slot of the Schur camera pass.  Inputs loaded a slot ahead: the point
+// record (X, v), the weight and the run length; C~^-1 of the point is loaded
+// at the start of the slot and used after the geometry.  Slots past the
+// chunk's end get weight 0 and no run head, so they add zeros.
+struct SchurIn {
+  double4 a;   // X, v0
+  double2 b;   // v1, v2
+  double w;
+  int rl, i;
+};
+
+__device__ __forceinline__ void schur_cam_slot(const Dev& d, const CamG& c, const SchurIn& in,
+                                               int s, bool on, double (&acc)[kSchurVals]) {
+  const double* Ci = d.Cinv + 6 * (int64_t)in.i;
+  const double2 ca = *reinterpret_cast<const double2*>(Ci);
+  const double2 cb = *reinterpret_cast<const double2*>(Ci + 2);
+  const double2 cc = *reinterpret_cast<const double2*>(Ci + 4);
+  Geo g;
+  geo_eval(c, in.a.x, in.a.y, in.a.z, g);
+  const double w = on ? in.w : 0.0;
+  double t0, t1;
+  jp_apply(g, c.R, in.a.w, in.b.x, in.b.y, t0, t1);
+  jct_acc(g, c.f, w * t0, w * t1, acc);
+  // W = the run's summed weight (a run of one: the weight itself, 0 + w = w)
+  double W = in.w;
+  if (in.rl > 1) {
+    W = 0.0;
+    for (int l = 0; l < in.rl; ++l) W += d.w_cam[s + l];
+  }
+  const double W2 = (on && in.rl > 0) ? W * W : 0.0;
+  double Jp[6];
+  jp_rows(g, c.R, Jp);
+  const double c00 = ca.x, c01 = ca.y, c02 = cb.x, c11 = cb.y, c12 = cc.x, c22 = cc.y;
+  double H[6];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    H[3 * a] = Jp[3 * a] * c00 + Jp[3 * a + 1] * c01 + Jp[3 * a + 2] * c02;
+    H[3 * a + 1] = Jp[3 * a] * c01 + Jp[3 * a + 1] * c11 + Jp[3 * a + 2] * c12;
+    H[3 * a + 2] = Jp[3 * a] * c02 + Jp[3 * a + 1] * c12 + Jp[3 * a + 2] * c22;
+  }
+  const double g00 = W2 * (H[0] * Jp[0] + H[1] * Jp[1] + H[2] * Jp[2]);
+  const double g01 = W2 * (H[0] * Jp[3] + H[1] * Jp[4] + H[2] * Jp[5]);
+  const double g11 = W2 * (H[3] * Jp[3] + H[4] * Jp[4] + H[5] * Jp[5]);
+  double J[18];
+  jc_rows(g, c.f, J);
+  int idx = 9;
+#pragma unroll
+  for (int a = 0; a < 9; ++a) {
+    const double k0 = g00 * J[a] + g01 * J[9 + a];
+    const double k1 = g01 * J[a] + g11 * J[9 + a];
+#pragma unroll
+    for (int b = a; b < 9; ++b) acc[idx++] += k0 * J[b] + k1 * J[9 + b];
+  }
+}
+
 // Camera-order pass: E v (right-hand side) and Ebar C~^-1 Ebar^T (diagonal
 // blocks of S).  Repeated (camera, point) observations share J, so
 // Ebar = (sum of their weights) Jc^T Jp and the run head adds
-// W^2 Jc^T (Jp C~^-1 Jp^T) Jc.
+// W^2 Jc^T (Jp C~^-1 Jp^T) Jc.  Pipelined as k_lin_cam.
 __global__ __launch_bounds__(kWave) void k_schur_cam(Dev d) {
+  __shared__ double s_red[2 * ((kSchurVals + 1) / 2) * 33];
   const int4 bi = d.blk_chunk[blockIdx.x];
   const int cb = bi.x, ce = bi.y, ch = bi.w;
   if (ch < 0) return;
+  const int lane = threadIdx.x;
+  const int last = ce - 1;
   CamG c;
   load_cam(d.tab, bi.z, c);
+  auto load_in = [&](int i, int s, SchurIn& in) {
+    const double* r = d.prec + 8 * (int64_t)i;
+    in.a = *reinterpret_cast<const double4*>(r);
+    in.b = *reinterpret_cast<const double2*>(r + 4);
+    const int sc = min(s, last);
+    in.w = d.w_cam[sc];
+    in.rl = d.run_len[sc];
+    in.i = i;
+  };
   double acc[kSchurVals];
 #pragma unroll
   for (int k = 0; k < kSchurVals; ++k) acc[k] = 0.0;
-  for (int s = cb + threadIdx.x; s < ce; s += kWave) {
-    const int i = d.c_pt[s];
-    const double4 ra = *reinterpret_cast<const double4*>(d.prec + 8 * (int64_t)i);      // X, v0
-    const double2 rb = *reinterpret_cast<const double2*>(d.prec + 8 * (int64_t)i + 4);  // v1, v2
-    Geo g;
-    geo_eval(c, ra.x, ra.y, ra.z, g);
-    const double w = d.w_cam[s];
-    double t0, t1;
-    jp_apply(g, c.R, ra.w, rb.x, rb.y, t0, t1);
-    jct_acc(g, c.f, w * t0, w * t1, acc);
-    const int rl = d.run_len[s];
-    if (rl > 0) {
-      double W = 0.0;
-      for (int l = 0; l < rl; ++l) W += d.w_cam[s + l];
-      double Jp[6];
-      jp_rows(g, c.R, Jp);
-      const double* Ci = d.Cinv + 6 * i;
-      const double c00 = Ci[0], c01 = Ci[1], c02 = Ci[2], c11 = Ci[3], c12 = Ci[4], c22 = Ci[5];
-      // H = Jp C~^-1 (2 x 3), G = H Jp^T (2 x 2 symmetric)
-      double H[6];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        H[3 * a] = Jp[3 * a] * c00 + Jp[3 * a + 1] * c01 + Jp[3 * a + 2] * c02;
-        H[3 * a + 1] = Jp[3 * a] * c01 + Jp[3 * a + 1] * c11 + Jp[3 * a + 2] * c12;
-        H[3 * a + 2] = Jp[3 * a] * c02 + Jp[3 * a + 1] * c12 + Jp[3 * a + 2] * c22;
-      }
-      const double W2 = W * W;
-      const double g00 = W2 * (H[0] * Jp[0] + H[1] * Jp[1] + H[2] * Jp[2]);
-      const double g01 = W2 * (H[0] * Jp[3] + H[1] * Jp[4] + H[2] * Jp[5]);
-      const double g11 = W2 * (H[3] * Jp[3] + H[4] * Jp[4] + H[5] * Jp[5]);
-      double J[18];
-      jc_rows(g, c.f, J);
-      int idx = 9;
-#pragma unroll
-      for (int a = 0; a < 9; ++a) {
-        const double k0 = g00 * J[a] + g01 * J[9 + a];
-        const double k1 = g01 * J[a] + g11 * J[9 + a];
-#pragma unroll
-        for (int b = a; b < 9; ++b) acc[idx++] += k0 * J[b] + k1 * J[9 + b];
-      }
-    }
+  SchurIn ia, ib;
+  int ib_pt = d.c_pt[min(cb + lane + kWave, last)];
+  load_in(d.c_pt[min(cb + lane, last)], cb + lane, ia);
+  for (int base = cb; base < ce; base += 2 * kWave) {
+    const int s = base + lane;
+    const int ic_pt = d.c_pt[min(s + 2 * kWave, last)];
+    load_in(ib_pt, s + kWave, ib);
+    __builtin_amdgcn_sched_barrier(0);
+    schur_cam_slot(d, c, ia, s, s < ce, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (base + kWave >= ce) break;
+    ib_pt = d.c_pt[min(s + 3 * kWave, last)];
+    load_in(ic_pt, s + 2 * kWave, ia);
+    __builtin_amdgcn_sched_barrier(0);
+    schur_cam_slot(d, c, ib, s + kWave, s + kWave < ce, acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  wave_reduce_store<kSchurVals>(acc, d.schur_part + (int64_t)ch * kSchurVals);
+  wave_sum_store_lds<kSchurVals>(acc, d.schur_part + (int64_t)ch * kSchurVals, s_red);
 }
 
 // Per camera: B and g_c as the chunk partials summed in chunk order.
@@ -735,6 +859,15 @@ __global__ __launch_bounds__(kWave) void k_pcg_init(Dev d) {
     rr = r * r;
     rz = r * z;
     zbz = z * bz;
+    if (d.cam_lds_bytes > 0) {
+      // the LDS point pass's camera rows: q (4), t, f, k1, k2 (lane a holds
+      // element a, lane 0 also element 9), then z
+      double* row = d.cam_rows + kCamLdsStride * c.j;
+      const double* tabd = reinterpret_cast<const double*>(d.tab) + 16 * c.j;
+      row[c.a] = c.a < 4 ? d.camq[4 * c.j + c.a] : tabd[9 + (c.a - 4)];
+      if (c.a == 0) row[9] = tabd[14];
+      row[10 + c.a] = z;
+    }
   }
   rr = wave_sum(rr);
   rz = wave_sum(rz);
@@ -842,13 +975,19 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     const double* tabd = reinterpret_cast<const double*>(d.tab);
     int done = MODE == 0 ? d.pcg->done : 0;
     double t[kCamLdsFill];
+    if (MODE == 0) {
+      // the PCG keeps the rows in this layout in memory (padded to the whole copy)
 #pragma unroll
-    for (int u = 0; u < kCamLdsFill; ++u) {
-      const int e = min((int)threadIdx.x + u * kLdsBlock, ne - 1);
-      const int j = e / kCamLdsStride, k = e - j * kCamLdsStride;
-      const double* src = k < 4 ? d.camq + 4 * j + k
-                                : (k < 10 ? tabd + 16 * j + 9 + (k - 4) : xbase + 9 * j + (k - 10));
-      t[u] = *src;
+      for (int u = 0; u < kCamLdsFill; ++u) t[u] = d.cam_rows[threadIdx.x + u * kLdsBlock];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kCamLdsFill; ++u) {
+        const int e = min((int)threadIdx.x + u * kLdsBlock, ne - 1);
+        const int j = e / kCamLdsStride, k = e - j * kCamLdsStride;
+        const double* src = k < 4 ? d.camq + 4 * j + k
+                                  : (k < 10 ? tabd + 16 * j + 9 + (k - 4) : xbase + 9 * j + (k - 10));
+        t[u] = *src;
+      }
     }
     const bool tester = MODE == 0 && threadIdx.x < kWave;
     double part[2] = {0.0, 0.0};
@@ -1040,61 +1179,92 @@ __global__ __launch_bounds__(kLdsBlock) void k_pcg_pt_lds(Dev d, int it) {
 __global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d) { pcg_pt_lds_body<1>(d, 0); }
 
 // Camera side of S p, one wavefront per camera chunk (placed as in k_lin_cam).
-// The camera is uniform, so its parameters sit in scalar registers.  Loads run
-// ahead of the arithmetic (point indices two slots, point records one slot),
-// issued unconditionally with indices clamped into the chunk; slots past the
-// chunk's end get weight 0.  The loop body is written out for two slots so
-// that the two record buffers alternate in place: loop-carried copies would
-// make each iteration wait for the loads it has just issued.  The lane sums
-// are added by a DPP scan.
-struct PtRec {
-  double4 a;   // X, z0
-  double2 b;   // z1, z2
+// The camera is uniform, so its parameters sit in scalar registers.
+// Cooperative gathers: the 64-byte point record of observation o of a slot is
+// fetched by four lanes, one 16-byte piece each (lane l of load t takes piece
+// l & 3 of observation 16 t + l / 4), so each record costs one cache-line
+// access instead of three; the pieces meet in the wavefront's LDS buffer (a
+// record every 80 bytes, so that reads of 16 lanes fall in distinct banks) and
+// each lane reads back its own observation's three pieces.  Indices in this
+// layout are loaded two slots ahead, the pieces and the lane's weight one slot
+// ahead, all unconditionally with indices clamped into the chunk (slots past
+// its end get weight 0); the body covers two slots so that the buffers
+// alternate in place (loop-carried copies would make each slot wait for the
+// loads just issued).  The lane sums are added by a DPP scan.
+struct CoopIdx {
+  int i0, i1, i2, i3;
+};
+typedef double v2d __attribute__((ext_vector_type(2)));
+struct CoopIn {
+  v2d p0, p1, p2, p3;
   double w;
 };
 
-__device__ __forceinline__ void pcg_cam_slot(const CamG& c, const PtRec& r, bool on,
-                                             double (&acc)[9]) {
+__device__ __forceinline__ void coop_idx(const Dev& d, int base, int qo, int last, CoopIdx& ci) {
+  ci.i0 = d.c_pt[min(base + qo, last)];
+  ci.i1 = d.c_pt[min(base + 16 + qo, last)];
+  ci.i2 = d.c_pt[min(base + 32 + qo, last)];
+  ci.i3 = d.c_pt[min(base + 48 + qo, last)];
+}
+
+__device__ __forceinline__ void coop_in(const Dev& d, const CoopIdx& ci, int base, int qp,
+                                        int last, CoopIn& in) {
+  const double* pr = d.prec + 2 * qp;
+  in.p0 = *reinterpret_cast<const v2d*>(pr + 8 * (int64_t)ci.i0);
+  in.p1 = *reinterpret_cast<const v2d*>(pr + 8 * (int64_t)ci.i1);
+  in.p2 = *reinterpret_cast<const v2d*>(pr + 8 * (int64_t)ci.i2);
+  in.p3 = *reinterpret_cast<const v2d*>(pr + 8 * (int64_t)ci.i3);
+  in.w = d.w_cam[min(base + (int)threadIdx.x, last)];
+}
+
+__device__ __forceinline__ void coop_slot(const CamG& c, const CoopIn& in, bool on, int qo, int qp,
+                                          v2d* s_piece, double (&acc)[9]) {
+  const int lane = threadIdx.x;
+  s_piece[qo * 5 + qp] = in.p0;
+  s_piece[(16 + qo) * 5 + qp] = in.p1;
+  s_piece[(32 + qo) * 5 + qp] = in.p2;
+  s_piece[(48 + qo) * 5 + qp] = in.p3;
+  __builtin_amdgcn_wave_barrier();
+  const v2d r0 = s_piece[lane * 5], r1 = s_piece[lane * 5 + 1], r2 = s_piece[lane * 5 + 2];
+  __builtin_amdgcn_wave_barrier();
   Geo g;
-  geo_eval(c, r.a.x, r.a.y, r.a.z, g);
+  geo_eval(c, r0.x, r0.y, r1.x, g);
   double t0, t1;
-  jp_apply(g, c.R, r.a.w, r.b.x, r.b.y, t0, t1);
-  const double w = on ? r.w : 0.0;
+  jp_apply(g, c.R, r1.y, r2.x, r2.y, t0, t1);
+  const double w = on ? in.w : 0.0;
   jct_acc(g, c.f, w * t0, w * t1, acc);
 }
 
 __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
+  __shared__ v2d s_piece[kWave * 5];
   const int done = d.pcg->done;
   const int4 bi = d.blk_chunk[blockIdx.x];
   const int cb = bi.x, ce = bi.y, ch = bi.w;
   if (done || ch < 0) return;
   const int lane = threadIdx.x;
-  const int last = ce - 1;   // chunks are never empty
+  const int last = ce - 1;
+  const int qo = lane >> 2, qp = lane & 3;
   CamG c;
   load_cam(d.tab, bi.z, c);
-  const double* pr = d.prec;
-  auto load_rec = [&](int i, int s, PtRec& r) {
-    r.a = *reinterpret_cast<const double4*>(pr + 8 * (int64_t)i);
-    r.b = *reinterpret_cast<const double2*>(pr + 8 * (int64_t)i + 4);
-    r.w = d.w_cam[min(s, last)];
-  };
-  PtRec ra, rb;
-  int ib = d.c_pt[min(cb + lane + kWave, last)];
-  load_rec(d.c_pt[min(cb + lane, last)], cb + lane, ra);
   double acc[9];
 #pragma unroll
   for (int k = 0; k < 9; ++k) acc[k] = 0.0;
+  CoopIdx ia, ib;
+  CoopIn xa, xb;
+  coop_idx(d, cb, qo, last, ia);
+  coop_idx(d, cb + kWave, qo, last, ib);
+  coop_in(d, ia, cb, qp, last, xa);
   for (int base = cb; base < ce; base += 2 * kWave) {
-    const int s = base + lane;
-    const int ic = d.c_pt[min(s + 2 * kWave, last)];
-    load_rec(ib, s + kWave, rb);
+    coop_idx(d, base + 2 * kWave, qo, last, ia);
+    coop_in(d, ib, base + kWave, qp, last, xb);
     __builtin_amdgcn_sched_barrier(0);
-    pcg_cam_slot(c, ra, s < ce, acc);
+    coop_slot(c, xa, base + lane < ce, qo, qp, s_piece, acc);
     __builtin_amdgcn_sched_barrier(0);
-    ib = d.c_pt[min(s + 3 * kWave, last)];
-    load_rec(ic, s + 2 * kWave, ra);
+    if (base + kWave >= ce) break;   // uniform: the chunk ends in this slot
+    coop_idx(d, base + 3 * kWave, qo, last, ib);
+    coop_in(d, ia, base + 2 * kWave, qp, last, xa);
     __builtin_amdgcn_sched_barrier(0);
-    pcg_cam_slot(c, rb, s + kWave < ce, acc);
+    coop_slot(c, xb, base + kWave + lane < ce, qo, qp, s_piece, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
   seg_scan_dpp<9>(acc, lane, 0);
@@ -1299,6 +1469,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_step(Dev d, int it) {
   double rr = 0.0, rzn = 0.0, zbz = 0.0;
   if (c.on) {
     d.zc[e] = zn;
+    d.cam_rows[kCamLdsStride * c.j + 10 + c.a] = zn;
     rr = r * r;
     rzn = r * zn;
     zbz = zn * bz;
