@@ -724,8 +724,8 @@ def copy_calibration():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     help="scene (default: large for ba and backward, medium for "
                          "schur-dense and covariance, sphere for pgo)")
