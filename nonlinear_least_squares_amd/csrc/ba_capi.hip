@@ -107,7 +107,7 @@ struct ba_problem {
   int ds_ld = 0, ds_T = 0, ds_nruns = 0, ds_nblk = 0;
   int32_t *ds_run = nullptr, *ds_blk_ptr = nullptr;
   int2 *ds_blk = nullptr, *ds_pair = nullptr;
-  double *ds_F = nullptr, *ds_S = nullptr, *ds_diag = nullptr, *ds_diagT = nullptr, *ds_dinv = nullptr,
+  double *ds_F = nullptr, *ds_S = nullptr, *ds_diag = nullptr, *ds_diagT = nullptr, *ds_dinv = nullptr, *ds_v = nullptr,
          *ds_cov = nullptr;
   // work arrays
   double *w_pt = nullptr, *w_cam = nullptr, *C = nullptr, *gp = nullptr, *B = nullptr,
@@ -229,6 +229,7 @@ Dev make_dev(const ba_problem* h) {
   d.ds_diag = h->ds_diag;
   d.ds_diagT = h->ds_diagT;
   d.ds_dinv = h->ds_dinv;
+  d.ds_v = h->ds_v;
   return d;
 }
 
@@ -369,11 +370,18 @@ int stage_dense_factor(ba_problem* h, int cov) {
   TIMED(BA_K_DS_RUNS, -1, launch_ds_runs(d, s));
   TIMED(BA_K_DS_FILL, -1, launch_ds_fill(d, s));
   TIMED(BA_K_DS_ASSEMBLE, -1, launch_ds_assemble(d, s));
-  if (cov) TIMED(BA_K_COV_ZERO, -1, launch_cov_zero(d, s));
-  TIMED(BA_K_DS_PANEL, -1, launch_ds_diag0(d, s));
-  for (int k = 0; k < h->ds_T; ++k) {
-    TIMED(BA_K_DS_PANEL, -1, launch_ds_panel(d, k, cov, s));
-    TIMED(BA_K_DS_UPDATE, -1, launch_ds_update(d, k, cov, s));
+  if (cov) {
+    // the covariance's Z tiles share the diagonal tiles' storage, so it keeps
+    // separate panel and update launches
+    TIMED(BA_K_COV_ZERO, -1, launch_cov_zero(d, s));
+    TIMED(BA_K_DS_PANEL, -1, launch_ds_diag0(d, s));
+    for (int k = 0; k < h->ds_T; ++k) {
+      TIMED(BA_K_DS_PANEL, -1, launch_ds_panel(d, k, cov, s));
+      TIMED(BA_K_DS_UPDATE, -1, launch_ds_update(d, k, cov, s));
+    }
+  } else {
+    for (int k = -1; k < h->ds_T - 1; ++k)
+      TIMED(k < 0 ? BA_K_DS_PANEL : BA_K_DS_UPDATE, -1, launch_ds_step(d, k, s));
   }
   HIPC(hipGetLastError());
   return BA_OK;
@@ -903,6 +911,7 @@ int plan_dense(ba_problem* h) {
   A.add(h->ds_diag, (int64_t)h->ds_T * kt * kt);
   A.add(h->ds_diagT, (int64_t)h->ds_T * kt * kt);
   A.add(h->ds_dinv, (int64_t)h->ds_ld);
+  A.add(h->ds_v, 2 * (int64_t)h->ds_ld);
   A.add(h->ds_cov, 81 * nc);
   CHECK_RC(A.commit());
   HIPC(hipMemcpyAsync(h->ds_run, run.data(), sizeof(int32_t) * run.size(), hipMemcpyHostToDevice, s));

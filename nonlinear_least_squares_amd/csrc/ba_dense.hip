@@ -356,6 +356,219 @@ __global__ __launch_bounds__(64) void k_ds_update(Dev d, int k, int cov) {
   }
 }
 
+// acc = C - A B^T (sub) or acc = C, for 32 x 32 tiles of S, in the MFMA
+// accumulator layout of tile_sub_abt; nothing is stored.
+__device__ __forceinline__ void tile_abt(const double* C, const double* A, const double* B,
+                                         int64_t ld, bool sub, v4d (&acc)[2][2]) {
+  const int l = threadIdx.x;
+  const int lr = l & 15, lk = l >> 4;
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[mh][nh][v] = C[(int64_t)(16 * mh + 4 * v + lk) * ld + 16 * nh + lr];
+  if (!sub) return;
+  double av[2][8], bv[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      av[h][s] = -A[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
+      bv[h][s] = B[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+      for (int nh = 0; nh < 2; ++nh)
+        acc[mh][nh] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mh][s], bv[nh][s], acc[mh][nh], 0, 0, 0);
+}
+
+// The diagonal tile and one tile of the same tile column after the update,
+// accd = Cd - B B^T and acco = Co - Ao B^T (no subtraction without `sub`),
+// with every load issued before the first product: B (the tile column's
+// block of the previous column, L_dk) serves as both operands of the first
+// and as the right operand of the second.
+__device__ __forceinline__ void tile_abt_pair(const double* Cd, const double* Co, const double* Ao,
+                                              const double* B, int64_t ld, bool sub,
+                                              v4d (&accd)[2][2], v4d (&acco)[2][2]) {
+  const int l = threadIdx.x;
+  const int lr = l & 15, lk = l >> 4;
+  // the diagonal tile is accumulated negated, -(Cd) + B B^T, and negated
+  // back (exact), so that both products take B as it is loaded
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t o = (int64_t)(16 * mh + 4 * v + lk) * ld + 16 * nh + lr;
+        accd[mh][nh][v] = -Cd[o];
+        acco[mh][nh][v] = Co[o];
+      }
+  if (sub) {
+  double bv[2][8], ao[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bv[h][s] = B[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
+      ao[h][s] = -Ao[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+      for (int nh = 0; nh < 2; ++nh) {
+        accd[mh][nh] = __builtin_amdgcn_mfma_f64_16x16x4f64(bv[mh][s], bv[nh][s], accd[mh][nh], 0, 0, 0);
+        acco[mh][nh] = __builtin_amdgcn_mfma_f64_16x16x4f64(ao[mh][s], bv[nh][s], acco[mh][nh], 0, 0, 0);
+      }
+  }
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh) accd[mh][nh] = -accd[mh][nh];
+}
+
+// The accumulator tile as rows of s_t (kT x kT, row-major).
+__device__ __forceinline__ void acc_to_rows(const v4d (&acc)[2][2], double* s_t) {
+  const int l = threadIdx.x;
+  const int lr = l & 15, lk = l >> 4;
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_t[(16 * mh + 4 * v + lk) * kT + 16 * nh + lr] = acc[mh][nh][v];
+}
+
+// Factor the diagonal tile whose row r lane r holds in a[] (lanes 32..63
+// repeat lanes 0..31), as factor_diag_tile does, leaving its transpose and
+// the pivot reciprocals in s_l (the layout panel_solve stages) and, with
+// `to_global`, in ds_diag, ds_diagT and ds_dinv.  Every caller runs the same
+// instructions on the same data, so each holds the same bits.
+__device__ __forceinline__ void factor_rows(const Dev& d, int kt, double (&a)[kT], double* s_l,
+                                            bool to_global) {
+  const int r = threadIdx.x & (kT - 1);
+  bool bad = false;
+  double myinv = 0.0;
+#pragma unroll
+  for (int c = 0; c < kT; ++c) {
+    double piv = lane_bcast(a[c], c);
+    if (!(piv > 0.0) || !isfinite(piv)) {
+      bad = true;
+      piv = 1.0;
+    }
+    const double inv = rsqrt_newton(piv);
+    a[c] = r == c ? piv * inv : a[c] * inv;   // L(r, c) for r >= c
+    if (r == c) myinv = inv;
+#pragma unroll
+    for (int j = c + 1; j < kT; ++j) a[j] -= a[c] * lane_bcast(a[c], j);   // L(j, c)
+  }
+  if (threadIdx.x >= kT) return;
+#pragma unroll
+  for (int c = 0; c < kT; ++c) s_l[kT * c + r] = c <= r ? a[c] : 0.0;
+  s_l[kT * kT + r] = myinv;
+  if (!to_global) return;
+  if (bad) d.flags[1] = 1;
+  double* L = d.ds_diag + (int64_t)kt * kT * kT;
+  double* LT = d.ds_diagT + (int64_t)kt * kT * kT;
+#pragma unroll
+  for (int c = 0; c < kT; ++c) {
+    const double v = c <= r ? a[c] : 0.0;
+    L[kT * r + c] = v;
+    LT[kT * c + r] = v;
+  }
+  d.ds_dinv[kT * kt + r] = myinv;
+}
+
+// Row r (lane r) of the tile held as rows of s_t solved against the factor
+// in s_l, X L^T = A, and stored to dst (stride ld).
+__device__ __forceinline__ void solve_rows(const double* s_t, const double* s_l, double* dst,
+                                           int64_t ld) {
+  const int r = threadIdx.x & (kT - 1);
+  double b[kT];
+#pragma unroll
+  for (int c = 0; c < kT; ++c) b[c] = s_t[r * kT + c];
+#pragma unroll
+  for (int c = 0; c < kT; ++c) {
+    b[c] *= s_l[kT * kT + c];
+#pragma unroll
+    for (int j = c + 1; j < kT; ++j) b[j] -= b[c] * s_l[kT * c + j];   // L(j, c)
+  }
+  if (threadIdx.x >= kT) return;
+#pragma unroll
+  for (int c = 0; c < kT; ++c) dst[(int64_t)r * ld + c] = b[c];
+}
+
+// One step of the factorisation for the camera solve: the trailing update
+// after tile column k (none for k = -1) and the panel of tile column
+// kc = k + 1 in one launch, so that the chain is one launch per tile column.
+// With m = T - kc, block b < m takes tile (kc + b, kc) and block m the rhs
+// tile (T, kc): each forms the diagonal tile A_dd - L_dk L_dk^T of column kc
+// and factors it (the same instructions on the same data in every block, so
+// the same bits; block 0 also stores the factor), then updates its own tile
+// and solves it in place, L_ikc = (A_ikc - L_ik L_kck^T) L_dd^-T.  No block
+// writes the diagonal tile of S, so each reads it before its update.  The
+// remaining blocks take the other trailing tiles (i, j), kc < j <= i < T, and
+// rhs tiles (T, j), j > kc, and only update them.  Column kc's blocks come
+// first, so their longer chains start in the first round.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_ds_step(Dev d, int k) {
+  __shared__ double s_t[kT * kT];
+  __shared__ double s_l[kT * kT + kT];
+  const int T = d.ds_T, kc = k + 1, m = T - kc;
+  const int k0 = max(k, 0);
+  const bool sub = k >= 0;
+  const int64_t ld = d.ds_ld;
+  double* S = d.ds_S;
+  const int id = blockIdx.x;
+  v4d acc[2][2];
+  if (id > m) {
+    int rid = id - m - 1;
+    const int ntr = (m - 1) * m / 2;
+    int i, j;
+    if (rid < ntr) {
+      int ii = (int)((sqrt(8.0 * rid + 1.0) - 1.0) * 0.5);
+      while ((ii + 1) * (ii + 2) / 2 <= rid) ++ii;
+      while (ii * (ii + 1) / 2 > rid) --ii;
+      i = kc + 1 + ii;
+      j = kc + 1 + (rid - ii * (ii + 1) / 2);
+    } else {
+      i = T;
+      j = kc + 1 + (rid - ntr);
+    }
+    tile_sub_abt(S + (int64_t)(kT * i) * ld + kT * j, S + (int64_t)(kT * i) * ld + kT * k0,
+                 S + (int64_t)(kT * j) * ld + kT * k0, ld, acc);
+    return;
+  }
+  const int i = id < m ? kc + id : T;
+  const double* Ld = S + (int64_t)(kT * kc) * ld + kT * k0;
+  double* own = S + (int64_t)(kT * i) * ld + kT * kc;
+  v4d acco[2][2];
+  tile_abt_pair(S + (int64_t)(kT * kc) * ld + kT * kc, own, S + (int64_t)(kT * i) * ld + kT * k0,
+                Ld, ld, sub, acc, acco);
+  // the diagonal tile's rows go to the lanes through s_t, which then takes
+  // the block's own tile (so that its accumulators are not held through the
+  // factorisation)
+  acc_to_rows(acc, s_t);
+  __syncthreads();
+  const int r = threadIdx.x & (kT - 1);
+  double a[kT];
+#pragma unroll
+  for (int c = 0; c < kT; ++c) a[c] = s_t[r * kT + c];
+  __syncthreads();
+  if (id != 0) acc_to_rows(acco, s_t);
+  factor_rows(d, kc, a, s_l, id == 0);
+  __syncthreads();
+  if (id == 0) return;
+  solve_rows(s_t, s_l, own, ld);
+}
+
 // ---- camera marginal covariance: blocks of S^-1 = L^-T L^-1 ---------------
 //
 // Z = L^-T (upper triangular) is formed by tiles in the strictly upper tiles
@@ -491,6 +704,160 @@ __global__ __launch_bounds__(kSolveThreads) void k_ds_backsolve(Dev d) {
   }
 }
 
+// Back-substitution L^T x = y by blocks of kBsTiles tiles (128 rows) from the
+// last, one launch per block b = B - 1 .. 0 (B = ceil(T / kBsTiles)), with
+// v (y with the solved blocks' contributions taken out) and x in ds_v:
+//   workgroup 0 stages the block's ten tiles in LDS (its diagonal tiles of
+//   the factor from ds_diag, the six below them from S, each a contiguous
+//   32 x 32 slot), takes x_{b+1}, which the previous launch solved, out of
+//   its own block, v_b -= L_{b+1,b}^T x_{b+1}, then solves L_bb^T x_b = v_b
+//   tile by tile from the bottom: each 32 x 32 triangle by one wavefront
+//   (lane c holds column c of the diagonal tile with its pivot set apart, so
+//   each of the 32 steps is a broadcast and a multiply-add on every lane),
+//   then the tile's x taken out of the block's rows above it.
+//   The other workgroups take x_{b+1} out of the rows above block b, 64
+//   columns each, v_j -= sum_e L(r_e, j) x_{b+1}(e), four quarters of the
+//   rows summed in a fixed order; in the first launch (no x_{b+1}) they copy
+//   y into v.
+// Row and column indices past the matrix are clamped to real ones and their
+// products multiplied by zero, so every load is issued unconditionally.
+constexpr int kBsTiles = 4;
+constexpr int kBsRows = kBsTiles * kT;   // 128
+constexpr int kBsSlots = kBsTiles + kBsTiles * (kBsTiles - 1) / 2;   // 10 tiles
+constexpr int kBsThreads = 256;
+
+// Slot of block-local tile (i, j), j <= i: diagonal tiles first, then the
+// tiles below the diagonal in row order.
+__host__ __device__ constexpr int bs_slot(int i, int j) {
+  return i == j ? i : kBsTiles + i * (i - 1) / 2 + j;
+}
+
+__global__ __launch_bounds__(kBsThreads) void k_ds_bsolve(Dev d, int b) {
+  extern __shared__ double s_L[];                 // kBsSlots tiles of kT x kT (workgroup 0)
+  __shared__ double s_v[kBsRows], s_x1[kBsRows];
+  __shared__ double s_p[4][64];
+  const int T = d.ds_T, B = (T + kBsTiles - 1) / kBsTiles;
+  const int64_t ld = d.ds_ld;
+  const double* S = d.ds_S;
+  const double* y = S + ld * ld;
+  double* v = d.ds_v;
+  double* xs = d.ds_v + ld;
+  const int t = threadIdx.x;
+  const int t0 = kBsTiles * b, nb = min(kBsTiles, T - t0), nr = kT * nb;
+  const int r0 = kT * t0, r1 = r0 + nr;                                   // rows of block b
+  const int n1 = b + 1 < B ? kT * min(kBsTiles, T - t0 - kBsTiles) : 0;   // rows of block b + 1
+  if (blockIdx.x > 0) {
+    const int j = 64 * (blockIdx.x - 1) + (t & 63);
+    const int q = t >> 6;
+    if (n1 == 0) {   // first launch: v = y above the last block
+      if (q == 0 && j < r0) v[j] = y[j];
+      return;
+    }
+    const int jc = min(j, r0 - 1);
+    double lv[kT], xv[kT];
+#pragma unroll
+    for (int e = 0; e < kT; ++e) {
+      const int row = kT * q + e;
+      const int rc = min(row, n1 - 1);
+      lv[e] = S[(int64_t)(r1 + rc) * ld + jc];
+      xv[e] = row < n1 ? xs[r1 + rc] : 0.0;
+    }
+    double part = 0.0;
+#pragma unroll
+    for (int e = 0; e < kT; ++e) part = fma(lv[e], xv[e], part);
+    s_p[q][t & 63] = part;
+    __syncthreads();
+    if (q == 0 && j < r0) v[j] -= (s_p[0][t] + s_p[1][t]) + (s_p[2][t] + s_p[3][t]);
+    return;
+  }
+  // Workgroup 0.  All loads first: the ten tiles (40 doubles per thread; a
+  // tile outside a short last block is a clamped copy of a real one, never
+  // read), v_b, x_{b+1}, and for the elimination of x_{b+1} column c = t & 127
+  // of the next block's rows, half h = t >> 7 of them.
+  const int c = t & (kBsRows - 1), h = t >> 7;
+  {
+    double lt[kBsSlots * 4];
+#pragma unroll
+    for (int u = 0; u < kBsSlots * 4; ++u) {
+      const int slot = u >> 2, e = t + kBsThreads * (u & 3);
+      const int rr = e >> 5, cc = e & (kT - 1);
+      int ti = slot, tj = slot;
+      if (slot >= kBsTiles) {
+        const int q = slot - kBsTiles;
+        ti = q < 1 ? 1 : (q < 3 ? 2 : 3);
+        tj = q - ti * (ti - 1) / 2;
+      }
+      ti = min(ti, nb - 1);
+      tj = min(tj, nb - 1);
+      lt[u] = slot < kBsTiles ? d.ds_diag[(int64_t)(t0 + ti) * kT * kT + e]
+                              : S[(int64_t)(r0 + kT * ti + rr) * ld + r0 + kT * tj + cc];
+    }
+    double nv[kBsRows / 2];
+    const int cc = min(c, nr - 1);
+#pragma unroll
+    for (int u = 0; u < kBsRows / 2; ++u) {
+      const int e = kBsRows / 2 * h + u;
+      nv[u] = n1 > 0 ? S[(int64_t)(r1 + min(e, n1 - 1)) * ld + r0 + cc] : 0.0;
+    }
+    if (t < nr) s_v[t] = n1 == 0 ? y[r0 + t] : v[r0 + t];
+    if (t < n1) s_x1[t] = xs[r1 + t];
+#pragma unroll
+    for (int u = 0; u < kBsSlots * 4; ++u) s_L[(u >> 2) * kT * kT + t + kBsThreads * (u & 3)] = lt[u];
+    __syncthreads();
+    if (n1 > 0) {
+      // x_{b+1} out of block b: each half's sum, then half 0 + half 1
+      double part = 0.0;
+#pragma unroll
+      for (int u = 0; u < kBsRows / 2; ++u) {
+        const int e = kBsRows / 2 * h + u;
+        part = fma(nv[u], e < n1 ? s_x1[e] : 0.0, part);
+      }
+      __syncthreads();
+      if (h == 1) s_x1[c] = part;   // s_x1's values are all in the sums now
+      __syncthreads();
+      if (h == 0 && c < nr) s_v[c] -= part + s_x1[c];
+      __syncthreads();
+    }
+  }
+  // the triangles of the block from the bottom
+  for (int p = nb - 1; p >= 0; --p) {
+    const int o = kT * p;
+    if (t < 64) {
+      const int cl = t & (kT - 1);
+      const double* Lt = s_L + bs_slot(p, p) * kT * kT;
+      double col[kT];
+#pragma unroll
+      for (int e = 0; e < kT; ++e) col[e] = e == cl ? 0.0 : Lt[e * kT + cl];   // L(e, cl), pivot apart
+      const double inv = 1.0 / Lt[cl * kT + cl];
+      double vv = s_v[o + cl];
+#pragma unroll
+      for (int e = kT - 1; e >= 0; --e) vv = fma(-col[e], lane_bcast(vv * inv, e), vv);
+      if (t < kT) s_v[o + cl] = vv * inv;
+    }
+    __syncthreads();
+    // x of tile p out of the block's rows above it (block-local columns < o)
+    if (t < o) {
+      const double* Lr = s_L + bs_slot(p, t >> 5) * kT * kT + (t & (kT - 1));
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < kT; ++e) acc = fma(Lr[e * kT], s_v[o + e], acc);
+      s_v[t] -= acc;
+    }
+    __syncthreads();
+  }
+  if (t < nr) {
+    xs[r0 + t] = s_v[t];
+    if (r0 + t < d.ds_n) d.x[r0 + t] = s_v[t];
+  }
+  if (b == 0 && t == 0) {
+    d.pcg->done = 1;
+    d.pcg->iters = 0;
+    d.pcg->res_norm = 0.0;
+    d.pcg->rhs_norm = 0.0;
+    d.pcg->breakdown = 0;
+  }
+}
+
 }  // namespace
 
 int ds_tile() { return kT; }
@@ -522,16 +889,29 @@ int ds_update_tiles(const Dev& d, int k) {
   const int m = d.ds_T - k - 1;
   return m * (m + 1) / 2 + m;
 }
+int ds_step_blocks(const Dev& d, int k) {
+  const int m = d.ds_T - k - 1;
+  return k < 0 ? m + 1 : m * (m + 1) / 2 + m;
+}
+void launch_ds_step(const Dev& d, int k, hipStream_t s) {
+  launch_timed(k_ds_step, dim3(ds_step_blocks(d, k)), dim3(64), s, 0u, d, k);
+}
 void launch_ds_update(const Dev& d, int k, int cov, hipStream_t s) {
   const int n = ds_update_tiles(d, k) + (cov ? cov_update_tiles(d, k) : 0);
   if (n > 0) launch_timed(k_ds_update, dim3(n), dim3(64), s, 0u, d, k, cov);
 }
 hipError_t ds_backsolve_limit(int ld) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ds_backsolve),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(8 * ld));
+  (void)ld;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ds_bsolve),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)(8 * kBsSlots * kT * kT));
 }
 void launch_ds_backsolve(const Dev& d, hipStream_t s) {
-  launch_timed(k_ds_backsolve, dim3(1), dim3(kSolveThreads), s, (uint32_t)(8 * d.ds_ld), d);
+  const int B = (d.ds_T + kBsTiles - 1) / kBsTiles;
+  for (int b = B - 1; b >= 0; --b) {
+    const int nw = 1 + (kT * kBsTiles * b + 63) / 64;   // workgroup 0 + 64 columns each above
+    launch_timed(k_ds_bsolve, dim3(nw), dim3(kBsThreads), s, (uint32_t)(8 * kBsSlots * kT * kT), d, b);
+  }
 }
 
 }  // namespace ba

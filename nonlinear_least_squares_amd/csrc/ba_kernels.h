@@ -141,6 +141,7 @@ struct Dev {
   double* ds_diag;   // ds_T tiles of tile^2: the factor's diagonal tiles (lower, row-major)
   double* ds_diagT;  // the same tiles transposed
   double* ds_dinv;   // ds_ld: reciprocals of the factor's diagonal
+  double* ds_v;      // 2 ds_ld: the back-substitution's right-hand side v, then x
 };
 
 // Events that the next kernel dispatch records at its start and end (set by
@@ -191,6 +192,9 @@ void launch_ds_diag0(const Dev& d, hipStream_t s);
 void launch_ds_panel(const Dev& d, int k, int cov, hipStream_t s);
 int ds_update_tiles(const Dev& d, int k);
 void launch_ds_update(const Dev& d, int k, int cov, hipStream_t s);
+// One launch per tile column for the camera solve: update after column k fused
+// with the panel of column k + 1 (k = -1: the first panel alone).
+void launch_ds_step(const Dev& d, int k, hipStream_t s);
 hipError_t ds_backsolve_limit(int ld);
 void launch_ds_backsolve(const Dev& d, hipStream_t s);
 // Dogleg (ba_dogleg.hip): the six sums of the step's model, and the trial
