@@ -1274,6 +1274,23 @@ __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
   }
 }
 
+// sz minus camera j's chunk partials of row a, in chunk order: the first
+// kChunkLoads are loaded together (indices clamped into the camera's range,
+// the extra ones subtracted as zeros, which leaves sz's bits as they are),
+// the rest, for cameras with more chunks, one by one.
+constexpr int kChunkLoads = 8;
+__device__ __forceinline__ double minus_chunk_partials(const Dev& d, int c0, int c1, int a, double sz) {
+  const int n = c1 - c0;
+  double pp[kChunkLoads];
+#pragma unroll
+  for (int u = 0; u < kChunkLoads; ++u)
+    pp[u] = d.pcg_part[(int64_t)max(min(c0 + u, c1 - 1), 0) * 9 + a];
+#pragma unroll
+  for (int u = 0; u < kChunkLoads; ++u) sz -= u < n ? pp[u] : 0.0;
+  for (int ch = c0 + kChunkLoads; ch < c1; ++ch) sz -= d.pcg_part[(int64_t)ch * 9 + a];
+  return sz;
+}
+
 __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
   const CamLane c = cam_lane(blockIdx.x, d.nc);
   const int64_t e = 9 * c.j + c.a;
@@ -1308,7 +1325,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
   double sz = 0.0;
 #pragma unroll
   for (int b = 0; b < 9; ++b) sz += bd[b] * zv[b];
-  for (int ch = c0; ch < c1; ++ch) sz -= d.pcg_part[(int64_t)ch * 9 + c.a];
+  sz = minus_chunk_partials(d, c0, c1, c.a, sz);
   double pn = ze, qn = sz;
   if (it > 0) {
     const double beta = wave_sum(part[0]) / wave_sum(part[1]);
@@ -1433,7 +1450,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_step(Dev d, int it) {
   double sz = 0.0;
 #pragma unroll
   for (int b = 0; b < 9; ++b) sz += bd[b] * zv[b];
-  for (int ch = c0; ch < c1; ++ch) sz -= d.pcg_part[(int64_t)ch * 9 + c.a];
+  sz = minus_chunk_partials(d, c0, c1, c.a, sz);
   const double rz = wave_sum(part[0]);
   double pq = wave_sum(part[2]) - wave_sum(ydot);
   double pn = ze, qn = sz;
