@@ -445,28 +445,75 @@ __global__ void k_damp_pt(Dev d) {
                         Ci[2] * g[0] + Ci[4] * g[1] + Ci[5] * g[2]);
 }
 
-// One slot of the Schur camera pass.  Inputs loaded a slot ahead: the point
-// record (X, v), the weight and the run length; C~^-1 of the point is loaded
-// at the start of the slot and used after the geometry.  Slots past the
+// Indices of the cooperative-gather layout of the camera passes: lane l of
+// load t serves observation 16 t + l / 4 of a 64-observation slot.
+struct CoopIdx {
+  int i0, i1, i2, i3;
+};
+typedef double v2d __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void coop_idx(const Dev& d, int base, int qo, int last, CoopIdx& ci) {
+  ci.i0 = d.c_pt[min(base + qo, last)];
+  ci.i1 = d.c_pt[min(base + 16 + qo, last)];
+  ci.i2 = d.c_pt[min(base + 32 + qo, last)];
+  ci.i3 = d.c_pt[min(base + 48 + qo, last)];
+}
+
+// One slot of the Schur camera pass.  The point record (X, v) and C~^-1 of
+// each observation are gathered cooperatively, as in k_pcg_cam: lane l of
+// load t fetches 16-byte piece l & 3 of observation 16 t + l / 4's record
+// and piece min(l & 3, 2) of its C~^-1, so each costs one cache-line access
+// instead of three; the pieces meet in the wavefront's LDS buffer (nine
+// pieces per observation, a 144-byte stride, so that the reads of 16 lanes
+// fall in distinct banks) and each lane reads back its own.  The weight and
+// run length come a slot ahead in the lane's own layout.  Slots past the
 // chunk's end get weight 0 and no run head, so they add zeros.
-struct SchurIn {
-  double4 a;   // X, v0
-  double2 b;   // v1, v2
+struct SchurCoop {
+  v2d r0, r1, r2, r3;   // record pieces of loads 0..3
+  v2d c0, c1, c2, c3;   // C~^-1 pieces of loads 0..3
   double w;
-  int rl, i;
+  int rl;
 };
 
-__device__ __forceinline__ void schur_cam_slot(const Dev& d, const CamG& c, const SchurIn& in,
-                                               int s, bool on, double (&acc)[kSchurVals]) {
-  const double* Ci = d.Cinv + 6 * (int64_t)in.i;
-  const double2 ca = *reinterpret_cast<const double2*>(Ci);
-  const double2 cb = *reinterpret_cast<const double2*>(Ci + 2);
-  const double2 cc = *reinterpret_cast<const double2*>(Ci + 4);
+__device__ __forceinline__ void schur_coop_in(const Dev& d, const CoopIdx& ci, int base, int qp,
+                                              int last, SchurCoop& in) {
+  const double* pr = d.prec + 2 * qp;
+  const double* pc = d.Cinv + 2 * min(qp, 2);
+  in.r0 = *reinterpret_cast<const v2d*>(pr + 8 * (int64_t)ci.i0);
+  in.r1 = *reinterpret_cast<const v2d*>(pr + 8 * (int64_t)ci.i1);
+  in.r2 = *reinterpret_cast<const v2d*>(pr + 8 * (int64_t)ci.i2);
+  in.r3 = *reinterpret_cast<const v2d*>(pr + 8 * (int64_t)ci.i3);
+  in.c0 = *reinterpret_cast<const v2d*>(pc + 6 * (int64_t)ci.i0);
+  in.c1 = *reinterpret_cast<const v2d*>(pc + 6 * (int64_t)ci.i1);
+  in.c2 = *reinterpret_cast<const v2d*>(pc + 6 * (int64_t)ci.i2);
+  in.c3 = *reinterpret_cast<const v2d*>(pc + 6 * (int64_t)ci.i3);
+  const int sc = min(base + (int)threadIdx.x, last);
+  in.w = d.w_cam[sc];
+  in.rl = d.run_len[sc];
+}
+
+__device__ __forceinline__ void schur_cam_slot(const Dev& d, const CamG& c, const SchurCoop& in,
+                                               int s, bool on, int qo, int qp, v2d* s_piece,
+                                               double (&acc)[kSchurVals]) {
+  const int lane = threadIdx.x;
+  s_piece[qo * 9 + qp] = in.r0;
+  s_piece[(16 + qo) * 9 + qp] = in.r1;
+  s_piece[(32 + qo) * 9 + qp] = in.r2;
+  s_piece[(48 + qo) * 9 + qp] = in.r3;
+  if (qp < 3) {
+    s_piece[qo * 9 + 4 + qp] = in.c0;
+    s_piece[(16 + qo) * 9 + 4 + qp] = in.c1;
+    s_piece[(32 + qo) * 9 + 4 + qp] = in.c2;
+    s_piece[(48 + qo) * 9 + 4 + qp] = in.c3;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const v2d ra = s_piece[lane * 9], rb = s_piece[lane * 9 + 1], rc = s_piece[lane * 9 + 2];
+  const v2d ca = s_piece[lane * 9 + 4], cb = s_piece[lane * 9 + 5], cc = s_piece[lane * 9 + 6];
+  __builtin_amdgcn_wave_barrier();
   Geo g;
-  geo_eval(c, in.a.x, in.a.y, in.a.z, g);
+  geo_eval(c, ra.x, ra.y, rb.x, g);
   const double w = on ? in.w : 0.0;
   double t0, t1;
-  jp_apply(g, c.R, in.a.w, in.b.x, in.b.y, t0, t1);
+  jp_apply(g, c.R, rb.y, rc.x, rc.y, t0, t1);
   jct_acc(g, c.f, w * t0, w * t1, acc);
   // W = the run's summed weight (a run of one: the weight itself, 0 + w = w)
   double W = in.w;
@@ -503,46 +550,45 @@ __device__ __forceinline__ void schur_cam_slot(const Dev& d, const CamG& c, cons
 // Camera-order pass: E v (right-hand side) and Ebar C~^-1 Ebar^T (diagonal
 // blocks of S).  Repeated (camera, point) observations share J, so
 // Ebar = (sum of their weights) Jc^T Jp and the run head adds
-// W^2 Jc^T (Jp C~^-1 Jp^T) Jc.  Pipelined as k_lin_cam.
+// W^2 Jc^T (Jp C~^-1 Jp^T) Jc.  Pipelined as k_lin_cam: indices in the
+// cooperative layout two slots ahead, the pieces one slot ahead.  The LDS
+// buffer of the gathers and that of the closing sum share one array.
+constexpr int kSchurRedDoubles = 2 * ((kSchurVals + 1) / 2) * 33;
+constexpr int kSchurPieceDoubles = 2 * kWave * 9;
 __global__ __launch_bounds__(kWave) void k_schur_cam(Dev d) {
-  __shared__ double s_red[2 * ((kSchurVals + 1) / 2) * 33];
+  __shared__ double s_buf[kSchurRedDoubles > kSchurPieceDoubles ? kSchurRedDoubles : kSchurPieceDoubles];
+  v2d* s_piece = reinterpret_cast<v2d*>(s_buf);
   const int4 bi = d.blk_chunk[blockIdx.x];
   const int cb = bi.x, ce = bi.y, ch = bi.w;
   if (ch < 0) return;
   const int lane = threadIdx.x;
   const int last = ce - 1;
+  const int qo = lane >> 2, qp = lane & 3;
   CamG c;
   load_cam(d.tab, bi.z, c);
-  auto load_in = [&](int i, int s, SchurIn& in) {
-    const double* r = d.prec + 8 * (int64_t)i;
-    in.a = *reinterpret_cast<const double4*>(r);
-    in.b = *reinterpret_cast<const double2*>(r + 4);
-    const int sc = min(s, last);
-    in.w = d.w_cam[sc];
-    in.rl = d.run_len[sc];
-    in.i = i;
-  };
   double acc[kSchurVals];
 #pragma unroll
   for (int k = 0; k < kSchurVals; ++k) acc[k] = 0.0;
-  SchurIn ia, ib;
-  int ib_pt = d.c_pt[min(cb + lane + kWave, last)];
-  load_in(d.c_pt[min(cb + lane, last)], cb + lane, ia);
+  CoopIdx ia, ib;
+  SchurCoop xa, xb;
+  coop_idx(d, cb, qo, last, ia);
+  coop_idx(d, cb + kWave, qo, last, ib);
+  schur_coop_in(d, ia, cb, qp, last, xa);
   for (int base = cb; base < ce; base += 2 * kWave) {
-    const int s = base + lane;
-    const int ic_pt = d.c_pt[min(s + 2 * kWave, last)];
-    load_in(ib_pt, s + kWave, ib);
+    coop_idx(d, base + 2 * kWave, qo, last, ia);
+    schur_coop_in(d, ib, base + kWave, qp, last, xb);
     __builtin_amdgcn_sched_barrier(0);
-    schur_cam_slot(d, c, ia, s, s < ce, acc);
+    schur_cam_slot(d, c, xa, base + lane, base + lane < ce, qo, qp, s_piece, acc);
     __builtin_amdgcn_sched_barrier(0);
-    if (base + kWave >= ce) break;
-    ib_pt = d.c_pt[min(s + 3 * kWave, last)];
-    load_in(ic_pt, s + 2 * kWave, ia);
+    if (base + kWave >= ce) break;   // uniform: the chunk ends in this slot
+    coop_idx(d, base + 3 * kWave, qo, last, ib);
+    schur_coop_in(d, ia, base + 2 * kWave, qp, last, xa);
     __builtin_amdgcn_sched_barrier(0);
-    schur_cam_slot(d, c, ib, s + kWave, s + kWave < ce, acc);
+    schur_cam_slot(d, c, xb, base + kWave + lane, base + kWave + lane < ce, qo, qp, s_piece, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
-  wave_sum_store_lds<kSchurVals>(acc, d.schur_part + (int64_t)ch * kSchurVals, s_red);
+  __syncthreads();
+  wave_sum_store_lds<kSchurVals>(acc, d.schur_part + (int64_t)ch * kSchurVals, s_buf);
 }
 
 // Per camera: B and g_c as the chunk partials summed in chunk order.
@@ -1191,21 +1237,10 @@ __global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d) { pcg_pt_lds_b
 // its end get weight 0); the body covers two slots so that the buffers
 // alternate in place (loop-carried copies would make each slot wait for the
 // loads just issued).  The lane sums are added by a DPP scan.
-struct CoopIdx {
-  int i0, i1, i2, i3;
-};
-typedef double v2d __attribute__((ext_vector_type(2)));
 struct CoopIn {
   v2d p0, p1, p2, p3;
   double w;
 };
-
-__device__ __forceinline__ void coop_idx(const Dev& d, int base, int qo, int last, CoopIdx& ci) {
-  ci.i0 = d.c_pt[min(base + qo, last)];
-  ci.i1 = d.c_pt[min(base + 16 + qo, last)];
-  ci.i2 = d.c_pt[min(base + 32 + qo, last)];
-  ci.i3 = d.c_pt[min(base + 48 + qo, last)];
-}
 
 __device__ __forceinline__ void coop_in(const Dev& d, const CoopIdx& ci, int base, int qp,
                                         int last, CoopIn& in) {
