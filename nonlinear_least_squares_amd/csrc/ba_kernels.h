@@ -32,6 +32,7 @@ constexpr int kCamLdsFill = 20;   // table elements per thread in the copy (>= 1
 constexpr int kCamLdsMaxCams = kCamLdsFill * 1024 / kCamLdsStride;   // 1,077
 constexpr int kCamLdsMaxBytes = kCamLdsStride * 8 * kCamLdsMaxCams;
 constexpr int kCostLdsFill = (10 * kCamLdsMaxCams + 1023) / 1024;   // geometry elements per thread
+constexpr int kChunkLoads = 8;   // a camera's chunk partials loaded together in the per-camera sums
 constexpr int kChunk = 1024;      // observations per camera chunk (one wavefront)
 constexpr int kPointBands = 4;    // point-index bands of the camera chunks (block b: band b % 4,
                                   // on dies b % 8: two dies' L2 per band)

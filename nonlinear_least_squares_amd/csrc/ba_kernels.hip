@@ -591,26 +591,25 @@ __global__ __launch_bounds__(kWave) void k_schur_cam(Dev d) {
   wave_sum_store_lds<kSchurVals>(acc, d.schur_part + (int64_t)ch * kSchurVals, s_buf);
 }
 
-// Per camera: B and g_c as the chunk partials summed in chunk order.
-__global__ void k_lin_final(Dev d) {
-  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (j >= d.nc) return;
-  double B[45], g[9];
+// Per camera: B and g_c as the chunk partials summed in chunk order, one
+// wavefront per camera and one lane per value, the first kChunkLoads
+// partials of every lane loaded together (indices clamped, the extra ones
+// added as zeros, which leaves the sums' bits as they are).
+__global__ __launch_bounds__(kWave) void k_lin_final(Dev d) {
+  const int64_t j = blockIdx.x;
+  const int k = threadIdx.x;
+  const int c0 = d.cam_chunk_ptr[j], c1 = d.cam_chunk_ptr[j + 1], n = c1 - c0;
+  const int kc = min(k, kLinCamVals - 1);
+  double pp[kChunkLoads];
 #pragma unroll
-  for (int k = 0; k < 45; ++k) B[k] = 0.0;
+  for (int u = 0; u < kChunkLoads; ++u)
+    pp[u] = d.lin_part[(int64_t)max(min(c0 + u, c1 - 1), 0) * kLinCamVals + kc];
+  double v = 0.0;
 #pragma unroll
-  for (int k = 0; k < 9; ++k) g[k] = 0.0;
-  for (int ch = d.cam_chunk_ptr[j]; ch < d.cam_chunk_ptr[j + 1]; ++ch) {
-    const double* pp = d.lin_part + (int64_t)ch * kLinCamVals;
-#pragma unroll
-    for (int k = 0; k < 45; ++k) B[k] += pp[k];
-#pragma unroll
-    for (int k = 0; k < 9; ++k) g[k] += pp[45 + k];
-  }
-#pragma unroll
-  for (int k = 0; k < 45; ++k) d.B[45 * j + k] = B[k];
-#pragma unroll
-  for (int k = 0; k < 9; ++k) d.gc[9 * j + k] = g[k];
+  for (int u = 0; u < kChunkLoads; ++u) v += u < n ? pp[u] : 0.0;
+  for (int ch = c0 + kChunkLoads; ch < c1; ++ch) v += d.lin_part[(int64_t)ch * kLinCamVals + kc];
+  if (k < 45) d.B[45 * j + k] = v;
+  else if (k < kLinCamVals) d.gc[9 * j + (k - 45)] = v;
 }
 
 // Per camera: B~ = B + lambda D, rhs = -g_c + E v, S_jj = B~ - sum Ebar C~^-1
@@ -621,10 +620,14 @@ __global__ __launch_bounds__(64) void k_precond(Dev d) {
   // nine threads per camera: each forms the damped block, S_jj and its factor
   // (the same bits in all nine), writes a ninth of B~ and S_jj, one rhs entry,
   // and column `col` of S_jj^-1
-  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t >= 9 * d.nc) return;
-  const int64_t j = t / 9;
-  const int col = (int)(t - 9 * j);
+  // seven cameras per block (threads 0..62), so that a camera's nine threads
+  // share the block; threads past the last camera (and the block's 64th)
+  // repeat the last camera's work up to the exchange and store nothing
+  const int cam = threadIdx.x / 9;
+  const int64_t jr = (int64_t)blockIdx.x * 7 + cam;
+  const bool live = threadIdx.x < 63 && jr < d.nc;
+  const int64_t j = live ? jr : d.nc - 1;
+  const int col = live ? (int)threadIdx.x - 9 * cam : 8;
   const int c0 = d.cam_chunk_ptr[j], c1 = d.cam_chunk_ptr[j + 1];
   double B[45];
 #pragma unroll
@@ -637,14 +640,49 @@ __global__ __launch_bounds__(64) void k_precond(Dev d) {
   }
 #pragma unroll
   for (int k = 0; k < 45; ++k)
-    if (k % 9 == col) d.Bd[45 * j + k] = B[k];
+    if (live && k % 9 == col) d.Bd[45 * j + k] = B[k];
+  // the chunk partials: thread col takes E v's entry col and the five
+  // entries k = 5 col .. 5 col + 4 of the Schur block, each in chunk order
+  // (the first kChunkLoads partials loaded together, the extra ones as
+  // zeros), and the camera's nine threads exchange the block through LDS
+  __shared__ double s_sch[8][45];
   double ev = 0.0;
-  for (int ch = c0; ch < c1; ++ch) {
-    const double* pp = d.schur_part + (int64_t)ch * kSchurVals;
-    ev += pp[col];
+  {
+    const int n = c1 - c0;
+    double pe[kChunkLoads], ps[kChunkLoads][5];
 #pragma unroll
-    for (int k = 0; k < 45; ++k) B[k] -= pp[9 + k];
+    for (int u = 0; u < kChunkLoads; ++u) {
+      const double* pp = d.schur_part + (int64_t)max(min(c0 + u, c1 - 1), 0) * kSchurVals;
+      pe[u] = pp[col];
+#pragma unroll
+      for (int q = 0; q < 5; ++q) ps[u][q] = pp[9 + min(5 * col + q, 44)];
+    }
+    double bs[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) bs[q] = 0.0;
+#pragma unroll
+    for (int k = 0; k < 45; ++k)
+      if (k / 5 == col) bs[k % 5] = B[k];
+#pragma unroll
+    for (int u = 0; u < kChunkLoads; ++u) {
+      ev += u < n ? pe[u] : 0.0;
+#pragma unroll
+      for (int q = 0; q < 5; ++q) bs[q] -= u < n ? ps[u][q] : 0.0;
+    }
+    for (int ch = c0 + kChunkLoads; ch < c1; ++ch) {
+      const double* pp = d.schur_part + (int64_t)ch * kSchurVals;
+      ev += pp[col];
+#pragma unroll
+      for (int q = 0; q < 5; ++q) bs[q] -= pp[9 + min(5 * col + q, 44)];
+    }
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+      if (live && 5 * col + q < 45) s_sch[cam][5 * col + q] = bs[q];
   }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 45; ++k) B[k] = s_sch[cam][k];
+  if (!live) return;
   d.rhs[9 * j + col] = -g + ev;
 #pragma unroll
   for (int k = 0; k < 45; ++k)
@@ -1313,7 +1351,6 @@ __global__ __launch_bounds__(kWave) void k_pcg_cam(Dev d) {
 // kChunkLoads are loaded together (indices clamped into the camera's range,
 // the extra ones subtracted as zeros, which leaves sz's bits as they are),
 // the rest, for cameras with more chunks, one by one.
-constexpr int kChunkLoads = 8;
 __device__ __forceinline__ double minus_chunk_partials(const Dev& d, int c0, int c1, int a, double sz) {
   const int n = c1 - c0;
   double pp[kChunkLoads];
@@ -1966,10 +2003,10 @@ void launch_schur_cam(const Dev& d, hipStream_t s) {
   if (d.n_chunk_blocks > 0) launch(k_schur_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
 }
 void launch_lin_final(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) launch(k_lin_final, dim3(blocks_for(d.nc, 64)), dim3(64), s, 0u, d);
+  if (d.nc > 0) launch(k_lin_final, dim3((unsigned)d.nc), dim3(kWave), s, 0u, d);
 }
 void launch_precond(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) launch(k_precond, dim3(blocks_for(9 * d.nc, 64)), dim3(64), s, 0u, d);
+  if (d.nc > 0) launch(k_precond, dim3((unsigned)((d.nc + 6) / 7)), dim3(64), s, 0u, d);
 }
 void launch_pcg_init(const Dev& d, hipStream_t s) {
   launch(k_pcg_init, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d);
