@@ -18,18 +18,16 @@
 // Cholesky factorisation of [[S, b], [b^T, .]] leaves y = L^-1 b in that row.
 // Only the lower triangle is read or written after assembly.
 //
-// Factorisation, right-looking by 32 x 32 tiles, two launches per tile
-// column k:
-//   panel   one wavefront per tile row i > k (and the rhs row) solves its
-//           tile against the factored diagonal tile, L_ik = A_ik L_kk^-T;
-//   update  one wavefront per trailing tile (i, j), k < j <= i:
-//           A_ij -= L_ik L_jk^T with fp64 MFMA (16x16x4), the one dense
-//           contraction of the bundle-adjustment pages' methods; the
-//           wavefront of tile (k + 1, k + 1) then factors it (lane r holds
-//           row r, column values move by readlane), so the next panel starts
-//           from a factored diagonal tile.
-// The factor's diagonal tiles are kept apart (ds_diag); the back-substitution
-// L^T dc = y runs in one workgroup, tile by tile.
+// Factorisation, right-looking by 32 x 32 tiles, one launch per tile column
+// for the camera solve (k_ds_step): the trailing update after column k,
+// A_ij -= L_ik L_jk^T with fp64 MFMA (16x16x4), the one dense contraction of
+// the bundle-adjustment pages' methods, fused with the panel of column k + 1:
+// the blocks of that column form and factor its diagonal tile themselves and
+// solve their own tiles against it, L_ik = A_ik L_kk^-T.  The covariance keeps
+// two launches per column (panel, then update), because its Z tiles share the
+// diagonal tiles' storage.  The factor's diagonal tiles are kept apart
+// (ds_diag); the back-substitution L^T dc = y runs by 128-row blocks over
+// many workgroups (k_ds_bsolve).
 #include <hip/hip_runtime.h>
 
 #include "ba_launch.h"
@@ -40,8 +38,6 @@ namespace {
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr int kT = 32;            // tile order of the factorisation
-constexpr int kSolveThreads = 1024;
-static_assert(kT * kT == kSolveThreads, "the back-substitution loads one diagonal tile per thread");
 
 __device__ __forceinline__ double lane_bcast(double x, int l) {
   const int lo = __builtin_amdgcn_readlane(__double2loint(x), l);
@@ -356,37 +352,6 @@ __global__ __launch_bounds__(64) void k_ds_update(Dev d, int k, int cov) {
   }
 }
 
-// acc = C - A B^T (sub) or acc = C, for 32 x 32 tiles of S, in the MFMA
-// accumulator layout of tile_sub_abt; nothing is stored.
-__device__ __forceinline__ void tile_abt(const double* C, const double* A, const double* B,
-                                         int64_t ld, bool sub, v4d (&acc)[2][2]) {
-  const int l = threadIdx.x;
-  const int lr = l & 15, lk = l >> 4;
-#pragma unroll
-  for (int mh = 0; mh < 2; ++mh)
-#pragma unroll
-    for (int nh = 0; nh < 2; ++nh)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[mh][nh][v] = C[(int64_t)(16 * mh + 4 * v + lk) * ld + 16 * nh + lr];
-  if (!sub) return;
-  double av[2][8], bv[2][8];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      av[h][s] = -A[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
-      bv[h][s] = B[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-#pragma unroll
-    for (int mh = 0; mh < 2; ++mh)
-#pragma unroll
-      for (int nh = 0; nh < 2; ++nh)
-        acc[mh][nh] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mh][s], bv[nh][s], acc[mh][nh], 0, 0, 0);
-}
-
 // The diagonal tile and one tile of the same tile column after the update,
 // accd = Cd - B B^T and acco = Co - Ao B^T (no subtraction without `sub`),
 // with every load issued before the first product: B (the tile column's
@@ -638,69 +603,6 @@ __global__ __launch_bounds__(256) void k_cov_blocks(Dev d, double* out) {
     const int b = a + rem;
     out[81 * (int64_t)c + 9 * a + b] = v;
     out[81 * (int64_t)c + 9 * b + a] = v;
-  }
-}
-
-// L^T dc = y by tile columns from the last, right-looking: v starts as y (in
-// LDS); for each tile column kt, one wavefront solves the 32 x 32 triangle
-// L_kk^T x_kt = v_kt (lane c holds column c of L_kk; the pivots' reciprocals
-// are formed up front, so each of the 32 dependent steps is a broadcast and a
-// multiply-add), then all threads take x_kt out of the unknowns above it,
-// v_j -= sum_e L(32 kt + e, j) x_e for j < 32 kt, reading tile row kt of L
-// row by row (coalesced; 32 loads in flight per column).  The next diagonal
-// tile is loaded one step ahead.  Writes dc and the solver state.
-__global__ __launch_bounds__(kSolveThreads) void k_ds_backsolve(Dev d) {
-  extern __shared__ double s_v[];               // N_p: y, then x where solved
-  __shared__ double s_diag[kT * kT];
-  const int64_t ld = d.ds_ld;
-  const double* S = d.ds_S;
-  const double* y = S + ld * ld;                // the rhs row after the factorisation
-  const int t = threadIdx.x, c = t & (kT - 1);
-  for (int64_t j = t; j < ld; j += kSolveThreads) s_v[j] = y[j];
-  s_diag[t] = d.ds_diag[(int64_t)(d.ds_T - 1) * kT * kT + t];   // kT * kT == kSolveThreads
-  __syncthreads();
-  for (int kt = d.ds_T - 1; kt >= 0; --kt) {
-    const double dg_next = d.ds_diag[(int64_t)max(kt - 1, 0) * kT * kT + t];
-    if (t < 64) {
-      double col[kT];
-#pragma unroll
-      for (int e = 0; e < kT; ++e) col[e] = s_diag[kT * e + c];   // L(e, c)
-      double dsel = col[0];
-#pragma unroll
-      for (int e = 1; e < kT; ++e)
-        if (c == e) dsel = col[e];
-      const double inv = 1.0 / dsel;
-      double v = s_v[kT * kt + c];
-      double xm = 0.0;
-#pragma unroll
-      for (int e = kT - 1; e >= 0; --e) {
-        const double xe = lane_bcast(v * inv, e);
-        if (c == e) xm = xe;
-        if (c < e) v -= col[e] * xe;
-      }
-      if (t < kT) s_v[kT * kt + c] = xm;
-    }
-    __syncthreads();
-    s_diag[t] = dg_next;
-    const double* Lrow = S + (int64_t)(kT * kt) * ld;
-    for (int64_t j = t; j < kT * (int64_t)kt; j += kSolveThreads) {
-      double lv[kT];
-#pragma unroll
-      for (int e = 0; e < kT; ++e) lv[e] = Lrow[e * ld + j];
-      double acc = 0.0;
-#pragma unroll
-      for (int e = 0; e < kT; ++e) acc += lv[e] * s_v[kT * kt + e];
-      s_v[j] -= acc;
-    }
-    __syncthreads();
-  }
-  for (int e = t; e < d.ds_n; e += kSolveThreads) d.x[e] = s_v[e];
-  if (t == 0) {
-    d.pcg->done = 1;
-    d.pcg->iters = 0;
-    d.pcg->res_norm = 0.0;
-    d.pcg->rhs_norm = 0.0;
-    d.pcg->breakdown = 0;
   }
 }
 

@@ -1,12 +1,18 @@
 // gfx950 kernels for one Levenberg-Marquardt iteration of bundle adjustment.
 //
 // Point-order passes (linearisation + point blocks, PCG point side,
-// back-substitution) run one thread per observation over tiles of whole
-// points; a point's sums are formed by a wavefront segmented scan, carried
-// across wavefronts through LDS and across sub-tiles for points longer than
-// a tile.  Camera-order passes (camera blocks, Schur right-hand side and
-// preconditioner, PCG camera side) run over chunks of one camera and reduce
-// with a fixed tree; per-camera totals add chunk partials in chunk order.
+// back-substitution, cost): with at most 1,077 cameras, one persistent
+// 1,024-thread block per compute unit holds the camera table in LDS and each
+// wavefront streams a point-aligned range of observations 64 at a time; a
+// point's sums are formed by a DPP segmented scan across the lanes and carried
+// across slots in registers.  With more cameras, tiles of whole points read
+// the camera table from memory and carry partial sums across wavefronts
+// through LDS.  Camera-order passes (camera blocks, Schur right-hand side and
+// diagonal blocks, PCG camera side) run one wavefront per chunk of one
+// camera: each lane accumulates its observations, software-pipelined (the
+// PCG and Schur passes gather each point's 64-byte record with four lanes),
+// and the lanes are summed in a fixed order (through LDS, or a DPP scan);
+// per-camera totals add the chunk partials in chunk order.
 // No floating-point atomics: results are bitwise reproducible run to run.
 #include "ba_kernels.h"
 
@@ -48,21 +54,6 @@ __device__ __forceinline__ void block_reduce(double (&v)[K], double* s_buf, doub
     s_out[k] = s;
   }
   __syncthreads();
-}
-
-// K per-lane partials of one wavefront summed by a fixed butterfly (every lane
-// ends with the same bits); lane 0 stores the totals.
-template <int K>
-__device__ __forceinline__ void wave_reduce_store(double (&v)[K], double* out) {
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) v[k] += __shfl_xor(v[k], off, kWave);
-  }
-  if ((threadIdx.x & (kWave - 1)) == 0) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) out[k] = v[k];
-  }
 }
 
 // K per-lane partials of a one-wavefront block summed through LDS, in two
