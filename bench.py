@@ -280,6 +280,13 @@ def main_dense(args):
                 "unit": "TFLOP/s", "frac": round(ach / FP32_PEAK_TFLOPS, 6), "traffic": None,
                 "kernel": dominant, "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches,
                 "algorithmic_flops_per_launch": fl}
+        if dominant == "solve":
+            # one workgroup: the reduced system's Cholesky is a chain of dependent
+            # block steps, so the chip's peak is not what bounds it
+            roof["note"] = ("one workgroup on one compute unit, a chain of dependent block "
+                            "steps: bound by latency; its rate is also given against one "
+                            "compute unit's share of the fp32 peak")
+            roof["frac_of_one_cu"] = round(ach / (FP32_PEAK_TFLOPS / 256), 5)
     out = {
         "metric": DENSE_METRIC, "value": round(value, 2), "unit": "GN iterations/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
