@@ -4,6 +4,7 @@
 #include <hipcub/hipcub.hpp>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -12,6 +13,8 @@
 #include <vector>
 
 #include "../../include/ba.h"
+#include <chrono>
+
 #include "ba_kernels.h"
 
 using namespace ba;
@@ -41,7 +44,6 @@ int fail(int code, const std::string& msg) {
 }
 
 // PCG batches in flight: the host waits for a batch when this many are queued.
-constexpr int kBatchEvents = 2;
 
 struct Arena {
   char* base = nullptr;
@@ -128,10 +130,10 @@ struct ba_problem {
   StepOut* out = nullptr;
   int* flags = nullptr;
   StepOut* h_out = nullptr;  // pinned
-  int* h_done = nullptr;     // pinned, device-mapped: PCG stop flag
+  int* h_done = nullptr;     // pinned, device-mapped: [0] PCG stop flag, [1] last iteration
+                             // whose stop test found the solve still running
   int* h_done_dev = nullptr;
   int last_pcg_iters = 0;
-  hipEvent_t batch_ev[kBatchEvents] = {};
   // LM state
   double lambda = 0.0, cost = 0.0;
   int linearized = 0;
@@ -314,15 +316,22 @@ int stage_schur(ba_problem* h) {
   return BA_OK;
 }
 
-// PCG iterations are queued in batches.  The first batch is as long as the
-// previous solve took (the iteration count changes slowly across LM steps),
-// later ones one iteration long, always one batch ahead of the batch whose
-// completion the host waits for; the kernels raise a host-mapped flag when
-// the solve stops and every launch after that exits at once.
+// PCG iterations: the first batch is as long as the previous solve took (the
+// iteration count changes slowly across LM steps) less one; after it the host
+// queues one iteration at a time, as soon as the stop test of the last queued
+// one (made at the start of its point pass) has found the solve still running,
+// which block 0 reports in host-mapped memory.  The new iteration is then
+// queued while the last one's camera pass and update run, so the device does
+// not wait for the host, and once the test stops the solve no further
+// iteration has been queued.  The kernels raise the host-mapped stop flag when
+// the solve stops; every launch after that exits at once.  A wait that takes
+// far longer than an iteration falls back to synchronising the stream, which
+// also reports device errors.
 int stage_pcg(ba_problem* h) {
   Dev d = make_dev(h);
   const int maxit = h->opt.pcg_max_iters;
-  *h->h_done = 0;
+  h->h_done[0] = 0;
+  __atomic_store_n(&h->h_done[1], -1, __ATOMIC_RELEASE);
   TIMED(BA_K_PCG_INIT, -1, launch_pcg_init(d, h->stream));
   int next_it = 0;
   auto enqueue = [&](int n) -> int {
@@ -340,20 +349,23 @@ int stage_pcg(ba_problem* h) {
   };
   int launched = std::min(maxit, std::max(1, h->last_pcg_iters - 1));
   if (maxit > 0) {
-    // batch b ends with event b % kBatchEvents; the host waits for batch b
-    // only once batches b + 1 .. b + kBatchEvents - 1 are queued behind it
     CHECK_RC(enqueue(launched));
-    HIPC(hipEventRecord(h->batch_ev[0], h->stream));
-    int queued = 1, waited = 0;
     while (launched < maxit) {
+      // wait for the stop test of iteration launched - 1
+      const auto t0 = std::chrono::steady_clock::now();
+      bool synced = false;
+      for (;;) {
+        if (__atomic_load_n(&h->h_done[0], __ATOMIC_ACQUIRE)) break;
+        if (__atomic_load_n(&h->h_done[1], __ATOMIC_ACQUIRE) >= launched - 1) break;
+        if (synced) break;   // everything queued has run: nothing more will change
+        if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(20)) {
+          HIPC(hipStreamSynchronize(h->stream));
+          synced = true;
+        }
+      }
+      if (__atomic_load_n(&h->h_done[0], __ATOMIC_ACQUIRE)) break;
       CHECK_RC(enqueue(1));
       launched += 1;
-      HIPC(hipEventRecord(h->batch_ev[queued % kBatchEvents], h->stream));
-      ++queued;
-      if (queued - waited < kBatchEvents) continue;
-      HIPC(hipEventSynchronize(h->batch_ev[waited % kBatchEvents]));
-      ++waited;
-      if (__atomic_load_n(h->h_done, __ATOMIC_ACQUIRE)) break;
     }
   }
   launch_pcg_final(d, next_it, h->stream);
@@ -997,8 +1009,6 @@ void ba_destroy(ba_problem* h) {
   (void)hipFree(h->arena3.base);
   if (h->h_out) (void)hipHostFree(h->h_out);
   if (h->h_done) (void)hipHostFree(h->h_done);
-  for (hipEvent_t e : h->batch_ev)
-    if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
   delete h;
 }
@@ -1036,17 +1046,16 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
     ba_destroy(h);
     return fail(BA_ERR_ALLOC, "hipHostMalloc");
   }
-  bool ok = hipHostMalloc(reinterpret_cast<void**>(&h->h_done), sizeof(int), hipHostMallocMapped) ==
+  bool ok = hipHostMalloc(reinterpret_cast<void**>(&h->h_done), 2 * sizeof(int), hipHostMallocMapped) ==
                 hipSuccess &&
             hipHostGetDevicePointer(reinterpret_cast<void**>(&h->h_done_dev), h->h_done, 0) ==
                 hipSuccess;
-  for (int k = 0; ok && k < kBatchEvents; ++k)
-    ok = hipEventCreateWithFlags(&h->batch_ev[k], hipEventDisableTiming) == hipSuccess;
   if (!ok) {
     ba_destroy(h);
-    return fail(BA_ERR_ALLOC, "pinned flag or events");
+    return fail(BA_ERR_ALLOC, "pinned flag");
   }
-  *h->h_done = 0;
+  h->h_done[0] = 0;
+  h->h_done[1] = -1;
   rc = build(h, cams, points, obs_cam_idx, obs_pt_idx, obs_uv);
   if (rc == BA_OK && h->opt.solver == BA_SOLVER_DENSE_SCHUR) rc = plan_dense(h);
   if (rc != BA_OK) {

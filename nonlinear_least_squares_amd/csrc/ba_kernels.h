@@ -119,7 +119,8 @@ struct Dev {
   double* cam_rows;  // LDS point pass, PCG: the camera table rows (kCamLdsStride doubles:
                      // q, t, f, k1, k2, z) padded to kCamLdsFill * kLdsBlock, copied as is
   int red_nb;        // blocks of the camera-vector kernels
-  int* host_done;    // host-mapped copy of pcg->done, polled between batches
+  int* host_done;    // host-mapped: [0] copy of pcg->done, [1] last iteration whose stop
+                     // test found the solve still running (the host's pacing)
   PcgState* pcg;
   // update
   double* dp;

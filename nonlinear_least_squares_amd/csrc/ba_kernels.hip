@@ -970,11 +970,17 @@ __device__ __forceinline__ bool pcg_stop_test(const Dev& d, int it, double rhs2,
   if (it == 0) {
     const bool stop = rhs_norm == 0.0;
     if (stop && record && threadIdx.x == 0) stop_pcg(d, 0, 0.0, 0.0, 0);
+    if (!stop && record && threadIdx.x == 0)
+      __hip_atomic_store(d.host_done + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     return stop;
   }
   const double res = sqrt(wave_sum(rr));
   const bool stop = res <= d.tol * rhs_norm;
   if (stop && record && threadIdx.x == 0) stop_pcg(d, it, res, rhs_norm, 0);
+  // the host queues the next iteration on seeing this (a system-scope store;
+  // its order with other stores does not matter)
+  if (!stop && record && threadIdx.x == 0)
+    __hip_atomic_store(d.host_done + 1, it, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   return stop;
 }
 
