@@ -316,8 +316,8 @@ int stage_schur(ba_problem* h) {
   return BA_OK;
 }
 
-// PCG iterations: the first batch is as long as the previous solve took (the
-// iteration count changes slowly across LM steps) less one; after it the host
+// PCG iterations: the first batch is three shorter than the previous solve
+// (the iteration count changes slowly across LM steps); after it the host
 // queues one iteration at a time, as soon as the stop test of the last queued
 // one (made at the start of its point pass) has found the solve still running,
 // which block 0 reports in host-mapped memory.  The new iteration is then
@@ -347,7 +347,7 @@ int stage_pcg(ba_problem* h) {
     }
     return BA_OK;
   };
-  int launched = std::min(maxit, std::max(1, h->last_pcg_iters - 1));
+  int launched = std::min(maxit, std::max(1, h->last_pcg_iters - 3));
   if (maxit > 0) {
     CHECK_RC(enqueue(launched));
     while (launched < maxit) {
