@@ -325,7 +325,8 @@ enum {
   BA_K_DAMP_PT,      /* damped point blocks, their inverses, v                     */
   BA_K_SCHUR_CAM,    /* camera-order E v and Ebar C~^-1 Ebar^T partials            */
   BA_K_PRECOND,      /* per camera B~, rhs, S_jj and its Cholesky factor           */
-  BA_K_PCG_INIT,     /* PCG start: r = rhs, z = M^-1 r                              */
+  BA_K_PCG_INIT,     /* PCG start: r = rhs, z = M^-1 r (no launches of its own: it
+                        runs in the BA_K_PRECOND launch)                            */
   BA_K_PCG_PT,       /* PCG point pass: stop test, C~^-1 E^T z                      */
   BA_K_PCG_CAM,      /* PCG camera pass: chunk partials of E C~^-1 E^T z            */
   BA_K_PCG_Q,        /* PCG p, q = S p by recurrence, p.q partials (no launches
@@ -333,7 +334,8 @@ enum {
   BA_K_PCG_XR,       /* PCG update of x, r, z (with the camera table in LDS, one
                         kernel that also forms p, q and p.q)                        */
   BA_K_BACKSUB,      /* point back-substitution and trial points                   */
-  BA_K_RETRACT,      /* trial cameras                                              */
+  BA_K_RETRACT,      /* trial cameras (no launches of its own in an LM step when the
+                        camera table fits in LDS: BA_K_BACKSUB forms them)          */
   BA_K_COST,         /* trial cost                                                 */
   BA_K_DS_RUNS,      /* dense solver: F = Ebar chol(C~^-1) per (point, camera) run  */
   BA_K_DS_FILL,      /* dense solver: S cleared, padding, rhs row                  */

@@ -13,7 +13,6 @@
 #include <vector>
 
 #include "../../include/ba.h"
-#include <chrono>
 
 #include "ba_kernels.h"
 
@@ -42,8 +41,6 @@ int fail(int code, const std::string& msg) {
   g_err = msg;
   return code;
 }
-
-// PCG batches in flight: the host waits for a batch when this many are queued.
 
 struct Arena {
   char* base = nullptr;
@@ -76,6 +73,7 @@ struct Arena {
 struct ProfRec {
   int kernel;
   int pcg_iter;
+  int step;          // queued LM step (0 otherwise)
   hipEvent_t a, b;
 };
 
@@ -130,10 +128,24 @@ struct ba_problem {
   StepOut* out = nullptr;
   int* flags = nullptr;
   StepOut* h_out = nullptr;  // pinned
-  int* h_done = nullptr;     // pinned, device-mapped: [0] PCG stop flag, [1] last iteration
-                             // whose stop test found the solve still running
-  int* h_done_dev = nullptr;
-  int last_pcg_iters = 0;
+  long long* h_done = nullptr;  // pinned, device-mapped, tagged with the solve's number in
+                                // the upper 32 bits: [0] the solve stopped (low bits: its
+                                // iteration count), [1] the last iteration whose stop test
+                                // found the solve still running
+  long long* h_done_dev = nullptr;
+  long long pcg_seq = 0;        // PCG solves started on this handle
+  int last_pcg_iters = 0;       // -1: the last solve's count was not yet seen
+  // queued LM steps (ba_solve): the device state, its staging copy, the records
+  LmDev* lm = nullptr;
+  LmDev* h_lm = nullptr;        // pinned
+  LmLog* lm_log = nullptr;
+  int64_t lm_log_cap = 0;
+  int queued = 0, q_step = 0;   // stages are building queued step q_step
+  // work a stage left to the next one's launch: k_lin_final's (to the damping
+  // launch) and k_pcg_final's, for a solve capped at this many iterations (to
+  // the back-substitution; -1: none)
+  int lin_final_pending = 0;
+  int pcg_final_iters = -1;
   // LM state
   double lambda = 0.0, cost = 0.0;
   int linearized = 0;
@@ -212,6 +224,13 @@ Dev make_dev(const ba_problem* h) {
   d.cam_rows = h->cam_rows;
   d.red_nb = pcg_red_blocks(h->nc);
   d.host_done = h->h_done_dev;
+  d.pcg_seq = h->pcg_seq;
+  d.lm = h->queued ? h->lm : nullptr;
+  d.lm_log = h->queued ? h->lm_log : nullptr;
+  d.lm_up = h->opt.lambda_up;
+  d.lm_down = h->opt.lambda_down;
+  d.lm_min = h->opt.lambda_min;
+  d.lm_max = h->opt.lambda_max;
   d.pcg = h->pcg;
   d.dp = h->dp;
   d.cost_part = h->cost_part;
@@ -255,7 +274,7 @@ int prof_begin(ba_problem* h, int kernel, int pcg_iter, hipEvent_t* stop) {
   ev.start = a;
   ev.stop = b;
   ev.used = false;
-  h->prof_recs.push_back({kernel, pcg_iter, a, b});
+  h->prof_recs.push_back({kernel, pcg_iter, h->queued ? h->q_step : 0, a, b});
   *stop = b;
   return BA_OK;
 }
@@ -273,10 +292,14 @@ int prof_end(ba_problem* h, hipEvent_t stop) {
 }
 
 // After a synchronisation: fold the recorded pairs into the totals.  PCG
-// launches after convergence exit at once and are not counted.
-int prof_collect(ba_problem* h, int pcg_iters) {
+// launches after convergence exit at once and are not counted, nor are the
+// linearisation launches of queued steps that followed a rejected one
+// (lin_ran[step] == 0; null: all ran).
+int prof_collect_steps(ba_problem* h, const int* step_iters, const int* lin_ran) {
   for (auto& r : h->prof_recs) {
-    if (r.pcg_iter >= 0 && r.pcg_iter >= pcg_iters) continue;
+    if (r.pcg_iter >= 0 && r.pcg_iter >= step_iters[r.step]) continue;
+    if (lin_ran && !lin_ran[r.step] && (r.kernel == BA_K_LIN_PT || r.kernel == BA_K_LIN_CAM))
+      continue;
     float ms = 0.f;
     HIPC(hipEventElapsedTime(&ms, r.a, r.b));
     h->prof_ms[r.kernel] += ms;
@@ -285,6 +308,10 @@ int prof_collect(ba_problem* h, int pcg_iters) {
   h->prof_recs.clear();
   h->prof_used = 0;
   return BA_OK;
+}
+
+int prof_collect(ba_problem* h, int pcg_iters) {
+  return prof_collect_steps(h, &pcg_iters, nullptr);
 }
 
 #define TIMED(kid, it, call)                   \
@@ -297,21 +324,27 @@ int prof_collect(ba_problem* h, int pcg_iters) {
 
 // ---- pieces of one LM iteration -------------------------------------------
 
-int stage_linearize(ba_problem* h) {
+// defer_final: the per-camera sums are left to stage_schur's first launch,
+// which must follow.
+int stage_linearize(ba_problem* h, bool defer_final = false) {
   Dev d = make_dev(h);
   TIMED(BA_K_LIN_PT, -1, launch_lin_pt(d, h->stream));
   TIMED(BA_K_LIN_CAM, -1, launch_lin_cam(d, h->stream));
-  launch_lin_final(d, h->stream);
+  h->lin_final_pending = defer_final ? 1 : 0;
+  if (!defer_final) launch_lin_final(d, h->stream);
   HIPC(hipGetLastError());
   return BA_OK;
 }
 
 int stage_schur(ba_problem* h) {
   Dev d = make_dev(h);
-  HIPC(hipMemsetAsync(h->flags, 0, 2 * sizeof(int), h->stream));
-  TIMED(BA_K_DAMP_PT, -1, launch_damp_pt(d, h->stream));
+  // a queued step after the first finds the flags cleared by the last decision
+  if (!(h->queued && h->q_step > 0)) HIPC(hipMemsetAsync(h->flags, 0, 2 * sizeof(int), h->stream));
+  TIMED(BA_K_DAMP_PT, -1, launch_damp_pt(d, h->stream, h->lin_final_pending != 0));
+  h->lin_final_pending = 0;
   TIMED(BA_K_SCHUR_CAM, -1, launch_schur_cam(d, h->stream));
-  TIMED(BA_K_PRECOND, -1, launch_precond(d, h->stream));
+  // the PCG, which always follows, starts in the same launch
+  TIMED(BA_K_PRECOND, -1, launch_precond(d, h->stream, h->opt.solver != BA_SOLVER_DENSE_SCHUR));
   HIPC(hipGetLastError());
   return BA_OK;
 }
@@ -322,17 +355,24 @@ int stage_schur(ba_problem* h) {
 // one (made at the start of its point pass) has found the solve still running,
 // which block 0 reports in host-mapped memory.  The new iteration is then
 // queued while the last one's camera pass and update run, so the device does
-// not wait for the host, and once the test stops the solve no further
-// iteration has been queued.  The kernels raise the host-mapped stop flag when
-// the solve stops; every launch after that exits at once.  A wait that takes
-// far longer than an iteration falls back to synchronising the stream, which
-// also reports device errors.
-int stage_pcg(ba_problem* h) {
-  Dev d = make_dev(h);
+// not wait for the host and always has the next kernels in its queue, and once
+// the test stops the solve no further iteration has been queued.  The kernels
+// raise the host-mapped stop flag when the solve stops; every launch after
+// that exits at once.  Both host-mapped words carry the solve's number, so a
+// late write of an earlier solve (queued LM steps do not wait for one to
+// finish) is never taken for this one's.  A wait that takes far longer than
+// an iteration falls back to synchronising the stream, which also reports
+// device errors.
+int stage_pcg(ba_problem* h, bool defer_final) {
   const int maxit = h->opt.pcg_max_iters;
-  h->h_done[0] = 0;
-  __atomic_store_n(&h->h_done[1], -1, __ATOMIC_RELEASE);
-  TIMED(BA_K_PCG_INIT, -1, launch_pcg_init(d, h->stream));
+  if (h->last_pcg_iters < 0) {
+    // the last solve was queued to its cap before its stop was seen
+    const long long v = __atomic_load_n(&h->h_done[0], __ATOMIC_ACQUIRE);
+    h->last_pcg_iters = v >= (h->pcg_seq << 32) ? (int)(v & 0xffffffffll) : maxit;
+  }
+  h->pcg_seq += 1;
+  const long long tag = h->pcg_seq << 32;
+  Dev d = make_dev(h);   // the start (r, x, z, partials) was made by k_precond
   int next_it = 0;
   auto enqueue = [&](int n) -> int {
     for (int k = 0; k < n; ++k, ++next_it) {
@@ -355,20 +395,25 @@ int stage_pcg(ba_problem* h) {
       const auto t0 = std::chrono::steady_clock::now();
       bool synced = false;
       for (;;) {
-        if (__atomic_load_n(&h->h_done[0], __ATOMIC_ACQUIRE)) break;
-        if (__atomic_load_n(&h->h_done[1], __ATOMIC_ACQUIRE) >= launched - 1) break;
+        if (__atomic_load_n(&h->h_done[0], __ATOMIC_ACQUIRE) >= tag) break;
+        if (__atomic_load_n(&h->h_done[1], __ATOMIC_ACQUIRE) >= tag + launched - 1) break;
         if (synced) break;   // everything queued has run: nothing more will change
         if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(20)) {
           HIPC(hipStreamSynchronize(h->stream));
           synced = true;
         }
       }
-      if (__atomic_load_n(&h->h_done[0], __ATOMIC_ACQUIRE)) break;
+      if (__atomic_load_n(&h->h_done[0], __ATOMIC_ACQUIRE) >= tag) break;
       CHECK_RC(enqueue(1));
       launched += 1;
     }
   }
-  launch_pcg_final(d, next_it, h->stream);
+  const long long v = __atomic_load_n(&h->h_done[0], __ATOMIC_ACQUIRE);
+  h->last_pcg_iters = v >= tag ? (int)(v & 0xffffffffll) : -1;
+  // a capped solve's record: here, or with defer_final in the back-substitution
+  // launch of stage_update, which must follow
+  h->pcg_final_iters = defer_final ? next_it : -1;
+  if (!defer_final) launch_pcg_final(d, next_it, h->stream);
   HIPC(hipGetLastError());
   return BA_OK;
 }
@@ -408,15 +453,20 @@ int stage_dense(ba_problem* h) {
   return BA_OK;
 }
 
-int stage_solve(ba_problem* h) {
-  return h->opt.solver == BA_SOLVER_DENSE_SCHUR ? stage_dense(h) : stage_pcg(h);
+int stage_solve(ba_problem* h, bool defer_final = false) {
+  h->pcg_final_iters = -1;
+  return h->opt.solver == BA_SOLVER_DENSE_SCHUR ? stage_dense(h) : stage_pcg(h, defer_final);
 }
 
 int stage_update(ba_problem* h) {
   Dev d = make_dev(h);
-  TIMED(BA_K_BACKSUB, -1, launch_backsub(d, h->stream));
-  TIMED(BA_K_RETRACT, -1, launch_retract(d, h->stream));
-  TIMED(BA_K_COST, -1, launch_cost(d, d.pts_trial, d.tab_trial, d.camq_trial, h->stream));
+  // the trial cameras (and a capped PCG solve's record) ride on the
+  // back-substitution launch
+  TIMED(BA_K_BACKSUB, -1, launch_backsub(d, h->stream, h->pcg_final_iters, true));
+  h->pcg_final_iters = -1;
+  TIMED(BA_K_COST, -1, launch_cost(d, d.pts_trial, d.tab_trial, d.camq_trial, h->stream,
+                                   h->queued ? h->q_step : -1));
+  if (h->queued) launch_lm_commit(d, h->stream);
   HIPC(hipGetLastError());
   return BA_OK;
 }
@@ -440,10 +490,10 @@ int dogleg_step(ba_problem* h, ba_step_info* info);
 
 int lm_step(ba_problem* h, ba_step_info* info) {
   if (h->opt.strategy == BA_STRATEGY_DOGLEG) return dogleg_step(h, info);
-  if (!h->linearized) CHECK_RC(stage_linearize(h));
+  if (!h->linearized) CHECK_RC(stage_linearize(h, true));
   CHECK_RC(stage_schur(h));
   h->linearized = 1;
-  CHECK_RC(stage_solve(h));
+  CHECK_RC(stage_solve(h, true));
   CHECK_RC(stage_update(h));
   CHECK_RC(read_out(h));
   const StepOut o = *h->h_out;
@@ -673,6 +723,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   A.add(h->pcg, 1);
   A.add(h->out, 1);
   A.add(h->flags, 2);
+  A.add(h->lm, 1);
   A.add(h->cam_chunk_ptr, nc + 1);
 
   // Partitions need the CSR offsets first, so they get a second small arena
@@ -975,6 +1026,72 @@ const char* kKernelNames[BA_K_NUM] = {"lin_pt",   "lin_cam",  "damp_pt",     "sc
                                       "ds_panel", "ds_update", "ds_backsolve", "cov_zero",
                                       "cov_blocks", "dl_obs",      "dl_step"};
 
+// n LM steps queued without reading each one back: the accept/reject
+// decision, the damping update and the copy of an accepted trial into the
+// current parameters run on the device (k_cost_final, k_lm_commit), the
+// linearisation is launched every step and runs only after an accepted one,
+// and the host waits only for the PCG pacing.  The per-step records are read
+// back after the last step.  Same decisions and arithmetic as lm_step.
+int solve_queued(ba_problem* h, int n, ba_summary* s) {
+  ba_summary sum{};
+  sum.initial_cost = h->cost;
+  if (n > h->lm_log_cap) {
+    if (h->lm_log) HIPC(hipFree(h->lm_log));
+    h->lm_log = nullptr;
+    h->lm_log_cap = 0;
+    HIPC(hipMalloc(reinterpret_cast<void**>(&h->lm_log), sizeof(LmLog) * (size_t)n));
+    h->lm_log_cap = n;
+  }
+  *h->h_lm = LmDev{h->cost, h->lambda, h->linearized ? 0 : 1, 0, {0, 0}};
+  HIPC(hipMemcpyAsync(h->lm, h->h_lm, sizeof(LmDev), hipMemcpyHostToDevice, h->stream));
+  h->queued = 1;
+  int rc = BA_OK;
+  for (int k = 0; k < n && rc == BA_OK; ++k) {
+    h->q_step = k;
+    if (k > 0 || !h->linearized) rc = stage_linearize(h, true);
+    if (rc == BA_OK) rc = stage_schur(h);
+    if (rc == BA_OK) rc = stage_solve(h, true);
+    if (rc == BA_OK) rc = stage_update(h);
+  }
+  h->queued = 0;
+  if (rc != BA_OK) {
+    h->lin_final_pending = 0;
+    h->pcg_final_iters = -1;
+    (void)hipStreamSynchronize(h->stream);
+    return rc;
+  }
+  std::vector<LmLog> log((size_t)n);
+  LmDev L{};
+  HIPC(hipMemcpyAsync(log.data(), h->lm_log, sizeof(LmLog) * (size_t)n, hipMemcpyDeviceToHost,
+                      h->stream));
+  HIPC(hipMemcpyAsync(&L, h->lm, sizeof(LmDev), hipMemcpyDeviceToHost, h->stream));
+  HIPC(hipStreamSynchronize(h->stream));
+  int done = 0;
+  for (; done < n && !log[done].not_spd; ++done) {
+    sum.accepted += log[done].accepted;
+    sum.pcg_iters_total += log[done].pcg_iters;
+  }
+  h->cost = L.cost;
+  h->lambda = L.lambda;
+  h->linearized = L.relin ? 0 : 1;
+  h->iteration += done;
+  h->last_pcg_iters = log[(size_t)n - 1].pcg_iters;
+  if (h->prof_on) {
+    std::vector<int> iters((size_t)n), lin((size_t)n);
+    for (int k = 0; k < n; ++k) {
+      iters[k] = log[k].pcg_iters;
+      lin[k] = k == 0 ? 1 : log[k - 1].accepted;
+    }
+    CHECK_RC(prof_collect_steps(h, iters.data(), lin.data()));
+  }
+  if (done < n) return fail(BA_ERR_NOT_SPD, "a damped block is not positive definite");
+  sum.iterations = n;
+  sum.final_cost = h->cost;
+  sum.lambda = h->lambda;
+  if (s) *s = sum;
+  return BA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1009,6 +1126,8 @@ void ba_destroy(ba_problem* h) {
   (void)hipFree(h->arena3.base);
   if (h->h_out) (void)hipHostFree(h->h_out);
   if (h->h_done) (void)hipHostFree(h->h_done);
+  if (h->h_lm) (void)hipHostFree(h->h_lm);
+  if (h->lm_log) (void)hipFree(h->lm_log);
   for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
   delete h;
 }
@@ -1046,8 +1165,8 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
     ba_destroy(h);
     return fail(BA_ERR_ALLOC, "hipHostMalloc");
   }
-  bool ok = hipHostMalloc(reinterpret_cast<void**>(&h->h_done), 2 * sizeof(int), hipHostMallocMapped) ==
-                hipSuccess &&
+  bool ok = hipHostMalloc(reinterpret_cast<void**>(&h->h_done), 2 * sizeof(long long),
+                          hipHostMallocMapped) == hipSuccess &&
             hipHostGetDevicePointer(reinterpret_cast<void**>(&h->h_done_dev), h->h_done, 0) ==
                 hipSuccess;
   if (!ok) {
@@ -1055,7 +1174,13 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
     return fail(BA_ERR_ALLOC, "pinned flag");
   }
   h->h_done[0] = 0;
-  h->h_done[1] = -1;
+  h->h_done[1] = 0;
+  if (hipHostMalloc(reinterpret_cast<void**>(&h->h_lm), sizeof(LmDev), hipHostMallocDefault) !=
+      hipSuccess) {
+    h->h_lm = nullptr;
+    ba_destroy(h);
+    return fail(BA_ERR_ALLOC, "hipHostMalloc");
+  }
   rc = build(h, cams, points, obs_cam_idx, obs_pt_idx, obs_uv);
   if (rc == BA_OK && h->opt.solver == BA_SOLVER_DENSE_SCHUR) rc = plan_dense(h);
   if (rc != BA_OK) {
@@ -1087,6 +1212,8 @@ int ba_lm_step(ba_problem* h, ba_step_info* info) {
 
 int ba_solve(ba_problem* h, int n_iters, ba_summary* s) {
   if (!h || n_iters < 0) return fail(BA_ERR_ARG, "bad arguments");
+  if (n_iters > 0 && h->opt.strategy == BA_STRATEGY_LM)
+    return solve_queued(h, n_iters, s);
   ba_summary sum{};
   sum.initial_cost = h->cost;
   for (int it = 0; it < n_iters; ++it) {

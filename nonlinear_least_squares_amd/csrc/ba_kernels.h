@@ -62,6 +62,24 @@ struct StepOut {     // everything the host reads back after a step
   int pad;
 };
 
+// LM state on the device while ba_solve queues its steps without reading
+// each one back: the decision after each step (accept if the trial cost is
+// finite and lower, then lower the damping, else raise it) is taken by the
+// cost reduction kernel, and an accepted trial is copied into the current
+// parameters.
+struct LmDev {
+  double cost;       // cost at the current parameters
+  double lambda;     // damping of the next step
+  int relin;         // the last step was accepted: linearise again before the next
+  int halted;        // a damped block was not positive definite: nothing more is applied
+  int pad[2];
+};
+
+struct LmLog {       // one record per queued step, read back after the last
+  double cost_before, cost_after, lambda, pcg_rel_res;
+  int pcg_iters, accepted, not_spd, pad;
+};
+
 struct Dev {
   int64_t nc, np, nobs;
   int n_tiles, n_chunks, n_cost_blocks;
@@ -119,14 +137,21 @@ struct Dev {
   double* cam_rows;  // LDS point pass, PCG: the camera table rows (kCamLdsStride doubles:
                      // q, t, f, k1, k2, z) padded to kCamLdsFill * kLdsBlock, copied as is
   int red_nb;        // blocks of the camera-vector kernels
-  int* host_done;    // host-mapped: [0] copy of pcg->done, [1] last iteration whose stop
-                     // test found the solve still running (the host's pacing)
+  long long* host_done;  // host-mapped, tagged with pcg_seq in the upper 32 bits: [0] the
+                         // solve stopped (low bits: its iteration count), [1] the last
+                         // iteration whose stop test found it still running (the host's pacing)
+  long long pcg_seq;     // number of this PCG solve on the handle (from 1)
   PcgState* pcg;
   // update
   double* dp;
   double* cost_part;
   StepOut* out;
   int* flags;        // [0] non-finite seen, [1] not SPD
+  // queued LM steps (null otherwise): the state, the per-step records and the
+  // damping update factors and bounds
+  LmDev* lm;
+  LmLog* lm_log;
+  double lm_up, lm_down, lm_min, lm_max;
   // dense reduced-camera solve (ba_dense.hip), when selected
   int ds_n;          // 9 nc
   int ds_ld;         // ds_n rounded up to the tile order: order and row stride of S
@@ -146,6 +171,16 @@ struct Dev {
   double* ds_v;      // 2 ds_ld: the back-substitution's right-hand side v, then x
 };
 
+// Damping of the step: the LM state's when steps are queued, else the launch's.
+__device__ __forceinline__ double step_damping(const Dev& d) {
+  return d.lm ? d.lm->lambda : d.lambda;
+}
+// Queued LM steps launch the linearisation every step; it runs only after an
+// accepted step.
+__device__ __forceinline__ bool lin_skipped(const Dev& d) {
+  return d.lm != nullptr && d.lm->relin == 0;
+}
+
 // Events that the next kernel dispatch records at its start and end (set by
 // the profiler before a timed launch, consumed by that launch; null when not
 // timing).  Recorded by the dispatch itself, so they time the kernel alone.
@@ -161,11 +196,13 @@ hipError_t set_lds_camera_limit(int bytes);
 void launch_cam_prep(const double* cams, CamT* tab, double* camq, int64_t nc, hipStream_t s);
 void launch_lin_pt(const Dev& d, hipStream_t s);
 void launch_lin_cam(const Dev& d, hipStream_t s);
-void launch_damp_pt(const Dev& d, hipStream_t s);
+// with_lin_final: the same launch also runs k_lin_final's work (extra blocks).
+void launch_damp_pt(const Dev& d, hipStream_t s, bool with_lin_final = false);
 void launch_schur_cam(const Dev& d, hipStream_t s);
 void launch_lin_final(const Dev& d, hipStream_t s);
-void launch_precond(const Dev& d, hipStream_t s);
-void launch_pcg_init(const Dev& d, hipStream_t s);
+// with_pcg_init: the same launch also starts the PCG (r = rhs, x = 0, z = M^-1 r,
+// the first partial sums, the camera rows of the LDS point pass).
+void launch_precond(const Dev& d, hipStream_t s, bool with_pcg_init = false);
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s);
 void launch_pcg_cam(const Dev& d, hipStream_t s);
 void launch_pcg_q(const Dev& d, int it, hipStream_t s);
@@ -175,10 +212,17 @@ bool pcg_fused_step(const Dev& d);
 void launch_pcg_step(const Dev& d, int it, hipStream_t s);
 void launch_pcg_final(const Dev& d, int iters, hipStream_t s);
 int pcg_red_blocks(int64_t nc);   // blocks of the camera-vector kernels
-void launch_backsub(const Dev& d, hipStream_t s);
+// pcg_iters >= 0: also k_pcg_final's record of a solve capped at pcg_iters;
+// with_retract: also the trial cameras (k_retract's work).
+void launch_backsub(const Dev& d, hipStream_t s, int pcg_iters = -1, bool with_retract = false);
 void launch_retract(const Dev& d, hipStream_t s);
+// Trial cost and the step record; with step >= 0 and d.lm set, also the LM
+// decision for queued step `step` (its record goes to d.lm_log[step]).
 void launch_cost(const Dev& d, const double* pts, const CamT* tab, const double* camq,
-                 hipStream_t s);
+                 hipStream_t s, int step = -1);
+// Queued LM steps: the trial parameters become the current ones if the
+// decision accepted them.
+void launch_lm_commit(const Dev& d, hipStream_t s);
 void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* Jc, double* Jp,
                       double* w, hipStream_t s);
 

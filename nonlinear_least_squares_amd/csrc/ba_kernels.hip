@@ -299,6 +299,7 @@ struct LinPtOp {
 };
 
 __global__ __launch_bounds__(kTile) void k_lin_pt(Dev d) {
+  if (lin_skipped(d)) return;
   LinPtOp op{d};
   point_tile_reduce<9>(d, op, blockIdx.x);
 }
@@ -342,6 +343,7 @@ __device__ __forceinline__ void lin_cam_slot(const Dev& d, const CamG& c, const 
 // slot wait for the loads just issued).
 __global__ __launch_bounds__(kWave) void k_lin_cam(Dev d) {
   __shared__ double s_red[2 * ((kLinCamVals + 1) / 2) * 33];
+  if (lin_skipped(d)) return;
   const int4 bi = d.blk_chunk[blockIdx.x];
   const int cb = bi.x, ce = bi.y, ch = bi.w;
   if (ch < 0) return;
@@ -383,9 +385,36 @@ __global__ __launch_bounds__(kWave) void k_lin_cam(Dev d) {
 
 // ----------------------------------------------------- damping and Schur
 
+// Camera j's B and g_c: its chunk partials summed in chunk order, lane k of a
+// wavefront holding value k, the first kChunkLoads partials of every lane
+// loaded together (indices clamped, the extra ones added as zeros, which
+// leaves the sums' bits as they are).
+__device__ __forceinline__ void lin_final_cam(const Dev& d, int64_t j, int k) {
+  const int c0 = d.cam_chunk_ptr[j], c1 = d.cam_chunk_ptr[j + 1], n = c1 - c0;
+  const int kc = min(k, kLinCamVals - 1);
+  double pp[kChunkLoads];
+#pragma unroll
+  for (int u = 0; u < kChunkLoads; ++u)
+    pp[u] = d.lin_part[(int64_t)max(min(c0 + u, c1 - 1), 0) * kLinCamVals + kc];
+  double v = 0.0;
+#pragma unroll
+  for (int u = 0; u < kChunkLoads; ++u) v += u < n ? pp[u] : 0.0;
+  for (int ch = c0 + kChunkLoads; ch < c1; ++ch) v += d.lin_part[(int64_t)ch * kLinCamVals + kc];
+  if (k < 45) d.B[45 * j + k] = v;
+  else if (k < kLinCamVals) d.gc[9 * j + (k - 45)] = v;
+}
+
 // Damped point block, its inverse through a 3x3 Cholesky factor, v = C~^-1 g_p.
-__global__ void k_damp_pt(Dev d) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+// The first lin_blocks blocks instead finish the linearisation (k_lin_final's
+// work, four cameras per block), which does not depend on the point blocks.
+__global__ void k_damp_pt(Dev d, int lin_blocks) {
+  if ((int)blockIdx.x < lin_blocks) {
+    if (lin_skipped(d)) return;
+    const int64_t j = 4 * (int64_t)blockIdx.x + threadIdx.x / kWave;
+    if (j < d.nc) lin_final_cam(d, j, threadIdx.x & (kWave - 1));
+    return;
+  }
+  const int64_t i = (blockIdx.x - lin_blocks) * (int64_t)blockDim.x + threadIdx.x;
   if (i >= d.np) return;
   double C[6], g[3];
   const bool empty = d.pt_ptr[i] == d.pt_ptr[i + 1];
@@ -406,8 +435,9 @@ __global__ void k_damp_pt(Dev d) {
   }
   const int diag[3] = {0, 3, 5};
   const double X0 = d.pts[3 * i], X1 = d.pts[3 * i + 1], X2 = d.pts[3 * i + 2];
+  const double lam = step_damping(d);
 #pragma unroll
-  for (int a = 0; a < 3; ++a) C[diag[a]] += d.lambda * fmax(C[diag[a]], d.diag_floor);
+  for (int a = 0; a < 3; ++a) C[diag[a]] += lam * fmax(C[diag[a]], d.diag_floor);
   if (!chol_packed<3>(C)) {
     d.flags[1] = 1;
     return;
@@ -582,111 +612,10 @@ __global__ __launch_bounds__(kWave) void k_schur_cam(Dev d) {
   wave_sum_store_lds<kSchurVals>(acc, d.schur_part + (int64_t)ch * kSchurVals, s_buf);
 }
 
-// Per camera: B and g_c as the chunk partials summed in chunk order, one
-// wavefront per camera and one lane per value, the first kChunkLoads
-// partials of every lane loaded together (indices clamped, the extra ones
-// added as zeros, which leaves the sums' bits as they are).
+// One wavefront per camera.
 __global__ __launch_bounds__(kWave) void k_lin_final(Dev d) {
-  const int64_t j = blockIdx.x;
-  const int k = threadIdx.x;
-  const int c0 = d.cam_chunk_ptr[j], c1 = d.cam_chunk_ptr[j + 1], n = c1 - c0;
-  const int kc = min(k, kLinCamVals - 1);
-  double pp[kChunkLoads];
-#pragma unroll
-  for (int u = 0; u < kChunkLoads; ++u)
-    pp[u] = d.lin_part[(int64_t)max(min(c0 + u, c1 - 1), 0) * kLinCamVals + kc];
-  double v = 0.0;
-#pragma unroll
-  for (int u = 0; u < kChunkLoads; ++u) v += u < n ? pp[u] : 0.0;
-  for (int ch = c0 + kChunkLoads; ch < c1; ++ch) v += d.lin_part[(int64_t)ch * kLinCamVals + kc];
-  if (k < 45) d.B[45 * j + k] = v;
-  else if (k < kLinCamVals) d.gc[9 * j + (k - 45)] = v;
-}
-
-// Per camera: B~ = B + lambda D, rhs = -g_c + E v, S_jj = B~ - sum Ebar C~^-1
-// Ebar^T, and the preconditioner block M_j^-1 = S_jj^-1 formed once from the
-// Cholesky factor, column by column, so that a PCG iteration applies it as a
-// plain 9 x 9 product.
-__global__ __launch_bounds__(64) void k_precond(Dev d) {
-  // nine threads per camera: each forms the damped block, S_jj and its factor
-  // (the same bits in all nine), writes a ninth of B~ and S_jj, one rhs entry,
-  // and column `col` of S_jj^-1
-  // seven cameras per block (threads 0..62), so that a camera's nine threads
-  // share the block; threads past the last camera (and the block's 64th)
-  // repeat the last camera's work up to the exchange and store nothing
-  const int cam = threadIdx.x / 9;
-  const int64_t jr = (int64_t)blockIdx.x * 7 + cam;
-  const bool live = threadIdx.x < 63 && jr < d.nc;
-  const int64_t j = live ? jr : d.nc - 1;
-  const int col = live ? (int)threadIdx.x - 9 * cam : 8;
-  const int c0 = d.cam_chunk_ptr[j], c1 = d.cam_chunk_ptr[j + 1];
-  double B[45];
-#pragma unroll
-  for (int k = 0; k < 45; ++k) B[k] = d.B[45 * j + k];
-  const double g = d.gc[9 * j + col];
-#pragma unroll
-  for (int a = 0; a < 9; ++a) {
-    const int ii = sym_idx(9, a, a);
-    B[ii] += d.lambda * fmax(B[ii], d.diag_floor);
-  }
-#pragma unroll
-  for (int k = 0; k < 45; ++k)
-    if (live && k % 9 == col) d.Bd[45 * j + k] = B[k];
-  // the chunk partials: thread col takes E v's entry col and the five
-  // entries k = 5 col .. 5 col + 4 of the Schur block, each in chunk order
-  // (the first kChunkLoads partials loaded together, the extra ones as
-  // zeros), and the camera's nine threads exchange the block through LDS
-  __shared__ double s_sch[8][45];
-  double ev = 0.0;
-  {
-    const int n = c1 - c0;
-    double pe[kChunkLoads], ps[kChunkLoads][5];
-#pragma unroll
-    for (int u = 0; u < kChunkLoads; ++u) {
-      const double* pp = d.schur_part + (int64_t)max(min(c0 + u, c1 - 1), 0) * kSchurVals;
-      pe[u] = pp[col];
-#pragma unroll
-      for (int q = 0; q < 5; ++q) ps[u][q] = pp[9 + min(5 * col + q, 44)];
-    }
-    double bs[5];
-#pragma unroll
-    for (int q = 0; q < 5; ++q) bs[q] = 0.0;
-#pragma unroll
-    for (int k = 0; k < 45; ++k)
-      if (k / 5 == col) bs[k % 5] = B[k];
-#pragma unroll
-    for (int u = 0; u < kChunkLoads; ++u) {
-      ev += u < n ? pe[u] : 0.0;
-#pragma unroll
-      for (int q = 0; q < 5; ++q) bs[q] -= u < n ? ps[u][q] : 0.0;
-    }
-    for (int ch = c0 + kChunkLoads; ch < c1; ++ch) {
-      const double* pp = d.schur_part + (int64_t)ch * kSchurVals;
-      ev += pp[col];
-#pragma unroll
-      for (int q = 0; q < 5; ++q) bs[q] -= pp[9 + min(5 * col + q, 44)];
-    }
-#pragma unroll
-    for (int q = 0; q < 5; ++q)
-      if (live && 5 * col + q < 45) s_sch[cam][5 * col + q] = bs[q];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 45; ++k) B[k] = s_sch[cam][k];
-  if (!live) return;
-  d.rhs[9 * j + col] = -g + ev;
-#pragma unroll
-  for (int k = 0; k < 45; ++k)
-    if (k % 9 == col) d.Mfull[45 * j + k] = B[k];
-  if (!chol_packed<9>(B)) d.flags[1] = 1;
-  double e[9], x[9];
-#pragma unroll
-  for (int a = 0; a < 9; ++a) e[a] = a == col ? 1.0 : 0.0;
-  chol_solve_packed<9>(B, e, x);
-  double* Mi = d.Minv + 45 * j;
-#pragma unroll
-  for (int a = 0; a < 9; ++a)
-    if (a <= col) Mi[sym_idx(9, a, col)] = x[a];
+  if (lin_skipped(d)) return;
+  lin_final_cam(d, blockIdx.x, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------- PCG
@@ -915,39 +844,153 @@ __device__ __forceinline__ void stop_pcg(const Dev& d, int iters, double res, do
   d.pcg->res_norm = res;
   d.pcg->rhs_norm = rhs_norm;
   d.pcg->breakdown = breakdown;
-  *d.host_done = 1;
+  __hip_atomic_store(d.host_done, (d.pcg_seq << 32) | iters, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_SYSTEM);
   __threadfence_system();
 }
 
-__global__ __launch_bounds__(kWave) void k_pcg_init(Dev d) {
-  const int64_t wave = blockIdx.x;
-  const CamLane c = cam_lane(wave, d.nc);
-  const int64_t e = 9 * c.j + c.a;
-  const double r = c.on ? d.rhs[e] : 0.0;
-  const double z = precond_lane(d, c, r);
-  const double bz = bd_row_times(d, c, z);
+// Per camera: B~ = B + lambda D, rhs = -g_c + E v, S_jj = B~ - sum Ebar C~^-1
+// Ebar^T, and the preconditioner block M_j^-1 = S_jj^-1 formed once from the
+// Cholesky factor, column by column, so that a PCG iteration applies it as a
+// plain 9 x 9 product.
+__global__ __launch_bounds__(64) void k_precond(Dev d, int with_init) {
+  // nine threads per camera: each forms the damped block, S_jj and its factor
+  // (the same bits in all nine), writes a ninth of B~ and S_jj, one rhs entry,
+  // and column `col` of S_jj^-1
+  // seven cameras per block (threads 0..62), so that a camera's nine threads
+  // share the block; threads past the last camera (and the block's 64th)
+  // repeat the last camera's work up to the exchange and store nothing
+  const int cam = threadIdx.x / 9;
+  const int64_t jr = (int64_t)blockIdx.x * 7 + cam;
+  const bool live = threadIdx.x < 63 && jr < d.nc;
+  const int64_t j = live ? jr : d.nc - 1;
+  const int col = live ? (int)threadIdx.x - 9 * cam : 8;
+  const int c0 = d.cam_chunk_ptr[j], c1 = d.cam_chunk_ptr[j + 1];
+  double B[45];
+#pragma unroll
+  for (int k = 0; k < 45; ++k) B[k] = d.B[45 * j + k];
+  const double g = d.gc[9 * j + col];
+  const double lam = step_damping(d);
+#pragma unroll
+  for (int a = 0; a < 9; ++a) {
+    const int ii = sym_idx(9, a, a);
+    B[ii] += lam * fmax(B[ii], d.diag_floor);
+  }
+  __shared__ double s_bd[8][45];   // B~ of the block's cameras, for the PCG start
+#pragma unroll
+  for (int k = 0; k < 45; ++k)
+    if (k % 9 == col) {
+      if (live) d.Bd[45 * j + k] = B[k];
+      s_bd[cam][k] = B[k];
+    }
+  // the chunk partials: thread col takes E v's entry col and the five
+  // entries k = 5 col .. 5 col + 4 of the Schur block, each in chunk order
+  // (the first kChunkLoads partials loaded together, the extra ones as
+  // zeros), and the camera's nine threads exchange the block through LDS
+  __shared__ double s_sch[8][45];
+  double ev = 0.0;
+  {
+    const int n = c1 - c0;
+    double pe[kChunkLoads], ps[kChunkLoads][5];
+#pragma unroll
+    for (int u = 0; u < kChunkLoads; ++u) {
+      const double* pp = d.schur_part + (int64_t)max(min(c0 + u, c1 - 1), 0) * kSchurVals;
+      pe[u] = pp[col];
+#pragma unroll
+      for (int q = 0; q < 5; ++q) ps[u][q] = pp[9 + min(5 * col + q, 44)];
+    }
+    double bs[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) bs[q] = 0.0;
+#pragma unroll
+    for (int k = 0; k < 45; ++k)
+      if (k / 5 == col) bs[k % 5] = B[k];
+#pragma unroll
+    for (int u = 0; u < kChunkLoads; ++u) {
+      ev += u < n ? pe[u] : 0.0;
+#pragma unroll
+      for (int q = 0; q < 5; ++q) bs[q] -= u < n ? ps[u][q] : 0.0;
+    }
+    for (int ch = c0 + kChunkLoads; ch < c1; ++ch) {
+      const double* pp = d.schur_part + (int64_t)ch * kSchurVals;
+      ev += pp[col];
+#pragma unroll
+      for (int q = 0; q < 5; ++q) bs[q] -= pp[9 + min(5 * col + q, 44)];
+    }
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+      if (live && 5 * col + q < 45) s_sch[cam][5 * col + q] = bs[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 45; ++k) B[k] = s_sch[cam][k];
+  const double rv = -g + ev;
+  if (live) {
+    d.rhs[9 * j + col] = rv;
+#pragma unroll
+    for (int k = 0; k < 45; ++k)
+      if (k % 9 == col) d.Mfull[45 * j + k] = B[k];
+  }
+  const bool spd = chol_packed<9>(B);
+  if (live && !spd) d.flags[1] = 1;
+  double e[9], x[9];
+#pragma unroll
+  for (int a = 0; a < 9; ++a) e[a] = a == col ? 1.0 : 0.0;
+  chol_solve_packed<9>(B, e, x);
+  if (live) {
+    double* Mi = d.Minv + 45 * j;
+#pragma unroll
+    for (int a = 0; a < 9; ++a)
+      if (a <= col) Mi[sym_idx(9, a, col)] = x[a];
+  }
+  if (!with_init) return;
+  // PCG start for the block's cameras, on the lanes of the camera-vector
+  // kernels (block b, lane 9 c + a: camera 7 b + c, row a): r = rhs, x = 0,
+  // z = M^-1 r, and the block's partials of |r|^2, r.z and z.B~z.  M^-1 and
+  // B~ are applied in the packed element order in which they are stored, so
+  // z and B~z have the bits those stored blocks give.
+  __shared__ double s_x[8][9][9];   // column col of S_jj^-1, x[a] at [cam][col][a]
+#pragma unroll
+  for (int a = 0; a < 9; ++a) s_x[cam][col][a] = x[a];
+  __syncthreads();
+  const int lane = threadIdx.x;
+  const int base = lane < 63 ? 9 * cam : 0;
+  const double r = live ? rv : 0.0;
+  double z = 0.0, bz = 0.0;
+  {
+    double m[9];
+#pragma unroll
+    for (int b = 0; b < 9; ++b) m[b] = col <= b ? s_x[cam][b][col] : s_x[cam][col][b];
+#pragma unroll
+    for (int b = 0; b < 9; ++b) z += m[b] * __shfl(r, base + b, kWave);
+#pragma unroll
+    for (int b = 0; b < 9; ++b) m[b] = s_bd[cam][col <= b ? sym_idx(9, col, b) : sym_idx(9, b, col)];
+#pragma unroll
+    for (int b = 0; b < 9; ++b) bz += m[b] * __shfl(z, base + b, kWave);
+  }
   double rr = 0.0, rz = 0.0, zbz = 0.0;
-  if (c.on) {
-    d.r[e] = r;
-    d.x[e] = 0.0;
-    d.zc[e] = z;
+  if (live) {
+    const int64_t el = 9 * j + col;
+    d.r[el] = r;
+    d.x[el] = 0.0;
+    d.zc[el] = z;
     rr = r * r;
     rz = r * z;
     zbz = z * bz;
     if (d.cam_lds_bytes > 0) {
       // the LDS point pass's camera rows: q (4), t, f, k1, k2 (lane a holds
       // element a, lane 0 also element 9), then z
-      double* row = d.cam_rows + kCamLdsStride * c.j;
-      const double* tabd = reinterpret_cast<const double*>(d.tab) + 16 * c.j;
-      row[c.a] = c.a < 4 ? d.camq[4 * c.j + c.a] : tabd[9 + (c.a - 4)];
-      if (c.a == 0) row[9] = tabd[14];
-      row[10 + c.a] = z;
+      double* row = d.cam_rows + kCamLdsStride * j;
+      const double* tabd = reinterpret_cast<const double*>(d.tab) + 16 * j;
+      row[col] = col < 4 ? d.camq[4 * j + col] : tabd[9 + (col - 4)];
+      if (col == 0) row[9] = tabd[14];
+      row[10 + col] = z;
     }
   }
   rr = wave_sum(rr);
   rz = wave_sum(rz);
   zbz = wave_sum(zbz);
-  if (threadIdx.x == 0) {
+  if (lane == 0) {
     red_rr(d, 0)[blockIdx.x] = rr;
     red_rz(d, 0)[blockIdx.x] = rz;
     red_zbz(d, 0)[blockIdx.x] = zbz;
@@ -971,7 +1014,8 @@ __device__ __forceinline__ bool pcg_stop_test(const Dev& d, int it, double rhs2,
     const bool stop = rhs_norm == 0.0;
     if (stop && record && threadIdx.x == 0) stop_pcg(d, 0, 0.0, 0.0, 0);
     if (!stop && record && threadIdx.x == 0)
-      __hip_atomic_store(d.host_done + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(d.host_done + 1, d.pcg_seq << 32, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
     return stop;
   }
   const double res = sqrt(wave_sum(rr));
@@ -980,7 +1024,8 @@ __device__ __forceinline__ bool pcg_stop_test(const Dev& d, int it, double rhs2,
   // the host queues the next iteration on seeing this (a system-scope store;
   // its order with other stores does not matter)
   if (!stop && record && threadIdx.x == 0)
-    __hip_atomic_store(d.host_done + 1, it, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(d.host_done + 1, (d.pcg_seq << 32) | it, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
   return stop;
 }
 
@@ -1257,7 +1302,6 @@ __global__ __launch_bounds__(kLdsBlock) void k_pcg_pt_lds(Dev d, int it) {
   pcg_pt_lds_body<0>(d, it);
 }
 
-__global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d) { pcg_pt_lds_body<1>(d, 0); }
 
 // Camera side of S p, one wavefront per camera chunk (placed as in k_lin_cam).
 // The camera is uniform, so its parameters sit in scalar registers.
@@ -1573,20 +1617,22 @@ __global__ __launch_bounds__(kWave) void k_pcg_step(Dev d, int it) {
 
 // After the last queued iteration: record the outcome if the solve ran to the
 // iteration limit (a stop inside the loop has already been recorded).
-__global__ __launch_bounds__(kWave) void k_pcg_final(Dev d, int iters) {
+// A solve that ran to its cap (`iters` iterations) without stopping: its
+// residual and the stop record.  One full wavefront.
+__device__ __forceinline__ void pcg_final_wave(const Dev& d, int iters) {
   if (d.pcg->done) return;
   const double rhs_norm = sqrt(wave_sum_array(red_rhs(d), d.red_nb));
   const double res = iters == 0 ? rhs_norm : sqrt(wave_sum_array(red_rr(d, iters & 1), d.red_nb));
   if (threadIdx.x == 0) stop_pcg(d, iters, res, rhs_norm, 0);
 }
 
+__global__ __launch_bounds__(kWave) void k_pcg_final(Dev d, int iters) { pcg_final_wave(d, iters); }
+
 // ------------------------------------------------------------ update, cost
 
 // Trial camera: rotation q(dphi) (x) q(w) in the hemisphere qw >= 0, back to
 // axis-angle by 2 atan2(|v|, qw) v / |v|; the other parameters additive.
-__global__ void k_retract(Dev d) {
-  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (j >= d.nc) return;
+__device__ __forceinline__ void retract_camera(const Dev& d, int64_t j) {
   const double* c = d.cams + 9 * j;
   const double* dx = d.x + 9 * j;
   double qa[4], qb[4];
@@ -1639,6 +1685,26 @@ __global__ void k_retract(Dev d) {
   t.k1 = o[7];
   t.k2 = o[8];
   store_geometry(d.tab_trial + j, t);
+}
+
+__global__ void k_retract(Dev d) {
+  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (j < d.nc) retract_camera(d, j);
+}
+
+// Point back-substitution with the camera table in LDS.  After its own work,
+// wavefront 0 of each block forms the trial cameras j = block + 64 k * blocks
+// (lane k) when `with_retract` is set (k_retract's work), and wavefront 0 of
+// block 0 records a PCG solve that ran to its cap of `pcg_iters` iterations
+// when pcg_iters >= 0 (k_pcg_final's work): neither depends on the points.
+__global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d, int pcg_iters, int with_retract) {
+  pcg_pt_lds_body<1>(d, 0);
+  if (threadIdx.x >= kWave) return;
+  if (pcg_iters >= 0 && blockIdx.x == 0) pcg_final_wave(d, pcg_iters);
+  if (with_retract)
+    for (int64_t j = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; j < d.nc;
+         j += (int64_t)kWave * gridDim.x)
+      retract_camera(d, j);
 }
 
 __global__ __launch_bounds__(256) void k_cost(Dev d, const double* __restrict__ pts,
@@ -1752,6 +1818,7 @@ __global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __r
 // point's last observation, the robust weight at every observation.
 __global__ __launch_bounds__(kLdsBlock) void k_lin_pt_lds(Dev d) {
   extern __shared__ double s_cam[];
+  if (lin_skipped(d)) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * (kLdsBlock / kWave) + threadIdx.x / kWave;
   const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
@@ -1831,18 +1898,83 @@ __global__ __launch_bounds__(kLdsBlock) void k_lin_pt_lds(Dev d) {
   }
 }
 
-__global__ __launch_bounds__(kUpdBlock) void k_cost_final(Dev d, int n_parts) {
+// The cost from the per-block partials and the step record.  For a queued LM
+// step (step >= 0) also the decision: the trial is accepted when its cost is
+// finite and below the current one, and the damping is then divided by the
+// lowering factor (floored at the minimum), else multiplied by the raising
+// factor (capped at the maximum); a damped block that was not positive
+// definite halts the queue, after which no step changes the state.  The flags
+// are cleared for the next step.
+__global__ __launch_bounds__(kUpdBlock) void k_cost_final(Dev d, int n_parts, int step) {
   __shared__ double s_buf[kUpdBlock / kWave];
   double acc = 0.0;
   for (int b = threadIdx.x; b < n_parts; b += kUpdBlock) acc += d.cost_part[b];
   acc = block_sum<kUpdBlock>(acc, s_buf);
   if (threadIdx.x == 0) {
+    const int iters = d.pcg->iters;
+    const double rel = d.pcg->rhs_norm > 0.0 ? d.pcg->res_norm / d.pcg->rhs_norm : 0.0;
+    const int not_spd = d.flags[1];
     d.out->trial_cost = acc;
-    d.out->pcg_iters = d.pcg->iters;
-    d.out->pcg_rel_res = d.pcg->rhs_norm > 0.0 ? d.pcg->res_norm / d.pcg->rhs_norm : 0.0;
+    d.out->pcg_iters = iters;
+    d.out->pcg_rel_res = rel;
     d.out->nonfinite = isfinite(acc) ? 0 : 1;
-    d.out->not_spd = d.flags[1];
+    d.out->not_spd = not_spd;
+    if (step >= 0 && d.lm) {
+      LmDev& L = *d.lm;
+      const double before = L.cost, lam = L.lambda;
+      int accepted = 0;
+      if (!L.halted) {
+        if (not_spd) {
+          L.halted = 1;
+        } else if (isfinite(acc) && acc < before) {
+          accepted = 1;
+          L.cost = acc;
+          L.lambda = fmax(lam / d.lm_down, d.lm_min);
+        } else {
+          L.lambda = fmin(lam * d.lm_up, d.lm_max);
+        }
+      }
+      L.relin = accepted;
+      LmLog& g = d.lm_log[step];
+      g.cost_before = before;
+      g.cost_after = acc;
+      g.lambda = lam;
+      g.pcg_rel_res = rel;
+      g.pcg_iters = iters;
+      g.accepted = accepted;
+      g.not_spd = not_spd;
+      g.pad = 0;
+      d.flags[0] = 0;
+      d.flags[1] = 0;
+    }
   }
+}
+
+// Accepted queued step: the trial cameras, points, camera tables and
+// quaternions become the current ones (blockIdx.y picks the array).
+__global__ __launch_bounds__(256) void k_lm_commit(Dev d) {
+  if (!d.lm->relin) return;
+  const double* src;
+  double* dst;
+  int64_t n;
+  switch (blockIdx.y) {
+    case 0: src = d.pts_trial; dst = const_cast<double*>(d.pts); n = 3 * d.np; break;
+    case 1: src = d.cams_trial; dst = const_cast<double*>(d.cams); n = 9 * d.nc; break;
+    case 2:
+      src = reinterpret_cast<const double*>(d.tab_trial);
+      dst = const_cast<double*>(reinterpret_cast<const double*>(d.tab));
+      n = (int64_t)(sizeof(CamT) / sizeof(double)) * d.nc;
+      break;
+    default: src = d.camq_trial; dst = const_cast<double*>(d.camq); n = 4 * d.nc; break;
+  }
+  // the arrays start on 256-byte boundaries: pairs as 16-byte moves, then an odd tail
+  const int64_t pairs = n / 2;
+  const double2* s2 = reinterpret_cast<const double2*>(src);
+  double2* d2 = reinterpret_cast<double2*>(dst);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < pairs; i += stride)
+    d2[i] = s2[i];
+  if ((n & 1) && blockIdx.x == 0 && threadIdx.x == 0) dst[n - 1] = src[n - 1];
 }
 
 // ------------------------------------------------------------------- debug
@@ -1993,8 +2125,10 @@ void launch_lin_pt(const Dev& d, hipStream_t s) {
 void launch_lin_cam(const Dev& d, hipStream_t s) {
   if (d.n_chunk_blocks > 0) launch(k_lin_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
 }
-void launch_damp_pt(const Dev& d, hipStream_t s) {
-  if (d.np > 0) launch(k_damp_pt, dim3(blocks_for(d.np, 256)), dim3(256), s, 0u, d);
+void launch_damp_pt(const Dev& d, hipStream_t s, bool with_lin_final) {
+  const int lin_blocks = with_lin_final ? (int)((d.nc + 3) / 4) : 0;
+  const unsigned nb = (unsigned)lin_blocks + (d.np > 0 ? blocks_for(d.np, 256) : 0u);
+  if (nb > 0) launch(k_damp_pt, dim3(nb), dim3(256), s, 0u, d, lin_blocks);
 }
 void launch_schur_cam(const Dev& d, hipStream_t s) {
   if (d.n_chunk_blocks > 0) launch(k_schur_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
@@ -2002,11 +2136,10 @@ void launch_schur_cam(const Dev& d, hipStream_t s) {
 void launch_lin_final(const Dev& d, hipStream_t s) {
   if (d.nc > 0) launch(k_lin_final, dim3((unsigned)d.nc), dim3(kWave), s, 0u, d);
 }
-void launch_precond(const Dev& d, hipStream_t s) {
-  if (d.nc > 0) launch(k_precond, dim3((unsigned)((d.nc + 6) / 7)), dim3(64), s, 0u, d);
-}
-void launch_pcg_init(const Dev& d, hipStream_t s) {
-  launch(k_pcg_init, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d);
+void launch_precond(const Dev& d, hipStream_t s, bool with_pcg_init) {
+  if (d.nc > 0)
+    launch(k_precond, dim3((unsigned)cam_vector_blocks(d.nc)), dim3(64), s, 0u, d,
+           with_pcg_init ? 1 : 0);
 }
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
   if (pcg_fused_step(d)) {
@@ -2034,27 +2167,37 @@ void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
   launch(k_pcg_final, dim3(1), dim3(kWave), s, 0u, d, iters);
 }
 int pcg_red_blocks(int64_t nc) { return cam_vector_blocks(nc); }
-void launch_backsub(const Dev& d, hipStream_t s) {
-  if (d.cam_lds_bytes > 0) {
-    if (d.lds_blocks > 0)
-      launch(k_backsub_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s, d.cam_lds_bytes, d);
-  } else if (d.n_tiles > 0) {
-    launch(k_backsub, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
+void launch_backsub(const Dev& d, hipStream_t s, int pcg_iters, bool with_retract) {
+  if (d.cam_lds_bytes > 0 && d.lds_blocks > 0) {
+    launch(k_backsub_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s, d.cam_lds_bytes, d, pcg_iters,
+           with_retract ? 1 : 0);
+    return;
   }
+  // the back-substitution first: a timed launch times the first dispatch
+  if (d.cam_lds_bytes == 0 && d.n_tiles > 0) launch(k_backsub, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
+  if (pcg_iters >= 0) launch_pcg_final(d, pcg_iters, s);
+  if (with_retract) launch_retract(d, s);
 }
 void launch_retract(const Dev& d, hipStream_t s) {
   if (d.nc > 0) launch(k_retract, dim3(blocks_for(d.nc, 128)), dim3(128), s, 0u, d);
 }
 void launch_cost(const Dev& d, const double* pts, const CamT* tab, const double* camq,
-                 hipStream_t s) {
+                 hipStream_t s, int step) {
   if (d.cam_lds_bytes > 0 && d.lds_blocks > 0) {
     launch(k_cost_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
            (uint32_t)(kGeoLdsStride * 8 * d.nc), d, pts, tab, camq);
-    launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.lds_blocks);
+    launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.lds_blocks, step);
   } else {
     if (d.n_cost_blocks > 0) launch(k_cost, dim3(d.n_cost_blocks), dim3(256), s, 0u, d, pts, tab);
-    launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.n_cost_blocks);
+    launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.n_cost_blocks, step);
   }
+}
+void launch_lm_commit(const Dev& d, hipStream_t s) {
+  // 3 np doubles of points dominate: two per thread, at most 2048 blocks
+  const int64_t n = 3 * d.np > 16 * d.nc ? 3 * d.np : 16 * d.nc;
+  const unsigned want = blocks_for(n / 2 + 1, 256);
+  const unsigned bx = want < 2048u ? want : 2048u;
+  launch(k_lm_commit, dim3(bx, 4), dim3(256), s, 0u, d);
 }
 void launch_debug_obs(const Dev& d, const int32_t* perm_pt, double* r, double* Jc, double* Jp,
                       double* w, hipStream_t s) {
