@@ -177,7 +177,17 @@ int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t 
  * be NULL.  A rejected step is not an error. */
 int ba_lm_step(ba_problem* h, ba_step_info* info);
 
-/* Exactly n_iters LM iterations (no early exit).  s may be NULL. */
+/* Exactly n_iters LM iterations (no early exit).  s may be NULL.  With the LM
+ * strategy the iterations are queued on the handle's stream without reading
+ * each one back: the accept/reject decision and the damping update are taken
+ * on the device, with the same comparisons and arithmetic as ba_lm_step, so
+ * the result equals n_iters calls of ba_lm_step.  The call returns after the
+ * last iteration has finished.  A damped block that is not positive definite
+ * stops the changes at that iteration: BA_ERR_NOT_SPD is returned and the
+ * handle keeps the state after the last good iteration (s is not written),
+ * as a loop of ba_lm_step calls would leave it.  The per-iteration records
+ * take 48 bytes per iteration of device memory, allocated by the first call
+ * that needs more. */
 int ba_solve(ba_problem* h, int n_iters, ba_summary* s);
 
 /* Cost at the current parameters, recomputed on the device. */
