@@ -13,7 +13,15 @@
 // PCG and Schur passes gather each point's 64-byte record with four lanes),
 // and the lanes are summed in a fixed order (through LDS, or a DPP scan);
 // per-camera totals add the chunk partials in chunk order.
-// No floating-point atomics: results are bitwise reproducible run to run.
+// Per-camera vector kernels (preconditioner, PCG start and update) run seven
+// cameras per wavefront, nine lanes per camera.  Small per-camera jobs ride on
+// the launches of larger passes: the PCG start on the preconditioner's, the
+// trial cameras and a capped solve's record on the back-substitution's, the
+// per-camera linearisation sums on the damping's.  For queued LM steps the
+// cost reduction also takes the accept/reject decision and a copy kernel
+// commits an accepted trial.
+// No floating-point atomics and fixed summation orders throughout, so that
+// results reproduce bit for bit run to run.
 #include "ba_kernels.h"
 
 #include <hip/hip_ext.h>
