@@ -728,6 +728,26 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_copy": n * 8, "copies": 3}), flush=True)
 
 
+def gather_calibration():
+    """A gather of known size: 8 Mi rows of 64 bytes (512 MiB), each read once
+    in a random order (a permutation), the shape of the camera passes' point
+    record gathers.  Its FETCH_SIZE reading, set against the plain copy's,
+    shows how the counter counts 64-byte gathers."""
+    import torch
+    rows = 8 * 1024 * 1024
+    table = torch.ones(rows, 8, dtype=torch.float64, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    idx = torch.randperm(rows, device="cuda", generator=gen)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out = torch.index_select(table, 0, idx)
+    torch.cuda.synchronize()
+    del out
+    print(json.dumps({"gather_calibration_rows": rows, "row_bytes": 64, "index_bytes": rows * 8,
+                      "gathers": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -741,9 +761,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (byte-counter calibration)")
+    ap.add_argument("--gather-calibration", action="store_true",
+                    help="run only a 512 MiB gather of 64-byte rows (byte-counter calibration)")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration()
+    if args.gather_calibration:
+        return gather_calibration()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the libraries have no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
