@@ -163,10 +163,15 @@ int ba_options_default(ba_options* o);
  * CSR offsets and work partitions, allocates the whole arena and evaluates
  * the initial cost.  The caller may free its inputs when this returns.
  * opts may be NULL (defaults).  On error *out is left NULL.
- * When the camera table fits in LDS (up to about 1,100 cameras) the point
- * passes of the PCG and the back-substitution keep it there; the environment
- * variable BA_NO_LDS_CAMERAS=1 at creation selects the global-table kernels
- * instead (same results up to rounding). */
+ * The point passes keep camera data in each compute unit's LDS by size: up
+ * to 1,077 cameras the whole rows (geometry and the PCG's 9-vector), up to
+ * 2,240 cameras only the 9-vectors of the PCG and back-substitution passes,
+ * with the geometry read from memory (the linearisation and cost passes then
+ * read memory too); past that every pass reads the camera table from memory.
+ * The first two layouts give the same bits.  The environment variables
+ * BA_NO_LDS_CAMERAS=1 (memory) and BA_SPLIT_LDS_CAMERAS=1 (the 9-vectors
+ * only, where they fit) at creation select another layout; the memory
+ * layout's results differ from the others only by rounding. */
 int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t n_pts,
               const int32_t* obs_cam_idx, const int32_t* obs_pt_idx, const double* obs_uv,
               int64_t n_obs, const ba_options* opts, ba_problem** out);

@@ -86,7 +86,7 @@ struct ba_problem {
   ba_options opt{};
   hipStream_t stream = nullptr;
   int n_tiles = 0, n_chunks = 0, n_cost_blocks = 0, lds_blocks = 0,
-      cam_lds_bytes = 0, n_chunk_blocks = 0;
+      cam_lds_bytes = 0, lds_split = 0, n_chunk_blocks = 0;
   Arena arena;   // everything sized by n_cams, n_pts, n_obs
   Arena arena2;  // partitions and partial sums, sized after the CSR offsets
   Arena arena3;  // dense solver: runs, block pair lists, S
@@ -174,6 +174,7 @@ Dev make_dev(const ba_problem* h) {
   d.blk_chunk = h->blk_chunk;
   d.lds_blocks = h->lds_blocks;
   d.cam_lds_bytes = h->cam_lds_bytes;
+  d.lds_split = h->lds_split;
   d.wave_begin = h->wave_begin;
   d.n_cost_blocks = h->n_cost_blocks;
   d.loss = h->opt.loss;
@@ -805,16 +806,31 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   // The kernels that keep the camera table in LDS run one block per compute
   // unit; each wavefront takes an equal share of the observations, moved to
   // the nearest point start at or after the even split.
+  // Up to kCamLdsMaxCams cameras their whole rows go to LDS; up to
+  // kZLdsMaxCams only their 9-vectors (the split layout); past that every
+  // pass reads the camera table from memory.  BA_NO_LDS_CAMERAS=1 at creation
+  // selects the memory-table kernels, BA_SPLIT_LDS_CAMERAS=1 the split layout
+  // when it fits (for the tests of those paths on small scenes).
   std::vector<int32_t> wave_begin;
   {
-    const int64_t bytes = (int64_t)kCamLdsStride * 8 * nc;
     int dev = 0, cus = 0;
     TRY(hipGetDevice(&dev));
     TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     h->cam_lds_bytes = 0;
+    h->lds_split = 0;
     h->lds_blocks = 0;
     const char* off = std::getenv("BA_NO_LDS_CAMERAS");
-    if (bytes <= kCamLdsMaxBytes && N > 0 && !(off && off[0] == '1')) {
+    const char* spl = std::getenv("BA_SPLIT_LDS_CAMERAS");
+    int64_t bytes = 0;
+    if (N > 0 && !(off && off[0] == '1')) {
+      if (nc <= kCamLdsMaxCams && !(spl && spl[0] == '1')) {
+        bytes = (int64_t)kCamLdsStride * 8 * nc;
+      } else if (nc <= kZLdsMaxCams) {
+        bytes = (int64_t)kZLdsStride * 8 * nc;
+        h->lds_split = 1;
+      }
+    }
+    if (bytes > 0) {
       TRY(set_lds_camera_limit((int)bytes));
       h->cam_lds_bytes = (int)bytes;
       constexpr int wpb = kLdsBlock / kWave;
@@ -882,7 +898,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   P.add(h->cost_part, (int64_t)std::max(h->n_cost_blocks, 1));
   P.add(h->red_part, 8 * (int64_t)pcg_red_blocks(nc) + 2);
   P.add(h->pt_dot, (int64_t)std::max(h->lds_blocks, 1));
-  P.add(h->cam_rows, h->cam_lds_bytes > 0 ? (int64_t)kCamLdsFill * kLdsBlock : 1);
+  P.add(h->cam_rows, h->cam_lds_bytes > 0 && !h->lds_split ? (int64_t)kCamLdsFill * kLdsBlock : 1);
   P.add(h->dl_vpart, 3 * (int64_t)dl_vec_blocks(nc, h->np));
   P.add(h->dl_opart, 3 * (int64_t)std::max(h->n_chunk_blocks, 1));
   P.add(h->dl_out, 6);

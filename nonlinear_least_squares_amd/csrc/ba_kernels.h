@@ -30,8 +30,12 @@ constexpr int kLdsBlock = 1024;   // threads of the persistent LDS-camera-table 
 constexpr int kCamLdsStride = 19; // doubles per camera in the LDS table: q (4), t, f, k1, k2, vector (9)
 constexpr int kCamLdsFill = 20;   // table elements per thread in the copy (>= 19 * max cameras / kLdsBlock)
 constexpr int kCamLdsMaxCams = kCamLdsFill * 1024 / kCamLdsStride;   // 1,077
-constexpr int kCamLdsMaxBytes = kCamLdsStride * 8 * kCamLdsMaxCams;
 constexpr int kCostLdsFill = (10 * kCamLdsMaxCams + 1023) / 1024;   // geometry elements per thread
+// Past kCamLdsMaxCams the PCG and back-substitution point passes keep only the
+// cameras' 9-vectors in LDS (stride 9) and read the geometry from the camera
+// table in memory; the linearisation and cost passes then read memory too.
+constexpr int kZLdsStride = 9;
+constexpr int kZLdsMaxCams = 2240;   // 9 * 2240 <= kCamLdsFill * kLdsBlock, 161 KB of LDS
 constexpr int kChunkLoads = 8;   // a camera's chunk partials loaded together in the per-camera sums
 constexpr int kChunk = 1024;      // observations per camera chunk (one wavefront)
 constexpr int kPointBands = 4;    // point-index bands of the camera chunks (block b: band b % 4,
@@ -136,6 +140,7 @@ struct Dev {
   double* pt_dot;    // per-block partials of z^T E C~^-1 E^T z from the LDS point pass
   double* cam_rows;  // LDS point pass, PCG: the camera table rows (kCamLdsStride doubles:
                      // q, t, f, k1, k2, z) padded to kCamLdsFill * kLdsBlock, copied as is
+  int lds_split;     // 1: the LDS point passes hold only the camera vectors (kZLdsStride)
   int red_nb;        // blocks of the camera-vector kernels
   long long* host_done;  // host-mapped, tagged with pcg_seq in the upper 32 bits: [0] the
                          // solve stopped (low bits: its iteration count), [1] the last

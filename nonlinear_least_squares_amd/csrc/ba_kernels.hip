@@ -985,7 +985,7 @@ __global__ __launch_bounds__(64) void k_precond(Dev d, int with_init) {
     rr = r * r;
     rz = r * z;
     zbz = z * bz;
-    if (d.cam_lds_bytes > 0) {
+    if (d.cam_lds_bytes > 0 && !d.lds_split) {
       // the LDS point pass's camera rows: q (4), t, f, k1, k2 (lane a holds
       // element a, lane 0 also element 9), then z
       double* row = d.cam_rows + kCamLdsStride * j;
@@ -1071,7 +1071,12 @@ __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d) {
 //   MODE 0: u = C~^-1 (E^T z) into the point records (PCG), after the
 //           iteration's stop test, which wavefront 0 of each block makes;
 //   MODE 1: dp = C~^-1 (-g_p - E^T dc) and the trial points (back-substitution).
-template <int MODE>
+// SPLIT: the LDS rows hold only the cameras' 9-vectors (kZLdsStride), and each
+// observation reads its camera's geometry (R, t, f, k1, k2) from the camera
+// table in memory: the layout for more cameras than whole rows fit.  R in that
+// table was formed from the same quaternion by the same function, so both
+// layouts compute with the same bits.
+template <int MODE, int SPLIT>
 __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   extern __shared__ double s_cam[];
   __shared__ int s_prog;
@@ -1105,11 +1110,16 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   // the test; its outcome reaches the other wavefronts through LDS at the
   // barrier before the loop.
   {
-    const int ne = kCamLdsStride * (int)d.nc;
+    const int ne = (SPLIT ? kZLdsStride : kCamLdsStride) * (int)d.nc;
     const double* tabd = reinterpret_cast<const double*>(d.tab);
     int done = MODE == 0 ? d.pcg->done : 0;
     double t[kCamLdsFill];
-    if (MODE == 0) {
+    if (SPLIT) {
+      // the vectors are stored nine per camera in memory already
+      const double* src = MODE == 0 ? d.zc : d.x;
+#pragma unroll
+      for (int u = 0; u < kCamLdsFill; ++u) t[u] = src[min((int)threadIdx.x + u * kLdsBlock, ne - 1)];
+    } else if (MODE == 0) {
       // the PCG keeps the rows in this layout in memory (padded to the whole copy)
 #pragma unroll
       for (int u = 0; u < kCamLdsFill; ++u) t[u] = d.cam_rows[threadIdx.x + u * kLdsBlock];
@@ -1170,6 +1180,10 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     // unconditionally (indices clamped into range, results of idle lanes
     // dropped), so the loads in flight are the same on every path and each
     // wait, by count in issue order, covers only what is needed by then.
+    // split layout: the camera's geometry first, so that its latency runs
+    // under the issue of the loads after it
+    CamG c;
+    if (SPLIT) load_cam(d.tab, cj, c);
     double ci[6];
     const double* Ci = d.Cinv + 6 * (int64_t)cpt_c;
 #pragma unroll
@@ -1188,9 +1202,12 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     const double nx0 = d.pts[3 * npt_c], nx1 = d.pts[3 * npt_c + 1], nx2 = d.pts[3 * npt_c + 2];
     const double nw = d.w_pt[min(s + kWave, last)];
     __builtin_amdgcn_sched_barrier(0);
-    CamG c;
     double xv[9];
-    {
+    if (SPLIT) {
+      const double* r = s_cam + kZLdsStride * cj;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) xv[k] = r[k];
+    } else {
       const double* r = s_cam + kCamLdsStride * cj;
       double q[4];
 #pragma unroll
@@ -1306,8 +1323,9 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   }
 }
 
+template <int SPLIT>
 __global__ __launch_bounds__(kLdsBlock) void k_pcg_pt_lds(Dev d, int it) {
-  pcg_pt_lds_body<0>(d, it);
+  pcg_pt_lds_body<0, SPLIT>(d, it);
 }
 
 
@@ -1607,7 +1625,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_step(Dev d, int it) {
   double rr = 0.0, rzn = 0.0, zbz = 0.0;
   if (c.on) {
     d.zc[e] = zn;
-    d.cam_rows[kCamLdsStride * c.j + 10 + c.a] = zn;
+    if (!d.lds_split) d.cam_rows[kCamLdsStride * c.j + 10 + c.a] = zn;
     rr = r * r;
     rzn = r * zn;
     zbz = zn * bz;
@@ -1705,8 +1723,9 @@ __global__ void k_retract(Dev d) {
 // (lane k) when `with_retract` is set (k_retract's work), and wavefront 0 of
 // block 0 records a PCG solve that ran to its cap of `pcg_iters` iterations
 // when pcg_iters >= 0 (k_pcg_final's work): neither depends on the points.
+template <int SPLIT>
 __global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d, int pcg_iters, int with_retract) {
-  pcg_pt_lds_body<1>(d, 0);
+  pcg_pt_lds_body<1, SPLIT>(d, 0);
   if (threadIdx.x >= kWave) return;
   if (pcg_iters >= 0 && blockIdx.x == 0) pcg_final_wave(d, pcg_iters);
   if (with_retract)
@@ -2084,17 +2103,15 @@ DispatchEvents& dispatch_events() {
 }
 
 hipError_t set_lds_camera_limit(int bytes) {
-  hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin_pt_lds),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e0 != hipSuccess) return e0;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pcg_pt_lds),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cost_lds),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_backsub_lds),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  const void* const kernels[] = {
+      reinterpret_cast<const void*>(&k_lin_pt_lds),     reinterpret_cast<const void*>(&k_cost_lds),
+      reinterpret_cast<const void*>(&k_pcg_pt_lds<0>),  reinterpret_cast<const void*>(&k_pcg_pt_lds<1>),
+      reinterpret_cast<const void*>(&k_backsub_lds<0>), reinterpret_cast<const void*>(&k_backsub_lds<1>)};
+  for (const void* k : kernels) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 namespace {
@@ -2122,7 +2139,7 @@ void launch_cam_prep(const double* cams, CamT* tab, double* camq, int64_t nc, hi
   if (nc > 0) launch(k_cam_prep, dim3(blocks_for(nc, 256)), dim3(256), s, 0u, cams, tab, camq, nc);
 }
 void launch_lin_pt(const Dev& d, hipStream_t s) {
-  if (d.cam_lds_bytes > 0) {
+  if (d.cam_lds_bytes > 0 && !d.lds_split) {
     if (d.lds_blocks > 0)
       launch(k_lin_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
              (uint32_t)(kGeoLdsStride * 8 * d.nc), d);
@@ -2151,7 +2168,8 @@ void launch_precond(const Dev& d, hipStream_t s, bool with_pcg_init) {
 }
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
   if (pcg_fused_step(d)) {
-    launch(k_pcg_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s, d.cam_lds_bytes, d, it);
+    launch(d.lds_split ? k_pcg_pt_lds<1> : k_pcg_pt_lds<0>, dim3(d.lds_blocks), dim3(kLdsBlock), s,
+           d.cam_lds_bytes, d, it);
     return;
   }
   launch(k_pcg_stop, dim3(1), dim3(kWave), s, 0u, d, it);
@@ -2177,8 +2195,8 @@ void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
 int pcg_red_blocks(int64_t nc) { return cam_vector_blocks(nc); }
 void launch_backsub(const Dev& d, hipStream_t s, int pcg_iters, bool with_retract) {
   if (d.cam_lds_bytes > 0 && d.lds_blocks > 0) {
-    launch(k_backsub_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s, d.cam_lds_bytes, d, pcg_iters,
-           with_retract ? 1 : 0);
+    launch(d.lds_split ? k_backsub_lds<1> : k_backsub_lds<0>, dim3(d.lds_blocks), dim3(kLdsBlock), s,
+           d.cam_lds_bytes, d, pcg_iters, with_retract ? 1 : 0);
     return;
   }
   // the back-substitution first: a timed launch times the first dispatch
@@ -2191,7 +2209,7 @@ void launch_retract(const Dev& d, hipStream_t s) {
 }
 void launch_cost(const Dev& d, const double* pts, const CamT* tab, const double* camq,
                  hipStream_t s, int step) {
-  if (d.cam_lds_bytes > 0 && d.lds_blocks > 0) {
+  if (d.cam_lds_bytes > 0 && d.lds_blocks > 0 && !d.lds_split) {
     launch(k_cost_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
            (uint32_t)(kGeoLdsStride * 8 * d.nc), d, pts, tab, camq);
     launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.lds_blocks, step);

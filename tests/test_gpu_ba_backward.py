@@ -15,6 +15,8 @@ import pytest
 import oracle
 from synthetic import ba_scene, heavy_camera_scene
 
+from test_gpu_ba_parity import CAMERA_TABLES, use_camera_table
+
 pytestmark = pytest.mark.gpu
 
 bamod = pytest.importorskip("nonlinear_least_squares_amd.ba")
@@ -121,12 +123,11 @@ def test_backward_device_arrays_match_host():
     assert np.array_equal(out_d.cpu().numpy(), out_h)
 
 
-@pytest.mark.parametrize("lds_cameras", [True, False])
-def test_backward_heavy_camera(lds_cameras, monkeypatch):
+@pytest.mark.parametrize("cameras", CAMERA_TABLES)
+def test_backward_heavy_camera(cameras, monkeypatch):
     """The per-observation products of a camera with about 3,200 observations
     in one point band run over several of its chunks (Huber loss, outliers)."""
-    if not lds_cameras:
-        monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
+    use_camera_table(cameras, monkeypatch)
     sc = heavy_camera_scene()
     G_c, G_p = _grads(sc, seed=14)
     gpu = bamod.Problem.from_scene(sc)

@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 from synthetic import ba_scene
-from test_gpu_ba_parity import _edge_scene
+from test_gpu_ba_parity import CAMERA_TABLES, _edge_scene, use_camera_table
 
 pytestmark = pytest.mark.gpu
 
@@ -121,12 +121,11 @@ def test_dogleg_edge_scene(solver):
     np.testing.assert_array_equal(cams[9], sc["cams"][9])
 
 
-@pytest.mark.parametrize("lds_cameras", [True, False])
-def test_dogleg_heavy_camera(lds_cameras, monkeypatch):
+@pytest.mark.parametrize("cameras", CAMERA_TABLES)
+def test_dogleg_heavy_camera(cameras, monkeypatch):
     """A camera with about 3,200 observations in one point band: the model
     sums over the observations run over several chunks of that camera."""
-    if not lds_cameras:
-        monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
+    use_camera_table(cameras, monkeypatch)
     from synthetic import heavy_camera_scene
     sc = heavy_camera_scene()
     gpu = bamod.Problem.from_scene(sc, strategy=bamod.BA_STRATEGY_DOGLEG)

@@ -94,6 +94,22 @@ def traces_agree(g_tr, o_tr, cost_tol=1e-6):
     return True
 
 
+# Camera-table layouts of the point passes, chosen at creation by size; the
+# environment switches select the other two on scenes that would not get them.
+CAMERA_TABLES = ["lds", "split", "memory"]
+
+
+def use_camera_table(kind, monkeypatch):
+    """For handles created next: whole camera rows in LDS (the default up to
+    1,077 cameras), the split layout (only the cameras' 9-vectors in LDS, the
+    geometry read from memory; chosen by size up to 2,240 cameras), or the
+    camera table read from memory by every pass."""
+    if kind == "split":
+        monkeypatch.setenv("BA_SPLIT_LDS_CAMERAS", "1")
+    elif kind == "memory":
+        monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
+
+
 def make_pair(sc, **kw):
     gpu = bamod.Problem.from_scene(sc, **kw)
     orc = oracle.Problem.from_scene(sc, **kw)
@@ -152,12 +168,11 @@ def test_schur_parity(scene, lam):
 
 
 @pytest.mark.parametrize("config", ["tiny", "small"])
-@pytest.mark.parametrize("lds_cameras", [True, False])
-def test_pcg_and_update_parity(config, lds_cameras, monkeypatch):
-    # the camera table of these scenes fits in LDS; the environment switch,
-    # read when the handle is created, selects the global-table kernels
-    if not lds_cameras:
-        monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
+@pytest.mark.parametrize("cameras", CAMERA_TABLES)
+def test_pcg_and_update_parity(config, cameras, monkeypatch):
+    # the camera table of these scenes fits in LDS; the environment switches,
+    # read when the handle is created, select the other layouts
+    use_camera_table(cameras, monkeypatch)
     sc = ba_scene(config)
     gpu, orc = make_pair(sc)
     gpu.debug_run(bamod.BA_STAGE_UPDATE)
@@ -326,15 +341,15 @@ def _max_band_segment(sc, bands=4):
     return int(np.bincount(key).max())
 
 
-@pytest.mark.parametrize("lds_cameras", [True, False])
-def test_heavy_camera_multi_chunk_parity(lds_cameras, monkeypatch):
+@pytest.mark.parametrize("cameras", CAMERA_TABLES)
+def test_heavy_camera_multi_chunk_parity(cameras, monkeypatch):
     """One camera with about 3,200 observations in one point band: its
     camera-order segment is split into several chunks, whose partials the
     per-camera kernels (B and g_c, rhs and S_jj, the PCG's camera side) add in
-    chunk order.  Both kernel families: the camera table in LDS and, by the
-    environment switch read at creation, in global memory."""
-    if not lds_cameras:
-        monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
+    chunk order.  All three camera-table layouts (whole rows in LDS, the split
+    layout, the table in memory), selected by the environment switches read
+    at creation."""
+    use_camera_table(cameras, monkeypatch)
     sc = heavy_camera_scene()
     assert _max_band_segment(sc) > 2048
     gpu, orc = make_pair(sc)

@@ -1,8 +1,12 @@
 """Parity on the wide scene (1,500 ring cameras, 90,000 points, about 495,000
-observations, Huber loss): more cameras than the point passes can keep in one
-compute unit's LDS, so the library chooses the kernels that read the camera
-table from global memory (the tile point pass, a separate stop test, the q and
-update kernels) by size, with no switch.
+observations, Huber loss): more cameras than whole camera rows fit in one
+compute unit's LDS, so the library chooses by size, with no switch, the split
+layout: the PCG and back-substitution point passes keep only the cameras'
+9-vectors in LDS and read the geometry from memory, and the linearisation and
+cost passes read the camera table from memory.  The kernels that read every
+camera datum from memory (the tile point pass, a separate stop test, the q and
+update kernels), chosen by size past 2,240 cameras, run here under the
+environment switch.
 
 Bars as for the other scenes: every block of the linearisation within 1e-10,
 the blocks built from inverted point blocks within their first-order bound,
@@ -15,7 +19,8 @@ import pytest
 import oracle
 from synthetic import ba_scene
 
-from test_gpu_ba_parity import blocks_close, inverse_bounds, residual_bounds, traces_agree
+from test_gpu_ba_parity import (blocks_close, inverse_bounds, residual_bounds, traces_agree,
+                                use_camera_table)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,13 +32,19 @@ def wide():
     return ba_scene("wide")
 
 
-def test_wide_scene_selects_global_table_kernels(wide):
-    assert len(wide["cams"]) > 1077
+def test_wide_scene_selects_split_layout(wide, monkeypatch):
+    assert 1077 < len(wide["cams"]) <= 2240
     g = bamod.Problem.from_scene(wide)
     g.profile()
     g.debug_run(bamod.BA_STAGE_PCG)
     prof = g.profile_get()
-    # the separate p, q kernel runs only when the camera table is not in LDS
+    # the separate q kernel runs only when no camera data is in LDS
+    assert prof["pcg_q"][0] == 0 and prof["pcg_xr"][0] > 0 and prof["pcg_pt"][0] > 0
+    use_camera_table("memory", monkeypatch)
+    g = bamod.Problem.from_scene(wide)
+    g.profile()
+    g.debug_run(bamod.BA_STAGE_PCG)
+    prof = g.profile_get()
     assert prof["pcg_q"][0] > 0 and prof["pcg_pt"][0] > 0
 
 
@@ -55,7 +66,9 @@ def test_wide_linearisation_and_schur(wide):
         blocks_close(name, g.debug_get(name), o.get(name), tols[name])
 
 
-def test_wide_pcg_and_backsubstitution(wide):
+@pytest.mark.parametrize("cameras", ["split", "memory"])
+def test_wide_pcg_and_backsubstitution(wide, cameras, monkeypatch):
+    use_camera_table(cameras, monkeypatch)
     sc = wide
     g = bamod.Problem.from_scene(sc)
     o = oracle.Problem.from_scene(sc)
@@ -77,7 +90,9 @@ def test_wide_pcg_and_backsubstitution(wide):
     assert abs(trial - ref) <= 1e-8 * ref
 
 
-def test_wide_three_lm_steps(wide):
+@pytest.mark.parametrize("cameras", ["split", "memory"])
+def test_wide_three_lm_steps(wide, cameras, monkeypatch):
+    use_camera_table(cameras, monkeypatch)
     sc = wide
     g = bamod.Problem.from_scene(sc)
     o = oracle.Problem.from_scene(sc)
