@@ -168,10 +168,11 @@ int ba_options_default(ba_options* o);
  * 2,240 cameras only the 9-vectors of the PCG and back-substitution passes,
  * with the geometry read from memory (the linearisation and cost passes then
  * read memory too); past that every pass reads the camera table from memory.
- * The first two layouts give the same bits.  The environment variables
- * BA_NO_LDS_CAMERAS=1 (memory) and BA_SPLIT_LDS_CAMERAS=1 (the 9-vectors
- * only, where they fit) at creation select another layout; the memory
- * layout's results differ from the others only by rounding. */
+ * The environment variables BA_NO_LDS_CAMERAS=1 (memory) and
+ * BA_SPLIT_LDS_CAMERAS=1 (the 9-vectors only, where they fit) at creation
+ * select another layout.  Results differ between layouts only by rounding
+ * (the sums over observations are taken in different orders); each layout
+ * reproduces its own bits run to run. */
 int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t n_pts,
               const int32_t* obs_cam_idx, const int32_t* obs_pt_idx, const double* obs_uv,
               int64_t n_obs, const ba_options* opts, ba_problem** out);
