@@ -163,15 +163,12 @@ int ba_options_default(ba_options* o);
  * CSR offsets and work partitions, allocates the whole arena and evaluates
  * the initial cost.  The caller may free its inputs when this returns.
  * opts may be NULL (defaults).  On error *out is left NULL.
- * The point passes keep camera data in each compute unit's LDS by size: up
- * to 1,077 cameras the whole rows (geometry and the PCG's 9-vector), up to
- * 2,240 cameras only the 9-vectors of the PCG and back-substitution passes,
- * with the geometry read from memory (the linearisation and cost passes then
- * read memory too); past that every pass reads the camera table from memory.
- * The environment variables BA_NO_LDS_CAMERAS=1 (memory) and
- * BA_SPLIT_LDS_CAMERAS=1 (the 9-vectors only, where they fit) at creation
- * select another layout.  Results differ between layouts only by rounding
- * (the sums over observations are taken in different orders); each layout
+ * Up to 1,077 cameras the point passes keep whole camera rows (geometry and
+ * the PCG's 9-vector) in each compute unit's LDS; past that they read the
+ * camera table and vectors from memory.  The environment variable
+ * BA_NO_LDS_CAMERAS=1 at creation selects the memory layout for any size.
+ * Results differ between the layouts only by rounding (the linearisation and
+ * cost sums over observations are taken in different orders); each layout
  * reproduces its own bits run to run. */
 int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t n_pts,
               const int32_t* obs_cam_idx, const int32_t* obs_pt_idx, const double* obs_uv,
@@ -345,13 +342,13 @@ enum {
                         runs in the BA_K_PRECOND launch)                            */
   BA_K_PCG_PT,       /* PCG point pass: stop test, C~^-1 E^T z                      */
   BA_K_PCG_CAM,      /* PCG camera pass: chunk partials of E C~^-1 E^T z            */
-  BA_K_PCG_Q,        /* PCG p, q = S p by recurrence, p.q partials (no launches
-                        when the camera table fits in LDS: BA_K_PCG_XR does it)     */
-  BA_K_PCG_XR,       /* PCG update of x, r, z (with the camera table in LDS, one
-                        kernel that also forms p, q and p.q)                        */
+  BA_K_PCG_Q,        /* PCG p, q = S p, p.q: no launches of its own (the
+                        BA_K_PCG_XR launch forms them by recurrence); kept so that
+                        the ids after it keep their values                        */
+  BA_K_PCG_XR,       /* PCG update of x, r, z, with p, q and p.q                   */
   BA_K_BACKSUB,      /* point back-substitution and trial points                   */
-  BA_K_RETRACT,      /* trial cameras (no launches of its own in an LM step when the
-                        camera table fits in LDS: BA_K_BACKSUB forms them)          */
+  BA_K_RETRACT,      /* trial cameras (no launches of its own in an LM step:
+                        BA_K_BACKSUB forms them; the dogleg launches it)           */
   BA_K_COST,         /* trial cost                                                 */
   BA_K_DS_RUNS,      /* dense solver: F = Ebar chol(C~^-1) per (point, camera) run  */
   BA_K_DS_FILL,      /* dense solver: S cleared, padding, rhs row                  */

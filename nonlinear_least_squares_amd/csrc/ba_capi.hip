@@ -86,7 +86,7 @@ struct ba_problem {
   ba_options opt{};
   hipStream_t stream = nullptr;
   int n_tiles = 0, n_chunks = 0, n_cost_blocks = 0, lds_blocks = 0,
-      cam_lds_bytes = 0, lds_split = 0, n_chunk_blocks = 0;
+      cam_lds_bytes = 0, cam_layout = 0, n_chunk_blocks = 0;
   Arena arena;   // everything sized by n_cams, n_pts, n_obs
   Arena arena2;  // partitions and partial sums, sized after the CSR offsets
   Arena arena3;  // dense solver: runs, block pair lists, S
@@ -174,7 +174,7 @@ Dev make_dev(const ba_problem* h) {
   d.blk_chunk = h->blk_chunk;
   d.lds_blocks = h->lds_blocks;
   d.cam_lds_bytes = h->cam_lds_bytes;
-  d.lds_split = h->lds_split;
+  d.cam_layout = h->cam_layout;
   d.wave_begin = h->wave_begin;
   d.n_cost_blocks = h->n_cost_blocks;
   d.loss = h->opt.loss;
@@ -379,12 +379,7 @@ int stage_pcg(ba_problem* h, bool defer_final) {
     for (int k = 0; k < n; ++k, ++next_it) {
       TIMED(BA_K_PCG_PT, next_it, launch_pcg_pt(d, next_it, h->stream));
       TIMED(BA_K_PCG_CAM, next_it, launch_pcg_cam(d, h->stream));
-      if (pcg_fused_step(d)) {
-        TIMED(BA_K_PCG_XR, next_it, launch_pcg_step(d, next_it, h->stream));
-      } else {
-        TIMED(BA_K_PCG_Q, next_it, launch_pcg_q(d, next_it, h->stream));
-        TIMED(BA_K_PCG_XR, next_it, launch_pcg_xr(d, next_it, h->stream));
-      }
+      TIMED(BA_K_PCG_XR, next_it, launch_pcg_step(d, next_it, h->stream));
     }
     return BA_OK;
   };
@@ -806,36 +801,29 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   // The kernels that keep the camera table in LDS run one block per compute
   // unit; each wavefront takes an equal share of the observations, moved to
   // the nearest point start at or after the even split.
-  // Up to kCamLdsMaxCams cameras their whole rows go to LDS; up to
-  // kZLdsMaxCams only their 9-vectors (the split layout); past that every
-  // pass reads the camera table from memory.  BA_NO_LDS_CAMERAS=1 at creation
-  // selects the memory-table kernels, BA_SPLIT_LDS_CAMERAS=1 the split layout
-  // when it fits (for the tests of those paths on small scenes).
+  // The point passes' camera data: up to kCamLdsMaxCams cameras whole rows
+  // in LDS, past that read from memory.  BA_NO_LDS_CAMERAS=1 at creation
+  // selects the memory layout (for its tests on small scenes).
   std::vector<int32_t> wave_begin;
   {
     int dev = 0, cus = 0;
     TRY(hipGetDevice(&dev));
     TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     h->cam_lds_bytes = 0;
-    h->lds_split = 0;
+    h->cam_layout = kCamMemory;
     h->lds_blocks = 0;
     const char* off = std::getenv("BA_NO_LDS_CAMERAS");
-    const char* spl = std::getenv("BA_SPLIT_LDS_CAMERAS");
-    int64_t bytes = 0;
-    if (N > 0 && !(off && off[0] == '1')) {
-      if (nc <= kCamLdsMaxCams && !(spl && spl[0] == '1')) {
-        bytes = (int64_t)kCamLdsStride * 8 * nc;
-      } else if (nc <= kZLdsMaxCams) {
-        bytes = (int64_t)kZLdsStride * 8 * nc;
-        h->lds_split = 1;
-      }
+    if (!(off && off[0] == '1') && nc <= kCamLdsMaxCams) {
+      h->cam_layout = kCamRows;
+      h->cam_lds_bytes = (int)(kCamLdsStride * 8 * nc);
     }
-    if (bytes > 0) {
-      TRY(set_lds_camera_limit((int)bytes));
-      h->cam_lds_bytes = (int)bytes;
+    if (h->cam_lds_bytes > 0) TRY(set_lds_camera_limit(h->cam_lds_bytes));
+    {
+      // with no observations one block of empty ranges still makes the
+      // PCG's stop test and per-block partials
       constexpr int wpb = kLdsBlock / kWave;
       const int64_t want = (N + (int64_t)wpb * kWave - 1) / ((int64_t)wpb * kWave);
-      h->lds_blocks = (int)std::min<int64_t>(std::max(cus, 1), want);
+      h->lds_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(cus, 1), want));
       const int64_t W = (int64_t)h->lds_blocks * wpb;
       wave_begin.resize(W + 1);
       for (int64_t w = 0; w <= W; ++w) {
@@ -898,7 +886,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   P.add(h->cost_part, (int64_t)std::max(h->n_cost_blocks, 1));
   P.add(h->red_part, 8 * (int64_t)pcg_red_blocks(nc) + 2);
   P.add(h->pt_dot, (int64_t)std::max(h->lds_blocks, 1));
-  P.add(h->cam_rows, h->cam_lds_bytes > 0 && !h->lds_split ? (int64_t)kCamLdsFill * kLdsBlock : 1);
+  P.add(h->cam_rows, h->cam_layout == kCamRows ? (int64_t)kCamLdsFill * kLdsBlock : 1);
   P.add(h->dl_vpart, 3 * (int64_t)dl_vec_blocks(nc, h->np));
   P.add(h->dl_opart, 3 * (int64_t)std::max(h->n_chunk_blocks, 1));
   P.add(h->dl_out, 6);

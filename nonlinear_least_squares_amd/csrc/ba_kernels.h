@@ -31,11 +31,9 @@ constexpr int kCamLdsStride = 19; // doubles per camera in the LDS table: q (4),
 constexpr int kCamLdsFill = 20;   // table elements per thread in the copy (>= 19 * max cameras / kLdsBlock)
 constexpr int kCamLdsMaxCams = kCamLdsFill * 1024 / kCamLdsStride;   // 1,077
 constexpr int kCostLdsFill = (10 * kCamLdsMaxCams + 1023) / 1024;   // geometry elements per thread
-// Past kCamLdsMaxCams the PCG and back-substitution point passes keep only the
-// cameras' 9-vectors in LDS (stride 9) and read the geometry from the camera
-// table in memory; the linearisation and cost passes then read memory too.
-constexpr int kZLdsStride = 9;
-constexpr int kZLdsMaxCams = 2240;   // 9 * 2240 <= kCamLdsFill * kLdsBlock, 161 KB of LDS
+// Where the PCG and back-substitution point passes find the camera data.
+constexpr int kCamRows = 0;      // whole rows in LDS (up to kCamLdsMaxCams cameras)
+constexpr int kCamMemory = 1;    // the camera table and vectors in memory (any number)
 constexpr int kChunkLoads = 8;   // a camera's chunk partials loaded together in the per-camera sums
 constexpr int kChunk = 1024;      // observations per camera chunk (one wavefront)
 constexpr int kPointBands = 4;    // point-index bands of the camera chunks (block b: band b % 4,
@@ -140,7 +138,7 @@ struct Dev {
   double* pt_dot;    // per-block partials of z^T E C~^-1 E^T z from the LDS point pass
   double* cam_rows;  // LDS point pass, PCG: the camera table rows (kCamLdsStride doubles:
                      // q, t, f, k1, k2, z) padded to kCamLdsFill * kLdsBlock, copied as is
-  int lds_split;     // 1: the LDS point passes hold only the camera vectors (kZLdsStride)
+  int cam_layout;    // kCamRows or kCamMemory (the point passes' camera data)
   int red_nb;        // blocks of the camera-vector kernels
   long long* host_done;  // host-mapped, tagged with pcg_seq in the upper 32 bits: [0] the
                          // solve stopped (low bits: its iteration count), [1] the last
@@ -210,10 +208,7 @@ void launch_lin_final(const Dev& d, hipStream_t s);
 void launch_precond(const Dev& d, hipStream_t s, bool with_pcg_init = false);
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s);
 void launch_pcg_cam(const Dev& d, hipStream_t s);
-void launch_pcg_q(const Dev& d, int it, hipStream_t s);
-void launch_pcg_xr(const Dev& d, int it, hipStream_t s);
 // With the LDS point pass, k_pcg_step replaces k_pcg_q and k_pcg_xr.
-bool pcg_fused_step(const Dev& d);
 void launch_pcg_step(const Dev& d, int it, hipStream_t s);
 void launch_pcg_final(const Dev& d, int iters, hipStream_t s);
 int pcg_red_blocks(int64_t nc);   // blocks of the camera-vector kernels

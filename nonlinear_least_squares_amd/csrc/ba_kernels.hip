@@ -636,67 +636,6 @@ __device__ __forceinline__ double block_sum(double v, double* s_buf) {
   return s_out[0];
 }
 
-// Point side of S p: z_i = C~_i^-1 sum_{k in i} w Jp^T (Jc p_cam(k)), stored in
-// the point record (MODE 0).  MODE 1
-// (back-substitution): dp_i = C~_i^-1 (-g_p,i - sum_k w Jp^T (Jc dc_cam(k))) and
-// the trial point.
-template <int MODE>
-struct PcgPtOp {
-  const Dev& d;
-  double ci[6];          // C~^-1 of this thread's point, loaded with the point
-  double gq[3];          // g_p of this thread's point (back-substitution)
-  __device__ void compute(int s, int pt, double* v) {
-    const int j = d.o_cam[s];
-    // everything that depends only on the point is loaded up front, so that
-    // finish() has no load of its own on the critical path
-    const double* Ci = d.Cinv + 6 * (int64_t)pt;
-#pragma unroll
-    for (int k = 0; k < 6; ++k) ci[k] = Ci[k];
-    if (MODE == 1) {
-      gq[0] = d.gp[3 * pt];
-      gq[1] = d.gp[3 * pt + 1];
-      gq[2] = d.gp[3 * pt + 2];
-    }
-    CamG c;
-    load_cam(d.tab, j, c);
-    const double* xc = (MODE == 0 ? d.zc : d.x) + 9 * (int64_t)j;
-    Geo g;
-    geo_eval(c, d.pts[3 * pt], d.pts[3 * pt + 1], d.pts[3 * pt + 2], g);
-    double u0, u1;
-    jc_apply(g, c.f, xc, u0, u1);
-    const double w = d.w_pt[s];
-    jpt_apply(g, c.R, w * u0, w * u1, v[0], v[1], v[2]);
-  }
-  __device__ void finish(int pt, const double* v) {
-    double y0 = v[0], y1 = v[1], y2 = v[2];
-    if (MODE == 1) {
-      y0 = -gq[0] - y0;
-      y1 = -gq[1] - y1;
-      y2 = -gq[2] - y2;
-    }
-    const double z0 = ci[0] * y0 + ci[1] * y1 + ci[2] * y2;
-    const double z1 = ci[1] * y0 + ci[3] * y1 + ci[4] * y2;
-    const double z2 = ci[2] * y0 + ci[4] * y1 + ci[5] * y2;
-    if (MODE == 0) {
-      d.prec[8 * (int64_t)pt + 3] = z0;
-      d.prec[8 * (int64_t)pt + 4] = z1;
-      d.prec[8 * (int64_t)pt + 5] = z2;
-    } else {
-      d.dp[3 * pt] = z0;
-      d.dp[3 * pt + 1] = z1;
-      d.dp[3 * pt + 2] = z2;
-      d.pts_trial[3 * pt] = d.pts[3 * pt] + z0;
-      d.pts_trial[3 * pt + 1] = d.pts[3 * pt + 1] + z1;
-      d.pts_trial[3 * pt + 2] = d.pts[3 * pt + 2] + z2;
-    }
-  }
-};
-
-__global__ __launch_bounds__(kTile) void k_backsub(Dev d) {
-  PcgPtOp<1> op{d, {}, {}};
-  point_tile_reduce<3>(d, op, blockIdx.x);
-}
-
 // z_j = M_j^-1 r_j with the packed Cholesky factor of S_jj.
 // Camera vectors in the persistent solve are handled 7 cameras per wavefront,
 // 9 lanes per camera (lane 63 idle), so every load and store is coalesced.
@@ -985,7 +924,7 @@ __global__ __launch_bounds__(64) void k_precond(Dev d, int with_init) {
     rr = r * r;
     rz = r * z;
     zbz = z * bz;
-    if (d.cam_lds_bytes > 0 && !d.lds_split) {
+    if (d.cam_layout == kCamRows) {
       // the LDS point pass's camera rows: q (4), t, f, k1, k2 (lane a holds
       // element a, lane 0 also element 9), then z
       double* row = d.cam_rows + kCamLdsStride * j;
@@ -1037,26 +976,6 @@ __device__ __forceinline__ bool pcg_stop_test(const Dev& d, int it, double rhs2,
   return stop;
 }
 
-// The stop test on its own, ahead of the tile-parallel point pass (the LDS
-// point pass makes it in each block itself).
-__global__ __launch_bounds__(kWave) void k_pcg_stop(Dev d, int it) {
-  int done = d.pcg->done;
-  const double* const arr[2] = {red_rhs(d), red_rr(d, it & 1)};
-  double part[2];
-  lane_partials<2>(arr, d.red_nb, part);
-  pin(part[0]);
-  pin(part[1]);
-  pin(done);
-  if (done) return;
-  (void)pcg_stop_test(d, it, part[0], part[1], true);
-}
-
-__global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d) {
-  if (d.pcg->done) return;
-  PcgPtOp<0> op{d, {}, {}};
-  point_tile_reduce<3>(d, op, blockIdx.x);
-}
-
 // The same passes with the camera table resident in LDS.  One persistent
 // block of kLdsBlock threads per compute unit copies the table once
 // (kCamLdsStride doubles per camera, an odd number of dword pairs so that
@@ -1071,12 +990,15 @@ __global__ __launch_bounds__(kTile) void k_pcg_pt(Dev d) {
 //   MODE 0: u = C~^-1 (E^T z) into the point records (PCG), after the
 //           iteration's stop test, which wavefront 0 of each block makes;
 //   MODE 1: dp = C~^-1 (-g_p - E^T dc) and the trial points (back-substitution).
-// SPLIT: the LDS rows hold only the cameras' 9-vectors (kZLdsStride), and each
-// observation reads its camera's geometry (R, t, f, k1, k2) from the camera
-// table in memory: the layout for more cameras than whole rows fit.  R in that
-// table was formed from the same quaternion by the same function, so both
-// layouts compute with the same bits.
-template <int MODE, int SPLIT>
+// LAYOUT (where the pass finds each observation's camera data):
+//   kCamRows:   whole camera rows in LDS (geometry as a quaternion, and the
+//               9-vector), copied per launch;
+//   kCamMemory: no LDS table: the geometry (R, t, f, k1, k2) from the camera
+//               table and the 9-vector read per observation from memory, for
+//               more cameras than whole rows fit.
+// R in the camera table was formed from the same quaternion by the same
+// function, so both layouts compute with the same bits.
+template <int MODE, int LAYOUT>
 __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   extern __shared__ double s_cam[];
   __shared__ int s_prog;
@@ -1110,15 +1032,12 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   // the test; its outcome reaches the other wavefronts through LDS at the
   // barrier before the loop.
   {
-    const int ne = (SPLIT ? kZLdsStride : kCamLdsStride) * (int)d.nc;
+    const int ne = kCamLdsStride * (int)d.nc;
     const double* tabd = reinterpret_cast<const double*>(d.tab);
     int done = MODE == 0 ? d.pcg->done : 0;
     double t[kCamLdsFill];
-    if (SPLIT) {
-      // the vectors are stored nine per camera in memory already
-      const double* src = MODE == 0 ? d.zc : d.x;
-#pragma unroll
-      for (int u = 0; u < kCamLdsFill; ++u) t[u] = src[min((int)threadIdx.x + u * kLdsBlock, ne - 1)];
+    if (LAYOUT == kCamMemory) {
+      // no table
     } else if (MODE == 0) {
       // the PCG keeps the rows in this layout in memory (padded to the whole copy)
 #pragma unroll
@@ -1140,10 +1059,12 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
       lane_partials<2>(arr, d.red_nb, part);
     }
     if (done) return;
+    if (LAYOUT != kCamMemory) {
 #pragma unroll
-    for (int u = 0; u < kCamLdsFill; ++u) {
-      const int e = (int)threadIdx.x + u * kLdsBlock;
-      if (e < ne) s_cam[e] = t[u];
+      for (int u = 0; u < kCamLdsFill; ++u) {
+        const int e = (int)threadIdx.x + u * kLdsBlock;
+        if (e < ne) s_cam[e] = t[u];
+      }
     }
     if (tester) {
       const bool stop = pcg_stop_test(d, it, part[0], part[1], blockIdx.x == 0);
@@ -1180,10 +1101,10 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     // unconditionally (indices clamped into range, results of idle lanes
     // dropped), so the loads in flight are the same on every path and each
     // wait, by count in issue order, covers only what is needed by then.
-    // split layout: the camera's geometry first, so that its latency runs
+    // memory layout: the camera's geometry first, so that its latency runs
     // under the issue of the loads after it
     CamG c;
-    if (SPLIT) load_cam(d.tab, cj, c);
+    if (LAYOUT == kCamMemory) load_cam(d.tab, cj, c);
     double ci[6];
     const double* Ci = d.Cinv + 6 * (int64_t)cpt_c;
 #pragma unroll
@@ -1203,8 +1124,8 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     const double nw = d.w_pt[min(s + kWave, last)];
     __builtin_amdgcn_sched_barrier(0);
     double xv[9];
-    if (SPLIT) {
-      const double* r = s_cam + kZLdsStride * cj;
+    if (LAYOUT == kCamMemory) {
+      const double* r = xbase + 9 * (int64_t)cj;
 #pragma unroll
       for (int k = 0; k < 9; ++k) xv[k] = r[k];
     } else {
@@ -1323,9 +1244,9 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   }
 }
 
-template <int SPLIT>
+template <int LAYOUT>
 __global__ __launch_bounds__(kLdsBlock) void k_pcg_pt_lds(Dev d, int it) {
-  pcg_pt_lds_body<0, SPLIT>(d, it);
+  pcg_pt_lds_body<0, LAYOUT>(d, it);
 }
 
 
@@ -1430,116 +1351,8 @@ __device__ __forceinline__ double minus_chunk_partials(const Dev& d, int c0, int
   return sz;
 }
 
-__global__ __launch_bounds__(kWave) void k_pcg_q(Dev d, int it) {
-  const CamLane c = cam_lane(blockIdx.x, d.nc);
-  const int64_t e = 9 * c.j + c.a;
-  const double* z = d.zc + 9 * c.j;
-  const double* Bd = d.Bd + 45 * c.j;
-  int done = d.pcg->done;
-  int c0 = d.cam_chunk_ptr[c.j], c1 = d.cam_chunk_ptr[c.j + 1];
-  double bd[9], zv[9];
-#pragma unroll
-  for (int b = 0; b < 9; ++b) {
-    bd[b] = Bd[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)];
-    zv[b] = z[b];
-  }
-  double ze = z[c.a], pe = d.pbuf[e], qe = d.q[e];   // p and q of it - 1 (unused at it = 0)
-  const double* const arr[2] = {red_rz(d, it & 1), red_rz(d, (it + 1) & 1)};
-  double part[2];
-  lane_partials<2>(arr, d.red_nb, part);
-#pragma unroll
-  for (int b = 0; b < 9; ++b) {
-    pin(bd[b]);
-    pin(zv[b]);
-  }
-  pin(ze);
-  pin(pe);
-  pin(qe);
-  pin(part[0]);
-  pin(part[1]);
-  pin(c0);
-  pin(c1);
-  pin(done);
-  if (done) return;
-  double sz = 0.0;
-#pragma unroll
-  for (int b = 0; b < 9; ++b) sz += bd[b] * zv[b];
-  sz = minus_chunk_partials(d, c0, c1, c.a, sz);
-  double pn = ze, qn = sz;
-  if (it > 0) {
-    const double beta = wave_sum(part[0]) / wave_sum(part[1]);
-    pn = ze + beta * pe;
-    qn = sz + beta * qe;
-  }
-  double pq = 0.0;
-  if (c.on) {
-    d.pbuf[e] = pn;
-    d.q[e] = qn;
-    pq = pn * qn;
-  }
-  pq = wave_sum(pq);
-  if (threadIdx.x == 0) red_pq(d)[blockIdx.x] = pq;
-}
-
-__global__ __launch_bounds__(kWave) void k_pcg_xr(Dev d, int it) {
-  const CamLane c = cam_lane(blockIdx.x, d.nc);
-  const int64_t e = 9 * c.j + c.a;
-  int done = d.pcg->done;
-  double pe = d.pbuf[e];
-  double xe = d.x[e], re = d.r[e], qe = d.q[e];
-  const double* Mi = d.Minv + 45 * c.j;
-  double m[9];
-#pragma unroll
-  for (int b = 0; b < 9; ++b) m[b] = Mi[c.a <= b ? sym_idx(9, c.a, b) : sym_idx(9, b, c.a)];
-  const double* const arr[2] = {red_pq(d), red_rz(d, it & 1)};
-  double part[2];
-  lane_partials<2>(arr, d.red_nb, part);
-  double pq = part[0], rz = part[1];
-  pin(pq);
-  pin(rz);
-  pin(pe);
-  pin(xe);
-  pin(re);
-  pin(qe);
-#pragma unroll
-  for (int b = 0; b < 9; ++b) pin(m[b]);
-  pin(done);
-  if (done) return;
-  pq = wave_sum(pq);
-  if (!(pq > 0.0) || !isfinite(pq)) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      const double rhs_norm = sqrt(block_sum_array_serial(red_rhs(d), d.red_nb));
-      const double res = it == 0 ? rhs_norm : sqrt(block_sum_array_serial(red_rr(d, it & 1), d.red_nb));
-      stop_pcg(d, it, res, rhs_norm, 1);
-    }
-    return;
-  }
-  const double alpha = wave_sum(rz) / pq;
-  double r = 0.0;
-  if (c.on) {
-    d.x[e] = xe + alpha * pe;
-    r = re - alpha * qe;
-    d.r[e] = r;
-  }
-  double z = 0.0;
-#pragma unroll
-  for (int b = 0; b < 9; ++b) z += m[b] * __shfl(r, c.base + b, kWave);
-  double rr = 0.0, rzn = 0.0;
-  if (c.on) {
-    d.zc[e] = z;
-    rr = r * r;
-    rzn = r * z;
-  }
-  rr = wave_sum(rr);
-  rzn = wave_sum(rzn);
-  if (threadIdx.x == 0) {
-    red_rr(d, (it + 1) & 1)[blockIdx.x] = rr;
-    red_rz(d, (it + 1) & 1)[blockIdx.x] = rzn;
-  }
-}
-
-// q, p.q and the update in one launch (used with the LDS point pass, which
-// leaves one partial of z^T E C~^-1 E^T z per block).  p.q needs no sum over
+// q, p.q and the update in one launch (the point pass leaves one partial of
+// z^T E C~^-1 E^T z per block).  p.q needs no sum over
 // the new q: with p = z + beta p_prev and the directions S-conjugate,
 // p^T S p = z^T S z - beta^2 p_prev^T S p_prev (the recurrence of Chronopoulos
 // and Gear), and z^T S z = z^T B~ z - z^T E C~^-1 E^T z comes from partials
@@ -1625,7 +1438,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_step(Dev d, int it) {
   double rr = 0.0, rzn = 0.0, zbz = 0.0;
   if (c.on) {
     d.zc[e] = zn;
-    if (!d.lds_split) d.cam_rows[kCamLdsStride * c.j + 10 + c.a] = zn;
+    if (d.cam_layout == kCamRows) d.cam_rows[kCamLdsStride * c.j + 10 + c.a] = zn;
     rr = r * r;
     rzn = r * zn;
     zbz = zn * bz;
@@ -1723,9 +1536,9 @@ __global__ void k_retract(Dev d) {
 // (lane k) when `with_retract` is set (k_retract's work), and wavefront 0 of
 // block 0 records a PCG solve that ran to its cap of `pcg_iters` iterations
 // when pcg_iters >= 0 (k_pcg_final's work): neither depends on the points.
-template <int SPLIT>
+template <int LAYOUT>
 __global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d, int pcg_iters, int with_retract) {
-  pcg_pt_lds_body<1, SPLIT>(d, 0);
+  pcg_pt_lds_body<1, LAYOUT>(d, 0);
   if (threadIdx.x >= kWave) return;
   if (pcg_iters >= 0 && blockIdx.x == 0) pcg_final_wave(d, pcg_iters);
   if (with_retract)
@@ -2105,8 +1918,8 @@ DispatchEvents& dispatch_events() {
 hipError_t set_lds_camera_limit(int bytes) {
   const void* const kernels[] = {
       reinterpret_cast<const void*>(&k_lin_pt_lds),     reinterpret_cast<const void*>(&k_cost_lds),
-      reinterpret_cast<const void*>(&k_pcg_pt_lds<0>),  reinterpret_cast<const void*>(&k_pcg_pt_lds<1>),
-      reinterpret_cast<const void*>(&k_backsub_lds<0>), reinterpret_cast<const void*>(&k_backsub_lds<1>)};
+      reinterpret_cast<const void*>(&k_pcg_pt_lds<kCamRows>),
+      reinterpret_cast<const void*>(&k_backsub_lds<kCamRows>)};
   for (const void* k : kernels) {
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
@@ -2139,10 +1952,9 @@ void launch_cam_prep(const double* cams, CamT* tab, double* camq, int64_t nc, hi
   if (nc > 0) launch(k_cam_prep, dim3(blocks_for(nc, 256)), dim3(256), s, 0u, cams, tab, camq, nc);
 }
 void launch_lin_pt(const Dev& d, hipStream_t s) {
-  if (d.cam_lds_bytes > 0 && !d.lds_split) {
-    if (d.lds_blocks > 0)
-      launch(k_lin_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
-             (uint32_t)(kGeoLdsStride * 8 * d.nc), d);
+  if (d.cam_layout == kCamRows) {
+    launch(k_lin_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
+           (uint32_t)(kGeoLdsStride * 8 * d.nc), d);
   } else if (d.n_tiles > 0) {
     launch(k_lin_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
   }
@@ -2167,25 +1979,12 @@ void launch_precond(const Dev& d, hipStream_t s, bool with_pcg_init) {
            with_pcg_init ? 1 : 0);
 }
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
-  if (pcg_fused_step(d)) {
-    launch(d.lds_split ? k_pcg_pt_lds<1> : k_pcg_pt_lds<0>, dim3(d.lds_blocks), dim3(kLdsBlock), s,
-           d.cam_lds_bytes, d, it);
-    return;
-  }
-  launch(k_pcg_stop, dim3(1), dim3(kWave), s, 0u, d, it);
-  if (d.cam_lds_bytes == 0 && d.n_tiles > 0)
-    launch(k_pcg_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
+  void (*k)(Dev, int) = d.cam_layout == kCamRows ? k_pcg_pt_lds<kCamRows> : k_pcg_pt_lds<kCamMemory>;
+  launch(k, dim3(d.lds_blocks), dim3(kLdsBlock), s, (uint32_t)d.cam_lds_bytes, d, it);
 }
 void launch_pcg_cam(const Dev& d, hipStream_t s) {
   if (d.n_chunk_blocks > 0) launch(k_pcg_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
 }
-void launch_pcg_q(const Dev& d, int it, hipStream_t s) {
-  launch(k_pcg_q, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
-}
-void launch_pcg_xr(const Dev& d, int it, hipStream_t s) {
-  launch(k_pcg_xr, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
-}
-bool pcg_fused_step(const Dev& d) { return d.cam_lds_bytes > 0 && d.lds_blocks > 0; }
 void launch_pcg_step(const Dev& d, int it, hipStream_t s) {
   launch(k_pcg_step, dim3(cam_vector_blocks(d.nc)), dim3(kWave), s, 0u, d, it);
 }
@@ -2194,22 +1993,17 @@ void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
 }
 int pcg_red_blocks(int64_t nc) { return cam_vector_blocks(nc); }
 void launch_backsub(const Dev& d, hipStream_t s, int pcg_iters, bool with_retract) {
-  if (d.cam_lds_bytes > 0 && d.lds_blocks > 0) {
-    launch(d.lds_split ? k_backsub_lds<1> : k_backsub_lds<0>, dim3(d.lds_blocks), dim3(kLdsBlock), s,
-           d.cam_lds_bytes, d, pcg_iters, with_retract ? 1 : 0);
-    return;
-  }
-  // the back-substitution first: a timed launch times the first dispatch
-  if (d.cam_lds_bytes == 0 && d.n_tiles > 0) launch(k_backsub, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
-  if (pcg_iters >= 0) launch_pcg_final(d, pcg_iters, s);
-  if (with_retract) launch_retract(d, s);
+  void (*k)(Dev, int, int) = d.cam_layout == kCamRows ? k_backsub_lds<kCamRows>
+                                                       : k_backsub_lds<kCamMemory>;
+  launch(k, dim3(d.lds_blocks), dim3(kLdsBlock), s, (uint32_t)d.cam_lds_bytes, d, pcg_iters,
+         with_retract ? 1 : 0);
 }
 void launch_retract(const Dev& d, hipStream_t s) {
   if (d.nc > 0) launch(k_retract, dim3(blocks_for(d.nc, 128)), dim3(128), s, 0u, d);
 }
 void launch_cost(const Dev& d, const double* pts, const CamT* tab, const double* camq,
                  hipStream_t s, int step) {
-  if (d.cam_lds_bytes > 0 && d.lds_blocks > 0 && !d.lds_split) {
+  if (d.cam_layout == kCamRows) {
     launch(k_cost_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
            (uint32_t)(kGeoLdsStride * 8 * d.nc), d, pts, tab, camq);
     launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.lds_blocks, step);

@@ -25,8 +25,6 @@ Configurations (sizes from the workload list of the task):
   outliers, Huber 2 px, 30 LM iterations.
 * ``wide``   : as ``large`` with 1,500 ring cameras and 90,000 points (about
   500,000 observations), 20 LM iterations.
-* ``widest`` : as ``large`` with 2,500 ring cameras and 30,000 points (about
-  165,000 observations), 5 LM iterations.
 
 ``heavy_camera_scene`` adds to a ring scene one camera that sees thousands of
 points of one contiguous index range (a camera far busier than the rest).
@@ -51,15 +49,10 @@ CONFIGS = {
                   outlier_frac=0.05, loss="huber", huber_delta=2.0, n_iters=30,
                   pcg_max_iters=50, pcg_rel_tol=1e-6),
     # more cameras than whole per-camera rows of the point passes fit in one
-    # compute unit's LDS (the library then keeps only the camera vectors there)
+    # compute unit's LDS (the library then reads the camera data from memory)
     "wide": dict(n_cams=1500, n_pts=90000, seed=6, layout="ring", tracks="powerlaw",
                  outlier_frac=0.05, loss="huber", huber_delta=2.0, n_iters=20,
                  pcg_max_iters=50, pcg_rel_tol=1e-6),
-    # more cameras than even the camera vectors fit in LDS (every pass then
-    # reads the camera table from memory)
-    "widest": dict(n_cams=2500, n_pts=30000, seed=7, layout="ring", tracks="powerlaw",
-                   outlier_frac=0.05, loss="huber", huber_delta=2.0, n_iters=5,
-                   pcg_max_iters=50, pcg_rel_tol=1e-6),
 }
 
 RING_RADIUS = 20.0      # ring cameras sit 20 units from the centre of the point box

@@ -94,19 +94,15 @@ def traces_agree(g_tr, o_tr, cost_tol=1e-6):
     return True
 
 
-# Camera-table layouts of the point passes, chosen at creation by size; the
-# environment switches select the other two on scenes that would not get them.
-CAMERA_TABLES = ["lds", "split", "memory"]
+# Camera layouts of the point passes, chosen at creation by size; the
+# environment switch selects the memory layout on scenes that would not get it.
+CAMERA_TABLES = ["lds", "memory"]
 
 
 def use_camera_table(kind, monkeypatch):
     """For handles created next: whole camera rows in LDS (the default up to
-    1,077 cameras), the split layout (only the cameras' 9-vectors in LDS, the
-    geometry read from memory; chosen by size up to 2,240 cameras), or the
-    camera table read from memory by every pass."""
-    if kind == "split":
-        monkeypatch.setenv("BA_SPLIT_LDS_CAMERAS", "1")
-    elif kind == "memory":
+    1,077 cameras) or the camera table and vectors read from memory."""
+    if kind == "memory":
         monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
 
 
@@ -170,8 +166,8 @@ def test_schur_parity(scene, lam):
 @pytest.mark.parametrize("config", ["tiny", "small"])
 @pytest.mark.parametrize("cameras", CAMERA_TABLES)
 def test_pcg_and_update_parity(config, cameras, monkeypatch):
-    # the camera table of these scenes fits in LDS; the environment switches,
-    # read when the handle is created, select the other layouts
+    # the camera table of these scenes fits in LDS; the environment switch,
+    # read when the handle is created, selects the memory layout
     use_camera_table(cameras, monkeypatch)
     sc = ba_scene(config)
     gpu, orc = make_pair(sc)
@@ -346,9 +342,8 @@ def test_heavy_camera_multi_chunk_parity(cameras, monkeypatch):
     """One camera with about 3,200 observations in one point band: its
     camera-order segment is split into several chunks, whose partials the
     per-camera kernels (B and g_c, rhs and S_jj, the PCG's camera side) add in
-    chunk order.  All three camera-table layouts (whole rows in LDS, the split
-    layout, the table in memory), selected by the environment switches read
-    at creation."""
+    chunk order.  Both camera layouts (whole rows in LDS, the table in
+    memory), selected by the environment switch read at creation."""
     use_camera_table(cameras, monkeypatch)
     sc = heavy_camera_scene()
     assert _max_band_segment(sc) > 2048

@@ -1,12 +1,8 @@
 """Parity on the wide scene (1,500 ring cameras, 90,000 points, about 495,000
 observations, Huber loss): more cameras than whole camera rows fit in one
-compute unit's LDS, so the library chooses by size, with no switch, the split
-layout: the PCG and back-substitution point passes keep only the cameras'
-9-vectors in LDS and read the geometry from memory, and the linearisation and
-cost passes read the camera table from memory.  The kernels that read every
-camera datum from memory (the tile point pass, a separate stop test, the q and
-update kernels), chosen by size past 2,240 cameras, run here under the
-environment switch and, on the widest scene (2,500 cameras), by size.
+compute unit's LDS, so the library chooses by size, with no switch, the memory
+layout: the point passes read each observation's camera geometry and vector
+from memory.
 
 Bars as for the other scenes: every block of the linearisation within 1e-10,
 the blocks built from inverted point blocks within their first-order bound,
@@ -19,8 +15,7 @@ import pytest
 import oracle
 from synthetic import ba_scene
 
-from test_gpu_ba_parity import (blocks_close, inverse_bounds, residual_bounds, traces_agree,
-                                use_camera_table)
+from test_gpu_ba_parity import blocks_close, inverse_bounds, residual_bounds, traces_agree
 
 pytestmark = pytest.mark.gpu
 
@@ -30,22 +25,6 @@ bamod = pytest.importorskip("nonlinear_least_squares_amd.ba")
 @pytest.fixture(scope="module")
 def wide():
     return ba_scene("wide")
-
-
-def test_wide_scene_selects_split_layout(wide, monkeypatch):
-    assert 1077 < len(wide["cams"]) <= 2240
-    g = bamod.Problem.from_scene(wide)
-    g.profile()
-    g.debug_run(bamod.BA_STAGE_PCG)
-    prof = g.profile_get()
-    # the separate q kernel runs only when no camera data is in LDS
-    assert prof["pcg_q"][0] == 0 and prof["pcg_xr"][0] > 0 and prof["pcg_pt"][0] > 0
-    use_camera_table("memory", monkeypatch)
-    g = bamod.Problem.from_scene(wide)
-    g.profile()
-    g.debug_run(bamod.BA_STAGE_PCG)
-    prof = g.profile_get()
-    assert prof["pcg_q"][0] > 0 and prof["pcg_pt"][0] > 0
 
 
 def test_wide_linearisation_and_schur(wide):
@@ -66,9 +45,7 @@ def test_wide_linearisation_and_schur(wide):
         blocks_close(name, g.debug_get(name), o.get(name), tols[name])
 
 
-@pytest.mark.parametrize("cameras", ["split", "memory"])
-def test_wide_pcg_and_backsubstitution(wide, cameras, monkeypatch):
-    use_camera_table(cameras, monkeypatch)
+def test_wide_pcg_and_backsubstitution(wide):
     sc = wide
     g = bamod.Problem.from_scene(sc)
     o = oracle.Problem.from_scene(sc)
@@ -90,9 +67,7 @@ def test_wide_pcg_and_backsubstitution(wide, cameras, monkeypatch):
     assert abs(trial - ref) <= 1e-8 * ref
 
 
-@pytest.mark.parametrize("cameras", ["split", "memory"])
-def test_wide_three_lm_steps(wide, cameras, monkeypatch):
-    use_camera_table(cameras, monkeypatch)
+def test_wide_three_lm_steps(wide):
     sc = wide
     g = bamod.Problem.from_scene(sc)
     o = oracle.Problem.from_scene(sc)
@@ -103,44 +78,3 @@ def test_wide_three_lm_steps(wide, cameras, monkeypatch):
         assert a["pcg_iters"] == b["pcg_iters"]
     assert abs(g.get_state()["cost"] - o.cost) <= 1e-6 * o.cost
 
-
-@pytest.fixture(scope="module")
-def widest():
-    return ba_scene("widest")
-
-
-def test_widest_scene_selects_memory_layout(widest):
-    """2,500 cameras: more than even the camera vectors fit in LDS, so every
-    pass reads the camera table from memory, chosen by size."""
-    assert len(widest["cams"]) > 2240
-    g = bamod.Problem.from_scene(widest)
-    g.profile()
-    g.debug_run(bamod.BA_STAGE_PCG)
-    prof = g.profile_get()
-    assert prof["pcg_q"][0] > 0 and prof["pcg_pt"][0] > 0
-
-
-def test_widest_pcg_and_three_lm_steps(widest):
-    sc = widest
-    g = bamod.Problem.from_scene(sc)
-    o = oracle.Problem.from_scene(sc)
-    g.debug_run(bamod.BA_STAGE_UPDATE)
-    o.linearize()
-    o.damp()
-    o.schur()
-    it, rel = o.pcg(sc["pcg_max_iters"], sc["pcg_rel_tol"])
-    o.backsub()
-    g_it, g_rel = g.debug_get("pcg")
-    assert int(g_it) == it, (g_it, it)
-    dc, dc_ref = g.debug_get("dc"), o.get("dc")
-    assert np.linalg.norm(dc - dc_ref) <= 1e-8 * np.linalg.norm(dc_ref)
-    dp, dp_ref = g.debug_get("dp"), o.get("dp")
-    assert np.linalg.norm(dp - dp_ref) <= 1e-8 * np.linalg.norm(dp_ref)
-    g = bamod.Problem.from_scene(sc)
-    o = oracle.Problem.from_scene(sc)
-    g_tr = [g.lm_step() for _ in range(3)]
-    o_tr = o.solve(3)
-    assert traces_agree(g_tr, o_tr)
-    for a, b in zip(g_tr, o_tr):
-        assert a["pcg_iters"] == b["pcg_iters"]
-    assert abs(g.get_state()["cost"] - o.cost) <= 1e-6 * o.cost
