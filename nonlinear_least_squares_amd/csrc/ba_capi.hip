@@ -812,8 +812,10 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
     h->cam_lds_bytes = 0;
     h->cam_layout = kCamMemory;
     h->lds_blocks = 0;
+    // (a scene with no observations takes the memory layout, whose point
+    // passes load nothing from an empty range)
     const char* off = std::getenv("BA_NO_LDS_CAMERAS");
-    if (!(off && off[0] == '1') && nc <= kCamLdsMaxCams) {
+    if (!(off && off[0] == '1') && nc <= kCamLdsMaxCams && N > 0) {
       h->cam_layout = kCamRows;
       h->cam_lds_bytes = (int)(kCamLdsStride * 8 * nc);
     }

@@ -258,6 +258,34 @@ def _edge_scene():
     return sc
 
 
+@pytest.mark.parametrize("queued", [False, True])
+def test_scene_without_observations(queued):
+    """Cameras and points with no observations at all: the cost is 0, the
+    reduced system is the damping alone with a zero right-hand side, so the PCG
+    stops before its first iteration; no step lowers the cost strictly, so
+    every step is rejected and the parameters stay, as in the oracle's run.
+    Step by step and queued (ba_solve)."""
+    sc = dict(ba_scene("tiny"))
+    sc["obs_cam"] = np.zeros(0, np.int32)
+    sc["obs_pt"] = np.zeros(0, np.int32)
+    sc["obs_uv"] = np.zeros((0, 2))
+    gpu, orc = make_pair(sc)
+    o_tr = orc.solve(3)
+    if queued:
+        s = gpu.solve(3)
+        assert s["accepted"] == 0 and s["pcg_iters_total"] == 0 and s["final_cost"] == 0.0
+    else:
+        g_tr = [gpu.lm_step() for _ in range(3)]
+        for a, b in zip(g_tr, o_tr):
+            assert a["accepted"] == b["accepted"] == 0
+            assert a["pcg_iters"] == b["pcg_iters"] == 0
+            assert a["cost_before"] == a["cost_after"] == 0.0
+    cams, pts = gpu.get_params()
+    assert np.array_equal(cams, sc["cams"]) and np.array_equal(pts, sc["points"])
+    st = gpu.get_state()
+    assert st["cost"] == 0.0 and abs(st["lam"] - 10 * o_tr[-1]["lam"]) <= 1e-15 * st["lam"]
+
+
 def test_edge_cases_parity():
     sc = _edge_scene()
     gpu, orc = make_pair(sc)
