@@ -85,7 +85,7 @@ struct ba_problem {
   int64_t nc = 0, np = 0, nobs = 0;
   ba_options opt{};
   hipStream_t stream = nullptr;
-  int n_tiles = 0, n_chunks = 0, n_cost_blocks = 0, lds_blocks = 0,
+  int n_chunks = 0, lds_blocks = 0,
       cam_lds_bytes = 0, cam_layout = 0, n_chunk_blocks = 0;
   Arena arena;   // everything sized by n_cams, n_pts, n_obs
   Arena arena2;  // partitions and partial sums, sized after the CSR offsets
@@ -100,8 +100,7 @@ struct ba_problem {
   int32_t *perm_pt = nullptr, *perm_cam = nullptr, *pt_ptr = nullptr, *cam_ptr = nullptr;
   int32_t *o_cam = nullptr, *o_pt = nullptr, *c_pt = nullptr, *run_len = nullptr;
   double *o_uv = nullptr, *c_uv = nullptr;
-  int32_t *tile_begin = nullptr,
-          *cam_chunk_ptr = nullptr, *wave_begin = nullptr;
+  int32_t *cam_chunk_ptr = nullptr, *wave_begin = nullptr;
   int4* blk_chunk = nullptr;
   // dense solver
   int ds_ld = 0, ds_T = 0, ds_nruns = 0, ds_nblk = 0;
@@ -168,7 +167,6 @@ Dev make_dev(const ba_problem* h) {
   d.nc = h->nc;
   d.np = h->np;
   d.nobs = h->nobs;
-  d.n_tiles = h->n_tiles;
   d.n_chunks = h->n_chunks;
   d.n_chunk_blocks = h->n_chunk_blocks;
   d.blk_chunk = h->blk_chunk;
@@ -176,7 +174,6 @@ Dev make_dev(const ba_problem* h) {
   d.cam_lds_bytes = h->cam_lds_bytes;
   d.cam_layout = h->cam_layout;
   d.wave_begin = h->wave_begin;
-  d.n_cost_blocks = h->n_cost_blocks;
   d.loss = h->opt.loss;
   d.delta = h->opt.huber_delta;
   d.diag_floor = h->opt.diag_floor;
@@ -198,7 +195,6 @@ Dev make_dev(const ba_problem* h) {
   d.c_uv = h->c_uv;
   d.run_len = h->run_len;
   d.pt_ptr = h->pt_ptr;
-  d.tile_begin = h->tile_begin;
   d.cam_chunk_ptr = h->cam_chunk_ptr;
   d.w_pt = h->w_pt;
   d.w_cam = h->w_cam;
@@ -788,16 +784,6 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   d_uv = nullptr;
   d_flags = nullptr;
 
-  // Point tiles: whole points, at most kTile observations unless one point is longer.
-  std::vector<int32_t> tiles{0};
-  int32_t start = 0;
-  for (int64_t i = 0; i < np; ++i) {
-    if (pt_ptr[i + 1] - start > kTile && pt_ptr[i] > start) {
-      tiles.push_back(pt_ptr[i]);
-      start = pt_ptr[i];
-    }
-  }
-  if (N > start) tiles.push_back((int32_t)N);
   // The kernels that keep the camera table in LDS run one block per compute
   // unit; each wavefront takes an equal share of the observations, moved to
   // the nearest point start at or after the even split.
@@ -812,10 +798,8 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
     h->cam_lds_bytes = 0;
     h->cam_layout = kCamMemory;
     h->lds_blocks = 0;
-    // (a scene with no observations takes the memory layout, whose point
-    // passes load nothing from an empty range)
     const char* off = std::getenv("BA_NO_LDS_CAMERAS");
-    if (!(off && off[0] == '1') && nc <= kCamLdsMaxCams && N > 0) {
+    if (!(off && off[0] == '1') && nc <= kCamLdsMaxCams) {
       h->cam_layout = kCamRows;
       h->cam_lds_bytes = (int)(kCamLdsStride * 8 * nc);
     }
@@ -873,19 +857,16 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
       blk_chunk[i * kPointBands + bnd] = make_int4(chunk_begin[ch], chunk_begin[ch + 1], chunk_cam[ch], ch);
     }
   h->n_chunk_blocks = (int)blk_chunk.size();
-  h->n_tiles = (int)tiles.size() - 1;
   h->n_chunks = (int)chunk_cam.size();
-  h->n_cost_blocks = (int)((N + kCostBlock - 1) / kCostBlock);
 
   Arena& P = h->arena2;
-  P.add(h->tile_begin, (int64_t)tiles.size());
   P.add(h->wave_begin, (int64_t)std::max<size_t>(wave_begin.size(), 1));
   const int64_t n_ch1 = std::max(h->n_chunks, 1);
   P.add(h->blk_chunk, (int64_t)std::max<size_t>(blk_chunk.size(), 1));
   P.add(h->lin_part, n_ch1 * kLinCamVals);
   P.add(h->schur_part, n_ch1 * kSchurVals);
   P.add(h->pcg_part, n_ch1 * 9);
-  P.add(h->cost_part, (int64_t)std::max(h->n_cost_blocks, 1));
+  P.add(h->cost_part, (int64_t)std::max(h->lds_blocks, 1));
   P.add(h->red_part, 8 * (int64_t)pcg_red_blocks(nc) + 2);
   P.add(h->pt_dot, (int64_t)std::max(h->lds_blocks, 1));
   P.add(h->cam_rows, h->cam_layout == kCamRows ? (int64_t)kCamLdsFill * kLdsBlock : 1);
@@ -896,8 +877,6 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   rc = P.commit();
   if (rc != BA_OK) return rc;
   TRY(hipMemsetAsync(P.base, 0, P.size, s));
-  TRY(hipMemcpyAsync(h->tile_begin, tiles.data(), sizeof(int32_t) * tiles.size(),
-                     hipMemcpyHostToDevice, s));
   if (!wave_begin.empty())
     TRY(hipMemcpyAsync(h->wave_begin, wave_begin.data(), sizeof(int32_t) * wave_begin.size(),
                        hipMemcpyHostToDevice, s));

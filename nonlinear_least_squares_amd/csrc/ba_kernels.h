@@ -10,10 +10,11 @@
 //                  z (3), dp (3)
 //   per camera   : parameters (9), CamT table (16), B (45), g_c (9), B~ (45),
 //                  rhs (9), S_jj^-1 (45, packed), PCG vectors (9 each)
-//   partitions   : point tiles (whole points, <= kTile observations unless a
-//                  single point is longer); camera chunks: the observations
-//                  of one camera whose points lie in one of kPointBands equal
-//                  point-index bands, cut into pieces of <= kChunk
+//   partitions   : point-order ranges of whole points, one per wavefront of
+//                  the persistent point-pass blocks; camera chunks: the
+//                  observations of one camera whose points lie in one of
+//                  kPointBands equal point-index bands, cut into pieces of
+//                  <= kChunk
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -25,20 +26,18 @@
 namespace ba {
 
 constexpr int kWave = 64;         // wavefront width on gfx950
-constexpr int kTile = 256;        // observations per point-order sub-tile (= block size)
 constexpr int kLdsBlock = 1024;   // threads of the persistent LDS-camera-table kernels
 constexpr int kCamLdsStride = 19; // doubles per camera in the LDS table: q (4), t, f, k1, k2, vector (9)
 constexpr int kCamLdsFill = 20;   // table elements per thread in the copy (>= 19 * max cameras / kLdsBlock)
 constexpr int kCamLdsMaxCams = kCamLdsFill * 1024 / kCamLdsStride;   // 1,077
 constexpr int kCostLdsFill = (10 * kCamLdsMaxCams + 1023) / 1024;   // geometry elements per thread
-// Where the PCG and back-substitution point passes find the camera data.
+// Where the point passes find the camera data.
 constexpr int kCamRows = 0;      // whole rows in LDS (up to kCamLdsMaxCams cameras)
 constexpr int kCamMemory = 1;    // the camera table and vectors in memory (any number)
 constexpr int kChunkLoads = 8;   // a camera's chunk partials loaded together in the per-camera sums
 constexpr int kChunk = 1024;      // observations per camera chunk (one wavefront)
 constexpr int kPointBands = 4;    // point-index bands of the camera chunks (block b: band b % 4,
                                   // on dies b % 8: two dies' L2 per band)
-constexpr int kCostBlock = 1024;  // observations per cost-reduction block
 constexpr int kUpdBlock = 1024;   // threads of the single-block cost reduction
 constexpr int kLinCamVals = 54;   // B (45) + g_c (9)
 constexpr int kSchurVals = 54;    // E v (9) + Ebar C~^-1 Ebar^T (45)
@@ -84,7 +83,7 @@ struct LmLog {       // one record per queued step, read back after the last
 
 struct Dev {
   int64_t nc, np, nobs;
-  int n_tiles, n_chunks, n_cost_blocks;
+  int n_chunks;
   int n_chunk_blocks;    // blocks of the camera passes (blk_chunk entries)
   int lds_blocks, cam_lds_bytes;  // LDS camera-table kernels (bytes 0: not used)
   int loss;
@@ -106,7 +105,6 @@ struct Dev {
   const double* c_uv;
   const int32_t* run_len;
   const int32_t* pt_ptr;
-  const int32_t* tile_begin;
   const int32_t* wave_begin;     // point-order range of each wavefront of the LDS kernels
   const int32_t* cam_chunk_ptr;  // chunks of each camera, in order
   const int4* blk_chunk;         // per block of the camera passes: chunk begin, end, camera,

@@ -1,13 +1,12 @@
 // gfx950 kernels for one Levenberg-Marquardt iteration of bundle adjustment.
 //
 // Point-order passes (linearisation + point blocks, PCG point side,
-// back-substitution, cost): with at most 1,077 cameras, one persistent
-// 1,024-thread block per compute unit holds the camera table in LDS and each
-// wavefront streams a point-aligned range of observations 64 at a time; a
-// point's sums are formed by a DPP segmented scan across the lanes and carried
-// across slots in registers.  With more cameras, tiles of whole points read
-// the camera table from memory and carry partial sums across wavefronts
-// through LDS.  Camera-order passes (camera blocks, Schur right-hand side and
+// back-substitution, cost): one persistent 1,024-thread block per compute
+// unit, each wavefront streaming a point-aligned range of observations 64 at
+// a time; a point's sums are formed by a DPP segmented scan across the lanes
+// and carried across slots in registers.  With at most 1,077 cameras each
+// block holds the camera table in LDS; with more, each observation reads its
+// camera's data from memory.  Camera-order passes (camera blocks, Schur right-hand side and
 // diagonal blocks, PCG camera side) run one wavefront per chunk of one
 // camera: each lane accumulates its observations, software-pipelined (the
 // PCG and Schur passes gather each point's 64-byte record with four lanes),
@@ -150,96 +149,6 @@ __device__ __forceinline__ void seg_scan_dpp(double (&v)[K], int lane, int seg0)
 #undef SEG_STEP
 }
 
-// Segmented reduction over whole points for one point-order tile.  Op supplies
-//   compute(s, pt, v[K])  : per-observation contribution (s = point-order index)
-//   finish(pt, v[K])      : called once per point with its total
-template <int K, int NT = kTile, class Op>
-__device__ __forceinline__ void point_tile_reduce(const Dev& d, Op& op, int tile,
-                                                  const int32_t* tile_begin = nullptr) {
-  __shared__ double s_tail[NT / kWave][K];
-  __shared__ int s_tail_pt[NT / kWave];
-  __shared__ int s_tail_full[NT / kWave];
-  __shared__ double s_carry[K];
-  __shared__ int s_carry_pt;
-  const int32_t* tb = tile_begin ? tile_begin : d.tile_begin;
-  const int ob = tb[tile], oe = tb[tile + 1];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  if (tid == 0) s_carry_pt = -1;
-  for (int base = ob; base < oe; base += NT) {
-    const int s = base + tid;
-    const bool valid = s < oe;
-    const int pt = valid ? d.o_pt[s] : -1;
-    double v[K];
-    if (valid) {
-      op.compute(s, pt, v);
-    } else {
-#pragma unroll
-      for (int k = 0; k < K; ++k) v[k] = 0.0;
-    }
-    // segment start within the wavefront
-    const int prev_pt = __shfl_up(pt, 1, kWave);
-    const bool head = (lane == 0) || (pt != prev_pt);
-    const unsigned long long heads = __ballot(head);
-    const unsigned long long upto = (lane == kWave - 1) ? ~0ull : ((2ull << lane) - 1ull);
-    const int seg0 = 63 - __clzll(heads & upto);
-#pragma unroll
-    for (int dd = 1; dd < kWave; dd <<= 1) {
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const double o = __shfl_up(v[k], dd, kWave);
-        if (lane - dd >= seg0) v[k] += o;
-      }
-    }
-    if (lane == kWave - 1) {
-#pragma unroll
-      for (int k = 0; k < K; ++k) s_tail[wv][k] = v[k];
-      s_tail_pt[wv] = pt;
-      s_tail_full[wv] = (seg0 == 0);
-    }
-    __syncthreads();
-    if (valid && seg0 == 0) {
-      // this wavefront's first segment may continue from earlier wavefronts or sub-tiles
-      double c[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) c[k] = 0.0;
-      int w = wv - 1;
-      bool more = true;
-      while (more) {
-        if (w >= 0) {
-          if (s_tail_pt[w] == pt) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) c[k] += s_tail[w][k];
-            more = s_tail_full[w] != 0;
-            --w;
-          } else {
-            more = false;
-          }
-        } else {
-          if (s_carry_pt == pt) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) c[k] += s_carry[k];
-          }
-          more = false;
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < K; ++k) v[k] += c[k];
-    }
-    const bool is_end = valid && (s + 1 >= oe || d.o_pt[s + 1] != pt);
-    if (is_end) op.finish(pt, v);
-    __syncthreads();
-    if (tid == NT - 1) {
-      if (valid && !is_end) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) s_carry[k] = v[k];
-        s_carry_pt = pt;
-      } else {
-        s_carry_pt = -1;
-      }
-    }
-    __syncthreads();
-  }
-}
 
 // ------------------------------------------------------------- camera table
 
@@ -274,43 +183,6 @@ __global__ void k_cam_prep(const double* __restrict__ cams, CamT* __restrict__ t
 }
 
 // ------------------------------------------------------------ linearisation
-
-struct LinPtOp {
-  const Dev& d;
-  __device__ void compute(int s, int pt, double* v) {
-    CamG c;
-    load_cam(d.tab, d.o_cam[s], c);
-    Geo g;
-    geo_eval(c, d.pts[3 * pt], d.pts[3 * pt + 1], d.pts[3 * pt + 2], g);
-    const double r0 = g.u0 - d.o_uv[2 * s], r1 = g.u1 - d.o_uv[2 * s + 1];
-    double w, rho;
-    robust(r0, r1, d.loss, d.delta, w, rho);
-    d.w_pt[s] = w;
-    double J[6];
-    jp_rows(g, c.R, J);
-    v[0] = w * (J[0] * J[0] + J[3] * J[3]);
-    v[1] = w * (J[0] * J[1] + J[3] * J[4]);
-    v[2] = w * (J[0] * J[2] + J[3] * J[5]);
-    v[3] = w * (J[1] * J[1] + J[4] * J[4]);
-    v[4] = w * (J[1] * J[2] + J[4] * J[5]);
-    v[5] = w * (J[2] * J[2] + J[5] * J[5]);
-    v[6] = w * (J[0] * r0 + J[3] * r1);
-    v[7] = w * (J[1] * r0 + J[4] * r1);
-    v[8] = w * (J[2] * r0 + J[5] * r1);
-  }
-  __device__ void finish(int pt, const double* v) {
-#pragma unroll
-    for (int k = 0; k < 6; ++k) d.C[6 * pt + k] = v[k];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) d.gp[3 * pt + k] = v[6 + k];
-  }
-};
-
-__global__ __launch_bounds__(kTile) void k_lin_pt(Dev d) {
-  if (lin_skipped(d)) return;
-  LinPtOp op{d};
-  point_tile_reduce<9>(d, op, blockIdx.x);
-}
 
 // One slot (64 observations) of a camera chunk: robust weight, stored for the
 // later camera passes (real slots only), and the lane's share of B and g_c.
@@ -740,15 +612,6 @@ __device__ __forceinline__ double lane_partial(const double* a, int n) {
 // Sum of n >= 1 doubles by one wavefront, in a fixed order.
 __device__ __forceinline__ double wave_sum_array(const double* a, int n) {
   return wave_sum(lane_partial(a, n));
-}
-
-// Sum of n doubles in index order by one block (fixed tree): every block that
-// calls it on the same data gets the same bits.
-__device__ __forceinline__ double block_sum_array(const double* a, int n, int stride,
-                                                  double* s_buf) {
-  double v = 0.0;
-  for (int k = threadIdx.x; k < n; k += kTile) v += a[(int64_t)k * stride];
-  return block_sum<kTile>(v, s_buf);
 }
 
 // PCG on S dc = rhs with the block-Jacobi preconditioner M = blockdiag(S_jj).
@@ -1547,25 +1410,6 @@ __global__ __launch_bounds__(kLdsBlock) void k_backsub_lds(Dev d, int pcg_iters,
       retract_camera(d, j);
 }
 
-__global__ __launch_bounds__(256) void k_cost(Dev d, const double* __restrict__ pts,
-                                              const CamT* __restrict__ tab) {
-  __shared__ double s_buf[256 / kWave];
-  const int64_t b0 = (int64_t)blockIdx.x * kCostBlock;
-  const int64_t b1 = b0 + kCostBlock < d.nobs ? b0 + kCostBlock : d.nobs;
-  double acc = 0.0;
-  for (int64_t s = b0 + threadIdx.x; s < b1; s += 256) {
-    const int i = d.o_pt[s];
-    CamG c;
-    load_cam(tab, d.o_cam[s], c);
-    Geo g;
-    geo_eval(c, pts[3 * i], pts[3 * i + 1], pts[3 * i + 2], g);
-    double w, rho;
-    robust(g.u0 - d.o_uv[2 * s], g.u1 - d.o_uv[2 * s + 1], d.loss, d.delta, w, rho);
-    acc += rho;
-  }
-  acc = block_sum<256>(acc, s_buf);
-  if (threadIdx.x == 0) d.cost_part[blockIdx.x] = acc;
-}
 
 // Camera geometry rows in LDS for the point-order kernels that need no camera
 // vector (linearisation, cost): q, t, f, k1, k2 at an odd stride; R is formed
@@ -1607,6 +1451,7 @@ __device__ __forceinline__ void geometry_from_lds(const double* s_geo, int j, Ca
 // unit, each wavefront summing its point-aligned observation range 64 at a
 // time with the next slot's loads in flight, then a DPP scan across the lanes
 // and the block's wavefronts in order.  One partial per block.
+template <int LAYOUT>
 __global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __restrict__ pts,
                                                         const CamT* __restrict__ tab,
                                                         const double* __restrict__ camq) {
@@ -1615,12 +1460,17 @@ __global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __r
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int wave = blockIdx.x * (kLdsBlock / kWave) + wv;
   const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
-  const int nlast = (int)d.nobs - 1;
-  fill_geometry_lds(s_cam, tab, camq, (int)d.nc);
+  const int nlast = max((int)d.nobs - 1, 0);
+  if (LAYOUT == kCamRows) fill_geometry_lds(s_cam, tab, camq, (int)d.nc);
   // first slot's observation data, in flight across the barrier
-  int s0 = min(sb + lane, nlast);
-  int pt = d.o_pt[s0], cj = d.o_cam[s0];
-  double2 uv = reinterpret_cast<const double2*>(d.o_uv)[s0];
+  int pt = 0, cj = 0;
+  double2 uv = make_double2(0.0, 0.0);
+  if (sb < se) {
+    const int s0 = min(sb + lane, nlast);
+    pt = d.o_pt[s0];
+    cj = d.o_cam[s0];
+    uv = reinterpret_cast<const double2*>(d.o_uv)[s0];
+  }
   __syncthreads();
   double acc = 0.0;
   for (int base = sb; base < se; base += kWave) {
@@ -1630,7 +1480,11 @@ __global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __r
     const int npt = d.o_pt[s1], ncj = d.o_cam[s1];
     const double2 nuv = reinterpret_cast<const double2*>(d.o_uv)[s1];
     CamG c;
-    geometry_from_lds(s_cam, cj, c);
+    if (LAYOUT == kCamRows) {
+      geometry_from_lds(s_cam, cj, c);
+    } else {
+      load_cam(tab, cj, c);
+    }
     Geo g;
     geo_eval(c, X0, X1, X2, g);
     double w, rho;
@@ -1656,18 +1510,19 @@ __global__ __launch_bounds__(kLdsBlock) void k_cost_lds(Dev d, const double* __r
 // at a time, a DPP segmented scan of the 9 values per observation (w Jp^T Jp,
 // w Jp^T r) with register carries across slots, C and g_p written at each
 // point's last observation, the robust weight at every observation.
+template <int LAYOUT>
 __global__ __launch_bounds__(kLdsBlock) void k_lin_pt_lds(Dev d) {
   extern __shared__ double s_cam[];
   if (lin_skipped(d)) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * (kLdsBlock / kWave) + threadIdx.x / kWave;
   const int sb = d.wave_begin[wave], se = d.wave_begin[wave + 1];
-  const int nlast = (int)d.nobs - 1;
-  fill_geometry_lds(s_cam, d.tab, d.camq, (int)d.nc);
+  const int nlast = max((int)d.nobs - 1, 0);
+  if (LAYOUT == kCamRows) fill_geometry_lds(s_cam, d.tab, d.camq, (int)d.nc);
   const double2* ouv = reinterpret_cast<const double2*>(d.o_uv);
-  int cpt, cj;
-  double2 uv;
-  {
+  int cpt = -1, cj = 0;
+  double2 uv = make_double2(0.0, 0.0);
+  if (sb < se) {
     const int s0 = min(sb + lane, nlast);
     const int p0 = d.o_pt[s0];
     cpt = sb + lane < se ? p0 : -1;
@@ -1689,7 +1544,11 @@ __global__ __launch_bounds__(kLdsBlock) void k_lin_pt_lds(Dev d) {
     const int npt = s + kWave < se ? p1 : -1;
     const double2 nuv = ouv[s1];
     CamG c;
-    geometry_from_lds(s_cam, cj, c);
+    if (LAYOUT == kCamRows) {
+      geometry_from_lds(s_cam, cj, c);
+    } else {
+      load_cam(d.tab, cj, c);
+    }
     Geo g;
     geo_eval(c, X0, X1, X2, g);
     const double r0 = g.u0 - uv.x, r1 = g.u1 - uv.y;
@@ -1917,7 +1776,8 @@ DispatchEvents& dispatch_events() {
 
 hipError_t set_lds_camera_limit(int bytes) {
   const void* const kernels[] = {
-      reinterpret_cast<const void*>(&k_lin_pt_lds),     reinterpret_cast<const void*>(&k_cost_lds),
+      reinterpret_cast<const void*>(&k_lin_pt_lds<kCamRows>),
+      reinterpret_cast<const void*>(&k_cost_lds<kCamRows>),
       reinterpret_cast<const void*>(&k_pcg_pt_lds<kCamRows>),
       reinterpret_cast<const void*>(&k_backsub_lds<kCamRows>)};
   for (const void* k : kernels) {
@@ -1952,12 +1812,11 @@ void launch_cam_prep(const double* cams, CamT* tab, double* camq, int64_t nc, hi
   if (nc > 0) launch(k_cam_prep, dim3(blocks_for(nc, 256)), dim3(256), s, 0u, cams, tab, camq, nc);
 }
 void launch_lin_pt(const Dev& d, hipStream_t s) {
-  if (d.cam_layout == kCamRows) {
-    launch(k_lin_pt_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
+  if (d.cam_layout == kCamRows)
+    launch(k_lin_pt_lds<kCamRows>, dim3(d.lds_blocks), dim3(kLdsBlock), s,
            (uint32_t)(kGeoLdsStride * 8 * d.nc), d);
-  } else if (d.n_tiles > 0) {
-    launch(k_lin_pt, dim3(d.n_tiles), dim3(kTile), s, 0u, d);
-  }
+  else
+    launch(k_lin_pt_lds<kCamMemory>, dim3(d.lds_blocks), dim3(kLdsBlock), s, 0u, d);
 }
 void launch_lin_cam(const Dev& d, hipStream_t s) {
   if (d.n_chunk_blocks > 0) launch(k_lin_cam, dim3(d.n_chunk_blocks), dim3(kWave), s, 0u, d);
@@ -2003,14 +1862,12 @@ void launch_retract(const Dev& d, hipStream_t s) {
 }
 void launch_cost(const Dev& d, const double* pts, const CamT* tab, const double* camq,
                  hipStream_t s, int step) {
-  if (d.cam_layout == kCamRows) {
-    launch(k_cost_lds, dim3(d.lds_blocks), dim3(kLdsBlock), s,
+  if (d.cam_layout == kCamRows)
+    launch(k_cost_lds<kCamRows>, dim3(d.lds_blocks), dim3(kLdsBlock), s,
            (uint32_t)(kGeoLdsStride * 8 * d.nc), d, pts, tab, camq);
-    launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.lds_blocks, step);
-  } else {
-    if (d.n_cost_blocks > 0) launch(k_cost, dim3(d.n_cost_blocks), dim3(256), s, 0u, d, pts, tab);
-    launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.n_cost_blocks, step);
-  }
+  else
+    launch(k_cost_lds<kCamMemory>, dim3(d.lds_blocks), dim3(kLdsBlock), s, 0u, d, pts, tab, camq);
+  launch(k_cost_final, dim3(1), dim3(kUpdBlock), s, 0u, d, d.lds_blocks, step);
 }
 void launch_lm_commit(const Dev& d, hipStream_t s) {
   // 3 np doubles of points dominate: two per thread, at most 2048 blocks

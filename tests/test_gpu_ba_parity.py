@@ -258,13 +258,16 @@ def _edge_scene():
     return sc
 
 
+@pytest.mark.parametrize("cameras", CAMERA_TABLES)
 @pytest.mark.parametrize("queued", [False, True])
-def test_scene_without_observations(queued):
+def test_scene_without_observations(queued, cameras, monkeypatch):
     """Cameras and points with no observations at all: the cost is 0, the
     reduced system is the damping alone with a zero right-hand side, so the PCG
     stops before its first iteration; no step lowers the cost strictly, so
     every step is rejected and the parameters stay, as in the oracle's run.
-    Step by step and queued (ba_solve)."""
+    Step by step and queued (ba_solve), in both camera layouts (every
+    point-pass wavefront has an empty range)."""
+    use_camera_table(cameras, monkeypatch)
     sc = dict(ba_scene("tiny"))
     sc["obs_cam"] = np.zeros(0, np.int32)
     sc["obs_pt"] = np.zeros(0, np.int32)
