@@ -163,13 +163,14 @@ int ba_options_default(ba_options* o);
  * CSR offsets and work partitions, allocates the whole arena and evaluates
  * the initial cost.  The caller may free its inputs when this returns.
  * opts may be NULL (defaults).  On error *out is left NULL.
- * Up to 1,077 cameras the point passes keep whole camera rows (geometry and
- * the PCG's 9-vector) in each compute unit's LDS; past that they read the
- * camera table and vectors from memory.  The environment variable
- * BA_NO_LDS_CAMERAS=1 at creation selects the memory layout for any size.
- * Results differ between the layouts only by rounding (the linearisation and
- * cost sums over observations are taken in different orders); each layout
- * reproduces its own bits run to run. */
+ * The point passes keep camera data in each compute unit's LDS by size: up
+ * to 1,077 cameras whole rows (geometry and the PCG's 9-vector), up to 2,240
+ * cameras only the 9-vectors of the PCG and back-substitution passes with the
+ * geometry read from memory, past that nothing (everything read from memory).
+ * The environment variables BA_NO_LDS_CAMERAS=1 (memory) and
+ * BA_SPLIT_LDS_CAMERAS=1 (vectors, where they fit) at creation select another
+ * layout.  All layouts compute the same arithmetic in the same order, so they
+ * give the same bits. */
 int ba_create(const double* cams, int64_t n_cams, const double* points, int64_t n_pts,
               const int32_t* obs_cam_idx, const int32_t* obs_pt_idx, const double* obs_uv,
               int64_t n_obs, const ba_options* opts, ba_problem** out);

@@ -788,8 +788,10 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
   // unit; each wavefront takes an equal share of the observations, moved to
   // the nearest point start at or after the even split.
   // The point passes' camera data: up to kCamLdsMaxCams cameras whole rows
-  // in LDS, past that read from memory.  BA_NO_LDS_CAMERAS=1 at creation
-  // selects the memory layout (for its tests on small scenes).
+  // in LDS; up to kZLdsMaxCams the PCG's 9-vectors there and the geometry in
+  // memory; past that everything in memory.  BA_NO_LDS_CAMERAS=1 at creation
+  // selects the memory layout, BA_SPLIT_LDS_CAMERAS=1 the vectors layout
+  // where it fits (for the tests of those layouts on small scenes).
   std::vector<int32_t> wave_begin;
   {
     int dev = 0, cus = 0;
@@ -799,9 +801,15 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
     h->cam_layout = kCamMemory;
     h->lds_blocks = 0;
     const char* off = std::getenv("BA_NO_LDS_CAMERAS");
-    if (!(off && off[0] == '1') && nc <= kCamLdsMaxCams) {
-      h->cam_layout = kCamRows;
-      h->cam_lds_bytes = (int)(kCamLdsStride * 8 * nc);
+    const char* spl = std::getenv("BA_SPLIT_LDS_CAMERAS");
+    if (!(off && off[0] == '1')) {
+      if (nc <= kCamLdsMaxCams && !(spl && spl[0] == '1')) {
+        h->cam_layout = kCamRows;
+        h->cam_lds_bytes = (int)(kCamLdsStride * 8 * nc);
+      } else if (nc <= kZLdsMaxCams) {
+        h->cam_layout = kCamVectors;
+        h->cam_lds_bytes = (int)(kZLdsStride * 8 * nc);
+      }
     }
     if (h->cam_lds_bytes > 0) TRY(set_lds_camera_limit(h->cam_lds_bytes));
     {

@@ -33,7 +33,10 @@ constexpr int kCamLdsMaxCams = kCamLdsFill * 1024 / kCamLdsStride;   // 1,077
 constexpr int kCostLdsFill = (10 * kCamLdsMaxCams + 1023) / 1024;   // geometry elements per thread
 // Where the point passes find the camera data.
 constexpr int kCamRows = 0;      // whole rows in LDS (up to kCamLdsMaxCams cameras)
-constexpr int kCamMemory = 1;    // the camera table and vectors in memory (any number)
+constexpr int kCamVectors = 1;   // the PCG's 9-vectors in LDS, geometry in memory (up to kZLdsMaxCams)
+constexpr int kCamMemory = 2;    // the camera table and vectors in memory (any number)
+constexpr int kZLdsStride = 9;   // doubles per camera in the vectors layout's LDS table
+constexpr int kZLdsMaxCams = 2240;   // 9 * 2240 <= kCamLdsFill * kLdsBlock, 161 KB of LDS
 constexpr int kChunkLoads = 8;   // a camera's chunk partials loaded together in the per-camera sums
 constexpr int kChunk = 1024;      // observations per camera chunk (one wavefront)
 constexpr int kPointBands = 4;    // point-index bands of the camera chunks (block b: band b % 4,
@@ -136,7 +139,7 @@ struct Dev {
   double* pt_dot;    // per-block partials of z^T E C~^-1 E^T z from the LDS point pass
   double* cam_rows;  // LDS point pass, PCG: the camera table rows (kCamLdsStride doubles:
                      // q, t, f, k1, k2, z) padded to kCamLdsFill * kLdsBlock, copied as is
-  int cam_layout;    // kCamRows or kCamMemory (the point passes' camera data)
+  int cam_layout;    // kCamRows, kCamVectors or kCamMemory (the point passes' camera data)
   int red_nb;        // blocks of the camera-vector kernels
   long long* host_done;  // host-mapped, tagged with pcg_seq in the upper 32 bits: [0] the
                          // solve stopped (low bits: its iteration count), [1] the last

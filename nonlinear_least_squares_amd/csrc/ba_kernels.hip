@@ -854,13 +854,16 @@ __device__ __forceinline__ bool pcg_stop_test(const Dev& d, int it, double rhs2,
 //           iteration's stop test, which wavefront 0 of each block makes;
 //   MODE 1: dp = C~^-1 (-g_p - E^T dc) and the trial points (back-substitution).
 // LAYOUT (where the pass finds each observation's camera data):
-//   kCamRows:   whole camera rows in LDS (geometry as a quaternion, and the
-//               9-vector), copied per launch;
-//   kCamMemory: no LDS table: the geometry (R, t, f, k1, k2) from the camera
-//               table and the 9-vector read per observation from memory, for
-//               more cameras than whole rows fit.
+//   kCamRows:    whole camera rows in LDS (geometry as a quaternion, and the
+//                9-vector), copied per launch;
+//   kCamVectors: only the 9-vectors in LDS (kZLdsStride, copied from the
+//                vector as it lies in memory), the geometry (R, t, f, k1, k2)
+//                read per observation from the camera table in memory, for
+//                more cameras than whole rows fit;
+//   kCamMemory:  no LDS table: geometry and 9-vector both read per
+//                observation from memory, for any number of cameras.
 // R in the camera table was formed from the same quaternion by the same
-// function, so both layouts compute with the same bits.
+// function, so all three layouts compute with the same bits.
 template <int MODE, int LAYOUT>
 __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   extern __shared__ double s_cam[];
@@ -895,12 +898,15 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
   // the test; its outcome reaches the other wavefronts through LDS at the
   // barrier before the loop.
   {
-    const int ne = kCamLdsStride * (int)d.nc;
+    const int ne = (LAYOUT == kCamVectors ? kZLdsStride : kCamLdsStride) * (int)d.nc;
     const double* tabd = reinterpret_cast<const double*>(d.tab);
     int done = MODE == 0 ? d.pcg->done : 0;
     double t[kCamLdsFill];
     if (LAYOUT == kCamMemory) {
       // no table
+    } else if (LAYOUT == kCamVectors) {
+#pragma unroll
+      for (int u = 0; u < kCamLdsFill; ++u) t[u] = xbase[min((int)threadIdx.x + u * kLdsBlock, ne - 1)];
     } else if (MODE == 0) {
       // the PCG keeps the rows in this layout in memory (padded to the whole copy)
 #pragma unroll
@@ -964,10 +970,10 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     // unconditionally (indices clamped into range, results of idle lanes
     // dropped), so the loads in flight are the same on every path and each
     // wait, by count in issue order, covers only what is needed by then.
-    // memory layout: the camera's geometry first, so that its latency runs
-    // under the issue of the loads after it
+    // geometry from memory: issued first, so that its latency runs under the
+    // issue of the loads after it
     CamG c;
-    if (LAYOUT == kCamMemory) load_cam(d.tab, cj, c);
+    if (LAYOUT != kCamRows) load_cam(d.tab, cj, c);
     double ci[6];
     const double* Ci = d.Cinv + 6 * (int64_t)cpt_c;
 #pragma unroll
@@ -987,8 +993,8 @@ __device__ __forceinline__ void pcg_pt_lds_body(Dev d, int it) {
     const double nw = d.w_pt[min(s + kWave, last)];
     __builtin_amdgcn_sched_barrier(0);
     double xv[9];
-    if (LAYOUT == kCamMemory) {
-      const double* r = xbase + 9 * (int64_t)cj;
+    if (LAYOUT != kCamRows) {
+      const double* r = LAYOUT == kCamVectors ? s_cam + kZLdsStride * cj : xbase + 9 * (int64_t)cj;
 #pragma unroll
       for (int k = 0; k < 9; ++k) xv[k] = r[k];
     } else {
@@ -1779,7 +1785,9 @@ hipError_t set_lds_camera_limit(int bytes) {
       reinterpret_cast<const void*>(&k_lin_pt_lds<kCamRows>),
       reinterpret_cast<const void*>(&k_cost_lds<kCamRows>),
       reinterpret_cast<const void*>(&k_pcg_pt_lds<kCamRows>),
-      reinterpret_cast<const void*>(&k_backsub_lds<kCamRows>)};
+      reinterpret_cast<const void*>(&k_pcg_pt_lds<kCamVectors>),
+      reinterpret_cast<const void*>(&k_backsub_lds<kCamRows>),
+      reinterpret_cast<const void*>(&k_backsub_lds<kCamVectors>)};
   for (const void* k : kernels) {
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
@@ -1838,7 +1846,9 @@ void launch_precond(const Dev& d, hipStream_t s, bool with_pcg_init) {
            with_pcg_init ? 1 : 0);
 }
 void launch_pcg_pt(const Dev& d, int it, hipStream_t s) {
-  void (*k)(Dev, int) = d.cam_layout == kCamRows ? k_pcg_pt_lds<kCamRows> : k_pcg_pt_lds<kCamMemory>;
+  void (*k)(Dev, int) = d.cam_layout == kCamRows      ? k_pcg_pt_lds<kCamRows>
+                        : d.cam_layout == kCamVectors ? k_pcg_pt_lds<kCamVectors>
+                                                      : k_pcg_pt_lds<kCamMemory>;
   launch(k, dim3(d.lds_blocks), dim3(kLdsBlock), s, (uint32_t)d.cam_lds_bytes, d, it);
 }
 void launch_pcg_cam(const Dev& d, hipStream_t s) {
@@ -1852,8 +1862,9 @@ void launch_pcg_final(const Dev& d, int iters, hipStream_t s) {
 }
 int pcg_red_blocks(int64_t nc) { return cam_vector_blocks(nc); }
 void launch_backsub(const Dev& d, hipStream_t s, int pcg_iters, bool with_retract) {
-  void (*k)(Dev, int, int) = d.cam_layout == kCamRows ? k_backsub_lds<kCamRows>
-                                                       : k_backsub_lds<kCamMemory>;
+  void (*k)(Dev, int, int) = d.cam_layout == kCamRows      ? k_backsub_lds<kCamRows>
+                             : d.cam_layout == kCamVectors ? k_backsub_lds<kCamVectors>
+                                                           : k_backsub_lds<kCamMemory>;
   launch(k, dim3(d.lds_blocks), dim3(kLdsBlock), s, (uint32_t)d.cam_lds_bytes, d, pcg_iters,
          with_retract ? 1 : 0);
 }

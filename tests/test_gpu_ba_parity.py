@@ -95,14 +95,18 @@ def traces_agree(g_tr, o_tr, cost_tol=1e-6):
 
 
 # Camera layouts of the point passes, chosen at creation by size; the
-# environment switch selects the memory layout on scenes that would not get it.
-CAMERA_TABLES = ["lds", "memory"]
+# environment switches select the other two on scenes that would not get them.
+CAMERA_TABLES = ["lds", "vectors", "memory"]
 
 
 def use_camera_table(kind, monkeypatch):
     """For handles created next: whole camera rows in LDS (the default up to
-    1,077 cameras) or the camera table and vectors read from memory."""
-    if kind == "memory":
+    1,077 cameras), only the PCG's camera vectors in LDS with the geometry read
+    from memory (chosen by size up to 2,240 cameras), or the camera table and
+    vectors read from memory."""
+    if kind == "vectors":
+        monkeypatch.setenv("BA_SPLIT_LDS_CAMERAS", "1")
+    elif kind == "memory":
         monkeypatch.setenv("BA_NO_LDS_CAMERAS", "1")
 
 
@@ -166,8 +170,8 @@ def test_schur_parity(scene, lam):
 @pytest.mark.parametrize("config", ["tiny", "small"])
 @pytest.mark.parametrize("cameras", CAMERA_TABLES)
 def test_pcg_and_update_parity(config, cameras, monkeypatch):
-    # the camera table of these scenes fits in LDS; the environment switch,
-    # read when the handle is created, selects the memory layout
+    # the camera table of these scenes fits in LDS; the environment switches,
+    # read when the handle is created, select the other layouts
     use_camera_table(cameras, monkeypatch)
     sc = ba_scene(config)
     gpu, orc = make_pair(sc)
@@ -258,6 +262,25 @@ def _edge_scene():
     return sc
 
 
+def test_camera_layouts_bitwise(monkeypatch):
+    """The three camera layouts differ only in where the point passes find the
+    camera data (R in the camera table is formed from the same quaternion by
+    the same function as the LDS rows' R, and every sum keeps its order), so
+    five LM steps leave the same parameters, cost and damping to the bit."""
+    sc = ba_scene("small")
+    runs = []
+    for kind in CAMERA_TABLES:
+        with monkeypatch.context() as m:
+            use_camera_table(kind, m)
+            g = bamod.Problem.from_scene(sc)
+        tr = [g.lm_step() for _ in range(5)]
+        runs.append((tr, g.get_params(), g.get_state()))
+    for tr, (cams, pts), st in runs[1:]:
+        assert tr == runs[0][0]
+        assert np.array_equal(cams, runs[0][1][0]) and np.array_equal(pts, runs[0][1][1])
+        assert st == runs[0][2]
+
+
 @pytest.mark.parametrize("cameras", CAMERA_TABLES)
 @pytest.mark.parametrize("queued", [False, True])
 def test_scene_without_observations(queued, cameras, monkeypatch):
@@ -265,7 +288,7 @@ def test_scene_without_observations(queued, cameras, monkeypatch):
     reduced system is the damping alone with a zero right-hand side, so the PCG
     stops before its first iteration; no step lowers the cost strictly, so
     every step is rejected and the parameters stay, as in the oracle's run.
-    Step by step and queued (ba_solve), in both camera layouts (every
+    Step by step and queued (ba_solve), in all three camera layouts (every
     point-pass wavefront has an empty range)."""
     use_camera_table(cameras, monkeypatch)
     sc = dict(ba_scene("tiny"))
@@ -373,8 +396,8 @@ def test_heavy_camera_multi_chunk_parity(cameras, monkeypatch):
     """One camera with about 3,200 observations in one point band: its
     camera-order segment is split into several chunks, whose partials the
     per-camera kernels (B and g_c, rhs and S_jj, the PCG's camera side) add in
-    chunk order.  Both camera layouts (whole rows in LDS, the table in
-    memory), selected by the environment switch read at creation."""
+    chunk order.  All three camera layouts, selected by the environment
+    switches read at creation."""
     use_camera_table(cameras, monkeypatch)
     sc = heavy_camera_scene()
     assert _max_band_segment(sc) > 2048

@@ -1,8 +1,10 @@
 """Parity on the wide scene (1,500 ring cameras, 90,000 points, about 495,000
 observations, Huber loss): more cameras than whole camera rows fit in one
-compute unit's LDS, so the library chooses by size, with no switch, the memory
-layout: the point passes read each observation's camera geometry and vector
-from memory.
+compute unit's LDS, so the library chooses by size, with no switch, the
+vectors layout: the PCG and back-substitution point passes keep only the
+cameras' 9-vectors in LDS and read each observation's camera geometry from
+memory.  The PCG and LM tests also run the memory layout (everything read from
+memory, chosen by size past 2,240 cameras) under its environment switch.
 
 Bars as for the other scenes: every block of the linearisation within 1e-10,
 the blocks built from inverted point blocks within their first-order bound,
@@ -15,7 +17,8 @@ import pytest
 import oracle
 from synthetic import ba_scene
 
-from test_gpu_ba_parity import blocks_close, inverse_bounds, residual_bounds, traces_agree
+from test_gpu_ba_parity import (blocks_close, inverse_bounds, residual_bounds, traces_agree,
+                                use_camera_table)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +48,9 @@ def test_wide_linearisation_and_schur(wide):
         blocks_close(name, g.debug_get(name), o.get(name), tols[name])
 
 
-def test_wide_pcg_and_backsubstitution(wide):
+@pytest.mark.parametrize("cameras", ["vectors", "memory"])
+def test_wide_pcg_and_backsubstitution(wide, cameras, monkeypatch):
+    use_camera_table(cameras, monkeypatch)
     sc = wide
     g = bamod.Problem.from_scene(sc)
     o = oracle.Problem.from_scene(sc)
@@ -67,7 +72,9 @@ def test_wide_pcg_and_backsubstitution(wide):
     assert abs(trial - ref) <= 1e-8 * ref
 
 
-def test_wide_three_lm_steps(wide):
+@pytest.mark.parametrize("cameras", ["vectors", "memory"])
+def test_wide_three_lm_steps(wide, cameras, monkeypatch):
+    use_camera_table(cameras, monkeypatch)
     sc = wide
     g = bamod.Problem.from_scene(sc)
     o = oracle.Problem.from_scene(sc)
