@@ -164,7 +164,7 @@ int ba_options_default(ba_options* o);
  * the initial cost.  The caller may free its inputs when this returns.
  * opts may be NULL (defaults).  On error *out is left NULL.
  * The point passes keep camera data in each compute unit's LDS by size: up
- * to 1,077 cameras whole rows (geometry and the PCG's 9-vector), up to 2,240
+ * to 1,076 cameras whole rows (geometry and the PCG's 9-vector), up to 2,240
  * cameras only the 9-vectors of the PCG and back-substitution passes with the
  * geometry read from memory, past that nothing (everything read from memory).
  * The environment variables BA_NO_LDS_CAMERAS=1 (memory) and

@@ -811,7 +811,7 @@ int build(ba_problem* h, const double* cams_in, const double* pts_in, const int3
         h->cam_lds_bytes = (int)(kZLdsStride * 8 * nc);
       }
     }
-    if (h->cam_lds_bytes > 0) TRY(set_lds_camera_limit(h->cam_lds_bytes));
+    if (h->cam_lds_bytes > 0) TRY(set_lds_camera_limit());
     {
       // with no observations one block of empty ranges still makes the
       // PCG's stop test and per-block partials

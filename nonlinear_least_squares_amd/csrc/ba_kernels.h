@@ -29,7 +29,10 @@ constexpr int kWave = 64;         // wavefront width on gfx950
 constexpr int kLdsBlock = 1024;   // threads of the persistent LDS-camera-table kernels
 constexpr int kCamLdsStride = 19; // doubles per camera in the LDS table: q (4), t, f, k1, k2, vector (9)
 constexpr int kCamLdsFill = 20;   // table elements per thread in the copy (>= 19 * max cameras / kLdsBlock)
-constexpr int kCamLdsMaxCams = kCamLdsFill * 1024 / kCamLdsStride;   // 1,077
+// cameras whose whole rows fit: 160 KiB of LDS less 256 bytes for the
+// kernels' own LDS variables (and their alignment)
+constexpr int kCamLdsMaxCams = (160 * 1024 - 256) / (8 * kCamLdsStride);   // 1,076
+static_assert(kCamLdsStride * kCamLdsMaxCams <= kCamLdsFill * 1024, "the copy covers the table");
 constexpr int kCostLdsFill = (10 * kCamLdsMaxCams + 1023) / 1024;   // geometry elements per thread
 // Where the point passes find the camera data.
 constexpr int kCamRows = 0;      // whole rows in LDS (up to kCamLdsMaxCams cameras)
@@ -37,6 +40,10 @@ constexpr int kCamVectors = 1;   // the PCG's 9-vectors in LDS, geometry in memo
 constexpr int kCamMemory = 2;    // the camera table and vectors in memory (any number)
 constexpr int kZLdsStride = 9;   // doubles per camera in the vectors layout's LDS table
 constexpr int kZLdsMaxCams = 2240;   // 9 * 2240 <= kCamLdsFill * kLdsBlock, 161 KB of LDS
+static_assert(kZLdsStride * kZLdsMaxCams <= kCamLdsFill * 1024, "the copy covers the table");
+// the largest dynamic LDS any point pass takes
+constexpr int kMaxCamLdsBytes = 8 * (kCamLdsStride * kCamLdsMaxCams > kZLdsStride * kZLdsMaxCams
+                                         ? kCamLdsStride * kCamLdsMaxCams : kZLdsStride * kZLdsMaxCams);
 constexpr int kChunkLoads = 8;   // a camera's chunk partials loaded together in the per-camera sums
 constexpr int kChunk = 1024;      // observations per camera chunk (one wavefront)
 constexpr int kPointBands = 4;    // point-index bands of the camera chunks (block b: band b % 4,
@@ -195,7 +202,9 @@ struct DispatchEvents {
 DispatchEvents& dispatch_events();
 
 // Allows the LDS-camera-table kernels `bytes` of dynamic LDS.
-hipError_t set_lds_camera_limit(int bytes);
+// Allows the point passes kMaxCamLdsBytes of dynamic LDS (a per-process
+// attribute of the kernels; idempotent, so every handle may call it).
+hipError_t set_lds_camera_limit();
 
 void launch_cam_prep(const double* cams, CamT* tab, double* camq, int64_t nc, hipStream_t s);
 void launch_lin_pt(const Dev& d, hipStream_t s);

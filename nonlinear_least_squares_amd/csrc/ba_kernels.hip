@@ -4,7 +4,7 @@
 // back-substitution, cost): one persistent 1,024-thread block per compute
 // unit, each wavefront streaming a point-aligned range of observations 64 at
 // a time; a point's sums are formed by a DPP segmented scan across the lanes
-// and carried across slots in registers.  With at most 1,077 cameras each
+// and carried across slots in registers.  With at most 1,076 cameras each
 // block holds the camera table in LDS; with more, each observation reads its
 // camera's data from memory.  Camera-order passes (camera blocks, Schur right-hand side and
 // diagonal blocks, PCG camera side) run one wavefront per chunk of one
@@ -1780,7 +1780,8 @@ DispatchEvents& dispatch_events() {
   return ev;
 }
 
-hipError_t set_lds_camera_limit(int bytes) {
+hipError_t set_lds_camera_limit() {
+  const int bytes = kMaxCamLdsBytes;
   const void* const kernels[] = {
       reinterpret_cast<const void*>(&k_lin_pt_lds<kCamRows>),
       reinterpret_cast<const void*>(&k_cost_lds<kCamRows>),

@@ -101,7 +101,7 @@ CAMERA_TABLES = ["lds", "vectors", "memory"]
 
 def use_camera_table(kind, monkeypatch):
     """For handles created next: whole camera rows in LDS (the default up to
-    1,077 cameras), only the PCG's camera vectors in LDS with the geometry read
+    1,076 cameras), only the PCG's camera vectors in LDS with the geometry read
     from memory (chosen by size up to 2,240 cameras), or the camera table and
     vectors read from memory."""
     if kind == "vectors":

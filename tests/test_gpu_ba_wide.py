@@ -85,3 +85,37 @@ def test_wide_three_lm_steps(wide, cameras, monkeypatch):
         assert a["pcg_iters"] == b["pcg_iters"]
     assert abs(g.get_state()["cost"] - o.cost) <= 1e-6 * o.cost
 
+
+
+@pytest.mark.parametrize("n_cams", [1076, 1077])
+def test_layout_boundary_scenes(n_cams):
+    """The largest scene whose whole camera rows fit in LDS (1,076 cameras:
+    the table fills the compute unit's LDS less room for the kernels' own LDS
+    variables) and the smallest that takes the vectors layout, each created
+    after a tiny handle and stepped in turn with it (the LDS limit is a
+    per-process kernel attribute and must hold for every handle): the PCG
+    step, the point step and three LM steps against the oracle."""
+    sc = ba_scene("wide", n_cams=n_cams, n_pts=6000, seed=40 + n_cams % 2, n_iters=3)
+    small = bamod.Problem.from_scene(ba_scene("tiny"))
+    g = bamod.Problem.from_scene(sc)
+    small.lm_step()
+    o = oracle.Problem.from_scene(sc)
+    g.debug_run(bamod.BA_STAGE_UPDATE)
+    o.linearize()
+    o.damp()
+    o.schur()
+    it, rel = o.pcg(sc["pcg_max_iters"], sc["pcg_rel_tol"])
+    o.backsub()
+    g_it, g_rel = g.debug_get("pcg")
+    assert int(g_it) == it, (g_it, it)
+    dc, dc_ref = g.debug_get("dc"), o.get("dc")
+    assert np.linalg.norm(dc - dc_ref) <= 1e-8 * np.linalg.norm(dc_ref)
+    dp, dp_ref = g.debug_get("dp"), o.get("dp")
+    assert np.linalg.norm(dp - dp_ref) <= 1e-8 * np.linalg.norm(dp_ref)
+    g = bamod.Problem.from_scene(sc)
+    small.lm_step()
+    o = oracle.Problem.from_scene(sc)
+    g_tr = [g.lm_step() for _ in range(3)]
+    o_tr = o.solve(3)
+    assert traces_agree(g_tr, o_tr)
+    assert abs(g.get_state()["cost"] - o.cost) <= 1e-6 * o.cost
