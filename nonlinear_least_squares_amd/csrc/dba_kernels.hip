@@ -34,6 +34,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1371,18 +1372,28 @@ int create(const float* poses, const float* inv_depth, int n, int H, int W, cons
   h->lin_lds = (size_t)fac * sizeof(float) + cost_lds();
   h->solve_lds = ((size_t)(h->nv + 1) * (h->nv + 1) + 6 * (size_t)std::max(h->nv - 5, 0) +
                   3 * (size_t)h->nv + 4) * sizeof(float);
-  if (h->lin_lds > 65536)
-    HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin<true, true>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lin_lds));
-  if (h->lin_lds > 65536)
-    HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin<false, true>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lin_lds));
-  if (h->solve_lds > 65536) {
-    HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_solve),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->solve_lds));
-    // k_cov needs nv (nv + 2) floats, within the solver's size
-    HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cov),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->solve_lds));
+  {
+    // The dynamic-LDS limit is a per-process attribute of each kernel: it is
+    // only ever raised, to the largest size any handle has needed, so that a
+    // smaller handle created later cannot lower it below an earlier one's.
+    static std::mutex mu;
+    static size_t lin_max = 65536, solve_max = 65536;
+    std::lock_guard<std::mutex> lock(mu);
+    if (h->lin_lds > lin_max) {
+      HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin<true, true>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lin_lds));
+      HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_lin<false, true>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lin_lds));
+      lin_max = h->lin_lds;
+    }
+    if (h->solve_lds > solve_max) {
+      HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_solve),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->solve_lds));
+      // k_cov needs nv (nv + 2) floats, within the solver's size
+      HIPC(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_cov),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->solve_lds));
+      solve_max = h->solve_lds;
+    }
   }
 
   const int64_t P = h->P;

@@ -470,3 +470,19 @@ def test_rejected_set_state_leaves_the_state(scenes):
     p1, d1 = G.get_state()
     assert np.array_equal(p0, p1) and np.array_equal(d0, d1)
     assert G.gn_step() == H.gn_step()
+
+
+def test_handles_of_different_sizes():
+    """Above 64 KiB the solver's dynamic-LDS limit is a per-process kernel
+    attribute: a handle with 24 free frames (the largest reduced system, 144
+    unknowns), then one with 21, then steps of both, each against the oracle
+    (the second handle must not lower the limit below the first's need)."""
+    kw = dict(height=8, width=10, hops=2, cx=4.5, cy=3.5)
+    big, mid = droid_scene(n_frames=26, **kw), droid_scene(n_frames=23, **kw)
+    Gb = gpu().Problem.from_scene(big)
+    Gm = gpu().Problem.from_scene(mid)
+    for sc, G in ((mid, Gm), (big, Gb)):
+        O = odroid.DroidProblem.from_scene(sc)
+        c0, c1 = G.gn_step()
+        o0, o1 = O.gn_step()
+        assert abs(c0 - o0) <= 1e-4 * o0 and abs(c1 - o1) <= 1e-3 * o1, (c0, c1, o0, o1)
