@@ -169,33 +169,88 @@ __device__ __forceinline__ double rsqrt_newton(double x) {
   return y * fma(-0.5 * x, y * y, 1.5);
 }
 
-// Factor one 32 x 32 diagonal tile held as rows src[r * stride + c] (lane r
-// holds row r) into ds_diag (L, row-major, zeros above the diagonal),
-// ds_diagT (its transpose) and ds_dinv (1 / L(c, c)).  Column c's values move
-// to every lane by readlane.  One wavefront; lanes 32..63 repeat lanes 0..31
-// and store nothing.  A pivot that is not positive and finite sets the not-SPD
-// flag (and is taken as 1).
-__device__ __forceinline__ void factor_diag_tile(const Dev& d, int kt, const double* src,
-                                                 int64_t stride) {
+constexpr int kH = kT / 2;                       // half a tile
+constexpr int kFactorScratch = 2 * kH * kH + kT;   // LDS doubles factor_tile uses
+
+// Factor in place the 32 x 32 tile whose row r lane r holds in a[] (lanes
+// 32..63 repeat lanes 0..31): afterwards a[c] = L(r, c) for c <= r (the
+// entries above the diagonal are left meaningless) and s_x[2 kH^2 + c] =
+// 1 / L(c, c).  Blocked by halves: the first 16 columns by rows, each column's
+// entries moving to every lane by readlane and only the first 16 columns
+// updated; then the trailing block A22 - L21 L21^T with fp64 MFMA
+// (16x16x4), its operands and result passed through LDS (s_x, kFactorScratch
+// doubles); then its 16 columns as the first.  Readlane throughput bounds the
+// unblocked form, and the blocking halves the broadcasts (272 for 528).  A
+// pivot that is not positive and finite sets `bad` and is taken as 1.  Every
+// caller runs the same instructions on the same data, so each holds the same
+// bits.
+__device__ __forceinline__ void factor_tile(double (&a)[kT], double* s_x, bool& bad) {
   const int r = threadIdx.x & (kT - 1);
-  double a[kT];
-#pragma unroll
-  for (int c = 0; c < kT; ++c) a[c] = src[r * stride + c];
-  bool bad = false;
-  double myinv = 0.0;
+  double* s_p = s_x;                  // L21, rows 16..31 of the tile, 16 x 16
+  double* s_q = s_x + kH * kH;        // A22
+  double* s_inv = s_x + 2 * kH * kH;
+  bad = false;
 #pragma unroll
   for (int c = 0; c < kT; ++c) {
+    if (c == kH) {
+      if (r >= kH) {
+#pragma unroll
+        for (int u = 0; u < kH; ++u) {
+          s_p[kH * (r - kH) + u] = a[u];
+          s_q[kH * (r - kH) + u] = a[kH + u];
+        }
+      }
+      __syncthreads();
+      // acc(m, n) = A22(m, n) - sum_k L21(m, k) L21(n, k); both operands take
+      // L21(l % 16, 4 s + l / 16) (see tile_sub_abt for the layout)
+      const int l = threadIdx.x;
+      const int lr = l & 15, lk = l >> 4;
+      v4d acc;
+      double pv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = s_q[kH * (4 * v + lk) + lr];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) pv[st] = s_p[kH * lr + 4 * st + lk];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-pv[st], pv[st], acc, 0, 0, 0);
+      // each lane writes back the elements it read
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_q[kH * (4 * v + lk) + lr] = acc[v];
+      __syncthreads();
+      // lanes of rows 0..15 take a row of it too, into entries they never use
+#pragma unroll
+      for (int u = 0; u < kH; ++u) a[kH + u] = s_q[kH * (r & (kH - 1)) + u];
+    }
     double piv = lane_bcast(a[c], c);
     if (!(piv > 0.0) || !isfinite(piv)) {
       bad = true;
       piv = 1.0;
     }
     const double inv = rsqrt_newton(piv);
-    a[c] = r == c ? piv * inv : a[c] * inv;   // L(r, c) for r >= c
-    if (r == c) myinv = inv;
+    a[c] *= inv;   // L(r, c); on lane c, piv * inv
+    s_inv[c] = inv;   // the same value from every lane
+    const int e = c < kH ? kH : kT;
 #pragma unroll
-    for (int j = c + 1; j < kT; ++j) a[j] -= a[c] * lane_bcast(a[c], j);   // L(j, c)
+    for (int j = c + 1; j < e; ++j) a[j] -= a[c] * lane_bcast(a[c], j);   // L(j, c)
   }
+  __syncthreads();
+}
+
+// Factor one 32 x 32 diagonal tile held as rows src[r * stride + c] (lane r
+// holds row r) with factor_tile into ds_diag (L, row-major, zeros above the
+// diagonal), ds_diagT (its transpose) and ds_dinv (1 / L(c, c)).  One
+// wavefront; lanes 32..63 repeat lanes 0..31 and store nothing.  A pivot that
+// is not positive and finite sets the not-SPD flag.  s_x: kFactorScratch
+// doubles of LDS, which may be src itself.
+__device__ __forceinline__ void factor_diag_tile(const Dev& d, int kt, const double* src,
+                                                 int64_t stride, double* s_x) {
+  const int r = threadIdx.x & (kT - 1);
+  double a[kT];
+#pragma unroll
+  for (int c = 0; c < kT; ++c) a[c] = src[r * stride + c];
+  __syncthreads();
+  bool bad;
+  factor_tile(a, s_x, bad);
   if (bad && threadIdx.x == 0) d.flags[1] = 1;
   if (threadIdx.x >= kT) return;
   double* L = d.ds_diag + (int64_t)kt * kT * kT;
@@ -206,12 +261,13 @@ __device__ __forceinline__ void factor_diag_tile(const Dev& d, int kt, const dou
     L[kT * r + c] = v;
     LT[kT * c + r] = v;
   }
-  d.ds_dinv[kT * kt + r] = myinv;
+  d.ds_dinv[kT * kt + r] = s_x[2 * kH * kH + r];
 }
 
 // The first diagonal tile (the update kernel factors each later one).
 __global__ __launch_bounds__(64) void k_ds_diag0(Dev d) {
-  factor_diag_tile(d, 0, d.ds_S, d.ds_ld);
+  __shared__ double s_x[kFactorScratch];
+  factor_diag_tile(d, 0, d.ds_S, d.ds_ld, s_x);
 }
 
 // Tile column k, its diagonal tile already factored: one wavefront per tile
@@ -348,7 +404,7 @@ __global__ __launch_bounds__(64) void k_ds_update(Dev d, int k, int cov) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) s_t[(16 * mh + 4 * v + lk) * kT + 16 * nh + lr] = acc[mh][nh][v];
     __syncthreads();
-    factor_diag_tile(d, k + 1, s_t, kT);
+    factor_diag_tile(d, k + 1, s_t, kT, s_t);
   }
 }
 
@@ -413,28 +469,16 @@ __device__ __forceinline__ void acc_to_rows(const v4d (&acc)[2][2], double* s_t)
 }
 
 // Factor the diagonal tile whose row r lane r holds in a[] (lanes 32..63
-// repeat lanes 0..31), as factor_diag_tile does, leaving its transpose and
-// the pivot reciprocals in s_l (the layout panel_solve stages) and, with
-// `to_global`, in ds_diag, ds_diagT and ds_dinv.  Every caller runs the same
-// instructions on the same data, so each holds the same bits.
+// repeat lanes 0..31) with factor_tile, s_l serving as its scratch, leaving
+// its transpose and the pivot reciprocals in s_l (the layout panel_solve
+// stages) and, with `to_global`, in ds_diag, ds_diagT and ds_dinv.
 __device__ __forceinline__ void factor_rows(const Dev& d, int kt, double (&a)[kT], double* s_l,
                                             bool to_global) {
   const int r = threadIdx.x & (kT - 1);
-  bool bad = false;
-  double myinv = 0.0;
-#pragma unroll
-  for (int c = 0; c < kT; ++c) {
-    double piv = lane_bcast(a[c], c);
-    if (!(piv > 0.0) || !isfinite(piv)) {
-      bad = true;
-      piv = 1.0;
-    }
-    const double inv = rsqrt_newton(piv);
-    a[c] = r == c ? piv * inv : a[c] * inv;   // L(r, c) for r >= c
-    if (r == c) myinv = inv;
-#pragma unroll
-    for (int j = c + 1; j < kT; ++j) a[j] -= a[c] * lane_bcast(a[c], j);   // L(j, c)
-  }
+  bool bad;
+  factor_tile(a, s_l, bad);
+  const double myinv = s_l[2 * kH * kH + r];
+  __syncthreads();
   if (threadIdx.x >= kT) return;
 #pragma unroll
   for (int c = 0; c < kT; ++c) s_l[kT * c + r] = c <= r ? a[c] : 0.0;
