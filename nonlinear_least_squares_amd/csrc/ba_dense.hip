@@ -525,7 +525,7 @@ __device__ __forceinline__ void solve_rows(const double* s_t, const double* s_l,
 // and solves it in place, L_ikc = (A_ikc - L_ik L_kck^T) L_dd^-T.  No block
 // writes the diagonal tile of S, so each reads it before its update.  The
 // remaining blocks take the other trailing tiles (i, j), kc < j <= i < T, and
-// rhs tiles (T, j), j > kc, and only update them.  Column kc's blocks come
+// rhs tiles (T, j), j > kc, and only update them, after a short sleep.  Column kc's blocks come
 // first, so their longer chains start in the first round.
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_ds_step(Dev d, int k) {
   __shared__ double s_t[kT * kT];
@@ -538,6 +538,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   const int id = blockIdx.x;
   v4d acc[2][2];
   if (id > m) {
+    // Column kc's blocks start the chain the next launch waits on; about
+    // 1.7 us of sleep here lets their loads reach memory ahead of the
+    // trailing tiles' (1.61 -> 1.54 ms per medium LM step; more was slower).
+    __builtin_amdgcn_s_sleep(32);
+    __builtin_amdgcn_s_sleep(32);
     int rid = id - m - 1;
     const int ntr = (m - 1) * m / 2;
     int i, j;

@@ -639,10 +639,16 @@ __device__ __forceinline__ double wave_sum_array(const double* a, int n) {
 __host__ __device__ inline int cam_vector_blocks(int64_t nc) { return (int)((nc + 6) / 7); }
 
 // Per-block partial-sum arrays of the camera-vector kernels (nb blocks each).
+// A launch never writes a slot that one of its blocks reads in full, since a
+// block that starts after another has finished would see part of the new sums.
 __device__ __forceinline__ double* red_rr(const Dev& d, int par) { return d.red_part + 2 * par * d.red_nb; }
-__device__ __forceinline__ double* red_rz(const Dev& d, int par) { return red_rr(d, par) + d.red_nb; }
+// r.z of iteration it, in three slots (1, 3, 5): the step of iteration it
+// reads those of it and it - 1 and writes those of it + 1.
+__device__ __forceinline__ double* red_rz(const Dev& d, int it) {
+  const int s = it % 3;
+  return d.red_part + (2 * s + 1) * d.red_nb;
+}
 __device__ __forceinline__ double* red_rhs(const Dev& d) { return d.red_part + 4 * d.red_nb; }
-__device__ __forceinline__ double* red_pq(const Dev& d) { return d.red_part + 5 * d.red_nb; }
 __device__ __forceinline__ double* red_zbz(const Dev& d, int par) { return d.red_part + (6 + par) * d.red_nb; }
 // p.q of the iterations of either parity (written by block 0 of k_pcg_step)
 __device__ __forceinline__ double* pcg_pq_hist(const Dev& d) { return d.red_part + 8 * d.red_nb; }
@@ -1244,7 +1250,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_step(Dev d, int it) {
   }
   double ze = z[c.a], pe = d.pbuf[e], qe = d.q[e], xe = d.x[e], re = d.r[e];
   double pq_prev = pcg_pq_hist(d)[(it + 1) & 1];
-  const double* const arr[3] = {red_rz(d, it & 1), red_rz(d, (it + 1) & 1), red_zbz(d, it & 1)};
+  const double* const arr[3] = {red_rz(d, it), red_rz(d, it + 2), red_zbz(d, it & 1)};
   double part[3];
   lane_partials<3>(arr, d.red_nb, part);
   double ydot = lane_partial(d.pt_dot, d.lds_blocks);
@@ -1317,7 +1323,7 @@ __global__ __launch_bounds__(kWave) void k_pcg_step(Dev d, int it) {
   zbz = wave_sum(zbz);
   if (threadIdx.x == 0) {
     red_rr(d, (it + 1) & 1)[blockIdx.x] = rr;
-    red_rz(d, (it + 1) & 1)[blockIdx.x] = rzn;
+    red_rz(d, it + 1)[blockIdx.x] = rzn;
     red_zbz(d, (it + 1) & 1)[blockIdx.x] = zbz;
     if (blockIdx.x == 0) pcg_pq_hist(d)[it & 1] = pq;
   }
