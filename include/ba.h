@@ -354,13 +354,16 @@ enum {
   BA_K_DS_RUNS,      /* dense solver: F = Ebar chol(C~^-1) per (point, camera) run  */
   BA_K_DS_FILL,      /* dense solver: S cleared, padding, rhs row                  */
   BA_K_DS_ASSEMBLE,  /* dense solver: lower 9x9 blocks of S                        */
-  BA_K_DS_PANEL,     /* dense solver: diagonal tile factor and tile-row solves      */
-  BA_K_DS_UPDATE,    /* dense solver: trailing update (fp64 MFMA)                  */
+  BA_K_DS_PANEL,     /* dense solver: the first tile column (factor and solves)     */
+  BA_K_DS_UPDATE,    /* dense solver: one launch per later tile column, the trailing
+                        update after the previous column (fp64 MFMA) fused with
+                        this column's diagonal factor and tile solves             */
   BA_K_DS_BACKSOLVE, /* dense solver: L^T dc = L^-1 rhs                            */
   BA_K_COV_ZERO,     /* covariance: zeros in the strictly upper tiles of S, which
-                        then receive Z = L^-T: its tiles are solved and updated
-                        (fp64 MFMA) within the BA_K_DS_PANEL / BA_K_DS_UPDATE
-                        launches of the factorisation                           */
+                        then receive Z = L^-T (its diagonal tiles are kept apart):
+                        its tiles are solved and updated (fp64 MFMA) within the
+                        BA_K_DS_PANEL / BA_K_DS_UPDATE launches of the
+                        factorisation                                           */
   BA_K_COV_BLOCKS,   /* covariance: per camera, the 9x9 block of Z Z^T              */
   BA_K_DL_OBS,       /* dogleg: |J g|^2, (J g).(J h_gn), |J h_gn|^2 partials        */
   BA_K_DL_STEP,      /* dogleg: the step's camera part and the trial points         */

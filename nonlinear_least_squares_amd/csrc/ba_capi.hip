@@ -419,19 +419,10 @@ int stage_dense_factor(ba_problem* h, int cov) {
   TIMED(BA_K_DS_RUNS, -1, launch_ds_runs(d, s));
   TIMED(BA_K_DS_FILL, -1, launch_ds_fill(d, s));
   TIMED(BA_K_DS_ASSEMBLE, -1, launch_ds_assemble(d, s));
-  if (cov) {
-    // the covariance's Z tiles share the diagonal tiles' storage, so it keeps
-    // separate panel and update launches
-    TIMED(BA_K_COV_ZERO, -1, launch_cov_zero(d, s));
-    TIMED(BA_K_DS_PANEL, -1, launch_ds_diag0(d, s));
-    for (int k = 0; k < h->ds_T; ++k) {
-      TIMED(BA_K_DS_PANEL, -1, launch_ds_panel(d, k, cov, s));
-      TIMED(BA_K_DS_UPDATE, -1, launch_ds_update(d, k, cov, s));
-    }
-  } else {
-    for (int k = -1; k < h->ds_T - 1; ++k)
-      TIMED(k < 0 ? BA_K_DS_PANEL : BA_K_DS_UPDATE, -1, launch_ds_step(d, k, s));
-  }
+  // with `cov` the upper tiles, which take Z's off-diagonal tiles, start at zero
+  if (cov) TIMED(BA_K_COV_ZERO, -1, launch_cov_zero(d, s));
+  for (int k = -1; k < h->ds_T - 1; ++k)
+    TIMED(k < 0 ? BA_K_DS_PANEL : BA_K_DS_UPDATE, -1, launch_ds_step(d, k, cov, s));
   HIPC(hipGetLastError());
   return BA_OK;
 }

@@ -19,13 +19,12 @@
 // Only the lower triangle is read or written after assembly.
 //
 // Factorisation, right-looking by 32 x 32 tiles, one launch per tile column
-// for the camera solve (k_ds_step): the trailing update after column k,
-// A_ij -= L_ik L_jk^T with fp64 MFMA (16x16x4), the one dense contraction of
-// the bundle-adjustment pages' methods, fused with the panel of column k + 1:
-// the blocks of that column form and factor its diagonal tile themselves and
-// solve their own tiles against it, L_ik = A_ik L_kk^-T.  The covariance keeps
-// two launches per column (panel, then update), because its Z tiles share the
-// diagonal tiles' storage.  The factor's diagonal tiles are kept apart
+// (k_ds_step): the trailing update after column k, A_ij -= L_ik L_jk^T with
+// fp64 MFMA (16x16x4), the one dense contraction of the bundle-adjustment
+// pages' methods, fused with the panel of column k + 1: the blocks of that
+// column form and factor its diagonal tile themselves and solve their own
+// tiles against it, L_ik = A_ik L_kk^-T.  The covariance's tiles of Z = L^-T
+// ride in the same launches.  The factor's diagonal tiles are kept apart
 // (ds_diag); the back-substitution L^T dc = y runs by 128-row blocks over
 // many workgroups (k_ds_bsolve).
 #include <hip/hip_runtime.h>
@@ -236,95 +235,14 @@ __device__ __forceinline__ void factor_tile(double (&a)[kT], double* s_x, bool& 
   __syncthreads();
 }
 
-// Factor one 32 x 32 diagonal tile held as rows src[r * stride + c] (lane r
-// holds row r) with factor_tile into ds_diag (L, row-major, zeros above the
-// diagonal), ds_diagT (its transpose) and ds_dinv (1 / L(c, c)).  One
-// wavefront; lanes 32..63 repeat lanes 0..31 and store nothing.  A pivot that
-// is not positive and finite sets the not-SPD flag.  s_x: kFactorScratch
-// doubles of LDS, which may be src itself.
-__device__ __forceinline__ void factor_diag_tile(const Dev& d, int kt, const double* src,
-                                                 int64_t stride, double* s_x) {
-  const int r = threadIdx.x & (kT - 1);
-  double a[kT];
-#pragma unroll
-  for (int c = 0; c < kT; ++c) a[c] = src[r * stride + c];
-  __syncthreads();
-  bool bad;
-  factor_tile(a, s_x, bad);
-  if (bad && threadIdx.x == 0) d.flags[1] = 1;
-  if (threadIdx.x >= kT) return;
-  double* L = d.ds_diag + (int64_t)kt * kT * kT;
-  double* LT = d.ds_diagT + (int64_t)kt * kT * kT;
-#pragma unroll
-  for (int c = 0; c < kT; ++c) {
-    const double v = c <= r ? a[c] : 0.0;
-    L[kT * r + c] = v;
-    LT[kT * c + r] = v;
-  }
-  d.ds_dinv[kT * kt + r] = s_x[2 * kH * kH + r];
-}
-
-// The first diagonal tile (the update kernel factors each later one).
-__global__ __launch_bounds__(64) void k_ds_diag0(Dev d) {
-  __shared__ double s_x[kFactorScratch];
-  factor_diag_tile(d, 0, d.ds_S, d.ds_ld, s_x);
-}
-
-// Tile column k, its diagonal tile already factored: one wavefront per tile
-// row i = k + 1 .. T (T: the rhs tile row) solves L_ik L_kk^T = A_ik in place,
-// lane r taking row r.  The factor's columns and pivot reciprocals are staged
-// in LDS and read at wavefront-uniform addresses (broadcasts).
-// Row r (lane r & 31) of one tile at `row` (stride ld) solved in place
-// against the factored diagonal tile k, X L_kk^T = A: the factor's columns and
-// pivot reciprocals are staged in LDS (s_l, kT * kT + kT doubles) and read at
-// wavefront-uniform addresses (broadcasts).
-// With `ident` the tile starts as the identity instead of being read.
-__device__ __forceinline__ void panel_solve(const Dev& d, int k, double* row, double* s_l,
-                                            bool ident) {
-  const double* LT = d.ds_diagT + (int64_t)k * kT * kT;
-  const int r = threadIdx.x & (kT - 1);
-  double b[kT];
-#pragma unroll
-  for (int c = 0; c < kT; ++c) b[c] = ident ? (c == r ? 1.0 : 0.0) : row[c];
-  double lt[kT * kT / 64];
-#pragma unroll
-  for (int u = 0; u < kT * kT / 64; ++u) lt[u] = LT[threadIdx.x + 64 * u];
-#pragma unroll
-  for (int u = 0; u < kT * kT / 64; ++u) s_l[threadIdx.x + 64 * u] = lt[u];
-  if (threadIdx.x < kT) s_l[kT * kT + threadIdx.x] = d.ds_dinv[kT * k + threadIdx.x];
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < kT; ++c) {
-    b[c] *= s_l[kT * kT + c];
-#pragma unroll
-    for (int j = c + 1; j < kT; ++j) b[j] -= b[c] * s_l[kT * c + j];   // L(j, c)
-  }
-  if (threadIdx.x >= kT) return;
-#pragma unroll
-  for (int c = 0; c < kT; ++c) row[c] = b[c];
-}
-
-// Tile column k, its diagonal tile already factored: one wavefront per tile
-// row i = k + 1 .. T (T: the rhs tile row) solves L_ik L_kk^T = A_ik in place,
-// lane r taking row r.  With `cov`, k + 1 more wavefronts solve the tiles
-// Z_jk (j <= k) of Z = L^-T against the same L_kk^T (Z_kk from the identity).
-__global__ __launch_bounds__(64) void k_ds_panel(Dev d, int k, int cov) {
-  __shared__ double s_l[kT * kT + kT];
-  const int nds = d.ds_T - k;
-  const int b = blockIdx.x;
-  const int r = threadIdx.x & (kT - 1);
-  const int row_tile = b < nds ? k + 1 + b : b - nds;
-  panel_solve(d, k, d.ds_S + (int64_t)(kT * row_tile + r) * d.ds_ld + kT * k, s_l,
-              b >= nds && row_tile == k);
-}
-
 // C -= A B^T for 32 x 32 tiles of S (leading dimension ld) as 2 x 2 MFMA
 // tiles of 16 x 16 over K = 32 in steps of 4; the accumulators are left in acc.
 // Operand layout of v_mfma_f64_16x16x4_f64 (lane l): A(m, kk) with m = l % 16,
 // kk = l / 16; B(kk, n) with n = l % 16; accumulator element v (0..3) is row
 // 4 v + l / 16 of column l % 16.
 __device__ __forceinline__ void tile_sub_abt(double* C, const double* A, const double* B,
-                                             int64_t ld, v4d (&acc)[2][2]) {
+                                             int64_t ld, v4d (&acc)[2][2], int64_t lda = 0) {
+  const int64_t la = lda ? lda : ld;
   const int l = threadIdx.x;
   const int lr = l & 15, lk = l >> 4;
   double av[2][8], bv[2][8];
@@ -332,7 +250,7 @@ __device__ __forceinline__ void tile_sub_abt(double* C, const double* A, const d
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      av[h][s] = -A[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
+      av[h][s] = -A[(int64_t)(16 * h + lr) * la + 4 * s + lk];
       bv[h][s] = B[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
     }
   }
@@ -357,57 +275,6 @@ __device__ __forceinline__ void tile_sub_abt(double* C, const double* A, const d
       for (int v = 0; v < 4; ++v) C[(int64_t)(16 * mh + 4 * v + lk) * ld + 16 * nh + lr] = acc[mh][nh][v];
 }
 
-// Trailing update after tile column k: one wavefront per tile (i, j) with
-// k < j <= i < T, then the rhs tile row (T, j): A_ij -= L_ik L_jk^T.  The
-// wavefront of tile (k + 1, k + 1) then factors that tile for the next panel.
-// With `cov`, one more wavefront per tile Z_ji, j <= k < i: Z_ji -= Z_jk L_ik^T.
-__global__ __launch_bounds__(64) void k_ds_update(Dev d, int k, int cov) {
-  const int m = d.ds_T - k - 1;          // trailing tile columns
-  const int tri = m * (m + 1) / 2;
-  const int id = blockIdx.x;
-  if (id >= tri + m) {
-    const int cid = id - (tri + m);
-    const int j = cid % (k + 1), i = k + 1 + cid / (k + 1);
-    const int64_t ld = d.ds_ld;
-    double* S = d.ds_S;
-    v4d acc[2][2];
-    tile_sub_abt(S + (int64_t)(kT * j) * ld + kT * i, S + (int64_t)(kT * j) * ld + kT * k,
-                 S + (int64_t)(kT * i) * ld + kT * k, ld, acc);
-    return;
-  }
-  int i, j;
-  if (id < tri) {
-    int ii = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
-    while ((ii + 1) * (ii + 2) / 2 <= id) ++ii;
-    while (ii * (ii + 1) / 2 > id) --ii;
-    i = k + 1 + ii;
-    j = k + 1 + (id - ii * (ii + 1) / 2);
-  } else {
-    i = d.ds_T;
-    j = k + 1 + (id - tri);
-  }
-  const int l = threadIdx.x;
-  const int lr = l & 15, lk = l >> 4;
-  const int64_t ld = d.ds_ld;
-  double* S = d.ds_S;
-  v4d acc[2][2];
-  tile_sub_abt(S + (int64_t)(kT * i) * ld + kT * j, S + (int64_t)(kT * i) * ld + kT * k,
-               S + (int64_t)(kT * j) * ld + kT * k, ld, acc);
-  if (id == 0) {
-    // tile (k + 1, k + 1) is final now: factor it for the next panel, its
-    // rows passed through LDS
-    __shared__ double s_t[kT * kT];
-#pragma unroll
-    for (int mh = 0; mh < 2; ++mh)
-#pragma unroll
-      for (int nh = 0; nh < 2; ++nh)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) s_t[(16 * mh + 4 * v + lk) * kT + 16 * nh + lr] = acc[mh][nh][v];
-    __syncthreads();
-    factor_diag_tile(d, k + 1, s_t, kT, s_t);
-  }
-}
-
 // The diagonal tile and one tile of the same tile column after the update,
 // accd = Cd - B B^T and acco = Co - Ao B^T (no subtraction without `sub`),
 // with every load issued before the first product: B (the tile column's
@@ -415,7 +282,9 @@ __global__ __launch_bounds__(64) void k_ds_update(Dev d, int k, int cov) {
 // and as the right operand of the second.
 __device__ __forceinline__ void tile_abt_pair(const double* Cd, const double* Co, const double* Ao,
                                               const double* B, int64_t ld, bool sub,
-                                              v4d (&accd)[2][2], v4d (&acco)[2][2]) {
+                                              v4d (&accd)[2][2], v4d (&acco)[2][2], int64_t ldco = 0,
+                                              int64_t ldao = 0) {
+  const int64_t lc = ldco ? ldco : ld, la = ldao ? ldao : ld;
   const int l = threadIdx.x;
   const int lr = l & 15, lk = l >> 4;
   // the diagonal tile is accumulated negated, -(Cd) + B B^T, and negated
@@ -428,7 +297,7 @@ __device__ __forceinline__ void tile_abt_pair(const double* Cd, const double* Co
       for (int v = 0; v < 4; ++v) {
         const int64_t o = (int64_t)(16 * mh + 4 * v + lk) * ld + 16 * nh + lr;
         accd[mh][nh][v] = -Cd[o];
-        acco[mh][nh][v] = Co[o];
+        acco[mh][nh][v] = Co[(int64_t)(16 * mh + 4 * v + lk) * lc + 16 * nh + lr];
       }
   if (sub) {
   double bv[2][8], ao[2][8];
@@ -437,7 +306,7 @@ __device__ __forceinline__ void tile_abt_pair(const double* Cd, const double* Co
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       bv[h][s] = B[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
-      ao[h][s] = -Ao[(int64_t)(16 * h + lr) * ld + 4 * s + lk];
+      ao[h][s] = -Ao[(int64_t)(16 * h + lr) * la + 4 * s + lk];
     }
   }
 #pragma unroll
@@ -470,10 +339,11 @@ __device__ __forceinline__ void acc_to_rows(const v4d (&acc)[2][2], double* s_t)
 
 // Factor the diagonal tile whose row r lane r holds in a[] (lanes 32..63
 // repeat lanes 0..31) with factor_tile, s_l serving as its scratch, leaving
-// its transpose and the pivot reciprocals in s_l (the layout panel_solve
-// stages) and, with `to_global`, in ds_diag, ds_diagT and ds_dinv.
+// its transpose and the pivot reciprocals in s_l (the layout solve_rows
+// reads) and, with `to_global`, in ds_diag, ds_dinv and (with `write_lt`)
+// ds_diagT.
 __device__ __forceinline__ void factor_rows(const Dev& d, int kt, double (&a)[kT], double* s_l,
-                                            bool to_global) {
+                                            bool to_global, bool write_lt = true) {
   const int r = threadIdx.x & (kT - 1);
   bool bad;
   factor_tile(a, s_l, bad);
@@ -491,7 +361,7 @@ __device__ __forceinline__ void factor_rows(const Dev& d, int kt, double (&a)[kT
   for (int c = 0; c < kT; ++c) {
     const double v = c <= r ? a[c] : 0.0;
     L[kT * r + c] = v;
-    LT[kT * c + r] = v;
+    if (write_lt) LT[kT * c + r] = v;
   }
   d.ds_dinv[kT * kt + r] = myinv;
 }
@@ -515,19 +385,24 @@ __device__ __forceinline__ void solve_rows(const double* s_t, const double* s_l,
   for (int c = 0; c < kT; ++c) dst[(int64_t)r * ld + c] = b[c];
 }
 
-// One step of the factorisation for the camera solve: the trailing update
-// after tile column k (none for k = -1) and the panel of tile column
-// kc = k + 1 in one launch, so that the chain is one launch per tile column.
-// With m = T - kc, block b < m takes tile (kc + b, kc) and block m the rhs
-// tile (T, kc): each forms the diagonal tile A_dd - L_dk L_dk^T of column kc
-// and factors it (the same instructions on the same data in every block, so
-// the same bits; block 0 also stores the factor), then updates its own tile
-// and solves it in place, L_ikc = (A_ikc - L_ik L_kck^T) L_dd^-T.  No block
-// writes the diagonal tile of S, so each reads it before its update.  The
-// remaining blocks take the other trailing tiles (i, j), kc < j <= i < T, and
-// rhs tiles (T, j), j > kc, and only update them, after a short sleep.  Column kc's blocks come
-// first, so their longer chains start in the first round.
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_ds_step(Dev d, int k) {
+// One step of the factorisation: the trailing update after tile column k
+// (none for k = -1) and the panel of tile column kc = k + 1 in one launch, so
+// that the chain is one launch per tile column.  With m = T - kc, block
+// b < m takes tile (kc + b, kc) and block m the rhs tile (T, kc): each forms
+// the diagonal tile A_dd - L_dk L_dk^T of column kc and factors it (the same
+// instructions on the same data in every block, so the same bits; block 0
+// also stores the factor), then updates its own tile and solves it in place,
+// L_ikc = (A_ikc - L_ik L_kck^T) L_dd^-T.  No block writes the diagonal tile
+// of S, so each reads it before its update.  With `cov` (the covariance),
+// kc + 1 more blocks do the same for the tiles Z_jkc (j <= kc) of Z = L^-T,
+// Z_jkc L_dd^T = delta_jkc I - Z_jk L_kck^T, which keep Z's earlier updates
+// in the strictly upper tiles of S; Z_kckc, which starts as the identity, goes
+// to ds_diagT (the diagonal tile of S is still being read in this launch).
+// The remaining blocks, after a short sleep, take the other trailing tiles
+// (i, j), kc < j <= i < T, and rhs tiles (T, j), j > kc, and only update them,
+// and with `cov` the tiles Z_ji -= Z_jk L_ik^T, j <= k < kc < i.  The column
+// blocks come first, so their longer chains start in the first round.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_ds_step(Dev d, int k, int cov) {
   __shared__ double s_t[kT * kT];
   __shared__ double s_l[kT * kT + kT];
   const int T = d.ds_T, kc = k + 1, m = T - kc;
@@ -535,37 +410,68 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   const bool sub = k >= 0;
   const int64_t ld = d.ds_ld;
   double* S = d.ds_S;
+  double* Zd = d.ds_diagT;   // Z's diagonal tiles, with `cov`
   const int id = blockIdx.x;
+  const int ncol = m + 1, nzp = cov ? kc + 1 : 0;
   v4d acc[2][2];
-  if (id > m) {
+  if (id >= ncol + nzp) {
     // Column kc's blocks start the chain the next launch waits on; about
     // 1.7 us of sleep here lets their loads reach memory ahead of the
     // trailing tiles' (1.61 -> 1.54 ms per medium LM step; more was slower).
     __builtin_amdgcn_s_sleep(32);
     __builtin_amdgcn_s_sleep(32);
-    int rid = id - m - 1;
-    const int ntr = (m - 1) * m / 2;
-    int i, j;
-    if (rid < ntr) {
-      int ii = (int)((sqrt(8.0 * rid + 1.0) - 1.0) * 0.5);
-      while ((ii + 1) * (ii + 2) / 2 <= rid) ++ii;
-      while (ii * (ii + 1) / 2 > rid) --ii;
-      i = kc + 1 + ii;
-      j = kc + 1 + (rid - ii * (ii + 1) / 2);
+    const int rid = id - ncol - nzp;
+    const int ntr = (m - 1) * m / 2, nts = ntr + m - 1;
+    if (rid < nts) {
+      int i, j;
+      if (rid < ntr) {
+        int ii = (int)((sqrt(8.0 * rid + 1.0) - 1.0) * 0.5);
+        while ((ii + 1) * (ii + 2) / 2 <= rid) ++ii;
+        while (ii * (ii + 1) / 2 > rid) --ii;
+        i = kc + 1 + ii;
+        j = kc + 1 + (rid - ii * (ii + 1) / 2);
+      } else {
+        i = T;
+        j = kc + 1 + (rid - ntr);
+      }
+      tile_sub_abt(S + (int64_t)(kT * i) * ld + kT * j, S + (int64_t)(kT * i) * ld + kT * k0,
+                   S + (int64_t)(kT * j) * ld + kT * k0, ld, acc);
     } else {
-      i = T;
-      j = kc + 1 + (rid - ntr);
+      const int zid = rid - nts;
+      const int j = zid % (k + 1), i = kc + 1 + zid / (k + 1);
+      const double* Zjk = j == k ? Zd + (int64_t)k * kT * kT : S + (int64_t)(kT * j) * ld + kT * k;
+      tile_sub_abt(S + (int64_t)(kT * j) * ld + kT * i, Zjk, S + (int64_t)(kT * i) * ld + kT * k, ld, acc,
+                   j == k ? kT : ld);
     }
-    tile_sub_abt(S + (int64_t)(kT * i) * ld + kT * j, S + (int64_t)(kT * i) * ld + kT * k0,
-                 S + (int64_t)(kT * j) * ld + kT * k0, ld, acc);
     return;
   }
-  const int i = id < m ? kc + id : T;
+  const bool zt = id >= ncol;
+  const int j = id - ncol;
+  const bool ident = zt && j == kc;
   const double* Ld = S + (int64_t)(kT * kc) * ld + kT * k0;
-  double* own = S + (int64_t)(kT * i) * ld + kT * kc;
+  const double* Cd = S + (int64_t)(kT * kc) * ld + kT * kc;
+  double* own;
+  const double* Ao;
+  int64_t ldo, ldao;
+  if (!zt) {
+    const int i = id < m ? kc + id : T;
+    own = S + (int64_t)(kT * i) * ld + kT * kc;
+    Ao = S + (int64_t)(kT * i) * ld + kT * k0;
+    ldo = ld;
+    ldao = ld;
+  } else if (!ident) {
+    own = S + (int64_t)(kT * j) * ld + kT * kc;
+    Ao = j == k ? Zd + (int64_t)k * kT * kT : S + (int64_t)(kT * j) * ld + kT * k0;
+    ldo = ld;
+    ldao = j == k ? kT : ld;
+  } else {
+    own = Zd + (int64_t)kc * kT * kT;
+    Ao = Ld;   // not used: the tile starts as the identity
+    ldo = kT;
+    ldao = ld;
+  }
   v4d acco[2][2];
-  tile_abt_pair(S + (int64_t)(kT * kc) * ld + kT * kc, own, S + (int64_t)(kT * i) * ld + kT * k0,
-                Ld, ld, sub, acc, acco);
+  tile_abt_pair(Cd, ident ? Cd : own, Ao, Ld, ld, sub, acc, acco, ident ? ld : ldo, ldao);
   // the diagonal tile's rows go to the lanes through s_t, which then takes
   // the block's own tile (so that its accumulators are not held through the
   // factorisation)
@@ -576,23 +482,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 #pragma unroll
   for (int c = 0; c < kT; ++c) a[c] = s_t[r * kT + c];
   __syncthreads();
-  if (id != 0) acc_to_rows(acco, s_t);
-  factor_rows(d, kc, a, s_l, id == 0);
+  if (id != 0) {
+    if (ident) {
+#pragma unroll
+      for (int c = 0; c < kT; ++c) s_t[r * kT + c] = c == r ? 1.0 : 0.0;
+    } else {
+      acc_to_rows(acco, s_t);
+    }
+  }
+  factor_rows(d, kc, a, s_l, id == 0, !cov);
   __syncthreads();
   if (id == 0) return;
-  solve_rows(s_t, s_l, own, ld);
+  solve_rows(s_t, s_l, own, ldo);
 }
 
 // ---- camera marginal covariance: blocks of S^-1 = L^-T L^-1 ---------------
 //
 // Z = L^-T (upper triangular) is formed by tiles in the strictly upper tiles
-// of S, which the factorisation never reads, and in its diagonal tiles once
-// they are factored (the factor's diagonal tiles live in ds_diag).  Z L^T = I
-// gives, tile by tile,
+// of S, which the factorisation never reads, and its diagonal tiles in
+// ds_diagT (the factor's diagonal tiles live in ds_diag).  Z L^T = I gives,
+// tile by tile,
 //   Z_jk L_kk^T = delta_jk I - sum_{m < k} Z_jm L_km^T,
-// so the factorisation's launches carry it along: the panel of tile column k
-// also solves the tiles Z_jk, j <= k, against L_kk^T, and the update after it
-// also takes them out of the later columns, Z_ji -= Z_jk L_ik^T for j <= k < i.
+// so the factorisation's launches carry it along (k_ds_step with `cov`): the
+// launch of tile column k also solves the tiles Z_jk, j <= k, against L_kk^T,
+// and takes the tiles of column k - 1 out of the later columns,
+// Z_ji -= Z_j,k-1 L_i,k-1^T for j <= k - 1 < k < i.
 // Each camera's 9x9 block of S^-1 = Z Z^T is then the 45 dot products of its
 // 9 rows of Z.
 
@@ -625,7 +539,10 @@ __global__ __launch_bounds__(256) void k_cov_blocks(Dev d, double* out) {
   for (int64_t col = start[0] + threadIdx.x; col < n; col += 256) {
     double z[9];
 #pragma unroll
-    for (int a = 0; a < 9; ++a) z[a] = col >= start[a] ? Z[(r0 + a) * ld + col] : 0.0;
+    for (int a = 0; a < 9; ++a)
+      z[a] = col < start[a] ? 0.0
+           : (col < start[a] + kT ? d.ds_diagT[start[a] * kT + (r0 + a - start[a]) * kT + (col - start[a])]
+                                  : Z[(r0 + a) * ld + col]);
     int q = 0;
 #pragma unroll
     for (int a = 0; a < 9; ++a)
@@ -817,7 +734,6 @@ void launch_cov_zero(const Dev& d, hipStream_t s) {
   const int64_t n = (int64_t)d.ds_ld * d.ds_ld;
   launch_timed(k_cov_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), s, 0u, d);
 }
-int cov_update_tiles(const Dev& d, int k) { return (k + 1) * (d.ds_T - k - 1); }
 void launch_cov_blocks(const Dev& d, double* out, int64_t n_cams, hipStream_t s) {
   if (n_cams > 0) launch_timed(k_cov_blocks, dim3((unsigned)n_cams), dim3(256), s, 0u, d, out);
 }
@@ -832,24 +748,14 @@ void launch_ds_fill(const Dev& d, hipStream_t s) {
 void launch_ds_assemble(const Dev& d, hipStream_t s) {
   if (d.ds_nblk > 0) launch_timed(k_ds_assemble, dim3(d.ds_nblk), dim3(64 * kAsmWaves), s, 0u, d);
 }
-void launch_ds_diag0(const Dev& d, hipStream_t s) { launch_timed(k_ds_diag0, dim3(1), dim3(64), s, 0u, d); }
-void launch_ds_panel(const Dev& d, int k, int cov, hipStream_t s) {
-  launch_timed(k_ds_panel, dim3(d.ds_T - k + (cov ? k + 1 : 0)), dim3(64), s, 0u, d, k, cov);
+int ds_step_blocks(const Dev& d, int k, int cov) {
+  const int kc = k + 1, m = d.ds_T - kc;
+  int n = m + 1 + (cov ? kc + 1 : 0);
+  if (k >= 0) n += (m - 1) * m / 2 + (m - 1) + (cov ? (k + 1) * (m - 1) : 0);
+  return n;
 }
-int ds_update_tiles(const Dev& d, int k) {
-  const int m = d.ds_T - k - 1;
-  return m * (m + 1) / 2 + m;
-}
-int ds_step_blocks(const Dev& d, int k) {
-  const int m = d.ds_T - k - 1;
-  return k < 0 ? m + 1 : m * (m + 1) / 2 + m;
-}
-void launch_ds_step(const Dev& d, int k, hipStream_t s) {
-  launch_timed(k_ds_step, dim3(ds_step_blocks(d, k)), dim3(64), s, 0u, d, k);
-}
-void launch_ds_update(const Dev& d, int k, int cov, hipStream_t s) {
-  const int n = ds_update_tiles(d, k) + (cov ? cov_update_tiles(d, k) : 0);
-  if (n > 0) launch_timed(k_ds_update, dim3(n), dim3(64), s, 0u, d, k, cov);
+void launch_ds_step(const Dev& d, int k, int cov, hipStream_t s) {
+  launch_timed(k_ds_step, dim3(ds_step_blocks(d, k, cov)), dim3(64), s, 0u, d, k, cov);
 }
 hipError_t ds_backsolve_limit(int ld) {
   (void)ld;

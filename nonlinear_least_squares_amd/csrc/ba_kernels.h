@@ -244,13 +244,9 @@ int ds_tile();
 void launch_ds_runs(const Dev& d, hipStream_t s);
 void launch_ds_fill(const Dev& d, hipStream_t s);
 void launch_ds_assemble(const Dev& d, hipStream_t s);
-void launch_ds_diag0(const Dev& d, hipStream_t s);
-void launch_ds_panel(const Dev& d, int k, int cov, hipStream_t s);
-int ds_update_tiles(const Dev& d, int k);
-void launch_ds_update(const Dev& d, int k, int cov, hipStream_t s);
 // One launch per tile column for the camera solve: update after column k fused
 // with the panel of column k + 1 (k = -1: the first panel alone).
-void launch_ds_step(const Dev& d, int k, hipStream_t s);
+void launch_ds_step(const Dev& d, int k, int cov, hipStream_t s);
 hipError_t ds_backsolve_limit(int ld);
 void launch_ds_backsolve(const Dev& d, hipStream_t s);
 // Dogleg (ba_dogleg.hip): the six sums of the step's model, and the trial
@@ -264,7 +260,6 @@ void launch_dl_step(const Dev& d, double s_g, double s_n, double* hc, hipStream_
 // (its tiles of Z = L^-T ride on the factorisation's panel and update
 // launches when their `cov` flag is set)
 void launch_cov_zero(const Dev& d, hipStream_t s);
-int cov_update_tiles(const Dev& d, int k);
 void launch_cov_blocks(const Dev& d, double* out, int64_t n_cams, hipStream_t s);
 
 // Implicit backward: a <- -a; per observation psi'(r) (Jc x_cam + Jp dp_pt) to
